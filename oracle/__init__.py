@@ -1,0 +1,241 @@
+"""CPU oracle for the block-quantized weight matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of `bench.py` may import
+this package.  The product path (the HIP library and its binding) never calls it.
+
+This is a ctypes wrapper over `qg_oracle.c` (plain C, built with gcc), which holds every piece
+of arithmetic: the format decoders, the f16 / bf16 conversions, the f64 GEMM, the row scaling,
+the routing plan and the combine.  The wrapper only marshals numpy arrays.  Each function's
+definition and its sources are stated in `qg_oracle.c`.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+FMT = {"q4": 0, "q4a": 1, "q8": 2}
+XT = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
+
+_p = C.c_void_p
+_i = C.c_int
+_sz = C.c_size_t
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(_LIB_PATH)
+        L.orc_f16_value.restype = C.c_double
+        L.orc_f16_value.argtypes = [C.c_uint16]
+        L.orc_bf16_value.restype = C.c_double
+        L.orc_bf16_value.argtypes = [C.c_uint16]
+        L.orc_f32_to_f16.restype = C.c_uint16
+        L.orc_f32_to_f16.argtypes = [C.c_float]
+        L.orc_f32_to_bf16.restype = C.c_uint16
+        L.orc_f32_to_bf16.argtypes = [C.c_float]
+        L.orc_weight_exact.restype = C.c_double
+        L.orc_weight_exact.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i]
+        L.orc_weight_f32.restype = C.c_float
+        L.orc_weight_f32.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i]
+        L.orc_dequant_tile.restype = None
+        L.orc_dequant_tile.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
+        L.orc_gemm.restype = _i
+        L.orc_gemm.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _i, _p, _p, _i]
+        L.orc_x_half.restype = None
+        L.orc_x_half.argtypes = [_p, _i, _p, _i, _p, _p]
+        L.orc_swiglu.restype = None
+        L.orc_swiglu.argtypes = [_p, _p, _sz, _p]
+        L.orc_moe_plan.restype = _i
+        L.orc_moe_plan.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
+        L.orc_moe_combine.restype = None
+        L.orc_moe_combine.argtypes = [_p, _i, _p, _p, _i, _i, _p, _p]
+        for name in ("orc_f16_values", "orc_bf16_values"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [_p, _sz, _p]
+        for name in ("orc_f32_to_f16_array", "orc_f32_to_bf16_array"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [_p, _sz, _p]
+        L.orc_dequant_exact.restype = None
+        L.orc_dequant_exact.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _weights(fmt, codes, scales, offsets):
+    if fmt == "q8":
+        return _c(codes, np.int8), _c(scales, np.float32), None
+    return _c(codes, np.uint8), _c(scales, np.uint16), (_c(offsets, np.uint16) if fmt == "q4a" else None)
+
+
+# ---- 16-bit float definitions ------------------------------------------------------------------
+def f16_values(bits) -> np.ndarray:
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    lib().orc_f16_values(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def bf16_values(bits) -> np.ndarray:
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    lib().orc_bf16_values(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def f32_to_f16(x) -> np.ndarray:
+    a = _c(x, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().orc_f32_to_f16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    a = _c(x, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().orc_f32_to_bf16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+# ---- dequantization ----------------------------------------------------------------------------
+def weight_exact(fmt, codes, scales, offsets, group, N, K, n, k) -> float:
+    c, s, o = _weights(fmt, codes, scales, offsets)
+    return lib().orc_weight_exact(FMT[fmt], _ptr(c), _ptr(s), _ptr(o), group, N, K, n, k)
+
+
+def dequant_exact(fmt, codes, scales, offsets, group, N, K) -> np.ndarray:
+    """Whole matrix of exact weight values, f64 [N, K]."""
+    c, s, o = _weights(fmt, codes, scales, offsets)
+    out = np.empty((N, K), np.float64)
+    lib().orc_dequant_exact(FMT[fmt], _ptr(c), _ptr(s), _ptr(o), group, N, K, _ptr(out))
+    return out
+
+
+def dequant_tile(fmt, codes, scales, offsets, group, N, K, n0, k0, rows, cols, staged) -> np.ndarray:
+    """The staged tile [rows, cols]: f32 values, or f16 / bf16 bits (uint16)."""
+    c, s, o = _weights(fmt, codes, scales, offsets)
+    out = np.empty((rows, cols), np.float32 if staged == "f32" else np.uint16)
+    lib().orc_dequant_tile(FMT[fmt], _ptr(c), _ptr(s), _ptr(o), group, N, K, n0, k0, rows, cols, XT[staged],
+                           _ptr(out))
+    return out
+
+
+# ---- GEMM --------------------------------------------------------------------------------------
+def gemm(fmt, codes, scales, offsets, group, N, K, X, xtype, T, ns=None, ts=None, threads=None):
+    """(Y, S, threads_used): Y[t][n] = sum_k x*v32 and S = sum_k |x*v32| in f64, over the selected
+    rows ns (default all N) and tokens ts (default all T); arrays [len(ts), len(ns)]."""
+    c, s, o = _weights(fmt, codes, scales, offsets)
+    xdt = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64}[xtype]
+    if xtype == "f16" and np.asarray(X).dtype == np.float16:
+        X = np.asarray(X).view(np.uint16)
+    x = _c(X, xdt)
+    nsa = None if ns is None else _c(ns, np.int32)
+    tsa = None if ts is None else _c(ts, np.int32)
+    nn = N if nsa is None else nsa.size
+    nt = T if tsa is None else tsa.size
+    Y = np.empty((nt, nn), np.float64)
+    S = np.empty((nt, nn), np.float64)
+    if threads is None:
+        threads = os.cpu_count() or 1
+    used = lib().orc_gemm(FMT[fmt], _ptr(c), _ptr(s), _ptr(o), group, N, K, _ptr(x), XT[xtype], T,
+                          _ptr(nsa), nn, _ptr(tsa), nt, _ptr(Y), _ptr(S), int(threads))
+    return Y, S, used
+
+
+# ---- MoE pieces --------------------------------------------------------------------------------
+def x_half(X, K, src=None, R=None):
+    """(xh f16 bits [R, K], rs f32 [R]) of the per-row power-of-two scaling of f32 rows."""
+    x = _c(X, np.float32)
+    srca = None if src is None else _c(src, np.int32)
+    if R is None:
+        R = srca.size if srca is not None else x.size // K
+    xh = np.empty((R, K), np.uint16)
+    rs = np.empty(R, np.float32)
+    lib().orc_x_half(_ptr(x), K, _ptr(srca), R, _ptr(xh), _ptr(rs))
+    return xh, rs
+
+
+def swiglu(G, U) -> np.ndarray:
+    g = _c(G, np.float64)
+    u = _c(U, np.float64)
+    out = np.empty(g.shape, np.float64)
+    lib().orc_swiglu(_ptr(g), _ptr(u), g.size, _ptr(out))
+    return out
+
+
+def moe_plan(logits, T, E, k) -> dict:
+    lg = _c(logits, np.float32)
+    seg_off = np.empty(E + 1, np.int32)
+    row_src = np.empty(T * k, np.int32)
+    slot_row = np.empty(T * k, np.int32)
+    slot_w = np.empty(T * k, np.float64)
+    slot_e = np.empty(T * k, np.int32)
+    R = lib().orc_moe_plan(_ptr(lg), T, E, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w),
+                           _ptr(slot_e))
+    return {"R": R, "seg_off": seg_off, "row_src": row_src, "slot_row": slot_row, "slot_w": slot_w,
+            "slot_expert": slot_e}
+
+
+def moe_combine(O, H, slot_row, slot_w, T, k):
+    """(y [T, H], b [T, H]) with y = sum_j w_j O[row_j] and b = sum_j |w_j O[row_j]| in f64."""
+    o = _c(O, np.float64)
+    sr = _c(slot_row, np.int32)
+    sw = _c(slot_w, np.float64)
+    y = np.empty((T, H), np.float64)
+    b = np.empty((T, H), np.float64)
+    lib().orc_moe_combine(_ptr(o), H, _ptr(sr), _ptr(sw), T, k, _ptr(y), _ptr(b))
+    return y, b
+
+
+def moe_ffn(m: dict, plan: dict, experts=None, threads=None) -> dict:
+    """The MoE chain in f64: per routed row r of expert e (token t = row_src[r]):
+    [g | u] = W_gu[e] x_t, a = SiLU(g) u, o_r = W_dn[e] a, y_t = sum_j w_j o_{slot_j}.
+
+    Also returns the first-order error bound B[t][c] used by the end-to-end check:
+    B = sum_j |w_j| (sum_i |a_i w_dn[c][i]| + sum_i |w_dn[c][i]| (1.1 |u_i| Sg_i + |silu(g_i)| Su_i)),
+    where Sg, Su are the S sums of the gate and up rows (the propagated gate/up error is at
+    most tol * S, and |d silu / dg| <= 1.1)."""
+    E, H, I, T = m["E"], m["H"], m["I"], m["T"]
+    X = np.asarray(m["X"], np.float32).reshape(T, H)
+    R = plan["R"]
+    seg = plan["seg_off"]
+    src = plan["row_src"]
+    O = np.zeros((R, H), np.float64)
+    Bo = np.zeros((R, H), np.float64)
+    Gs = np.zeros((R, 2 * I), np.float64)
+    for e in range(E):
+        r0, r1 = int(seg[e]), int(seg[e + 1])
+        if r1 == r0:
+            continue
+        xr = X[src[r0:r1]]
+        gu, sgu, _ = gemm("q4", m["gu_codes"][e], m["gu_scales"][e], None, 64, 2 * I, H, xr, "f32", r1 - r0,
+                          threads=threads)
+        Gs[r0:r1] = gu
+        g, u = gu[:, :I], gu[:, I:]
+        a = swiglu(g, u)
+        o, so, _ = gemm("q4", m["dn_codes"][e], m["dn_scales"][e], None, 64, H, I, a, "f64", r1 - r0,
+                        threads=threads)
+        sig = 1.0 / (1.0 + np.exp(-g))
+        da = 1.1 * np.abs(u) * sgu[:, :I] + np.abs(g * sig) * sgu[:, I:]
+        wabs = np.abs(dequant_exact("q4", m["dn_codes"][e], m["dn_scales"][e], None, 64, H, I))
+        O[r0:r1] = o
+        Bo[r0:r1] = so + da @ wabs.T
+    y, _ = moe_combine(O, H, plan["slot_row"], plan["slot_w"], T, len(plan["slot_w"]) // T)
+    B, _ = moe_combine(Bo, H, plan["slot_row"], np.abs(plan["slot_w"]), T, len(plan["slot_w"]) // T)
+    return {"y": y, "bound": B, "O": O, "GU": Gs}

@@ -1,0 +1,375 @@
+/*
+ * qg_oracle.c -- plain, slow, obviously correct CPU oracle for the block-quantized
+ * weight matrix multiply Y[T x N] = X[T x K] . dequant(W)[N x K]^T and its MoE chain.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline load this library.  It shares no code, header, table or helper with the HIP
+ * library: it has its own bit decoding, its own f16 / bf16 conversions and its own
+ * rounding routines, written from the definitions of the formats.
+ *
+ * Sources (all on the page "oxinfer 0.0.5 src/metal.rs" unless another page is named):
+ *   - Q4 block layout and value, SHADER_SRC, "Dequantizers" (struct Q4W, nib_lo, nib_hi,
+ *     load(Q4W)): block b of row n is 16 bytes at n*K/2 + 16 b; byte j carries element j in
+ *     its low nibble and element j + 16 in its high nibble; the f16 scale of the block is
+ *     entry n*K/32 + b of the scale array; value = (nibble - 8) * scale, evaluated in f32.
+ *   - Affine Q4, SHADER_SRC (struct Q4A, load(Q4A)) and Backend::upload (offsets row
+ *     stride K/group, group/32 blocks per offset): a bf16 offset m, entry
+ *     n*(K/group) + floor(k/group), is added (in f32) to every element of the group.
+ *   - Q8, SHADER_SRC (struct Q8W, load(Q8W)): int8 code at n*K + k, f32 scale of the
+ *     32-element block at n*K/32 + floor(k/32); value = float(q) * scale in f32.
+ *   - Fast-mode staging, MMA_SHADER_SRC (mma_tile): the f32 value is converted to a 16-bit
+ *     float as it is written to the tile (round to nearest, ties to even).
+ *   - Row scaling to f16, MMA_SHADER_SRC (row_scale, x_half): per row, amax; frexp exponent
+ *     e; scale 2^(14 - e) clamped to 2^[-100, 100]; scale 1 for a zero or non-finite amax;
+ *     the inverse scale is kept for the epilogue.
+ *   - SiLU(gate) * up, MMA_SHADER_SRC (silu_half) and the tests' MoE reference.
+ *   - Weighted combine, MMA_SHADER_SRC (moe_combine): out[t] = sum over the token's slots
+ *     of weight * o[row], in slot order.
+ *   - Routing: page "cortiq-engine 0.8.44 src/clover.rs", coreset_from_logits (top-k set:
+ *     descending logit, lower index first on ties) and the route closure of
+ *     clover_metal_pass (weight = p[e] / sum of the kept p); segment order: Backend::moe
+ *     (experts ascending; rows of one expert in token order).
+ *
+ * Arithmetic: the dequantized weight is the f32 value the pages' decoders compute (v32);
+ * every sum is taken in f64 in ascending index order.  Build with -ffp-contract=off so the
+ * f32 decode is two separately rounded operations, as written.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_Q4 = 0, ORC_Q4A = 1, ORC_Q8 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_F64 = 3 };
+
+/* ---------------------------------------------------------------------------------------
+ * 16-bit float definitions, decoded field by field.
+ * f16: 1 sign, 5 exponent (bias 15), 10 fraction bits.  bf16: 1 sign, 8 exponent (bias 127),
+ * 7 fraction bits.  Subnormals have exponent field 0 and no implicit bit.
+ */
+double orc_f16_value(uint16_t h) {
+    int sign = h >> 15, ex = (h >> 10) & 0x1F, fr = h & 0x3FF;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -24);
+    else if (ex == 0x1F)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fr + 1024), ex - 25);
+    return sign ? -v : v;
+}
+
+double orc_bf16_value(uint16_t b) {
+    int sign = b >> 15, ex = (b >> 7) & 0xFF, fr = b & 0x7F;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -133);
+    else if (ex == 0xFF)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fr + 128), ex - 134);
+    return sign ? -v : v;
+}
+
+/* Round a finite magnitude a >= 0 to the grid of a binary float with `p` significand bits,
+ * smallest normal exponent emin (value 2^emin) and ties to even.  Returns the rounded
+ * magnitude (may be 2^(emax+1), which the caller turns into infinity). */
+static double round_to_grid(double a, int p, int emin) {
+    if (a == 0.0) return 0.0;
+    int e2;
+    frexp(a, &e2);               /* a = f * 2^e2, f in [0.5, 1): floor(log2 a) = e2 - 1 */
+    int lsb = e2 - 1 - (p - 1);  /* exponent of the last significand bit */
+    if (lsb < emin - (p - 1)) lsb = emin - (p - 1);
+    double q = ldexp(1.0, lsb);
+    double r = a / q;            /* exact: division by a power of two */
+    double fl = floor(r);
+    double frac = r - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    return fl * q;
+}
+
+/* Encode an already representable magnitude into the fields of a 16-bit float. */
+static uint16_t encode16(double a, int fbits, int bias, int emax_field) {
+    if (a == 0.0) return 0;
+    int e2;
+    double f = frexp(a, &e2);    /* a = f 2^e2 */
+    int ex = e2 - 1 + bias;      /* biased exponent if normal */
+    if (ex >= emax_field) return (uint16_t)(emax_field << fbits);  /* infinity */
+    if (ex <= 0) {               /* subnormal: a = fr * 2^(1 - bias - fbits) */
+        double fr = ldexp(a, bias - 1 + fbits);
+        return (uint16_t)fr;
+    }
+    double fr = (2.0 * f - 1.0) * (double)(1 << fbits);
+    return (uint16_t)((ex << fbits) | (int)fr);
+}
+
+uint16_t orc_f32_to_f16(float x) {
+    if (isnan(x)) return 0x7E00;
+    uint16_t s = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isinf(x) || a >= 65520.0) return s | 0x7C00;
+    double r = round_to_grid(a, 11, -14);
+    return s | encode16(r, 10, 15, 31);
+}
+
+uint16_t orc_f32_to_bf16(float x) {
+    if (isnan(x)) return 0x7FC0;
+    uint16_t s = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isinf(x)) return s | 0x7F80;
+    double r = round_to_grid(a, 8, -126);
+    return s | encode16(r, 7, 127, 255);
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Dequantization of one element (n, k).
+ */
+static int q4_nibble(const uint8_t* codes, int K, int n, int k) {
+    int b = k / 32, j = k % 32;
+    uint8_t byte = codes[(size_t)n * (K / 2) + 16 * b + (j % 16)];
+    return j < 16 ? (byte & 0xF) : (byte >> 4);
+}
+
+/* Exact real value of the weight (all three formats are exact in f64). */
+double orc_weight_exact(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                        int N, int K, int n, int k) {
+    (void)N;
+    size_t bi = (size_t)n * (K / 32) + k / 32;
+    if (fmt == ORC_Q8) {
+        int q = ((const int8_t*)codes)[(size_t)n * K + k];
+        return (double)q * (double)((const float*)scales)[bi];
+    }
+    int nib = q4_nibble((const uint8_t*)codes, K, n, k);
+    double v = (double)(nib - 8) * orc_f16_value(((const uint16_t*)scales)[bi]);
+    if (fmt == ORC_Q4A) v += orc_bf16_value(offs[(size_t)n * (K / group) + k / group]);
+    return v;
+}
+
+/* The f32 value the decoders compute (v32). */
+float orc_weight_f32(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                     int N, int K, int n, int k) {
+    (void)N;
+    size_t bi = (size_t)n * (K / 32) + k / 32;
+    if (fmt == ORC_Q8) {
+        int q = ((const int8_t*)codes)[(size_t)n * K + k];
+        float d = ((const float*)scales)[bi];
+        float v = (float)q * d;
+        return v;
+    }
+    int nib = q4_nibble((const uint8_t*)codes, K, n, k);
+    float d = (float)orc_f16_value(((const uint16_t*)scales)[bi]);
+    float v = (float)(nib - 8) * d;
+    if (fmt == ORC_Q4A) {
+        float m = (float)orc_bf16_value(offs[(size_t)n * (K / group) + k / group]);
+        v = v + m;
+    }
+    return v;
+}
+
+/* The tile a GEMM stages: out[r][c] for element (n0 + r, k0 + c), as f32 (exact mode) or as
+ * the f16 / bf16 bits of the nearest-even rounding of the f32 value (fast mode). */
+void orc_dequant_tile(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                      int N, int K, int n0, int k0, int rows, int cols, int staged, void* out) {
+    for (int r = 0; r < rows; r++)
+        for (int c = 0; c < cols; c++) {
+            float v = orc_weight_f32(fmt, codes, scales, offs, group, N, K, n0 + r, k0 + c);
+            size_t o = (size_t)r * cols + c;
+            if (staged == ORC_F32)
+                ((float*)out)[o] = v;
+            else if (staged == ORC_F16)
+                ((uint16_t*)out)[o] = orc_f32_to_f16(v);
+            else
+                ((uint16_t*)out)[o] = orc_f32_to_bf16(v);
+        }
+}
+
+/* Activation element as stored, widened exactly to f64. */
+double orc_x_value(const void* X, int xtype, size_t i) {
+    switch (xtype) {
+    case ORC_F32: return (double)((const float*)X)[i];
+    case ORC_F16: return orc_f16_value(((const uint16_t*)X)[i]);
+    case ORC_BF16: return orc_bf16_value(((const uint16_t*)X)[i]);
+    default: return ((const double*)X)[i];
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * GEMM: Y[t][n] = sum_k x[t][k] * v32[n][k] and S[t][n] = sum_k |x[t][k] * v32[n][k]|, in
+ * f64, k ascending.  Optional index lists select a sample of rows n (ns, nn) and tokens
+ * (ts, nt); outputs are [nt][nn].  Threads split the selected n.
+ */
+typedef struct {
+    int fmt; const void* codes; const void* scales; const uint16_t* offs; int group;
+    int N, K; const void* X; int xtype; const int* ns; int nn; const int* ts; int nt;
+    double* Y; double* S; int i0, i1;
+} gemm_job;
+
+static void* gemm_worker(void* arg) {
+    gemm_job* j = (gemm_job*)arg;
+    double* w = (double*)malloc(sizeof(double) * (size_t)j->K);
+    for (int i = j->i0; i < j->i1; i++) {
+        int n = j->ns ? j->ns[i] : i;
+        for (int k = 0; k < j->K; k++)
+            w[k] = (double)orc_weight_f32(j->fmt, j->codes, j->scales, j->offs, j->group, j->N, j->K, n, k);
+        for (int a = 0; a < j->nt; a++) {
+            int t = j->ts ? j->ts[a] : a;
+            double y = 0.0, s = 0.0;
+            for (int k = 0; k < j->K; k++) {
+                double p = orc_x_value(j->X, j->xtype, (size_t)t * j->K + k) * w[k];
+                y += p;
+                s += fabs(p);
+            }
+            j->Y[(size_t)a * j->nn + i] = y;
+            if (j->S) j->S[(size_t)a * j->nn + i] = s;
+        }
+    }
+    free(w);
+    return NULL;
+}
+
+int orc_gemm(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group, int N, int K,
+             const void* X, int xtype, int T, const int* ns, int nn, const int* ts, int nt,
+             double* Y, double* S, int nthreads) {
+    if (!ns) nn = N;
+    if (!ts) nt = T;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nn) nthreads = nn > 0 ? nn : 1;
+    gemm_job jobs[256];
+    pthread_t th[256];
+    if (nthreads > 256) nthreads = 256;
+    for (int i = 0; i < nthreads; i++) {
+        gemm_job j = {fmt, codes, scales, offs, group, N, K, X, xtype, ns, nn, ts, nt, Y, S,
+                      (int)((long)nn * i / nthreads), (int)((long)nn * (i + 1) / nthreads)};
+        jobs[i] = j;
+    }
+    for (int i = 1; i < nthreads; i++) pthread_create(&th[i], NULL, gemm_worker, &jobs[i]);
+    gemm_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; i++) pthread_join(th[i], NULL);
+    return nthreads;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Per-row power-of-two scaling to f16.  Row r of the output is source row src[r] (or r).
+ * xh gets the f16 bits of x * 2^e (product in f32, then nearest-even), rs the inverse 2^-e.
+ */
+void orc_x_half(const float* X, int K, const int* src, int R, uint16_t* xh, float* rs) {
+    for (int r = 0; r < R; r++) {
+        const float* row = X + (size_t)(src ? src[r] : r) * K;
+        float amax = 0.0f;
+        for (int k = 0; k < K; k++) {
+            float a = fabsf(row[k]);
+            if (a > amax) amax = a;
+        }
+        int e = 0;
+        if (amax > 0.0f && isfinite(amax)) {
+            int fe;
+            frexpf(amax, &fe);
+            e = 14 - fe;
+            if (e < -100) e = -100;
+            if (e > 100) e = 100;
+        }
+        float s = ldexpf(1.0f, e);
+        for (int k = 0; k < K; k++) {
+            float v = row[k] * s;
+            xh[(size_t)r * K + k] = orc_f32_to_f16(v);
+        }
+        rs[r] = ldexpf(1.0f, -e);
+    }
+}
+
+/* a = SiLU(g) * u = g / (1 + exp(-g)) * u, f64, elementwise. */
+void orc_swiglu(const double* G, const double* U, size_t n, double* A) {
+    for (size_t i = 0; i < n; i++) A[i] = G[i] / (1.0 + exp(-G[i])) * U[i];
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Routing plan for T rows of E router logits, k experts per row.
+ * Top-k: logits sorted descending, equal logits in ascending expert index; the first k.
+ * Weights: exp(l_j - l_max) / sum over the kept of exp(l_i - l_max)  (= p_j / sum kept p).
+ * Segments: experts ascending; seg_off[e] .. seg_off[e+1] are expert e's gathered rows,
+ * holding its tokens in ascending order.  row_src[r] = token of gathered row r.
+ * slot_row[t*k + j] = gathered row of token t's j-th expert (j in top-k order),
+ * slot_w[t*k + j] its weight.  Returns R = T*k.
+ */
+static const float* sort_row;
+static int cmp_desc(const void* a, const void* b) {
+    int x = *(const int*)a, y = *(const int*)b;
+    if (sort_row[x] > sort_row[y]) return -1;
+    if (sort_row[x] < sort_row[y]) return 1;
+    return x < y ? -1 : (x > y);
+}
+
+int orc_moe_plan(const float* logits, int T, int E, int k, int* seg_off, int* row_src, int* slot_row,
+                 double* slot_w, int* slot_expert) {
+    int* idx = (int*)malloc(sizeof(int) * (size_t)E);
+    int* topk = (int*)malloc(sizeof(int) * (size_t)T * k);
+    for (int t = 0; t < T; t++) {
+        const float* row = logits + (size_t)t * E;
+        for (int e = 0; e < E; e++) idx[e] = e;
+        sort_row = row;
+        qsort(idx, (size_t)E, sizeof(int), cmp_desc);
+        double lmax = (double)row[idx[0]], sum = 0.0;
+        for (int j = 0; j < k; j++) sum += exp((double)row[idx[j]] - lmax);
+        for (int j = 0; j < k; j++) {
+            topk[t * k + j] = idx[j];
+            slot_w[t * k + j] = exp((double)row[idx[j]] - lmax) / sum;
+            if (slot_expert) slot_expert[t * k + j] = idx[j];
+        }
+    }
+    for (int e = 0; e <= E; e++) seg_off[e] = 0;
+    for (int i = 0; i < T * k; i++) seg_off[topk[i] + 1]++;
+    for (int e = 0; e < E; e++) seg_off[e + 1] += seg_off[e];
+    int* fill = (int*)malloc(sizeof(int) * (size_t)E);
+    for (int e = 0; e < E; e++) fill[e] = seg_off[e];
+    for (int t = 0; t < T; t++)
+        for (int j = 0; j < k; j++) {
+            int e = topk[t * k + j];
+            int r = fill[e]++;
+            row_src[r] = t;
+            slot_row[t * k + j] = r;
+        }
+    free(fill);
+    free(topk);
+    free(idx);
+    return T * k;
+}
+
+/* y[t][c] = sum_j slot_w[t*k+j] * O[slot_row[t*k+j]][c] (f64, j ascending);
+ * b[t][c] = sum_j |slot_w * O| (the tolerance denominator). */
+void orc_moe_combine(const double* O, int H, const int* slot_row, const double* slot_w, int T, int k,
+                     double* y, double* b) {
+    for (int t = 0; t < T; t++)
+        for (int c = 0; c < H; c++) {
+            double acc = 0.0, s = 0.0;
+            for (int j = 0; j < k; j++) {
+                double p = slot_w[t * k + j] * O[(size_t)slot_row[t * k + j] * H + c];
+                acc += p;
+                s += fabs(p);
+            }
+            y[(size_t)t * H + c] = acc;
+            if (b) b[(size_t)t * H + c] = s;
+        }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Array forms of the conversions (used by the tests to sweep whole encodings). */
+void orc_f16_values(const uint16_t* h, size_t n, double* out) {
+    for (size_t i = 0; i < n; i++) out[i] = orc_f16_value(h[i]);
+}
+void orc_bf16_values(const uint16_t* h, size_t n, double* out) {
+    for (size_t i = 0; i < n; i++) out[i] = orc_bf16_value(h[i]);
+}
+void orc_f32_to_f16_array(const float* x, size_t n, uint16_t* out) {
+    for (size_t i = 0; i < n; i++) out[i] = orc_f32_to_f16(x[i]);
+}
+void orc_f32_to_bf16_array(const float* x, size_t n, uint16_t* out) {
+    for (size_t i = 0; i < n; i++) out[i] = orc_f32_to_bf16(x[i]);
+}
+/* Whole dequantized matrix, exact (f64) or as the f32 decode. */
+void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                       int N, int K, double* out) {
+    for (int n = 0; n < N; n++)
+        for (int k = 0; k < K; k++)
+            out[(size_t)n * K + k] = orc_weight_exact(fmt, codes, scales, offs, group, N, K, n, k);
+}

@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle to facts fixed outside it: hand-worked decoder values, IEEE encodings,
+library rounding routines, closed forms, exact rational brute force and routing by full sort.
+
+Each test is chosen so that a plausible mistake in the oracle (swapped nibble halves, a dropped
+offset, a wrong block or group index, a transposed operand, a wrong tie rule) fails it."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _h(s):
+    return int(s, 16)
+
+
+# ---- 16-bit float encodings ----------------------------------------------------------------------
+
+def test_f16_known_and_all_patterns(orc):
+    g = json.load(open(os.path.join(GOLD, "q4a_q8_blocks.json")))
+    for bits, val in g["f16_known"]["pairs"]:
+        assert orc.f16_values(np.array([_h(bits)], np.uint16))[0] == val
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = orc.f16_values(allb)
+    ref = allb.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def test_bf16_known_and_all_patterns(orc):
+    g = json.load(open(os.path.join(GOLD, "q4a_q8_blocks.json")))
+    for bits, val in g["bf16_known"]["pairs"]:
+        assert orc.bf16_values(np.array([_h(bits)], np.uint16))[0] == val
+    allb = np.arange(65536, dtype=np.int32).astype(np.int16)
+    ref = torch.from_numpy(allb).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = orc.bf16_values(allb.view(np.uint16))
+    fin = np.isfinite(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+
+
+def _f32_sample(rng, n):
+    """Random f32 patterns over all exponents, plus exact halfway points of the f16 and bf16
+    grids (ties), the f16 overflow boundary and the subnormal ranges."""
+    bits = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    # f16 ties: odd multiples of 2^(e-11) for exponents across the f16 range
+    m = rng.integers(0, 2048, 20000)
+    e = rng.integers(-25, 16, 20000)
+    ties16 = ((2 * m + 1) * np.ldexp(1.0, e - 11)).astype(np.float32)
+    # bf16 ties: bit 15 set, bits 0..14 clear
+    tb = (rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    tiesb = tb.view(np.float32)
+    tiesb = tiesb[np.isfinite(tiesb)]
+    edge = np.array([65504, 65519.99, 65520, 65535, 65536, 1e-8, 2.0**-24, 2.0**-25, 3 * 2.0**-26, 2.0**-14,
+                     -0.0, 0.0, 1.0, -1.0, 3.4e38, 1e-45, 2.0**-133, 2.0**-134, 3 * 2.0**-135], np.float32)
+    return np.concatenate([x, ties16, -ties16, tiesb, edge]).astype(np.float32)
+
+
+def test_f32_to_f16_matches_numpy(orc):
+    rng = np.random.default_rng(5)
+    x = _f32_sample(rng, 1 << 20)
+    ours = orc.f32_to_f16(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_f32_to_bf16_matches_torch(orc):
+    rng = np.random.default_rng(6)
+    x = _f32_sample(rng, 1 << 20)
+    ours = orc.f32_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ---- decoders against hand-worked blocks -----------------------------------------------------------
+
+def test_q4_hand_packed_blocks(orc):
+    g = json.load(open(os.path.join(GOLD, "q4_blocks.json")))
+    for c in g["cases"]:
+        codes = np.frombuffer(bytes.fromhex(c["bytes_hex"]), np.uint8)
+        scales = np.array([_h(c["scale_f16_bits"])], np.uint16)
+        got = [orc.weight_exact("q4", codes, scales, None, 64, 1, 32, 0, k) for k in range(32)]
+        if c.get("expected") is not None:
+            exp = [float(v) for v in c["expected"]]
+        else:
+            exp = [f * c["scale_value"] for f in c["expected_factor"]]
+        assert got == exp, c["name"]
+        v32 = orc.dequant_tile("q4", codes, scales, None, 64, 1, 32, 0, 0, 1, 32, "f32")[0]
+        assert [float(v) for v in v32] == exp, c["name"]
+
+
+def test_q4_block_and_row_addressing(orc):
+    """Two rows of two blocks with distinct scales: element (n, k) must use block k // 32 of row n."""
+    ramp = bytes.fromhex("f0e1d2c3b4a5968778695a4b3c2d1e0f")
+    zero = bytes(16)
+    codes = np.frombuffer(ramp + zero + zero + ramp, np.uint8)    # row 0: [ramp, zero], row 1: [zero, ramp]
+    scales = np.array([0x3C00, 0x4000, 0x4200, 0x4400], np.uint16)  # 1, 2, 3, 4
+    fac = list(range(-8, 8)) + list(range(7, -9, -1))
+    W = orc.dequant_exact("q4", codes, scales, None, 64, 2, 64)
+    assert list(W[0, :32]) == [1.0 * f for f in fac]
+    assert list(W[0, 32:]) == [-16.0] * 32
+    assert list(W[1, :32]) == [-24.0] * 32
+    assert list(W[1, 32:]) == [4.0 * f for f in fac]
+
+
+def test_q4a_hand_packed(orc):
+    g = json.load(open(os.path.join(GOLD, "q4a_q8_blocks.json")))
+    for c in g["q4a_cases"]:
+        K, group = c["K"], c["group"]
+        codes = np.frombuffer(b"".join(bytes.fromhex(h) for h in c["bytes_hex_per_block"]), np.uint8)
+        scales = np.array([_h(s) for s in c["scales_f16_bits"]], np.uint16)
+        offs = np.array([_h(s) for s in c["offsets_bf16_bits"]], np.uint16)
+        W = orc.dequant_exact("q4a", codes, scales, offs, group, 1, K)[0]
+        if "expected_group_values" in c:
+            for gi, v in enumerate(c["expected_group_values"]):
+                assert list(W[gi * group:(gi + 1) * group]) == [v] * group, c["name"]
+        else:
+            for b, v in enumerate(c["expected_block_values"]):
+                assert list(W[b * 32:(b + 1) * 32]) == [v] * 32, c["name"]
+        v32 = orc.dequant_tile("q4a", codes, scales, offs, group, 1, K, 0, 0, 1, K, "f32")[0]
+        assert np.array_equal(v32.astype(np.float64), W)
+
+
+def test_q8_hand_codes(orc):
+    g = json.load(open(os.path.join(GOLD, "q4a_q8_blocks.json")))
+    for c in g["q8_cases"]:
+        codes = np.array(c["codes"], np.int8)
+        scales = np.array([c["scale"]], np.float32)
+        W = orc.dequant_exact("q8", codes, scales, None, 64, 1, 32)[0]
+        assert list(W) == c["expected"]
+    # block indexing: K = 64, second block has its own scale
+    codes = np.full(64, 3, np.int8)
+    scales = np.array([0.5, -0.25], np.float32)
+    W = orc.dequant_exact("q8", codes, scales, None, 64, 1, 64)[0]
+    assert list(W) == [1.5] * 32 + [-0.75] * 32
+
+
+def test_staged_f32_rounding_q8_q4a(orc):
+    """The f32 decode rounds once: q * d (Q8) and (nib-8) * d + m (Q4A), nearest-even in f32."""
+    rng = np.random.default_rng(11)
+    N, K = 3, 64
+    codes8 = rng.integers(-127, 128, N * K).astype(np.int8)
+    sc8 = rng.uniform(0.002, 0.01, N * K // 32).astype(np.float32)
+    v = orc.dequant_tile("q8", codes8, sc8, None, 64, N, K, 0, 0, N, K, "f32")
+    ref = codes8.reshape(N, K).astype(np.float32) * np.repeat(sc8.reshape(N, K // 32), 32, axis=1)
+    assert np.array_equal(v, ref)
+    codes4 = rng.integers(0, 256, N * K // 2).astype(np.uint8)
+    sc4 = rng.uniform(0.01, 0.05, N * K // 32).astype(np.float16).view(np.uint16)
+    off = torch.from_numpy(rng.normal(0, 0.02, N * K // 64).astype(np.float32)).to(torch.bfloat16)
+    offb = off.view(torch.int16).numpy().view(np.uint16)
+    v = orc.dequant_tile("q4a", codes4, sc4, offb, 64, N, K, 0, 0, N, K, "f32")
+    nib = np.empty((N, K), np.int32)
+    cb = codes4.reshape(N, K // 32, 16)
+    nib[:, :] = np.concatenate([cb & 15, cb >> 4], axis=2).reshape(N, K)
+    d = np.repeat(sc4.view(np.float16).astype(np.float32).reshape(N, K // 32), 32, axis=1)
+    m = np.repeat(off.to(torch.float32).numpy().reshape(N, K // 64), 64, axis=1)
+    prod = (nib - 8).astype(np.float32) * d
+    assert np.array_equal(v, prod + m)
+    # and the fast-mode tiles are nearest-even narrowings of exactly these f32 values
+    t16 = orc.dequant_tile("q4a", codes4, sc4, offb, 64, N, K, 0, 0, N, K, "f16")
+    assert np.array_equal(t16, (prod + m).astype(np.float16).view(np.uint16))
+    tb = orc.dequant_tile("q4a", codes4, sc4, offb, 64, N, K, 0, 0, N, K, "bf16")
+    refb = torch.from_numpy(prod + m).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(tb, refb)
+
+
+# ---- GEMM ------------------------------------------------------------------------------------------
+
+def _frac_f16(bits):
+    s = -1 if bits >> 15 else 1
+    e = (bits >> 10) & 31
+    f = bits & 1023
+    if e == 0:
+        return s * Fraction(f, 1 << 24)
+    return s * Fraction(f + 1024, 1 << 10) * (Fraction(2) ** (e - 15))
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+def test_gemm_brute_force_rationals(orc, fmt):
+    """Tiny shapes: Y from the raw bytes in exact rationals (Q4 values are exact; Q8 values are
+    the f32 products, rounded by numpy's IEEE f32 multiply); the oracle's f64 sums must agree to
+    f64 rounding (K terms: |err| <= K * 2^-52 * S)."""
+    rng = np.random.default_rng(3)
+    for (N, K, T) in [(3, 32, 2), (4, 64, 3), (1, 64, 1)]:
+        if fmt == "q4":
+            codes = rng.integers(0, 256, N * K // 2).astype(np.uint8)
+            scales = rng.uniform(0.01, 0.05, N * K // 32).astype(np.float16).view(np.uint16)
+        else:
+            codes = rng.integers(-127, 128, N * K).astype(np.int8)
+            scales = rng.uniform(0.002, 0.01, N * K // 32).astype(np.float32)
+        X = rng.normal(0, 1, T * K).astype(np.float32)
+        Y, S, _ = orc.gemm(fmt, codes, scales, None, 64, N, K, X, "f32", T, threads=1)
+        for t in range(T):
+            for n in range(N):
+                acc = Fraction(0)
+                for k in range(K):
+                    b = k // 32
+                    if fmt == "q4":
+                        byte = int(codes[n * K // 2 + 16 * b + (k % 32) % 16])
+                        nib = byte & 15 if (k % 32) < 16 else byte >> 4
+                        w = (nib - 8) * _frac_f16(int(scales[n * K // 32 + b]))
+                    else:
+                        # the decoder evaluates q * d in f32 (one nearest-even rounding)
+                        w = Fraction(float(np.float32(int(codes[n * K + k])) * np.float32(scales[n * K // 32 + b])))
+                    acc += Fraction(float(X[t * K + k])) * w
+                assert abs(Fraction(Y[t, n]) - acc) <= Fraction(K) * Fraction(2) ** -52 * Fraction(S[t, n])
+
+
+def test_gemm_identity_and_one_hot(orc):
+    K = N = 64
+    # identity: nibble 9 on the diagonal, 8 elsewhere, scale 1.0 -> W = I, so Y = X exactly
+    nib = np.full((N, K), 8, np.uint8)
+    np.fill_diagonal(nib, 9)
+    codes = np.empty((N, K // 32, 16), np.uint8)
+    nb = nib.reshape(N, K // 32, 32)
+    codes[:] = nb[:, :, :16] | (nb[:, :, 16:] << 4)
+    scales = np.full(N * K // 32, 0x3C00, np.uint16)
+    X = np.random.default_rng(1).normal(0, 1, (5, K)).astype(np.float32)
+    Y, S, _ = orc.gemm("q4", codes.reshape(-1), scales, None, 64, N, K, X, "f32", 5)
+    assert np.array_equal(Y, X.astype(np.float64))
+    assert np.array_equal(S, np.abs(X.astype(np.float64)))
+    # one-hot: a single nonzero weight at (n*, k*) = (17, 40): nibble 15, scale 0.25 -> 1.75
+    nib = np.full((N, K), 8, np.uint8)
+    nib[17, 40] = 15
+    nb = nib.reshape(N, K // 32, 32)
+    codes[:] = nb[:, :, :16] | (nb[:, :, 16:] << 4)
+    scales = np.full(N * K // 32, 0x3400, np.uint16)
+    Y, _, _ = orc.gemm("q4", codes.reshape(-1), scales, None, 64, N, K, X, "f32", 5)
+    exp = np.zeros((5, N))
+    exp[:, 17] = X[:, 40].astype(np.float64) * 1.75
+    assert np.array_equal(Y, exp)
+
+
+def test_gemm_orientation_one_hot_tokens(orc):
+    """x[t][k] = [k == t] makes Y[t][n] = w[n][t]: pins Y = X W^T, not its transpose."""
+    rng = np.random.default_rng(8)
+    N, K, T = 6, 64, 5
+    codes = rng.integers(0, 256, N * K // 2).astype(np.uint8)
+    scales = rng.uniform(0.01, 0.05, N * K // 32).astype(np.float16).view(np.uint16)
+    W = orc.dequant_exact("q4", codes, scales, None, 64, N, K)
+    X = np.zeros((T, K), np.float32)
+    for t in range(T):
+        X[t, t] = 1.0
+    Y, _, _ = orc.gemm("q4", codes, scales, None, 64, N, K, X, "f32", T)
+    assert np.array_equal(Y, W[:, :T].T)
+
+
+def test_gemm_closed_form_constant_blocks(orc):
+    """Every nibble of block b of row n equal to c[n][b] and x = 1: Y[n] = 32 sum_b (c-8) d + 64 sum_g m."""
+    rng = np.random.default_rng(4)
+    N, K = 5, 256
+    c = rng.integers(0, 16, (N, K // 32))
+    codes = np.repeat((c | (c << 4)).astype(np.uint8), 16, axis=1).reshape(-1)
+    scales = rng.uniform(0.01, 0.05, N * K // 32).astype(np.float16).view(np.uint16)
+    offs = torch.from_numpy(rng.normal(0, 0.02, N * K // 64).astype(np.float32)).to(torch.bfloat16)
+    offb = offs.view(torch.int16).numpy().view(np.uint16)
+    X = np.ones((1, K), np.float32)
+    d = scales.view(np.float16).astype(np.float64).reshape(N, K // 32)
+    m = offs.to(torch.float64).numpy().reshape(N, K // 64)
+    Y, _, _ = orc.gemm("q4", codes, scales, None, 64, N, K, X, "f32", 1)
+    assert np.allclose(Y[0], 32 * ((c - 8) * d).sum(1), rtol=1e-14, atol=0)
+    Y, _, _ = orc.gemm("q4a", codes, scales, offb, 64, N, K, X, "f32", 1)
+    # each element rounds to f32 once; compare within that rounding
+    exact = 32 * ((c - 8) * d).sum(1) + 64 * m.sum(1)
+    assert np.allclose(Y[0], exact, rtol=0, atol=K * 2.0**-24 * 0.5)
+
+
+def test_gemm_x_storage_types(orc):
+    """f16 and bf16 activations are widened exactly; the result equals the f32-typed call."""
+    rng = np.random.default_rng(9)
+    N, K, T = 4, 64, 3
+    codes = rng.integers(0, 256, N * K // 2).astype(np.uint8)
+    scales = rng.uniform(0.01, 0.05, N * K // 32).astype(np.float16).view(np.uint16)
+    x16 = rng.normal(0, 1, T * K).astype(np.float16)
+    Ya, _, _ = orc.gemm("q4", codes, scales, None, 64, N, K, x16.view(np.uint16), "f16", T)
+    Yb, _, _ = orc.gemm("q4", codes, scales, None, 64, N, K, x16.astype(np.float32), "f32", T)
+    assert np.array_equal(Ya, Yb)
+    xb = torch.from_numpy(rng.normal(0, 1, T * K).astype(np.float32)).to(torch.bfloat16)
+    Ya, _, _ = orc.gemm("q4", codes, scales, None, 64, N, K, xb.view(torch.int16).numpy().view(np.uint16), "bf16", T)
+    Yb, _, _ = orc.gemm("q4", codes, scales, None, 64, N, K, xb.to(torch.float32).numpy(), "f32", T)
+    assert np.array_equal(Ya, Yb)
+
+
+def test_gemm_sampled_matches_full(orc):
+    rng = np.random.default_rng(10)
+    N, K, T = 40, 128, 7
+    codes = rng.integers(-127, 128, N * K).astype(np.int8)
+    scales = rng.uniform(0.002, 0.01, N * K // 32).astype(np.float32)
+    X = rng.normal(0, 1, T * K).astype(np.float32)
+    Yf, Sf, _ = orc.gemm("q8", codes, scales, None, 64, N, K, X, "f32", T, threads=3)
+    ns, ts = np.array([39, 0, 17]), np.array([6, 2])
+    Ys, Ss, _ = orc.gemm("q8", codes, scales, None, 64, N, K, X, "f32", T, ns=ns, ts=ts)
+    assert np.array_equal(Ys, Yf[np.ix_(ts, ns)])
+    assert np.array_equal(Ss, Sf[np.ix_(ts, ns)])
+
+
+# ---- row scaling to f16 -------------------------------------------------------------------------------
+
+def test_x_half_closed_forms(orc):
+    K = 8
+    X = np.array([
+        [1.0, -0.5, 0.25, 0, 0, 0, 0, 0],          # amax 1 = 0.5 * 2^1 -> scale 2^13
+        [3.0, 1.0, 0, 0, 0, 0, 0, 0],              # amax 3 = 0.75 * 2^2 -> scale 2^12
+        [0, 0, 0, 0, 0, 0, 0, 0],                  # zero row -> scale 1
+        [2.0**-120, 0, 0, 0, 0, 0, 0, 0],          # frexp exponent -119 -> 14 + 119 clamped to 100
+        [np.inf, 1.0, 0, 0, 0, 0, 0, 0],           # non-finite amax -> scale 1
+    ], np.float32)
+    xh, rs = orc.x_half(X, K)
+    assert list(rs) == [2.0**-13, 2.0**-12, 1.0, 2.0**-100, 1.0]
+    v = xh.view(np.float16).astype(np.float64)
+    assert list(v[0, :3]) == [8192.0, -4096.0, 2048.0]
+    assert list(v[1, :2]) == [12288.0, 4096.0]
+    assert not v[2].any()
+    assert v[3, 0] == 2.0**-20
+    assert v[4, 0] == np.inf and v[4, 1] == 1.0
+    # gather: row r is source row src[r]
+    xh2, rs2 = orc.x_half(X, K, src=np.array([1, 0, 1]))
+    assert np.array_equal(xh2[0], xh[1]) and np.array_equal(xh2[1], xh[0]) and list(rs2) == [2.0**-12, 2.0**-13, 2.0**-12]
+
+
+def test_x_half_range_random(orc):
+    rng = np.random.default_rng(12)
+    X = (rng.normal(0, 1, (50, 96)) * np.logspace(-6, 6, 50)[:, None]).astype(np.float32)
+    xh, rs = orc.x_half(X, 96)
+    v = xh.view(np.float16).astype(np.float64)
+    amax = np.abs(v).max(1)
+    assert np.all(amax >= 2.0**13) and np.all(amax < 2.0**14 + 1)
+    assert np.all(np.log2(rs) == np.round(np.log2(rs)))
+    back = v * rs[:, None]
+    assert np.all(np.abs(back - X) <= 2.0**-11 * np.abs(X) + 1e-300)
+
+
+def test_swiglu_closed_forms(orc):
+    g = np.array([0.0, math.log(3.0), -50.0, 2.0])
+    u = np.array([5.0, 2.0, 3.0, 1.0])
+    a = orc.swiglu(g, u)
+    assert a[0] == 0.0
+    assert abs(a[1] - 0.75 * math.log(3.0) * 2.0) < 1e-15
+    assert abs(a[2]) < 1e-19
+    assert abs(a[3] - 2.0 / (1.0 + math.exp(-2.0))) < 1e-15
+
+
+# ---- routing plan and combine --------------------------------------------------------------------------
+
+def test_moe_plan_brute_force(orc):
+    rng = np.random.default_rng(13)
+    T, E, k = 32, 128, 8
+    lg = rng.normal(0, 1, (T, E)).astype(np.float32)
+    lg[3, 10] = lg[3, 20] = lg[3, 30] = 9.0      # a three-way tie at the top
+    lg[4, :] = 0.5                               # all equal: experts 0..7 in order
+    p = orc.moe_plan(lg, T, E, k)
+    assert p["R"] == T * k
+    seg, src, srow, sw, se = p["seg_off"], p["row_src"], p["slot_row"], p["slot_w"], p["slot_expert"]
+    assert seg[0] == 0 and seg[-1] == T * k and np.all(np.diff(seg) >= 0)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))[:k]
+        assert list(se[t * k:(t + 1) * k]) == order
+        ex = np.exp(lg[t, order].astype(np.float64) - float(lg[t, order[0]]))
+        assert np.allclose(sw[t * k:(t + 1) * k], ex / ex.sum(), rtol=1e-15, atol=0)
+        assert abs(sw[t * k:(t + 1) * k].sum() - 1.0) < 1e-15
+        for j, e in enumerate(order):
+            r = srow[t * k + j]
+            assert seg[e] <= r < seg[e + 1] and src[r] == t
+    assert list(se[3 * k:3 * k + 3]) == [10, 20, 30]
+    assert list(se[4 * k:5 * k]) == list(range(8))
+    assert np.allclose(sw[4 * k:5 * k], 1.0 / 8, rtol=0, atol=1e-16)
+    for e in range(E):
+        rows = src[seg[e]:seg[e + 1]]
+        assert np.all(np.diff(rows) > 0)                 # ascending tokens within a segment
+        assert len(rows) == sum(e in se[t * k:(t + 1) * k] for t in range(T))
+
+
+def test_moe_combine_closed_forms(orc):
+    O = np.arange(12, dtype=np.float64).reshape(3, 4)
+    y, b = orc.moe_combine(O, 4, np.array([2]), np.array([1.0]), 1, 1)
+    assert np.array_equal(y[0], O[2])
+    y, b = orc.moe_combine(O, 4, np.array([0, 1, 1, 2]), np.array([0.7, 0.3, 0.25, -0.5]), 2, 2)
+    assert np.allclose(y[0], 0.7 * O[0] + 0.3 * O[1], rtol=1e-15)
+    assert np.allclose(y[1], 0.25 * O[1] - 0.5 * O[2], rtol=1e-15)
+    assert np.allclose(b[1], 0.25 * O[1] + 0.5 * O[2], rtol=1e-15)
