@@ -1,0 +1,256 @@
+"""Python binding of libqgemm.so, the block-quantized weight matmul for MI355X (gfx950).
+
+The functions below carry the names of the C entry points declared in include/qgemm.h and only
+marshal arguments: torch tensors become device pointers, dtypes become the activation-type enum,
+the current torch stream is passed as the hipStream_t, and a non-zero status raises QGError.
+Every step of the computation runs in the library's HIP kernels.  There is no fallback: if the
+library is not built, loading raises.
+
+Host-side helpers for the packed layout (pack_q4 / pack_q4_blocks, expert tables) live here too;
+they only move bytes.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+QG_OK, QG_EINVAL, QG_EALIGN, QG_ESHAPE, QG_EUNSUPPORTED, QG_ELAUNCH, QG_EPLAN, QG_EWORKSPACE = range(8)
+QG_X_F32, QG_X_F16, QG_X_BF16 = 0, 1, 2
+QG_EXACT, QG_FAST = 0, 1
+QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8 = 0, 1, 2
+
+FMT = {"q4": QG_FMT_Q4, "q4a": QG_FMT_Q4A, "q8": QG_FMT_Q8}
+MODE = {"exact": QG_EXACT, "fast": QG_FAST}
+
+# exported symbols of include/qgemm.h, in declaration order
+SYMBOLS = [
+    "qg_strerror", "qg_abi_version",
+    "qgemm_q4", "qgemm_q4a", "qgemm_q8",
+    "qgemv_q4", "qgemv_q4a", "qgemv_q8",
+    "qg_dequant_dump",
+    "qg_moe_plan_host", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
+    "qg_moe_ffn_workspace", "qg_moe_ffn",
+]
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+_lib = None
+_p, _i, _sz = C.c_void_p, C.c_int, C.c_size_t
+
+
+def lib() -> C.CDLL:
+    """The loaded libqgemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                              f"g.build()'` (or block_quantized_weight_affine_amd/build.py)")
+        L = C.CDLL(LIB_PATH)
+        L.qg_strerror.restype = C.c_char_p
+        L.qg_strerror.argtypes = [_i]
+        L.qg_abi_version.restype = _i
+        L.qg_abi_version.argtypes = []
+        sig_dense = [_p, _p, _p, _i, _p, _i, _i, _i, _i, _p]
+        L.qgemm_q4.argtypes = sig_dense
+        L.qgemm_q8.argtypes = sig_dense
+        L.qgemm_q4a.argtypes = [_p, _p, _p, _i, _p, _i, _p, _i, _i, _i, _i, _p]
+        sig_gemv = [_p, _p, _p, _i, _p, _i, _i, _i, _p]
+        L.qgemv_q4.argtypes = sig_gemv
+        L.qgemv_q8.argtypes = sig_gemv
+        L.qgemv_q4a.argtypes = [_p, _p, _p, _i, _p, _i, _p, _i, _i, _i, _p]
+        L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
+        L.qg_moe_plan_host.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
+        L.qg_x_half.argtypes = [_p, _i, _p, _i, _i, _p, _p, _p]
+        L.qgemm_moe_grouped.argtypes = [_i, _p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]
+        L.qg_swiglu.argtypes = [_p, _i, _i, _p, _i, _p, _p]
+        L.qg_moe_combine.argtypes = [_p, _i, _p, _p, _p, _i, _i, _i, _i, _p]
+        L.qg_moe_ffn_workspace.restype = _sz
+        L.qg_moe_ffn_workspace.argtypes = [_i, _i, _i, _i, _i]
+        L.qg_moe_ffn.argtypes = [_i, _p, _p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _i, _i, _p, _sz, _p]
+        for name in SYMBOLS:
+            if name not in ("qg_strerror", "qg_abi_version", "qg_moe_ffn_workspace"):
+                getattr(L, name).restype = _i
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().qg_strerror(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().qg_abi_version()
+
+
+# ---- marshalling helpers ------------------------------------------------------------------------
+def _ptr(t):
+    """Device (or host) address of a torch tensor / numpy array / int; None for None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _xt(t) -> int:
+    import torch
+    return {torch.float32: QG_X_F32, torch.float16: QG_X_F16, torch.bfloat16: QG_X_BF16}[t.dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != QG_OK:
+        raise QGError(status, where)
+
+
+def _mode(mode):
+    return MODE[mode] if isinstance(mode, str) else int(mode)
+
+
+# ---- dense matmuls ------------------------------------------------------------------------------
+def qgemm_q4(codes, scales, X, Y, N, K, T, mode="exact", xt=None, stream=None):
+    _check(lib().qgemm_q4(_ptr(codes), _ptr(scales), _ptr(X), _xt(X) if xt is None else xt, _ptr(Y), N, K, T,
+                          _mode(mode), _stream(stream)), "qgemm_q4")
+
+
+def qgemm_q4a(codes, scales, offsets, group, X, Y, N, K, T, mode="exact", xt=None, stream=None):
+    _check(lib().qgemm_q4a(_ptr(codes), _ptr(scales), _ptr(offsets), group, _ptr(X), _xt(X) if xt is None else xt,
+                           _ptr(Y), N, K, T, _mode(mode), _stream(stream)), "qgemm_q4a")
+
+
+def qgemm_q8(codes, scales, X, Y, N, K, T, mode="exact", xt=None, stream=None):
+    _check(lib().qgemm_q8(_ptr(codes), _ptr(scales), _ptr(X), _xt(X) if xt is None else xt, _ptr(Y), N, K, T,
+                          _mode(mode), _stream(stream)), "qgemm_q8")
+
+
+def qgemv_q4(codes, scales, X, Y, N, K, T, xt=None, stream=None):
+    _check(lib().qgemv_q4(_ptr(codes), _ptr(scales), _ptr(X), _xt(X) if xt is None else xt, _ptr(Y), N, K, T,
+                          _stream(stream)), "qgemv_q4")
+
+
+def qgemv_q4a(codes, scales, offsets, group, X, Y, N, K, T, xt=None, stream=None):
+    _check(lib().qgemv_q4a(_ptr(codes), _ptr(scales), _ptr(offsets), group, _ptr(X), _xt(X) if xt is None else xt,
+                           _ptr(Y), N, K, T, _stream(stream)), "qgemv_q4a")
+
+
+def qgemv_q8(codes, scales, X, Y, N, K, T, xt=None, stream=None):
+    _check(lib().qgemv_q8(_ptr(codes), _ptr(scales), _ptr(X), _xt(X) if xt is None else xt, _ptr(Y), N, K, T,
+                          _stream(stream)), "qgemv_q8")
+
+
+def qgemm(fmt, codes, scales, offsets, group, X, Y, N, K, T, mode="exact", stream=None):
+    """Dispatch by format name: 'q4' | 'q4a' | 'q8'."""
+    if fmt == "q4":
+        return qgemm_q4(codes, scales, X, Y, N, K, T, mode, stream=stream)
+    if fmt == "q4a":
+        return qgemm_q4a(codes, scales, offsets, group, X, Y, N, K, T, mode, stream=stream)
+    return qgemm_q8(codes, scales, X, Y, N, K, T, mode, stream=stream)
+
+
+def qgemv(fmt, codes, scales, offsets, group, X, Y, N, K, T, stream=None):
+    if fmt == "q4":
+        return qgemv_q4(codes, scales, X, Y, N, K, T, stream=stream)
+    if fmt == "q4a":
+        return qgemv_q4a(codes, scales, offsets, group, X, Y, N, K, T, stream=stream)
+    return qgemv_q8(codes, scales, X, Y, N, K, T, stream=stream)
+
+
+def qg_dequant_dump(fmt, codes, scales, offsets, group, N, K, n0, k0, rows, cols, staged, out, stream=None):
+    _check(lib().qg_dequant_dump(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(codes), _ptr(scales),
+                                 _ptr(offsets), group, N, K, n0, k0, rows, cols, staged, _ptr(out),
+                                 _stream(stream)), "qg_dequant_dump")
+
+
+# ---- MoE ----------------------------------------------------------------------------------------
+def qg_moe_plan_host(logits: np.ndarray, T: int, E: int, k: int) -> dict:
+    """Routing plan on the host (numpy in, numpy out)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    seg_off = np.empty(E + 1, np.int32)
+    row_src = np.empty(T * k, np.int32)
+    slot_row = np.empty(T * k, np.int32)
+    slot_w = np.empty(T * k, np.float32)
+    slot_e = np.empty(T * k, np.int32)
+    _check(lib().qg_moe_plan_host(_ptr(lg), T, E, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w),
+                                  _ptr(slot_e)), "qg_moe_plan_host")
+    return {"seg_off": seg_off, "row_src": row_src, "slot_row": slot_row, "slot_w": slot_w, "slot_expert": slot_e}
+
+
+def qg_x_half(X, x_rows, row_src, R, K, Xh, rs, stream=None):
+    _check(lib().qg_x_half(_ptr(X), x_rows, _ptr(row_src), R, K, _ptr(Xh), _ptr(rs), _stream(stream)), "qg_x_half")
+
+
+def qgemm_moe_grouped(fmt, experts, group, seg_off, row_src, x_rows, X, rs, Y, N, K, R, E, mode="exact", xt=None,
+                      stream=None):
+    _check(lib().qgemm_moe_grouped(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(experts), group, _ptr(seg_off),
+                                   _ptr(row_src), x_rows, _ptr(X), _xt(X) if xt is None else xt, _ptr(rs), _ptr(Y),
+                                   N, K, R, E, _mode(mode), _stream(stream)), "qgemm_moe_grouped")
+
+
+def qg_swiglu(GU, R, I, A, at, rs=None, stream=None):
+    _check(lib().qg_swiglu(_ptr(GU), R, I, _ptr(A), at, _ptr(rs), _stream(stream)), "qg_swiglu")
+
+
+def qg_moe_combine(O, R, slot_row, slot_w, Y, H, T, k, accumulate=0, stream=None):
+    _check(lib().qg_moe_combine(_ptr(O), R, _ptr(slot_row), _ptr(slot_w), _ptr(Y), H, T, k, int(accumulate),
+                                _stream(stream)), "qg_moe_combine")
+
+
+def qg_moe_ffn_workspace(H, I, T, k, mode="exact") -> int:
+    return int(lib().qg_moe_ffn_workspace(H, I, T, k, _mode(mode)))
+
+
+def qg_moe_ffn(fmt, gate_up, down, group, E, H, I, X, T, k, seg_off, row_src, slot_row, slot_w, Y, accumulate,
+               mode, workspace, ws_bytes, stream=None):
+    _check(lib().qg_moe_ffn(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(gate_up), _ptr(down), group, E, H, I,
+                            _ptr(X), T, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w), _ptr(Y),
+                            int(accumulate), _mode(mode), _ptr(workspace), int(ws_bytes), _stream(stream)),
+           "qg_moe_ffn")
+
+
+# ---- host layout helpers (byte movement only) ----------------------------------------------------
+def pack_q4(nibbles: np.ndarray) -> np.ndarray:
+    """Nibble matrix [N][K] (values 0..15, element order) -> packed Q4 codes uint8 [N][K/2] in the
+    block layout: byte j of block b holds element 32b+j (low nibble) and 32b+16+j (high nibble)."""
+    nb = np.asarray(nibbles, dtype=np.uint8)
+    N, K = nb.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if nb.max(initial=0) > 15:
+        raise ValueError("nibbles must be in 0..15")
+    b = nb.reshape(N, K // 32, 32)
+    return (b[:, :, :16] | (b[:, :, 16:] << 4)).reshape(N, K // 2)
+
+
+def unpack_q4(codes: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of pack_q4: packed codes -> nibble matrix [N][K]."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(N, K // 32, 16)
+    return np.concatenate([c & 15, c >> 4], axis=2).reshape(N, K)
+
+
+def expert_table(experts, device="cuda"):
+    """Device array of qg_expert {codes, scales, offsets} (three 64-bit pointers each) for a list of
+    (codes, scales, offsets-or-None) device tensors."""
+    import torch
+    rows = [[_ptr(c), _ptr(s), _ptr(o) if o is not None else 0] for (c, s, o) in experts]
+    host = torch.tensor(np.array(rows, dtype=np.uint64).view(np.int64), dtype=torch.int64)
+    return host.to(device)

@@ -1,0 +1,302 @@
+// qg_capi.cpp -- the C ABI declared in include/qgemm.h: argument validation (on the host, before
+// any HIP call), kernel selection and launch, the host routing planner and the MoE chain.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <numeric>
+#include <vector>
+
+#include "qgemm.h"
+#include "qg_internal.hpp"
+
+using qg::GemmParams;
+
+namespace {
+
+constexpr int kMaxN = 1 << 24;
+constexpr int kMaxK = 1 << 20;
+constexpr int kMaxT = 1 << 21;
+constexpr int kMaxGridY = 65535;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8; }
+bool xt_ok(int x) { return x == QG_X_F32 || x == QG_X_F16 || x == QG_X_BF16; }
+bool mode_ok(int m) { return m == QG_EXACT || m == QG_FAST; }
+size_t scale_bytes(int fmt) { return fmt == QG_FMT_Q8 ? 4 : 2; }
+
+// Shared checks of the dense matmul / GEMV entry points.
+qg_status check_dense(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                      const void* X, int xt, const float* Y, int N, int K, int T, int mode) {
+    if (!fmt_ok(fmt) || !xt_ok(xt) || !mode_ok(mode)) return QG_EINVAL;
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || T < 0 || T > kMaxT) return QG_ESHAPE;
+    if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
+    if (T == 0) return QG_OK;
+    if (!codes || !scales || !X || !Y || (fmt == QG_FMT_Q4A && !offs)) return QG_EINVAL;
+    if (!aligned(codes, 16) || !aligned(X, 16) || !aligned(Y, 4) || !aligned(scales, scale_bytes(fmt)) ||
+        (offs && !aligned(offs, 2)))
+        return QG_EALIGN;
+    return QG_OK;
+}
+
+GemmParams dense_params(const void* codes, const void* scales, const uint16_t* offs, int group, const void* X,
+                        float* Y, int N, int K, int T) {
+    GemmParams p{};
+    p.codes = codes;
+    p.scales = scales;
+    p.offs = offs;
+    p.group = group > 0 ? group : 64;
+    p.X = X;
+    p.Y = Y;
+    p.N = N;
+    p.K = K;
+    p.R = T;
+    p.E = 1;
+    p.x_rows = T;
+    return p;
+}
+
+qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ELAUNCH; }
+
+qg_status run_dense(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group, const void* X,
+                    int xt, float* Y, int N, int K, int T, int mode, bool gemv_only, hipStream_t s) {
+    qg_status st = check_dense(fmt, codes, scales, offs, group, X, xt, Y, N, K, T, mode);
+    if (st != QG_OK) return st;
+    if (gemv_only && T > 8) return QG_ESHAPE;
+    if (T == 0) return QG_OK;
+    GemmParams p = dense_params(codes, scales, offs, group, X, Y, N, K, T);
+    if (T <= 8) return launched(qg::launch_gemv(fmt, xt, p, false, s));
+    if (mode == QG_EXACT) return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
+    if (xt == QG_X_F32) return QG_EUNSUPPORTED;
+    return launched(qg::launch_gemm_fast(fmt, xt, p, false, s));
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_strerror(qg_status s) {
+    switch (s) {
+        case QG_OK: return "ok";
+        case QG_EINVAL: return "invalid argument (null pointer, unknown enum value or inconsistent sizes)";
+        case QG_EALIGN: return "misaligned pointer";
+        case QG_ESHAPE: return "unsupported shape";
+        case QG_EUNSUPPORTED: return "unsupported mode / activation type combination";
+        case QG_ELAUNCH: return "kernel launch failed";
+        case QG_EPLAN: return "invalid routing plan input";
+        case QG_EWORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+int qg_abi_version(void) { return QG_ABI_VERSION; }
+
+qg_status qgemm_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt, float* Y, int N,
+                   int K, int T, qg_mode mode, hipStream_t stream) {
+    return run_dense(QG_FMT_Q4, codes, scales_f16, nullptr, 64, X, xt, Y, N, K, T, mode, false, stream);
+}
+
+qg_status qgemm_q4a(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* offsets_bf16, int group,
+                    const void* X, qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode, hipStream_t stream) {
+    return run_dense(QG_FMT_Q4A, codes, scales_f16, offsets_bf16, group, X, xt, Y, N, K, T, mode, false, stream);
+}
+
+qg_status qgemm_q8(const int8_t* codes, const float* scales_f32, const void* X, qg_xtype xt, float* Y, int N, int K,
+                   int T, qg_mode mode, hipStream_t stream) {
+    return run_dense(QG_FMT_Q8, codes, scales_f32, nullptr, 64, X, xt, Y, N, K, T, mode, false, stream);
+}
+
+qg_status qgemv_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt, float* Y, int N,
+                   int K, int T, hipStream_t stream) {
+    return run_dense(QG_FMT_Q4, codes, scales_f16, nullptr, 64, X, xt, Y, N, K, T, QG_EXACT, true, stream);
+}
+
+qg_status qgemv_q4a(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* offsets_bf16, int group,
+                    const void* X, qg_xtype xt, float* Y, int N, int K, int T, hipStream_t stream) {
+    return run_dense(QG_FMT_Q4A, codes, scales_f16, offsets_bf16, group, X, xt, Y, N, K, T, QG_EXACT, true, stream);
+}
+
+qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, qg_xtype xt, float* Y, int N, int K,
+                   int T, hipStream_t stream) {
+    return run_dense(QG_FMT_Q8, codes, scales_f32, nullptr, 64, X, xt, Y, N, K, T, QG_EXACT, true, stream);
+}
+
+qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales, const uint16_t* offsets_bf16,
+                          int group, int N, int K, int n0, int k0, int rows, int cols, qg_xtype staged, void* out,
+                          hipStream_t stream) {
+    if (!fmt_ok(fmt) || !xt_ok(staged)) return QG_EINVAL;
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0) return QG_ESHAPE;
+    if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
+    if (rows < 1 || cols < 32 || (cols % 32) != 0 || (k0 % 32) != 0 || n0 < 0 || k0 < 0 || n0 + rows > N ||
+        k0 + cols > K)
+        return QG_ESHAPE;
+    if (!codes || !scales || !out || (fmt == QG_FMT_Q4A && !offsets_bf16)) return QG_EINVAL;
+    if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(scales, scale_bytes(fmt)) ||
+        (offsets_bf16 && !aligned(offsets_bf16, 2)))
+        return QG_EALIGN;
+    return launched(qg::launch_dequant_dump(fmt, codes, scales, offsets_bf16, group, N, K, n0, k0, rows, cols,
+                                            staged, out, stream));
+}
+
+// ---- routing plan (host) ---------------------------------------------------------------------------
+qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
+                           int32_t* slot_row, float* slot_w, int32_t* slot_expert) {
+    if (!logits || !seg_off || !row_src || !slot_row || !slot_w) return QG_EINVAL;
+    if (T < 1 || E < 1 || E > 4096 || k < 1 || k > E || (long)T * k > (1L << 30)) return QG_ESHAPE;
+    for (long i = 0; i < (long)T * E; i++)
+        if (std::isnan(logits[i])) return QG_EPLAN;
+    std::vector<int> idx(E), top((size_t)T * k);
+    for (int t = 0; t < T; t++) {
+        const float* row = logits + (size_t)t * E;
+        std::iota(idx.begin(), idx.end(), 0);
+        // descending logit; equal logits: lower expert index first
+        std::partial_sort(idx.begin(), idx.begin() + k, idx.end(), [row](int a, int b) {
+            return row[a] > row[b] || (row[a] == row[b] && a < b);
+        });
+        const double lmax = row[idx[0]];
+        double sum = 0.0;
+        for (int j = 0; j < k; j++) sum += std::exp((double)row[idx[j]] - lmax);
+        for (int j = 0; j < k; j++) {
+            top[(size_t)t * k + j] = idx[j];
+            slot_w[(size_t)t * k + j] = (float)(std::exp((double)row[idx[j]] - lmax) / sum);
+            if (slot_expert) slot_expert[(size_t)t * k + j] = idx[j];
+        }
+    }
+    std::vector<int32_t> fill(E, 0);
+    for (int e = 0; e <= E; e++) seg_off[e] = 0;
+    for (size_t i = 0; i < top.size(); i++) seg_off[top[i] + 1]++;
+    for (int e = 0; e < E; e++) seg_off[e + 1] += seg_off[e];
+    for (int e = 0; e < E; e++) fill[e] = seg_off[e];
+    for (int t = 0; t < T; t++)
+        for (int j = 0; j < k; j++) {
+            const int e = top[(size_t)t * k + j];
+            const int r = fill[e]++;
+            row_src[r] = t;
+            slot_row[(size_t)t * k + j] = r;
+        }
+    return QG_OK;
+}
+
+qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh, float* rs,
+                    hipStream_t stream) {
+    if (R < 0 || R > kMaxT || K < 8 || K > kMaxK || (K % 8) != 0 || x_rows < 0) return QG_ESHAPE;
+    if (R == 0) return QG_OK;
+    if (!X || !Xh || !rs) return QG_EINVAL;
+    if (!aligned(X, 16) || !aligned(Xh, 16) || !aligned(rs, 4) || (row_src && !aligned(row_src, 4)))
+        return QG_EALIGN;
+    return launched(qg::launch_x_half(X, x_rows, row_src, R, K, Xh, rs, stream));
+}
+
+qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, const int32_t* seg_off,
+                            const int32_t* row_src, int x_rows, const void* X, qg_xtype xt, const float* rs,
+                            float* Y, int N, int K, int R, int E, qg_mode mode, hipStream_t stream) {
+    if (!fmt_ok(fmt) || !xt_ok(xt) || !mode_ok(mode)) return QG_EINVAL;
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || R < 0 || R > kMaxT || E < 1 ||
+        E > kMaxGridY || x_rows < 0)
+        return QG_ESHAPE;
+    if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
+    if (mode == QG_FAST && (R + 31) / 32 + std::min(E, R) > kMaxGridY) return QG_ESHAPE;
+    if (R == 0) return QG_OK;
+    if (!experts || !seg_off || !X || !Y) return QG_EINVAL;
+    if (!aligned(experts, 8) || !aligned(seg_off, 4) || !aligned(X, 16) || !aligned(Y, 4) ||
+        (row_src && !aligned(row_src, 4)) || (rs && !aligned(rs, 4)))
+        return QG_EALIGN;
+    if (mode == QG_FAST && xt == QG_X_F32) return QG_EUNSUPPORTED;
+    GemmParams p{};
+    p.experts = (const qg::ExpertPtr*)experts;
+    p.seg_off = seg_off;
+    p.row_src = row_src;
+    p.x_rows = row_src ? x_rows : R;
+    p.X = X;
+    p.rs = rs;
+    p.Y = Y;
+    p.group = group > 0 ? group : 64;
+    p.N = N;
+    p.K = K;
+    p.R = R;
+    p.E = E;
+    if (mode == QG_EXACT) return launched(qg::launch_gemv(fmt, xt, p, true, stream));
+    return launched(qg::launch_gemm_fast(fmt, xt, p, true, stream));
+}
+
+qg_status qg_swiglu(const float* GU, int R, int I, void* A, qg_xtype at, float* rs, hipStream_t stream) {
+    if (at != QG_X_F32 && at != QG_X_F16) return xt_ok(at) ? QG_EUNSUPPORTED : QG_EINVAL;
+    if (R < 0 || R > kMaxT || I < 8 || (I % 8) != 0 || I > kMaxK) return QG_ESHAPE;
+    if (R == 0) return QG_OK;
+    if (!GU || !A || (at == QG_X_F16 && !rs)) return QG_EINVAL;
+    if (!aligned(GU, 16) || !aligned(A, 16) || (rs && !aligned(rs, 4))) return QG_EALIGN;
+    return launched(qg::launch_swiglu(GU, R, I, A, at, rs, stream));
+}
+
+qg_status qg_moe_combine(const float* O, int R, const int32_t* slot_row, const float* slot_w, float* Y, int H,
+                         int T, int k, int accumulate, hipStream_t stream) {
+    if (R < 0 || H < 4 || (H % 4) != 0 || H > kMaxK || T < 0 || T > kMaxGridY || k < 1 || k > 4096)
+        return QG_ESHAPE;
+    if (T == 0) return QG_OK;
+    if (!O || !slot_row || !slot_w || !Y) return QG_EINVAL;
+    if (!aligned(O, 16) || !aligned(Y, 16) || !aligned(slot_row, 4) || !aligned(slot_w, 4)) return QG_EALIGN;
+    return launched(qg::launch_moe_combine(O, R, slot_row, slot_w, Y, H, T, k, accumulate ? 1 : 0, stream));
+}
+
+size_t qg_moe_ffn_workspace(int H, int I, int T, int k, qg_mode mode) {
+    if (H < 1 || I < 1 || T < 0 || k < 1) return 0;
+    const size_t R = (size_t)T * (size_t)k;
+    size_t b = align256(R * 2 * I * 4) + align256(R * H * 4);  // GU, O
+    if (mode == QG_FAST)
+        b += align256(R * H * 2) + 2 * align256(R * 4) + align256(R * I * 2);  // Xh, rs1, rs2, A f16
+    else
+        b += align256(R * I * 4);  // A f32
+    return b;
+}
+
+qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* down, int group, int E, int H, int I,
+                     const float* X, int T, int k, const int32_t* seg_off, const int32_t* row_src,
+                     const int32_t* slot_row, const float* slot_w, float* Y, int accumulate, qg_mode mode,
+                     void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!fmt_ok(fmt) || !mode_ok(mode)) return QG_EINVAL;
+    if (E < 1 || E > kMaxGridY || H < 32 || (H % 32) != 0 || H > kMaxK || I < 32 || (I % 32) != 0 || I > kMaxK ||
+        T < 0 || T > kMaxGridY || k < 1 || k > E)
+        return QG_ESHAPE;
+    if (T == 0) return QG_OK;
+    if (!gate_up || !down || !X || !seg_off || !row_src || !slot_row || !slot_w || !Y || !workspace)
+        return QG_EINVAL;
+    if (!aligned(workspace, 256)) return QG_EALIGN;
+    if (ws_bytes < qg_moe_ffn_workspace(H, I, T, k, mode)) return QG_EWORKSPACE;
+    const int R = T * k;
+    char* w = (char*)workspace;
+    float* GU = (float*)w;
+    w += align256((size_t)R * 2 * I * 4);
+    float* O = (float*)w;
+    w += align256((size_t)R * H * 4);
+    qg_status st;
+    if (mode == QG_FAST) {
+        uint16_t* Xh = (uint16_t*)w;
+        w += align256((size_t)R * H * 2);
+        float* rs1 = (float*)w;
+        w += align256((size_t)R * 4);
+        float* rs2 = (float*)w;
+        w += align256((size_t)R * 4);
+        uint16_t* A = (uint16_t*)w;
+        if ((st = qg_x_half(X, T, row_src, R, H, Xh, rs1, stream)) != QG_OK) return st;
+        if ((st = qgemm_moe_grouped(fmt, gate_up, group, seg_off, nullptr, R, Xh, QG_X_F16, rs1, GU, 2 * I, H, R, E,
+                                    QG_FAST, stream)) != QG_OK)
+            return st;
+        if ((st = qg_swiglu(GU, R, I, A, QG_X_F16, rs2, stream)) != QG_OK) return st;
+        if ((st = qgemm_moe_grouped(fmt, down, group, seg_off, nullptr, R, A, QG_X_F16, rs2, O, H, I, R, E, QG_FAST,
+                                    stream)) != QG_OK)
+            return st;
+    } else {
+        float* A = (float*)w;
+        if ((st = qgemm_moe_grouped(fmt, gate_up, group, seg_off, row_src, T, X, QG_X_F32, nullptr, GU, 2 * I, H, R,
+                                    E, QG_EXACT, stream)) != QG_OK)
+            return st;
+        if ((st = qg_swiglu(GU, R, I, A, QG_X_F32, nullptr, stream)) != QG_OK) return st;
+        if ((st = qgemm_moe_grouped(fmt, down, group, seg_off, nullptr, R, A, QG_X_F32, nullptr, O, H, I, R, E,
+                                    QG_EXACT, stream)) != QG_OK)
+            return st;
+    }
+    return qg_moe_combine(O, R, slot_row, slot_w, Y, H, T, k, accumulate, stream);
+}
+
+}  // extern "C"

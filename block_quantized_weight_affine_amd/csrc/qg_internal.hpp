@@ -1,0 +1,48 @@
+// qg_internal.hpp -- launch parameters shared by the host entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+struct ExpertPtr {
+    const void* codes;
+    const void* scales;
+    const uint16_t* offsets;
+};
+
+// One matmul launch: either dense (one weight matrix, rows 0..R-1 of X) or grouped (an expert
+// table and the row segments seg_off[e]..seg_off[e+1]-1 of each expert).
+struct GemmParams {
+    const void* codes;           // dense weights
+    const void* scales;
+    const uint16_t* offs;
+    const ExpertPtr* experts;    // grouped: device table [E]
+    const int32_t* seg_off;      // grouped: device [E+1]
+    const int32_t* row_src;      // optional: X row of output row r
+    const void* X;
+    const float* rs;             // optional per-row output scale
+    float* Y;                    // [R][N]
+    int group;
+    int N, K;
+    int R;                       // output rows (dense: T)
+    int E;                       // grouped: experts
+    int x_rows;                  // rows of X (bounds for row_src)
+};
+
+// Kernel launchers; each returns a hipError_t from hipGetLastError after the launch.
+hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s);
+hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
+hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
+hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                               int N, int K, int n0, int k0, int rows, int cols, int staged, void* out,
+                               hipStream_t s);
+hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh, float* rs,
+                         hipStream_t s);
+hipError_t launch_swiglu(const float* GU, int R, int I, void* A, int at, float* rs, hipStream_t s);
+hipError_t launch_moe_combine(const float* O, int R, const int32_t* slot_row, const float* slot_w, float* Y, int H,
+                              int T, int k, int accumulate, hipStream_t s);
+
+}  // namespace qg

@@ -1,0 +1,203 @@
+// qg_misc.hip -- the dequant dump, the per-row f16 scaling, SwiGLU and the weighted combine.
+#include "qg_device.hpp"
+#include "qg_internal.hpp"
+
+namespace qg {
+
+// ---- dequant dump ------------------------------------------------------------------------------
+// One thread per (row, block) of the requested tile.  It runs the same block load and decode the
+// MFMA kernels run (load_block + block_to_f32 for exact mode, load_block + block_to_frags16 for
+// fast mode) and writes element e of the block to out[r][32*bb + e].
+template <int FMT, int ST>
+__global__ void dequant_dump_kernel(const void* codes, const void* scales, const uint16_t* offs, int group, int K,
+                                    int n0, int k0, int rows, int cols, void* out) {
+    const int nb = cols >> 5;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nb) return;
+    const int r = idx / nb, bb = idx % nb;
+    const RawBlock<FMT> raw = load_block<FMT>(codes, scales, offs, group, K, n0 + r, (k0 >> 5) + bb);
+    if constexpr (ST == XT_F32) {
+        float v[32];
+        block_to_f32<FMT>(raw, v);
+        float* o = (float*)out + (size_t)r * cols + 32 * bb;
+#pragma unroll
+        for (int e = 0; e < 32; e++) o[e] = v[e];
+    } else {
+        short8_t f[4];
+        block_to_frags16<FMT, ST>(raw, f);
+        uint16_t* o = (uint16_t*)out + (size_t)r * cols + 32 * bb;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int s = 0; s < 8; s++) o[8 * j + s] = (uint16_t)f[j][s];
+    }
+}
+
+template <int FMT>
+static void dump_st(int staged, const void* codes, const void* scales, const uint16_t* offs, int group, int K,
+                    int n0, int k0, int rows, int cols, void* out, hipStream_t s) {
+    const int total = rows * (cols >> 5);
+    dim3 grid((total + 255) / 256);
+    if (staged == XT_F32)
+        hipLaunchKernelGGL((dequant_dump_kernel<FMT, XT_F32>), grid, dim3(256), 0, s, codes, scales, offs, group, K,
+                           n0, k0, rows, cols, out);
+    else if (staged == XT_F16)
+        hipLaunchKernelGGL((dequant_dump_kernel<FMT, XT_F16>), grid, dim3(256), 0, s, codes, scales, offs, group, K,
+                           n0, k0, rows, cols, out);
+    else
+        hipLaunchKernelGGL((dequant_dump_kernel<FMT, XT_BF16>), grid, dim3(256), 0, s, codes, scales, offs, group, K,
+                           n0, k0, rows, cols, out);
+}
+
+hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
+                               int N, int K, int n0, int k0, int rows, int cols, int staged, void* out,
+                               hipStream_t s) {
+    (void)N;
+    if (fmt == FMT_Q4) dump_st<FMT_Q4>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
+    else if (fmt == FMT_Q4A) dump_st<FMT_Q4A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
+    else dump_st<FMT_Q8>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
+    return hipGetLastError();
+}
+
+// ---- block-wide max / helpers ---------------------------------------------------------------------
+__device__ __forceinline__ float block_max256(float m, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = m;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Power-of-two row scale (page "oxinfer 0.0.5 src/metal.rs", MMA_SHADER_SRC, row_scale): the
+// largest magnitude lands in [2^13, 2^14); a zero or non-finite amax keeps scale 1.
+__device__ __forceinline__ int row_scale_exp(float amax) {
+    int e = 0;
+    if (amax > 0.f && isfinite(amax)) {
+        int fe;
+        frexpf(amax, &fe);
+        e = min(max(14 - fe, -100), 100);
+    }
+    return e;
+}
+
+// ---- x_half: gathered per-row scaling to f16 -----------------------------------------------------
+__global__ __launch_bounds__(256) void x_half_kernel(const float* X, int x_rows, const int32_t* row_src, int K,
+                                                      uint16_t* Xh, float* rs) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    int s = row_src ? row_src[r] : r;
+    const bool valid = s >= 0 && s < x_rows;
+    const float4* row = (const float4*)(X + (size_t)(valid ? s : 0) * K);
+    const int n4 = K >> 2;
+    float m = 0.f;
+    if (valid)
+        for (int i = threadIdx.x; i < n4; i += 256) {
+            const float4 v = row[i];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    m = block_max256(m, red);
+    const int e = row_scale_exp(m);
+    const float sc = ldexpf(1.0f, e);
+    uint2* out = (uint2*)(Xh + (size_t)r * K);
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        float4 v = valid ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint32_t a = (uint32_t)f32_to_f16_bits(v.x * sc) | ((uint32_t)f32_to_f16_bits(v.y * sc) << 16);
+        const uint32_t b = (uint32_t)f32_to_f16_bits(v.z * sc) | ((uint32_t)f32_to_f16_bits(v.w * sc) << 16);
+        out[i] = make_uint2(a, b);
+    }
+    if (threadIdx.x == 0) rs[r] = ldexpf(1.0f, -e);
+}
+
+hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh, float* rs,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(x_half_kernel, dim3(R), dim3(256), 0, s, X, x_rows, row_src, K, Xh, rs);
+    return hipGetLastError();
+}
+
+// ---- SwiGLU (page section silu_half): a = g / (1 + exp(-g)) * u ------------------------------------
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__global__ __launch_bounds__(256) void swiglu_f32_kernel(const float* GU, int I, float* A) {
+    const int r = blockIdx.x;
+    const float4* g = (const float4*)(GU + (size_t)r * 2 * I);
+    const float4* u = g + (I >> 2);
+    float4* a = (float4*)(A + (size_t)r * I);
+    for (int i = threadIdx.x; i < (I >> 2); i += 256) {
+        const float4 gv = g[i], uv = u[i];
+        a[i] = make_float4(silu_mul(gv.x, uv.x), silu_mul(gv.y, uv.y), silu_mul(gv.z, uv.z), silu_mul(gv.w, uv.w));
+    }
+}
+
+__global__ __launch_bounds__(256) void swiglu_f16_kernel(const float* GU, int I, uint16_t* A, float* rs) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    const float4* g = (const float4*)(GU + (size_t)r * 2 * I);
+    const float4* u = g + (I >> 2);
+    float m = 0.f;
+    for (int i = threadIdx.x; i < (I >> 2); i += 256) {
+        const float4 gv = g[i], uv = u[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(silu_mul(gv.x, uv.x)), fabsf(silu_mul(gv.y, uv.y))),
+                           fmaxf(fabsf(silu_mul(gv.z, uv.z)), fabsf(silu_mul(gv.w, uv.w)))));
+    }
+    m = block_max256(m, red);
+    const int e = row_scale_exp(m);
+    const float sc = ldexpf(1.0f, e);
+    uint2* out = (uint2*)(A + (size_t)r * I);
+    for (int i = threadIdx.x; i < (I >> 2); i += 256) {
+        const float4 gv = g[i], uv = u[i];
+        const uint32_t a = (uint32_t)f32_to_f16_bits(silu_mul(gv.x, uv.x) * sc) |
+                           ((uint32_t)f32_to_f16_bits(silu_mul(gv.y, uv.y) * sc) << 16);
+        const uint32_t b = (uint32_t)f32_to_f16_bits(silu_mul(gv.z, uv.z) * sc) |
+                           ((uint32_t)f32_to_f16_bits(silu_mul(gv.w, uv.w) * sc) << 16);
+        out[i] = make_uint2(a, b);
+    }
+    if (threadIdx.x == 0) rs[r] = ldexpf(1.0f, -e);
+}
+
+hipError_t launch_swiglu(const float* GU, int R, int I, void* A, int at, float* rs, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    if (at == XT_F32)
+        hipLaunchKernelGGL(swiglu_f32_kernel, dim3(R), dim3(256), 0, s, GU, I, (float*)A);
+    else
+        hipLaunchKernelGGL(swiglu_f16_kernel, dim3(R), dim3(256), 0, s, GU, I, (uint16_t*)A, rs);
+    return hipGetLastError();
+}
+
+// ---- weighted combine (page section moe_combine), f32 in slot order --------------------------------
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* O, int R, const int32_t* slot_row,
+                                                           const float* slot_w, float* Y, int H, int k,
+                                                           int accumulate) {
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; j++) {
+        const int row = slot_row[t * k + j];
+        if (row < 0 || row >= R) continue;
+        const float w = slot_w[t * k + j];
+        const float4 o = *(const float4*)(O + (size_t)row * H + c);
+        acc.x += w * o.x;
+        acc.y += w * o.y;
+        acc.z += w * o.z;
+        acc.w += w * o.w;
+    }
+    float4* y = (float4*)(Y + (size_t)t * H + c);
+    if (accumulate) {
+        const float4 p = *y;
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
+    }
+    *y = acc;
+}
+
+hipError_t launch_moe_combine(const float* O, int R, const int32_t* slot_row, const float* slot_w, float* Y, int H,
+                              int T, int k, int accumulate, hipStream_t s) {
+    dim3 grid((H / 4 + 255) / 256, T);
+    hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, O, R, slot_row, slot_w, Y, H, k, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace qg

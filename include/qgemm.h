@@ -1,0 +1,196 @@
+/*
+ * qgemm.h -- C ABI of the block-quantized weight matrix multiply for MI355X (gfx950).
+ *
+ *     Y[T x N] = X[T x K] . dequant(W)[N x K]^T
+ *
+ * W is block-quantized along K and is dequantized while it is staged into on-chip tiles; it is
+ * never written out to memory in dequantized form.  All pointers passed to the entry points below
+ * are DEVICE pointers (memory the caller allocated on the GPU), except where an argument says
+ * "host".  The caller owns every buffer; the library allocates nothing, keeps no state between
+ * calls besides cached kernel attributes, never synchronizes, and enqueues its kernels on the
+ * caller's stream.  Every entry point validates its arguments on the host before any HIP call and
+ * returns a status code; nothing else is reported through the return value, and no C++ exception
+ * crosses this boundary.
+ *
+ * Formats (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC, the dequantizers Q4W, Q4A and Q8W, and
+ * Backend::upload for the offsets):
+ *   Q4   codes  uint8 [N][K/2]: block b (32 consecutive k) of row n is the 16 bytes at
+ *               n*K/2 + 16*b; byte j holds element 32b+j in its low nibble and element 32b+16+j
+ *               in its high nibble.
+ *        scales f16 bits [N][K/32]: one per block.
+ *        value  w = (nibble - 8) * scale, computed in f32.
+ *   Q4A  Q4 plus offsets bf16 bits [N][K/group]: w = (nibble - 8) * scale + offset, in f32, the
+ *        offset of group floor(k/group) added to every element of the group (group a multiple
+ *        of 32 that divides K).
+ *   Q8   codes  int8 [N][K] (row-major), scales f32 [N][K/32]: w = float(q) * scale, in f32.
+ * Activations X are row-major [T][K] in f32, f16 or bf16; results Y are row-major [T][N] f32.
+ *
+ * Modes (same page, module notes and MMA_SHADER_SRC):
+ *   QG_EXACT  f32 operands, f32 accumulation (f32 MFMA or f32 FMA); 16-bit X is widened exactly.
+ *   QG_FAST   the dequantized f32 weight is rounded to nearest-even into the 16-bit type of X
+ *             (f16 or bf16) as it is staged; f16/bf16 MFMA with f32 accumulation.
+ *
+ * Shape and alignment rules shared by the matmul entry points (violations return the code named):
+ *   N >= 1, T >= 0, K >= 32, K % 32 == 0                                 else QG_ESHAPE
+ *   codes, X and Y 16-byte aligned; scales / offsets aligned to their element size; expert tables,
+ *   index arrays and row scales 4-byte aligned                           else QG_EALIGN
+ *   null pointers (with T > 0), or an enum value out of range            QG_EINVAL
+ *   T == 0 returns QG_OK without launching anything.
+ * Rows of Y at or beyond T, and columns at or beyond N, are never written.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+typedef enum {
+    QG_OK = 0,
+    QG_EINVAL = 1,       /* null pointer, unknown enum value, or inconsistent sizes */
+    QG_EALIGN = 2,       /* a pointer is not aligned as required */
+    QG_ESHAPE = 3,       /* N, K, T, group, E or k outside what the kernels support */
+    QG_EUNSUPPORTED = 4, /* a mode / activation type combination the library does not provide */
+    QG_ELAUNCH = 5,      /* the HIP launch reported an error (hipGetLastError) */
+    QG_EPLAN = 6,        /* a routing plan input is invalid (expert id, non-finite logit) */
+    QG_EWORKSPACE = 7    /* the workspace is smaller than the call needs */
+} qg_status;
+
+typedef enum { QG_X_F32 = 0, QG_X_F16 = 1, QG_X_BF16 = 2 } qg_xtype;
+typedef enum { QG_EXACT = 0, QG_FAST = 1 } qg_mode;
+typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2 } qg_format;
+
+/* Text for a status code (static storage; never NULL). */
+const char* qg_strerror(qg_status s);
+/* QG_ABI_VERSION of the library that was loaded. */
+int qg_abi_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Dense matmuls.  Y[t][n] = sum_k X[t][k] * w(n, k) for t < T, n < N; Y is overwritten.
+ * T <= 8 runs the wavefront-reduction GEMV (exact f32 arithmetic whatever the mode); larger T
+ * runs the MFMA tile kernel of the mode.  QG_FAST needs X in f16 or bf16 (the MFMA operand
+ * type); an f32 X in QG_FAST with T > 8 returns QG_EUNSUPPORTED (convert it with qg_x_half and
+ * use qgemm_moe_grouped with one expert, or use QG_EXACT).
+ * Sources: oxinfer src/metal.rs, Backend::matmul (f32 GEMM) and matmul_mma (matrix-unit GEMM).
+ */
+qg_status qgemm_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt,
+                   float* Y, int N, int K, int T, qg_mode mode, hipStream_t stream);
+qg_status qgemm_q4a(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* offsets_bf16,
+                    int group, const void* X, qg_xtype xt, float* Y, int N, int K, int T,
+                    qg_mode mode, hipStream_t stream);
+qg_status qgemm_q8(const int8_t* codes, const float* scales_f32, const void* X, qg_xtype xt,
+                   float* Y, int N, int K, int T, qg_mode mode, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * T <= 8 GEMV: one weight row per wavefront group, coalesced 16-byte loads of the packed blocks,
+ * decode in registers, f32 FMA, wavefront reduction.  T > 8 returns QG_ESHAPE.
+ * Source: page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", q4rows (the narrow <= 8-row
+ * kernel) and oxinfer src/metal.rs module notes on memory-bound decode.
+ */
+qg_status qgemv_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt,
+                   float* Y, int N, int K, int T, hipStream_t stream);
+qg_status qgemv_q4a(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* offsets_bf16,
+                    int group, const void* X, qg_xtype xt, float* Y, int N, int K, int T,
+                    hipStream_t stream);
+qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, qg_xtype xt,
+                   float* Y, int N, int K, int T, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Debug dump of a staged weight tile: out[r][c] = the value the GEMM kernels stage for element
+ * (n0 + r, k0 + c), produced by the same device decoder and tile writer the GEMMs use.
+ * staged = QG_X_F32: f32 values (exact mode); QG_X_F16 / QG_X_BF16: 16-bit patterns (fast mode).
+ * Needs k0 % 32 == 0, cols % 32 == 0, 0 <= n0, n0 + rows <= N, k0 + cols <= K, rows >= 1;
+ * out is [rows][cols] of 4 or 2 bytes, 16-byte aligned.  fmt QG_FMT_Q4 / Q4A take uint16 f16
+ * scales, QG_FMT_Q8 f32 scales; offsets are read only for QG_FMT_Q4A.
+ */
+qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales,
+                          const uint16_t* offsets_bf16, int group, int N, int K, int n0, int k0,
+                          int rows, int cols, qg_xtype staged, void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * MoE pieces.  Sources: oxinfer src/metal.rs, Backend::upload_moe (per-expert address tables),
+ * Backend::moe (the plan: rows grouped by expert, experts ascending, tokens ascending within an
+ * expert; the chain x_half -> grouped gate|up -> silu_half -> grouped down -> combine), the
+ * kernels x_half, silu_half and moe_combine of MMA_SHADER_SRC; page "cortiq-engine 0.8.44
+ * src/clover.rs" for the top-k rule and the renormalised weights.
+ */
+
+/* One expert's weights (device pointers).  scales point to f16 bits (Q4, Q4A) or f32 (Q8);
+ * offsets are used by Q4A only (may be NULL otherwise). */
+typedef struct {
+    const void* codes;
+    const void* scales;
+    const uint16_t* offsets;
+} qg_expert;
+
+/* Routing plan, on the HOST (all pointers host memory).  logits f32 [T][E].  For each token:
+ * the k largest logits, equal logits in ascending expert index; weight_j = exp(l_j - l_max) /
+ * sum over the k kept of exp(l_i - l_max).  Outputs: seg_off [E+1] (expert e's gathered rows are
+ * seg_off[e] .. seg_off[e+1]-1), row_src [T*k] (token of each gathered row; tokens ascending
+ * within an expert), slot_row [T*k] (gathered row of token t's j-th choice at t*k + j, j in
+ * descending-logit order), slot_w [T*k] (its weight, f32), slot_expert [T*k] (its expert id; may
+ * be NULL).  Needs 1 <= k <= E <= 4096, T >= 1; QG_EPLAN if a logit is NaN. */
+qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* seg_off,
+                           int32_t* row_src, int32_t* slot_row, float* slot_w, int32_t* slot_expert);
+
+/* Gathered per-row power-of-two scaling of f32 rows to f16 (page section x_half / row_scale):
+ * for r < R, source row s = row_src ? row_src[r] : r (rows with s outside [0, x_rows) read as
+ * zeros); amax over the row; e from frexp(amax) -> scale 2^(14 - e) clamped to 2^[-100, 100]
+ * (scale 1 for a zero or non-finite amax); Xh[r][:] = f16(X[s][:] * scale) (nearest-even),
+ * rs[r] = 1 / scale.  X f32 [x_rows][K], Xh f16 bits [R][K], rs f32 [R].  K % 8 == 0. */
+qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh,
+                    float* rs, hipStream_t stream);
+
+/* Ragged grouped matmul over experts: for every expert e < E and every gathered row r in
+ * [seg_off[e], seg_off[e+1]), Y[r][n] = (rs ? rs[r] : 1) * sum_k x_r[k] * w_e(n, k), n < N, where
+ * x_r = X[row_src[r]] if row_src is given (row ids outside [0, x_rows) read as zeros) else X[r].
+ * experts is a DEVICE array of E qg_expert (all of format fmt, each [N][K]); seg_off is a DEVICE
+ * int32 [E+1], non-decreasing, seg_off[0] >= 0, seg_off[E] <= R (rows outside every segment are
+ * not written).  QG_EXACT: X f32 / f16 / bf16, f32 FMA.  QG_FAST: X f16 or bf16 (for f32 rows,
+ * first run qg_x_half and pass its Xh and rs), f16 / bf16 MFMA.  Y f32 [R][N]. */
+qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group,
+                            const int32_t* seg_off, const int32_t* row_src, int x_rows,
+                            const void* X, qg_xtype xt, const float* rs, float* Y, int N, int K,
+                            int R, int E, qg_mode mode, hipStream_t stream);
+
+/* SwiGLU of fused [gate | up] rows (page section silu_half): GU f32 [R][2I] (gate in columns
+ * 0..I-1, up in I..2I-1); a = gate / (1 + exp(-gate)) * up.  at = QG_X_F32: A f32 [R][I], rs
+ * unused (may be NULL).  at = QG_X_F16: A f16 bits [R][I] scaled per row by a power of two as
+ * qg_x_half does, rs f32 [R] the inverse scales.  I % 8 == 0. */
+qg_status qg_swiglu(const float* GU, int R, int I, void* A, qg_xtype at, float* rs,
+                    hipStream_t stream);
+
+/* Weighted combine (page section moe_combine): for t < T, c < H:
+ * Y[t][c] (+)= sum_{j<k} slot_w[t*k+j] * O[slot_row[t*k+j]][c], summed in f32 in j order;
+ * accumulate = 0 overwrites Y, 1 adds to it (the page's y += out).  O f32 [R][H], slot_row int32
+ * and slot_w f32 [T*k] (device); slot rows outside [0, R) contribute nothing.  H % 4 == 0. */
+qg_status qg_moe_combine(const float* O, int R, const int32_t* slot_row, const float* slot_w,
+                         float* Y, int H, int T, int k, int accumulate, hipStream_t stream);
+
+/* Workspace bytes qg_moe_ffn needs for R = T*k routed rows. */
+size_t qg_moe_ffn_workspace(int H, int I, int T, int k, qg_mode mode);
+
+/* The whole expert block on the stream (page section Backend::moe): [fast: qg_x_half gather] ->
+ * grouped gate|up ([2I][H] per expert) -> qg_swiglu -> grouped down ([H][I] per expert) ->
+ * qg_moe_combine into Y f32 [T][H] (accumulate as above).  gate_up / down are DEVICE arrays of E
+ * experts of format fmt; seg_off, row_src, slot_row, slot_w are the device copies of a plan
+ * (qg_moe_plan_host) for these T tokens and k slots; X f32 [T][H].  The workspace (device,
+ * 256-byte aligned) holds the intermediates; QG_EWORKSPACE if ws_bytes is too small. */
+qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* down, int group,
+                     int E, int H, int I, const float* X, int T, int k, const int32_t* seg_off,
+                     const int32_t* row_src, const int32_t* slot_row, const float* slot_w,
+                     float* Y, int accumulate, qg_mode mode, void* workspace, size_t ws_bytes,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

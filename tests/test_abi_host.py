@@ -1,0 +1,133 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/qgemm.h declares,
+rejects bad arguments with the documented codes before any HIP call, and its host routing planner
+and packing helpers agree with the oracle.  Nothing here launches a kernel."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_quantized_weight_affine_amd as qg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+char\s*\*|int|qg_status|size_t)\s+(\w+)\s*\(", src, flags=re.M)
+
+
+def test_exports_every_declared_symbol():
+    L = qg.lib()
+    names = _declared()
+    assert set(names) == set(qg.SYMBOLS), (names, qg.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert qg.abi_version() == 1
+    for s in range(8):
+        assert qg.strerror(s)
+
+
+# fake, never-dereferenced addresses: validation runs entirely on the host
+A16 = 0x10000
+A16b = 0x20000
+A16c = 0x30000
+A16d = 0x40000
+
+
+def _q4(**kw):
+    a = dict(codes=A16, scales=A16b, X=A16c, xt=qg.QG_X_F32, Y=A16d, N=256, K=512, T=16, mode=qg.QG_EXACT)
+    a.update(kw)
+    return qg.lib().qgemm_q4(a["codes"], a["scales"], a["X"], a["xt"], a["Y"], a["N"], a["K"], a["T"], a["mode"], None)
+
+
+def test_dense_validation_codes():
+    assert _q4(K=48) == qg.QG_ESHAPE            # K % 32
+    assert _q4(K=16) == qg.QG_ESHAPE
+    assert _q4(N=0) == qg.QG_ESHAPE
+    assert _q4(T=-1) == qg.QG_ESHAPE
+    assert _q4(codes=None) == qg.QG_EINVAL
+    assert _q4(Y=None) == qg.QG_EINVAL
+    assert _q4(xt=7) == qg.QG_EINVAL
+    assert _q4(mode=5) == qg.QG_EINVAL
+    assert _q4(codes=A16 + 8) == qg.QG_EALIGN
+    assert _q4(X=A16c + 4) == qg.QG_EALIGN
+    assert _q4(scales=A16b + 1) == qg.QG_EALIGN
+    assert _q4(T=0) == qg.QG_OK                 # nothing to do, nothing launched
+    assert _q4(T=0, codes=None) == qg.QG_OK
+    assert _q4(T=16, mode=qg.QG_FAST, xt=qg.QG_X_F32) == qg.QG_EUNSUPPORTED
+    L = qg.lib()
+    # affine: group must be a multiple of 32 dividing K, offsets required
+    assert L.qgemm_q4a(A16, A16b, A16, 48, A16c, 0, A16d, 256, 512, 16, 0, None) == qg.QG_ESHAPE
+    assert L.qgemm_q4a(A16, A16b, A16, 96, A16c, 0, A16d, 256, 512, 16, 0, None) == qg.QG_ESHAPE
+    assert L.qgemm_q4a(A16, A16b, None, 64, A16c, 0, A16d, 256, 512, 16, 0, None) == qg.QG_EINVAL
+    # q8 scales are f32: 4-byte alignment
+    assert L.qgemm_q8(A16, A16b + 2, A16c, 0, A16d, 256, 512, 16, 0, None) == qg.QG_EALIGN
+    # GEMV takes at most 8 rows
+    assert L.qgemv_q8(A16, A16b, A16c, 0, A16d, 256, 512, 9, None) == qg.QG_ESHAPE
+    assert L.qgemv_q4(A16, A16b, A16c, 0, A16d, 256, 512, 0, None) == qg.QG_OK
+
+
+def test_dump_and_moe_validation_codes():
+    L = qg.lib()
+    # dump: tile must be inside the matrix, block aligned
+    assert L.qg_dequant_dump(0, A16, A16b, None, 64, 64, 128, 0, 16, 4, 32, 0, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_dequant_dump(0, A16, A16b, None, 64, 64, 128, 60, 0, 8, 32, 0, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_dequant_dump(0, A16, A16b, None, 64, 64, 128, 0, 96, 1, 64, 0, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_dequant_dump(3, A16, A16b, None, 64, 64, 128, 0, 0, 1, 32, 0, A16c, None) == qg.QG_EINVAL
+    # grouped: fast mode needs 16-bit X; E >= 1
+    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 512, 8, 4, 1, None) == \
+        qg.QG_EUNSUPPORTED
+    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 8, 0, 1, None) == \
+        qg.QG_ESHAPE
+    assert L.qgemm_moe_grouped(0, None, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 8, 4, 1, None) == \
+        qg.QG_EINVAL
+    assert L.qgemm_moe_grouped(0, A16 + 4, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 8, 4, 1, None) == \
+        qg.QG_EALIGN
+    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 0, 4, 1, None) == qg.QG_OK
+    assert L.qg_swiglu(A16, 4, 12, A16b, 0, None, None) == qg.QG_ESHAPE
+    assert L.qg_swiglu(A16, 4, 16, A16b, 2, None, None) == qg.QG_EUNSUPPORTED
+    assert L.qg_swiglu(A16, 4, 16, A16b, 1, None, None) == qg.QG_EINVAL
+    assert L.qg_moe_combine(A16, 8, A16b, A16c, A16d, 6, 2, 2, 0, None) == qg.QG_ESHAPE
+    assert L.qg_moe_combine(A16, 8, A16b, A16c, A16d + 8, 8, 2, 2, 0, None) == qg.QG_EALIGN
+    assert L.qg_x_half(A16, 4, None, 4, 12, A16b, A16c, None) == qg.QG_ESHAPE
+    ws = qg.qg_moe_ffn_workspace(2048, 1536, 32, 8, "fast")
+    assert ws >= 256 * (3072 * 4 + 2048 * 4 + 2048 * 2 + 1536 * 2)
+    assert L.qg_moe_ffn(0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d, 0, 1,
+                        0x100000, ws - 1, None) == qg.QG_EWORKSPACE
+    assert L.qg_moe_ffn(0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d, 0, 1,
+                        0x100010, ws, None) == qg.QG_EALIGN
+
+
+def test_plan_host_matches_oracle(orc):
+    import synth
+    for (T, E, k, seed) in [(32, 128, 8, 1004), (75, 8, 2, 7), (5, 16, 16, 3)]:
+        lg = synth.normal_as(seed, synth.STREAM_LOGITS, T * E, 0.0, 1.0, "f32").reshape(T, E)
+        if T == 5:
+            lg[1, :] = 0.25                 # all tied: experts in index order
+            lg[2, 3] = lg[2, 9] = 5.0        # a tie at the top
+        ours = qg.qg_moe_plan_host(lg, T, E, k)
+        ref = orc.moe_plan(lg, T, E, k)
+        for key in ("seg_off", "row_src", "slot_row", "slot_expert"):
+            assert np.array_equal(ours[key], ref[key]), key
+        assert np.allclose(ours["slot_w"], ref["slot_w"], rtol=2e-7, atol=1e-12)
+    bad = np.zeros((2, 4), np.float32)
+    bad[1, 2] = np.nan
+    with pytest.raises(qg.QGError) as e:
+        qg.qg_moe_plan_host(bad, 2, 4, 2)
+    assert e.value.status == qg.QG_EPLAN
+
+
+def test_pack_q4_round_trip_against_oracle(orc):
+    rng = np.random.default_rng(2)
+    N, K = 7, 96
+    nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    codes = qg.pack_q4(nib)
+    assert codes.shape == (N, K // 2)
+    assert np.array_equal(qg.unpack_q4(codes, N, K), nib)
+    scales = np.full(N * K // 32, 0x3C00, np.uint16)     # scale 1.0: weight = nibble - 8
+    W = orc.dequant_exact("q4", codes.reshape(-1), scales, None, 64, N, K)
+    assert np.array_equal(W, nib.astype(np.float64) - 8.0)
+    with pytest.raises(ValueError):
+        qg.pack_q4(np.full((1, 32), 16, np.uint8))

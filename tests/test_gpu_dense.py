@@ -1,0 +1,137 @@
+"""Dense matmul parity: GEMV (T <= 8), exact (f32 MFMA) and fast (f16 / bf16 MFMA) tile kernels
+against the f64 oracle, at tile-spanning sizes with ragged tails and at the workloads' full sizes
+(sampled outputs), plus edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_affine_amd as qg
+import synth
+from helpers import TAU, check_tol, dev, dev_x, oracle_x, sample_idx, weights_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(fmt, w, X, xtype, N, K, T, mode, extra_rows=0):
+    """Runs the dense entry point; returns Y (numpy) and the untouched padding rows."""
+    codes, scales, offs = weights_dev(w)
+    Xd = dev_x(X, xtype)
+    Y = torch.full((T + extra_rows, N), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qgemm(fmt, codes, scales, offs, w["group"], Xd, Y, N, K, T, mode)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    return y[:T], y[T:]
+
+
+def _ref(orc, fmt, w, X, xtype, N, K, T, ns=None, ts=None):
+    Yr, S, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), w["group"], N, K, oracle_x(X, xtype), xtype, T,
+                        ns=ns, ts=ts)
+    return Yr, S
+
+
+CASES = [
+    # fmt, N, K, T, xtype, mode
+    ("q4", 256, 512, 16, "f32", "exact"),        # the tiny Q4 workload
+    ("q4", 200, 224, 37, "f16", "exact"),        # ragged N, K % 64 == 32, ragged T
+    ("q4", 200, 224, 37, "f16", "fast"),
+    ("q4a", 136, 320, 70, "bf16", "fast"),
+    ("q4a", 136, 320, 70, "bf16", "exact"),
+    ("q4a", 96, 256, 33, "f16", "fast"),
+    ("q8", 160, 288, 45, "f32", "exact"),
+    ("q8", 160, 288, 45, "bf16", "fast"),
+    ("q8", 160, 288, 45, "f16", "fast"),
+    ("q4", 96, 128, 9, "bf16", "fast"),          # first T above the GEMV range
+    ("q4", 1000, 2048, 300, "f16", "fast"),      # several tiles both ways
+    ("q4a", 520, 1024, 260, "bf16", "fast"),
+    ("q8", 390, 1024, 130, "f32", "exact"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_dense_tiles(orc, case):
+    fmt, N, K, T, xtype, mode = case
+    w = synth.make_dense(fmt, N, K, T, xtype, 1.0, 500 + N + K + T)
+    Y, pad = _run(fmt, w, w["X"], xtype, N, K, T, mode, extra_rows=3)
+    Yr, S = _ref(orc, fmt, w, w["X"], xtype, N, K, T)
+    check_tol(Y, Yr, S, TAU[mode], str(case))
+    assert np.all(np.isnan(pad)), "rows at or beyond T were written"
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("xtype", ["f32", "f16", "bf16"])
+def test_gemv(orc, fmt, T, xtype):
+    N, K = 72, 1088          # K not a multiple of the 1024-element wavefront step
+    w = synth.make_dense(fmt, N, K, T, xtype, 1.0, 900 + T)
+    codes, scales, offs = weights_dev(w)
+    Y = torch.full((T + 2, N), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qgemv(fmt, codes, scales, offs, w["group"], dev_x(w["X"], xtype), Y, N, K, T)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    Yr, S = _ref(orc, fmt, w, w["X"], xtype, N, K, T)
+    check_tol(y[:T], Yr, S, TAU["exact"], f"gemv {fmt} T={T} {xtype}")
+    assert np.all(np.isnan(y[T:]))
+
+
+def test_mixed_row_magnitudes_exact(orc):
+    """X rows of magnitude 1e-3, 1, 300 and 2e5 (the matrix-unit test design of oxinfer src/metal.rs,
+    tests: mma_matmul_matches_cpu) at 192 x 512 with T = 150 and 37, exact mode."""
+    N, K = 192, 512
+    for T in (150, 37):
+        for fmt in ("q8", "q4"):
+            w = synth.make_dense(fmt, N, K, T, "f32", 1.0, 31 + T)
+            mag = np.array([1e-3, 1.0, 300.0, 2e5])[np.arange(T) % 4]
+            X = (w["X"].reshape(T, K) * mag[:, None]).astype(np.float32)
+            Y, _ = _run(fmt, w, X, "f32", N, K, T, "exact")
+            Yr, S = _ref(orc, fmt, w, X, "f32", N, K, T)
+            check_tol(Y, Yr, S, TAU["exact"], f"mixed {fmt} T={T}")
+
+
+def test_edge_shapes(orc):
+    # T = 0 launches nothing and leaves Y untouched
+    w = synth.make_dense("q4", 64, 64, 4, "f32", 1.0, 1)
+    codes, scales, _ = weights_dev(w)
+    Y = torch.full((4, 64), 7.0, device="cuda")
+    qg.qgemm_q4(codes, scales, dev_x(w["X"], "f32"), Y, 64, 64, 0)
+    torch.cuda.synchronize()
+    assert torch.all(Y == 7.0)
+    # one block, one row, one token
+    for (N, K, T, mode, xt) in [(1, 32, 1, "exact", "f32"), (1, 32, 9, "exact", "f32"), (1, 32, 9, "fast", "f16"),
+                                (16, 32, 40, "fast", "bf16"), (33, 64, 8, "fast", "f16")]:
+        w = synth.make_dense("q4", N, K, T, xt, 1.0, 11 + N + T)
+        Y, _ = _run("q4", w, w["X"], xt, N, K, T, mode)
+        Yr, S = _ref(orc, "q4", w, w["X"], xt, N, K, T)
+        check_tol(Y, Yr, S, TAU[mode], f"edge {N} {K} {T} {mode}")
+
+
+def test_zero_weights_give_exact_zero(orc):
+    """All nibbles 8 (Q4 weight 0): S = 0, so Y must be exactly 0 in every path."""
+    N, K = 64, 256
+    codes = np.full(N * K // 2, 0x88, np.uint8)
+    scales = np.full(N * K // 32, 0x3C00, np.uint16)
+    for T, mode, xt in [(4, "exact", "f32"), (40, "exact", "f32"), (40, "fast", "f16")]:
+        X = synth.normal_as(5, 3, T * K, 0, 1, xt)
+        Y = torch.empty((T, N), device="cuda")
+        qg.qgemm_q4(dev(codes), dev(scales), dev_x(X, xt), Y, N, K, T, mode)
+        torch.cuda.synchronize()
+        assert torch.all(Y == 0), (T, mode)
+
+
+# ---- the workloads at full size (sampled outputs), in the launch configuration the benchmark uses ----
+FULL = [
+    (1, "exact"), (2, "exact"), (2, "fast"), (3, "fast"),
+]
+
+
+@pytest.mark.parametrize("cfg_mode", FULL, ids=lambda c: f"cfg{c[0]}-{c[1]}")
+def test_full_size_sampled(orc, cfg_mode):
+    ci, mode = cfg_mode
+    c = synth.CONFIGS[ci]
+    print(f"full-size workload {c.name} {mode}", flush=True)
+    w = synth.make_dense(c.fmt, c.N, c.K, c.T, c.xtype, c.x_sigma, c.seed, group=c.group)
+    Y, _ = _run(c.fmt, w, w["X"], c.xtype, c.N, c.K, c.T, mode)
+    ns = sample_idx(c.N, 160, 1)
+    ts = sample_idx(c.T, 24, 2)
+    Yr, S = _ref(orc, c.fmt, w, w["X"], c.xtype, c.N, c.K, c.T, ns=ns, ts=ts)
+    check_tol(Y[np.ix_(ts, ns)], Yr, S, TAU[mode], c.name)
+    assert np.all(np.isfinite(Y))

@@ -1,0 +1,163 @@
+"""MoE pieces on the GPU against the oracle: row scaling to f16, the ragged grouped matmul (exact and
+fast), SwiGLU, the weighted combine, and the whole expert block end to end (small design with an
+unused expert and uneven loads, and the 128-expert top-8 workload)."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_affine_amd as qg
+import synth
+from helpers import TAU, check_tol, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_x_half_bit_exact(orc):
+    R, K, T = 12, 256, 5
+    X = synth.normal_as(3, 3, T * K, 0, 1, "f32").reshape(T, K)
+    X *= np.array([1e-6, 1.0, 3.0, 2e5, 0.0])[:, None].astype(np.float32)
+    src = np.array([0, 1, 2, 3, 4, 4, 3, 2, 1, 0, 7, -1], np.int32)   # 7 and -1: outside X -> zero rows
+    Xh = torch.empty((R, K), dtype=torch.int16, device="cuda")
+    rs = torch.empty(R, dtype=torch.float32, device="cuda")
+    qg.qg_x_half(dev(X), T, dev(src), R, K, Xh, rs)
+    torch.cuda.synchronize()
+    Xz = np.concatenate([X, np.zeros((1, K), np.float32)])
+    srcz = np.where((src >= 0) & (src < T), src, T)
+    xh_ref, rs_ref = orc.x_half(Xz, K, src=srcz)
+    assert np.array_equal(Xh.cpu().numpy().view(np.uint16), xh_ref)
+    assert np.array_equal(rs.cpu().numpy(), rs_ref)
+
+
+def _experts(m, which):
+    """Device tensors of every expert's gate|up or down weights plus the device table."""
+    if which == "gu":
+        codes, scales = m["gu_codes"], m["gu_scales"]
+    else:
+        codes, scales = m["dn_codes"], m["dn_scales"]
+    C = dev(codes)
+    S = dev(scales)
+    table = qg.expert_table([(C[e], S[e], None) for e in range(codes.shape[0])])
+    return C, S, table
+
+
+def _plan_dev(plan):
+    return {k: dev(np.ascontiguousarray(v)) for k, v in plan.items() if isinstance(v, np.ndarray)}
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_grouped_matches_oracle(orc, mode):
+    """Grouped gate|up on seeded rows: every expert's segment against the oracle (rows gathered through
+    row_src in exact mode; pre-scaled f16 rows in fast mode)."""
+    E, H, I, T, k = 8, 256, 96, 75, 2
+    m = synth.make_moe(E, H, I, T, 21)
+    lg = m["logits"].reshape(T, E).copy()
+    lg[:, 5] = -1e9                      # expert 5 unused
+    plan = orc.moe_plan(lg, T, E, k)
+    R = plan["R"]
+    C, S, table = _experts(m, "gu")
+    pd = _plan_dev({"seg_off": plan["seg_off"], "row_src": plan["row_src"]})
+    X = m["X"].reshape(T, H)
+    Y = torch.full((R, 2 * I), float("nan"), device="cuda")
+    if mode == "exact":
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], pd["row_src"], T, dev(X), None, Y, 2 * I, H, R, E, mode)
+        Xo, xt = X[plan["row_src"]], "f32"
+    else:
+        Xh = torch.empty((R, H), dtype=torch.int16, device="cuda")
+        rs = torch.empty(R, dtype=torch.float32, device="cuda")
+        qg.qg_x_half(dev(X), T, pd["row_src"], R, H, Xh, rs)
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], None, R, Xh.view(torch.float16), rs, Y, 2 * I, H, R, E,
+                             mode)
+        Xo, xt = X[plan["row_src"]], "f32"
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    seg = plan["seg_off"]
+    for e in range(E):
+        r0, r1 = seg[e], seg[e + 1]
+        if r0 == r1:
+            continue
+        Yr, Sr, _ = orc.gemm("q4", m["gu_codes"][e], m["gu_scales"][e], None, 64, 2 * I, H, Xo[r0:r1], xt, r1 - r0)
+        check_tol(y[r0:r1], Yr, Sr, TAU[mode], f"expert {e}")
+    assert seg[6] - seg[5] == 0
+
+
+@pytest.mark.parametrize("at", ["f32", "f16"])
+def test_swiglu(orc, at):
+    R, I = 9, 200
+    GU = synth.normal_as(8, 3, R * 2 * I, 0, 2, "f32").reshape(R, 2 * I)
+    GU[3] *= 1e4
+    GU[4] = 0
+    A = torch.empty((R, I), dtype=torch.float32 if at == "f32" else torch.int16, device="cuda")
+    rs = torch.empty(R, device="cuda")
+    qg.qg_swiglu(dev(GU), R, I, A, qg.QG_X_F32 if at == "f32" else qg.QG_X_F16, rs if at == "f16" else None)
+    torch.cuda.synchronize()
+    ref = orc.swiglu(GU[:, :I].astype(np.float64), GU[:, I:].astype(np.float64))
+    if at == "f32":
+        a = A.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(a - ref) <= 4e-6 * np.abs(ref) + 1e-30)
+    else:
+        a = A.cpu().numpy().view(np.uint16).view(np.float16).astype(np.float64)
+        r = rs.cpu().numpy().astype(np.float64)
+        amax = np.abs(a).max(axis=1)
+        nz = np.abs(ref).max(axis=1) > 0
+        assert np.all(amax[nz] >= 2.0**13) and np.all(amax[nz] < 2.0**14)
+        assert np.all(r[~nz] == 1.0)
+        assert np.all(np.log2(r) == np.round(np.log2(r)))
+        back = a * r[:, None]
+        assert np.all(np.abs(back - ref) <= 2.0**-11 * np.abs(ref) + 4e-6 * np.abs(ref) + 1e-30)
+
+
+def test_combine(orc):
+    T, k, H, R = 6, 3, 64, 18
+    O = synth.normal_as(9, 3, R * H, 0, 1, "f32").reshape(R, H)
+    rng = np.random.default_rng(0)
+    slot_row = rng.permutation(R).astype(np.int32)
+    slot_w = rng.uniform(0, 1, T * k).astype(np.float32)
+    y0 = synth.normal_as(9, 4, T * H, 0, 1, "f32").reshape(T, H)
+    for acc in (0, 1):
+        Y = dev(y0.copy())
+        qg.qg_moe_combine(dev(O), R, dev(slot_row), dev(slot_w), Y, H, T, k, acc)
+        torch.cuda.synchronize()
+        yr, b = orc.moe_combine(O.astype(np.float64), H, slot_row, slot_w.astype(np.float64), T, k)
+        if acc:
+            yr = yr + y0
+            b = b + np.abs(y0)
+        check_tol(Y.cpu().numpy(), yr, b, 1e-6, f"combine acc={acc}")
+
+
+def _ffn(orc, E, H, I, T, k, seed, mode, unused=None, sample=None):
+    m = synth.make_moe(E, H, I, T, seed)
+    lg = m["logits"].reshape(T, E).copy()
+    if unused is not None:
+        lg[:, unused] = -1e9
+    plan = orc.moe_plan(lg, T, E, k)
+    hp = qg.qg_moe_plan_host(lg, T, E, k)
+    for key in ("seg_off", "row_src", "slot_row"):
+        assert np.array_equal(hp[key], plan[key])
+    Cg, Sg, tg = _experts(m, "gu")
+    Cd, Sd, td = _experts(m, "dn")
+    pd = _plan_dev({k2: hp[k2] for k2 in ("seg_off", "row_src", "slot_row", "slot_w")})
+    ws_bytes = qg.qg_moe_ffn_workspace(H, I, T, k, mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    Y = torch.zeros((T, H), device="cuda")
+    qg.qg_moe_ffn("q4", tg, td, 64, E, H, I, dev(m["X"].reshape(T, H)), T, k, pd["seg_off"], pd["row_src"],
+                  pd["slot_row"], pd["slot_w"], Y, 0, mode, ws, ws_bytes)
+    torch.cuda.synchronize()
+    ref = orc.moe_ffn(m, plan)
+    return Y.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_ffn_small_design(orc, mode):
+    """8 experts, h = 128, mi = 64, t = 75, two routes per token, one expert unused (the MoE test design
+    of oxinfer src/metal.rs, tests: mma_moe_matches_cpu), end to end against the oracle's bound."""
+    y, ref = _ffn(orc, 8, 128, 64, 75, 2, 7, mode, unused=5)
+    check_tol(y, ref["y"], ref["bound"], 2 * TAU[mode], f"ffn small {mode}")
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_ffn_full_workload(orc, mode):
+    """128 experts, H 2048, I 1536, 32 tokens, top-8: the whole chain against the oracle."""
+    c = synth.CONFIGS[4]
+    print(f"moe workload {c.name} {mode}", flush=True)
+    y, ref = _ffn(orc, c.extra["experts"], c.N, c.extra["inter"], c.T, c.extra["top_k"], c.seed, mode)
+    check_tol(y, ref["y"], ref["bound"], 2 * TAU[mode], f"ffn full {mode}")
