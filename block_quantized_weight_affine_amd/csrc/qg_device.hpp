@@ -43,6 +43,14 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// The staged 16-bit value is the nearest-even rounding of the f32 value.  Keeping the f32 value
+// materialised stops the compiler from folding the f32 multiply-add and the narrowing into one
+// mixed-precision FMA with a 16-bit result, which rounds the exact result once and so differs
+// from the f32-then-narrow sequence on ties.
+__device__ __forceinline__ float keep_f32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 template <int ST>
 __device__ __forceinline__ uint16_t f32_to_16(float f) {
     return ST == XT_F16 ? f32_to_f16_bits(f) : f32_to_bf16_bits(f);
@@ -135,7 +143,7 @@ __device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int s = 0; s < 8; s++) f[j][s] = (short)f32_to_16<ST>(block_value<FMT>(r, 8 * j + s));
+        for (int s = 0; s < 8; s++) f[j][s] = (short)f32_to_16<ST>(keep_f32(block_value<FMT>(r, 8 * j + s)));
 }
 
 // ---- activations ---------------------------------------------------------------------------------

@@ -102,8 +102,12 @@ __global__ __launch_bounds__(256) void x_half_kernel(const float* X, int x_rows,
     uint2* out = (uint2*)(Xh + (size_t)r * K);
     for (int i = threadIdx.x; i < n4; i += 256) {
         float4 v = valid ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        const uint32_t a = (uint32_t)f32_to_f16_bits(v.x * sc) | ((uint32_t)f32_to_f16_bits(v.y * sc) << 16);
-        const uint32_t b = (uint32_t)f32_to_f16_bits(v.z * sc) | ((uint32_t)f32_to_f16_bits(v.w * sc) << 16);
+        // f32 product, then nearest-even narrowing (keep_f32 stops a fused multiply-add with a +0
+        // addend, which would turn -0 into +0, and a one-rounding mixed-precision form)
+        const uint32_t a = (uint32_t)f32_to_f16_bits(keep_f32(v.x * sc)) |
+                           ((uint32_t)f32_to_f16_bits(keep_f32(v.y * sc)) << 16);
+        const uint32_t b = (uint32_t)f32_to_f16_bits(keep_f32(v.z * sc)) |
+                           ((uint32_t)f32_to_f16_bits(keep_f32(v.w * sc)) << 16);
         out[i] = make_uint2(a, b);
     }
     if (threadIdx.x == 0) rs[r] = ldexpf(1.0f, -e);
@@ -146,10 +150,10 @@ __global__ __launch_bounds__(256) void swiglu_f16_kernel(const float* GU, int I,
     uint2* out = (uint2*)(A + (size_t)r * I);
     for (int i = threadIdx.x; i < (I >> 2); i += 256) {
         const float4 gv = g[i], uv = u[i];
-        const uint32_t a = (uint32_t)f32_to_f16_bits(silu_mul(gv.x, uv.x) * sc) |
-                           ((uint32_t)f32_to_f16_bits(silu_mul(gv.y, uv.y) * sc) << 16);
-        const uint32_t b = (uint32_t)f32_to_f16_bits(silu_mul(gv.z, uv.z) * sc) |
-                           ((uint32_t)f32_to_f16_bits(silu_mul(gv.w, uv.w) * sc) << 16);
+        const uint32_t a = (uint32_t)f32_to_f16_bits(keep_f32(silu_mul(gv.x, uv.x) * sc)) |
+                           ((uint32_t)f32_to_f16_bits(keep_f32(silu_mul(gv.y, uv.y) * sc)) << 16);
+        const uint32_t b = (uint32_t)f32_to_f16_bits(keep_f32(silu_mul(gv.z, uv.z) * sc)) |
+                           ((uint32_t)f32_to_f16_bits(keep_f32(silu_mul(gv.w, uv.w) * sc)) << 16);
         out[i] = make_uint2(a, b);
     }
     if (threadIdx.x == 0) rs[r] = ldexpf(1.0f, -e);

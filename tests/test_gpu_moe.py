@@ -24,7 +24,9 @@ def test_x_half_bit_exact(orc):
     Xz = np.concatenate([X, np.zeros((1, K), np.float32)])
     srcz = np.where((src >= 0) & (src < T), src, T)
     xh_ref, rs_ref = orc.x_half(Xz, K, src=srcz)
-    assert np.array_equal(Xh.cpu().numpy().view(np.uint16), xh_ref)
+    got = Xh.cpu().numpy().view(np.uint16)
+    bad = np.argwhere(got != xh_ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}: {got[tuple(bad[0])]:#06x} vs {xh_ref[tuple(bad[0])]:#06x}"
     assert np.array_equal(rs.cpu().numpy(), rs_ref)
 
 
