@@ -1,0 +1,267 @@
+"""Benchmark of the block-quantized weight matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-also] [--no-cpu]
+
+Prints ONE JSON line.  The headline workload (`value`) is the T = 1 Q8 GEMV decode (N = K = 4096,
+int8 weights with f32 block scales, f32 activations), reported in HBM GB/s of algorithmic bytes
+(codes + scales + X + Y) per step; each step reads the next of 16 weight copies (302 MB > the 256 MB
+Infinity Cache) so the bytes come from HBM.  The timed region holds exactly K steps bracketed by
+torch.cuda.synchronize(); HIP events on the launch stream time it.  `roofline` relates the dominant
+kernel's achieved rate to the chip's peak; `cpu_baseline` times the CPU oracle on the host cores.
+`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak) and the MoE expert block (GB/s), each on
+its own synthetic workload; `--workload` selects one of them as the headline instead.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm": 8000.0, "f32": 157.3, "f16": 2500.0, "bf16": 2500.0}   # GB/s, TFLOP/s (dense)
+
+WORKLOADS = {
+    # name: (config index, mode)
+    "q8_gemv_decode": (1, "exact"),
+    "q4_tiny_exact": (0, "exact"),
+    "q4_prefill_exact": (2, "exact"),
+    "q4_prefill_fast": (2, "fast"),
+    "q4a_upproj_fast": (3, "fast"),
+    "moe_block_exact": (4, "exact"),
+    "moe_block_fast": (4, "fast"),
+}
+HEADLINE = "q8_gemv_decode"
+KERNEL_SOURCES = ["qg_device.hpp", "qg_internal.hpp", "qg_gemm.hip", "qg_gemv.hip", "qg_misc.hip", "qg_capi.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_quantized_weight_affine_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def _timed(fn, steps: int, warmup: int):
+    """Runs fn(i) warmup times, then times exactly `steps` calls with events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+# ---------------------------------------------------------------------------------------------------
+def setup_dense(ci: int, mode: str, copies: int):
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    c = synth.CONFIGS[ci]
+    w = synth.make_dense(c.fmt, c.N, c.K, c.T, c.xtype, c.x_sigma, c.seed, group=c.group)
+    codes = [_dev(w["codes"]) for _ in range(copies)]
+    scales = [_dev(w["scales"]) for _ in range(copies)]
+    offs = [_dev(w["offsets"]) for _ in range(copies)] if c.fmt == "q4a" else [None] * copies
+    X = _dev(w["X"])
+    if c.xtype == "bf16":
+        X = X.view(torch.bfloat16)
+    Y = torch.empty((c.T, c.N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        j = i % copies
+        qg.qgemm(c.fmt, codes[j], scales[j], offs[j], c.group, X, Y, c.N, c.K, c.T, mode)
+
+    wbytes = w["codes"].nbytes + w["scales"].nbytes + (w["offsets"].nbytes if c.fmt == "q4a" else 0)
+    xbytes = w["X"].nbytes
+    ybytes = c.T * c.N * 4
+    info = {
+        "name": c.name, "cfg": c, "mode": mode, "flops": 2.0 * c.T * c.N * c.K,
+        "bytes": float(wbytes + xbytes + ybytes), "copies": copies, "weights": w,
+        "dtype": ("f32" if mode == "exact" else c.xtype),
+        "kernel": ("gemv_kernel" if c.T <= 8 else ("gemm_exact_kernel" if mode == "exact" else "gemm_fast_kernel")),
+    }
+    return step, info
+
+
+def setup_moe(mode: str):
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    c = synth.CONFIGS[4]
+    E, H, I, T, k = c.extra["experts"], c.N, c.extra["inter"], c.T, c.extra["top_k"]
+    m = synth.make_moe(E, H, I, T, c.seed)
+    t0 = time.perf_counter()
+    plan = qg.qg_moe_plan_host(m["logits"].reshape(T, E), T, E, k)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    G, GS = _dev(m["gu_codes"]), _dev(m["gu_scales"])
+    D, DS = _dev(m["dn_codes"]), _dev(m["dn_scales"])
+    tg = qg.expert_table([(G[e], GS[e], None) for e in range(E)])
+    td = qg.expert_table([(D[e], DS[e], None) for e in range(E)])
+    pd = {key: _dev(plan[key]) for key in ("seg_off", "row_src", "slot_row", "slot_w")}
+    X = _dev(m["X"].reshape(T, H))
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws_bytes = qg.qg_moe_ffn_workspace(H, I, T, k, mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        qg.qg_moe_ffn("q4", tg, td, 64, E, H, I, X, T, k, pd["seg_off"], pd["row_src"], pd["slot_row"],
+                      pd["slot_w"], Y, 0, mode, ws, ws_bytes)
+
+    used = int(np.count_nonzero(np.diff(plan["seg_off"])))
+    gu_b = m["gu_codes"][0].nbytes + m["gu_scales"][0].nbytes
+    dn_b = m["dn_codes"][0].nbytes + m["dn_scales"][0].nbytes
+    info = {
+        "name": c.name, "cfg": c, "mode": mode, "flops": 2.0 * T * k * (2 * I * H + H * I),
+        "bytes": float(used * (gu_b + dn_b) + 2 * T * H * 4), "used_experts": used, "plan_host_ms": plan_ms,
+        "copies": 1, "dtype": "f32" if mode == "exact" else "f16",
+        "kernel": "gemv_kernel" if mode == "exact" else "gemm_fast_kernel",
+    }
+    return step, info
+
+
+def setup(name: str):
+    ci, mode = WORKLOADS[name]
+    if ci == 4:
+        return setup_moe(mode)
+    copies = 16 if ci == 1 else 1
+    return setup_dense(ci, mode, copies)
+
+
+def measure(name: str, steps: int, warmup: int) -> dict:
+    step, info = setup(name)
+    ms, wall = _timed(step, steps, warmup)
+    c = info["cfg"]
+    out = {"workload": name, "config": info["name"], "mode": info["mode"], "ms_per_step": ms,
+           "us_per_step": ms * 1e3, "dtype": info["dtype"], "kernel": info["kernel"]}
+    if c.index in (1, 4):
+        gbs = info["bytes"] / (ms * 1e-3) / 1e9
+        out.update({"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
+                    "bytes_per_step": info["bytes"]})
+        if c.index == 4:
+            out.update({"used_experts": info["used_experts"], "plan_host_ms": info["plan_host_ms"],
+                        "tflops": info["flops"] / (ms * 1e-3) / 1e12})
+    else:
+        tf = info["flops"] / (ms * 1e-3) / 1e12
+        pk = PEAK["f32"] if info["mode"] == "exact" else PEAK[c.xtype]
+        out.update({"value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": pk, "frac": tf / pk,
+                    "flops_per_step": info["flops"]})
+    out["_info"] = info
+    return out
+
+
+# ---------------------------------------------------------------------------------------------------
+def cpu_baseline(info: dict, budget_s: float = 12.0) -> dict:
+    """The CPU oracle (plain C, f64) as it stands, on this host's cores, over a bounded sample."""
+    import oracle
+    c = info["cfg"]
+    w = info["weights"]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
+                w["X"].view(np.uint16) if c.xtype != "f32" else w["X"], c.xtype, c.T, threads=threads)
+    one = time.perf_counter() - t0
+    reps = max(1, min(50, int(budget_s / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        _, _, used = oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
+                                 w["X"].view(np.uint16) if c.xtype != "f32" else w["X"], c.xtype, c.T,
+                                 threads=threads)
+    dt = (time.perf_counter() - t0) / reps
+    if c.index == 1:
+        value, unit = info["bytes"] / dt / 1e9, "GB/s"
+    else:
+        value, unit = info["flops"] / dt / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(used), "kind": "oracle",
+            "sample": f"the whole workload ({c.N} rows x K {c.K}, T {c.T}), {reps} repeats, {dt * 1e3:.1f} ms each"}
+
+
+def traffic_for(name: str, info: dict, ms: float) -> float | None:
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return float(t["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    head = measure(args.workload, args.steps, args.warmup)
+    info = head.pop("_info")
+    roofline = {"bound": head["bound"], "achieved": head["value"], "peak": head["peak"],
+                "unit": head["unit"], "frac": head["frac"], "traffic": traffic_for(args.workload, info,
+                                                                                 head["ms_per_step"]),
+                "kernel": head["kernel"], "per_launch": (info["bytes"] if head["unit"] == "GB/s" else info["flops"])}
+    cpu = None
+    if not args.no_cpu and info["cfg"].index != 4:
+        cpu = cpu_baseline(info)
+    also = []
+    if not args.no_also:
+        for name in WORKLOADS:
+            if name == args.workload:
+                continue
+            st = 200 if "moe" in name or "prefill" in name or "upproj" in name else 500
+            r = measure(name, st, 20)
+            r.pop("_info")
+            also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+            torch.cuda.empty_cache()
+    c = info["cfg"]
+    line = {
+        "metric": "TFLOP/s (prefill qgemm) & HBM GB/s (T=1 qgemv), as % of MI355X roofline",
+        "value": round(head["value"], 3), "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+        "config": {"workload": head["config"], "format": c.fmt, "mode": head["mode"], "N": c.N, "K": c.K,
+                   "T": c.T, "x_dtype": c.xtype, "weight_copies": info["copies"], "parallelism": "single GPU"},
+        "roofline": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in roofline.items()},
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -27,6 +27,14 @@ _i = C.c_int
 _sz = C.c_size_t
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the CPU share this process is meant to use (OMP_NUM_THREADS when
+    set, else the core count), at most 16."""
+    n = os.environ.get("OMP_NUM_THREADS")
+    n = int(n) if n and n.isdigit() else (os.cpu_count() or 1)
+    return max(1, min(n, 16))
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -152,7 +160,7 @@ def gemm(fmt, codes, scales, offsets, group, N, K, X, xtype, T, ns=None, ts=None
     Y = np.empty((nt, nn), np.float64)
     S = np.empty((nt, nn), np.float64)
     if threads is None:
-        threads = os.cpu_count() or 1
+        threads = default_threads()
     used = lib().orc_gemm(FMT[fmt], _ptr(c), _ptr(s), _ptr(o), group, N, K, _ptr(x), XT[xtype], T,
                           _ptr(nsa), nn, _ptr(tsa), nt, _ptr(Y), _ptr(S), int(threads))
     return Y, S, used
