@@ -1,29 +1,39 @@
-// qg_gemv.hip -- wavefront-reduction GEMV for T <= 8 rows of X, exact f32 arithmetic.
+// qg_gemv.hip -- wavefront-reduction GEMV for at most 8 rows of X, exact f32 arithmetic.
 //
 // Prior art: page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", q4rows (a narrow kernel that
 // takes at most 8 rows per dispatch, measured faster than tile GEMMs for expert panels) and the
 // memory-bound-decode notes of "oxinfer 0.0.5 src/metal.rs" (module notes).  The layout here:
 //
-//  * A wavefront owns RW consecutive weight rows and walks K in steps of 64 "units" of 16
-//    elements, one unit per lane per row: Q4 / Q4A unit u is the 8 code bytes 8u..8u+7 of the
-//    row (half of block u/2: low nibbles are elements 32b+8h..+7, high nibbles 32b+16+8h..+7 with
-//    b = u/2, h = u%2); Q8 unit u is the 16 code bytes 16u..16u+15.  Consecutive lanes read
-//    consecutive bytes, so every load instruction of a wavefront is one contiguous 512 B (Q4) or
-//    1 KiB (Q8) run of the row.
-//  * The lane's slice of each X row (16 values per unit) is loaded once per step and reused by
-//    all RW rows; loads of U steps are issued before any arithmetic.
-//  * Q4 / Q8: the f32 partial sum of (nibble - 8) * x (or q * x) over the unit is multiplied by the
-//    block scale once (the block scale applied to the f32 partial).  Q4A: each weight is decoded
-//    to its f32 value (nibble - 8) * d + m first.
-//  * After K, each accumulator is reduced across the 64 lanes with xor-shuffles.
-//  * Grouped launches (exact-mode MoE): blockIdx.y is the expert; the block walks the expert's
+//  * A workgroup is 4 wavefronts; wavefront w owns RW consecutive weight rows.  K is walked in
+//    steps of 64 "units" of 16 elements, one unit per lane per row: Q4 / Q4A unit u is the 8 code
+//    bytes 8u..8u+7 of the row (half of block u/2: low nibbles are elements 32b+8h..+7, high
+//    nibbles 32b+16+8h..+7 with b = u/2, h = u%2); Q8 unit u is the 16 code bytes 16u..16u+15.
+//    Consecutive lanes read consecutive bytes, so each load instruction of a wavefront is one
+//    contiguous 512 B (Q4) or 1 KiB (Q8) run of a row.
+//  * X rows are staged once per workgroup in LDS as f32, in K chunks of at most 16384 values in
+//    all; the chunk's X loads are issued first, then every weight load of the chunk, so the X
+//    store to LDS waits only for X while the weights stream in.
+//  * Per unit and X row: Sx = sum of the 16 x values; per weight row the f32 partial
+//    P = sum c_i x_i over the unit's codes c_i (Q4: nibbles; Q8: the byte XOR 0x80, i.e. q + 128,
+//    converted with one instruction), then acc += d (P - 8 Sx) [+ m Sx] (Q8: d (P - 128 Sx)) --
+//    the block scale applied to the f32 partial.
+//  * After K, each accumulator is reduced across the 64 lanes with xor shuffles.
+//  * Grouped launches (exact-mode MoE): blockIdx.y is the expert; the workgroup walks the expert's
 //    row segment in chunks of at most 8 rows.
+#include <algorithm>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
 namespace qg {
 
 constexpr int kGemvThreads = 256;
+
+template <int NT>
+struct GemvChunk {
+    static constexpr int steps = NT <= 4 ? 4 : 2;  // 1024-element steps per chunk
+    static constexpr int kc = 1024 * steps;        // NT * kc <= 16384 f32 values (64 KiB of LDS)
+};
 
 template <int FMT>
 struct Unit;
@@ -49,20 +59,23 @@ __device__ __forceinline__ Unit<FMT> load_unit(const void* codes, const void* sc
     Unit<FMT> r;
     const size_t bi = (size_t)n * (size_t)(K >> 5) + (size_t)(u >> 1);
     if constexpr (FMT == FMT_Q8) {
-        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)((const int8_t*)codes + (size_t)n * K + (size_t)u * 16));
+        const u32x4_t v =
+            __builtin_nontemporal_load((const u32x4_t*)((const int8_t*)codes + (size_t)n * K + (size_t)u * 16));
         r.q = make_uint4(v.x, v.y, v.z, v.w);
         r.d = ((const float*)scales)[bi];
         r.m = 0.f;
     } else {
-        const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)((const uint8_t*)codes + (size_t)n * (K >> 1) + (size_t)u * 8));
+        const u32x2_t v =
+            __builtin_nontemporal_load((const u32x2_t*)((const uint8_t*)codes + (size_t)n * (K >> 1) + (size_t)u * 8));
         r.q = make_uint2(v.x, v.y);
         r.d = f16_to_f32(((const uint16_t*)scales)[bi]);
-        r.m = FMT == FMT_Q4A ? bf16_to_f32(offs[(size_t)n * (size_t)(K / group) + (size_t)((u >> 1) * 32 / group)]) : 0.f;
+        r.m = FMT == FMT_Q4A ? bf16_to_f32(offs[(size_t)n * (size_t)(K / group) + (size_t)((u >> 1) * 32 / group)])
+                             : 0.f;
     }
     return r;
 }
 
-// Element offsets of unit u's 16 values: two runs of 8 starting at k0 and k1.
+// Element offsets (within the row) of unit u's two runs of 8 values.
 template <int FMT>
 __device__ __forceinline__ void unit_runs(int u, int& k0, int& k1) {
     if constexpr (FMT == FMT_Q8) {
@@ -75,50 +88,48 @@ __device__ __forceinline__ void unit_runs(int u, int& k0, int& k1) {
     }
 }
 
-// Sum over the unit of w(i) * x[i] with x[0..7] at run k0 and x[8..15] at run k1.
+// sum_i c_i x_i over the unit's 16 codes: Q4 nibbles (x[0..7] low, x[8..15] high), Q8 q + 128.
 template <int FMT>
-__device__ __forceinline__ float unit_dot(const Unit<FMT>& w, const float (&x)[16]) {
+__device__ __forceinline__ float unit_partial(const Unit<FMT>& w, const float (&x)[16]) {
+    float p = 0.f;
     if constexpr (FMT == FMT_Q8) {
-        const uint32_t ws[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
-        float p = 0.f;
+        const uint32_t ws[4] = {w.q.x ^ 0x80808080u, w.q.y ^ 0x80808080u, w.q.z ^ 0x80808080u, w.q.w ^ 0x80808080u};
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int q = (int)(int8_t)((ws[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-            p = fmaf((float)q, x[i], p);
-        }
-        return p * w.d;
-    } else if constexpr (FMT == FMT_Q4) {
-        const uint32_t ws[2] = {w.q.x, w.q.y};
-        float p = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t byte = (ws[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            p = fmaf((float)(byte & 15u) - 8.0f, x[i], p);
-            p = fmaf((float)(byte >> 4) - 8.0f, x[8 + i], p);
-        }
-        return p * w.d;
+        for (int i = 0; i < 16; i++) p = fmaf((float)((ws[i >> 2] >> (8 * (i & 3))) & 0xFFu), x[i], p);
     } else {
-        const uint32_t ws[2] = {w.q.x, w.q.y};
-        float p = 0.f;
+        const uint32_t lo[2] = {w.q.x & 0x0F0F0F0Fu, w.q.y & 0x0F0F0F0Fu};
+        const uint32_t hi[2] = {(w.q.x >> 4) & 0x0F0F0F0Fu, (w.q.y >> 4) & 0x0F0F0F0Fu};
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t byte = (ws[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            const float lo = fmaf((float)(byte & 15u) - 8.0f, w.d, w.m);
-            const float hi = fmaf((float)(byte >> 4) - 8.0f, w.d, w.m);
-            p = fmaf(lo, x[i], p);
-            p = fmaf(hi, x[8 + i], p);
-        }
-        return p;
+        for (int i = 0; i < 8; i++) p = fmaf((float)((lo[i >> 2] >> (8 * (i & 3))) & 0xFFu), x[i], p);
+#pragma unroll
+        for (int i = 0; i < 8; i++) p = fmaf((float)((hi[i >> 2] >> (8 * (i & 3))) & 0xFFu), x[8 + i], p);
     }
+    return p;
 }
 
-// RW weight rows starting at nrow0, NT X rows (xrow[t], -1 = zero row), outputs at Y rows yrow0 + t.
+// Contribution of one unit: the block scale (and offset) applied to the f32 partial.
+template <int FMT>
+__device__ __forceinline__ float unit_value(const Unit<FMT>& w, float p, float sx) {
+    if constexpr (FMT == FMT_Q8)
+        return w.d * fmaf(-128.0f, sx, p);
+    else if constexpr (FMT == FMT_Q4)
+        return w.d * fmaf(-8.0f, sx, p);
+    else
+        return fmaf(w.d, fmaf(-8.0f, sx, p), w.m * sx);
+}
+
+// RW weight rows starting at nrow0; NT X rows (xrow[t], -1 = zero row) -> Y rows yrow0 + t.
 template <int FMT, int XT, int RW, int NT>
 __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes, const void* scales,
-                                          const uint16_t* offs, int nrow0, int yrow0, const int* xrow) {
-    constexpr int U = NT == 1 ? 4 : (NT == 2 ? 2 : 1);
+                                          const uint16_t* offs, int nrow0, int yrow0, const int* xrow, float* xs) {
+    constexpr int S = GemvChunk<NT>::steps;
+    constexpr int KC = GemvChunk<NT>::kc;
+    constexpr int G = (16 / RW) < S ? (16 / RW) : S;                     // steps whose loads are in flight together
+    constexpr int XV = (XT == XT_F32) ? 4 : 8;                          // X values per 16-byte load
+    constexpr int XL = (NT * KC / XV + kGemvThreads - 1) / kGemvThreads;  // X loads per thread per chunk
     const int lane = threadIdx.x & 63;
     const int K = p.K, units = K >> 4;
+    const int KS = min(K, KC);  // LDS row stride of the staged X chunk
     int rows[RW];
 #pragma unroll
     for (int r = 0; r < RW; r++) rows[r] = min(nrow0 + r, p.N - 1);
@@ -128,42 +139,96 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[r][t] = 0.f;
 
-    for (int u0 = 0; u0 < units; u0 += 64 * U) {
-        Unit<FMT> w[U][RW];
-        float x[U][NT][16];
-        bool ok[U];
+    for (int k0 = 0; k0 < K; k0 += KC) {
+        const int kn = min(KC, K - k0);
+        const int u0 = k0 >> 4;
+        const int nsteps = (kn + 1023) >> 10;
+        // 1. X loads of the chunk (16 bytes each): load i covers values [e, e + XV) of X row t of
+        //    the chunk, with c = tid + i * threads, t = c / (kn / XV), e = XV * (c % (kn / XV)).
+        uint4 xl[XL];
+        const int per_row = kn / XV;
 #pragma unroll
-        for (int j = 0; j < U; j++) {
-            const int u = u0 + 64 * j + lane;
-            ok[j] = u < units;
-            const int uc = ok[j] ? u : units - 1;
+        for (int i = 0; i < XL; i++) {
+            const int c = threadIdx.x + i * kGemvThreads;
+            const int t = c / per_row, e = (c - t * per_row) * XV;
+            xl[i] = make_uint4(0, 0, 0, 0);
+            if (t < NT && xrow[t] >= 0) {
+                if constexpr (XT == XT_F32)
+                    xl[i] = *(const uint4*)((const float*)p.X + (size_t)xrow[t] * K + k0 + e);
+                else
+                    xl[i] = *(const uint4*)((const uint16_t*)p.X + (size_t)xrow[t] * K + k0 + e);
+            }
+        }
+        for (int g0 = 0; g0 < nsteps; g0 += G) {
+            // 2. the weight loads of G steps
+            Unit<FMT> w[G][RW];
 #pragma unroll
-            for (int r = 0; r < RW; r++) w[j][r] = load_unit<FMT>(codes, scales, offs, p.group, K, rows[r], uc);
-            int k0, k1;
-            unit_runs<FMT>(uc, k0, k1);
+            for (int j = 0; j < G; j++) {
+                const int u = min(u0 + 64 * (g0 + j) + lane, units - 1);
 #pragma unroll
-            for (int t = 0; t < NT; t++) {
-                if (xrow[t] >= 0 && ok[j]) {
-                    float a[8], b[8];
-                    x_load8<XT>(p.X, (size_t)xrow[t] * K + k0, a);
-                    x_load8<XT>(p.X, (size_t)xrow[t] * K + k1, b);
+                for (int r = 0; r < RW; r++) w[j][r] = load_unit<FMT>(codes, scales, offs, p.group, K, rows[r], u);
+            }
+            if (g0 == 0) {
+                // 3. X to LDS as f32: X row t of the chunk at xs[t * KS + e]
 #pragma unroll
-                    for (int i = 0; i < 8; i++) {
-                        x[j][t][i] = a[i];
-                        x[j][t][8 + i] = b[i];
+                for (int i = 0; i < XL; i++) {
+                    const int c = threadIdx.x + i * kGemvThreads;
+                    const int t = c / per_row, e = (c - t * per_row) * XV;
+                    if (t < NT) {
+                        float4* d = (float4*)(xs + t * KS + e);
+                        if constexpr (XT == XT_F32) {
+                            d[0] = make_float4(__uint_as_float(xl[i].x), __uint_as_float(xl[i].y),
+                                               __uint_as_float(xl[i].z), __uint_as_float(xl[i].w));
+                        } else {
+                            const uint32_t q[4] = {xl[i].x, xl[i].y, xl[i].z, xl[i].w};
+                            float v[8];
+#pragma unroll
+                            for (int h = 0; h < 4; h++) {
+                                if constexpr (XT == XT_F16) {
+                                    v[2 * h] = f16_to_f32((uint16_t)(q[h] & 0xFFFFu));
+                                    v[2 * h + 1] = f16_to_f32((uint16_t)(q[h] >> 16));
+                                } else {
+                                    v[2 * h] = __uint_as_float(q[h] << 16);
+                                    v[2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
+                                }
+                            }
+                            d[0] = make_float4(v[0], v[1], v[2], v[3]);
+                            d[1] = make_float4(v[4], v[5], v[6], v[7]);
+                        }
                     }
-                } else {
+                }
+                __syncthreads();
+            }
+            // 4. arithmetic of the G steps
 #pragma unroll
-                    for (int i = 0; i < 16; i++) x[j][t][i] = 0.f;
+            for (int j = 0; j < G; j++) {
+                const int u = u0 + 64 * (g0 + j) + lane;
+                if (g0 + j < nsteps && u < units) {
+                    int e0, e1;
+                    unit_runs<FMT>(u, e0, e1);
+                    e0 -= k0;
+                    e1 -= k0;
+#pragma unroll
+                    for (int t = 0; t < NT; t++) {
+                        float x[16];
+                        const float4* a = (const float4*)(xs + t * KS + e0);
+                        const float4* b = (const float4*)(xs + t * KS + e1);
+                        const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+                        x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+                        x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+                        x[8] = b0.x; x[9] = b0.y; x[10] = b0.z; x[11] = b0.w;
+                        x[12] = b1.x; x[13] = b1.y; x[14] = b1.z; x[15] = b1.w;
+                        float sx = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 16; i++) sx += x[i];
+#pragma unroll
+                        for (int r = 0; r < RW; r++)
+                            acc[r][t] += unit_value<FMT>(w[j][r], unit_partial<FMT>(w[j][r], x), sx);
+                    }
                 }
             }
         }
-#pragma unroll
-        for (int j = 0; j < U; j++)
-#pragma unroll
-            for (int r = 0; r < RW; r++)
-#pragma unroll
-                for (int t = 0; t < NT; t++) acc[r][t] += unit_dot<FMT>(w[j][r], x[j][t]);
+        __syncthreads();  // the next chunk (or the next rows' chunk) overwrites xs
     }
 
 #pragma unroll
@@ -172,15 +237,16 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
         for (int t = 0; t < NT; t++) {
             const float v = wave_sum(acc[r][t]);
             const int n = nrow0 + r;
-            float sc = 1.f;
-            if (p.rs) sc = p.rs[yrow0 + t];
-            if (lane == ((r * NT + t) & 63) && n < p.N) p.Y[(size_t)(yrow0 + t) * p.N + n] = v * sc;
+            if (lane == ((r * NT + t) & 63) && n < p.N) {
+                const float sc = p.rs ? p.rs[yrow0 + t] : 1.f;
+                p.Y[(size_t)(yrow0 + t) * p.N + n] = v * sc;
+            }
         }
 }
 
 template <int FMT, int XT, int RW, int NT>
 __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* codes, const void* scales,
-                                           const uint16_t* offs, int nrow0, int c) {
+                                           const uint16_t* offs, int nrow0, int c, float* xs) {
     int xrow[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) {
@@ -192,52 +258,89 @@ __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* code
         }
         xrow[t] = s;
     }
-    gemv_rows<FMT, XT, RW, NT>(p, codes, scales, offs, nrow0, c, xrow);
+    gemv_rows<FMT, XT, RW, NT>(p, codes, scales, offs, nrow0, c, xrow, xs);
 }
 
-template <int FMT, int XT, int RW>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p, bool grouped) {
+// NTD > 0: dense call with NTD = T rows of X (T <= 8).  NTD == 0: grouped call; blockIdx.y is the
+// expert and the workgroup walks the expert's rows in chunks of at most 8.
+template <int FMT, int XT, int RW, int NTD>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // gemv_lds_bytes()
     const int wave = threadIdx.x >> 6;
     const int nrow0 = (blockIdx.x * 4 + wave) * RW;
-    int r0 = 0, r1 = p.R;
-    const void* codes = p.codes;
-    const void* scales = p.scales;
-    const uint16_t* offs = p.offs;
-    if (grouped) {
+    // Every wavefront stays to the end (the X chunks are staged by the whole workgroup); rows
+    // beyond N are clamped on load and never stored.
+    if constexpr (NTD > 0) {
+        gemv_chunk<FMT, XT, RW, NTD>(p, p.codes, p.scales, p.offs, nrow0, 0, xs);
+    } else {
         const int e = blockIdx.y;
-        r0 = min(max(p.seg_off[e], 0), p.R);
-        r1 = min(max(p.seg_off[e + 1], r0), p.R);
-        codes = p.experts[e].codes;
-        scales = p.experts[e].scales;
-        offs = p.experts[e].offsets;
-    }
-    if (nrow0 >= p.N) return;  // whole wavefront beyond N (no barriers in this kernel)
-    for (int c = r0; c < r1; c += 8) {
-        switch (min(8, r1 - c)) {
-            case 1: gemv_chunk<FMT, XT, RW, 1>(p, codes, scales, offs, nrow0, c); break;
-            case 2: gemv_chunk<FMT, XT, RW, 2>(p, codes, scales, offs, nrow0, c); break;
-            case 3: gemv_chunk<FMT, XT, RW, 3>(p, codes, scales, offs, nrow0, c); break;
-            case 4: gemv_chunk<FMT, XT, RW, 4>(p, codes, scales, offs, nrow0, c); break;
-            case 5: gemv_chunk<FMT, XT, RW, 5>(p, codes, scales, offs, nrow0, c); break;
-            case 6: gemv_chunk<FMT, XT, RW, 6>(p, codes, scales, offs, nrow0, c); break;
-            case 7: gemv_chunk<FMT, XT, RW, 7>(p, codes, scales, offs, nrow0, c); break;
-            default: gemv_chunk<FMT, XT, RW, 8>(p, codes, scales, offs, nrow0, c); break;
+        const int r0 = min(max(p.seg_off[e], 0), p.R);
+        const int r1 = min(max(p.seg_off[e + 1], r0), p.R);
+        const void* codes = p.experts[e].codes;
+        const void* scales = p.experts[e].scales;
+        const uint16_t* offs = p.experts[e].offsets;
+        for (int c = r0; c < r1; c += 8) {
+            switch (min(8, r1 - c)) {
+                case 1: gemv_chunk<FMT, XT, RW, 1>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 2: gemv_chunk<FMT, XT, RW, 2>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 3: gemv_chunk<FMT, XT, RW, 3>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 4: gemv_chunk<FMT, XT, RW, 4>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 5: gemv_chunk<FMT, XT, RW, 5>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 6: gemv_chunk<FMT, XT, RW, 6>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 7: gemv_chunk<FMT, XT, RW, 7>(p, codes, scales, offs, nrow0, c, xs); break;
+                default: gemv_chunk<FMT, XT, RW, 8>(p, codes, scales, offs, nrow0, c, xs); break;
+            }
         }
     }
 }
 
+// LDS bytes for the X chunks: the largest NT * min(K, chunk(NT)) over the row counts NT a chunk of
+// output rows can have (dense: T; grouped: 1..8).
+template <int NT>
+static size_t chunk_floats(int K) {
+    return (size_t)NT * (size_t)std::min(K, GemvChunk<NT>::kc);
+}
+static size_t gemv_lds_bytes(int K, int nt_lo, int nt_hi) {
+    const size_t f[8] = {chunk_floats<1>(K), chunk_floats<2>(K), chunk_floats<3>(K), chunk_floats<4>(K),
+                         chunk_floats<5>(K), chunk_floats<6>(K), chunk_floats<7>(K), chunk_floats<8>(K)};
+    size_t m = 0;
+    for (int i = nt_lo - 1; i < nt_hi; i++) m = std::max(m, f[i]);
+    return 4 * m;
+}
+
+// Rows per wavefront: 1 for a single X row (most wavefronts in flight), more as X rows grow so
+// that the X staged per workgroup stays small next to the weights it serves.
+template <int FMT, int XT, int NT>
+static void gemv_dense(const GemmParams& p, hipStream_t s) {
+    constexpr int RW = NT == 1 ? 1 : NT == 2 ? 2 : 4;
+    dim3 grid((p.N + 4 * RW - 1) / (4 * RW));
+    hipLaunchKernelGGL((gemv_kernel<FMT, XT, RW, NT>), grid, dim3(kGemvThreads), gemv_lds_bytes(p.K, NT, NT), s, p);
+}
+
 template <int FMT, int XT>
-static void gemv_launch(const GemmParams& p, bool grouped, hipStream_t s) {
-    constexpr int RW = 2;
-    dim3 grid((p.N + 4 * RW - 1) / (4 * RW), grouped ? p.E : 1);
-    hipLaunchKernelGGL((gemv_kernel<FMT, XT, RW>), grid, dim3(kGemvThreads), 0, s, p, grouped);
+static void gemv_pick(const GemmParams& p, bool grouped, hipStream_t s) {
+    if (grouped) {
+        dim3 grid((p.N + 15) / 16, p.E);
+        hipLaunchKernelGGL((gemv_kernel<FMT, XT, 4, 0>), grid, dim3(kGemvThreads), gemv_lds_bytes(p.K, 1, 8), s, p);
+        return;
+    }
+    switch (p.R) {
+        case 1: return gemv_dense<FMT, XT, 1>(p, s);
+        case 2: return gemv_dense<FMT, XT, 2>(p, s);
+        case 3: return gemv_dense<FMT, XT, 3>(p, s);
+        case 4: return gemv_dense<FMT, XT, 4>(p, s);
+        case 5: return gemv_dense<FMT, XT, 5>(p, s);
+        case 6: return gemv_dense<FMT, XT, 6>(p, s);
+        case 7: return gemv_dense<FMT, XT, 7>(p, s);
+        default: return gemv_dense<FMT, XT, 8>(p, s);
+    }
 }
 
 template <int FMT>
 static void gemv_xt(int xt, const GemmParams& p, bool grouped, hipStream_t s) {
-    if (xt == XT_F32) gemv_launch<FMT, XT_F32>(p, grouped, s);
-    else if (xt == XT_F16) gemv_launch<FMT, XT_F16>(p, grouped, s);
-    else gemv_launch<FMT, XT_BF16>(p, grouped, s);
+    if (xt == XT_F32) gemv_pick<FMT, XT_F32>(p, grouped, s);
+    else if (xt == XT_F16) gemv_pick<FMT, XT_F16>(p, grouped, s);
+    else gemv_pick<FMT, XT_BF16>(p, grouped, s);
 }
 
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s) {
