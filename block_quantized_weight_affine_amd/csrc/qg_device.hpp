@@ -57,26 +57,26 @@ __device__ __forceinline__ uint16_t f32_to_16(float f) {
 }
 
 // ---- raw block of one row: the packed bytes and the block's scale (and offset) ------------------
-// Q4 / Q4A: 16 code bytes; Q8: 32 code bytes.
+// Q4 / Q4A: 16 code bytes; Q8: 32 code bytes.  dh keeps the f16 scale bits for the packed-f16 path.
 template <int FMT>
 struct RawBlock;
 template <>
 struct RawBlock<FMT_Q4> {
     uint4 q;
-    float d;
-    float m;
+    float d, m;
+    uint32_t dh;
 };
 template <>
 struct RawBlock<FMT_Q4A> {
     uint4 q;
-    float d;
-    float m;
+    float d, m;
+    uint32_t dh;
 };
 template <>
 struct RawBlock<FMT_Q8> {
     uint4 q0, q1;
-    float d;
-    float m;
+    float d, m;
+    uint32_t dh;
 };
 
 // Loads block b of row n (all addresses in bounds: the caller clamps n and b).
@@ -91,10 +91,12 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
         r.q1 = p[1];
         r.d = ((const float*)scales)[bi];
         r.m = 0.f;
+        r.dh = 0;
     } else {
         const uint4* p = (const uint4*)((const uint8_t*)codes + (size_t)n * (size_t)(K >> 1) + (size_t)b * 16);
         r.q = *p;
-        r.d = f16_to_f32(((const uint16_t*)scales)[bi]);
+        r.dh = ((const uint16_t*)scales)[bi];
+        r.d = f16_to_f32((uint16_t)r.dh);
         if constexpr (FMT == FMT_Q4A)
             r.m = bf16_to_f32(offs[(size_t)n * (size_t)(K / group) + (size_t)((b * 32) / group)]);
         else
@@ -103,47 +105,131 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
     return r;
 }
 
-// Code byte i (0..15) of a Q4 block.
-__device__ __forceinline__ uint32_t q4_byte(const uint4& q, int i) {
-    const uint32_t w = i < 4 ? q.x : i < 8 ? q.y : i < 12 ? q.z : q.w;
-    return (w >> (8 * (i & 3))) & 0xFFu;
-}
-
-// The f32 value of element e (0..31) of a block: exactly what the pages' decoders compute.
+// The code bytes of a block as "value bytes" c, one per element, in eight 32-bit words: element e
+// is byte e % 4 of word e / 4.  Q4: c = nibble (words 0..3 the low nibbles of bytes 0..15, words
+// 4..7 the high nibbles); Q8: c = q XOR 0x80 = q + 128.  Every element's f32 value is then
+//   w = fma(float(c), d, c0)                                                         (1)
+// with c0 = -8d (Q4), -128d (Q8) or m - 8d (Q4A): the exact value c*d + c0 is the pages' value
+// ((nibble - 8) d, q d or (nibble - 8) d + m), and one FMA rounds it once to f32 -- the same
+// rounding as the pages' f32 decode, since (nibble - 8) d is exact in f32 and q d is their only
+// rounding.  (1) is used for a block when its scale is positive (so a zero result has the
+// pages' sign) and, for Q4A, when m - 8d is itself exact in f32.  Otherwise (negative scales, or a
+// tiny offset next to a large scale) the block takes the pages' order of operations:
+// (c - 8) d, (c - 128) d, or fma(c - 8, d, m) -- the product is exact, so the fused add rounds as
+// the separate one.  The choice is made for the whole wavefront at once.
 template <int FMT>
-__device__ __forceinline__ float block_value(const RawBlock<FMT>& r, int e) {
+__device__ __forceinline__ void value_bytes(const RawBlock<FMT>& r, uint32_t (&c)[8]) {
     if constexpr (FMT == FMT_Q8) {
-        const uint4& q = e < 16 ? r.q0 : r.q1;
-        const int i = e & 15;
-        const uint32_t w = i < 4 ? q.x : i < 8 ? q.y : i < 12 ? q.z : q.w;
-        const int c = (int)(int8_t)((w >> (8 * (i & 3))) & 0xFFu);
-        return (float)c * r.d;
+        c[0] = r.q0.x ^ 0x80808080u; c[1] = r.q0.y ^ 0x80808080u; c[2] = r.q0.z ^ 0x80808080u; c[3] = r.q0.w ^ 0x80808080u;
+        c[4] = r.q1.x ^ 0x80808080u; c[5] = r.q1.y ^ 0x80808080u; c[6] = r.q1.z ^ 0x80808080u; c[7] = r.q1.w ^ 0x80808080u;
     } else {
-        const uint32_t byte = q4_byte(r.q, e & 15);
-        const uint32_t nib = e < 16 ? (byte & 15u) : (byte >> 4);
-        const float v = ((float)nib - 8.0f) * r.d;
-        if constexpr (FMT == FMT_Q4A)
-            return v + r.m;
-        else
-            return v;
+        const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            c[i] = w[i] & 0x0F0F0F0Fu;
+            c[4 + i] = (w[i] >> 4) & 0x0F0F0F0Fu;
+        }
     }
 }
 
-// Whole block to f32, element order.
+// c0 of (1) and whether (1) gives the pages' bits for this block.
+template <int FMT>
+__device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
+    fast = r.d > 0.0f;  // zero or negative scales (and NaN) take the pages' order
+    if constexpr (FMT == FMT_Q8) {
+        return -128.0f * r.d;
+    } else if constexpr (FMT == FMT_Q4) {
+        return -8.0f * r.d;
+    } else {
+        // TwoSum of m and -8d: the rounding error of s = m - 8d is zero iff s is exact.
+        const float a = r.m, b = keep_f32(-8.0f * r.d);
+        const float s = keep_f32(a + b);
+        const float bb = keep_f32(s - a);
+        const float err = (a - (s - bb)) + (b - bb);
+        fast = fast && err == 0.0f && isfinite(s);
+        return s;
+    }
+}
+
+// The pages' order of operations for one element (value byte as f32).
+template <int FMT>
+__device__ __forceinline__ float slow_value(const RawBlock<FMT>& r, float cf) {
+    if constexpr (FMT == FMT_Q8)
+        return (cf - 128.0f) * r.d;
+    else if constexpr (FMT == FMT_Q4)
+        return (cf - 8.0f) * r.d;
+    else
+        return fmaf(cf - 8.0f, r.d, r.m);
+}
+
+__device__ __forceinline__ float byte_f32(uint32_t word, int i) { return (float)((word >> (8 * i)) & 0xFFu); }
+
+// Whole block to f32 (element order): exact-mode staging.
 template <int FMT>
 __device__ __forceinline__ void block_to_f32(const RawBlock<FMT>& r, float (&v)[32]) {
+    uint32_t c[8];
+    value_bytes<FMT>(r, c);
+    bool fast;
+    const float c0 = block_c0<FMT>(r, fast);
+    if (__all(fast)) {
 #pragma unroll
-    for (int e = 0; e < 32; e++) v[e] = block_value<FMT>(r, e);
+        for (int e = 0; e < 32; e++) v[e] = fmaf(byte_f32(c[e >> 2], e & 3), r.d, c0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 32; e++) v[e] = keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3)));
+    }
 }
 
 // Fast-mode fragments: element 8j + s of the block, rounded to the staged 16-bit type ST, is
-// slot s of fragment j (j = 0..3).  Each fragment is one 8-wide operand of a 16-k MFMA step.
+// slot s of fragment j (j = 0..3); each fragment is one 8-wide operand of a 16-k MFMA step.
+// Q4 into f16: packed f16 arithmetic.  The half with bits 0x6400 | c is 1024 + c, so
+// (1024 + c) - 1032 = c - 8 exactly, and one f16 multiply by d rounds (c - 8) d -- exact in f32 --
+// once to nearest-even: the same bits as narrowing the f32 value.  Other cases: the f32 value of
+// (1), kept in a register, then narrowed (nearest-even).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
 template <int FMT, int ST>
 __device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_t (&f)[4]) {
+    uint32_t c[8];
+    value_bytes<FMT>(r, c);
+    if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
+        const half2_t d2 = __builtin_bit_cast(half2_t, r.dh | (r.dh << 16));
+        const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 4; j++) {
+            uint32_t o[4];
 #pragma unroll
-        for (int s = 0; s < 8; s++) f[j][s] = (short)f32_to_16<ST>(keep_f32(block_value<FMT>(r, 8 * j + s)));
+            for (int h = 0; h < 2; h++) {
+                const uint32_t wd = c[2 * j + h];
+                // halves (c0 | 0x6400, c1 | 0x6400) and (c2 | 0x6400, c3 | 0x6400)
+                const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, wd, 0x04010400u));
+                const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, wd, 0x04030402u));
+                o[2 * h] = __builtin_bit_cast(uint32_t, (lo - off) * d2);
+                o[2 * h + 1] = __builtin_bit_cast(uint32_t, (hi - off) * d2);
+            }
+            f[j] = __builtin_bit_cast(short8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        }
+    } else {
+        bool fast;
+        const float c0 = block_c0<FMT>(r, fast);
+        if (__all(fast)) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int s = 0; s < 8; s++) {
+                    const int e = 8 * j + s;
+                    f[j][s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[e >> 2], e & 3), r.d, c0)));
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int s = 0; s < 8; s++) {
+                    const int e = 8 * j + s;
+                    f[j][s] = (short)f32_to_16<ST>(keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3))));
+                }
+        }
+    }
 }
 
 // ---- activations ---------------------------------------------------------------------------------

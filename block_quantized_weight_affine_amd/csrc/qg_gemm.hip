@@ -84,8 +84,11 @@ __device__ __forceinline__ int x_row_of(const GemmParams& p, int r) {
 
 // ================================================================================================
 // Fast mode: f16 / bf16 MFMA, f32 accumulation.  X is f16 (ST = XT_F16) or bf16 (ST = XT_BF16).
+// Software pipeline per wavefront: while the MFMAs of stage s run on fragments decoded earlier,
+// the raw blocks of stage s+1 are decoded (independent instructions the scheduler can interleave
+// with the MFMAs), the blocks of stage s+2 and the X chunk of stage s+1 are in flight.
 template <int FMT, int ST, int MT, int MN>
-__global__ __launch_bounds__(kThreads) void gemm_fast_kernel(GemmParams p, bool grouped) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bool grouped) {
     constexpr int BT = 32 * MT;
     constexpr int BN = 4 * 32 * MN;
     constexpr int PITCH = 72;  // halves per LDS row: 64 + 8 (16-byte pad)
@@ -113,14 +116,13 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(GemmParams p, bool 
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
         const int c = tid + i * kThreads;
-        const int r = r0 + c / 8;
-        xrow[i] = x_row_of(p, min(r, r1 - 1));
+        xrow[i] = x_row_of(p, min(r0 + c / 8, r1 - 1));
     }
-    auto load_x = [&](int s, uint4 (&v)[XCH]) {
+    auto load_x = [&](int st, uint4 (&v)[XCH]) {
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * kThreads;
-            const int k = s * 64 + 8 * (c & 7);
+            const int k = st * 64 + 8 * (c & 7);
             if (xrow[i] >= 0 && k < K)
                 v[i] = *(const uint4*)(X + (size_t)xrow[i] * K + k);
             else
@@ -134,14 +136,24 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(GemmParams p, bool 
             *(uint4*)(&xs[buf][(c >> 3) * PITCH + 8 * (c & 7)]) = v[i];
         }
     };
-    // Weight rows of this lane (clamped to N-1 for loads; never stored beyond N).
     int wrow[MN];
 #pragma unroll
     for (int mn = 0; mn < MN; mn++) wrow[mn] = min(n_base + 32 * mn + li, p.N - 1);
-    auto load_w = [&](int s, RawBlock<FMT> (&w)[MN]) {
-        const int b = min(2 * s + g, nblk - 1);
+    auto load_w = [&](int st, RawBlock<FMT> (&w)[MN]) {
+        const int b = min(2 * st + g, nblk - 1);
 #pragma unroll
         for (int mn = 0; mn < MN; mn++) w[mn] = load_block<FMT>(codes, scales, offs, p.group, K, wrow[mn], b);
+    };
+    // B fragments of stage st (zero for a block beyond K, i.e. K % 64 == 32 at the last stage).
+    auto decode = [&](int st, const RawBlock<FMT> (&w)[MN], short8_t (&bf)[MN][4]) {
+        const bool valid = 2 * st + g < nblk;
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+            block_to_frags16<FMT, ST>(w[mn], bf[mn]);
+            if (!valid)
+#pragma unroll
+                for (int j = 0; j < 4; j++) bf[mn][j] = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        }
     };
 
     f32x16_t acc[MT][MN];
@@ -153,30 +165,26 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(GemmParams p, bool 
             for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
     uint4 xv[XCH];
-    RawBlock<FMT> wr[MN];
-    load_x(0, xv);
-    load_w(0, wr);
-    store_x(0, xv);
+    RawBlock<FMT> w1[MN];
+    short8_t fc[MN][4];
+    {
+        RawBlock<FMT> w0[MN];
+        load_x(0, xv);
+        load_w(0, w0);
+        if (nstage > 1) load_w(1, w1);
+        store_x(0, xv);
+        decode(0, w0, fc);
+    }
     __syncthreads();
 
     for (int s = 0; s < nstage; s++) {
         const int buf = s & 1;
         const bool more = s + 1 < nstage;
-        RawBlock<FMT> wn[MN];
-        if (more) {
-            load_x(s + 1, xv);
-            load_w(s + 1, wn);
-        }
-        // Decode this stage's blocks into B fragments (zero for a block beyond K).
-        short8_t bf[MN][4];
-        const bool valid = 2 * s + g < nblk;
-#pragma unroll
-        for (int mn = 0; mn < MN; mn++) {
-            block_to_frags16<FMT, ST>(wr[mn], bf[mn]);
-            if (!valid)
-#pragma unroll
-                for (int j = 0; j < 4; j++) bf[mn][j] = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        RawBlock<FMT> w2[MN];
+        if (s + 2 < nstage) load_w(s + 2, w2);
+        if (more) load_x(s + 1, xv);
+        short8_t fn[MN][4];
+        if (more) decode(s + 1, w1, fn);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
 #pragma unroll
@@ -186,10 +194,10 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(GemmParams p, bool 
                 for (int mn = 0; mn < MN; mn++) {
                     if constexpr (ST == XT_F16)
                         acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, bf[mn][j]), acc[mt][mn], 0, 0, 0);
+                            __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, fc[mn][j]), acc[mt][mn], 0, 0, 0);
                     else
                         acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bf[mn][j]), acc[mt][mn], 0, 0,
+                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, fc[mn][j]), acc[mt][mn], 0, 0,
                             0);
                 }
             }
@@ -197,7 +205,11 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(GemmParams p, bool 
         if (more) {
             store_x(buf ^ 1, xv);
 #pragma unroll
-            for (int mn = 0; mn < MN; mn++) wr[mn] = wn[mn];
+            for (int mn = 0; mn < MN; mn++) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) fc[mn][j] = fn[mn][j];
+                w1[mn] = w2[mn];
+            }
         }
         __syncthreads();
     }
@@ -371,10 +383,12 @@ static void fast_launch(const GemmParams& p, bool grouped, hipStream_t s) {
 template <int FMT, int ST>
 static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) return fast_launch<FMT, ST, 1, 2>(p, grouped, s);
-    const long big = (long)((p.N + 255) / 256) * ((p.R + 127) / 128);
-    const long mid = (long)((p.N + 127) / 128) * ((p.R + 127) / 128);
-    if (big >= 200) return fast_launch<FMT, ST, 4, 2>(p, grouped, s);
-    if (mid >= 200) return fast_launch<FMT, ST, 4, 1>(p, grouped, s);
+    // The largest tile that still gives about one workgroup per CU: big tiles amortize each
+    // decoded weight over more tokens and each staged X row over more weight rows.
+    auto wgs = [&](int bt, int bn) { return (long)((p.N + bn - 1) / bn) * ((p.R + bt - 1) / bt); };
+    if (wgs(256, 256) >= 200) return fast_launch<FMT, ST, 8, 2>(p, grouped, s);
+    if (wgs(128, 256) >= 200) return fast_launch<FMT, ST, 4, 2>(p, grouped, s);
+    if (wgs(128, 128) >= 200) return fast_launch<FMT, ST, 4, 1>(p, grouped, s);
     return fast_launch<FMT, ST, 2, 1>(p, grouped, s);
 }
 

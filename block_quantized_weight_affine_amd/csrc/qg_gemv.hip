@@ -126,7 +126,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
     constexpr int KC = GemvChunk<NT>::kc;
     constexpr int G = (16 / RW) < S ? (16 / RW) : S;                     // steps whose loads are in flight together
     constexpr int XV = (XT == XT_F32) ? 4 : 8;                          // X values per 16-byte load
-    constexpr int XL = (NT * KC / XV + kGemvThreads - 1) / kGemvThreads;  // X loads per thread per chunk
+    constexpr int XL = (KC / XV + kGemvThreads - 1) / kGemvThreads;  // X loads per thread per X row and chunk
     const int lane = threadIdx.x & 63;
     const int K = p.K, units = K >> 4;
     const int KS = min(K, KC);  // LDS row stride of the staged X chunk
@@ -143,22 +143,22 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
         const int kn = min(KC, K - k0);
         const int u0 = k0 >> 4;
         const int nsteps = (kn + 1023) >> 10;
-        // 1. X loads of the chunk (16 bytes each): load i covers values [e, e + XV) of X row t of
-        //    the chunk, with c = tid + i * threads, t = c / (kn / XV), e = XV * (c % (kn / XV)).
-        uint4 xl[XL];
-        const int per_row = kn / XV;
+        // 1. X loads of the chunk, 16 bytes each: load (t, i) covers values [e, e + XV) of X row t of
+        //    the chunk with e = XV * (tid + i * threads).
+        uint4 xl[NT][XL];
 #pragma unroll
-        for (int i = 0; i < XL; i++) {
-            const int c = threadIdx.x + i * kGemvThreads;
-            const int t = c / per_row, e = (c - t * per_row) * XV;
-            xl[i] = make_uint4(0, 0, 0, 0);
-            if (t < NT && xrow[t] >= 0) {
-                if constexpr (XT == XT_F32)
-                    xl[i] = *(const uint4*)((const float*)p.X + (size_t)xrow[t] * K + k0 + e);
-                else
-                    xl[i] = *(const uint4*)((const uint16_t*)p.X + (size_t)xrow[t] * K + k0 + e);
+        for (int t = 0; t < NT; t++)
+#pragma unroll
+            for (int i = 0; i < XL; i++) {
+                const int e = XV * (int)(threadIdx.x + i * kGemvThreads);
+                xl[t][i] = make_uint4(0, 0, 0, 0);
+                if (e < kn && xrow[t] >= 0) {
+                    if constexpr (XT == XT_F32)
+                        xl[t][i] = *(const uint4*)((const float*)p.X + (size_t)xrow[t] * K + k0 + e);
+                    else
+                        xl[t][i] = *(const uint4*)((const uint16_t*)p.X + (size_t)xrow[t] * K + k0 + e);
+                }
             }
-        }
         for (int g0 = 0; g0 < nsteps; g0 += G) {
             // 2. the weight loads of G steps
             Unit<FMT> w[G][RW];
@@ -171,32 +171,34 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
             if (g0 == 0) {
                 // 3. X to LDS as f32: X row t of the chunk at xs[t * KS + e]
 #pragma unroll
-                for (int i = 0; i < XL; i++) {
-                    const int c = threadIdx.x + i * kGemvThreads;
-                    const int t = c / per_row, e = (c - t * per_row) * XV;
-                    if (t < NT) {
-                        float4* d = (float4*)(xs + t * KS + e);
-                        if constexpr (XT == XT_F32) {
-                            d[0] = make_float4(__uint_as_float(xl[i].x), __uint_as_float(xl[i].y),
-                                               __uint_as_float(xl[i].z), __uint_as_float(xl[i].w));
-                        } else {
-                            const uint32_t q[4] = {xl[i].x, xl[i].y, xl[i].z, xl[i].w};
-                            float v[8];
+                for (int t = 0; t < NT; t++)
 #pragma unroll
-                            for (int h = 0; h < 4; h++) {
-                                if constexpr (XT == XT_F16) {
-                                    v[2 * h] = f16_to_f32((uint16_t)(q[h] & 0xFFFFu));
-                                    v[2 * h + 1] = f16_to_f32((uint16_t)(q[h] >> 16));
-                                } else {
-                                    v[2 * h] = __uint_as_float(q[h] << 16);
-                                    v[2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
+                    for (int i = 0; i < XL; i++) {
+                        const int e = XV * (int)(threadIdx.x + i * kGemvThreads);
+                        if (e < kn) {
+                            float4* d = (float4*)(xs + t * KS + e);
+                            const uint4 q4 = xl[t][i];
+                            if constexpr (XT == XT_F32) {
+                                d[0] = make_float4(__uint_as_float(q4.x), __uint_as_float(q4.y), __uint_as_float(q4.z),
+                                                   __uint_as_float(q4.w));
+                            } else {
+                                const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
+                                float v[8];
+#pragma unroll
+                                for (int h = 0; h < 4; h++) {
+                                    if constexpr (XT == XT_F16) {
+                                        v[2 * h] = f16_to_f32((uint16_t)(q[h] & 0xFFFFu));
+                                        v[2 * h + 1] = f16_to_f32((uint16_t)(q[h] >> 16));
+                                    } else {
+                                        v[2 * h] = __uint_as_float(q[h] << 16);
+                                        v[2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
+                                    }
                                 }
+                                d[0] = make_float4(v[0], v[1], v[2], v[3]);
+                                d[1] = make_float4(v[4], v[5], v[6], v[7]);
                             }
-                            d[0] = make_float4(v[0], v[1], v[2], v[3]);
-                            d[1] = make_float4(v[4], v[5], v[6], v[7]);
                         }
                     }
-                }
                 __syncthreads();
             }
             // 4. arithmetic of the G steps
