@@ -27,6 +27,19 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Pointers into global memory.  Loads through them compile to global_load_* rather than
+// flat_load_*; flat loads also count against the LDS wait counter, so a wait for an LDS read would
+// otherwise wait for weight loads issued stages ahead.
+#define QG_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const QG_GLOBAL T* gptr(const void* p) {
+    return (const QG_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ QG_GLOBAL T* gptr_mut(void* p) {
+    return (QG_GLOBAL T*)(p);
+}
+
 // Same layout as qg_expert in qgemm.h.
 struct Expert {
     const void* codes;
@@ -48,6 +61,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // mixed-precision FMA with a 16-bit result, which rounds the exact result once and so differs
 // from the f32-then-narrow sequence on ties.
 __device__ __forceinline__ float keep_f32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+// An opaque copy of an integer: keeps a masked word as is, so each of its bytes converts with one
+// v_cvt_f32_ubyteN instead of a re-derived bit-field extract plus an integer conversion.
+__device__ __forceinline__ uint32_t keep_u32(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
 }
@@ -86,19 +105,20 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
     RawBlock<FMT> r;
     const size_t bi = (size_t)n * (size_t)(K >> 5) + (size_t)b;
     if constexpr (FMT == FMT_Q8) {
-        const uint4* p = (const uint4*)((const int8_t*)codes + (size_t)n * (size_t)K + (size_t)b * 32);
-        r.q0 = p[0];
-        r.q1 = p[1];
-        r.d = ((const float*)scales)[bi];
+        const QG_GLOBAL u32x4_t* p = gptr<u32x4_t>((const int8_t*)codes + (size_t)n * (size_t)K + (size_t)b * 32);
+        const u32x4_t a = p[0], c = p[1];
+        r.q0 = make_uint4(a.x, a.y, a.z, a.w);
+        r.q1 = make_uint4(c.x, c.y, c.z, c.w);
+        r.d = gptr<float>(scales)[bi];
         r.m = 0.f;
         r.dh = 0;
     } else {
-        const uint4* p = (const uint4*)((const uint8_t*)codes + (size_t)n * (size_t)(K >> 1) + (size_t)b * 16);
-        r.q = *p;
-        r.dh = ((const uint16_t*)scales)[bi];
+        const u32x4_t a = *gptr<u32x4_t>((const uint8_t*)codes + (size_t)n * (size_t)(K >> 1) + (size_t)b * 16);
+        r.q = make_uint4(a.x, a.y, a.z, a.w);
+        r.dh = gptr<uint16_t>(scales)[bi];
         r.d = f16_to_f32((uint16_t)r.dh);
         if constexpr (FMT == FMT_Q4A)
-            r.m = bf16_to_f32(offs[(size_t)n * (size_t)(K / group) + (size_t)((b * 32) / group)]);
+            r.m = bf16_to_f32(gptr<uint16_t>(offs)[(size_t)n * (size_t)(K / group) + (size_t)((b * 32) / group)]);
         else
             r.m = 0.f;
     }
@@ -120,14 +140,16 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
 template <int FMT>
 __device__ __forceinline__ void value_bytes(const RawBlock<FMT>& r, uint32_t (&c)[8]) {
     if constexpr (FMT == FMT_Q8) {
-        c[0] = r.q0.x ^ 0x80808080u; c[1] = r.q0.y ^ 0x80808080u; c[2] = r.q0.z ^ 0x80808080u; c[3] = r.q0.w ^ 0x80808080u;
-        c[4] = r.q1.x ^ 0x80808080u; c[5] = r.q1.y ^ 0x80808080u; c[6] = r.q1.z ^ 0x80808080u; c[7] = r.q1.w ^ 0x80808080u;
+        c[0] = keep_u32(r.q0.x ^ 0x80808080u); c[1] = keep_u32(r.q0.y ^ 0x80808080u);
+        c[2] = keep_u32(r.q0.z ^ 0x80808080u); c[3] = keep_u32(r.q0.w ^ 0x80808080u);
+        c[4] = keep_u32(r.q1.x ^ 0x80808080u); c[5] = keep_u32(r.q1.y ^ 0x80808080u);
+        c[6] = keep_u32(r.q1.z ^ 0x80808080u); c[7] = keep_u32(r.q1.w ^ 0x80808080u);
     } else {
         const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            c[i] = w[i] & 0x0F0F0F0Fu;
-            c[4 + i] = (w[i] >> 4) & 0x0F0F0F0Fu;
+            c[i] = keep_u32(w[i] & 0x0F0F0F0Fu);
+            c[4 + i] = keep_u32((w[i] >> 4) & 0x0F0F0F0Fu);
         }
     }
 }
@@ -188,8 +210,9 @@ __device__ __forceinline__ void block_to_f32(const RawBlock<FMT>& r, float (&v)[
 // (1), kept in a register, then narrowed (nearest-even).
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// The fragments as (1) gives them, without the fallback for blocks where (1) does not apply.
 template <int FMT, int ST>
-__device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_t (&f)[4]) {
+__device__ __forceinline__ void block_to_frags16_fast(const RawBlock<FMT>& r, short8_t (&f)[4]) {
     uint32_t c[8];
     value_bytes<FMT>(r, c);
     if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
@@ -212,24 +235,54 @@ __device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_
     } else {
         bool fast;
         const float c0 = block_c0<FMT>(r, fast);
-        if (__all(fast)) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 4; j++)
 #pragma unroll
-                for (int s = 0; s < 8; s++) {
-                    const int e = 8 * j + s;
-                    f[j][s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[e >> 2], e & 3), r.d, c0)));
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-#pragma unroll
-                for (int s = 0; s < 8; s++) {
-                    const int e = 8 * j + s;
-                    f[j][s] = (short)f32_to_16<ST>(keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3))));
-                }
-        }
+            for (int s = 0; s < 8; s++) {
+                const int e = 8 * j + s;
+                f[j][s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[e >> 2], e & 3), r.d, c0)));
+            }
     }
+}
+
+// True when (1) is not exact for some lane's block of this wavefront (then every lane re-decodes
+// its block with block_frags16_fixup, which gives the same bits where (1) was exact).
+template <int FMT, int ST>
+__device__ __forceinline__ bool frags16_need_fixup(const RawBlock<FMT>& r) {
+    if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
+        return false;
+    } else {
+        bool fast;
+        block_c0<FMT>(r, fast);
+        return !__all(fast);
+    }
+}
+
+// The pages' order of operations for every element of the block.
+template <int FMT, int ST>
+__device__ __forceinline__ void block_frags16_fixup(const RawBlock<FMT>& r, short8_t (&f)[4]) {
+    uint32_t c[8];
+    value_bytes<FMT>(r, c);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            const int e = 8 * j + s;
+            f[j][s] = (short)f32_to_16<ST>(keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3))));
+        }
+}
+
+// Fast-mode fragments: element 8j + s of the block, rounded to the staged 16-bit type ST, is
+// slot s of fragment j (j = 0..3); each fragment is one 8-wide operand of a 16-k MFMA step.
+// Q4 into f16: packed f16 arithmetic.  The half with bits 0x6400 | c is 1024 + c, so
+// (1024 + c) - 1032 = c - 8 exactly, and one f16 multiply by d rounds (c - 8) d -- exact in f32 --
+// once to nearest-even: the same bits as narrowing the f32 value.  Other cases: the f32 value of
+// (1), kept in a register, then narrowed (nearest-even); blocks where (1) does not apply are
+// re-decoded in the pages' order.
+template <int FMT, int ST>
+__device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_t (&f)[4]) {
+    block_to_frags16_fast<FMT, ST>(r, f);
+    if (frags16_need_fixup<FMT, ST>(r)) block_frags16_fixup<FMT, ST>(r, f);
 }
 
 // ---- activations ---------------------------------------------------------------------------------

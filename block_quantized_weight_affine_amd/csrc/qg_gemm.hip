@@ -83,10 +83,56 @@ __device__ __forceinline__ int x_row_of(const GemmParams& p, int r) {
 }
 
 // ================================================================================================
+// Weight rows of one lane: row pointers into the codes, scales and offsets of the lane's rows.
+template <int FMT, int MN>
+struct LaneRows {
+    const QG_GLOBAL uint8_t* codes[MN];
+    const QG_GLOBAL uint8_t* scales[MN];  // f16 (Q4, Q4A) or f32 (Q8) scales of the row
+    const QG_GLOBAL uint16_t* offs[MN];   // Q4A offsets of the row
+    int group;
+
+    __device__ __forceinline__ void init(const void* c, const void* sc, const uint16_t* of, int grp, int K, int N,
+                                         int row0) {
+        group = grp;
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+            const size_t n = (size_t)min(row0 + 32 * mn, N - 1);
+            const size_t row_bytes = FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1);
+            codes[mn] = gptr<uint8_t>((const uint8_t*)c + n * row_bytes);
+            scales[mn] = gptr<uint8_t>((const uint8_t*)sc + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
+            offs[mn] = FMT == FMT_Q4A ? gptr<uint16_t>(of + n * (size_t)(K / grp)) : nullptr;
+        }
+    }
+    // Block b (in bounds) of every row.
+    __device__ __forceinline__ void load(int b, RawBlock<FMT> (&w)[MN]) const {
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+            if constexpr (FMT == FMT_Q8) {
+                const QG_GLOBAL u32x4_t* q = (const QG_GLOBAL u32x4_t*)(codes[mn] + 32 * b);
+                const u32x4_t a = q[0], c = q[1];
+                w[mn].q0 = make_uint4(a.x, a.y, a.z, a.w);
+                w[mn].q1 = make_uint4(c.x, c.y, c.z, c.w);
+                w[mn].d = ((const QG_GLOBAL float*)scales[mn])[b];
+                w[mn].m = 0.f;
+                w[mn].dh = 0;
+            } else {
+                const u32x4_t a = *(const QG_GLOBAL u32x4_t*)(codes[mn] + 16 * b);
+                w[mn].q = make_uint4(a.x, a.y, a.z, a.w);
+                w[mn].dh = ((const QG_GLOBAL uint16_t*)scales[mn])[b];
+                w[mn].d = f16_to_f32((uint16_t)w[mn].dh);
+                w[mn].m = FMT == FMT_Q4A ? bf16_to_f32(offs[mn][(32 * b) / group]) : 0.f;
+            }
+        }
+    }
+};
+
 // Fast mode: f16 / bf16 MFMA, f32 accumulation.  X is f16 (ST = XT_F16) or bf16 (ST = XT_BF16).
 // Software pipeline per wavefront: while the MFMAs of stage s run on fragments decoded earlier,
 // the raw blocks of stage s+1 are decoded (independent instructions the scheduler can interleave
-// with the MFMAs), the blocks of stage s+2 and the X chunk of stage s+1 are in flight.
+// with the MFMAs), and the blocks of stage s+2 and the X chunk of stage s+1 are in flight.  The
+// stage body is one basic block: loads past the end are clamped to valid addresses (and unused),
+// a K tail of one block (K % 64 == 32) is handled by zero X columns (the clamped weight block is
+// multiplied by zeros), and the rare Q4A re-decode runs as a fix-up after the MFMAs.
 template <int FMT, int ST, int MT, int MN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bool grouped) {
     constexpr int BT = 32 * MT;
@@ -108,53 +154,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
     const int n_base = blockIdx.x * BN + wave * 32 * MN;
     const int g = lane >> 5, li = lane & 31;
     const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
-    const uint16_t* X = (const uint16_t*)p.X;
 
-    // X staging: chunk c (16 bytes = 8 halves) -> tile row c / 8, column 8 * (c % 8).
-    constexpr int XCH = BT * 8 / kThreads;  // chunks per thread
-    int xrow[XCH];
+    // X staging: chunk c = tid + i * threads (16 bytes = 8 halves) -> tile row c / 8, column
+    // xcol = 8 * (tid % 8) (the same for every chunk of the thread).
+    constexpr int XCH = BT * 8 / kThreads;
+    const int xcol = 8 * (tid & 7);
+    const QG_GLOBAL u32x4_t* xp[XCH];
+    bool xok[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
         const int c = tid + i * kThreads;
-        xrow[i] = x_row_of(p, min(r0 + c / 8, r1 - 1));
+        const int row = x_row_of(p, min(r0 + c / 8, r1 - 1));
+        xok[i] = row >= 0;
+        xp[i] = gptr<u32x4_t>((const uint16_t*)p.X + (size_t)max(row, 0) * K + xcol);
     }
+    // Stage st's chunk: columns st*64 + xcol .. +7 of the thread's rows, zero for a zero row or for
+    // columns at or beyond K; the address is clamped to columns K-8 .. K-1 so it stays in bounds.
     auto load_x = [&](int st, uint4 (&v)[XCH]) {
+        const bool kin = st * 64 + xcol < K;
+        const int off = min(st * 64, K - 8 - xcol) >> 3;  // in 16-byte units from the row's column xcol
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
-            const int c = tid + i * kThreads;
-            const int k = st * 64 + 8 * (c & 7);
-            if (xrow[i] >= 0 && k < K)
-                v[i] = *(const uint4*)(X + (size_t)xrow[i] * K + k);
-            else
-                v[i] = make_uint4(0, 0, 0, 0);
+            const u32x4_t t = xp[i][off];
+            const bool ok = xok[i] && kin;
+            v[i] = make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
         }
     };
     auto store_x = [&](int buf, const uint4 (&v)[XCH]) {
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * kThreads;
-            *(uint4*)(&xs[buf][(c >> 3) * PITCH + 8 * (c & 7)]) = v[i];
+            *(uint4*)(&xs[buf][(c >> 3) * PITCH + xcol]) = v[i];
         }
     };
-    int wrow[MN];
-#pragma unroll
-    for (int mn = 0; mn < MN; mn++) wrow[mn] = min(n_base + 32 * mn + li, p.N - 1);
-    auto load_w = [&](int st, RawBlock<FMT> (&w)[MN]) {
-        const int b = min(2 * st + g, nblk - 1);
-#pragma unroll
-        for (int mn = 0; mn < MN; mn++) w[mn] = load_block<FMT>(codes, scales, offs, p.group, K, wrow[mn], b);
-    };
-    // B fragments of stage st (zero for a block beyond K, i.e. K % 64 == 32 at the last stage).
-    auto decode = [&](int st, const RawBlock<FMT> (&w)[MN], short8_t (&bf)[MN][4]) {
-        const bool valid = 2 * st + g < nblk;
-#pragma unroll
-        for (int mn = 0; mn < MN; mn++) {
-            block_to_frags16<FMT, ST>(w[mn], bf[mn]);
-            if (!valid)
-#pragma unroll
-                for (int j = 0; j < 4; j++) bf[mn][j] = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    };
+    LaneRows<FMT, MN> rows;
+    rows.init(codes, scales, offs, p.group, K, p.N, n_base + li);
+    auto load_w = [&](int st, RawBlock<FMT> (&w)[MN]) { rows.load(min(2 * st + g, nblk - 1), w); };
 
     f32x16_t acc[MT][MN];
 #pragma unroll
@@ -164,6 +199,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
 #pragma unroll
             for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
+    // MFMAs of one stage; the A fragments of step j+1 are read from LDS before the MFMAs of step j.
+    auto mfmas = [&](int buf, const short8_t (&fc)[MN][4]) {
+        const uint16_t* xb = &xs[buf][li * PITCH + 32 * g];
+        short8_t a[2][MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) a[0][mt] = *(const short8_t*)(xb + mt * 32 * PITCH);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if (j < 3)
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) a[(j + 1) & 1][mt] = *(const short8_t*)(xb + mt * 32 * PITCH + 8 * (j + 1));
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+                for (int mn = 0; mn < MN; mn++) {
+                    if constexpr (ST == XT_F16)
+                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a[j & 1][mt]),
+                                                                             __builtin_bit_cast(half8_t, fc[mn][j]),
+                                                                             acc[mt][mn], 0, 0, 0);
+                    else
+                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, a[j & 1][mt]), __builtin_bit_cast(bf16x8_t, fc[mn][j]),
+                            acc[mt][mn], 0, 0, 0);
+                }
+            }
+        }
+    };
+
     uint4 xv[XCH];
     RawBlock<FMT> w1[MN];
     short8_t fc[MN][4];
@@ -171,50 +234,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
         RawBlock<FMT> w0[MN];
         load_x(0, xv);
         load_w(0, w0);
-        if (nstage > 1) load_w(1, w1);
+        load_w(min(1, nstage - 1), w1);
         store_x(0, xv);
-        decode(0, w0, fc);
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) block_to_frags16<FMT, ST>(w0[mn], fc[mn]);
     }
     __syncthreads();
 
     for (int s = 0; s < nstage; s++) {
         const int buf = s & 1;
-        const bool more = s + 1 < nstage;
         RawBlock<FMT> w2[MN];
-        if (s + 2 < nstage) load_w(s + 2, w2);
-        if (more) load_x(s + 1, xv);
+        load_w(min(s + 2, nstage - 1), w2);
+        load_x(min(s + 1, nstage - 1), xv);
         short8_t fn[MN][4];
-        if (more) decode(s + 1, w1, fn);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int mn = 0; mn < MN; mn++) block_to_frags16_fast<FMT, ST>(w1[mn], fn[mn]);
+        mfmas(buf, fc);
+        store_x(buf ^ 1, xv);
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-                const short8_t a = *(const short8_t*)(&xs[buf][(mt * 32 + li) * PITCH + 32 * g + 8 * j]);
-#pragma unroll
-                for (int mn = 0; mn < MN; mn++) {
-                    if constexpr (ST == XT_F16)
-                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, fc[mn][j]), acc[mt][mn], 0, 0, 0);
-                    else
-                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, fc[mn][j]), acc[mt][mn], 0, 0,
-                            0);
-                }
-            }
-        }
-        if (more) {
-            store_x(buf ^ 1, xv);
-#pragma unroll
-            for (int mn = 0; mn < MN; mn++) {
-#pragma unroll
-                for (int j = 0; j < 4; j++) fc[mn][j] = fn[mn][j];
-                w1[mn] = w2[mn];
-            }
-        }
+        for (int mn = 0; mn < MN; mn++)
+            if (frags16_need_fixup<FMT, ST>(w1[mn])) block_frags16_fixup<FMT, ST>(w1[mn], fn[mn]);
         __syncthreads();
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) fc[mn][j] = fn[mn][j];
+            w1[mn] = w2[mn];
+        }
     }
 
     // Epilogue: D[row][col] with col = lane % 32 (weight row), row = 8*(i/4) + 4*(lane/32) + i%4 (token).
+    QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -227,8 +277,186 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
                 if (r < r1) {
                     float v = acc[mt][mn][i];
                     if (p.rs) v *= p.rs[r];
-                    p.Y[(size_t)r * p.N + n] = v;
+                    Y[(size_t)r * p.N + n] = v;
                 }
+            }
+        }
+}
+
+// ================================================================================================
+// Dense fast mode through LDS tiles (large token counts).  Per 64-k stage the workgroup decodes the
+// weight slab once, cooperatively, into an LDS tile of BN rows (f16 / bf16, 16-byte padded rows,
+// natural k order), next to the X slab.  The 4 wavefronts sit in a WM x WN grid; wavefront
+// (wm, wn) reads its A fragments (32*MT token rows) and B fragments (32*MN weight rows) from LDS,
+// so each fragment read feeds MN or MT MFMAs, and the fragments of MFMA step j+1 are read before
+// the MFMAs of step j.  Pipeline: the raw blocks of stage s+2 and the X slab of stage s+1 load
+// while stage s+1 is decoded into the other LDS buffer and stage s is multiplied; one barrier per
+// stage.  MFMA step j covers k 16j .. 16j+15 of the stage; lane group g holds k 16j+8g .. +7 of
+// both operands.
+template <int FMT, int ST, int WM, int MT, int MN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p) {
+    constexpr int WN = 4 / WM;
+    constexpr int BT = 32 * MT * WM;
+    constexpr int BN = 32 * MN * WN;
+    constexpr int PITCH = 72;           // halves per LDS row: 64 + 8 (16-byte pad)
+    constexpr int WB = 2 * BN / kThreads;  // weight blocks decoded per thread per stage
+    static_assert(WB >= 1 && 2 * BN % kThreads == 0, "tile");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT * PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][BN * PITCH];
+
+    const int r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
+    const int n0 = blockIdx.x * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const int g = lane >> 5, li = lane & 31;
+    const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
+
+    // X staging: chunk c = tid + i * threads -> tile row c / 8, column xcol = 8 * (tid % 8).
+    constexpr int XCH = BT * 8 / kThreads;
+    const int xcol = 8 * (tid & 7);
+    const QG_GLOBAL u32x4_t* xp[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; i++) {
+        const int c = tid + i * kThreads;
+        xp[i] = gptr<u32x4_t>((const uint16_t*)p.X + (size_t)min(r0 + c / 8, r1 - 1) * K + xcol);
+    }
+    auto load_x = [&](int st, uint4 (&v)[XCH]) {
+        const bool kin = st * 64 + xcol < K;
+        const int off = min(st * 64, K - 8 - xcol) >> 3;
+#pragma unroll
+        for (int i = 0; i < XCH; i++) {
+            const u32x4_t t = xp[i][off];
+            v[i] = make_uint4(kin ? t.x : 0u, kin ? t.y : 0u, kin ? t.z : 0u, kin ? t.w : 0u);
+        }
+    };
+    auto store_x = [&](int buf, const uint4 (&v)[XCH]) {
+#pragma unroll
+        for (int i = 0; i < XCH; i++) {
+            const int c = tid + i * kThreads;
+            *(uint4*)(&xs[buf][(c >> 3) * PITCH + xcol]) = v[i];
+        }
+    };
+    // Weight decode: block q = tid + i * threads of the stage -> tile row q / 2, half h = q % 2
+    // (global block 2 st + h of that row), written to columns 32 h .. 32 h + 31.
+    const int hsel = tid & 1;
+    const QG_GLOBAL uint8_t* wc[WB];
+    const QG_GLOBAL uint8_t* wsc[WB];
+    const QG_GLOBAL uint16_t* wof[WB];
+#pragma unroll
+    for (int i = 0; i < WB; i++) {
+        const size_t n = (size_t)min(n0 + (tid + i * kThreads) / 2, p.N - 1);
+        wc[i] = gptr<uint8_t>((const uint8_t*)p.codes + n * (FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1)));
+        wsc[i] = gptr<uint8_t>((const uint8_t*)p.scales + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
+        wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(p.offs + n * (size_t)(K / p.group)) : nullptr;
+    }
+    auto load_w = [&](int st, RawBlock<FMT> (&w)[WB]) {
+        const int b = min(2 * st + hsel, nblk - 1);
+#pragma unroll
+        for (int i = 0; i < WB; i++) {
+            if constexpr (FMT == FMT_Q8) {
+                const QG_GLOBAL u32x4_t* q = (const QG_GLOBAL u32x4_t*)(wc[i] + 32 * b);
+                const u32x4_t a = q[0], c = q[1];
+                w[i].q0 = make_uint4(a.x, a.y, a.z, a.w);
+                w[i].q1 = make_uint4(c.x, c.y, c.z, c.w);
+                w[i].d = ((const QG_GLOBAL float*)wsc[i])[b];
+                w[i].m = 0.f;
+                w[i].dh = 0;
+            } else {
+                const u32x4_t a = *(const QG_GLOBAL u32x4_t*)(wc[i] + 16 * b);
+                w[i].q = make_uint4(a.x, a.y, a.z, a.w);
+                w[i].dh = ((const QG_GLOBAL uint16_t*)wsc[i])[b];
+                w[i].d = f16_to_f32((uint16_t)w[i].dh);
+                w[i].m = FMT == FMT_Q4A ? bf16_to_f32(wof[i][(32 * b) / p.group]) : 0.f;
+            }
+        }
+    };
+    auto decode_store = [&](int buf, const RawBlock<FMT> (&w)[WB]) {
+#pragma unroll
+        for (int i = 0; i < WB; i++) {
+            short8_t f[4];
+            block_to_frags16<FMT, ST>(w[i], f);
+            uint16_t* d = &wsh[buf][((tid + i * kThreads) >> 1) * PITCH + 32 * hsel];
+#pragma unroll
+            for (int j = 0; j < 4; j++) *(short8_t*)(d + 8 * j) = f[j];
+        }
+    };
+
+    f32x16_t acc[MT][MN];
+#pragma unroll
+    for (int a = 0; a < MT; a++)
+#pragma unroll
+        for (int b = 0; b < MN; b++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+
+    auto mfmas = [&](int buf) {
+        const uint16_t* xa = &xs[buf][(wm * 32 * MT + li) * PITCH + 8 * g];
+        const uint16_t* wb = &wsh[buf][(wn * 32 * MN + li) * PITCH + 8 * g];
+        short8_t A[2][MT], B[2][MN];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) A[0][mt] = *(const short8_t*)(xa + mt * 32 * PITCH);
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) B[0][mn] = *(const short8_t*)(wb + mn * 32 * PITCH);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int cur = j & 1, nxt = cur ^ 1;
+            if (j < 3) {
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) A[nxt][mt] = *(const short8_t*)(xa + mt * 32 * PITCH + 16 * (j + 1));
+#pragma unroll
+                for (int mn = 0; mn < MN; mn++) B[nxt][mn] = *(const short8_t*)(wb + mn * 32 * PITCH + 16 * (j + 1));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int mn = 0; mn < MN; mn++) {
+                    if constexpr (ST == XT_F16)
+                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, A[cur][mt]),
+                                                                             __builtin_bit_cast(half8_t, B[cur][mn]),
+                                                                             acc[mt][mn], 0, 0, 0);
+                    else
+                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A[cur][mt]),
+                                                                              __builtin_bit_cast(bf16x8_t, B[cur][mn]),
+                                                                              acc[mt][mn], 0, 0, 0);
+                }
+        }
+    };
+
+    uint4 xv[XCH];
+    RawBlock<FMT> w1[WB];
+    {
+        RawBlock<FMT> w0[WB];
+        load_x(0, xv);
+        load_w(0, w0);
+        load_w(min(1, nstage - 1), w1);
+        store_x(0, xv);
+        decode_store(0, w0);
+    }
+    __syncthreads();
+    for (int s = 0; s < nstage; s++) {
+        const int buf = s & 1;
+        RawBlock<FMT> w2[WB];
+        load_w(min(s + 2, nstage - 1), w2);
+        load_x(min(s + 1, nstage - 1), xv);
+        decode_store(buf ^ 1, w1);
+        mfmas(buf);
+        store_x(buf ^ 1, xv);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < WB; i++) w1[i] = w2[i];
+    }
+
+    QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+            const int n = n0 + wn * 32 * MN + 32 * mn + li;
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = r0 + wm * 32 * MT + mt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (r < r1) Y[(size_t)r * p.N + n] = acc[mt][mn][i];
             }
         }
 }
@@ -380,16 +608,23 @@ static void fast_launch(const GemmParams& p, bool grouped, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fast_kernel<FMT, ST, MT, MN>), grid, dim3(kThreads), 0, s, p, grouped);
 }
 
+template <int FMT, int ST, int WM, int MT, int MN>
+static void fast_lds_launch(const GemmParams& p, hipStream_t s) {
+    constexpr int BT = 32 * MT * WM, BN = 32 * MN * (4 / WM);
+    dim3 grid((p.N + BN - 1) / BN, (p.R + BT - 1) / BT);
+    hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN>), grid, dim3(kThreads), 0, s, p);
+}
+
 template <int FMT, int ST>
 static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) return fast_launch<FMT, ST, 1, 2>(p, grouped, s);
     // The largest tile that still gives about one workgroup per CU: big tiles amortize each
     // decoded weight over more tokens and each staged X row over more weight rows.
     auto wgs = [&](int bt, int bn) { return (long)((p.N + bn - 1) / bn) * ((p.R + bt - 1) / bt); };
-    if (wgs(256, 256) >= 200) return fast_launch<FMT, ST, 8, 2>(p, grouped, s);
-    if (wgs(128, 256) >= 200) return fast_launch<FMT, ST, 4, 2>(p, grouped, s);
-    if (wgs(128, 128) >= 200) return fast_launch<FMT, ST, 4, 1>(p, grouped, s);
-    return fast_launch<FMT, ST, 2, 1>(p, grouped, s);
+    if (wgs(256, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 4, 4>(p, s);
+    if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4>(p, s);
+    if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2>(p, s);
+    return fast_lds_launch<FMT, ST, 2, 1, 2>(p, s);
 }
 
 hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s) {
