@@ -61,13 +61,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // mixed-precision FMA with a 16-bit result, which rounds the exact result once and so differs
 // from the f32-then-narrow sequence on ties.
 __device__ __forceinline__ float keep_f32(float v) {
-    asm volatile("" : "+v"(v));
+    asm("" : "+v"(v));
     return v;
 }
 // An opaque copy of an integer: keeps a masked word as is, so each of its bytes converts with one
 // v_cvt_f32_ubyteN instead of a re-derived bit-field extract plus an integer conversion.
 __device__ __forceinline__ uint32_t keep_u32(uint32_t v) {
-    asm volatile("" : "+v"(v));
+    asm("" : "+v"(v));
     return v;
 }
 template <int ST>
@@ -210,39 +210,51 @@ __device__ __forceinline__ void block_to_f32(const RawBlock<FMT>& r, float (&v)[
 // (1), kept in a register, then narrowed (nearest-even).
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// The fragments as (1) gives them, without the fallback for blocks where (1) does not apply.
+// Value-byte word k (elements 4k .. 4k+3) of a block, as in value_bytes.
+template <int FMT>
+__device__ __forceinline__ uint32_t value_word(const RawBlock<FMT>& r, int k) {
+    if constexpr (FMT == FMT_Q8) {
+        const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        return keep_u32(w[k] ^ 0x80808080u);
+    } else {
+        const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        return k < 4 ? keep_u32(w[k] & 0x0F0F0F0Fu) : keep_u32((w[k - 4] >> 4) & 0x0F0F0F0Fu);
+    }
+}
+
+// Fragment jj (elements 8jj .. 8jj+7) of a block as (1) gives it, c0 from block_c0; no fallback.
 template <int FMT, int ST>
-__device__ __forceinline__ void block_to_frags16_fast(const RawBlock<FMT>& r, short8_t (&f)[4]) {
-    uint32_t c[8];
-    value_bytes<FMT>(r, c);
+__device__ __forceinline__ short8_t frag16_fast(const RawBlock<FMT>& r, float c0, int jj) {
+    const uint32_t c[2] = {value_word<FMT>(r, 2 * jj), value_word<FMT>(r, 2 * jj + 1)};
+    short8_t f;
     if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
         const half2_t d2 = __builtin_bit_cast(half2_t, r.dh | (r.dh << 16));
         const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            uint32_t o[4];
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const uint32_t wd = c[2 * j + h];
-                // halves (c0 | 0x6400, c1 | 0x6400) and (c2 | 0x6400, c3 | 0x6400)
-                const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, wd, 0x04010400u));
-                const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, wd, 0x04030402u));
-                o[2 * h] = __builtin_bit_cast(uint32_t, (lo - off) * d2);
-                o[2 * h + 1] = __builtin_bit_cast(uint32_t, (hi - off) * d2);
-            }
-            f[j] = __builtin_bit_cast(short8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        for (int h = 0; h < 2; h++) {
+            // halves (c0 | 0x6400, c1 | 0x6400) and (c2 | 0x6400, c3 | 0x6400)
+            const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c[h], 0x04010400u));
+            const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c[h], 0x04030402u));
+            o[2 * h] = __builtin_bit_cast(uint32_t, (lo - off) * d2);
+            o[2 * h + 1] = __builtin_bit_cast(uint32_t, (hi - off) * d2);
         }
+        f = __builtin_bit_cast(short8_t, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
-        bool fast;
-        const float c0 = block_c0<FMT>(r, fast);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int s = 0; s < 8; s++) {
-                const int e = 8 * j + s;
-                f[j][s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[e >> 2], e & 3), r.d, c0)));
-            }
+        for (int s = 0; s < 8; s++)
+            f[s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[s >> 2], s & 3), r.d, c0)));
     }
+    return f;
+}
+
+// The fragments as (1) gives them, without the fallback for blocks where (1) does not apply.
+template <int FMT, int ST>
+__device__ __forceinline__ void block_to_frags16_fast(const RawBlock<FMT>& r, short8_t (&f)[4]) {
+    bool fast;
+    const float c0 = block_c0<FMT>(r, fast);
+#pragma unroll
+    for (int j = 0; j < 4; j++) f[j] = frag16_fast<FMT, ST>(r, c0, j);
 }
 
 // True when (1) is not exact for some lane's block of this wavefront (then every lane re-decodes
@@ -272,17 +284,19 @@ __device__ __forceinline__ void block_frags16_fixup(const RawBlock<FMT>& r, shor
         }
 }
 
-// Fast-mode fragments: element 8j + s of the block, rounded to the staged 16-bit type ST, is
-// slot s of fragment j (j = 0..3); each fragment is one 8-wide operand of a 16-k MFMA step.
-// Q4 into f16: packed f16 arithmetic.  The half with bits 0x6400 | c is 1024 + c, so
-// (1024 + c) - 1032 = c - 8 exactly, and one f16 multiply by d rounds (c - 8) d -- exact in f32 --
-// once to nearest-even: the same bits as narrowing the f32 value.  Other cases: the f32 value of
-// (1), kept in a register, then narrowed (nearest-even); blocks where (1) does not apply are
-// re-decoded in the pages' order.
+// Fast-mode fragments with the fallback: blocks where (1) does not apply are re-decoded in the
+// pages' order.
 template <int FMT, int ST>
 __device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_t (&f)[4]) {
     block_to_frags16_fast<FMT, ST>(r, f);
     if (frags16_need_fixup<FMT, ST>(r)) block_frags16_fixup<FMT, ST>(r, f);
+}
+
+// ---- direct copies into LDS ---------------------------------------------------------------------
+// One buffer_load ... lds of 16 bytes per lane: lane l's bytes at byte offset voff of the buffer land
+// at lds + 16 l (lds is wave-uniform); offsets at or past the buffer's size read as zero.
+__device__ __forceinline__ void buffer_copy16_lds(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
 // ---- activations ---------------------------------------------------------------------------------

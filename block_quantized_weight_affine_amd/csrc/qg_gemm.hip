@@ -20,6 +20,8 @@
 //    workgroup finds its (expert, first row) by a wavefront prefix scan over seg_off.
 //  * Rows beyond the tile's valid range and weight rows beyond N are clamped on load and never
 //    stored; a K tail of one block (K % 64 == 32) zeroes both operands of the missing block.
+#include <type_traits>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -288,56 +290,68 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
 // weight slab once, cooperatively, into an LDS tile of BN rows (f16 / bf16, 16-byte padded rows,
 // natural k order), next to the X slab.  The 4 wavefronts sit in a WM x WN grid; wavefront
 // (wm, wn) reads its A fragments (32*MT token rows) and B fragments (32*MN weight rows) from LDS,
-// so each fragment read feeds MN or MT MFMAs, and the fragments of MFMA step j+1 are read before
-// the MFMAs of step j.  Pipeline: the raw blocks of stage s+2 and the X slab of stage s+1 load
-// while stage s+1 is decoded into the other LDS buffer and stage s is multiplied; one barrier per
-// stage.  MFMA step j covers k 16j .. 16j+15 of the stage; lane group g holds k 16j+8g .. +7 of
-// both operands.
+// so each fragment read feeds MN or MT MFMAs.  MFMA step j covers k 16j .. 16j+15 of the stage;
+// lane group g holds k 16j+8g .. +7 of both operands.
+//
+// X goes from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane): no registers, and
+// chunks past K or past the tile's last row read as zero.  One such load writes 64 consecutive
+// 16-byte slots, i.e. 8 whole rows of the slab; the lane for slot p of row r fetches chunk
+// p ^ ((r / 2) % 8), so chunk c of row r sits at slot c ^ ((r / 2) % 8).  A fragment read takes
+// one chunk from 16 consecutive rows per LDS cycle (16 lanes x 16 bytes over 64 banks): rows of
+// one parity land on 8 different slots and the two parities on the two 128-byte halves of the
+// bank space, so the 16 lanes hit 16 different bank quads.
+//
+// Pipeline of stage s (one wavefront per SIMD, so each wavefront keeps its matrix core busy by
+// itself): buffers C hold X(s) and W(s), the raw blocks of W(s+1) are in registers.  In one
+// straight-line region the wavefront starts the X(s+1) copy into the other X buffer and the raw
+// loads of W(s+2) into the second register set, decodes W(s+1) into the other weight buffer and
+// runs the 4 * MT * MN MFMAs of stage s, reading the fragments of step j+1 during step j; the
+// decode's VALU work is interleaved with the MFMAs (sched_group_barrier), where it runs beside
+// the matrix core.  Blocks whose fast decode (1) is not the pages' rounding are re-loaded and
+// re-decoded in the pages' order after the MFMAs; one barrier (which waits for all of the stage's
+// loads) ends the stage.  The two LDS buffers are separate arrays and the stage loop is unrolled
+// by two, so the compiler can see that the decode's stores and the MFMA reads never alias.
 template <int FMT, int ST, int WM, int MT, int MN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p) {
     constexpr int WN = 4 / WM;
     constexpr int BT = 32 * MT * WM;
     constexpr int BN = 32 * MN * WN;
-    constexpr int PITCH = 72;           // halves per LDS row: 64 + 8 (16-byte pad)
+    constexpr int PITCH = 72;              // halves per weight-tile row: 64 + 8 (16-byte pad)
     constexpr int WB = 2 * BN / kThreads;  // weight blocks decoded per thread per stage
-    static_assert(WB >= 1 && 2 * BN % kThreads == 0, "tile");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT * PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][BN * PITCH];
+    constexpr int XCH = BT / 32;           // X row-octets copied per wavefront per stage
+    static_assert(WB >= 1 && 2 * BN % kThreads == 0 && BT % 32 == 0, "tile");
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[BT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[BT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[BN * PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[BN * PITCH];
 
     const int r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
     const int n0 = blockIdx.x * BN;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int g = lane >> 5, li = lane & 31;
     const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
 
-    // X staging: chunk c = tid + i * threads -> tile row c / 8, column xcol = 8 * (tid % 8).
-    constexpr int XCH = BT * 8 / kThreads;
-    const int xcol = 8 * (tid & 7);
-    const QG_GLOBAL u32x4_t* xp[XCH];
+    // X copy i of wavefront w: rows 8 (4 i + w) .. +7 of the slab; this lane's slot is row
+    // r = 8 (4 i + w) + lane / 8, position lane % 8, holding chunk xc = (lane % 8) ^ ((r / 2) % 8),
+    // where (r / 2) % 8 = 4 (w % 2) + lane / 16.
+    const int xc = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    uint16_t* const xbase = (uint16_t*)p.X + (size_t)r0 * K;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(xbase, 0, (r1 - r0) * K * 2, 0x00020000);
+    int xoff[XCH];
 #pragma unroll
-    for (int i = 0; i < XCH; i++) {
-        const int c = tid + i * kThreads;
-        xp[i] = gptr<u32x4_t>((const uint16_t*)p.X + (size_t)min(r0 + c / 8, r1 - 1) * K + xcol);
-    }
-    auto load_x = [&](int st, uint4 (&v)[XCH]) {
-        const bool kin = st * 64 + xcol < K;
-        const int off = min(st * 64, K - 8 - xcol) >> 3;
+    for (int i = 0; i < XCH; i++) xoff[i] = (8 * (4 * i + wave) + (lane >> 3)) * K * 2 + 16 * xc;
+    auto copy_x = [&](int st, uint16_t* xs) {
+        const int koff = st * 64 + 8 * xc < K ? st * 128 : 0x40000000;  // 2^30 > any valid offset
 #pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const u32x4_t t = xp[i][off];
-            v[i] = make_uint4(kin ? t.x : 0u, kin ? t.y : 0u, kin ? t.z : 0u, kin ? t.w : 0u);
-        }
+        for (int i = 0; i < XCH; i++)
+            buffer_copy16_lds(xrs, xs + 8 * (4 * i + wave) * 64, xoff[i] + koff);
     };
-    auto store_x = [&](int buf, const uint4 (&v)[XCH]) {
-#pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const int c = tid + i * kThreads;
-            *(uint4*)(&xs[buf][(c >> 3) * PITCH + xcol]) = v[i];
-        }
-    };
-    // Weight decode: block q = tid + i * threads of the stage -> tile row q / 2, half h = q % 2
-    // (global block 2 st + h of that row), written to columns 32 h .. 32 h + 31.
+
+    // Weight block i of a thread: tile row (tid + i * threads) / 2, block 2 st + hsel of that row,
+    // written to columns 32 hsel .. 32 hsel + 31.  Blocks past K are loaded clamped and decoded
+    // with zero scale and offset, which gives +0 for every element.
     const int hsel = tid & 1;
     const QG_GLOBAL uint8_t* wc[WB];
     const QG_GLOBAL uint8_t* wsc[WB];
@@ -370,12 +384,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             }
         }
     };
-    auto decode_store = [&](int buf, const RawBlock<FMT> (&w)[WB]) {
+    auto w_dst = [&](uint16_t* ws, int i) { return ws + ((tid + i * kThreads) >> 1) * PITCH + 32 * hsel; };
+    // Fast decode (1) of stage st into ws; need is set where a valid block needs the pages' order.
+    auto decode_store = [&](int st, uint16_t* ws, const RawBlock<FMT> (&w)[WB], bool& need) {
+        const bool valid = 2 * st + hsel < nblk;
+#pragma unroll
+        for (int i = 0; i < WB; i++) {
+            RawBlock<FMT> r = w[i];
+            r.d = valid ? r.d : 0.f;
+            r.m = valid ? r.m : 0.f;
+            r.dh = valid ? r.dh : 0u;
+            short8_t f[4];
+            block_to_frags16_fast<FMT, ST>(r, f);
+            if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) {
+                bool fast;
+                block_c0<FMT>(r, fast);
+                need = need || (valid && !fast);
+            }
+            uint16_t* d = w_dst(ws, i);
+#pragma unroll
+            for (int j = 0; j < 4; j++) *(short8_t*)(d + 8 * j) = f[j];
+        }
+    };
+    // The pages' order for the blocks of stage st (rare: non-positive scales, inexact m - 8d).
+    auto fixup = [&](int st, uint16_t* ws) {
+        RawBlock<FMT> w[WB];
+        load_w(st, w);
 #pragma unroll
         for (int i = 0; i < WB; i++) {
             short8_t f[4];
-            block_to_frags16<FMT, ST>(w[i], f);
-            uint16_t* d = &wsh[buf][((tid + i * kThreads) >> 1) * PITCH + 32 * hsel];
+            block_frags16_fixup<FMT, ST>(w[i], f);
+            uint16_t* d = w_dst(ws, i);
 #pragma unroll
             for (int j = 0; j < 4; j++) *(short8_t*)(d + 8 * j) = f[j];
         }
@@ -389,62 +428,108 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
 #pragma unroll
             for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-    auto mfmas = [&](int buf) {
-        const uint16_t* xa = &xs[buf][(wm * 32 * MT + li) * PITCH + 8 * g];
-        const uint16_t* wb = &wsh[buf][(wn * 32 * MN + li) * PITCH + 8 * g];
-        short8_t A[2][MT], B[2][MN];
+    // Fragments of MFMA step j: A from the swizzled X slab (row r, chunk 2j + g at slot
+    // (2j + g) ^ ((r / 2) % 8), and (r / 2) % 8 = (li / 2) % 8), B from the padded weight tile.
+    auto frags_a = [&](const uint16_t* xs, int j, short8_t (&A)[MT]) {
+        const uint16_t* xa = xs + (wm * 32 * MT + li) * 64 + 8 * ((2 * j + g) ^ ((li >> 1) & 7));
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++) A[0][mt] = *(const short8_t*)(xa + mt * 32 * PITCH);
+        for (int mt = 0; mt < MT; mt++) A[mt] = *(const short8_t*)(xa + mt * 32 * 64);
+    };
+    auto frags_b = [&](const uint16_t* ws, int j, short8_t (&B)[MN]) {
+        const uint16_t* wb = ws + (wn * 32 * MN + li) * PITCH + 8 * g + 16 * j;
 #pragma unroll
-        for (int mn = 0; mn < MN; mn++) B[0][mn] = *(const short8_t*)(wb + mn * 32 * PITCH);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int cur = j & 1, nxt = cur ^ 1;
-            if (j < 3) {
-#pragma unroll
-                for (int mt = 0; mt < MT; mt++) A[nxt][mt] = *(const short8_t*)(xa + mt * 32 * PITCH + 16 * (j + 1));
-#pragma unroll
-                for (int mn = 0; mn < MN; mn++) B[nxt][mn] = *(const short8_t*)(wb + mn * 32 * PITCH + 16 * (j + 1));
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-                for (int mn = 0; mn < MN; mn++) {
-                    if constexpr (ST == XT_F16)
-                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, A[cur][mt]),
-                                                                             __builtin_bit_cast(half8_t, B[cur][mn]),
-                                                                             acc[mt][mn], 0, 0, 0);
-                    else
-                        acc[mt][mn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A[cur][mt]),
-                                                                              __builtin_bit_cast(bf16x8_t, B[cur][mn]),
-                                                                              acc[mt][mn], 0, 0, 0);
-                }
-        }
+        for (int mn = 0; mn < MN; mn++) B[mn] = *(const short8_t*)(wb + mn * 32 * PITCH);
+    };
+    auto mfma = [&](const short8_t& a, const short8_t& b, f32x16_t& c) {
+        if constexpr (ST == XT_F16)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     };
 
-    uint4 xv[XCH];
-    RawBlock<FMT> w1[WB];
+    // A stage is cut into NCH chunks, one per decoded fragment (WB blocks x 4 fragments), each
+    // with MPC of the stage's MFMAs; sched_barrier keeps every instruction in its chunk, so the
+    // decode of one fragment runs beside the MFMAs of its chunk, and the fragment reads of step
+    // j+1, issued in the first chunk of step j, have a whole step of MFMAs to arrive.
+    constexpr int NCH = 4 * WB;
+    constexpr int MPC = MT * MN / WB;
+    constexpr int CPS = WB;
+    static_assert(MPC * CPS == MT * MN && (CPS == 1 || CPS == 2), "chunking");
+
+    // Stage s: wd holds the raw blocks of W(s+1); wl receives those of W(s+2).
+    auto stage = [&](auto cur, int s, const RawBlock<FMT> (&wd)[WB], RawBlock<FMT> (&wl)[WB]) __attribute__((always_inline)) {
+        constexpr bool C1 = decltype(cur)::value;
+        const uint16_t* xc = C1 ? xs1 : xs0;
+        const uint16_t* wcur = C1 ? ws1 : ws0;
+        uint16_t* xn = C1 ? xs0 : xs1;
+        uint16_t* wnx = C1 ? ws0 : ws1;
+        short8_t A[2][MT], B[2][MN];
+        frags_a(xc, 0, A[0]);
+        frags_b(wcur, 0, B[0]);
+        copy_x(s + 1, xn);
+        load_w(s + 2, wl);
+        // Blocks past K decode with zero scale and offset (+0 everywhere).
+        const bool valid = 2 * (s + 1) + hsel < nblk;
+        RawBlock<FMT> r[WB];
+        float c0[WB];
+        bool need = false;
+#pragma unroll
+        for (int i = 0; i < WB; i++) {
+            r[i] = wd[i];
+            r[i].d = valid ? r[i].d : 0.f;
+            r[i].m = valid ? r[i].m : 0.f;
+            r[i].dh = valid ? r[i].dh : 0u;
+            bool fast;
+            c0[i] = block_c0<FMT>(r[i], fast);
+            if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) need = need || (valid && !fast);
+        }
+#pragma unroll
+        for (int q = 0; q < NCH; q++) {
+            const int j = q / CPS, part = q % CPS;
+            if (j < 3 && part == 0) {
+                frags_a(xc, j + 1, A[(j + 1) & 1]);
+                frags_b(wcur, j + 1, B[(j + 1) & 1]);
+            }
+#pragma unroll
+            for (int m = 0; m < MPC; m++) {
+                const int idx = part * MPC + m;
+                mfma(A[j & 1][idx / MN], B[j & 1][idx % MN], acc[idx / MN][idx % MN]);
+            }
+            const int i = q % WB, jj = q / WB;
+            *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_fast<FMT, ST>(r[i], c0[i], jj);
+            // In-order issue: VALU work only overlaps an MFMA if it sits between MFMAs, so each
+            // MFMA is followed by a share of the chunk's fragment reads and decode arithmetic.
+#pragma unroll
+            for (int m = 0; m < MPC; m++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (j < 3 && part == 0) __builtin_amdgcn_sched_group_barrier(0x100, (MT + MN + MPC - 1) / MPC, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (need) fixup(s + 1, wnx);
+        __syncthreads();
+    };
+
+    RawBlock<FMT> wa[WB], wb[WB];
     {
+        copy_x(0, xs0);
         RawBlock<FMT> w0[WB];
-        load_x(0, xv);
         load_w(0, w0);
-        load_w(min(1, nstage - 1), w1);
-        store_x(0, xv);
-        decode_store(0, w0);
+        load_w(1, wa);
+        bool need = false;
+        decode_store(0, ws0, w0, need);
+        if (need) fixup(0, ws0);
     }
     __syncthreads();
-    for (int s = 0; s < nstage; s++) {
-        const int buf = s & 1;
-        RawBlock<FMT> w2[WB];
-        load_w(min(s + 2, nstage - 1), w2);
-        load_x(min(s + 1, nstage - 1), xv);
-        decode_store(buf ^ 1, w1);
-        mfmas(buf);
-        store_x(buf ^ 1, xv);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < WB; i++) w1[i] = w2[i];
+    using C0 = std::integral_constant<bool, false>;
+    using C1 = std::integral_constant<bool, true>;
+    int s = 0;
+    for (; s + 1 < nstage; s += 2) {
+        stage(C0{}, s, wa, wb);
+        stage(C1{}, s + 1, wb, wa);
     }
+    if (s < nstage) stage(C0{}, s, wa, wb);
 
     QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
 #pragma unroll
