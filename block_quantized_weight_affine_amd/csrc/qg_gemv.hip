@@ -13,10 +13,11 @@
 //  * X rows are staged once per workgroup in LDS as f32, in K chunks of at most 16384 values in
 //    all; the chunk's X loads are issued first, then every weight load of the chunk, so the X
 //    store to LDS waits only for X while the weights stream in.
-//  * Per unit and X row: Sx = sum of the 16 x values; per weight row the f32 partial
-//    P = sum c_i x_i over the unit's codes c_i (Q4: nibbles; Q8: the byte XOR 0x80, i.e. q + 128,
-//    converted with one instruction), then acc += d (P - 8 Sx) [+ m Sx] (Q8: d (P - 128 Sx)) --
-//    the block scale applied to the f32 partial.
+//  * Per weight row and unit the f32 partial P = sum s_i x_i over signed codes s_i, each a signed
+//    byte converted to f32 by one instruction: Q8 s = q; Q4 / Q4A s = 16 (nibble - 8), made by
+//    moving the nibble to the byte's high half and flipping its top bit.  Then acc += d P (Q8) or
+//    (d / 16) P (Q4), and Q4A adds m Sx with Sx the sum of the unit's 16 x values -- the block
+//    scale applied to the f32 partial.
 //  * After K, each accumulator is reduced across the 64 lanes with xor shuffles.
 //  * Grouped launches (exact-mode MoE): blockIdx.y is the expert; the workgroup walks the expert's
 //    row segment in chunks of at most 8 rows.
@@ -27,7 +28,8 @@
 
 namespace qg {
 
-constexpr int kGemvThreads = 256;
+constexpr int kGemvThreads = 256;   // workgroup size of the multi-row and grouped launches
+constexpr int kGemv1Threads = 512;  // single X row: 8 wavefronts of 2 weight rows share one X copy
 
 template <int NT>
 struct GemvChunk {
@@ -88,45 +90,50 @@ __device__ __forceinline__ void unit_runs(int u, int& k0, int& k1) {
     }
 }
 
-// sum_i c_i x_i over the unit's 16 codes: Q4 nibbles (x[0..7] low, x[8..15] high), Q8 q + 128.
+__device__ __forceinline__ float sbyte_f32(uint32_t word, int i) { return (float)(int8_t)(word >> (8 * i)); }
+
+// sum_i s_i x_i over the unit's 16 signed codes (x[0..7] and x[8..15] the unit's two runs): Q8
+// s = q; Q4 / Q4A s = 16 (nibble - 8), the byte (nibble << 4) ^ 0x80 read as signed.
 template <int FMT>
 __device__ __forceinline__ float unit_partial(const Unit<FMT>& w, const float (&x)[16]) {
     float p = 0.f;
     if constexpr (FMT == FMT_Q8) {
-        const uint32_t ws[4] = {w.q.x ^ 0x80808080u, w.q.y ^ 0x80808080u, w.q.z ^ 0x80808080u, w.q.w ^ 0x80808080u};
+        const uint32_t ws[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
 #pragma unroll
-        for (int i = 0; i < 16; i++) p = fmaf((float)((ws[i >> 2] >> (8 * (i & 3))) & 0xFFu), x[i], p);
+        for (int i = 0; i < 16; i++) p = fmaf(sbyte_f32(ws[i >> 2], i & 3), x[i], p);
     } else {
-        const uint32_t lo[2] = {w.q.x & 0x0F0F0F0Fu, w.q.y & 0x0F0F0F0Fu};
-        const uint32_t hi[2] = {(w.q.x >> 4) & 0x0F0F0F0Fu, (w.q.y >> 4) & 0x0F0F0F0Fu};
+        const uint32_t lo[2] = {((w.q.x << 4) & 0xF0F0F0F0u) ^ 0x80808080u, ((w.q.y << 4) & 0xF0F0F0F0u) ^ 0x80808080u};
+        const uint32_t hi[2] = {(w.q.x & 0xF0F0F0F0u) ^ 0x80808080u, (w.q.y & 0xF0F0F0F0u) ^ 0x80808080u};
 #pragma unroll
-        for (int i = 0; i < 8; i++) p = fmaf((float)((lo[i >> 2] >> (8 * (i & 3))) & 0xFFu), x[i], p);
+        for (int i = 0; i < 8; i++) p = fmaf(sbyte_f32(lo[i >> 2], i & 3), x[i], p);
 #pragma unroll
-        for (int i = 0; i < 8; i++) p = fmaf((float)((hi[i >> 2] >> (8 * (i & 3))) & 0xFFu), x[8 + i], p);
+        for (int i = 0; i < 8; i++) p = fmaf(sbyte_f32(hi[i >> 2], i & 3), x[8 + i], p);
     }
     return p;
 }
 
-// Contribution of one unit: the block scale (and offset) applied to the f32 partial.
+// Contribution of one unit: the block scale (and offset) applied to the f32 partial; sx (the sum
+// of the unit's x values) is used by Q4A only.
 template <int FMT>
 __device__ __forceinline__ float unit_value(const Unit<FMT>& w, float p, float sx) {
     if constexpr (FMT == FMT_Q8)
-        return w.d * fmaf(-128.0f, sx, p);
+        return w.d * p;
     else if constexpr (FMT == FMT_Q4)
-        return w.d * fmaf(-8.0f, sx, p);
+        return (0.0625f * w.d) * p;
     else
-        return fmaf(w.d, fmaf(-8.0f, sx, p), w.m * sx);
+        return fmaf(0.0625f * w.d, p, w.m * sx);
 }
 
 // RW weight rows starting at nrow0; NT X rows (xrow[t], -1 = zero row) -> Y rows yrow0 + t.
-template <int FMT, int XT, int RW, int NT>
+// TH threads per workgroup stage each X chunk together.
+template <int FMT, int XT, int RW, int NT, int TH>
 __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes, const void* scales,
                                           const uint16_t* offs, int nrow0, int yrow0, const int* xrow, float* xs) {
     constexpr int S = GemvChunk<NT>::steps;
     constexpr int KC = GemvChunk<NT>::kc;
     constexpr int G = (16 / RW) < S ? (16 / RW) : S;                     // steps whose loads are in flight together
     constexpr int XV = (XT == XT_F32) ? 4 : 8;                          // X values per 16-byte load
-    constexpr int XL = (KC / XV + kGemvThreads - 1) / kGemvThreads;  // X loads per thread per X row and chunk
+    constexpr int XL = (KC / XV + TH - 1) / TH;  // X loads per thread per X row and chunk
     const int lane = threadIdx.x & 63;
     const int K = p.K, units = K >> 4;
     const int KS = min(K, KC);  // LDS row stride of the staged X chunk
@@ -150,7 +157,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
         for (int t = 0; t < NT; t++)
 #pragma unroll
             for (int i = 0; i < XL; i++) {
-                const int e = XV * (int)(threadIdx.x + i * kGemvThreads);
+                const int e = XV * (int)(threadIdx.x + i * TH);
                 xl[t][i] = make_uint4(0, 0, 0, 0);
                 if (e < kn && xrow[t] >= 0) {
                     if constexpr (XT == XT_F32)
@@ -174,7 +181,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
                 for (int t = 0; t < NT; t++)
 #pragma unroll
                     for (int i = 0; i < XL; i++) {
-                        const int e = XV * (int)(threadIdx.x + i * kGemvThreads);
+                        const int e = XV * (int)(threadIdx.x + i * TH);
                         if (e < kn) {
                             float4* d = (float4*)(xs + t * KS + e);
                             const uint4 q4 = xl[t][i];
@@ -221,8 +228,10 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
                         x[8] = b0.x; x[9] = b0.y; x[10] = b0.z; x[11] = b0.w;
                         x[12] = b1.x; x[13] = b1.y; x[14] = b1.z; x[15] = b1.w;
                         float sx = 0.f;
+                        if constexpr (FMT == FMT_Q4A) {
 #pragma unroll
-                        for (int i = 0; i < 16; i++) sx += x[i];
+                            for (int i = 0; i < 16; i++) sx += x[i];
+                        }
 #pragma unroll
                         for (int r = 0; r < RW; r++)
                             acc[r][t] += unit_value<FMT>(w[j][r], unit_partial<FMT>(w[j][r], x), sx);
@@ -246,7 +255,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
         }
 }
 
-template <int FMT, int XT, int RW, int NT>
+template <int FMT, int XT, int RW, int NT, int TH>
 __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* codes, const void* scales,
                                            const uint16_t* offs, int nrow0, int c, float* xs) {
     int xrow[NT];
@@ -260,20 +269,21 @@ __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* code
         }
         xrow[t] = s;
     }
-    gemv_rows<FMT, XT, RW, NT>(p, codes, scales, offs, nrow0, c, xrow, xs);
+    gemv_rows<FMT, XT, RW, NT, TH>(p, codes, scales, offs, nrow0, c, xrow, xs);
 }
 
 // NTD > 0: dense call with NTD = T rows of X (T <= 8).  NTD == 0: grouped call; blockIdx.y is the
-// expert and the workgroup walks the expert's rows in chunks of at most 8.
-template <int FMT, int XT, int RW, int NTD>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
+// expert and the workgroup walks the expert's rows in chunks of at most 8.  TH threads per
+// workgroup, each wavefront owning RW weight rows.
+template <int FMT, int XT, int RW, int NTD, int TH>
+__global__ __launch_bounds__(TH) void gemv_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) float xs[];  // gemv_lds_bytes()
     const int wave = threadIdx.x >> 6;
-    const int nrow0 = (blockIdx.x * 4 + wave) * RW;
+    const int nrow0 = (blockIdx.x * (TH / 64) + wave) * RW;
     // Every wavefront stays to the end (the X chunks are staged by the whole workgroup); rows
     // beyond N are clamped on load and never stored.
     if constexpr (NTD > 0) {
-        gemv_chunk<FMT, XT, RW, NTD>(p, p.codes, p.scales, p.offs, nrow0, 0, xs);
+        gemv_chunk<FMT, XT, RW, NTD, TH>(p, p.codes, p.scales, p.offs, nrow0, 0, xs);
     } else {
         const int e = blockIdx.y;
         const int r0 = min(max(p.seg_off[e], 0), p.R);
@@ -283,17 +293,141 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
         const uint16_t* offs = p.experts[e].offsets;
         for (int c = r0; c < r1; c += 8) {
             switch (min(8, r1 - c)) {
-                case 1: gemv_chunk<FMT, XT, RW, 1>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 2: gemv_chunk<FMT, XT, RW, 2>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 3: gemv_chunk<FMT, XT, RW, 3>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 4: gemv_chunk<FMT, XT, RW, 4>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 5: gemv_chunk<FMT, XT, RW, 5>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 6: gemv_chunk<FMT, XT, RW, 6>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 7: gemv_chunk<FMT, XT, RW, 7>(p, codes, scales, offs, nrow0, c, xs); break;
-                default: gemv_chunk<FMT, XT, RW, 8>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 1: gemv_chunk<FMT, XT, RW, 1, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 2: gemv_chunk<FMT, XT, RW, 2, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 3: gemv_chunk<FMT, XT, RW, 3, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 4: gemv_chunk<FMT, XT, RW, 4, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 5: gemv_chunk<FMT, XT, RW, 5, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 6: gemv_chunk<FMT, XT, RW, 6, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                case 7: gemv_chunk<FMT, XT, RW, 7, TH>(p, codes, scales, offs, nrow0, c, xs); break;
+                default: gemv_chunk<FMT, XT, RW, 8, TH>(p, codes, scales, offs, nrow0, c, xs); break;
             }
         }
     }
+}
+
+// ---- single X row: streaming kernel ---------------------------------------------------------------
+// Workgroups of 16 wavefronts stay resident (at most one per CU); each stages X once into LDS (f32)
+// and wavefront w of workgroup b walks rows b * 16 + w + i * (16 * grid).  A row is cut into items
+// of up to 4 steps (4096 values); the loads of a wavefront's next item are issued before the
+// arithmetic of its current item.  Measured on MI355X for a 4096 x 4096 Q8 matrix: X first and the
+// weight loads after the barrier beats every order that puts weight loads ahead of X (the X data
+// then return behind the weights of the CU's other wavefronts), and 16-wavefront workgroups beat
+// one-shot 4-wavefront ones, which re-stage X four times as often.
+constexpr int kStreamThreads = 1024;
+constexpr int kStreamKMax = 16384;  // X in LDS as f32: at most 64 KiB
+constexpr int kStreamSteps = 4;     // steps (64 units each) per item
+
+template <int FMT, int XT>
+__global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // K floats
+    constexpr int W = kStreamThreads / 64, S = kStreamSteps;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = p.K, units = K >> 4;
+    const int items = (units + 64 * S - 1) / (64 * S);  // items per row
+    {
+        constexpr int XV = (XT == XT_F32) ? 4 : 8;
+        for (int e = XV * (int)threadIdx.x; e < K; e += XV * kStreamThreads) {
+            float4* d = (float4*)(xs + e);
+            if constexpr (XT == XT_F32) {
+                d[0] = *(const float4*)((const float*)p.X + e);
+            } else {
+                const uint4 q4 = *(const uint4*)((const uint16_t*)p.X + e);
+                const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
+                float v[8];
+#pragma unroll
+                for (int h = 0; h < 4; h++) {
+                    if constexpr (XT == XT_F16) {
+                        v[2 * h] = f16_to_f32((uint16_t)(q[h] & 0xFFFFu));
+                        v[2 * h + 1] = f16_to_f32((uint16_t)(q[h] >> 16));
+                    } else {
+                        v[2 * h] = __uint_as_float(q[h] << 16);
+                        v[2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
+                    }
+                }
+                d[0] = make_float4(v[0], v[1], v[2], v[3]);
+                d[1] = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        }
+    }
+    __syncthreads();  // the only barrier: wavefronts may leave independently after it
+
+    const int tw = W * (int)gridDim.x;
+    const float sc = p.rs ? p.rs[0] : 1.f;
+    auto load_item = [&](int row, int c, Unit<FMT> (&w)[S]) {
+#pragma unroll
+        for (int j = 0; j < S; j++) {
+            const int u = min(64 * (S * c + j) + lane, units - 1);
+            w[j] = load_unit<FMT>(p.codes, p.scales, p.offs, p.group, K, row, u);
+        }
+    };
+    auto compute_item = [&](int c, const Unit<FMT> (&w)[S], float& acc) {
+#pragma unroll
+        for (int j = 0; j < S; j++) {
+            const int u = 64 * (S * c + j) + lane;
+            if (u < units) {
+                int e0, e1;
+                unit_runs<FMT>(u, e0, e1);
+                const float4* a = (const float4*)(xs + e0);
+                const float4* b = (const float4*)(xs + e1);
+                const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+                const float x[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                     b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                float sx = 0.f;
+                if constexpr (FMT == FMT_Q4A) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) sx += x[i];
+                }
+                acc += unit_value<FMT>(w[j], unit_partial<FMT>(w[j], x), sx);
+            }
+        }
+    };
+    // Item sequence of this wavefront: (row n, chunk c) in row-major order.
+    int n = (int)blockIdx.x * W + wave, c = 0;
+    if (n >= p.N) return;
+    Unit<FMT> wa[S], wb[S];
+    float acc = 0.f;
+    load_item(n, 0, wa);
+    // One item: issue the next item's loads into `nx`, compute `cu`, finish the row if its last
+    // chunk was just done.  Returns false after the wavefront's last item.
+    auto step = [&](Unit<FMT> (&cu)[S], Unit<FMT> (&nx)[S]) __attribute__((always_inline)) {
+        int n2 = n, c2 = c + 1;
+        if (c2 == items) {
+            c2 = 0;
+            n2 = n + tw;
+        }
+        const bool more = n2 < p.N;
+        if (more) load_item(n2, c2, nx);
+        compute_item(c, cu, acc);
+        if (c + 1 == items) {
+            const float v = wave_sum(acc);
+            if (lane == 0) p.Y[n] = v * sc;
+            acc = 0.f;
+        }
+        n = n2;
+        c = c2;
+        return more;
+    };
+    while (step(wa, wb) && step(wb, wa)) {
+    }
+}
+
+// Single X row with K <= kStreamKMax: at most one workgroup per CU.
+template <int FMT, int XT>
+static bool gemv1(const GemmParams& p, hipStream_t s) {
+    if (p.K > kStreamKMax) return false;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cus[dev] = v;
+    }
+    constexpr int W = kStreamThreads / 64;
+    const int grid = std::max(1, std::min((p.N + W - 1) / W, cus[dev]));
+    hipLaunchKernelGGL((gemv1_stream_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), (size_t)p.K * 4, s, p);
+    return true;
 }
 
 // LDS bytes for the X chunks: the largest NT * min(K, chunk(NT)) over the row counts NT a chunk of
@@ -310,24 +444,29 @@ static size_t gemv_lds_bytes(int K, int nt_lo, int nt_hi) {
     return 4 * m;
 }
 
-// Rows per wavefront: 1 for a single X row (most wavefronts in flight), more as X rows grow so
-// that the X staged per workgroup stays small next to the weights it serves.
+// Rows per workgroup: a single X row uses 8 wavefronts of 2 weight rows (one X copy in LDS serves
+// 16 rows, and each X value read from LDS serves 2); more X rows use 4 wavefronts of 2 or 4 rows,
+// so that the X staged per workgroup stays small next to the weights it serves.
 template <int FMT, int XT, int NT>
 static void gemv_dense(const GemmParams& p, hipStream_t s) {
-    constexpr int RW = NT == 1 ? 1 : NT == 2 ? 2 : 4;
-    dim3 grid((p.N + 4 * RW - 1) / (4 * RW));
-    hipLaunchKernelGGL((gemv_kernel<FMT, XT, RW, NT>), grid, dim3(kGemvThreads), gemv_lds_bytes(p.K, NT, NT), s, p);
+    constexpr int RW = NT == 1 ? 2 : NT == 2 ? 2 : 4;
+    constexpr int TH = NT == 1 ? kGemv1Threads : kGemvThreads;
+    constexpr int ROWS = RW * TH / 64;
+    dim3 grid((p.N + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((gemv_kernel<FMT, XT, RW, NT, TH>), grid, dim3(TH), gemv_lds_bytes(p.K, NT, NT), s, p);
 }
 
 template <int FMT, int XT>
 static void gemv_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) {
         dim3 grid((p.N + 15) / 16, p.E);
-        hipLaunchKernelGGL((gemv_kernel<FMT, XT, 4, 0>), grid, dim3(kGemvThreads), gemv_lds_bytes(p.K, 1, 8), s, p);
+        hipLaunchKernelGGL((gemv_kernel<FMT, XT, 4, 0, kGemvThreads>), grid, dim3(kGemvThreads), gemv_lds_bytes(p.K, 1, 8), s, p);
         return;
     }
     switch (p.R) {
-        case 1: return gemv_dense<FMT, XT, 1>(p, s);
+        case 1:
+            if (gemv1<FMT, XT>(p, s)) return;
+            return gemv_dense<FMT, XT, 1>(p, s);
         case 2: return gemv_dense<FMT, XT, 2>(p, s);
         case 3: return gemv_dense<FMT, XT, 3>(p, s);
         case 4: return gemv_dense<FMT, XT, 4>(p, s);
