@@ -137,7 +137,8 @@ def setup_dense(ci: int, mode: str, copies: int):
         "name": c.name, "cfg": c, "mode": mode, "flops": 2.0 * c.T * c.N * c.K,
         "bytes": float(wbytes + xbytes + ybytes), "copies": copies, "weights": w,
         "dtype": ("f32" if mode == "exact" else c.xtype),
-        "kernel": ("gemv_kernel" if c.T <= 8 else ("gemm_exact_kernel" if mode == "exact" else "gemm_fast_kernel")),
+        "kernel": (("gemv1_stream_kernel" if c.T == 1 and c.K <= 16384 else "gemv_kernel") if c.T <= 8
+                   else ("gemm_exact_kernel" if mode == "exact" else "gemm_fast_lds_kernel")),
         "keep": (codes, scales, offs, X, Y),
     }
     return step, info
@@ -221,7 +222,7 @@ def cpu_baseline(info: dict, budget_s: float = 12.0) -> dict:
     oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
                 w["X"].view(np.uint16) if c.xtype != "f32" else w["X"], c.xtype, c.T, threads=threads)
     one = time.perf_counter() - t0
-    reps = max(1, min(50, int(budget_s / max(one, 1e-3))))
+    reps = max(1, min(5000, int(budget_s / max(one, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(reps):
         _, _, used = oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
@@ -259,6 +260,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration only: run a plain device copy of this many bytes --steps times and exit "
+                         "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -269,6 +273,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "copies": args.steps}))
+        return
 
     head = measure(args.workload, args.steps, args.warmup)
     info = head.pop("_info")
