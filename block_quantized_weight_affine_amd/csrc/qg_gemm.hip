@@ -309,17 +309,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
 // decode's VALU work is interleaved with the MFMAs (sched_group_barrier), where it runs beside
 // the matrix core.  Blocks whose fast decode (1) is not the pages' rounding are re-loaded and
 // re-decoded in the pages' order after the MFMAs; one barrier (which waits for all of the stage's
-// loads) ends the stage.  The two LDS buffers are separate arrays and the stage loop is unrolled
-// by two, so the compiler can see that the decode's stores and the MFMA reads never alias.
-template <int FMT, int ST, int WM, int MT, int MN>
+// copies) ends the stage.  The two LDS buffers are separate arrays and the stage loop is unrolled,
+// so the compiler can see that the decode's stores and the MFMA reads never alias.
+//
+// Small tiles (DP = 4) have stages too short to cover a memory round trip with one stage of lead:
+// their X chunks load into a ring of 4 register sets 4 stages ahead (buffer loads, zero past K and
+// past the tile) and are stored to LDS at the end of the stage before they are used, and the raw
+// weight blocks load into 4 register sets, 4 stages ahead.  (A deeper ring of direct LDS copies
+// would not help: the stage-end barrier waits for every copy in flight.)
+//
+// Decode ownership: a stage holds 2 BN blocks = 8 BN fragments of 8 values, FPT = BN / 32 per
+// thread; a thread owns FPB = min(FPT, 4) fragments of each of its blocks, so narrow tiles still
+// spread the decode over all 256 threads.
+template <int FMT, int ST, int WM, int MT, int MN, int DP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p) {
     constexpr int WN = 4 / WM;
     constexpr int BT = 32 * MT * WM;
     constexpr int BN = 32 * MN * WN;
-    constexpr int PITCH = 72;              // halves per weight-tile row: 64 + 8 (16-byte pad)
-    constexpr int WB = 2 * BN / kThreads;  // weight blocks decoded per thread per stage
-    constexpr int XCH = BT / 32;           // X row-octets copied per wavefront per stage
-    static_assert(WB >= 1 && 2 * BN % kThreads == 0 && BT % 32 == 0, "tile");
+    constexpr int PITCH = 72;               // halves per weight-tile row: 64 + 8 (16-byte pad)
+    constexpr int FPT = BN / 32;            // 8-value fragments decoded per thread per stage
+    constexpr int FPB = FPT < 4 ? FPT : 4;  // fragments of one block a thread decodes
+    constexpr int TPB = 4 / FPB;            // threads sharing one block
+    constexpr int WB = FPT / FPB;           // blocks per thread per stage
+    constexpr int XCH = BT / 32;            // X row-octets copied per wavefront per stage
+    static_assert(FPT >= 1 && (FPT == 1 || FPT == 2 || FPT % 4 == 0) && BT % 32 == 0, "tile");
     __shared__ __attribute__((aligned(16))) uint16_t xs0[BT * 64];
     __shared__ __attribute__((aligned(16))) uint16_t xs1[BT * 64];
     __shared__ __attribute__((aligned(16))) uint16_t ws0[BN * PITCH];
@@ -333,32 +346,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     const int g = lane >> 5, li = lane & 31;
     const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
 
-    // X copy i of wavefront w: rows 8 (4 i + w) .. +7 of the slab; this lane's slot is row
-    // r = 8 (4 i + w) + lane / 8, position lane % 8, holding chunk xc = (lane % 8) ^ ((r / 2) % 8),
-    // where (r / 2) % 8 = 4 (w % 2) + lane / 16.
-    const int xc = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    // X rows r0 .. r1-1 as one buffer resource: offsets past its end (rows past the tile) and the
+    // offsets used for columns past K read as zero.
     uint16_t* const xbase = (uint16_t*)p.X + (size_t)r0 * K;
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(xbase, 0, (r1 - r0) * K * 2, 0x00020000);
+    // DP == 1, X copy i of wavefront w: rows 8 (4 i + w) .. +7 of the slab; this lane's slot is
+    // row r = 8 (4 i + w) + lane / 8, position lane % 8, holding chunk xc = (lane % 8) ^ ((r / 2) % 8),
+    // where (r / 2) % 8 = 4 (w % 2) + lane / 16.
+    // DP > 1, X chunk i of a thread: row r = tid / 8 + 32 i, chunk tid % 8, loaded DP stages ahead
+    // into registers and stored at slot (tid % 8) ^ ((r / 2) % 8), where (r / 2) % 8 = (tid / 16) % 8.
+    const int xc = DP == 1 ? (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7) : (tid & 7);
     int xoff[XCH];
 #pragma unroll
-    for (int i = 0; i < XCH; i++) xoff[i] = (8 * (4 * i + wave) + (lane >> 3)) * K * 2 + 16 * xc;
+    for (int i = 0; i < XCH; i++)
+        xoff[i] = (DP == 1 ? 8 * (4 * i + wave) + (lane >> 3) : (tid >> 3) + 32 * i) * K * 2 + 16 * xc;
+    auto xkoff = [&](int st) { return st * 64 + 8 * xc < K ? st * 128 : 0x40000000; };  // 2^30 > any valid offset
     auto copy_x = [&](int st, uint16_t* xs) {
-        const int koff = st * 64 + 8 * xc < K ? st * 128 : 0x40000000;  // 2^30 > any valid offset
+        const int koff = xkoff(st);
 #pragma unroll
         for (int i = 0; i < XCH; i++)
             buffer_copy16_lds(xrs, xs + 8 * (4 * i + wave) * 64, xoff[i] + koff);
     };
+    auto load_x = [&](int st, u32x4_t (&v)[XCH]) {
+        const int koff = xkoff(st);
+#pragma unroll
+        for (int i = 0; i < XCH; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i] + koff, 0, 0);
+    };
+    auto store_x = [&](uint16_t* xs, const u32x4_t (&v)[XCH]) {
+        const int slot = (tid & 7) ^ ((tid >> 4) & 7);
+#pragma unroll
+        for (int i = 0; i < XCH; i++) *(u32x4_t*)(xs + ((tid >> 3) + 32 * i) * 64 + 8 * slot) = v[i];
+    };
 
-    // Weight block i of a thread: tile row (tid + i * threads) / 2, block 2 st + hsel of that row,
-    // written to columns 32 hsel .. 32 hsel + 31.  Blocks past K are loaded clamped and decoded
-    // with zero scale and offset, which gives +0 for every element.
-    const int hsel = tid & 1;
+    // Weight block i of a thread: q = tid / TPB + i * (threads / TPB) of the stage's 2 BN blocks,
+    // tile row q / 2, block 2 st + hsel (hsel = q % 2) of that row, written to columns
+    // 32 hsel .. 32 hsel + 31; the thread decodes its fragments fb .. fb + FPB - 1 of it.  Blocks
+    // past K are loaded clamped and decoded with zero scale and offset, which gives +0 for every
+    // element.
+    const int hsel = (tid / TPB) & 1;
+    const int fb = (tid % TPB) * FPB;
+    auto blk = [&](int i) { return tid / TPB + i * (kThreads / TPB); };
     const QG_GLOBAL uint8_t* wc[WB];
     const QG_GLOBAL uint8_t* wsc[WB];
     const QG_GLOBAL uint16_t* wof[WB];
 #pragma unroll
     for (int i = 0; i < WB; i++) {
-        const size_t n = (size_t)min(n0 + (tid + i * kThreads) / 2, p.N - 1);
+        const size_t n = (size_t)min(n0 + blk(i) / 2, p.N - 1);
         wc[i] = gptr<uint8_t>((const uint8_t*)p.codes + n * (FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1)));
         wsc[i] = gptr<uint8_t>((const uint8_t*)p.scales + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
         wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(p.offs + n * (size_t)(K / p.group)) : nullptr;
@@ -384,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             }
         }
     };
-    auto w_dst = [&](uint16_t* ws, int i) { return ws + ((tid + i * kThreads) >> 1) * PITCH + 32 * hsel; };
+    auto w_dst = [&](uint16_t* ws, int i) { return ws + (blk(i) >> 1) * PITCH + 32 * hsel; };
     // Fast decode (1) of stage st into ws; need is set where a valid block needs the pages' order.
     auto decode_store = [&](int st, uint16_t* ws, const RawBlock<FMT> (&w)[WB], bool& need) {
         const bool valid = 2 * st + hsel < nblk;
@@ -394,16 +427,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             r.d = valid ? r.d : 0.f;
             r.m = valid ? r.m : 0.f;
             r.dh = valid ? r.dh : 0u;
-            short8_t f[4];
-            block_to_frags16_fast<FMT, ST>(r, f);
-            if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) {
-                bool fast;
-                block_c0<FMT>(r, fast);
-                need = need || (valid && !fast);
-            }
+            bool fast;
+            const float c0 = block_c0<FMT>(r, fast);
+            if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) need = need || (valid && !fast);
             uint16_t* d = w_dst(ws, i);
 #pragma unroll
-            for (int j = 0; j < 4; j++) *(short8_t*)(d + 8 * j) = f[j];
+            for (int j = 0; j < FPB; j++) *(short8_t*)(d + 8 * (fb + j)) = frag16_fast<FMT, ST>(r, c0, fb + j);
         }
     };
     // The pages' order for the blocks of stage st (rare: non-positive scales, inexact m - 8d).
@@ -416,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             block_frags16_fixup<FMT, ST>(w[i], f);
             uint16_t* d = w_dst(ws, i);
 #pragma unroll
-            for (int j = 0; j < 4; j++) *(short8_t*)(d + 8 * j) = f[j];
+            for (int j = 0; j < FPB; j++) *(short8_t*)(d + 8 * (fb + j)) = f[fb + j];
         }
     };
 
@@ -447,27 +476,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     };
 
-    // A stage is cut into NCH chunks, one per decoded fragment (WB blocks x 4 fragments), each
-    // with MPC of the stage's MFMAs; sched_barrier keeps every instruction in its chunk, so the
-    // decode of one fragment runs beside the MFMAs of its chunk, and the fragment reads of step
-    // j+1, issued in the first chunk of step j, have a whole step of MFMAs to arrive.
-    constexpr int NCH = 4 * WB;
-    constexpr int MPC = MT * MN / WB;
-    constexpr int CPS = WB;
-    static_assert(MPC * CPS == MT * MN && (CPS == 1 || CPS == 2), "chunking");
+    // A stage is cut into NCH chunks (CPS per MFMA step), each with MPC of the stage's MFMAs and
+    // at most one fragment decode (fragment f of the thread in chunk f * NCH / FPT);
+    // sched_barrier keeps every instruction in its chunk, so a decode runs beside the MFMAs of its
+    // chunk, and the fragment reads of step j+1, issued in the first chunk of step j, have a whole
+    // step of MFMAs to arrive.
+    constexpr int CPS = FPT >= 4 ? FPT / 4 : 1;
+    constexpr int NCH = 4 * CPS;
+    constexpr int MPC = MT * MN / CPS;
+    static_assert(MPC * CPS == MT * MN && (CPS == 1 || CPS == 2) && NCH % FPT == 0, "chunking");
 
-    // Stage s: wd holds the raw blocks of W(s+1); wl receives those of W(s+2).
-    auto stage = [&](auto cur, int s, const RawBlock<FMT> (&wd)[WB], RawBlock<FMT> (&wl)[WB]) __attribute__((always_inline)) {
-        constexpr bool C1 = decltype(cur)::value;
-        const uint16_t* xc = C1 ? xs1 : xs0;
-        const uint16_t* wcur = C1 ? ws1 : ws0;
-        uint16_t* xn = C1 ? xs0 : xs1;
-        uint16_t* wnx = C1 ? ws0 : ws1;
+    // Raw weights of stage t live in register set (t - 1) % NS and load NS stages ahead; with
+    // DP > 1, X of stage t lives in register set t % DP and loads DP stages ahead.  The loop is
+    // unrolled by U so every set and buffer index is a compile-time constant.
+    constexpr int NS = DP == 1 ? 2 : DP;
+    constexpr int U = NS;
+    static_assert(U % 2 == 0, "the LDS buffers alternate");
+    RawBlock<FMT> wr[NS][WB];
+    u32x4_t xr[DP == 1 ? 1 : DP][XCH];
+
+    auto stage = [&](auto uc, int s) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        const uint16_t* xc = (u & 1) ? xs1 : xs0;
+        const uint16_t* wcur = (u & 1) ? ws1 : ws0;
+        uint16_t* xn = (u & 1) ? xs0 : xs1;
+        uint16_t* wnx = (u & 1) ? ws0 : ws1;
         short8_t A[2][MT], B[2][MN];
         frags_a(xc, 0, A[0]);
         frags_b(wcur, 0, B[0]);
-        copy_x(s + 1, xn);
-        load_w(s + 2, wl);
+        if constexpr (DP == 1)
+            copy_x(s + 1, xn);
+        else
+            load_x(s + DP, xr[u % DP]);
+        load_w(s + NS, wr[(u + NS - 1) % NS]);
         // Blocks past K decode with zero scale and offset (+0 everywhere).
         const bool valid = 2 * (s + 1) + hsel < nblk;
         RawBlock<FMT> r[WB];
@@ -475,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
         bool need = false;
 #pragma unroll
         for (int i = 0; i < WB; i++) {
-            r[i] = wd[i];
+            r[i] = wr[u % NS][i];
             r[i].d = valid ? r[i].d : 0.f;
             r[i].m = valid ? r[i].m : 0.f;
             r[i].dh = valid ? r[i].dh : 0u;
@@ -495,8 +536,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
                 const int idx = part * MPC + m;
                 mfma(A[j & 1][idx / MN], B[j & 1][idx % MN], acc[idx / MN][idx % MN]);
             }
-            const int i = q % WB, jj = q / WB;
-            *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_fast<FMT, ST>(r[i], c0[i], jj);
+            if (q % (NCH / FPT) == 0) {
+                const int f = q / (NCH / FPT);  // fragment index of this thread: block f % WB, fragment f / WB
+                const int i = f % WB, jj = fb + f / WB;
+                *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_fast<FMT, ST>(r[i], c0[i], jj);
+            }
             // In-order issue: VALU work only overlaps an MFMA if it sits between MFMAs, so each
             // MFMA is followed by a share of the chunk's fragment reads and decode arithmetic.
 #pragma unroll
@@ -507,29 +551,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (DP > 1) store_x(xn, xr[(u + 1) % DP]);
         if (need) fixup(s + 1, wnx);
         __syncthreads();
     };
 
-    RawBlock<FMT> wa[WB], wb[WB];
     {
-        copy_x(0, xs0);
+        if constexpr (DP == 1) {
+            copy_x(0, xs0);
+        } else {
+            u32x4_t x0[XCH];
+            load_x(0, x0);
+#pragma unroll
+            for (int t = 1; t < DP; t++) load_x(t, xr[t]);
+            store_x(xs0, x0);
+        }
         RawBlock<FMT> w0[WB];
         load_w(0, w0);
-        load_w(1, wa);
+#pragma unroll
+        for (int t = 1; t < NS; t++) load_w(t, wr[t - 1]);
         bool need = false;
         decode_store(0, ws0, w0, need);
         if (need) fixup(0, ws0);
     }
     __syncthreads();
-    using C0 = std::integral_constant<bool, false>;
-    using C1 = std::integral_constant<bool, true>;
     int s = 0;
-    for (; s + 1 < nstage; s += 2) {
-        stage(C0{}, s, wa, wb);
-        stage(C1{}, s + 1, wb, wa);
+    for (; s + U - 1 < nstage; s += U) {
+        stage(std::integral_constant<int, 0>{}, s);
+        stage(std::integral_constant<int, 1>{}, s + 1);
+        if constexpr (U > 2) {
+            stage(std::integral_constant<int, 2 % U>{}, s + 2);
+            stage(std::integral_constant<int, 3 % U>{}, s + 3);
+        }
     }
-    if (s < nstage) stage(C0{}, s, wa, wb);
+    if (s < nstage) stage(std::integral_constant<int, 0>{}, s);
+    if constexpr (U > 2) {
+        if (s + 1 < nstage) stage(std::integral_constant<int, 1>{}, s + 1);
+        if (s + 2 < nstage) stage(std::integral_constant<int, 2 % U>{}, s + 2);
+    }
 
     QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
 #pragma unroll
@@ -693,11 +752,11 @@ static void fast_launch(const GemmParams& p, bool grouped, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fast_kernel<FMT, ST, MT, MN>), grid, dim3(kThreads), 0, s, p, grouped);
 }
 
-template <int FMT, int ST, int WM, int MT, int MN>
+template <int FMT, int ST, int WM, int MT, int MN, int DP>
 static void fast_lds_launch(const GemmParams& p, hipStream_t s) {
     constexpr int BT = 32 * MT * WM, BN = 32 * MN * (4 / WM);
     dim3 grid((p.N + BN - 1) / BN, (p.R + BT - 1) / BT);
-    hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN, DP>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <int FMT, int ST>
@@ -706,10 +765,10 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     // The largest tile that still gives about one workgroup per CU: big tiles amortize each
     // decoded weight over more tokens and each staged X row over more weight rows.
     auto wgs = [&](int bt, int bn) { return (long)((p.N + bn - 1) / bn) * ((p.R + bt - 1) / bt); };
-    if (wgs(256, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 4, 4>(p, s);
-    if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4>(p, s);
-    if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2>(p, s);
-    return fast_lds_launch<FMT, ST, 2, 1, 2>(p, s);
+    if (wgs(256, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 4, 4, 1>(p, s);
+    if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4, 4>(p, s);
+    if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
+    return fast_lds_launch<FMT, ST, 2, 1, 2, 4>(p, s);
 }
 
 hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s) {

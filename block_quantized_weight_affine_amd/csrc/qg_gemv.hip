@@ -272,10 +272,20 @@ __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* code
     gemv_rows<FMT, XT, RW, NT, TH>(p, codes, scales, offs, nrow0, c, xrow, xs);
 }
 
+// Grouped launches: the NT (1..NTG) X rows of one chunk of an expert's segment.
+template <int FMT, int XT, int RW, int TH, int NTG>
+__device__ __forceinline__ void gemv_grouped_chunk(const GemmParams& p, const void* codes, const void* scales,
+                                                   const uint16_t* offs, int nrow0, int c, int nt, float* xs) {
+    if constexpr (NTG > 1) {
+        if (nt < NTG) return gemv_grouped_chunk<FMT, XT, RW, TH, NTG - 1>(p, codes, scales, offs, nrow0, c, nt, xs);
+    }
+    gemv_chunk<FMT, XT, RW, NTG, TH>(p, codes, scales, offs, nrow0, c, xs);
+}
+
 // NTD > 0: dense call with NTD = T rows of X (T <= 8).  NTD == 0: grouped call; blockIdx.y is the
-// expert and the workgroup walks the expert's rows in chunks of at most 8.  TH threads per
+// expert and the workgroup walks the expert's rows in chunks of at most NTG.  TH threads per
 // workgroup, each wavefront owning RW weight rows.
-template <int FMT, int XT, int RW, int NTD, int TH>
+template <int FMT, int XT, int RW, int NTD, int TH, int NTG = 8>
 __global__ __launch_bounds__(TH) void gemv_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) float xs[];  // gemv_lds_bytes()
     const int wave = threadIdx.x >> 6;
@@ -291,18 +301,8 @@ __global__ __launch_bounds__(TH) void gemv_kernel(GemmParams p) {
         const void* codes = p.experts[e].codes;
         const void* scales = p.experts[e].scales;
         const uint16_t* offs = p.experts[e].offsets;
-        for (int c = r0; c < r1; c += 8) {
-            switch (min(8, r1 - c)) {
-                case 1: gemv_chunk<FMT, XT, RW, 1, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 2: gemv_chunk<FMT, XT, RW, 2, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 3: gemv_chunk<FMT, XT, RW, 3, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 4: gemv_chunk<FMT, XT, RW, 4, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 5: gemv_chunk<FMT, XT, RW, 5, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 6: gemv_chunk<FMT, XT, RW, 6, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                case 7: gemv_chunk<FMT, XT, RW, 7, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-                default: gemv_chunk<FMT, XT, RW, 8, TH>(p, codes, scales, offs, nrow0, c, xs); break;
-            }
-        }
+        for (int c = r0; c < r1; c += NTG)
+            gemv_grouped_chunk<FMT, XT, RW, TH, NTG>(p, codes, scales, offs, nrow0, c, min(NTG, r1 - c), xs);
     }
 }
 

@@ -117,6 +117,45 @@ def test_zero_weights_give_exact_zero(orc):
         assert torch.all(Y == 0), (T, mode)
 
 
+@pytest.mark.parametrize("K", [16384, 16416])
+def test_gemv_single_row_long_k(orc, K):
+    """T = 1 at the longest K whose X fits the streaming kernel's LDS copy, and just past it (the
+    chunked kernel takes over)."""
+    N = 40
+    w = synth.make_dense("q8", N, K, 1, "f32", 1.0, 990 + K)
+    codes, scales, offs = weights_dev(w)
+    Y = torch.full((2, N), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qgemv("q8", codes, scales, offs, w["group"], dev_x(w["X"], "f32"), Y, N, K, 1)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    Yr, S = _ref(orc, "q8", w, w["X"], "f32", N, K, 1)
+    check_tol(y[:1], Yr, S, TAU["exact"], f"gemv T=1 K={K}")
+    assert np.all(np.isnan(y[1:]))
+
+
+# Shapes that reach each fast tile configuration (sampled outputs): 128 x 256 and 128 x 128 tiles
+# with the 4-deep register prefetch, and 64 x 128 tiles over a long K; the stage counts 15, 10 and
+# 33 leave 3, 2 and 1 stages after the 4-way unrolled loop.
+TILE_SHAPES = [
+    ("q4", 6400, 928, 1024, "f16"),
+    ("q4a", 3200, 640, 1000, "bf16"),
+    ("q8", 4096, 2080, 512, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", TILE_SHAPES, ids=lambda c: "-".join(map(str, c)))
+def test_fast_tile_configs_sampled(orc, case):
+    fmt, N, K, T, xtype = case
+    print(f"fast tile shape {case}", flush=True)
+    w = synth.make_dense(fmt, N, K, T, xtype, 1.0, 700 + K)
+    Y, _ = _run(fmt, w, w["X"], xtype, N, K, T, "fast")
+    ns = sample_idx(N, 160, 3)
+    ts = sample_idx(T, 24, 4)
+    Yr, S = _ref(orc, fmt, w, w["X"], xtype, N, K, T, ns=ns, ts=ts)
+    check_tol(Y[np.ix_(ts, ns)], Yr, S, TAU["fast"], str(case))
+    assert np.all(np.isfinite(Y))
+
+
 # ---- the workloads at full size (sampled outputs), in the launch configuration the benchmark uses ----
 FULL = [
     (1, "exact"), (2, "exact"), (2, "fast"), (3, "fast"),
