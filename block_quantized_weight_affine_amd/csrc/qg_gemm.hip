@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
 // Decode ownership: a stage holds 2 BN blocks = 8 BN fragments of 8 values, FPT = BN / 32 per
 // thread; a thread owns FPB = min(FPT, 4) fragments of each of its blocks, so narrow tiles still
 // spread the decode over all 256 threads.
-template <int FMT, int ST, int WM, int MT, int MN, int DP>
+template <int FMT, int ST, int WM, int MT, int MN, int DP, bool GR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p) {
     constexpr int WN = 4 / WM;
     constexpr int BT = 32 * MT * WM;
@@ -335,10 +335,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     static_assert(FPT >= 1 && (FPT == 1 || FPT == 2 || FPT % 4 == 0) && BT % 32 == 0, "tile");
     __shared__ __attribute__((aligned(16))) uint16_t xs0[BT * 64];
     __shared__ __attribute__((aligned(16))) uint16_t xs1[BT * 64];
-    __shared__ __attribute__((aligned(16))) uint16_t ws0[BN * PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t ws1[BN * PITCH];
+    // The last row's pad is never touched: leaving it out keeps two 32 x 256 grouped workgroups
+    // (and their tile lookup slot) within one CU's 160 KiB.
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[BN * PITCH - 8];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[BN * PITCH - 8];
 
-    const int r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
+    // Grouped (MoE) launches: blockIdx.y enumerates the row tiles of every expert's segment
+    // (find_tile); the tile's weights are its expert's.  X rows are rows r0 .. r1-1 of p.X either way.
+    int e = 0, r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
+    if constexpr (GR) {
+        if (!find_tile<BT>(p, true, e, r0, r1)) return;
+    }
+    const void* const wcodes = GR ? p.experts[e].codes : p.codes;
+    const void* const wscales = GR ? p.experts[e].scales : p.scales;
+    const uint16_t* const woffs = GR ? p.experts[e].offsets : p.offs;
     const int n0 = blockIdx.x * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -392,9 +402,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
 #pragma unroll
     for (int i = 0; i < WB; i++) {
         const size_t n = (size_t)min(n0 + blk(i) / 2, p.N - 1);
-        wc[i] = gptr<uint8_t>((const uint8_t*)p.codes + n * (FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1)));
-        wsc[i] = gptr<uint8_t>((const uint8_t*)p.scales + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
-        wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(p.offs + n * (size_t)(K / p.group)) : nullptr;
+        wc[i] = gptr<uint8_t>((const uint8_t*)wcodes + n * (FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1)));
+        wsc[i] = gptr<uint8_t>((const uint8_t*)wscales + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
+        wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(woffs + n * (size_t)(K / p.group)) : nullptr;
     }
     auto load_w = [&](int st, RawBlock<FMT> (&w)[WB]) {
         const int b = min(2 * st + hsel, nblk - 1);
@@ -600,7 +610,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 const int r = r0 + wm * 32 * MT + mt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (r < r1) Y[(size_t)r * p.N + n] = acc[mt][mn][i];
+                if (r < r1) {
+                    if constexpr (GR)  // grouped calls may scale each output row
+                        Y[(size_t)r * p.N + n] = p.rs ? acc[mt][mn][i] * p.rs[r] : acc[mt][mn][i];
+                    else
+                        Y[(size_t)r * p.N + n] = acc[mt][mn][i];
+                }
             }
         }
 }
@@ -752,16 +767,21 @@ static void fast_launch(const GemmParams& p, bool grouped, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fast_kernel<FMT, ST, MT, MN>), grid, dim3(kThreads), 0, s, p, grouped);
 }
 
-template <int FMT, int ST, int WM, int MT, int MN, int DP>
+template <int FMT, int ST, int WM, int MT, int MN, int DP, bool GR = false>
 static void fast_lds_launch(const GemmParams& p, hipStream_t s) {
     constexpr int BT = 32 * MT * WM, BN = 32 * MN * (4 / WM);
-    dim3 grid((p.N + BN - 1) / BN, (p.R + BT - 1) / BT);
-    hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN, DP>), grid, dim3(kThreads), 0, s, p);
+    dim3 grid((p.N + BN - 1) / BN, grid_rows(p, GR, BT));
+    hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN, DP, GR>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <int FMT, int ST>
 static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
-    if (grouped) return fast_launch<FMT, ST, 1, 2>(p, grouped, s);
+    // Grouped launches: 32-row tiles (MoE segments are short), 256 weight rows, 4-deep prefetch;
+    // gathered X rows (row_src) take the register-direct kernel.
+    if (grouped) {
+        if (p.row_src) return fast_launch<FMT, ST, 1, 2>(p, grouped, s);
+        return fast_lds_launch<FMT, ST, 1, 1, 2, 4, true>(p, s);
+    }
     // The largest tile that still gives about one workgroup per CU: big tiles amortize each
     // decoded weight over more tokens and each staged X row over more weight rows.
     auto wgs = [&](int bt, int bn) { return (long)((p.N + bn - 1) / bn) * ((p.R + bt - 1) / bt); };
