@@ -112,6 +112,24 @@ __device__ __forceinline__ float unit_partial(const Unit<FMT>& w, const float (&
     return p;
 }
 
+// The unit's 16 signed codes as f32 (the factors unit_partial multiplies x by), for reuse across
+// several X rows.
+template <int FMT>
+__device__ __forceinline__ void unit_codes(const Unit<FMT>& w, float (&c)[16]) {
+    if constexpr (FMT == FMT_Q8) {
+        const uint32_t ws[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+#pragma unroll
+        for (int i = 0; i < 16; i++) c[i] = sbyte_f32(ws[i >> 2], i & 3);
+    } else {
+        const uint32_t lo[2] = {((w.q.x << 4) & 0xF0F0F0F0u) ^ 0x80808080u, ((w.q.y << 4) & 0xF0F0F0F0u) ^ 0x80808080u};
+        const uint32_t hi[2] = {(w.q.x & 0xF0F0F0F0u) ^ 0x80808080u, (w.q.y & 0xF0F0F0F0u) ^ 0x80808080u};
+#pragma unroll
+        for (int i = 0; i < 8; i++) c[i] = sbyte_f32(lo[i >> 2], i & 3);
+#pragma unroll
+        for (int i = 0; i < 8; i++) c[8 + i] = sbyte_f32(hi[i >> 2], i & 3);
+    }
+}
+
 // Contribution of one unit: the block scale (and offset) applied to the f32 partial; sx (the sum
 // of the unit's x values) is used by Q4A only.
 template <int FMT>
@@ -217,6 +235,10 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
                     unit_runs<FMT>(u, e0, e1);
                     e0 -= k0;
                     e1 -= k0;
+                    // each row's codes are converted once and serve all NT X rows
+                    float cv[RW][16];
+#pragma unroll
+                    for (int r = 0; r < RW; r++) unit_codes<FMT>(w[j][r], cv[r]);
 #pragma unroll
                     for (int t = 0; t < NT; t++) {
                         float x[16];
@@ -233,8 +255,12 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
                             for (int i = 0; i < 16; i++) sx += x[i];
                         }
 #pragma unroll
-                        for (int r = 0; r < RW; r++)
-                            acc[r][t] += unit_value<FMT>(w[j][r], unit_partial<FMT>(w[j][r], x), sx);
+                        for (int r = 0; r < RW; r++) {
+                            float pr = 0.f;
+#pragma unroll
+                            for (int i = 0; i < 16; i++) pr = fmaf(cv[r][i], x[i], pr);
+                            acc[r][t] += unit_value<FMT>(w[j][r], pr, sx);
+                        }
                     }
                 }
             }
