@@ -196,7 +196,7 @@ qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, 
         E > kMaxGridY || x_rows < 0)
         return QG_ESHAPE;
     if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
-    if (mode == QG_FAST && (R + 31) / 32 + std::min(E, R) > kMaxGridY) return QG_ESHAPE;
+    if ((mode == QG_FAST || R > 8 * E) && (R + 31) / 32 + std::min(E, R) > kMaxGridY) return QG_ESHAPE;
     if (R == 0) return QG_OK;
     if (!experts || !seg_off || !X || !Y) return QG_EINVAL;
     if (!aligned(experts, 8) || !aligned(seg_off, 4) || !aligned(X, 16) || !aligned(Y, 4) ||
@@ -216,7 +216,13 @@ qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, 
     p.K = K;
     p.R = R;
     p.E = E;
-    if (mode == QG_EXACT) return launched(qg::launch_gemv(fmt, xt, p, true, stream));
+    // Exact mode: short segments (at most 8 rows per expert on average) stream each expert's
+    // weights once through the GEMV; longer ones would make the GEMV re-read them for every 8 rows,
+    // so they take the f32 MFMA tile kernel.
+    if (mode == QG_EXACT) {
+        if (R <= 8 * E) return launched(qg::launch_gemv(fmt, xt, p, true, stream));
+        return launched(qg::launch_gemm_exact(fmt, xt, p, true, stream));
+    }
     return launched(qg::launch_gemm_fast(fmt, xt, p, true, stream));
 }
 

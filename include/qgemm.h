@@ -153,8 +153,11 @@ qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, i
  * x_r = X[row_src[r]] if row_src is given (row ids outside [0, x_rows) read as zeros) else X[r].
  * experts is a DEVICE array of E qg_expert (all of format fmt, each [N][K]); seg_off is a DEVICE
  * int32 [E+1], non-decreasing, seg_off[0] >= 0, seg_off[E] <= R (rows outside every segment are
- * not written).  QG_EXACT: X f32 / f16 / bf16, f32 FMA.  QG_FAST: X f16 or bf16 (for f32 rows,
- * first run qg_x_half and pass its Xh and rs), f16 / bf16 MFMA.  Y f32 [R][N]. */
+ * not written).  QG_EXACT: X f32 / f16 / bf16, f32 arithmetic (f32 FMA when R <= 8 E, i.e. short
+ * segments; the f32 MFMA tile kernel otherwise).  QG_FAST: X f16 or bf16 (for f32 rows, first run
+ * qg_x_half and pass its Xh and rs), f16 / bf16 MFMA.  Y f32 [R][N].  QG_ESHAPE also when a
+ * tile-kernel launch (QG_FAST, or QG_EXACT with R > 8 E) would need more than 65535 row tiles
+ * ((R + 31) / 32 + min(E, R)). */
 qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group,
                             const int32_t* seg_off, const int32_t* row_src, int x_rows,
                             const void* X, qg_xtype xt, const float* rs, float* Y, int N, int K,

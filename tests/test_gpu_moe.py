@@ -46,17 +46,18 @@ def _plan_dev(plan):
     return {k: dev(np.ascontiguousarray(v)) for k, v in plan.items() if isinstance(v, np.ndarray)}
 
 
-@pytest.mark.parametrize("mode", ["exact", "fast", "fast_gather", "fast_long_segment"])
+@pytest.mark.parametrize("mode", ["exact", "fast", "fast_gather", "fast_long_segment", "exact_long_segment"])
 def test_grouped_matches_oracle(orc, mode):
     """Grouped gate|up on seeded rows: every expert's segment against the oracle (rows gathered through
     row_src in exact mode; pre-scaled f16 rows in fast mode; f16 rows gathered through row_src in
     fast_gather; one expert taking every token, so its segment spans several row tiles, in
-    fast_long_segment)."""
+    fast_long_segment; the same in exact mode, where R = 150 > 8 E sends the call to the f32 MFMA
+    tile kernel instead of the GEMV)."""
     E, H, I, T, k = 8, 256, 96, 75, 2
     m = synth.make_moe(E, H, I, T, 21)
     lg = m["logits"].reshape(T, E).copy()
     lg[:, 5] = -1e9                      # expert 5 unused
-    if mode == "fast_long_segment":
+    if mode.endswith("long_segment"):
         lg[:, 2] += 1e6                  # expert 2 in every token's top k
     plan = orc.moe_plan(lg, T, E, k)
     R = plan["R"]
@@ -64,8 +65,9 @@ def test_grouped_matches_oracle(orc, mode):
     pd = _plan_dev({"seg_off": plan["seg_off"], "row_src": plan["row_src"]})
     X = m["X"].reshape(T, H)
     Y = torch.full((R, 2 * I), float("nan"), device="cuda")
-    if mode == "exact":
-        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], pd["row_src"], T, dev(X), None, Y, 2 * I, H, R, E, mode)
+    if mode.startswith("exact"):
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], pd["row_src"], T, dev(X), None, Y, 2 * I, H, R, E,
+                             "exact")
         Xo, xt = X[plan["row_src"]], "f32"
     elif mode == "fast_gather":
         X16 = X.astype(np.float16)
@@ -87,9 +89,9 @@ def test_grouped_matches_oracle(orc, mode):
         if r0 == r1:
             continue
         Yr, Sr, _ = orc.gemm("q4", m["gu_codes"][e], m["gu_scales"][e], None, 64, 2 * I, H, Xo[r0:r1], xt, r1 - r0)
-        check_tol(y[r0:r1], Yr, Sr, TAU["exact" if mode == "exact" else "fast"], f"expert {e}")
+        check_tol(y[r0:r1], Yr, Sr, TAU["exact" if mode.startswith("exact") else "fast"], f"expert {e}")
     assert seg[6] - seg[5] == 0
-    if mode == "fast_long_segment":
+    if mode.endswith("long_segment"):
         assert seg[3] - seg[2] == T
 
 
