@@ -117,6 +117,37 @@ def test_zero_weights_give_exact_zero(orc):
         assert torch.all(Y == 0), (T, mode)
 
 
+@pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
+@pytest.mark.parametrize("shape", [(200, 320, 40), (512, 1024, 300)], ids=["small-tiles", "128x128-tiles"])
+def test_fast_blocks_needing_pages_order(orc, fmt, shape):
+    """Fast mode through blocks whose one-FMA decode is not the pages' rounding: negative and zero
+    scales, and (Q4A) offsets next to scales so large that m - 8d is inexact in f32; every third
+    block is affected, so every wavefront re-decodes some blocks in the pages' order."""
+    N, K, T = shape
+    w = synth.make_dense(fmt, N, K, T, "bf16" if fmt == "q4a" else "f16", 1.0, 77 + N)
+    sc = w["scales"].copy()
+    nb = sc.size
+    neg, zero = np.arange(0, nb, 3), np.arange(1, nb, 9)
+    if fmt == "q8":
+        sc[neg] = -np.abs(sc[neg])
+        sc[zero] = 0.0
+    else:
+        sc[neg] |= np.uint16(0x8000)
+        sc[zero] = 0
+    w["scales"] = sc
+    if fmt == "q4a":
+        off = w["offsets"].copy()
+        big = np.arange(2, nb, 3)                     # scale 1024, offset 2^-13: 2^-13 - 8192 is not an f32
+        sc[big] = 0x6400
+        g_of = (big % (K // 32)) * 32 // w["group"] + (big // (K // 32)) * (K // w["group"])
+        off[g_of] = 0x3900
+        w["offsets"] = off
+    xt = "bf16" if fmt == "q4a" else "f16"
+    Y, _ = _run(fmt, w, w["X"], xt, N, K, T, "fast")
+    Yr, S = _ref(orc, fmt, w, w["X"], xt, N, K, T)
+    check_tol(Y, Yr, S, TAU["fast"], f"fixup {fmt} {shape}")
+
+
 @pytest.mark.parametrize("K", [16384, 16416])
 def test_gemv_single_row_long_k(orc, K):
     """T = 1 at the longest K whose X fits the streaming kernel's LDS copy, and just past it (the
