@@ -176,7 +176,7 @@ def setup_moe(mode: str):
         "name": c.name, "cfg": c, "mode": mode, "flops": 2.0 * T * k * (2 * I * H + H * I),
         "bytes": float(used * (gu_b + dn_b) + 2 * T * H * 4), "used_experts": used, "plan_host_ms": plan_ms,
         "copies": 1, "dtype": "f32" if mode == "exact" else "f16",
-        "kernel": "gemv_kernel" if mode == "exact" else "gemm_fast_kernel", "keep": keep,
+        "kernel": "gemv_kernel" if mode == "exact" else "gemm_fast_lds_kernel", "keep": keep,
     }
     return step, info
 
