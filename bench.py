@@ -167,7 +167,14 @@ def setup_moe(mode: str):
     step = _bound("qg_moe_ffn", qg.QG_FMT_Q4, tg.data_ptr(), td.data_ptr(), 64, E, H, I, X.data_ptr(), T, k,
                   pd["seg_off"].data_ptr(), pd["row_src"].data_ptr(), pd["slot_row"].data_ptr(),
                   pd["slot_w"].data_ptr(), Y.data_ptr(), 0, qg.MODE[mode], ws.data_ptr(), ws_bytes, st)
-    keep = (G, GS, D, DS, tg, td, pd, X, Y, ws)
+    # the routing plan built on the device instead (qg_moe_plan), timed on its own: the step keeps the
+    # host plan, whose time is reported as plan_host_ms
+    lg = _dev(np.ascontiguousarray(m["logits"].reshape(T, E), dtype=np.float32))
+    dp = [torch.empty(n, dtype=dt, device="cuda") for n, dt in
+          ((E + 1, torch.int32), (T * k, torch.int32), (T * k, torch.int32), (T * k, torch.float32))]
+    plan_step = _bound("qg_moe_plan", lg.data_ptr(), T, E, k, *[t.data_ptr() for t in dp], None, None, st)
+    plan_dev_ms, _ = _timed(plan_step, 200, 20)
+    keep = (G, GS, D, DS, tg, td, pd, X, Y, ws, lg, dp)
 
     used = int(np.count_nonzero(np.diff(plan["seg_off"])))
     gu_b = m["gu_codes"][0].nbytes + m["gu_scales"][0].nbytes
@@ -175,6 +182,7 @@ def setup_moe(mode: str):
     info = {
         "name": c.name, "cfg": c, "mode": mode, "flops": 2.0 * T * k * (2 * I * H + H * I),
         "bytes": float(used * (gu_b + dn_b) + 2 * T * H * 4), "used_experts": used, "plan_host_ms": plan_ms,
+        "plan_device_us": plan_dev_ms * 1e3,
         "copies": 1, "dtype": "f32" if mode == "exact" else "f16",
         "kernel": "gemv_kernel" if mode == "exact" else "gemm_fast_lds_kernel", "keep": keep,
     }
@@ -201,6 +209,7 @@ def measure(name: str, steps: int, warmup: int) -> dict:
                     "bytes_per_step": info["bytes"]})
         if c.index == 4:
             out.update({"used_experts": info["used_experts"], "plan_host_ms": info["plan_host_ms"],
+                        "plan_device_us": info["plan_device_us"],
                         "tflops": info["flops"] / (ms * 1e-3) / 1e12})
     else:
         tf = info["flops"] / (ms * 1e-3) / 1e12

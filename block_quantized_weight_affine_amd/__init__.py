@@ -33,7 +33,7 @@ SYMBOLS = [
     "qgemm_q4", "qgemm_q4a", "qgemm_q8",
     "qgemv_q4", "qgemv_q4a", "qgemv_q8",
     "qg_dequant_dump",
-    "qg_moe_plan_host", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
+    "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn",
 ]
 
@@ -70,6 +70,7 @@ def lib() -> C.CDLL:
         L.qgemv_q4a.argtypes = [_p, _p, _p, _i, _p, _i, _p, _i, _i, _i, _p]
         L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
         L.qg_moe_plan_host.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
+        L.qg_moe_plan.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
         L.qg_x_half.argtypes = [_p, _i, _p, _i, _i, _p, _p, _p]
         L.qgemm_moe_grouped.argtypes = [_i, _p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]
         L.qg_swiglu.argtypes = [_p, _i, _i, _p, _i, _p, _p]
@@ -193,6 +194,12 @@ def qg_moe_plan_host(logits: np.ndarray, T: int, E: int, k: int) -> dict:
     _check(lib().qg_moe_plan_host(_ptr(lg), T, E, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w),
                                   _ptr(slot_e)), "qg_moe_plan_host")
     return {"seg_off": seg_off, "row_src": row_src, "slot_row": slot_row, "slot_w": slot_w, "slot_expert": slot_e}
+
+
+def qg_moe_plan(logits, T, E, k, seg_off, row_src, slot_row, slot_w, slot_expert=None, status=None, stream=None):
+    """Routing plan on the device: every argument a device tensor (int32 / float32) or None."""
+    _check(lib().qg_moe_plan(_ptr(logits), T, E, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w),
+                             _ptr(slot_expert), _ptr(status), _stream(stream)), "qg_moe_plan")
 
 
 def qg_x_half(X, x_rows, row_src, R, K, Xh, rs, stream=None):

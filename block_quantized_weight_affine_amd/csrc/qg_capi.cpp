@@ -178,6 +178,17 @@ qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* se
     return QG_OK;
 }
 
+qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
+                      int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, hipStream_t stream) {
+    if (T < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32 || (long)T * k > 65536) return QG_ESHAPE;
+    if (!logits || !seg_off || !row_src || !slot_row || !slot_w) return QG_EINVAL;
+    if (!aligned(logits, 4) || !aligned(seg_off, 4) || !aligned(row_src, 4) || !aligned(slot_row, 4) ||
+        !aligned(slot_w, 4) || (slot_expert && !aligned(slot_expert, 4)) || (status && !aligned(status, 4)))
+        return QG_EALIGN;
+    return launched(qg::launch_moe_plan(logits, T, E, k, seg_off, row_src, slot_row, slot_w, slot_expert, status,
+                                        QG_EPLAN, stream));
+}
+
 qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh, float* rs,
                     hipStream_t stream) {
     if (R < 0 || R > kMaxT || K < 8 || K > kMaxK || (K % 8) != 0 || x_rows < 0) return QG_ESHAPE;

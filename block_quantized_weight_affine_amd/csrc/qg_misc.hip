@@ -1,4 +1,5 @@
-// qg_misc.hip -- the dequant dump, the per-row f16 scaling, SwiGLU and the weighted combine.
+// qg_misc.hip -- the dequant dump, the per-row f16 scaling, SwiGLU, the weighted combine and the
+// device routing plan.
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -201,6 +202,153 @@ hipError_t launch_moe_combine(const float* O, int R, const int32_t* slot_row, co
                               int T, int k, int accumulate, hipStream_t s) {
     dim3 grid((H / 4 + 255) / 256, T);
     hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, O, R, slot_row, slot_w, Y, H, k, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace qg
+
+namespace qg {
+
+// ---- routing plan on the device ----------------------------------------------------------------
+// Pages: "cortiq-engine 0.8.44 src/gpu_metal/clover.rs", coreset_from_logits (top-k of a token's
+// router logits, ties to the lower expert index) and the renormalised weights of its route step;
+// "oxinfer 0.0.5 src/metal.rs", Backend::moe (rows grouped per expert, tokens ascending).  The
+// pages build this on the host; here one workgroup builds it on the device, so a caller can chain
+// it with the grouped matmuls without a round trip.  Same outputs as the host plan:
+//  1. one wavefront per token: k rounds of a wavefront argmax under (larger logit, then lower
+//     index) over the logits held in registers (a NaN logit ranks below every other and sets the
+//     error flag); lane j keeps the j-th pick; weight_j = exp(l_j - l_max) / sum_i exp(l_i - l_max)
+//     in f64, summed in pick order, rounded to f32; slot_row temporarily holds the pick's expert;
+//  2. per-expert counts (LDS integer atomics) and their inclusive scan -> seg_off;
+//  3. one wavefront per expert walks the slots in token order, 64 at a time: the ballot of slots
+//     that picked it and their popcount ranks give each slot its gathered row, in ascending token
+//     order; row_src[row] = token, slot_row[slot] = -1 - row (negative, so no other expert's scan
+//     can match it); 4. slot_row = -1 - slot_row.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanNpl = 16;  // logits per lane: E <= 1024
+
+__device__ __forceinline__ bool plan_better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* logits, int T, int E, int k,
+                                                                int32_t* seg_off, int32_t* row_src, int32_t* slot_row,
+                                                                float* slot_w, int32_t* slot_expert, int32_t* status,
+                                                                int32_t err_code) {
+    __shared__ int cnt[kPlanNpl * 64 + 1];
+    __shared__ int bad;
+    constexpr int W = kPlanThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tk = T * k;
+    for (int e = tid; e <= E; e += kPlanThreads) cnt[e] = 0;
+    if (tid == 0) bad = 0;
+    __syncthreads();
+
+    for (int t = wave; t < T; t += W) {
+        const float* row = logits + (size_t)t * E;
+        float v[kPlanNpl];
+        uint32_t taken = 0;  // bit i: candidate lane + 64 i is gone (picked, or past E)
+        bool nan_seen = false;
+#pragma unroll
+        for (int i = 0; i < kPlanNpl; i++) {
+            const int e = lane + 64 * i;
+            v[i] = -INFINITY;
+            if (e < E) {
+                const float x = row[e];
+                if (x != x)
+                    nan_seen = true;
+                else
+                    v[i] = x;
+            } else {
+                taken |= 1u << i;
+            }
+        }
+        if (__any(nan_seen) && lane == 0) bad = 1;
+        int my_e = 0;
+        float my_v = 0.f;
+        for (int j = 0; j < k; j++) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;  // worse than every real candidate, -inf ones included
+#pragma unroll
+            for (int i = 0; i < kPlanNpl; i++) {
+                const int e = lane + 64 * i;
+                if (!((taken >> i) & 1u) && plan_better(v[i], e, bv, bi)) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (plan_better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            // j < k <= E: an untaken real candidate remains, so bi < E
+            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+            if (lane == j) {
+                my_e = bi;
+                my_v = bv;
+            }
+        }
+        const double lmax = (double)__shfl(my_v, 0, 64);
+        const double ex = lane < k ? exp((double)my_v - lmax) : 0.0;
+        double sum = 0.0;
+        for (int j = 0; j < k; j++) sum += __shfl(ex, j, 64);
+        if (lane < k) {
+            const size_t s = (size_t)t * k + lane;
+            slot_w[s] = (float)(ex / sum);
+            slot_row[s] = my_e;
+            if (slot_expert) slot_expert[s] = my_e;
+            atomicAdd(&cnt[my_e + 1], 1);
+        }
+    }
+    __syncthreads();
+
+    if (wave == 0) {  // inclusive scan of the counts: cnt[e] = seg_off[e]
+        int carry = 0;
+        for (int c0 = 1; c0 <= E; c0 += 64) {
+            const int e = c0 + lane;
+            int x = e <= E ? cnt[e] : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            x += carry;
+            if (e <= E) cnt[e] = x;
+            carry = __shfl(x, 63, 64);
+        }
+    }
+    if (tid == 0 && status) status[0] = bad ? err_code : 0;
+    __syncthreads();
+    for (int e = tid; e <= E; e += kPlanThreads) seg_off[e] = cnt[e];
+
+    for (int e = wave; e < E; e += W) {
+        int base = cnt[e];
+        for (int c = 0; c < tk; c += 64) {
+            const int i = c + lane;
+            const bool match = i < tk && slot_row[i] == e;
+            const uint64_t mask = __ballot(match);
+            if (match) {
+                const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+                row_src[pos] = i / k;
+                slot_row[i] = -1 - pos;
+            }
+            base += __popcll(mask);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < tk; i += kPlanThreads) slot_row[i] = -1 - slot_row[i];
+}
+
+hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
+                           int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, int err_code,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, logits, T, E, k, seg_off, row_src,
+                       slot_row, slot_w, slot_expert, status, err_code);
     return hipGetLastError();
 }
 

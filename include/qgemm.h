@@ -140,6 +140,22 @@ typedef struct {
 qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* seg_off,
                            int32_t* row_src, int32_t* slot_row, float* slot_w, int32_t* slot_expert);
 
+/* Routing plan on the DEVICE (pages: "cortiq-engine 0.8.44 src/gpu_metal/clover.rs",
+ * coreset_from_logits and its route step's renormalised weights; "oxinfer 0.0.5 src/metal.rs",
+ * Backend::moe, which builds the same grouping on the host).  The outputs of qg_moe_plan_host, for
+ * logits already in device memory, computed by one workgroup on `stream` without a host round trip:
+ * logits f32 [T][E]; seg_off [E+1], row_src [T*k], slot_row [T*k], slot_w [T*k] and slot_expert
+ * [T*k] (may be NULL) as described there; all pointers device memory owned by the caller, 4-byte
+ * aligned.  The index outputs equal the host plan's; the weights are the same f64 expression
+ * rounded to f32 (the device exp may differ from the host's in the last f64 bit, so a weight may
+ * differ by one f32 unit in the last place).  status (device int32, may be NULL) receives 0, or
+ * QG_EPLAN if some logit is NaN (NaN logits rank below all others; the plan is then still well
+ * formed but meaningless).  Needs T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k <= 65536,
+ * else QG_ESHAPE.  Asynchronous; nothing is allocated. */
+qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
+                      int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status,
+                      hipStream_t stream);
+
 /* Gathered per-row power-of-two scaling of f32 rows to f16 (page section x_half / row_scale):
  * for r < R, source row s = row_src ? row_src[r] : r (rows with s outside [0, x_rows) read as
  * zeros); amax over the row; e from frexp(amax) -> scale 2^(14 - e) clamped to 2^[-100, 100]

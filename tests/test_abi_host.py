@@ -100,6 +100,26 @@ def test_dump_and_moe_validation_codes():
                         0x100010, ws, None) == qg.QG_EALIGN
 
 
+def test_device_plan_validation_codes():
+    """qg_moe_plan checks its sizes and pointers on the host, before any HIP call."""
+    L = qg.lib()
+
+    def call(T=32, E=128, k=8, logits=A16, seg=A16b, rsrc=A16c, srow=A16d, sw=0x50000, se=None, st=None):
+        return L.qg_moe_plan(logits, T, E, k, seg, rsrc, srow, sw, se, st, None)
+
+    assert call(T=0) == qg.QG_ESHAPE
+    assert call(E=0) == qg.QG_ESHAPE
+    assert call(E=1025, k=8) == qg.QG_ESHAPE          # at most 1024 experts
+    assert call(k=0) == qg.QG_ESHAPE
+    assert call(E=8, k=9) == qg.QG_ESHAPE             # k <= E
+    assert call(E=128, k=33) == qg.QG_ESHAPE          # k <= 32
+    assert call(T=8193, k=8) == qg.QG_ESHAPE          # T * k <= 65536
+    assert call(logits=None) == qg.QG_EINVAL
+    assert call(sw=None) == qg.QG_EINVAL
+    assert call(srow=A16d + 2) == qg.QG_EALIGN
+    assert call(st=0x60001) == qg.QG_EALIGN
+
+
 def test_plan_host_matches_oracle(orc):
     import synth
     for (T, E, k, seed) in [(32, 128, 8, 1004), (75, 8, 2, 7), (5, 16, 16, 3)]:

@@ -1,6 +1,7 @@
-"""MoE pieces on the GPU against the oracle: row scaling to f16, the ragged grouped matmul (exact and
-fast), SwiGLU, the weighted combine, and the whole expert block end to end (small design with an
-unused expert and uneven loads, and the 128-expert top-8 workload)."""
+"""MoE pieces on the GPU against the oracle: the device routing plan, row scaling to f16, the ragged
+grouped matmul (exact and fast), SwiGLU, the weighted combine, and the whole expert block end to end
+(small design with an unused expert and uneven loads, and the 128-expert top-8 workload, also with the
+plan built on the device)."""
 import numpy as np
 import pytest
 import torch
@@ -176,3 +177,108 @@ def test_ffn_full_workload(orc, mode):
     print(f"moe workload {c.name} {mode}", flush=True)
     y, ref = _ffn(orc, c.extra["experts"], c.N, c.extra["inter"], c.T, c.extra["top_k"], c.seed, mode)
     check_tol(y, ref["y"], ref["bound"], 2 * TAU[mode], f"ffn full {mode}")
+
+
+# ---- routing plan on the device ------------------------------------------------------------------
+PLAN_CASES = [
+    (32, 128, 8, 1004, None),       # the MoE workload's routing shape
+    (75, 8, 2, 7, "unused"),        # an expert nobody picks
+    (5, 16, 16, 3, "ties"),         # k = E; an all-tied row; a tie at the top
+    (1, 1, 1, 11, None),            # one token, one expert
+    (300, 100, 6, 12, None),        # E not a multiple of 64; several tokens per wavefront
+    (2048, 64, 4, 13, "neg_inf"),   # T*k = 8192: many 64-slot scan chunks; -inf logits tie by index
+    (64, 1024, 32, 14, None),       # E and k at their maxima
+]
+
+
+def _device_plan(lg, T, E, k, status_init=-7):
+    out = {
+        "seg_off": torch.full((E + 1,), -5, dtype=torch.int32, device="cuda"),
+        "row_src": torch.full((T * k,), -5, dtype=torch.int32, device="cuda"),
+        "slot_row": torch.full((T * k,), -5, dtype=torch.int32, device="cuda"),
+        "slot_w": torch.full((T * k,), -5.0, dtype=torch.float32, device="cuda"),
+        "slot_expert": torch.full((T * k,), -5, dtype=torch.int32, device="cuda"),
+        "status": torch.full((1,), status_init, dtype=torch.int32, device="cuda"),
+    }
+    print(f"device plan T={T} E={E} k={k}", flush=True)
+    qg.qg_moe_plan(dev(np.ascontiguousarray(lg, np.float32)), T, E, k, out["seg_off"], out["row_src"],
+                   out["slot_row"], out["slot_w"], out["slot_expert"], out["status"])
+    torch.cuda.synchronize()
+    return {key: v.cpu().numpy() for key, v in out.items()}
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=lambda c: f"T{c[0]}-E{c[1]}-k{c[2]}-{c[4]}")
+def test_device_plan_matches_oracle(orc, case):
+    """Every index output equal to the oracle's plan (full sort per token, ties to the lower index);
+    weights within one f32 unit in the last place of the oracle's f64 weights."""
+    T, E, k, seed, kind = case
+    lg = synth.normal_as(seed, synth.STREAM_LOGITS, T * E, 0.0, 1.0, "f32").reshape(T, E).copy()
+    if kind == "unused":
+        lg[:, 5] = -1e9
+    elif kind == "ties":
+        lg[1, :] = 0.25
+        lg[2, 3] = lg[2, 9] = 5.0
+    elif kind == "neg_inf":
+        lg[:, ::3] = -np.inf
+        lg[7, :] = -np.inf
+        lg[7, 10] = lg[7, 20] = lg[7, 30] = lg[7, 40] = 0.0    # exactly k finite logits, rest tied at -inf
+    ref = orc.moe_plan(lg, T, E, k)
+    got = _device_plan(lg, T, E, k)
+    assert got["status"][0] == 0
+    for key in ("seg_off", "row_src", "slot_row", "slot_expert"):
+        assert np.array_equal(got[key], ref[key]), key
+    w = got["slot_w"].astype(np.float64)
+    assert np.all(np.abs(w - ref["slot_w"]) <= 2.0 ** -23 * np.abs(ref["slot_w"])), "weights"
+    host = qg.qg_moe_plan_host(lg, T, E, k)
+    for key in ("seg_off", "row_src", "slot_row", "slot_expert"):
+        assert np.array_equal(got[key], host[key]), key
+
+
+def test_device_plan_nan_logit_sets_status(orc):
+    """A NaN logit: status QG_EPLAN, and the plan is still well formed (every index in range, each
+    gathered row used once)."""
+    T, E, k = 6, 40, 3
+    lg = synth.normal_as(15, synth.STREAM_LOGITS, T * E, 0.0, 1.0, "f32").reshape(T, E).copy()
+    lg[2, 7] = np.nan
+    got = _device_plan(lg, T, E, k, status_init=0)
+    assert got["status"][0] == qg.QG_EPLAN
+    seg = got["seg_off"]
+    assert seg[0] == 0 and seg[-1] == T * k and np.all(np.diff(seg) >= 0)
+    assert np.array_equal(np.sort(got["slot_row"]), np.arange(T * k))
+    assert np.all((got["row_src"] >= 0) & (got["row_src"] < T))
+    assert np.all((got["slot_expert"] >= 0) & (got["slot_expert"] < E))
+    # rows outside the NaN token are the oracle's
+    ok = np.ones(T, bool)
+    ok[2] = False
+    ref = orc.moe_plan(np.where(np.isnan(lg), -np.inf, lg), T, E, k)
+    se = got["slot_expert"].reshape(T, k)
+    assert np.array_equal(se[ok], ref["slot_expert"].reshape(T, k)[ok])
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_ffn_full_workload_device_plan(orc, mode):
+    """The 128-expert top-8 block with its plan built on the device: the same plan as the host's, and
+    the chain's output within the oracle's bound."""
+    c = synth.CONFIGS[4]
+    E, H, I, T, k = c.extra["experts"], c.N, c.extra["inter"], c.T, c.extra["top_k"]
+    m = synth.make_moe(E, H, I, T, c.seed)
+    lg = m["logits"].reshape(T, E)
+    plan = orc.moe_plan(lg, T, E, k)
+    seg_off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    row_src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    slot_row = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    slot_w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    Cg, Sg, tg = _experts(m, "gu")
+    Cd, Sd, td = _experts(m, "dn")
+    ws_bytes = qg.qg_moe_ffn_workspace(H, I, T, k, mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    Y = torch.zeros((T, H), device="cuda")
+    print(f"moe workload {c.name} {mode} with the device plan", flush=True)
+    qg.qg_moe_plan(dev(np.ascontiguousarray(lg)), T, E, k, seg_off, row_src, slot_row, slot_w)
+    qg.qg_moe_ffn("q4", tg, td, 64, E, H, I, dev(m["X"].reshape(T, H)), T, k, seg_off, row_src, slot_row, slot_w,
+                  Y, 0, mode, ws, ws_bytes)
+    torch.cuda.synchronize()
+    for key, t in (("seg_off", seg_off), ("row_src", row_src), ("slot_row", slot_row)):
+        assert np.array_equal(t.cpu().numpy(), plan[key]), key
+    ref = orc.moe_ffn(m, plan)
+    check_tol(Y.cpu().numpy(), ref["y"], ref["bound"], 2 * TAU[mode], f"ffn full {mode}, device plan")
