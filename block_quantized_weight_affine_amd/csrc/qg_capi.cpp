@@ -180,7 +180,7 @@ qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* se
 
 qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                       int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, hipStream_t stream) {
-    if (T < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32 || (long)T * k > 65536) return QG_ESHAPE;
+    if (T < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32 || (long)T * k > 16384) return QG_ESHAPE;
     if (!logits || !seg_off || !row_src || !slot_row || !slot_w) return QG_EINVAL;
     if (!aligned(logits, 4) || !aligned(seg_off, 4) || !aligned(row_src, 4) || !aligned(slot_row, 4) ||
         !aligned(slot_w, 4) || (slot_expert && !aligned(slot_expert, 4)) || (status && !aligned(status, 4)))

@@ -186,19 +186,42 @@ __device__ __forceinline__ float slow_value(const RawBlock<FMT>& r, float cf) {
 
 __device__ __forceinline__ float byte_f32(uint32_t word, int i) { return (float)((word >> (8 * i)) & 0xFFu); }
 
+// Elements 4q .. 4q+3 of a block as f32 (exact-mode staging), in the pages' order of operations for
+// every scale: Q8 float(q) * d (their one rounding); Q4 (nibble - 8) d and Q4A (nibble - 8) d + m,
+// computed from the signed byte 16 (nibble - 8) (the nibble moved to the byte's high half with its
+// top bit flipped, converted by one instruction) times d / 16 -- exact, since d / 16 is a power-of-two
+// rescaling of an f16 value (normal in f32) and the product has at most 15 significant bits -- and,
+// for Q4A, one FMA with m (the product is exact, so the fused add rounds as the separate add does).
+// The sign of a zero product is sign(d), as in (nibble - 8) * d.
+template <int FMT>
+__device__ __forceinline__ void block_quad_f32(const RawBlock<FMT>& r, int q, float (&v)[4]) {
+    if constexpr (FMT == FMT_Q8) {
+        const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        const uint32_t x = w[q];
+#pragma unroll
+        for (int b = 0; b < 4; b++) v[b] = (float)(int8_t)(x >> (8 * b)) * r.d;
+    } else {
+        const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        const uint32_t x = keep_u32(q < 4 ? ((w[q & 3] << 4) & 0xF0F0F0F0u) ^ 0x80808080u
+                                          : (w[q & 3] & 0xF0F0F0F0u) ^ 0x80808080u);
+        const float d16 = 0.0625f * r.d;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float sv = (float)(int8_t)(x >> (8 * b));
+            v[b] = FMT == FMT_Q4A ? fmaf(sv, d16, r.m) : sv * d16;
+        }
+    }
+}
+
 // Whole block to f32 (element order): exact-mode staging.
 template <int FMT>
 __device__ __forceinline__ void block_to_f32(const RawBlock<FMT>& r, float (&v)[32]) {
-    uint32_t c[8];
-    value_bytes<FMT>(r, c);
-    bool fast;
-    const float c0 = block_c0<FMT>(r, fast);
-    if (__all(fast)) {
 #pragma unroll
-        for (int e = 0; e < 32; e++) v[e] = fmaf(byte_f32(c[e >> 2], e & 3), r.d, c0);
-    } else {
+    for (int q = 0; q < 8; q++) {
+        float t[4];
+        block_quad_f32<FMT>(r, q, t);
 #pragma unroll
-        for (int e = 0; e < 32; e++) v[e] = keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3)));
+        for (int b = 0; b < 4; b++) v[4 * q + b] = t[b];
     }
 }
 

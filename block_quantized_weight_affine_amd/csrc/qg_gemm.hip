@@ -321,6 +321,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(GemmParams p, bo
 // Decode ownership: a stage holds 2 BN blocks = 8 BN fragments of 8 values, FPT = BN / 32 per
 // thread; a thread owns FPB = min(FPT, 4) fragments of each of its blocks, so narrow tiles still
 // spread the decode over all 256 threads.
+// Stages s .. s+U-1 of an unrolled stage loop (stage u of the group gets u as a compile-time index),
+// and the at most U-1 stages left after the last whole group.
+template <int I, int U, class F>
+__device__ __forceinline__ void run_stages(F& f, int s) {
+    f(std::integral_constant<int, I>{}, s + I);
+    if constexpr (I + 1 < U) run_stages<I + 1, U>(f, s);
+}
+template <int I, int U, class F>
+__device__ __forceinline__ void run_tail_stages(F& f, int s, int nstage) {
+    if constexpr (I < U - 1) {
+        if (s + I < nstage) {
+            f(std::integral_constant<int, I>{}, s + I);
+            run_tail_stages<I + 1, U>(f, s, nstage);
+        }
+    }
+}
+
 template <int FMT, int ST, int WM, int MT, int MN, int DP, bool GR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p) {
     constexpr int WN = 4 / WM;
@@ -586,19 +603,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     }
     __syncthreads();
     int s = 0;
-    for (; s + U - 1 < nstage; s += U) {
-        stage(std::integral_constant<int, 0>{}, s);
-        stage(std::integral_constant<int, 1>{}, s + 1);
-        if constexpr (U > 2) {
-            stage(std::integral_constant<int, 2 % U>{}, s + 2);
-            stage(std::integral_constant<int, 3 % U>{}, s + 3);
-        }
-    }
-    if (s < nstage) stage(std::integral_constant<int, 0>{}, s);
-    if constexpr (U > 2) {
-        if (s + 1 < nstage) stage(std::integral_constant<int, 1>{}, s + 1);
-        if (s + 2 < nstage) stage(std::integral_constant<int, 2 % U>{}, s + 2);
-    }
+    for (; s + U - 1 < nstage; s += U) run_stages<0, U>(stage, s);
+    run_tail_stages<0, U>(stage, s, nstage);
 
     QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
 #pragma unroll
@@ -690,10 +696,25 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
 #pragma unroll
             for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
+    // Software pipeline: stage s runs its MFMAs on the decoded block wv while the raw block of stage
+    // s + 1 (wr) is decoded four values at a time between them and the raw block of stage s + 2
+    // loads; blocks past K decode with zero scale and offset (zeros).
     float xv[XCH][8];
     RawBlock<FMT> wr[MN];
+    float wv[MN][32];
     load_x(0, xv);
-    load_w(0, wr);
+    {
+        RawBlock<FMT> w0[MN];
+        load_w(0, w0);
+        load_w(1, wr);
+        const bool valid0 = g < nblk;
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+            w0[mn].d = valid0 ? w0[mn].d : 0.f;
+            w0[mn].m = valid0 ? w0[mn].m : 0.f;
+            block_to_f32<FMT>(w0[mn], wv[mn]);
+        }
+    }
     store_x(0, xv);
     __syncthreads();
 
@@ -701,19 +722,17 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
         const int buf = s & 1;
         const bool more = s + 1 < nstage;
         RawBlock<FMT> wn[MN];
-        if (more) {
-            load_x(s + 1, xv);
-            load_w(s + 1, wn);
-        }
-        const bool valid = 2 * s + g < nblk;
-        float wv[MN][32];
+        if (more) load_x(s + 1, xv);
+        load_w(s + 2, wn);
+        const bool valid = 2 * (s + 1) + g < nblk;
+        RawBlock<FMT> rn[MN];
 #pragma unroll
         for (int mn = 0; mn < MN; mn++) {
-            block_to_f32<FMT>(wr[mn], wv[mn]);
-            if (!valid)
-#pragma unroll
-                for (int j = 0; j < 32; j++) wv[mn][j] = 0.f;
+            rn[mn] = wr[mn];
+            rn[mn].d = valid ? rn[mn].d : 0.f;
+            rn[mn].m = valid ? rn[mn].m : 0.f;
         }
+        float wnv[MN][32];
 #pragma unroll
         for (int q = 0; q < 8; q++) {
 #pragma unroll
@@ -727,11 +746,20 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
                         acc[mt][mn] =
                             __builtin_amdgcn_mfma_f32_32x32x2f32(av[jj], wv[mn][4 * q + jj], acc[mt][mn], 0, 0, 0);
             }
-        }
-        if (more) {
-            store_x(buf ^ 1, xv);
 #pragma unroll
-            for (int mn = 0; mn < MN; mn++) wr[mn] = wn[mn];
+            for (int mn = 0; mn < MN; mn++) {
+                float t[4];
+                block_quad_f32<FMT>(rn[mn], q, t);
+#pragma unroll
+                for (int b = 0; b < 4; b++) wnv[mn][4 * q + b] = t[b];
+            }
+        }
+        if (more) store_x(buf ^ 1, xv);
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++) {
+            wr[mn] = wn[mn];
+#pragma unroll
+            for (int j = 0; j < 32; j++) wv[mn][j] = wnv[mn][j];
         }
         __syncthreads();
     }
@@ -814,8 +842,12 @@ static void exact_launch(const GemmParams& p, bool grouped, hipStream_t s) {
 template <int FMT, int XT>
 static void exact_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) return exact_launch<FMT, XT, 1, 1>(p, grouped, s);
+    // 32-row tiles unless 64-row tiles still give four workgroups per CU: with one workgroup per
+    // CU each SIMD holds a single wavefront and every barrier and LDS wait idles its matrix core.
+    // Measured on the Q4 prefill (N = K = 4096, T 512): 176 us with 32-row tiles (512 workgroups)
+    // against 198 us with 64-row tiles (256).
     const long mid = (long)((p.N + 127) / 128) * ((p.R + 63) / 64);
-    if (mid >= 200) return exact_launch<FMT, XT, 2, 1>(p, grouped, s);
+    if (mid >= 1024) return exact_launch<FMT, XT, 2, 1>(p, grouped, s);
     return exact_launch<FMT, XT, 1, 1>(p, grouped, s);
 }
 

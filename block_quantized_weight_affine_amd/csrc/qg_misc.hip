@@ -218,14 +218,14 @@ namespace qg {
 //  1. one wavefront per token: k rounds of a wavefront argmax under (larger logit, then lower
 //     index) over the logits held in registers (a NaN logit ranks below every other and sets the
 //     error flag); lane j keeps the j-th pick; weight_j = exp(l_j - l_max) / sum_i exp(l_i - l_max)
-//     in f64, summed in pick order, rounded to f32; slot_row temporarily holds the pick's expert;
+//     in f64, summed in pick order, rounded to f32; the pick's expert is kept in LDS;
 //  2. per-expert counts (LDS integer atomics) and their inclusive scan -> seg_off;
 //  3. one wavefront per expert walks the slots in token order, 64 at a time: the ballot of slots
 //     that picked it and their popcount ranks give each slot its gathered row, in ascending token
-//     order; row_src[row] = token, slot_row[slot] = -1 - row (negative, so no other expert's scan
-//     can match it); 4. slot_row = -1 - slot_row.
+//     order; row_src[row] = token, slot_row[slot] = row.
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanNpl = 16;  // logits per lane: E <= 1024
+constexpr int kPlanNpl = 16;         // logits per lane: E <= 1024
+constexpr int kPlanSlots = 16384;    // T * k: the picks live in LDS (32 KiB)
 
 __device__ __forceinline__ bool plan_better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
@@ -236,6 +236,7 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
                                                                 float* slot_w, int32_t* slot_expert, int32_t* status,
                                                                 int32_t err_code) {
     __shared__ int cnt[kPlanNpl * 64 + 1];
+    __shared__ uint16_t pick[kPlanSlots];
     __shared__ int bad;
     constexpr int W = kPlanThreads / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
         if (lane < k) {
             const size_t s = (size_t)t * k + lane;
             slot_w[s] = (float)(ex / sum);
-            slot_row[s] = my_e;
+            pick[s] = (uint16_t)my_e;
             if (slot_expert) slot_expert[s] = my_e;
             atomicAdd(&cnt[my_e + 1], 1);
         }
@@ -330,18 +331,16 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
         int base = cnt[e];
         for (int c = 0; c < tk; c += 64) {
             const int i = c + lane;
-            const bool match = i < tk && slot_row[i] == e;
+            const bool match = i < tk && pick[i] == e;
             const uint64_t mask = __ballot(match);
             if (match) {
                 const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
                 row_src[pos] = i / k;
-                slot_row[i] = -1 - pos;
+                slot_row[i] = pos;
             }
             base += __popcll(mask);
         }
     }
-    __syncthreads();
-    for (int i = tid; i < tk; i += kPlanThreads) slot_row[i] = -1 - slot_row[i];
 }
 
 hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,

@@ -150,7 +150,7 @@ qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* se
  * rounded to f32 (the device exp may differ from the host's in the last f64 bit, so a weight may
  * differ by one f32 unit in the last place).  status (device int32, may be NULL) receives 0, or
  * QG_EPLAN if some logit is NaN (NaN logits rank below all others; the plan is then still well
- * formed but meaningless).  Needs T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k <= 65536,
+ * formed but meaningless).  Needs T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k <= 16384,
  * else QG_ESHAPE.  Asynchronous; nothing is allocated. */
 qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                       int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status,

@@ -113,7 +113,8 @@ def test_device_plan_validation_codes():
     assert call(k=0) == qg.QG_ESHAPE
     assert call(E=8, k=9) == qg.QG_ESHAPE             # k <= E
     assert call(E=128, k=33) == qg.QG_ESHAPE          # k <= 32
-    assert call(T=8193, k=8) == qg.QG_ESHAPE          # T * k <= 65536
+    assert call(T=2049, k=8) == qg.QG_ESHAPE          # T * k <= 16384
+    assert call(T=8192, k=2, E=8, logits=None) == qg.QG_EINVAL   # 16384 slots pass the size check
     assert call(logits=None) == qg.QG_EINVAL
     assert call(sw=None) == qg.QG_EINVAL
     assert call(srow=A16d + 2) == qg.QG_EALIGN
