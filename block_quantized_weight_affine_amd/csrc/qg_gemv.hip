@@ -143,12 +143,15 @@ __device__ __forceinline__ float unit_value(const Unit<FMT>& w, float p, float s
 }
 
 // RW weight rows starting at nrow0; NT X rows (xrow[t], -1 = zero row) -> Y rows yrow0 + t.
-// TH threads per workgroup stage each X chunk together.
-template <int FMT, int XT, int RW, int NT, int TH>
+// TH threads per workgroup stage each X chunk together.  SOV > 0 sets the chunk to SOV 1024-value
+// steps.  DMA (f32 X only): X goes from memory straight into LDS (buffer_load ... lds, 16 bytes per
+// lane, lanes past the chunk masked off, rows outside X read as zero), which holds no registers.
+template <int FMT, int XT, int RW, int NT, int TH, int SOV = 0, bool DMA = false>
 __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes, const void* scales,
                                           const uint16_t* offs, int nrow0, int yrow0, const int* xrow, float* xs) {
-    constexpr int S = GemvChunk<NT>::steps;
-    constexpr int KC = GemvChunk<NT>::kc;
+    static_assert(!DMA || XT == XT_F32, "direct staging copies f32 rows");
+    constexpr int S = SOV > 0 ? SOV : GemvChunk<NT>::steps;
+    constexpr int KC = 1024 * S;
     constexpr int G = (16 / RW) < S ? (16 / RW) : S;                     // steps whose loads are in flight together
     constexpr int XV = (XT == XT_F32) ? 4 : 8;                          // X values per 16-byte load
     constexpr int XL = (KC / XV + TH - 1) / TH;  // X loads per thread per X row and chunk
@@ -170,9 +173,23 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
         const int nsteps = (kn + 1023) >> 10;
         // 1. X loads of the chunk, 16 bytes each: load (t, i) covers values [e, e + XV) of X row t of
         //    the chunk with e = XV * (tid + i * threads).
-        uint4 xl[NT][XL];
+        if constexpr (DMA) {
+            // the whole X matrix as one buffer (its size fits 31 bits: checked by the launcher)
+            const __amdgpu_buffer_rsrc_t xr =
+                __builtin_amdgcn_make_buffer_rsrc((void*)p.X, 0, p.x_rows * K * 4, 0x00020000);
+            const int wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int t = 0; t < NT; t++)
+            for (int t = 0; t < NT; t++)
+#pragma unroll
+                for (int i = 0; i < XL; i++) {
+                    const int e = XV * (int)(threadIdx.x + i * TH);
+                    const int off = xrow[t] >= 0 ? (xrow[t] * K + k0 + e) * 4 : 0x7FFFFFF0;
+                    if (e < kn) buffer_copy16_lds(xr, xs + t * KS + XV * (64 * wave + i * TH), off);
+                }
+        }
+        uint4 xl[DMA ? 1 : NT][DMA ? 1 : XL];
+#pragma unroll
+        for (int t = 0; t < (DMA ? 0 : NT); t++)
 #pragma unroll
             for (int i = 0; i < XL; i++) {
                 const int e = XV * (int)(threadIdx.x + i * TH);
@@ -196,7 +213,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
             if (g0 == 0) {
                 // 3. X to LDS as f32: X row t of the chunk at xs[t * KS + e]
 #pragma unroll
-                for (int t = 0; t < NT; t++)
+                for (int t = 0; t < (DMA ? 0 : NT); t++)
 #pragma unroll
                     for (int i = 0; i < XL; i++) {
                         const int e = XV * (int)(threadIdx.x + i * TH);
@@ -281,7 +298,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
         }
 }
 
-template <int FMT, int XT, int RW, int NT, int TH>
+template <int FMT, int XT, int RW, int NT, int TH, int SOV = 0, bool DMA = false>
 __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* codes, const void* scales,
                                            const uint16_t* offs, int nrow0, int c, float* xs) {
     int xrow[NT];
@@ -295,24 +312,27 @@ __device__ __forceinline__ void gemv_chunk(const GemmParams& p, const void* code
         }
         xrow[t] = s;
     }
-    gemv_rows<FMT, XT, RW, NT, TH>(p, codes, scales, offs, nrow0, c, xrow, xs);
+    gemv_rows<FMT, XT, RW, NT, TH, SOV, DMA>(p, codes, scales, offs, nrow0, c, xrow, xs);
 }
 
-// Grouped launches: the NT (1..NTG) X rows of one chunk of an expert's segment.
-template <int FMT, int XT, int RW, int TH, int NTG>
+// Grouped launches: the NT (1..NTG) X rows of one chunk of an expert's segment, in K chunks of
+// 2048 values; with DMA, f32 X is staged straight into LDS.
+constexpr int kGroupedSteps = 2;
+template <int FMT, int XT, int RW, int TH, int NTG, bool DMA>
 __device__ __forceinline__ void gemv_grouped_chunk(const GemmParams& p, const void* codes, const void* scales,
                                                    const uint16_t* offs, int nrow0, int c, int nt, float* xs) {
     if constexpr (NTG > 1) {
-        if (nt < NTG) return gemv_grouped_chunk<FMT, XT, RW, TH, NTG - 1>(p, codes, scales, offs, nrow0, c, nt, xs);
+        if (nt < NTG)
+            return gemv_grouped_chunk<FMT, XT, RW, TH, NTG - 1, DMA>(p, codes, scales, offs, nrow0, c, nt, xs);
     }
-    gemv_chunk<FMT, XT, RW, NTG, TH>(p, codes, scales, offs, nrow0, c, xs);
+    gemv_chunk<FMT, XT, RW, NTG, TH, kGroupedSteps, DMA>(p, codes, scales, offs, nrow0, c, xs);
 }
 
 // NTD > 0: dense call with NTD = T rows of X (T <= 8).  NTD == 0: grouped call; blockIdx.y is the
 // expert and the workgroup walks the expert's rows in chunks of at most NTG.  TH threads per
 // workgroup, each wavefront owning RW weight rows.
-template <int FMT, int XT, int RW, int NTD, int TH, int NTG = 8>
-__global__ __launch_bounds__(TH) void gemv_kernel(GemmParams p) {
+template <int FMT, int XT, int RW, int NTD, int TH, int NTG = 8, bool DMA = false>
+__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(DMA ? 3 : 1))) void gemv_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) float xs[];  // gemv_lds_bytes()
     const int wave = threadIdx.x >> 6;
     const int nrow0 = (blockIdx.x * (TH / 64) + wave) * RW;
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(TH) void gemv_kernel(GemmParams p) {
         const void* scales = p.experts[e].scales;
         const uint16_t* offs = p.experts[e].offsets;
         for (int c = r0; c < r1; c += NTG)
-            gemv_grouped_chunk<FMT, XT, RW, TH, NTG>(p, codes, scales, offs, nrow0, c, min(NTG, r1 - c), xs);
+            gemv_grouped_chunk<FMT, XT, RW, TH, NTG, DMA>(p, codes, scales, offs, nrow0, c, min(NTG, r1 - c), xs);
     }
 }
 
@@ -509,13 +529,24 @@ static void gemv_dense(const GemmParams& p, hipStream_t s) {
 template <int FMT, int XT>
 static void gemv_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) {
-        // Chunks of at most 4 segment rows: the LDS sized for them (32 KiB at K = 2048, instead of
-        // 64 KiB for 8 rows) lets five workgroups share a CU instead of two; segments longer than 4
-        // rows (a few percent of the routed experts) read their weights once per chunk.  Measured
-        // on the exact MoE block (128 experts, top 8, 32 tokens): 487 us against 517 us with
-        // 8-row chunks; 2-row chunks, or 8-row workgroups, are slower (545 us, 641 us).
+        // Chunks of at most 4 segment rows and 2048 values of K, LDS sized for them; segments longer
+        // than 4 rows (a few percent of the routed experts) read their weights once per chunk.  f32
+        // X is staged straight into LDS (no staging registers), which brings the kernel to 168
+        // VGPRs and three wavefronts per SIMD (a 36-byte spill).  Measured on the exact MoE block
+        // (128 experts, top 8, 32 tokens): 517 us with 8-row chunks through registers (two
+        // wavefronts per SIMD); 487 us with 4-row chunks; 439 us adding the direct staging and
+        // 2048-value chunks; 354 us at three wavefronts per SIMD; 760 us forced to four (spills).
         dim3 grid((p.N + 15) / 16, p.E);
-        hipLaunchKernelGGL((gemv_kernel<FMT, XT, 4, 0, kGemvThreads, 4>), grid, dim3(kGemvThreads), gemv_lds_bytes(p.K, 1, 4), s, p);
+        const size_t lds = 4 * 4 * (size_t)std::min(p.K, 1024 * kGroupedSteps);  // 4 rows of one K chunk
+        if constexpr (XT == XT_F32) {
+            // direct staging addresses X through one buffer range of 31 bits
+            if ((size_t)p.x_rows * (size_t)p.K * 4 <= 0x7FFFFFF0u) {
+                hipLaunchKernelGGL((gemv_kernel<FMT, XT, 4, 0, kGemvThreads, 4, true>), grid, dim3(kGemvThreads), lds,
+                                   s, p);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((gemv_kernel<FMT, XT, 4, 0, kGemvThreads, 4>), grid, dim3(kGemvThreads), lds, s, p);
         return;
     }
     switch (p.R) {
