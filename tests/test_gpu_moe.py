@@ -282,3 +282,43 @@ def test_ffn_full_workload_device_plan(orc, mode):
         assert np.array_equal(t.cpu().numpy(), plan[key]), key
     ref = orc.moe_ffn(m, plan)
     check_tol(Y.cpu().numpy(), ref["y"], ref["bound"], 2 * TAU[mode], f"ffn full {mode}, device plan")
+
+
+# ---- grouped exact GEMV: chunk walking, K chunks, gathered and zero rows --------------------------
+@pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
+@pytest.mark.parametrize("xt", ["f32", "f16"])
+def test_grouped_gemv_exact_chunks(orc, fmt, xt):
+    """Short segments (R <= 8 E, so the grouped GEMV runs): 12 experts with 0..9 rows each (segments
+    longer than 4 rows take several row chunks), N = 96 (a partial last workgroup of weight rows),
+    K = 3104 (a 2048-value K chunk, then a ragged one), X rows gathered through row_src with some ids
+    outside X (zero rows); f32 X is staged straight into LDS, f16 X through registers."""
+    E, N, K, x_rows, group = 12, 96, 3104, 20, 32
+    sizes = [0, 1, 2, 3, 4, 5, 9, 0, 1, 6, 2, 3]
+    seg = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(seg[-1])
+    assert R <= 8 * E
+    rng = np.random.default_rng(31)
+    row_src = rng.integers(0, x_rows, R).astype(np.int32)
+    row_src[[3, 11, 17]] = [-1, x_rows, x_rows + 5]       # outside X: zero rows
+    ws = [synth.make_dense(fmt, N, K, 1, "f32", 1.0, 4000 + e, group=group) for e in range(E)]
+    X = synth.normal_as(77, synth.STREAM_X, x_rows * K, 0.0, 1.0, xt).reshape(x_rows, K)
+    dw = [(dev(w["codes"]), dev(w["scales"]), dev(w["offsets"]) if "offsets" in w else None) for w in ws]
+    table = qg.expert_table(dw)
+    Y = torch.full((R, N), float("nan"), device="cuda")
+    Xd = dev(X).view(torch.float16) if xt == "f16" else dev(X)
+    print(f"grouped exact GEMV {fmt} {xt} R={R} K={K}", flush=True)
+    qg.qgemm_moe_grouped(fmt, table, group, dev(seg), dev(row_src), x_rows, Xd, None, Y, N, K, R, E, "exact")
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    Xz = np.concatenate([X, np.zeros((1, K), X.dtype)])
+    src = np.where((row_src >= 0) & (row_src < x_rows), row_src, x_rows)
+    Xg = np.ascontiguousarray(Xz[src])
+    for e in range(E):
+        r0, r1 = seg[e], seg[e + 1]
+        if r0 == r1:
+            continue
+        w = ws[e]
+        Yr, Sr, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), group, N, K, Xg[r0:r1], xt, r1 - r0)
+        check_tol(y[r0:r1], Yr, Sr, TAU["exact"], f"expert {e} ({r1 - r0} rows)")
+    for r in (3, 11, 17):
+        assert np.all(y[r] == 0.0), f"zero row {r}"
