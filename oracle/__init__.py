@@ -56,6 +56,12 @@ def lib():
         L.orc_weight_f32.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i]
         L.orc_dequant_tile.restype = None
         L.orc_dequant_tile.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
+        L.orc_gguf_weight_f32.restype = C.c_float
+        L.orc_gguf_weight_f32.argtypes = [_i, _p, _i, _i, _i]
+        L.orc_gguf_dequant.restype = None
+        L.orc_gguf_dequant.argtypes = [_i, _p, _i, _i, _p]
+        L.orc_gguf_repack.restype = None
+        L.orc_gguf_repack.argtypes = [_i, _p, _i, _i, _p, _p]
         L.orc_gemm.restype = _i
         L.orc_gemm.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _i, _p, _p, _i]
         L.orc_x_half.restype = None
@@ -247,3 +253,30 @@ def moe_ffn(m: dict, plan: dict, experts=None, threads=None) -> dict:
     y, _ = moe_combine(O, H, plan["slot_row"], plan["slot_w"], T, len(plan["slot_w"]) // T)
     B, _ = moe_combine(Bo, H, plan["slot_row"], np.abs(plan["slot_w"]), T, len(plan["slot_w"]) // T)
     return {"y": y, "bound": B, "O": O, "GU": Gs}
+
+
+# ---- GGUF blocks with in-block scales (Q4_0 = 2, Q8_0 = 8) ----------------------------------------
+GGUF = {"q4_0": 2, "q8_0": 8}
+GGUF_BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+
+
+def gguf_dequant(gtype, src, N, K) -> np.ndarray:
+    """f32 [N, K]: every element decoded from the GGUF bytes, as the pages' loaders evaluate it."""
+    b = _c(src, np.uint8)
+    out = np.empty((N, K), np.float32)
+    lib().orc_gguf_dequant(GGUF[gtype], _ptr(b), N, K, _ptr(out))
+    return out
+
+
+def gguf_repack(gtype, src, N, K) -> tuple:
+    """(codes, scales) of the split layout: Q4_0 -> uint8 [N*K/2], f16 bits uint16 [N*K/32];
+    Q8_0 -> int8 [N*K], f32 [N*K/32]."""
+    b = _c(src, np.uint8)
+    if gtype == "q4_0":
+        codes = np.empty(N * K // 2, np.uint8)
+        scales = np.empty(N * K // 32, np.uint16)
+    else:
+        codes = np.empty(N * K, np.uint8)
+        scales = np.empty(N * K // 32, np.float32)
+    lib().orc_gguf_repack(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales))
+    return (codes if gtype == "q4_0" else codes.view(np.int8)), scales

@@ -373,3 +373,57 @@ void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uin
         for (int k = 0; k < K; k++)
             out[(size_t)n * K + k] = orc_weight_exact(fmt, codes, scales, offs, group, N, K, n, k);
 }
+
+/* ---------------------------------------------------------------------------------------
+ * GGUF blocks with the scale inside the block (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC,
+ * the GGUF dequantizers Q4_0W and Q8_0W): a row is K/32 consecutive blocks.
+ *   Q4_0: 18 bytes = f16 scale d (little-endian), then 16 bytes; byte j holds element j in its
+ *         low nibble and element j + 16 in its high nibble; value = (nibble - 8) * d in f32.
+ *   Q8_0: 34 bytes = f16 scale d, then 32 signed bytes q; value = float(q) * d in f32.
+ * Type ids: 2 = Q4_0, 8 = Q8_0.
+ */
+#define ORC_GGUF_Q4_0 2
+#define ORC_GGUF_Q8_0 8
+
+static size_t gguf_block_bytes(int type) { return type == ORC_GGUF_Q4_0 ? 18 : 34; }
+
+/* The f32 value of element (n, k), read from the GGUF bytes. */
+float orc_gguf_weight_f32(int type, const uint8_t* src, int K, int n, int k) {
+    const uint8_t* B = src + (size_t)n * (K / 32) * gguf_block_bytes(type) + (size_t)(k / 32) * gguf_block_bytes(type);
+    uint16_t dh = (uint16_t)(B[0] | (B[1] << 8));
+    float d = (float)orc_f16_value(dh);
+    int j = k % 32;
+    if (type == ORC_GGUF_Q4_0) {
+        uint8_t byte = B[2 + (j % 16)];
+        int nib = j < 16 ? (byte & 0xF) : (byte >> 4);
+        float v = (float)(nib - 8) * d;
+        return v;
+    }
+    int q = (int8_t)B[2 + j];
+    float v = (float)q * d;
+    return v;
+}
+
+void orc_gguf_dequant(int type, const uint8_t* src, int N, int K, float* out) {
+    for (int n = 0; n < N; n++)
+        for (int k = 0; k < K; k++) out[(size_t)n * K + k] = orc_gguf_weight_f32(type, src, K, n, k);
+}
+
+/* The split layout of the same weights: Q4_0 -> Q4 codes [N][K/2] (the 16 code bytes of each
+ * block, unchanged) and f16 scales [N][K/32] (the block's 2 scale bytes); Q8_0 -> Q8 codes
+ * [N][K] and f32 scales [N][K/32] (the f16 scale widened, exactly). */
+void orc_gguf_repack(int type, const uint8_t* src, int N, int K, uint8_t* codes, void* scales) {
+    size_t bb = gguf_block_bytes(type), nb = (size_t)K / 32;
+    for (int n = 0; n < N; n++)
+        for (size_t b = 0; b < nb; b++) {
+            const uint8_t* B = src + ((size_t)n * nb + b) * bb;
+            uint16_t dh = (uint16_t)(B[0] | (B[1] << 8));
+            if (type == ORC_GGUF_Q4_0) {
+                for (int j = 0; j < 16; j++) codes[(size_t)n * (K / 2) + 16 * b + j] = B[2 + j];
+                ((uint16_t*)scales)[(size_t)n * nb + b] = dh;
+            } else {
+                for (int j = 0; j < 32; j++) codes[(size_t)n * K + 32 * b + j] = B[2 + j];
+                ((float*)scales)[(size_t)n * nb + b] = (float)orc_f16_value(dh);
+            }
+        }
+}

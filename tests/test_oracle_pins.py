@@ -388,3 +388,58 @@ def test_moe_combine_closed_forms(orc):
     assert np.allclose(y[0], 0.7 * O[0] + 0.3 * O[1], rtol=1e-15)
     assert np.allclose(y[1], 0.25 * O[1] - 0.5 * O[2], rtol=1e-15)
     assert np.allclose(b[1], 0.25 * O[1] + 0.5 * O[2], rtol=1e-15)
+
+
+# ---- GGUF blocks with in-block scales (oxinfer src/metal.rs, SHADER_SRC, Q4_0W and Q8_0W) ---------
+def _gguf_q4_0_block(d_bits, nib_bytes):
+    return np.concatenate([[d_bits & 0xFF, d_bits >> 8], nib_bytes]).astype(np.uint8)
+
+
+def test_gguf_q4_0_hand_blocks(orc):
+    """Two rows of two blocks, values worked by hand: block = f16 scale then 16 bytes whose low
+    nibble is element j and high nibble element j + 16; value (nibble - 8) * d."""
+    nib = np.full(16, 0x88, np.uint8)
+    nib[0], nib[15] = 0xF0, 0x1F
+    b00 = _gguf_q4_0_block(0x3800, nib)                      # d = 0.5
+    b01 = _gguf_q4_0_block(0xC000, np.full(16, 0xFF, np.uint8))  # d = -2, every nibble 15
+    b10 = _gguf_q4_0_block(0x3C00, np.zeros(16, np.uint8))   # d = 1, every nibble 0
+    b11 = _gguf_q4_0_block(0x0001, np.full(16, 0x9A, np.uint8))  # d = 2^-24 (subnormal), nibbles 10 / 9
+    src = np.concatenate([b00, b01, b10, b11])
+    w = orc.gguf_dequant("q4_0", src, 2, 64)
+    exp0 = np.zeros(32)
+    exp0[0], exp0[16], exp0[15], exp0[31] = -4.0, 3.5, 3.5, -3.5
+    assert np.array_equal(w[0, :32], exp0)
+    assert np.all(w[0, 32:] == -14.0)                        # (15 - 8) * -2
+    assert np.all(w[1, :32] == -8.0)
+    assert np.all(w[1, 32:48] == 2.0 * 2.0 ** -24) and np.all(w[1, 48:] == 1.0 * 2.0 ** -24)
+
+
+def test_gguf_q8_0_hand_block(orc):
+    """Q8_0: f16 scale then 32 signed bytes; value q * d."""
+    q = np.zeros(32, np.int8)
+    q[0], q[1], q[2], q[31] = 127, -128, -1, 5
+    src = np.concatenate([[0x00, 0x34], q.view(np.uint8)]).astype(np.uint8)   # d = 0.25
+    w = orc.gguf_dequant("q8_0", src, 1, 32)
+    exp = np.zeros(32)
+    exp[0], exp[1], exp[2], exp[31] = 31.75, -32.0, -0.25, 1.25
+    assert np.array_equal(w[0], exp)
+
+
+@pytest.mark.parametrize("gtype", ["q4_0", "q8_0"])
+def test_gguf_repack_matches_direct_decode(orc, gtype):
+    """The split-layout repack, decoded by the Q4 / Q8 decoders, gives every GGUF element's value
+    bit for bit (two independent paths: the in-block decoder and the split-layout decoder)."""
+    rng = np.random.default_rng(5)
+    N, K = 5, 128
+    nb = N * K // 32
+    bb = orc.GGUF_BLOCK_BYTES[gtype]
+    src = rng.integers(0, 256, nb * bb).astype(np.uint8).reshape(nb, bb)
+    import synth
+    d = synth.f16_uniform(9, 1, nb, -0.05, 0.05)                # negative scales too
+    src[:, 0], src[:, 1] = d & 0xFF, d >> 8
+    src = src.reshape(-1)
+    codes, scales = orc.gguf_repack(gtype, src, N, K)
+    direct = orc.gguf_dequant(gtype, src, N, K)
+    fmt = "q4" if gtype == "q4_0" else "q8"
+    split = orc.dequant_tile(fmt, codes, scales, None, 64, N, K, 0, 0, N, K, "f32")
+    assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
