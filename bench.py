@@ -10,7 +10,8 @@ torch.cuda.synchronize(); HIP events on the launch stream time it.  Each step is
 of the C entry point (arguments marshalled beforehand), so the host side keeps ahead of the GPU.
 `roofline` relates the dominant kernel's achieved rate to the chip's peak; `cpu_baseline` times the
 CPU oracle on the host cores.
-`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak) and the MoE expert block (GB/s), each on
+`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak), the MoE expert block (GB/s) and the GGUF
+Q4_0 repack of a 4096 x 4096 matrix (GB/s), each on
 its own synthetic workload; `--workload` selects one of them as the headline instead.
 """
 from __future__ import annotations
@@ -197,6 +198,30 @@ def setup(name: str):
     return setup_dense(ci, mode, copies)
 
 
+def measure_repack(steps: int, warmup: int) -> dict:
+    """GGUF Q4_0 -> split-layout repack of a 4096 x 4096 matrix (an upload-time step): GB/s of the
+    bytes it reads (18 per block) and writes (16 code bytes and a 2-byte scale per block)."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    N = K = 4096
+    nb = N * K // 32
+    rng = np.random.default_rng(3)
+    src = rng.integers(0, 256, nb * 18).astype(np.uint8).reshape(nb, 18)
+    src[:, 0], src[:, 1] = 0x00, 0x24                      # f16 scale 0.015625
+    s = _dev(src.reshape(-1))
+    codes = torch.empty(N * K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(nb, dtype=torch.int16, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    step = _bound("qg_repack_gguf", qg.QG_GGUF_Q4_0, s.data_ptr(), N, K, codes.data_ptr(), scales.data_ptr(), st)
+    ms, _ = _timed(step, steps, warmup)
+    nbytes = float(nb * (18 + 16 + 2))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "gguf_q4_0_repack", "config": "gguf_q4_0_repack_N4096_K4096", "mode": "exact",
+            "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "u8", "kernel": "repack_gguf_kernel",
+            "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
+            "bytes_per_step": nbytes}
+
+
 def measure(name: str, steps: int, warmup: int) -> dict:
     step, info = setup(name)
     ms, wall = _timed(step, steps, warmup)
@@ -311,6 +336,8 @@ def main():
             r.pop("_info")
             also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
             torch.cuda.empty_cache()
+        r = measure_repack(256, 20)
+        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
     c = info["cfg"]
     line = {
         "metric": "TFLOP/s (prefill qgemm) & HBM GB/s (T=1 qgemv), as % of MI355X roofline",

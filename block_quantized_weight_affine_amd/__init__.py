@@ -32,7 +32,7 @@ SYMBOLS = [
     "qg_strerror", "qg_abi_version",
     "qgemm_q4", "qgemm_q4a", "qgemm_q8",
     "qgemv_q4", "qgemv_q4a", "qgemv_q8",
-    "qg_dequant_dump",
+    "qg_dequant_dump", "qg_repack_gguf",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn",
 ]
@@ -70,6 +70,7 @@ def lib() -> C.CDLL:
         L.qgemv_q4a.argtypes = [_p, _p, _p, _i, _p, _i, _p, _i, _i, _i, _p]
         L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
         L.qg_moe_plan_host.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
+        L.qg_repack_gguf.argtypes = [_i, _p, _i, _i, _p, _p, _p]
         L.qg_moe_plan.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
         L.qg_x_half.argtypes = [_p, _i, _p, _i, _i, _p, _p, _p]
         L.qgemm_moe_grouped.argtypes = [_i, _p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]
@@ -180,6 +181,16 @@ def qg_dequant_dump(fmt, codes, scales, offsets, group, N, K, n0, k0, rows, cols
     _check(lib().qg_dequant_dump(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(codes), _ptr(scales),
                                  _ptr(offsets), group, N, K, n0, k0, rows, cols, staged, _ptr(out),
                                  _stream(stream)), "qg_dequant_dump")
+
+
+QG_GGUF_Q4_0, QG_GGUF_Q8_0 = 2, 8
+GGUF = {"q4_0": QG_GGUF_Q4_0, "q8_0": QG_GGUF_Q8_0}
+
+
+def qg_repack_gguf(gtype, src, N, K, codes, scales, stream=None):
+    """GGUF Q4_0 / Q8_0 blocks (device uint8 tensor) -> this library's codes and scales (device)."""
+    _check(lib().qg_repack_gguf(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K, _ptr(codes),
+                                _ptr(scales), _stream(stream)), "qg_repack_gguf")
 
 
 # ---- MoE ----------------------------------------------------------------------------------------

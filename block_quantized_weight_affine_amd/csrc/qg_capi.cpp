@@ -178,6 +178,17 @@ qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* se
     return QG_OK;
 }
 
+qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void* codes, void* scales,
+                         hipStream_t stream) {
+    if (type != QG_GGUF_Q4_0 && type != QG_GGUF_Q8_0) return QG_EINVAL;
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0) return QG_ESHAPE;
+    if (!src || !codes || !scales) return QG_EINVAL;
+    const bool q8 = type == QG_GGUF_Q8_0;
+    if (!aligned(src, 2) || !aligned(codes, 16) || !aligned(scales, q8 ? 4 : 2)) return QG_EALIGN;
+    const size_t nblocks = (size_t)N * (size_t)(K / 32);
+    return launched(qg::launch_repack_gguf(q8 ? 1 : 0, src, nblocks, codes, scales, stream));
+}
+
 qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                       int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, hipStream_t stream) {
     if (T < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32 || (long)T * k > 16384) return QG_ESHAPE;

@@ -45,6 +45,7 @@ hipError_t launch_swiglu(const float* GU, int R, int I, void* A, int at, float* 
 hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                            int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, int err_code,
                            hipStream_t s);
+hipError_t launch_repack_gguf(int q8, const void* src, size_t nblocks, void* codes, void* scales, hipStream_t s);
 hipError_t launch_moe_combine(const float* O, int R, const int32_t* slot_row, const float* slot_w, float* Y, int H,
                               int T, int k, int accumulate, hipStream_t s);
 

@@ -1,5 +1,7 @@
-// qg_misc.hip -- the dequant dump, the per-row f16 scaling, SwiGLU, the weighted combine and the
-// device routing plan.
+// qg_misc.hip -- the dequant dump, the per-row f16 scaling, SwiGLU, the weighted combine, the
+// device routing plan and the GGUF block repack.
+#include <algorithm>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -348,6 +350,46 @@ hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* se
                            hipStream_t s) {
     hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, logits, T, E, k, seg_off, row_src,
                        slot_row, slot_w, slot_expert, status, err_code);
+    return hipGetLastError();
+}
+
+}  // namespace qg
+
+namespace qg {
+
+// ---- GGUF blocks with in-block scales -> the split layout ------------------------------------------
+// Page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC, the GGUF dequantizers Q4_0W and Q8_0W: a row is
+// K/32 blocks; Q4_0 = f16 scale then 16 nibble bytes (18 bytes), Q8_0 = f16 scale then 32 signed
+// bytes (34 bytes); their values are those of Q4 and Q8 with the same codes and scale.  The repack
+// is exact: code bytes are copied, the f16 scale is copied (Q4) or widened to f32 (Q8).  One thread
+// per block, consecutive threads on consecutive blocks; blocks are 2-byte aligned, so they are read
+// as 16-bit words.
+template <int QB>  // code bytes per block: 16 (Q4_0) or 32 (Q8_0)
+__global__ void repack_gguf_kernel(const uint16_t* src, size_t nblocks, uint8_t* codes, void* scales) {
+    constexpr int W = 1 + QB / 2;  // 16-bit words per block
+    for (size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * blockDim.x) {
+        const uint16_t* B = src + b * W;
+        uint32_t w[QB / 4];
+#pragma unroll
+        for (int i = 0; i < QB / 4; i++) w[i] = (uint32_t)B[1 + 2 * i] | ((uint32_t)B[2 + 2 * i] << 16);
+        uint4* dst = (uint4*)(codes + b * QB);
+#pragma unroll
+        for (int i = 0; i < QB / 16; i++) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+        if constexpr (QB == 16)
+            ((uint16_t*)scales)[b] = B[0];
+        else
+            ((float*)scales)[b] = f16_to_f32(B[0]);
+    }
+}
+
+hipError_t launch_repack_gguf(int q8, const void* src, size_t nblocks, void* codes, void* scales, hipStream_t s) {
+    const unsigned grid = (unsigned)std::min<size_t>((nblocks + 255) / 256, 65535);
+    if (q8)
+        hipLaunchKernelGGL(repack_gguf_kernel<32>, dim3(grid), dim3(256), 0, s, (const uint16_t*)src, nblocks,
+                           (uint8_t*)codes, scales);
+    else
+        hipLaunchKernelGGL(repack_gguf_kernel<16>, dim3(grid), dim3(256), 0, s, (const uint16_t*)src, nblocks,
+                           (uint8_t*)codes, scales);
     return hipGetLastError();
 }
 

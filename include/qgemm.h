@@ -66,6 +66,8 @@ typedef enum {
 typedef enum { QG_X_F32 = 0, QG_X_F16 = 1, QG_X_BF16 = 2 } qg_xtype;
 typedef enum { QG_EXACT = 0, QG_FAST = 1 } qg_mode;
 typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2 } qg_format;
+/* GGUF block types with the scale inside each block (the values are GGML's type ids). */
+typedef enum { QG_GGUF_Q4_0 = 2, QG_GGUF_Q8_0 = 8 } qg_gguf_type;
 
 /* Text for a status code (static storage; never NULL). */
 const char* qg_strerror(qg_status s);
@@ -129,6 +131,20 @@ typedef struct {
     const void* scales;
     const uint16_t* offsets;
 } qg_expert;
+
+/* GGUF blocks to the split layout, on the device (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC,
+ * the GGUF dequantizers Q4_0W and Q8_0W).  src: N rows of K/32 blocks each, row after row;
+ * QG_GGUF_Q4_0 block = f16 scale d (little-endian) then 16 bytes, byte j holding element j in its low
+ * nibble and element j + 16 in its high nibble, value (nibble - 8) * d; QG_GGUF_Q8_0 block = f16 d
+ * then 32 signed bytes q, value q * d.  Writes the same weights in this library's layout, exactly:
+ * Q4_0 -> Q4 codes uint8 [N][K/2] and f16 scales [N][K/32] (bytes copied); Q8_0 -> Q8 codes int8
+ * [N][K] and f32 scales [N][K/32] (each f16 scale widened, which is exact), so every qgemm_q4 /
+ * qgemm_q8 / qgemv_* entry point then computes with them.  Device pointers owned by the caller;
+ * src 2-byte aligned, codes 16-byte aligned, scales 2- (Q4_0) or 4-byte (Q8_0) aligned, else
+ * QG_EALIGN; N >= 1, K >= 32, K % 32 == 0, else QG_ESHAPE; an unknown type or a null pointer gives
+ * QG_EINVAL.  Asynchronous on `stream`; nothing is allocated. */
+qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void* codes, void* scales,
+                         hipStream_t stream);
 
 /* Routing plan, on the HOST (all pointers host memory).  logits f32 [T][E].  For each token:
  * the k largest logits, equal logits in ascending expert index; weight_j = exp(l_j - l_max) /

@@ -100,6 +100,24 @@ def test_dump_and_moe_validation_codes():
                         0x100010, ws, None) == qg.QG_EALIGN
 
 
+def test_repack_gguf_validation_codes():
+    """qg_repack_gguf checks type, sizes, pointers and alignment on the host, before any HIP call."""
+    L = qg.lib()
+
+    def call(t=qg.QG_GGUF_Q4_0, src=A16, N=8, K=256, codes=A16b, scales=A16c):
+        return L.qg_repack_gguf(t, src, N, K, codes, scales, None)
+
+    assert call(t=3) == qg.QG_EINVAL
+    assert call(N=0) == qg.QG_ESHAPE
+    assert call(K=48) == qg.QG_ESHAPE
+    assert call(K=0) == qg.QG_ESHAPE
+    assert call(src=None) == qg.QG_EINVAL
+    assert call(scales=None) == qg.QG_EINVAL
+    assert call(src=A16 + 1) == qg.QG_EALIGN
+    assert call(codes=A16b + 8) == qg.QG_EALIGN
+    assert call(t=qg.QG_GGUF_Q8_0, scales=A16c + 2) == qg.QG_EALIGN
+
+
 def test_device_plan_validation_codes():
     """qg_moe_plan checks its sizes and pointers on the host, before any HIP call."""
     L = qg.lib()
