@@ -10,8 +10,9 @@ torch.cuda.synchronize(); HIP events on the launch stream time it.  Each step is
 of the C entry point (arguments marshalled beforehand), so the host side keeps ahead of the GPU.
 `roofline` relates the dominant kernel's achieved rate to the chip's peak; `cpu_baseline` times the
 CPU oracle on the host cores.
-`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak), the MoE expert block (GB/s) and the GGUF
-Q4_0 repack of a 4096 x 4096 matrix (GB/s), each on
+`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak), the MoE expert block (GB/s), the GGUF
+Q4_0 repack of a 4096 x 4096 matrix (GB/s) and a batched q / k / v decode step (GB/s, with the time
+of the same three matrices as separate calls), each on
 its own synthetic workload; `--workload` selects one of them as the headline instead.
 """
 from __future__ import annotations
@@ -198,6 +199,44 @@ def setup(name: str):
     return setup_dense(ci, mode, copies)
 
 
+def measure_batch(steps: int, warmup: int) -> dict:
+    """Decode step of three Q8 matrices sharing X (q / k / v shaped: N 4096, 1024, 1024; K 4096; T 1)
+    as one qgemm_batch call, against the same three matrices as three qgemv_q8 calls.  Each step
+    reads the next of 12 weight sets (340 MB, more than the 256 MB Infinity Cache)."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    K, Ns, copies = 4096, (4096, 1024, 1024), 12
+    base = [synth.make_dense("q8", N, K, 1, "f32", 1.0, 1001 + 10 * i) for i, N in enumerate(Ns)]
+    dev_sets = []
+    for c in range(copies):
+        js = []
+        for w, N in zip(base, Ns):
+            js.append((_dev(w["codes"]), _dev(w["scales"]), torch.empty((1, N), device="cuda"), N))
+        dev_sets.append(js)
+    X = _dev(base[0]["X"].reshape(1, K))
+    st = torch.cuda.current_stream().cuda_stream
+    arrs = [qg.job_array([(c_, s_, None, y, N) for (c_, s_, y, N) in js]) for js in dev_sets]
+    import ctypes as C
+    batch = _bound("qgemm_batch", qg.QG_FMT_Q8, 64, [C.cast(a, C.c_void_p).value for a in arrs], 3, X.data_ptr(),
+                   qg.QG_X_F32, K, 1, qg.QG_EXACT, st)
+    singles = [_bound("qgemv_q8", [js[i][0].data_ptr() for js in dev_sets], [js[i][1].data_ptr() for js in dev_sets],
+                      X.data_ptr(), qg.QG_X_F32, [js[i][2].data_ptr() for js in dev_sets], Ns[i], K, 1, st)
+               for i in range(3)]
+
+    def separate(i):
+        for f in singles:
+            f(i)
+    ms_b, _ = _timed(batch, steps, warmup)
+    ms_s, _ = _timed(separate, steps, warmup)
+    nbytes = float(sum(N * (K + K // 32 * 4) + 4 * N for N in Ns) + 4 * K)
+    gbs = nbytes / (ms_b * 1e-3) / 1e9
+    return {"workload": "q8_batch_qkv_decode", "config": "q8_jobs_N4096_1024_1024_K4096_T1", "mode": "exact",
+            "ms_per_step": ms_b, "us_per_step": ms_b * 1e3, "dtype": "f32", "kernel": "gemv1_batch_kernel",
+            "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
+            "bytes_per_step": nbytes, "us_three_separate_calls": ms_s * 1e3, "keep": (arrs, dev_sets, X)}
+
+
 def measure_repack(steps: int, warmup: int) -> dict:
     """GGUF Q4_0 -> split-layout repack of a 4096 x 4096 matrix (an upload-time step): GB/s of the
     bytes it reads (18 per block) and writes (16 code bytes and a 2-byte scale per block)."""
@@ -337,6 +376,9 @@ def main():
             also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
             torch.cuda.empty_cache()
         r = measure_repack(256, 20)
+        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        r = measure_batch(512, 50)
+        r.pop("keep")
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
     c = info["cfg"]
     line = {

@@ -30,7 +30,7 @@ MODE = {"exact": QG_EXACT, "fast": QG_FAST}
 # exported symbols of include/qgemm.h, in declaration order
 SYMBOLS = [
     "qg_strerror", "qg_abi_version",
-    "qgemm_q4", "qgemm_q4a", "qgemm_q8",
+    "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_batch",
     "qgemv_q4", "qgemv_q4a", "qgemv_q8",
     "qg_dequant_dump", "qg_repack_gguf",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
@@ -71,6 +71,7 @@ def lib() -> C.CDLL:
         L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
         L.qg_moe_plan_host.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
         L.qg_repack_gguf.argtypes = [_i, _p, _i, _i, _p, _p, _p]
+        L.qgemm_batch.argtypes = [_i, _i, _p, _i, _p, _i, _i, _i, _i, _p]
         L.qg_moe_plan.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
         L.qg_x_half.argtypes = [_p, _i, _p, _i, _i, _p, _p, _p]
         L.qgemm_moe_grouped.argtypes = [_i, _p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]
@@ -181,6 +182,27 @@ def qg_dequant_dump(fmt, codes, scales, offsets, group, N, K, n0, k0, rows, cols
     _check(lib().qg_dequant_dump(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(codes), _ptr(scales),
                                  _ptr(offsets), group, N, K, n0, k0, rows, cols, staged, _ptr(out),
                                  _stream(stream)), "qg_dequant_dump")
+
+
+class QgJob(C.Structure):
+    """qg_job of qgemm.h: one weight matrix of a batched call."""
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("offsets", C.c_void_p), ("Y", C.c_void_p),
+                ("N", C.c_int)]
+
+
+def job_array(jobs):
+    """Host array of qg_job from (codes, scales, offsets-or-None, Y, N) tuples of device tensors."""
+    arr = (QgJob * len(jobs))()
+    for i, (c, s, o, y, n) in enumerate(jobs):
+        arr[i] = QgJob(_ptr(c), _ptr(s), _ptr(o), _ptr(y), int(n))
+    return arr
+
+
+def qgemm_batch(fmt, group, jobs, X, K, T, mode="exact", xt=None, stream=None):
+    """jobs: list of (codes, scales, offsets-or-None, Y, N) sharing X [T][K]."""
+    arr = job_array(jobs)
+    _check(lib().qgemm_batch(FMT[fmt] if isinstance(fmt, str) else fmt, group, C.cast(arr, C.c_void_p), len(jobs),
+                             _ptr(X), _xt(X) if xt is None else xt, K, T, _mode(mode), _stream(stream)), "qgemm_batch")
 
 
 QG_GGUF_Q4_0, QG_GGUF_Q8_0 = 2, 8

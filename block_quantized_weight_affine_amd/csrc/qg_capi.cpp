@@ -178,6 +178,55 @@ qg_status qg_moe_plan_host(const float* logits, int T, int E, int k, int32_t* se
     return QG_OK;
 }
 
+qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const void* X, qg_xtype xt, int K,
+                      int T, qg_mode mode, hipStream_t stream) {
+    if (!jobs) return QG_EINVAL;
+    if (J < 1 || J > 64) return QG_ESHAPE;
+    for (int j = 0; j < J; j++) {
+        const qg_job& b = jobs[j];
+        const qg_status st = check_dense(fmt, b.codes, b.scales, b.offsets, group, X, xt, b.Y, b.N, K, T, mode);
+        if (st != QG_OK) return st;
+    }
+    if (T == 0) return QG_OK;
+    if (T > 8 && mode == QG_FAST && xt == QG_X_F32) return QG_EUNSUPPORTED;
+    if (T == 1) {
+        bool all = true;
+        for (int j0 = 0; j0 < J && all; j0 += qg::kMaxBatchJobs) {
+            qg::BatchJobs bj{};
+            bj.J = std::min(qg::kMaxBatchJobs, J - j0);
+            for (int i = 0; i < bj.J; i++) {
+                const qg_job& b = jobs[j0 + i];
+                bj.start[i + 1] = bj.start[i] + b.N;
+                bj.codes[i] = b.codes;
+                bj.scales[i] = b.scales;
+                bj.offs[i] = b.offsets;
+                bj.Y[i] = b.Y;
+            }
+            GemmParams p = dense_params(nullptr, nullptr, nullptr, group, X, nullptr, bj.start[bj.J], K, 1);
+            hipError_t err = hipSuccess;
+            if (!qg::launch_gemv1_batch(fmt, xt, p, bj, stream, err)) {
+                all = false;  // K beyond the streaming kernel: nothing was launched for this group
+                for (int j = j0; j < J; j++) {
+                    const qg_job& b = jobs[j];
+                    const qg_status st = run_dense(fmt, b.codes, b.scales, b.offsets, group, X, xt, b.Y, b.N, K, T,
+                                                   mode, false, stream);
+                    if (st != QG_OK) return st;
+                }
+            } else if (err != hipSuccess) {
+                return QG_ELAUNCH;
+            }
+        }
+        return QG_OK;
+    }
+    for (int j = 0; j < J; j++) {
+        const qg_job& b = jobs[j];
+        const qg_status st = run_dense(fmt, b.codes, b.scales, b.offsets, group, X, xt, b.Y, b.N, K, T, mode, false,
+                                       stream);
+        if (st != QG_OK) return st;
+    }
+    return QG_OK;
+}
+
 qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void* codes, void* scales,
                          hipStream_t stream) {
     if (type != QG_GGUF_Q4_0 && type != QG_GGUF_Q8_0) return QG_EINVAL;

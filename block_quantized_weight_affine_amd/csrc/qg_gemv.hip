@@ -368,8 +368,10 @@ constexpr int kStreamKMax = 16384;  // X in LDS as f32: at most 64 KiB
 constexpr int kStreamSteps = 4;     // steps (64 units each) per item
 constexpr int kStreamWgPerCu = 4;   // resident workgroups per CU when LDS allows
 
-template <int FMT, int XT>
-__global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams p) {
+// BATCH: p.N is the total row count of the jobs in bj; a wavefront's row g belongs to the job j
+// with start[j] <= g < start[j+1] (found by a scan over at most 8 wave-uniform entries).
+template <int FMT, int XT, bool BATCH>
+__device__ __forceinline__ void gemv1_body(const GemmParams& p, const BatchJobs& bj) {
     extern __shared__ __attribute__((aligned(16))) float xs[];  // K floats
     constexpr int W = kStreamThreads / 64, S = kStreamSteps;
     constexpr int XV = (XT == XT_F32) ? 4 : 8;  // X values per 16-byte load
@@ -406,11 +408,30 @@ __global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams
 
     const int tw = W * (int)gridDim.x;
     const float sc = p.rs ? p.rs[0] : 1.f;
+    auto job_of = [&](int g) {
+        int j = 0;
+        if constexpr (BATCH) {
+#pragma unroll
+            for (int i = 1; i < kMaxBatchJobs; i++)
+                if (i < bj.J && g >= bj.start[i]) j = i;
+        }
+        return j;
+    };
     auto load_item = [&](int row, int c, Unit<FMT> (&w)[S]) {
+        const void* codes = p.codes;
+        const void* scales = p.scales;
+        const uint16_t* offs = p.offs;
+        if constexpr (BATCH) {
+            const int j = job_of(row);
+            codes = bj.codes[j];
+            scales = bj.scales[j];
+            offs = bj.offs[j];
+            row -= bj.start[j];
+        }
 #pragma unroll
         for (int j = 0; j < S; j++) {
             const int u = min(64 * (S * c + j) + lane, units - 1);
-            w[j] = load_unit<FMT>(p.codes, p.scales, p.offs, p.group, K, row, u);
+            w[j] = load_unit<FMT>(codes, scales, offs, p.group, K, row, u);
         }
     };
     auto compute_item = [&](int c, const Unit<FMT> (&w)[S], float& acc) {
@@ -468,7 +489,14 @@ __global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams
         compute_item(c, cu, acc);
         if (c + 1 == items) {
             const float v = wave_sum(acc);
-            if (lane == 0) p.Y[n] = v * sc;
+            if (lane == 0) {
+                if constexpr (BATCH) {
+                    const int j = job_of(n);
+                    bj.Y[j][n - bj.start[j]] = v * sc;
+                } else {
+                    p.Y[n] = v * sc;
+                }
+            }
             acc = 0.f;
         }
         n = n2;
@@ -479,10 +507,20 @@ __global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams
     }
 }
 
+template <int FMT, int XT>
+__global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams p) {
+    gemv1_body<FMT, XT, false>(p, BatchJobs{});
+}
+
+template <int FMT, int XT>
+__global__ __launch_bounds__(kStreamThreads) void gemv1_batch_kernel(GemmParams p, BatchJobs bj) {
+    gemv1_body<FMT, XT, true>(p, bj);
+}
+
 // Single X row with K <= kStreamKMax: up to kStreamWgPerCu resident workgroups per CU, fewer when
 // their X copies would not fit in the CU's 160 KiB of LDS.
 template <int FMT, int XT>
-static bool gemv1(const GemmParams& p, hipStream_t s) {
+static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = nullptr) {
     if (p.K > kStreamKMax) return false;
     static int cus[64] = {0};
     int dev = 0;
@@ -496,7 +534,10 @@ static bool gemv1(const GemmParams& p, hipStream_t s) {
     const size_t lds = (size_t)p.K * 4;
     const int per_cu = std::max(1, std::min(kStreamWgPerCu, (int)((160u * 1024u) / lds)));
     const int grid = std::max(1, std::min((p.N + W - 1) / W, cus[dev] * per_cu));
-    hipLaunchKernelGGL((gemv1_stream_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p);
+    if (bj)
+        hipLaunchKernelGGL((gemv1_batch_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p, *bj);
+    else
+        hipLaunchKernelGGL((gemv1_stream_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p);
     return true;
 }
 
@@ -568,6 +609,22 @@ static void gemv_xt(int xt, const GemmParams& p, bool grouped, hipStream_t s) {
     if (xt == XT_F32) gemv_pick<FMT, XT_F32>(p, grouped, s);
     else if (xt == XT_F16) gemv_pick<FMT, XT_F16>(p, grouped, s);
     else gemv_pick<FMT, XT_BF16>(p, grouped, s);
+}
+
+template <int FMT>
+static bool gemv1_batch_xt(int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s) {
+    if (xt == XT_F32) return gemv1<FMT, XT_F32>(p, s, &bj);
+    if (xt == XT_F16) return gemv1<FMT, XT_F16>(p, s, &bj);
+    return gemv1<FMT, XT_BF16>(p, s, &bj);
+}
+
+bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err) {
+    bool ok;
+    if (fmt == FMT_Q4) ok = gemv1_batch_xt<FMT_Q4>(xt, p, bj, s);
+    else if (fmt == FMT_Q4A) ok = gemv1_batch_xt<FMT_Q4A>(xt, p, bj, s);
+    else ok = gemv1_batch_xt<FMT_Q8>(xt, p, bj, s);
+    err = ok ? hipGetLastError() : hipSuccess;
+    return ok;
 }
 
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s) {

@@ -32,10 +32,25 @@ struct GemmParams {
     int x_rows;                  // rows of X (bounds for row_src)
 };
 
+// Several weight matrices sharing one X row in one T = 1 launch: job j owns the global output rows
+// [start[j], start[j+1]) and writes them to Y[j] (page "oxinfer 0.0.5 src/metal.rs",
+// Backend::matmul, whose jobs share X).  Passed by value in the kernel arguments.
+constexpr int kMaxBatchJobs = 8;
+struct BatchJobs {
+    int J;
+    int start[kMaxBatchJobs + 1];
+    const void* codes[kMaxBatchJobs];
+    const void* scales[kMaxBatchJobs];
+    const uint16_t* offs[kMaxBatchJobs];
+    float* Y[kMaxBatchJobs];
+};
+
 // Kernel launchers; each returns a hipError_t from hipGetLastError after the launch.
 hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s);
 hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
+// T = 1, K <= 16384: every job of bj in one launch (p.N = bj.start[bj.J]); false if not applicable.
+bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err);
 hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
                                int N, int K, int n0, int k0, int rows, int cols, int staged, void* out,
                                hipStream_t s);

@@ -132,6 +132,27 @@ typedef struct {
     const uint16_t* offsets;
 } qg_expert;
 
+/* One weight matrix of a batched call: device pointers as in qgemm_q4 / qgemm_q4a / qgemm_q8
+ * (offsets used by QG_FMT_Q4A only), Y f32 [T][N]. */
+typedef struct {
+    const void* codes;
+    const void* scales;
+    const uint16_t* offsets;
+    float* Y;
+    int N;
+} qg_job;
+
+/* Several weight matrices that share one X (page "oxinfer 0.0.5 src/metal.rs", Backend::matmul,
+ * whose jobs share X): for every job j < J, jobs[j].Y = X . dequant(W_j)^T with the same rules as
+ * the single-matrix entry points (format fmt and group for all jobs, X [T][K] of type xt, mode).
+ * jobs is a HOST array (read during the call, not kept); its pointers are device memory.  T = 1
+ * with K <= 16384 runs every 8 jobs in one launch of the streaming GEMV (the jobs' rows walked as one
+ * matrix), which saves a launch per job in decode; other shapes run one call per job.  Every job is
+ * validated before anything is launched (the first failing job's status is returned, with the
+ * codes of qgemm_q4 / qgemm_q8); 1 <= J <= 64 else QG_ESHAPE; jobs NULL gives QG_EINVAL. */
+qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const void* X, qg_xtype xt,
+                      int K, int T, qg_mode mode, hipStream_t stream);
+
 /* GGUF blocks to the split layout, on the device (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC,
  * the GGUF dequantizers Q4_0W and Q8_0W).  src: N rows of K/32 blocks each, row after row;
  * QG_GGUF_Q4_0 block = f16 scale d (little-endian) then 16 bytes, byte j holding element j in its low

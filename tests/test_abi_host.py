@@ -100,6 +100,27 @@ def test_dump_and_moe_validation_codes():
                         0x100010, ws, None) == qg.QG_EALIGN
 
 
+def test_batch_validation_codes():
+    """qgemm_batch validates every job (with the dense entry points' codes) before any launch."""
+    L = qg.lib()
+
+    def call(jobs, J=None, T=1, mode=qg.QG_EXACT, xt=qg.QG_X_F32, K=256):
+        arr = qg.job_array(jobs) if jobs is not None else None
+        ptr = None if arr is None else __import__("ctypes").cast(arr, __import__("ctypes").c_void_p)
+        return L.qgemm_batch(qg.QG_FMT_Q4, 64, ptr, len(jobs) if J is None else J, A16c, xt, K, T, mode, None)
+
+    good = (A16, A16b, None, A16d, 64)
+    assert call(None, J=1) == qg.QG_EINVAL
+    assert call([good], J=0) == qg.QG_ESHAPE
+    assert call([good] * 65) == qg.QG_ESHAPE
+    assert call([good, (A16, A16b, None, A16d, 0)]) == qg.QG_ESHAPE            # N = 0 in job 1
+    assert call([good, good, (A16 + 8, A16b, None, A16d, 64)]) == qg.QG_EALIGN  # codes of job 2
+    assert call([good, (None, A16b, None, A16d, 64)]) == qg.QG_EINVAL
+    assert call([good], K=48) == qg.QG_ESHAPE
+    assert call([good], T=16, mode=qg.QG_FAST) == qg.QG_EUNSUPPORTED          # f32 X in fast mode, T > 8
+    assert call([good], T=0) == qg.QG_OK                                        # nothing to do
+
+
 def test_repack_gguf_validation_codes():
     """qg_repack_gguf checks type, sizes, pointers and alignment on the host, before any HIP call."""
     L = qg.lib()

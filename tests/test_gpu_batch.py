@@ -1,0 +1,47 @@
+"""Several weight matrices sharing one X (qgemm_batch) on the GPU: every job's Y against the oracle,
+for T = 1 (the jobs' rows walked by one streaming GEMV launch per 8 jobs), T = 3 (the GEMV per job)
+and T = 40 (the tile kernels per job); the batched T = 1 rows also equal single-matrix calls bit for
+bit (the same per-row arithmetic)."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_affine_amd as qg
+import synth
+from helpers import TAU, check_tol, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _jobs(fmt, Ns, K, seed):
+    ws = [synth.make_dense(fmt, N, K, 1, "f32", 1.0, seed + i, group=64) for i, N in enumerate(Ns)]
+    dw = [(dev(w["codes"]), dev(w["scales"]), dev(w["offsets"]) if "offsets" in w else None) for w in ws]
+    return ws, dw
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
+@pytest.mark.parametrize("case", [(1, [96, 160, 32, 48]), (1, [64] * 7 + [32, 96, 16]), (3, [96, 160, 32]),
+                                  (40, [128, 64])], ids=lambda c: f"T{c[0]}-J{len(c[1])}")
+def test_batch_matches_oracle(orc, fmt, case):
+    T, Ns = case
+    K = 576   # a multiple of the affine group (64); not of the 1024-value step
+    ws, dw = _jobs(fmt, Ns, K, 5000)
+    X = synth.normal_as(61, synth.STREAM_X, T * K, 0.0, 1.0, "f32").reshape(T, K)
+    Ys = [torch.full((T, N), float("nan"), device="cuda") for N in Ns]
+    print(f"batch {fmt} T={T} jobs={Ns}", flush=True)
+    qg.qgemm_batch(fmt, 64, [(c, s, o, y, N) for (c, s, o), y, N in zip(dw, Ys, Ns)], dev(X), K, T, "exact")
+    torch.cuda.synchronize()
+    for i, (w, y, N) in enumerate(zip(ws, Ys, Ns)):
+        Yr, S, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), 64, N, K, X, "f32", T)
+        check_tol(y.cpu().numpy(), Yr, S, TAU["exact"], f"job {i} (N {N})")
+    if T == 1:
+        for (c, s, o), y, N in zip(dw, Ys, Ns):
+            y1 = torch.full((1, N), float("nan"), device="cuda")
+            if fmt == "q4":
+                qg.qgemm_q4(c, s, dev(X), y1, N, K, 1, "exact")
+            elif fmt == "q4a":
+                qg.qgemm_q4a(c, s, o, 64, dev(X), y1, N, K, 1, "exact")
+            else:
+                qg.qgemm_q8(c, s, dev(X), y1, N, K, 1, "exact")
+            torch.cuda.synchronize()
+            assert np.array_equal(y1.cpu().numpy().view(np.uint32), y.cpu().numpy().view(np.uint32))
