@@ -11,8 +11,8 @@ of the C entry point (arguments marshalled beforehand), so the host side keeps a
 `roofline` relates the dominant kernel's achieved rate to the chip's peak; `cpu_baseline` times the
 CPU oracle on the host cores.
 `also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak), the MoE expert block (GB/s), the GGUF
-Q4_0 repack of a 4096 x 4096 matrix (GB/s) and a batched q / k / v decode step (GB/s, with the time
-of the same three matrices as separate calls), each on
+Q4_0 repack of a 4096 x 4096 matrix (GB/s), a batched q / k / v decode step (GB/s, with the time
+of the same three matrices as separate calls) and the Q8 GEMV with T = 4 (GB/s), each on
 its own synthetic workload; `--workload` selects one of them as the headline instead.
 """
 from __future__ import annotations
@@ -237,6 +237,31 @@ def measure_batch(steps: int, warmup: int) -> dict:
             "bytes_per_step": nbytes, "us_three_separate_calls": ms_s * 1e3, "keep": (arrs, dev_sets, X)}
 
 
+def measure_gemv_t(T: int, steps: int, warmup: int) -> dict:
+    """The Q8 GEMV decode shape (N = K = 4096, f32 X) with T = 2..8 rows of X: HBM GB/s of its
+    algorithmic bytes, 16 rotating weight copies."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    N = K = 4096
+    w = synth.make_dense("q8", N, K, T, "f32", 1.0, 1001)
+    copies = 16
+    C_ = [_dev(w["codes"]) for _ in range(copies)]
+    S_ = [_dev(w["scales"]) for _ in range(copies)]
+    X = _dev(w["X"].reshape(T, K))
+    Y = torch.empty((T, N), device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    step = _bound("qgemv_q8", [c.data_ptr() for c in C_], [s.data_ptr() for s in S_], X.data_ptr(), qg.QG_X_F32,
+                  Y.data_ptr(), N, K, T, st)
+    ms, _ = _timed(step, steps, warmup)
+    nbytes = float(N * K + N * K // 32 * 4 + T * K * 4 + T * N * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"q8_gemv_T{T}", "config": f"q8_gemv_T{T}_N4096_K4096", "mode": "exact",
+            "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f32", "kernel": "gemv_kernel",
+            "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
+            "bytes_per_step": nbytes}
+
+
 def measure_repack(steps: int, warmup: int) -> dict:
     """GGUF Q4_0 -> split-layout repack of a 4096 x 4096 matrix (an upload-time step): GB/s of the
     bytes it reads (18 per block) and writes (16 code bytes and a 2-byte scale per block)."""
@@ -379,6 +404,8 @@ def main():
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         r = measure_batch(512, 50)
         r.pop("keep")
+        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        r = measure_gemv_t(4, 512, 50)
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
     c = info["cfg"]
     line = {

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(DMA ? 3 : 1)
     // Every wavefront stays to the end (the X chunks are staged by the whole workgroup); rows
     // beyond N are clamped on load and never stored.
     if constexpr (NTD > 0) {
-        gemv_chunk<FMT, XT, RW, NTD, TH>(p, p.codes, p.scales, p.offs, nrow0, 0, xs);
+        gemv_chunk<FMT, XT, RW, NTD, TH, 0, DMA>(p, p.codes, p.scales, p.offs, nrow0, 0, xs);
     } else {
         const int e = blockIdx.y;
         const int r0 = min(max(p.seg_off[e], 0), p.R);
@@ -558,8 +558,22 @@ static size_t gemv_lds_bytes(int K, int nt_lo, int nt_hi) {
 // Rows per workgroup: a single X row uses 8 wavefronts of 2 weight rows (one X copy in LDS serves
 // 16 rows, and each X value read from LDS serves 2); more X rows use 4 wavefronts of 2 or 4 rows,
 // so that the X staged per workgroup stays small next to the weights it serves.
+template <int FMT, int XT, int NT, int RWX, int THX>
+static void gemv_dense_dma(const GemmParams& p, hipStream_t s) {
+    constexpr int ROWS = RWX * THX / 64;
+    dim3 grid((p.N + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((gemv_kernel<FMT, XT, RWX, NT, THX, 8, true>), grid, dim3(THX), gemv_lds_bytes(p.K, NT, NT), s, p);
+}
+
 template <int FMT, int XT, int NT>
 static void gemv_dense(const GemmParams& p, hipStream_t s) {
+    // 3..8 f32 X rows: X staged straight into LDS, 2 weight rows per wavefront (twice the
+    // workgroups of 4 rows), three wavefronts per SIMD.  Measured on the Q8 decode shape (N = K =
+    // 4096): T = 4 10.9 us against 12.6 (4 rows per wavefront through registers), T = 8 17.8
+    // against 19.7; at T = 2 both run 7.3-7.5 us, and 1 row per wavefront is slower.
+    if constexpr (XT == XT_F32 && NT > 2) {
+        if ((size_t)p.x_rows * (size_t)p.K * 4 <= 0x7FFFFFF0u) return gemv_dense_dma<FMT, XT, NT, 2, 256>(p, s);
+    }
     constexpr int RW = NT == 1 ? 2 : NT == 2 ? 2 : 4;
     constexpr int TH = NT == 1 ? kGemv1Threads : kGemvThreads;
     constexpr int ROWS = RW * TH / 64;
