@@ -45,3 +45,28 @@ def test_batch_matches_oracle(orc, fmt, case):
                 qg.qgemm_q8(c, s, dev(X), y1, N, K, 1, "exact")
             torch.cuda.synchronize()
             assert np.array_equal(y1.cpu().numpy().view(np.uint32), y.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("case", [("q4", 1, 576, "f16", "exact"), ("q8", 1, 576, "bf16", "exact"),
+                                  ("q4a", 40, 576, "bf16", "fast"), ("q8", 1, 16416, "f32", "exact")],
+                         ids=lambda c: f"{c[0]}-T{c[1]}-K{c[2]}-{c[3]}-{c[4]}")
+def test_batch_other_paths(orc, case):
+    """16-bit X in the batched T = 1 kernel, fast mode through the per-job tile kernels, and K past
+    the streaming kernel's LDS copy (every job then runs the chunked GEMV)."""
+    fmt, T, K, xt, mode = case
+    Ns = [64, 96, 32]
+    ws, dw = _jobs(fmt, Ns, K, 5100)
+    X = synth.normal_as(67, synth.STREAM_X, T * K, 0.0, 1.0, xt).reshape(T, K)
+    Xd = dev(X)
+    if xt == "f16":
+        Xd = Xd.view(torch.float16)
+    elif xt == "bf16":
+        Xd = Xd.view(torch.bfloat16)
+    Ys = [torch.full((T, N), float("nan"), device="cuda") for N in Ns]
+    print(f"batch {fmt} T={T} K={K} {xt} {mode}", flush=True)
+    qg.qgemm_batch(fmt, 64, [(c, s, o, y, N) for (c, s, o), y, N in zip(dw, Ys, Ns)], Xd, K, T, mode)
+    torch.cuda.synchronize()
+    xo = X.view(np.uint16) if X.dtype == np.float16 else X
+    for i, (w, y, N) in enumerate(zip(ws, Ys, Ns)):
+        Yr, S, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), 64, N, K, xo, xt, T)
+        check_tol(y.cpu().numpy(), Yr, S, TAU[mode], f"job {i} (N {N})")
