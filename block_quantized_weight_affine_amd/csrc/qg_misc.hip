@@ -218,8 +218,9 @@ namespace qg {
 // pages build this on the host; here one workgroup builds it on the device, so a caller can chain
 // it with the grouped matmuls without a round trip.  Same outputs as the host plan:
 //  1. one wavefront per token: k rounds of a wavefront argmax under (larger logit, then lower
-//     index) over the logits held in registers (a NaN logit ranks below every other and sets the
-//     error flag); lane j keeps the j-th pick; weight_j = exp(l_j - l_max) / sum_i exp(l_i - l_max)
+//     index) over the logits held in registers -- two DPP reductions, the largest order-preserving
+//     key and then the lowest index holding it (a NaN logit ranks as -inf and sets the error
+//     flag); lane j keeps the j-th pick; weight_j = exp(l_j - l_max) / sum_i exp(l_i - l_max)
 //     in f64, summed in pick order, rounded to f32; the pick's expert is kept in LDS;
 //  2. per-expert counts (LDS integer atomics) and their inclusive scan -> seg_off;
 //  3. one wavefront per expert walks the slots in token order, 64 at a time: the ballot of slots
@@ -229,8 +230,35 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanNpl = 16;         // logits per lane: E <= 1024
 constexpr int kPlanSlots = 16384;    // T * k: the picks live in LDS (32 KiB)
 
-__device__ __forceinline__ bool plan_better(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// Order-preserving 32-bit image of a logit (larger value, larger key; -0 taken as +0 so that equal
+// values compare equal); 0 lies below the key of every value, -inf included.
+__device__ __forceinline__ uint32_t plan_key(float x) {
+    const uint32_t u = __float_as_uint(x == 0.f ? 0.f : x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float plan_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// Wavefront maximum / minimum, the same in every lane: DPP row shifts by 1, 2, 4 and 8 leave each
+// row's extreme in its lane 15, the row-15 and row-31 broadcasts carry them to lane 63, which is read
+// back.  Lanes without a source keep the identity (0 for the maximum, ~0 for the minimum).
+__device__ __forceinline__ uint32_t wave_umax32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_umin32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* logits, int T, int E, int k,
@@ -270,30 +298,25 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
         int my_e = 0;
         float my_v = 0.f;
         for (int j = 0; j < k; j++) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;  // worse than every real candidate, -inf ones included
+            // the lane's best untaken candidate (ascending index, so the lowest index among equal
+            // keys), then the wavefront's largest key and the lowest index holding it
+            uint32_t bk = 0;
+            int bi = 0x7fffffff;
 #pragma unroll
             for (int i = 0; i < kPlanNpl; i++) {
-                const int e = lane + 64 * i;
-                if (!((taken >> i) & 1u) && plan_better(v[i], e, bv, bi)) {
-                    bv = v[i];
-                    bi = e;
+                const uint32_t key = ((taken >> i) & 1u) ? 0u : plan_key(v[i]);
+                if (key > bk) {
+                    bk = key;
+                    bi = lane + 64 * i;
                 }
             }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (plan_better(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            // j < k <= E: an untaken real candidate remains, so bi < E
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+            const uint32_t kmax = wave_umax32(bk);
+            // j < k <= E: an untaken real candidate remains, so kmax > 0 and the winner is < E
+            const int win = (int)wave_umin32(bk == kmax ? (uint32_t)bi : 0xFFFFFFFFu);
+            if ((win & 63) == lane) taken |= 1u << (win >> 6);
             if (lane == j) {
-                my_e = bi;
-                my_v = bv;
+                my_e = win;
+                my_v = plan_value(kmax);
             }
         }
         const double lmax = (double)__shfl(my_v, 0, 64);
