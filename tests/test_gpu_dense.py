@@ -148,6 +148,22 @@ def test_fast_blocks_needing_pages_order(orc, fmt, shape):
     check_tol(Y, Yr, S, TAU["fast"], f"fixup {fmt} {shape}")
 
 
+@pytest.mark.parametrize("T,K", [(2, 10240), (4, 5120), (4, 5248), (8, 2560), (3, 6912)])
+def test_gemv_rows_chunked_k(orc, T, K):
+    """T rows of X whose K spans several of the multi-row kernel's LDS chunks (4096 values for T <= 4,
+    2048 above), the last one ragged or whole."""
+    N = 136
+    w = synth.make_dense("q4a", N, K, T, "f32", 1.0, 970 + T + K)
+    codes, scales, offs = weights_dev(w)
+    Y = torch.full((T + 1, N), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qgemv("q4a", codes, scales, offs, w["group"], dev_x(w["X"], "f32"), Y, N, K, T)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    Yr, S = _ref(orc, "q4a", w, w["X"], "f32", N, K, T)
+    check_tol(y[:T], Yr, S, TAU["exact"], f"gemv T={T} K={K}")
+    assert np.all(np.isnan(y[T:]))
+
+
 @pytest.mark.parametrize("K", [16384, 16416])
 def test_gemv_single_row_long_k(orc, K):
     """T = 1 at the longest K whose X fits the streaming kernel's LDS copy, and just past it (the
