@@ -519,9 +519,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv1_batch_kernel(GemmParams 
 
 // Single X row with K <= kStreamKMax: up to kStreamWgPerCu resident workgroups per CU, fewer when
 // their X copies would not fit in the CU's 160 KiB of LDS.
-template <int FMT, int XT>
-static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = nullptr) {
-    if (p.K > kStreamKMax) return false;
+static int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -530,14 +528,149 @@ static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = null
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
         cus[dev] = v;
     }
+    return cus[dev];
+}
+
+template <int FMT, int XT>
+static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = nullptr) {
+    if (p.K > kStreamKMax) return false;
     constexpr int W = kStreamThreads / 64;
     const size_t lds = (size_t)p.K * 4;
     const int per_cu = std::max(1, std::min(kStreamWgPerCu, (int)((160u * 1024u) / lds)));
-    const int grid = std::max(1, std::min((p.N + W - 1) / W, cus[dev] * per_cu));
+    const int grid = std::max(1, std::min((p.N + W - 1) / W, device_cus() * per_cu));
     if (bj)
         hipLaunchKernelGGL((gemv1_batch_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p, *bj);
     else
         hipLaunchKernelGGL((gemv1_stream_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p);
+    return true;
+}
+
+// T = 2..4 rows of X, K <= 16384: K is split over the workgroup's wavefronts, 64 units (1024
+// values) each, so that a lane owns one unit of every weight row and keeps that unit's 16 X values
+// of every X row in registers for the whole launch; no X is read from LDS.  Each wavefront takes
+// batches of KS_RB weight rows (the next batch's loads issued before the current one is
+// computed), reduces each (row, X row) partial within its four 16-lane rows, and the workgroup adds
+// those four sums of each wavefront through LDS after one barrier per batch.  Every workgroup reads
+// its wavefronts' X slices (T * K values) once, so X traffic falls as workgroups take more batches:
+// 16 resident wavefronts per CU for T <= 3, 8 for T = 4.  Measured on the Q8 decode shape (N = K =
+// 4096, f32 X, 16 rotating weight copies), against the chunked LDS kernel on the same box: T = 2
+// 6.98 us against 7.32, T = 3 8.18 against 9.07, T = 4 10.31 against 10.8 (16 wavefronts per CU at
+// T = 4: 10.62).  Full-wavefront xor-shuffle sums instead of the row sums: T = 4 13.9 us.
+constexpr int kSplitRows = 4;  // weight rows per batch
+
+// Sums of each 16-lane row of the wavefront by DPP row shifts by 1, 2, 4, 8 (lanes without a source
+// add 0): lane 15 of every row ends with its row's sum.
+__device__ __forceinline__ float row16_sum_dpp(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+    return v;
+}
+template <int FMT, int XT, int NT>
+__global__ __launch_bounds__(1024) void gemv_ksplit_kernel(GemmParams p) {
+    constexpr int RB = kSplitRows;
+    __shared__ float part[2][16][RB * NT][4];  // [batch parity][wavefront][row * NT + t][lane row]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = (int)blockDim.x >> 6;
+    const int K = p.K, units = K >> 4, N = p.N;
+    const int nb = (N + RB - 1) / RB;
+    int b = (int)blockIdx.x;
+    if (b >= nb) return;  // uniform over the workgroup
+    const int u = 64 * wave + lane;
+    const bool on = u < units;
+    const int uc = min(u, units - 1);
+
+    // This lane's unit of every X row (zero for a lane past K, so its partials are zero).
+    float x[NT][16], sx[NT];
+    {
+        int e0, e1;
+        unit_runs<FMT>(uc, e0, e1);
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const size_t e = (size_t)t * K + (h ? e1 : e0);
+                if constexpr (XT == XT_F32) {
+                    const float4 a = *(const float4*)((const float*)p.X + e);
+                    const float4 c = *(const float4*)((const float*)p.X + e + 4);
+                    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+                    for (int i = 0; i < 8; i++) x[t][8 * h + i] = on ? v[i] : 0.f;
+                } else {
+                    const uint4 q = *(const uint4*)((const uint16_t*)p.X + e);
+                    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const uint16_t hv = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
+                        const float v = (XT == XT_F16) ? f16_to_f32(hv) : bf16_to_f32(hv);
+                        x[t][8 * h + i] = on ? v : 0.f;
+                    }
+                }
+            }
+            sx[t] = 0.f;
+            if constexpr (FMT == FMT_Q4A) {
+#pragma unroll
+                for (int i = 0; i < 16; i++) sx[t] += x[t][i];
+            }
+        }
+    }
+    float sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) sc[t] = p.rs ? p.rs[t] : 1.f;
+    auto load_batch = [&](int bb, Unit<FMT> (&w)[RB]) {
+#pragma unroll
+        for (int r = 0; r < RB; r++)
+            w[r] = load_unit<FMT>(p.codes, p.scales, p.offs, p.group, K, min(bb * RB + r, N - 1), uc);
+    };
+    Unit<FMT> wa[RB], wb[RB];
+    load_batch(b, wa);
+
+    int par = 0;
+    auto step = [&](const Unit<FMT> (&cu)[RB], Unit<FMT> (&nx)[RB]) __attribute__((always_inline)) {
+        const int b2 = b + (int)gridDim.x;
+        const bool more = b2 < nb;
+        if (more) load_batch(b2, nx);
+#pragma unroll
+        for (int r = 0; r < RB; r++) {
+            float c[16];
+            unit_codes<FMT>(cu[r], c);
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                float pr = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; i++) pr = fmaf(c[i], x[t][i], pr);
+                const float v = row16_sum_dpp(unit_value<FMT>(cu[r], pr, sx[t]));
+                if ((lane & 15) == 15) part[par][wave][r * NT + t][lane >> 4] = v;
+            }
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < RB * NT) {
+            const int r = (int)threadIdx.x / NT, t = (int)threadIdx.x % NT, row = b * RB + r;
+            if (row < N) {
+                float s = 0.f;
+                for (int w = 0; w < W; w++) {
+                    const float4 q = *(const float4*)part[par][w][threadIdx.x];
+                    s += (q.x + q.y) + (q.z + q.w);
+                }
+                p.Y[(size_t)t * N + row] = s * sc[t];
+            }
+        }
+        par ^= 1;
+        b = b2;
+        return more;
+    };
+    while (step(wa, wb) && step(wb, wa)) {
+    }
+}
+
+template <int FMT, int XT, int NT>
+static bool gemv_ksplit(const GemmParams& p, hipStream_t s) {
+    if (p.R != NT || p.row_src || p.K > kStreamKMax) return false;
+    const int W = (p.K / 16 + 63) / 64;  // 1..16 wavefronts
+    const int nb = (p.N + kSplitRows - 1) / kSplitRows;
+    const int per_cu = std::max(1, (NT >= 4 ? 8 : 16) / W);
+    const int grid = std::max(1, std::min(nb, device_cus() * per_cu));
+    hipLaunchKernelGGL((gemv_ksplit_kernel<FMT, XT, NT>), dim3(grid), dim3(64 * W), 0, s, p);
     return true;
 }
 
@@ -571,6 +704,9 @@ static void gemv_dense(const GemmParams& p, hipStream_t s) {
     // workgroups of 4 rows), three wavefronts per SIMD.  Measured on the Q8 decode shape (N = K =
     // 4096): T = 4 10.9 us against 12.6 (4 rows per wavefront through registers), T = 8 17.8
     // against 19.7; at T = 2 both run 7.3-7.5 us, and 1 row per wavefront is slower.
+    if constexpr (NT >= 2 && NT <= 4) {
+        if (gemv_ksplit<FMT, XT, NT>(p, s)) return;
+    }
     if constexpr (XT == XT_F32 && NT > 2) {
         if ((size_t)p.x_rows * (size_t)p.K * 4 <= 0x7FFFFFF0u) return gemv_dense_dma<FMT, XT, NT, 2, 256>(p, s);
     }
