@@ -164,6 +164,22 @@ def test_gemv_rows_chunked_k(orc, T, K):
     assert np.all(np.isnan(y[T:]))
 
 
+@pytest.mark.parametrize("fmt,N,K,T", [("q8", 4096, 4096, 4), ("q4", 40, 16384, 4), ("q8", 40, 16416, 2),
+                                        ("q4a", 33, 16384, 3)])
+def test_gemv_few_rows_full_and_long_k(orc, fmt, N, K, T):
+    """T = 2..4: the Q8 decode shape at full size (every output against the oracle), the longest K the
+    K-split kernel takes (16 wavefronts of 1024 values), and just past it (the chunked kernel)."""
+    w = synth.make_dense(fmt, N, K, T, "f32", 1.0, 960 + T + K)
+    codes, scales, offs = weights_dev(w)
+    Y = torch.full((T + 1, N), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qgemv(fmt, codes, scales, offs, w["group"], dev_x(w["X"], "f32"), Y, N, K, T)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    Yr, S = _ref(orc, fmt, w, w["X"], "f32", N, K, T)
+    check_tol(y[:T], Yr, S, TAU["exact"], f"gemv {fmt} N={N} K={K} T={T}")
+    assert np.all(np.isnan(y[T:]))
+
+
 @pytest.mark.parametrize("K", [16384, 16416])
 def test_gemv_single_row_long_k(orc, K):
     """T = 1 at the longest K whose X fits the streaming kernel's LDS copy, and just past it (the
