@@ -143,7 +143,8 @@ def setup_dense(ci: int, mode: str, copies: int):
         "bytes": float(wbytes + xbytes + ybytes), "copies": copies, "weights": w,
         "dtype": ("f32" if mode == "exact" else c.xtype),
         "kernel": (("gemv1_stream_kernel" if c.T == 1 and c.K <= 16384 else
-                    "gemv_ksplit_kernel" if 2 <= c.T <= 4 and c.K <= 16384 else "gemv_kernel") if c.T <= 8
+                    "gemv_ksplit_kernel" if c.T >= 2 and c.K <= (16384 if c.T <= 4 else 8192) else "gemv_kernel")
+                   if c.T <= 8
                    else ("gemm_exact_kernel" if mode == "exact" else "gemm_fast_lds_kernel")),
         "keep": (codes, scales, offs, X, Y),
     }
@@ -262,7 +263,7 @@ def measure_gemv_t(T: int, steps: int, warmup: int) -> dict:
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"q8_gemv_T{T}", "config": f"q8_gemv_T{T}_N4096_K4096", "mode": "exact",
             "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f32",
-            "kernel": "gemv_ksplit_kernel" if T <= 4 else "gemv_kernel",
+            "kernel": "gemv_ksplit_kernel",
             "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
             "bytes_per_step": nbytes}
 

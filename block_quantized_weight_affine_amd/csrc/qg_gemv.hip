@@ -545,7 +545,7 @@ static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = null
     return true;
 }
 
-// T = 2..4 rows of X, K <= 16384: K is split over the workgroup's wavefronts, 64 units (1024
+// T = 2..8 rows of X, K <= 16384 (8192 for T > 4): K is split over the workgroup's wavefronts, 64 units (1024
 // values) each, so that a lane owns one unit of every weight row and keeps that unit's 16 X values
 // of every X row in registers for the whole launch; no X is read from LDS.  Each wavefront takes
 // batches of KS_RB weight rows (the next batch's loads issued before the current one is
@@ -555,7 +555,9 @@ static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = null
 // 16 resident wavefronts per CU for T <= 3, 8 for T = 4.  Measured on the Q8 decode shape (N = K =
 // 4096, f32 X, 16 rotating weight copies), against the chunked LDS kernel on the same box: T = 2
 // 6.98 us against 7.32, T = 3 8.18 against 9.07, T = 4 10.31 against 10.8 (16 wavefronts per CU at
-// T = 4: 10.62).  Full-wavefront xor-shuffle sums instead of the row sums: T = 4 13.9 us.
+// T = 4: 10.62).  Full-wavefront xor-shuffle sums instead of the row sums: T = 4 13.9 us.  T > 4
+// (152..200 VGPRs, two or three wavefronts per SIMD): T = 5 10.97 us against 12.88, T = 6 11.64
+// against 14.61, T = 8 14.05 against 17.94.
 constexpr int kSplitRows = 4;  // weight rows per batch
 
 // Sums of each 16-lane row of the wavefront by DPP row shifts by 1, 2, 4, 8 (lanes without a source
@@ -568,7 +570,7 @@ __device__ __forceinline__ float row16_sum_dpp(float v) {
     return v;
 }
 template <int FMT, int XT, int NT>
-__global__ __launch_bounds__(1024) void gemv_ksplit_kernel(GemmParams p) {
+__global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmParams p) {
     constexpr int RB = kSplitRows;
     __shared__ float part[2][16][RB * NT][4];  // [batch parity][wavefront][row * NT + t][lane row]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = (int)blockDim.x >> 6;
@@ -665,7 +667,8 @@ __global__ __launch_bounds__(1024) void gemv_ksplit_kernel(GemmParams p) {
 
 template <int FMT, int XT, int NT>
 static bool gemv_ksplit(const GemmParams& p, hipStream_t s) {
-    if (p.R != NT || p.row_src || p.K > kStreamKMax) return false;
+    // T > 4: X takes 16 T registers per lane, so workgroups of at most 8 wavefronts (K <= 8192)
+    if (p.R != NT || p.row_src || p.K > (NT <= 4 ? kStreamKMax : kStreamKMax / 2)) return false;
     const int W = (p.K / 16 + 63) / 64;  // 1..16 wavefronts
     const int nb = (p.N + kSplitRows - 1) / kSplitRows;
     const int per_cu = std::max(1, (NT >= 4 ? 8 : 16) / W);
@@ -704,7 +707,7 @@ static void gemv_dense(const GemmParams& p, hipStream_t s) {
     // workgroups of 4 rows), three wavefronts per SIMD.  Measured on the Q8 decode shape (N = K =
     // 4096): T = 4 10.9 us against 12.6 (4 rows per wavefront through registers), T = 8 17.8
     // against 19.7; at T = 2 both run 7.3-7.5 us, and 1 row per wavefront is slower.
-    if constexpr (NT >= 2 && NT <= 4) {
+    if constexpr (NT >= 2) {
         if (gemv_ksplit<FMT, XT, NT>(p, s)) return;
     }
     if constexpr (XT == XT_F32 && NT > 2) {

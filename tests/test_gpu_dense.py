@@ -165,10 +165,12 @@ def test_gemv_rows_chunked_k(orc, T, K):
 
 
 @pytest.mark.parametrize("fmt,N,K,T", [("q8", 4096, 4096, 4), ("q4", 40, 16384, 4), ("q8", 40, 16416, 2),
-                                        ("q4a", 33, 16384, 3)])
+                                        ("q4a", 33, 16384, 3), ("q8", 1000, 4096, 8), ("q4", 40, 8192, 8),
+                                        ("q4a", 40, 8256, 6), ("q8", 24, 8224, 5)])
 def test_gemv_few_rows_full_and_long_k(orc, fmt, N, K, T):
-    """T = 2..4: the Q8 decode shape at full size (every output against the oracle), the longest K the
-    K-split kernel takes (16 wavefronts of 1024 values), and just past it (the chunked kernel)."""
+    """T = 2..8 rows of X: the Q8 decode shape at full size (every output against the oracle), the
+    longest K the K-split kernel takes (16 wavefronts of 1024 values for T <= 4, 8 above), and just
+    past it (the chunked kernel)."""
     w = synth.make_dense(fmt, N, K, T, "f32", 1.0, 960 + T + K)
     codes, scales, offs = weights_dev(w)
     Y = torch.full((T + 1, N), float("nan"), dtype=torch.float32, device="cuda")
