@@ -569,35 +569,40 @@ __device__ __forceinline__ float row16_sum_dpp(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
     return v;
 }
+// One pass of the scheme above: NT X rows xrow[t] (-1 = a zero row) against the weight-row batches
+// b, b + stride, ... < ceil(N / kSplitRows) of one matrix, into Y rows yrow0 + t.  part: LDS of
+// 2 * 16 * kSplitRows * NT * 4 floats, 16-byte aligned; par: the parity of the workgroup's next
+// batch (one barrier per batch).  Every wavefront of the workgroup calls it with the same arguments.
 template <int FMT, int XT, int NT>
-__global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmParams p) {
+__device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* codes, const void* scales,
+                                            const uint16_t* offs, const int (&xrow)[NT], int yrow0, int b, int stride,
+                                            float* part, int& par) {
     constexpr int RB = kSplitRows;
-    __shared__ float part[2][16][RB * NT][4];  // [batch parity][wavefront][row * NT + t][lane row]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = (int)blockDim.x >> 6;
     const int K = p.K, units = K >> 4, N = p.N;
     const int nb = (N + RB - 1) / RB;
-    int b = (int)blockIdx.x;
-    if (b >= nb) return;  // uniform over the workgroup
     const int u = 64 * wave + lane;
     const bool on = u < units;
     const int uc = min(u, units - 1);
 
-    // This lane's unit of every X row (zero for a lane past K, so its partials are zero).
+    // This lane's unit of every X row (zero for a lane past K or a zero row, so its partials are zero).
     float x[NT][16], sx[NT];
     {
         int e0, e1;
         unit_runs<FMT>(uc, e0, e1);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
+            const bool use = on && xrow[t] >= 0;
+            const size_t base = (size_t)max(xrow[t], 0) * K;
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                const size_t e = (size_t)t * K + (h ? e1 : e0);
+                const size_t e = base + (h ? e1 : e0);
                 if constexpr (XT == XT_F32) {
                     const float4 a = *(const float4*)((const float*)p.X + e);
                     const float4 c = *(const float4*)((const float*)p.X + e + 4);
                     const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
-                    for (int i = 0; i < 8; i++) x[t][8 * h + i] = on ? v[i] : 0.f;
+                    for (int i = 0; i < 8; i++) x[t][8 * h + i] = use ? v[i] : 0.f;
                 } else {
                     const uint4 q = *(const uint4*)((const uint16_t*)p.X + e);
                     const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmP
                     for (int i = 0; i < 8; i++) {
                         const uint16_t hv = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
                         const float v = (XT == XT_F16) ? f16_to_f32(hv) : bf16_to_f32(hv);
-                        x[t][8 * h + i] = on ? v : 0.f;
+                        x[t][8 * h + i] = use ? v : 0.f;
                     }
                 }
             }
@@ -618,20 +623,19 @@ __global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmP
     }
     float sc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; t++) sc[t] = p.rs ? p.rs[t] : 1.f;
+    for (int t = 0; t < NT; t++) sc[t] = p.rs ? p.rs[yrow0 + t] : 1.f;
     auto load_batch = [&](int bb, Unit<FMT> (&w)[RB]) {
 #pragma unroll
-        for (int r = 0; r < RB; r++)
-            w[r] = load_unit<FMT>(p.codes, p.scales, p.offs, p.group, K, min(bb * RB + r, N - 1), uc);
+        for (int r = 0; r < RB; r++) w[r] = load_unit<FMT>(codes, scales, offs, p.group, K, min(bb * RB + r, N - 1), uc);
     };
     Unit<FMT> wa[RB], wb[RB];
     load_batch(b, wa);
 
-    int par = 0;
     auto step = [&](const Unit<FMT> (&cu)[RB], Unit<FMT> (&nx)[RB]) __attribute__((always_inline)) {
-        const int b2 = b + (int)gridDim.x;
+        const int b2 = b + stride;
         const bool more = b2 < nb;
         if (more) load_batch(b2, nx);
+        float* pw = part + (size_t)(par * 16 + wave) * (RB * NT * 4);
 #pragma unroll
         for (int r = 0; r < RB; r++) {
             float c[16];
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmP
 #pragma unroll
                 for (int i = 0; i < 16; i++) pr = fmaf(c[i], x[t][i], pr);
                 const float v = row16_sum_dpp(unit_value<FMT>(cu[r], pr, sx[t]));
-                if ((lane & 15) == 15) part[par][wave][r * NT + t][lane >> 4] = v;
+                if ((lane & 15) == 15) pw[(r * NT + t) * 4 + (lane >> 4)] = v;
             }
         }
         __syncthreads();
@@ -651,10 +655,10 @@ __global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmP
             if (row < N) {
                 float s = 0.f;
                 for (int w = 0; w < W; w++) {
-                    const float4 q = *(const float4*)part[par][w][threadIdx.x];
+                    const float4 q = *(const float4*)(part + ((size_t)(par * 16 + w) * (RB * NT) + threadIdx.x) * 4);
                     s += (q.x + q.y) + (q.z + q.w);
                 }
-                p.Y[(size_t)t * N + row] = s * sc[t];
+                p.Y[(size_t)(yrow0 + t) * N + row] = s * sc[t];
             }
         }
         par ^= 1;
@@ -662,6 +666,56 @@ __global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmP
         return more;
     };
     while (step(wa, wb) && step(wb, wa)) {
+    }
+}
+
+template <int FMT, int XT, int NT>
+__global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) float part[2 * 16 * kSplitRows * NT * 4];
+    if ((int)blockIdx.x * kSplitRows >= p.N) return;  // uniform over the workgroup
+    int xrow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) xrow[t] = t;
+    int par = 0;
+    ksplit_pass<FMT, XT, NT>(p, p.codes, p.scales, p.offs, xrow, 0, (int)blockIdx.x, (int)gridDim.x, part, par);
+}
+
+// Grouped launches (exact-mode MoE): blockIdx.y is the expert; the workgroup walks the expert's row
+// segment in chunks of at most 4 X rows (gathered through row_src when given; ids outside X read as
+// zero rows), each chunk one pass over its share of the expert's weight-row batches.
+template <int FMT, int XT, int NTC>
+__device__ __forceinline__ void ksplit_grouped_chunk(const GemmParams& p, const void* codes, const void* scales,
+                                                     const uint16_t* offs, int c, float* part, int& par) {
+    int xrow[NTC];
+#pragma unroll
+    for (int t = 0; t < NTC; t++) {
+        int s = c + t;
+        if (p.row_src) {
+            s = p.row_src[c + t];
+            if (s < 0 || s >= p.x_rows) s = -1;
+        }
+        xrow[t] = s;
+    }
+    ksplit_pass<FMT, XT, NTC>(p, codes, scales, offs, xrow, c, (int)blockIdx.x, (int)gridDim.x, part, par);
+}
+
+template <int FMT, int XT>
+__global__ __launch_bounds__(512) void gemv_ksplit_grouped_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) float part[2 * 16 * kSplitRows * 4 * 4];
+    const int e = blockIdx.y;
+    const int r0 = min(max(p.seg_off[e], 0), p.R);
+    const int r1 = min(max(p.seg_off[e + 1], r0), p.R);
+    if (r1 <= r0 || (int)blockIdx.x * kSplitRows >= p.N) return;  // uniform over the workgroup
+    const void* codes = p.experts[e].codes;
+    const void* scales = p.experts[e].scales;
+    const uint16_t* offs = p.experts[e].offsets;
+    int par = 0;
+    for (int c = r0; c < r1; c += 4) {
+        const int nt = min(4, r1 - c);
+        if (nt == 1) ksplit_grouped_chunk<FMT, XT, 1>(p, codes, scales, offs, c, part, par);
+        else if (nt == 2) ksplit_grouped_chunk<FMT, XT, 2>(p, codes, scales, offs, c, part, par);
+        else if (nt == 3) ksplit_grouped_chunk<FMT, XT, 3>(p, codes, scales, offs, c, part, par);
+        else ksplit_grouped_chunk<FMT, XT, 4>(p, codes, scales, offs, c, part, par);
     }
 }
 
@@ -723,6 +777,20 @@ static void gemv_dense(const GemmParams& p, hipStream_t s) {
 template <int FMT, int XT>
 static void gemv_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) {
+        if (p.K <= kStreamKMax / 2) {
+            // K split over at most 8 wavefronts, X rows of each segment chunk in registers; about four
+            // resident rounds of workgroups if every expert has rows.  Exact MoE block (128 experts,
+            // top 8, 32 tokens): 377 us at one round, 314 at two, 271 at four, 273 at eight, 292 at
+            // sixteen; the chunked LDS kernel it replaces ran 345 us.  512-thread bounds (no spills,
+            // two or three wavefronts per SIMD) against 1024 (128 VGPRs, 24-49 spilled): 309.5 against
+            // 312.3 us at two rounds.
+            const int W = (p.K / 16 + 63) / 64;
+            const int nb = (p.N + kSplitRows - 1) / kSplitRows;
+            const int per_cu = std::max(1, 16 / W);
+            const int gx = std::max(1, std::min(nb, (4 * device_cus() * per_cu + p.E - 1) / p.E));
+            hipLaunchKernelGGL((gemv_ksplit_grouped_kernel<FMT, XT>), dim3(gx, p.E), dim3(64 * W), 0, s, p);
+            return;
+        }
         // Chunks of at most 4 segment rows and 2048 values of K, LDS sized for them; segments longer
         // than 4 rows (a few percent of the routed experts) read their weights once per chunk.  f32
         // X is staged straight into LDS (no staging registers), which brings the kernel to 168
