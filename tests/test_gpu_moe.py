@@ -287,12 +287,14 @@ def test_ffn_full_workload_device_plan(orc, mode):
 # ---- grouped exact GEMV: chunk walking, K chunks, gathered and zero rows --------------------------
 @pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
 @pytest.mark.parametrize("xt", ["f32", "f16"])
-def test_grouped_gemv_exact_chunks(orc, fmt, xt):
+@pytest.mark.parametrize("K", [3104, 8192, 8224])
+def test_grouped_gemv_exact_chunks(orc, fmt, xt, K):
     """Short segments (R <= 8 E, so the grouped GEMV runs): 12 experts with 0..9 rows each (segments
-    longer than 4 rows take several row chunks), N = 96 (a partial last workgroup of weight rows),
-    K = 3104 (a 2048-value K chunk, then a ragged one), X rows gathered through row_src with some ids
-    outside X (zero rows); f32 X is staged straight into LDS, f16 X through registers."""
-    E, N, K, x_rows, group = 12, 96, 3104, 20, 32
+    longer than 4 rows take several row chunks of 1..4 rows), N = 96 (a partial last batch of weight
+    rows), X rows gathered through row_src with some ids outside X (zero rows).  K = 3104 (a ragged
+    last wavefront of the K split) and 8192 (its longest K, 8 wavefronts) run the K-split kernel;
+    8224 the chunked LDS kernel (2048-value K chunks, f32 X staged straight into LDS)."""
+    E, N, x_rows, group = 12, 96, 20, 32
     sizes = [0, 1, 2, 3, 4, 5, 9, 0, 1, 6, 2, 3]
     seg = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     R = int(seg[-1])
