@@ -21,6 +21,11 @@
 //  * After K, each accumulator is reduced across the 64 lanes with xor shuffles.
 //  * Grouped launches (exact-mode MoE): blockIdx.y is the expert; the workgroup walks the expert's
 //    row segment in chunks of at most 4 rows.
+//
+// Three kernels use this unit layout: gemv1_stream_kernel (one X row, X in LDS, persistent
+// wavefronts streaming whole rows), gemv_ksplit_kernel / gemv_ksplit_grouped_kernel (2..8 X rows or
+// an expert's segment chunk: K split over the wavefronts, each lane's X unit in registers, DPP row
+// sums), and gemv_kernel (the chunked LDS kernel above, for K beyond the K-split limits).
 #include <algorithm>
 
 #include "qg_device.hpp"
