@@ -597,6 +597,8 @@ __device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* cod
         unit_runs<FMT>(uc, e0, e1);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
+            // a zero row loads X row 0 (the launchers guarantee X holds a row) and discards it: no
+            // branch around the loads
             const bool use = on && xrow[t] >= 0;
             const size_t base = (size_t)max(xrow[t], 0) * K;
 #pragma unroll
@@ -782,9 +784,10 @@ static void gemv_dense(const GemmParams& p, hipStream_t s) {
 template <int FMT, int XT>
 static void gemv_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (grouped) {
-        if (p.K <= kStreamKMax / 2) {
+        if (p.K <= kStreamKMax / 2 && p.x_rows >= 1) {
             // K split over at most 8 wavefronts, X rows of each segment chunk in registers; about four
-            // resident rounds of workgroups if every expert has rows.  Exact MoE block (128 experts,
+            // resident rounds of workgroups if every expert has rows.  Its zero rows read X row 0, so
+            // an X without rows goes to the chunked kernel, whose X loads are range-checked.  Exact MoE block (128 experts,
             // top 8, 32 tokens): 377 us at one round, 314 at two, 271 at four, 273 at eight, 292 at
             // sixteen; the chunked LDS kernel it replaces ran 345 us.  512-thread bounds (no spills,
             // two or three wavefronts per SIMD) against 1024 (128 VGPRs, 24-49 spilled): 309.5 against

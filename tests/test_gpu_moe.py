@@ -324,3 +324,24 @@ def test_grouped_gemv_exact_chunks(orc, fmt, xt, K):
         check_tol(y[r0:r1], Yr, Sr, TAU["exact"], f"expert {e} ({r1 - r0} rows)")
     for r in (3, 11, 17):
         assert np.all(y[r] == 0.0), f"zero row {r}"
+
+
+@pytest.mark.parametrize("xt", ["f32", "f16"])
+def test_grouped_gemv_exact_no_x_rows(xt):
+    """x_rows = 0 with every row_src id outside X: every output row is zero and X, a 16-byte buffer
+    here, is never read past its end."""
+    E, N, K, group = 3, 40, 3104, 32
+    seg = np.array([0, 2, 2, 5], np.int32)
+    R = int(seg[-1])
+    row_src = np.array([-1, 0, 3, -7, 1], np.int32)
+    ws = [synth.make_dense("q4", N, K, 1, "f32", 1.0, 4100 + e, group=group) for e in range(E)]
+    dw = [(dev(w["codes"]), dev(w["scales"]), None) for w in ws]
+    table = qg.expert_table(dw)
+    Xd = torch.zeros(4, dtype=torch.float32, device="cuda")
+    if xt == "f16":
+        Xd = Xd.view(torch.float16)
+    Y = torch.full((R, N), float("nan"), device="cuda")
+    print(f"grouped exact GEMV, no X rows, {xt}", flush=True)
+    qg.qgemm_moe_grouped("q4", table, group, dev(seg), dev(row_src), 0, Xd, None, Y, N, K, R, E, "exact")
+    torch.cuda.synchronize()
+    assert np.all(Y.cpu().numpy() == 0.0)
