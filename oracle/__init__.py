@@ -5,7 +5,8 @@ this package.  The product path (the HIP library and its binding) never calls it
 
 This is a ctypes wrapper over `qg_oracle.c` (plain C, built with gcc), which holds every piece
 of arithmetic: the format decoders, the f16 / bf16 conversions, the f64 GEMM, the row scaling,
-the routing plan and the combine.  The wrapper only marshals numpy arrays.  Each function's
+the routing plan, the combine, the MoE chain and its error-bound components.  The wrapper only
+marshals numpy arrays (and builds the per-expert pointer tables the chain takes).  Each function's
 definition and its sources are stated in `qg_oracle.c`.
 """
 from __future__ import annotations
@@ -72,6 +73,9 @@ def lib():
         L.orc_moe_plan.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
         L.orc_moe_combine.restype = None
         L.orc_moe_combine.argtypes = [_p, _i, _p, _p, _i, _i, _p, _p]
+        L.orc_moe_ffn.restype = _i
+        L.orc_moe_ffn.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _p,
+                                  _p, _p, _p, _p, _i]
         for name in ("orc_f16_values", "orc_bf16_values"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [_p, _sz, _p]
@@ -217,42 +221,47 @@ def moe_combine(O, H, slot_row, slot_w, T, k):
     return y, b
 
 
-def moe_ffn(m: dict, plan: dict, experts=None, threads=None) -> dict:
-    """The MoE chain in f64: per routed row r of expert e (token t = row_src[r]):
-    [g | u] = W_gu[e] x_t, a = SiLU(g) u, o_r = W_dn[e] a, y_t = sum_j w_j o_{slot_j}.
+def moe_ffn(m: dict, plan: dict, fmt: str = "q4", group: int = 64, threads=None) -> dict:
+    """The MoE expert block in f64, orc_moe_ffn of qg_oracle.c (definition and bound there).
 
-    Also returns the first-order error bound B[t][c] used by the end-to-end check:
-    B = sum_j |w_j| (sum_i |a_i w_dn[c][i]| + sum_i |w_dn[c][i]| (1.1 |u_i| Sg_i + |silu(g_i)| Su_i)),
-    where Sg, Su are the S sums of the gate and up rows (the propagated gate/up error is at
-    most tol * S, and |d silu / dg| <= 1.1)."""
+    m: E, H, I, T, X f32 [T*H], gu_codes / gu_scales [E][...] (fused [2I][H] per expert: gate rows
+    first), dn_codes / dn_scales [E][...] ([H][I]), and gu_offsets / dn_offsets for Q4A.  plan: the
+    oracle's routing plan.  Returns y [T][H], the bound components b_dn and b_gu [T][H], and the
+    stage values GU [R][2I], A [R][I], O [R][H]."""
     E, H, I, T = m["E"], m["H"], m["I"], m["T"]
-    X = np.asarray(m["X"], np.float32).reshape(T, H)
-    R = plan["R"]
-    seg = plan["seg_off"]
-    src = plan["row_src"]
-    O = np.zeros((R, H), np.float64)
-    Bo = np.zeros((R, H), np.float64)
-    Gs = np.zeros((R, 2 * I), np.float64)
-    for e in range(E):
-        r0, r1 = int(seg[e]), int(seg[e + 1])
-        if r1 == r0:
-            continue
-        xr = X[src[r0:r1]]
-        gu, sgu, _ = gemm("q4", m["gu_codes"][e], m["gu_scales"][e], None, 64, 2 * I, H, xr, "f32", r1 - r0,
-                          threads=threads)
-        Gs[r0:r1] = gu
-        g, u = gu[:, :I], gu[:, I:]
-        a = swiglu(g, u)
-        o, so, _ = gemm("q4", m["dn_codes"][e], m["dn_scales"][e], None, 64, H, I, a, "f64", r1 - r0,
-                        threads=threads)
-        sig = 1.0 / (1.0 + np.exp(-g))
-        da = 1.1 * np.abs(u) * sgu[:, :I] + np.abs(g * sig) * sgu[:, I:]
-        wabs = np.abs(dequant_exact("q4", m["dn_codes"][e], m["dn_scales"][e], None, 64, H, I))
-        O[r0:r1] = o
-        Bo[r0:r1] = so + da @ wabs.T
-    y, _ = moe_combine(O, H, plan["slot_row"], plan["slot_w"], T, len(plan["slot_w"]) // T)
-    B, _ = moe_combine(Bo, H, plan["slot_row"], np.abs(plan["slot_w"]), T, len(plan["slot_w"]) // T)
-    return {"y": y, "bound": B, "O": O, "GU": Gs}
+    k = len(plan["slot_w"]) // T
+    keep = []
+
+    def table(codes, scales, offs):
+        arr_c, arr_s, arr_o = (_p * E)(), (_p * E)(), (_p * E)()
+        for e in range(E):
+            c, s, o = _weights(fmt, codes[e], scales[e], None if offs is None else offs[e])
+            keep.extend([c, s, o])
+            arr_c[e], arr_s[e], arr_o[e] = _ptr(c), _ptr(s), _ptr(o)
+        return arr_c, arr_s, (arr_o if fmt == "q4a" else None)
+
+    gc, gs, go = table(m["gu_codes"], m["gu_scales"], m.get("gu_offsets"))
+    dc, ds, do = table(m["dn_codes"], m["dn_scales"], m.get("dn_offsets"))
+    X = _c(np.asarray(m["X"]).reshape(T, H), np.float32)
+    seg = _c(plan["seg_off"], np.int32)
+    src = _c(plan["row_src"], np.int32)
+    sr = _c(plan["slot_row"], np.int32)
+    sw = _c(plan["slot_w"], np.float64)
+    R = int(seg[E])
+    y = np.empty((T, H), np.float64)
+    bdn = np.empty((T, H), np.float64)
+    bgu = np.empty((T, H), np.float64)
+    GU = np.empty((R, 2 * I), np.float64)
+    A = np.empty((R, I), np.float64)
+    O = np.empty((R, H), np.float64)
+    if threads is None:
+        threads = default_threads()
+    got = lib().orc_moe_ffn(FMT[fmt], gc, gs, go, dc, ds, do, group, E, H, I, _ptr(X), T, k, _ptr(seg), _ptr(src),
+                            _ptr(sr), _ptr(sw), _ptr(y), _ptr(bdn), _ptr(bgu), _ptr(GU), _ptr(A), _ptr(O),
+                            int(threads))
+    if got != R:
+        raise ValueError("orc_moe_ffn: a gathered row names a token outside X")
+    return {"y": y, "b_dn": bdn, "b_gu": bgu, "GU": GU, "A": A, "O": O}
 
 
 # ---- GGUF blocks with in-block scales (Q4_0 = 2, Q8_0 = 8) ----------------------------------------

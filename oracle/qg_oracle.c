@@ -427,3 +427,86 @@ void orc_gguf_repack(int type, const uint8_t* src, int N, int K, uint8_t* codes,
             }
         }
 }
+
+/* ---------------------------------------------------------------------------------------
+ * The MoE expert block (page "oxinfer 0.0.5 src/metal.rs", Backend::upload_moe for the fused
+ * gate|up matrix [2I][H] -- gate rows 0..I-1, up rows I..2I-1 -- and the down matrix [H][I],
+ * Backend::moe for the chain, and the reference loop of its test mma_moe_matches_cpu):
+ * for every gathered row r of expert e (seg_off[e] <= r < seg_off[e+1]) and its token
+ * t = row_src[r]:
+ *     g = W_gate[e] x_t,  u = W_up[e] x_t                       (each an f64 GEMM row)
+ *     a_i = g_i / (1 + exp(-g_i)) * u_i                         (SiLU(gate) * up, f64)
+ *     o_r = W_down[e] a                                         (f64)
+ * and y[t] = sum_j slot_w[t*k+j] * o[slot_row[t*k+j]], j ascending.  Weights are the f32 values
+ * of the format (v32), as in orc_gemm.
+ *
+ * Error-bound components for a chain that evaluates these steps with per-step errors: for
+ * output (t, c),
+ *     b_dn = sum_j |w_j| sum_i |a_i wd[c][i]|                     (the down GEMM's own S)
+ *     b_gu = sum_j |w_j| sum_i |wd[c][i]| (1.1 |u_i| Sg_i + |silu(g_i)| Su_i)
+ * where Sg_i, Su_i are the S sums (sum_k |x_k w_k|) of gate / up row i.  A gate or up value off
+ * by at most tau*S moves a_i by at most 1.1 |u_i| tau Sg_i + |silu(g_i)| tau Su_i to first order
+ * (|d silu / dg| <= 1.1 for every g), and the down GEMM carries that through |wd|; a relative
+ * error rho in a itself and a down GEMM error of tau*S add (rho + tau) b_dn.
+ * Optional outputs: GU [R][2I], A [R][I], O [R][H].  X f32 [T][H].  Per-expert pointer arrays
+ * (offsets used by Q4A only).  Returns R = seg_off[E], or -1 if a row's token is out of range.
+ */
+static double silu_f64(double g) { return g / (1.0 + exp(-g)); }
+
+int orc_moe_ffn(int fmt, const void* const* gu_codes, const void* const* gu_scales, const uint16_t* const* gu_offs,
+                const void* const* dn_codes, const void* const* dn_scales, const uint16_t* const* dn_offs,
+                int group, int E, int H, int I, const float* X, int T, int k, const int* seg_off,
+                const int* row_src, const int* slot_row, const double* slot_w, double* y, double* b_dn,
+                double* b_gu, double* GU, double* A, double* O, int nthreads) {
+    const int R = seg_off[E];
+    for (int r = 0; r < R; r++)
+        if (row_src[r] < 0 || row_src[r] >= T) return -1;
+    double* o_all = (double*)calloc((size_t)R * H, sizeof(double));
+    double* so_all = (double*)calloc((size_t)R * H, sizeof(double));
+    double* sd_all = (double*)calloc((size_t)R * H, sizeof(double));
+    for (int e = 0; e < E; e++) {
+        const int r0 = seg_off[e], n = seg_off[e + 1] - r0;
+        if (n <= 0) continue;
+        float* xg = (float*)malloc(sizeof(float) * (size_t)n * H);
+        for (int i = 0; i < n; i++)
+            memcpy(xg + (size_t)i * H, X + (size_t)row_src[r0 + i] * H, sizeof(float) * (size_t)H);
+        double* gu = (double*)malloc(sizeof(double) * (size_t)n * 2 * I);
+        double* sgu = (double*)malloc(sizeof(double) * (size_t)n * 2 * I);
+        orc_gemm(fmt, gu_codes[e], gu_scales[e], gu_offs ? gu_offs[e] : NULL, group, 2 * I, H, xg, ORC_F32, n,
+                 NULL, 0, NULL, 0, gu, sgu, nthreads);
+        double* a = (double*)malloc(sizeof(double) * (size_t)n * I);
+        double* da = (double*)malloc(sizeof(double) * (size_t)n * I);
+        for (int i = 0; i < n; i++)
+            for (int c = 0; c < I; c++) {
+                const double g = gu[(size_t)i * 2 * I + c], u = gu[(size_t)i * 2 * I + I + c];
+                const double sg = sgu[(size_t)i * 2 * I + c], su = sgu[(size_t)i * 2 * I + I + c];
+                a[(size_t)i * I + c] = silu_f64(g) * u;
+                da[(size_t)i * I + c] = 1.1 * fabs(u) * sg + fabs(silu_f64(g)) * su;
+            }
+        /* o = W_down a, so = sum_i |a_i wd_i|; sd = sum_i |da_i wd_i| = sum_i da_i |wd_i| (da >= 0) */
+        orc_gemm(fmt, dn_codes[e], dn_scales[e], dn_offs ? dn_offs[e] : NULL, group, H, I, a, ORC_F64, n, NULL, 0,
+                 NULL, 0, o_all + (size_t)r0 * H, so_all + (size_t)r0 * H, nthreads);
+        double* junk = (double*)malloc(sizeof(double) * (size_t)n * H);
+        orc_gemm(fmt, dn_codes[e], dn_scales[e], dn_offs ? dn_offs[e] : NULL, group, H, I, da, ORC_F64, n, NULL, 0,
+                 NULL, 0, junk, sd_all + (size_t)r0 * H, nthreads);
+        if (GU) memcpy(GU + (size_t)r0 * 2 * I, gu, sizeof(double) * (size_t)n * 2 * I);
+        if (A) memcpy(A + (size_t)r0 * I, a, sizeof(double) * (size_t)n * I);
+        free(junk);
+        free(da);
+        free(a);
+        free(sgu);
+        free(gu);
+        free(xg);
+    }
+    if (O) memcpy(O, o_all, sizeof(double) * (size_t)R * H);
+    double* aw = (double*)malloc(sizeof(double) * (size_t)T * k);
+    for (int i = 0; i < T * k; i++) aw[i] = fabs(slot_w[i]);
+    orc_moe_combine(o_all, H, slot_row, slot_w, T, k, y, NULL);
+    if (b_dn) orc_moe_combine(so_all, H, slot_row, aw, T, k, b_dn, NULL);
+    if (b_gu) orc_moe_combine(sd_all, H, slot_row, aw, T, k, b_gu, NULL);
+    free(aw);
+    free(sd_all);
+    free(so_all);
+    free(o_all);
+    return R;
+}

@@ -9,6 +9,22 @@ import torch
 
 TAU = {"exact": 1e-5, "fast": 2e-3}
 
+# Relative error of the SwiGLU output a as the chain stores it: the f32 evaluation of
+# g / (1 + exp(-g)) * u (a few units in the last place, bounded by 2^-21), plus in fast mode the
+# nearest-even f16 rounding of the row-scaled a (2^-11).
+RHO_A = {"exact": 2.0 ** -21, "fast": 2.0 ** -11 + 2.0 ** -21}
+# The combine sums at most k products in f32 (the combine test's own rule, 1e-6 of sum |w o|), and
+# sum_j |w_j o_j| <= b_dn.
+RHO_COMBINE = 1e-6
+
+
+def chain_bound(ref: dict, mode: str) -> np.ndarray:
+    """Per-element bound of the MoE chain against the oracle's chain (oracle.moe_ffn): each GEMM
+    within tau * S of its own inputs, a stored with relative error RHO_A, the combine within
+    RHO_COMBINE: |y - y_ref| <= (tau + RHO_A + RHO_COMBINE) * b_dn + tau * b_gu, to first order."""
+    tau = TAU[mode]
+    return (tau + RHO_A[mode] + RHO_COMBINE) * ref["b_dn"] + tau * ref["b_gu"]
+
 
 def dev(a: np.ndarray) -> torch.Tensor:
     """numpy -> device tensor with the same bytes (uint16 bit patterns travel as int16)."""

@@ -443,3 +443,140 @@ def test_gguf_repack_matches_direct_decode(orc, gtype):
     fmt = "q4" if gtype == "q4_0" else "q8"
     split = orc.dequant_tile(fmt, codes, scales, None, 64, N, K, 0, 0, N, K, "f32")
     assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
+
+
+# ---- the MoE chain (oxinfer src/metal.rs, Backend::moe and the reference loop of its test
+# mma_moe_matches_cpu: gate = the first I rows of the fused matrix, up = the next I) -------------
+def _pack_nibbles(nib):
+    """Nibble matrix [N][K] -> Q4 code bytes (byte j of block b: element 32b+j low, 32b+16+j high),
+    written out here by hand so the pins do not depend on any packing helper."""
+    N, K = nib.shape
+    out = np.zeros((N, K // 2), np.uint8)
+    for n in range(N):
+        for b in range(K // 32):
+            for j in range(16):
+                out[n, 16 * b + j] = nib[n, 32 * b + j] | (nib[n, 32 * b + 16 + j] << 4)
+    return out.reshape(-1)
+
+
+def _diag_q4(rows, cols, pairs):
+    """Q4 matrix with weight 0 (nibble 8) except w[r][c] = v for (r, c, v) in pairs; scale 1."""
+    nib = np.full((rows, cols), 8, np.uint8)
+    for r, c, v in pairs:
+        nib[r, c] = 8 + v
+    return _pack_nibbles(nib), np.full(rows * cols // 32, 0x3C00, np.uint16)
+
+
+def _silu(x):
+    return x / (1.0 + math.exp(-x))
+
+
+def _moe_identity(E, H, down_gain, fmt="q4"):
+    """E experts with I = H: gate = identity, up = 2 * identity, down = down_gain[e] * identity."""
+    I = H
+    gu_c, gu_s, dn_c, dn_s = [], [], [], []
+    for e in range(E):
+        if fmt == "q4":
+            c, s = _diag_q4(2 * I, H, [(i, i, 1) for i in range(I)] + [(I + i, i, 2) for i in range(I)])
+            gu_c.append(c), gu_s.append(s)
+            c, s = _diag_q4(H, I, [(i, i, down_gain[e]) for i in range(H)])
+            dn_c.append(c), dn_s.append(s)
+        else:   # Q8: int8 codes, f32 scale 1
+            g = np.zeros((2 * I, H), np.int8)
+            g[np.arange(I), np.arange(I)] = 1
+            g[I + np.arange(I), np.arange(I)] = 2
+            d = np.zeros((H, I), np.int8)
+            d[np.arange(H), np.arange(H)] = down_gain[e]
+            gu_c.append(g.reshape(-1)), gu_s.append(np.ones(2 * I * H // 32, np.float32))
+            dn_c.append(d.reshape(-1)), dn_s.append(np.ones(H * I // 32, np.float32))
+    return np.array(gu_c), np.array(gu_s), np.array(dn_c), np.array(dn_s)
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+def test_moe_chain_closed_form(orc, fmt):
+    """Identity gate, doubled identity up, and down = 1x (expert 0) or 3x (expert 1) identity:
+    every routed row gives o = a = SiLU(x) * 2x (times the gain), so with router logits (0, ln 3)
+    the weights are 1/4 and 3/4 and y = (3/4 * 3 + 1/4 * 1) * SiLU(x) * 2x = 2.5 * 2x SiLU(x).
+    Swapping gate and up would give SiLU(2x) * x instead, which differs clearly for 0 < |x| <= 4."""
+    E, H, T, k = 2, 32, 3, 2
+    gu_c, gu_s, dn_c, dn_s = _moe_identity(E, H, [1, 3], fmt)
+    X = np.array([[0.5 * (c + 1) * (-1) ** c for c in range(H)],
+                  [-3.0 + 0.25 * c for c in range(H)],
+                  [0.0] * (H - 1) + [7.0]], np.float32)
+    lg = np.tile(np.array([0.0, math.log(3.0)], np.float32), (T, 1))
+    plan = orc.moe_plan(lg, T, E, k)
+    m = {"E": E, "H": H, "I": H, "T": T, "X": X, "gu_codes": gu_c, "gu_scales": gu_s, "dn_codes": dn_c,
+         "dn_scales": dn_s}
+    r = orc.moe_ffn(m, plan, fmt=fmt)
+    w1 = 1.0 / (1.0 + math.exp(float(np.float32(0.0)) - float(np.float32(math.log(3.0)))))
+    for t in range(T):
+        for c in range(H):
+            x = float(X[t, c])
+            a = _silu(x) * 2.0 * x
+            want = w1 * 3.0 * a + (1.0 - w1) * a
+            assert abs(r["y"][t, c] - want) <= 1e-14 * max(1.0, abs(want)), (t, c)
+            swapped = w1 * 3.0 * _silu(2.0 * x) * x + (1.0 - w1) * _silu(2.0 * x) * x
+            if x != 0.0 and abs(x) <= 4.0:     # (for large |x| both forms tend to 2 x^2)
+                assert abs(r["y"][t, c] - swapped) > 1e-3 * abs(want)
+    # the stage values: gate | up = (x, 2x), a, and o of expert 1 (row order: experts ascending)
+    src = plan["row_src"]
+    assert np.allclose(r["GU"][:, :H], X[src].astype(np.float64), rtol=0, atol=0)
+    assert np.allclose(r["GU"][:, H:], 2.0 * X[src].astype(np.float64), rtol=0, atol=0)
+    seg = plan["seg_off"]
+    assert np.allclose(r["O"][seg[1]:seg[2]], 3.0 * r["A"][seg[1]:seg[2]], rtol=1e-15, atol=0)
+
+
+def test_moe_chain_bound_one_hot(orc):
+    """The bound components for one token, one expert, identity gate and down, doubled identity up
+    and x = v e_0: g = v e_0, u = 2 v e_0, a_0 = SiLU(v) 2v; b_dn[0] = |a_0|;
+    b_gu[0] = 1.1 |u_0| Sg_0 + |SiLU(g_0)| Su_0 = 1.1 |2v| |v| + |SiLU(v)| |2v| (Sg_0 = |v|,
+    Su_0 = |2v|); every other column has zero bounds and zero output."""
+    E, H, T, k = 1, 32, 1, 1
+    I = H
+    gu_c, gu_s = _diag_q4(2 * I, H, [(i, i, 1) for i in range(I)] + [(I + i, i, 2) for i in range(I)])
+    dn_c, dn_s = _diag_q4(H, I, [(i, i, 1) for i in range(H)])
+    for v in (1.5, -2.25, 0.0):
+        X = np.zeros((T, H), np.float32)
+        X[0, 0] = v
+        plan = orc.moe_plan(np.zeros((T, E), np.float32), T, E, k)
+        m = {"E": E, "H": H, "I": I, "T": T, "X": X, "gu_codes": gu_c[None], "gu_scales": gu_s[None],
+             "dn_codes": dn_c[None], "dn_scales": dn_s[None]}
+        r = orc.moe_ffn(m, plan)
+        a0 = _silu(v) * 2.0 * v
+        assert r["y"][0, 0] == pytest.approx(a0, rel=1e-15, abs=0)
+        assert r["b_dn"][0, 0] == pytest.approx(abs(a0), rel=1e-15, abs=0)
+        assert r["b_gu"][0, 0] == pytest.approx(1.1 * abs(2.0 * v) * abs(v) + abs(_silu(v)) * abs(2.0 * v),
+                                                rel=1e-15, abs=0)
+        assert np.all(r["y"][0, 1:] == 0) and np.all(r["b_dn"][0, 1:] == 0) and np.all(r["b_gu"][0, 1:] == 0)
+
+
+def test_moe_chain_brute_force(orc):
+    """A small random chain (3 experts, H 64, I 32, 5 tokens, top 2, Q4) against plain Python loops
+    over weights decoded here from the raw bytes: gate rows first, then up rows, SiLU(g) u, down,
+    and the weighted sum in slot order."""
+    import synth
+    E, H, I, T, k = 3, 64, 32, 5, 2
+    m = synth.make_moe(E, H, I, T, 91)
+    lg = m["logits"].reshape(T, E)
+    plan = orc.moe_plan(lg, T, E, k)
+    r = orc.moe_ffn(m, plan)
+    X = m["X"].reshape(T, H).astype(np.float64)
+
+    def w_of(codes, scales, K, n, kk):
+        b, j = divmod(kk, 32)
+        byte = int(codes[n * (K // 2) + 16 * b + (j % 16)])
+        nib = byte & 15 if j < 16 else byte >> 4
+        return float(np.float32(nib - 8) * np.float32(np.uint16(scales[n * (K // 32) + b]).view(np.float16)))
+
+    for t in range(T):
+        for j in range(k):
+            e = int(plan["slot_expert"][t * k + j])
+            gu = [sum(X[t, h] * w_of(m["gu_codes"][e], m["gu_scales"][e], H, n, h) for h in range(H))
+                  for n in range(2 * I)]
+            a = [_silu(gu[i]) * gu[I + i] for i in range(I)]
+            o = [sum(a[i] * w_of(m["dn_codes"][e], m["dn_scales"][e], I, c, i) for i in range(I)) for c in range(H)]
+            row = plan["slot_row"][t * k + j]
+            assert np.allclose(r["O"][row], o, rtol=1e-12, atol=1e-12)
+    for t in range(T):
+        want = sum(plan["slot_w"][t * k + j] * r["O"][plan["slot_row"][t * k + j]] for j in range(k))
+        assert np.allclose(r["y"][t], want, rtol=1e-15, atol=0)
