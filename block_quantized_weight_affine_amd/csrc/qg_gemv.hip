@@ -576,12 +576,16 @@ __device__ __forceinline__ float row16_sum_dpp(float v) {
 }
 // One pass of the scheme above: NT X rows xrow[t] (-1 = a zero row) against the weight-row batches
 // b, b + stride, ... < ceil(N / kSplitRows) of one matrix, into Y rows yrow0 + t.  part: LDS of
-// 2 * 16 * kSplitRows * NT * 4 floats, 16-byte aligned; par: the parity of the workgroup's next
-// batch (one barrier per batch).  Every wavefront of the workgroup calls it with the same arguments.
-template <int FMT, int XT, int NT>
+// 2 * 16 * kSplitRows * NTS * 4 floats, 16-byte aligned, with a per-wavefront slot of
+// kSplitRows * NTS * 4 floats whatever NT is (NT <= NTS): passes of different NT that follow each
+// other (the grouped kernel's chunks) then keep the two parities' slots disjoint, so the
+// double buffer needs one barrier per batch only.  par: the parity of the workgroup's next batch.
+// Every wavefront of the workgroup calls it with the same arguments.
+template <int FMT, int XT, int NT, int NTS = NT>
 __device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* codes, const void* scales,
                                             const uint16_t* offs, const int (&xrow)[NT], int yrow0, int b, int stride,
                                             float* part, int& par) {
+    static_assert(NT <= NTS, "a pass's partials fit the per-wavefront slot");
     constexpr int RB = kSplitRows;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = (int)blockDim.x >> 6;
     const int K = p.K, units = K >> 4, N = p.N;
@@ -642,7 +646,7 @@ __device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* cod
         const int b2 = b + stride;
         const bool more = b2 < nb;
         if (more) load_batch(b2, nx);
-        float* pw = part + (size_t)(par * 16 + wave) * (RB * NT * 4);
+        float* pw = part + (size_t)(par * 16 + wave) * (RB * NTS * 4);
 #pragma unroll
         for (int r = 0; r < RB; r++) {
             float c[16];
@@ -662,7 +666,7 @@ __device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* cod
             if (row < N) {
                 float s = 0.f;
                 for (int w = 0; w < W; w++) {
-                    const float4 q = *(const float4*)(part + ((size_t)(par * 16 + w) * (RB * NT) + threadIdx.x) * 4);
+                    const float4 q = *(const float4*)(part + ((size_t)(par * 16 + w) * (RB * NTS) + threadIdx.x) * 4);
                     s += (q.x + q.y) + (q.z + q.w);
                 }
                 p.Y[(size_t)(yrow0 + t) * N + row] = s * sc[t];
@@ -703,7 +707,7 @@ __device__ __forceinline__ void ksplit_grouped_chunk(const GemmParams& p, const 
         }
         xrow[t] = s;
     }
-    ksplit_pass<FMT, XT, NTC>(p, codes, scales, offs, xrow, c, (int)blockIdx.x, (int)gridDim.x, part, par);
+    ksplit_pass<FMT, XT, NTC, 4>(p, codes, scales, offs, xrow, c, (int)blockIdx.x, (int)gridDim.x, part, par);
 }
 
 template <int FMT, int XT>
