@@ -32,8 +32,9 @@
  *
  * Shape and alignment rules shared by the matmul entry points (violations return the code named):
  *   N >= 1, T >= 0, K >= 32, K % 32 == 0                                 else QG_ESHAPE
- *   codes, X and Y 16-byte aligned; scales / offsets aligned to their element size; expert tables,
- *   index arrays and row scales 4-byte aligned                           else QG_EALIGN
+ *   codes and X 16-byte aligned; Y 4-byte aligned (f32 elements); scales / offsets aligned to their
+ *   element size; index arrays and row scales 4-byte aligned; expert tables 8-byte aligned
+ *                                                                        else QG_EALIGN
  *   null pointers (with T > 0), or an enum value out of range            QG_EINVAL
  *   T == 0 returns QG_OK without launching anything.
  * Rows of Y at or beyond T, and columns at or beyond N, are never written.
@@ -106,7 +107,8 @@ qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, 
 
 /* ---------------------------------------------------------------------------------------------
  * Debug dump of a staged weight tile: out[r][c] = the value the GEMM kernels stage for element
- * (n0 + r, k0 + c), produced by the same device decoder and tile writer the GEMMs use.
+ * (n0 + r, k0 + c), produced on the device by the block load and decode functions the GEMM kernels
+ * call (the f32 decode of exact mode; the nearest-even 16-bit rounding of that value in fast mode).
  * staged = QG_X_F32: f32 values (exact mode); QG_X_F16 / QG_X_BF16: 16-bit patterns (fast mode).
  * Needs k0 % 32 == 0, cols % 32 == 0, 0 <= n0, n0 + rows <= N, k0 + cols <= K, rows >= 1;
  * out is [rows][cols] of 4 or 2 bytes, 16-byte aligned.  fmt QG_FMT_Q4 / Q4A take uint16 f16

@@ -1,6 +1,6 @@
 """GGUF Q4_0 / Q8_0 blocks (scale inside each block) on the GPU: the device repack into the split
-layout against the oracle's repack (bit-exact), and matmuls through the repacked weights against an
-f64 product of the oracle's direct decode of the GGUF bytes."""
+layout against the oracle's repack (bit-exact), and matmuls through the repacked weights against the
+oracle's f64 GEMM over its own repack of the same bytes."""
 import numpy as np
 import pytest
 import torch
@@ -68,13 +68,10 @@ def test_matmul_through_repacked_weights(orc, gtype, case):
     else:
         qg.qgemm_q8(codes.view(torch.int8), scales, Xd, Y, N, K, T, mode)
     torch.cuda.synchronize()
-    W = orc.gguf_dequant(gtype, src, N, K).astype(np.float64)
-    if xt == "f32":
-        x = X.astype(np.float64)
-    elif xt == "f16":
-        x = orc.f16_values((X.view(np.uint16) if X.dtype == np.float16 else X).reshape(-1)).reshape(T, K)
-    else:
-        x = orc.bf16_values(X.reshape(-1)).reshape(T, K)
-    Yr = x @ W.T
-    S = np.abs(x) @ np.abs(W).T
+    # the oracle's GEMM over the oracle's repack of the same GGUF bytes (the repack is pinned on the
+    # CPU to decode bit-identically to the oracle's direct GGUF decoder)
+    rc, rsc = orc.gguf_repack(gtype, src, N, K)
+    fmt = "q4" if gtype == "q4_0" else "q8"
+    Xo = X.view(np.uint16) if xt in ("f16", "bf16") else X
+    Yr, S, _ = orc.gemm(fmt, rc, rsc, None, 64, N, K, Xo, xt, T)
     check_tol(Y.cpu().numpy(), Yr, S, TAU[mode], f"{gtype} {mode} T={T}")

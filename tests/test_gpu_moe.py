@@ -328,8 +328,8 @@ def test_grouped_gemv_exact_chunks(orc, fmt, xt, K):
 
 @pytest.mark.parametrize("xt", ["f32", "f16"])
 def test_grouped_gemv_exact_no_x_rows(xt):
-    """x_rows = 0 with every row_src id outside X: every output row is zero and X, a 16-byte buffer
-    here, is never read past its end."""
+    """x_rows = 0 with every row_src id outside X: such a call goes to the range-checked chunked
+    kernel (the K-split kernel would load X row 0 for a zero row), and every output row is zero."""
     E, N, K, group = 3, 40, 3104, 32
     seg = np.array([0, 2, 2, 5], np.int32)
     R = int(seg[-1])
@@ -345,3 +345,150 @@ def test_grouped_gemv_exact_no_x_rows(xt):
     qg.qgemm_moe_grouped("q4", table, group, dev(seg), dev(row_src), 0, Xd, None, Y, N, K, R, E, "exact")
     torch.cuda.synchronize()
     assert np.all(Y.cpu().numpy() == 0.0)
+
+
+# ---- every stage of the 128-expert block on its own, per element at tau -------------------------
+# Each stage is fed seeded inputs of the shapes and layouts the chain hands it (nothing computed by
+# the GPU feeds the oracle): gate|up from the seeded X through the seeded plan, down from a seeded
+# activation A, the combine from seeded expert outputs O.  The launches are the ones qg_moe_ffn
+# makes for the mode.
+def _c4_setup(orc):
+    c = synth.CONFIGS[4]
+    E, H, I, T, k = c.extra["experts"], c.N, c.extra["inter"], c.T, c.extra["top_k"]
+    m = synth.make_moe(E, H, I, T, c.seed)
+    plan = orc.moe_plan(m["logits"].reshape(T, E), T, E, k)
+    return c, m, plan, (E, H, I, T, k)
+
+
+def _per_expert(orc, y, plan, codes, scales, N, K, Xo, xt, tau, what):
+    seg = plan["seg_off"]
+    used = 0
+    for e in range(len(seg) - 1):
+        r0, r1 = int(seg[e]), int(seg[e + 1])
+        if r0 == r1:
+            continue
+        used += 1
+        Yr, Sr, _ = orc.gemm("q4", codes[e], scales[e], None, 64, N, K, Xo[r0:r1], xt, r1 - r0)
+        check_tol(y[r0:r1], Yr, Sr, tau, f"{what}: expert {e} ({r1 - r0} rows)")
+    return used
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_moe_workload_gate_up_stage(orc, mode):
+    """Grouped gate|up (128 experts, [3072 x 2048] each, 32 tokens, top 8): exact from the f32 rows
+    gathered through row_src; fast from qg_x_half's row-scaled f16 rows with the inverse scale in the
+    epilogue.  Every expert's segment against the oracle at tau * S (X as the f32 rows)."""
+    c, m, plan, (E, H, I, T, k) = _c4_setup(orc)
+    R = plan["R"]
+    _, _, table = _experts(m, "gu")
+    pd = _plan_dev({"seg_off": plan["seg_off"], "row_src": plan["row_src"]})
+    X = m["X"].reshape(T, H)
+    Y = torch.full((R, 2 * I), float("nan"), device="cuda")
+    print(f"moe workload gate|up stage {mode}", flush=True)
+    if mode == "exact":
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], pd["row_src"], T, dev(X), None, Y, 2 * I, H, R, E,
+                             "exact")
+    else:
+        Xh = torch.empty((R, H), dtype=torch.int16, device="cuda")
+        rs = torch.empty(R, dtype=torch.float32, device="cuda")
+        qg.qg_x_half(dev(X), T, pd["row_src"], R, H, Xh, rs)
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], None, R, Xh.view(torch.float16), rs, Y, 2 * I, H, R, E,
+                             "fast")
+    torch.cuda.synchronize()
+    used = _per_expert(orc, Y.cpu().numpy(), plan, m["gu_codes"], m["gu_scales"], 2 * I, H,
+                       np.ascontiguousarray(X[plan["row_src"]]), "f32", TAU[mode], f"gate|up {mode}")
+    assert used > 100
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_moe_workload_down_stage(orc, mode):
+    """Grouped down projection (128 experts, [2048 x 1536] each) over the seeded plan's 256 rows, no
+    gather (row r reads A row r), as the chain runs it: exact from f32 A, fast from f16 A with a
+    power-of-two inverse row scale rs (what qg_swiglu hands over).  The oracle takes A as the values
+    the kernel is given: the f32 rows, or the f16 values times rs (exact in f64)."""
+    c, m, plan, (E, H, I, T, k) = _c4_setup(orc)
+    R = plan["R"]
+    _, _, table = _experts(m, "dn")
+    pd = _plan_dev({"seg_off": plan["seg_off"]})
+    O = torch.full((R, H), float("nan"), device="cuda")
+    print(f"moe workload down stage {mode}", flush=True)
+    if mode == "exact":
+        A = synth.normal_as(c.seed, 20, R * I, 0.0, 1.0, "f32").reshape(R, I)
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], None, R, dev(A), None, O, H, I, R, E, "exact")
+        Ao, xt = A, "f32"
+    else:
+        A16 = synth.normal_as(c.seed, 20, R * I, 0.0, 4096.0, "f16").reshape(R, I)
+        rs = np.exp2(np.arange(R) % 9 - 16.0).astype(np.float32)     # 2^-16 .. 2^-8
+        qg.qgemm_moe_grouped("q4", table, 64, pd["seg_off"], None, R, dev(A16), dev(rs), O, H, I, R, E, "fast")
+        Ao = orc.f16_values(A16.view(np.uint16)) * rs.astype(np.float64)[:, None]
+        xt = "f64"
+    torch.cuda.synchronize()
+    used = _per_expert(orc, O.cpu().numpy(), plan, m["dn_codes"], m["dn_scales"], H, I, np.ascontiguousarray(Ao), xt,
+                       TAU[mode], f"down {mode}")
+    assert used > 100
+
+
+def test_moe_workload_combine_stage(orc):
+    """The weighted combine at the block's shape (32 tokens x top 8 over 256 routed rows of 2048):
+    seeded O through the seeded plan's slots, within 1e-6 of sum_j |w_j o_j| (an f32 sum of 8
+    products)."""
+    c, m, plan, (E, H, I, T, k) = _c4_setup(orc)
+    R = plan["R"]
+    O = synth.normal_as(c.seed, 21, R * H, 0.0, 1.0, "f32").reshape(R, H)
+    sw = plan["slot_w"].astype(np.float32)
+    Y = torch.full((T, H), float("nan"), device="cuda")
+    qg.qg_moe_combine(dev(O), R, dev(plan["slot_row"].astype(np.int32)), dev(sw), Y, H, T, k, 0)
+    torch.cuda.synchronize()
+    yr, b = orc.moe_combine(O.astype(np.float64), H, plan["slot_row"], sw.astype(np.float64), T, k)
+    check_tol(Y.cpu().numpy(), yr, b, 1e-6, "combine, block shape")
+
+
+@pytest.mark.parametrize("fmt", ["q4a", "q8"])
+@pytest.mark.parametrize("path", ["x_half", "gather_f16", "gather_bf16"])
+def test_grouped_fast_formats(orc, fmt, path):
+    """Fast grouped matmul with affine Q4 and Q8 experts: 9 experts with 0..40 rows (an empty expert,
+    segments over several 32-row tiles), N = 200 (a ragged weight-row tile), K = 320.  x_half: f32
+    rows gathered and row-scaled to f16 by qg_x_half (the chain's path); gather_*: 16-bit rows
+    gathered through row_src (ids outside X read as zero rows)."""
+    E, N, K, x_rows, group = 9, 200, 320, 30, 64
+    sizes = [3, 0, 40, 1, 7, 33, 2, 12, 5]
+    seg = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(seg[-1])
+    rng = np.random.default_rng(41)
+    row_src = rng.integers(0, x_rows, R).astype(np.int32)
+    ws = [synth.make_dense(fmt, N, K, 1, "f32", 1.0, 4200 + e, group=group) for e in range(E)]
+    dw = [(dev(w["codes"]), dev(w["scales"]), dev(w["offsets"]) if "offsets" in w else None) for w in ws]
+    table = qg.expert_table(dw)
+    Y = torch.full((R, N), float("nan"), device="cuda")
+    print(f"grouped fast {fmt} {path} R={R}", flush=True)
+    if path == "x_half":
+        X = synth.normal_as(43, synth.STREAM_X, x_rows * K, 0.0, 1.0, "f32").reshape(x_rows, K)
+        X[4] *= 1e-4
+        Xh = torch.empty((R, K), dtype=torch.int16, device="cuda")
+        rs = torch.empty(R, dtype=torch.float32, device="cuda")
+        qg.qg_x_half(dev(X), x_rows, dev(row_src), R, K, Xh, rs)
+        qg.qgemm_moe_grouped(fmt, table, group, dev(seg), None, R, Xh.view(torch.float16), rs, Y, N, K, R, E, "fast")
+        Xo, xt = np.ascontiguousarray(X[row_src]), "f32"
+        zero_rows = []
+    else:
+        xt = "f16" if path == "gather_f16" else "bf16"
+        row_src[[5, 20]] = [-3, x_rows]                       # zero rows
+        X = synth.normal_as(44, synth.STREAM_X, x_rows * K, 0.0, 1.0, xt).reshape(x_rows, K)
+        Xd = dev(X)
+        Xd = Xd.view(torch.float16) if xt == "f16" else Xd.view(torch.bfloat16)
+        qg.qgemm_moe_grouped(fmt, table, group, dev(seg), dev(row_src), x_rows, Xd, None, Y, N, K, R, E, "fast")
+        Xb = X.view(np.uint16)
+        Xz = np.concatenate([Xb, np.zeros((1, K), np.uint16)])
+        Xo = np.ascontiguousarray(Xz[np.where((row_src >= 0) & (row_src < x_rows), row_src, x_rows)])
+        zero_rows = [5, 20]
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    for e in range(E):
+        r0, r1 = seg[e], seg[e + 1]
+        if r0 == r1:
+            continue
+        w = ws[e]
+        Yr, Sr, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), group, N, K, Xo[r0:r1], xt, r1 - r0)
+        check_tol(y[r0:r1], Yr, Sr, TAU["fast"], f"expert {e} ({r1 - r0} rows)")
+    for r in zero_rows:
+        assert np.all(y[r] == 0.0), f"zero row {r}"
