@@ -316,29 +316,71 @@ def measure(name: str, steps: int, warmup: int) -> dict:
 
 
 # ---------------------------------------------------------------------------------------------------
-def cpu_baseline(info: dict, budget_s: float = 12.0) -> dict:
-    """The CPU oracle (plain C, f64) as it stands, on this host's cores, over a bounded sample."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_run(c, w, threads):
     import oracle
+    _, _, used = oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
+                             w["X"].view(np.uint16) if c.xtype != "f32" else w["X"], c.xtype, c.T, threads=threads)
+    return used
+
+
+def _oracle_median(c, w, threads, budget_s):
+    """Median over 3 timed batches of repeats of the whole workload, each batch about budget_s / 3 s."""
+    t0 = time.perf_counter()
+    used = _oracle_run(c, w, threads)
+    one = time.perf_counter() - t0
+    reps = max(1, min(5000, int(budget_s / 3 / max(one, 1e-4))))
+    per = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            _oracle_run(c, w, threads)
+        per.append((time.perf_counter() - t0) / reps)
+    return float(np.median(per)), reps, int(used)
+
+
+def cpu_baseline(info: dict, budget_s: float = 12.0) -> dict:
+    """The CPU oracle (plain C, f64) as it stands, timed on this host: threaded over output rows with
+    the process's CPU share (oracle.default_threads), the median of 3 timed batches; for the tiny Q4
+    and the Q8 decode workloads also single-threaded.  Reports the host's core count and CPU model
+    beside the thread count used."""
+    import oracle
+    import synth
     c = info["cfg"]
     w = info["weights"]
-    threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
-                w["X"].view(np.uint16) if c.xtype != "f32" else w["X"], c.xtype, c.T, threads=threads)
-    one = time.perf_counter() - t0
-    reps = max(1, min(5000, int(budget_s / max(one, 1e-3))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        _, _, used = oracle.gemm(c.fmt, w["codes"], w["scales"], w.get("offsets"), c.group, c.N, c.K,
-                                 w["X"].view(np.uint16) if c.xtype != "f32" else w["X"], c.xtype, c.T,
-                                 threads=threads)
-    dt = (time.perf_counter() - t0) / reps
-    if c.index == 1:
-        value, unit = info["bytes"] / dt / 1e9, "GB/s"
-    else:
-        value, unit = info["flops"] / dt / 1e12, "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": int(used), "kind": "oracle",
-            "sample": f"the whole workload ({c.N} rows x K {c.K}, T {c.T}), {reps} repeats, {dt * 1e3:.1f} ms each"}
+    dt, reps, used = _oracle_median(c, w, oracle.default_threads(), budget_s)
+
+    def rate(cfg, seconds, nbytes, flops):
+        if cfg.index == 1:
+            return nbytes / seconds / 1e9, "GB/s"
+        return flops / seconds / 1e12, "TFLOP/s"
+
+    value, unit = rate(c, dt, info["bytes"], info["flops"])
+    single = []
+    for ci in (0, 1):
+        cc = synth.CONFIGS[ci]
+        ww = w if ci == c.index else synth.make_dense(cc.fmt, cc.N, cc.K, cc.T, cc.xtype, cc.x_sigma, cc.seed,
+                                                      group=cc.group)
+        d1, r1, _ = _oracle_median(cc, ww, 1, 3.0)
+        nbytes = float(ww["codes"].nbytes + ww["scales"].nbytes + ww["X"].nbytes + cc.T * cc.N * 4)
+        v1, u1 = rate(cc, d1, nbytes, 2.0 * cc.T * cc.N * cc.K)
+        single.append({"workload": cc.name, "value": v1, "unit": u1, "ms": d1 * 1e3, "threads": 1,
+                       "gflops_f64": 2.0 * cc.T * cc.N * cc.K / d1 / 1e9, "repeats": 3 * r1})
+    return {"value": value, "unit": unit, "cores": used, "kind": "oracle",
+            "sample": f"the whole workload ({c.N} rows x K {c.K}, T {c.T}); median of 3 batches of {reps} "
+                      f"repeats, {dt * 1e3:.2f} ms each",
+            "threads": used, "host_cores": os.cpu_count(), "cpu_model": _cpu_model(),
+            "gflops_f64": info["flops"] / dt / 1e9, "single_thread": single}
 
 
 def traffic_for(name: str, info: dict, ms: float) -> float | None:
