@@ -19,7 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 
-QG_OK, QG_EINVAL, QG_EALIGN, QG_ESHAPE, QG_EUNSUPPORTED, QG_ELAUNCH, QG_EPLAN, QG_EWORKSPACE = range(8)
+QG_OK, QG_EINVAL, QG_EALIGN, QG_ESHAPE, QG_EUNSUPPORTED, QG_ELAUNCH, QG_EPLAN, QG_EWORKSPACE, QG_ESCRATCH = range(9)
+QG_NOALLOC_SCRATCH_BYTES = 16 << 20
 QG_X_F32, QG_X_F16, QG_X_BF16 = 0, 1, 2
 QG_EXACT, QG_FAST = 0, 1
 QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8 = 0, 1, 2
@@ -34,7 +35,7 @@ SYMBOLS = [
     "qgemv_q4", "qgemv_q4a", "qgemv_q8",
     "qg_dequant_dump", "qg_repack_gguf",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
-    "qg_moe_ffn_workspace", "qg_moe_ffn",
+    "qg_moe_ffn_workspace", "qg_moe_ffn", "qg_moe_ffn_noalloc",
 ]
 
 
@@ -80,6 +81,7 @@ def lib() -> C.CDLL:
         L.qg_moe_ffn_workspace.restype = _sz
         L.qg_moe_ffn_workspace.argtypes = [_i, _i, _i, _i, _i]
         L.qg_moe_ffn.argtypes = [_i, _p, _p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _i, _i, _p, _sz, _p]
+        L.qg_moe_ffn_noalloc.argtypes = [_i, _p, _p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _i, _i, _p]
         for name in SYMBOLS:
             if name not in ("qg_strerror", "qg_abi_version", "qg_moe_ffn_workspace"):
                 getattr(L, name).restype = _i
@@ -265,6 +267,14 @@ def qg_moe_ffn(fmt, gate_up, down, group, E, H, I, X, T, k, seg_off, row_src, sl
                             _ptr(X), T, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w), _ptr(Y),
                             int(accumulate), _mode(mode), _ptr(workspace), int(ws_bytes), _stream(stream)),
            "qg_moe_ffn")
+
+
+def qg_moe_ffn_noalloc(fmt, gate_up, down, group, E, H, I, X, T, k, seg_off, row_src, slot_row, slot_w, Y,
+                       accumulate, mode, stream=None):
+    _check(lib().qg_moe_ffn_noalloc(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(gate_up), _ptr(down), group, E, H,
+                                    I, _ptr(X), T, k, _ptr(seg_off), _ptr(row_src), _ptr(slot_row), _ptr(slot_w),
+                                    _ptr(Y), int(accumulate), _mode(mode), _stream(stream)),
+           "qg_moe_ffn_noalloc")
 
 
 # ---- host layout helpers (byte movement only) ----------------------------------------------------

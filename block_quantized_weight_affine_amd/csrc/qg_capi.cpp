@@ -86,6 +86,7 @@ const char* qg_strerror(qg_status s) {
         case QG_ELAUNCH: return "kernel launch failed";
         case QG_EPLAN: return "invalid routing plan input";
         case QG_EWORKSPACE: return "workspace too small";
+        case QG_ESCRATCH: return "the call needs more than the fixed scratch of the no-allocation entry point";
     }
     return "unknown status";
 }
@@ -327,17 +328,44 @@ size_t qg_moe_ffn_workspace(int H, int I, int T, int k, qg_mode mode) {
     return b;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Every check of the expert block's arguments except the workspace, before any HIP call (the stage
+// entry points check again what they need; with these passed, none of them can fail after an
+// earlier stage was launched).
+qg_status check_ffn(int fmt, const qg_expert* gate_up, const qg_expert* down, int group, int E, int H, int I,
+                    const float* X, int T, int k, const int32_t* seg_off, const int32_t* row_src,
+                    const int32_t* slot_row, const float* slot_w, const float* Y, int mode) {
+    if (!fmt_ok(fmt) || !mode_ok(mode)) return QG_EINVAL;
+    if (E < 1 || E > kMaxGridY || H < 32 || (H % 32) != 0 || H > kMaxK || I < 32 || (I % 32) != 0 || I > kMaxK ||
+        T < 0 || T > kMaxGridY || k < 1 || k > E || (int64_t)T * k > kMaxT)
+        return QG_ESHAPE;
+    if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (H % group) != 0 || (I % group) != 0))
+        return QG_ESHAPE;
+    const int R = T * k;
+    if ((mode == QG_FAST || R > 8 * E) && (R + 31) / 32 + std::min(E, R) > kMaxGridY) return QG_ESHAPE;
+    if (T == 0) return QG_OK;
+    if (!gate_up || !down || !X || !seg_off || !row_src || !slot_row || !slot_w || !Y) return QG_EINVAL;
+    if (!aligned(gate_up, 8) || !aligned(down, 8) || !aligned(X, 16) || !aligned(Y, 16) || !aligned(seg_off, 4) ||
+        !aligned(row_src, 4) || !aligned(slot_row, 4) || !aligned(slot_w, 4))
+        return QG_EALIGN;
+    return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* down, int group, int E, int H, int I,
                      const float* X, int T, int k, const int32_t* seg_off, const int32_t* row_src,
                      const int32_t* slot_row, const float* slot_w, float* Y, int accumulate, qg_mode mode,
                      void* workspace, size_t ws_bytes, hipStream_t stream) {
-    if (!fmt_ok(fmt) || !mode_ok(mode)) return QG_EINVAL;
-    if (E < 1 || E > kMaxGridY || H < 32 || (H % 32) != 0 || H > kMaxK || I < 32 || (I % 32) != 0 || I > kMaxK ||
-        T < 0 || T > kMaxGridY || k < 1 || k > E)
-        return QG_ESHAPE;
-    if (T == 0) return QG_OK;
-    if (!gate_up || !down || !X || !seg_off || !row_src || !slot_row || !slot_w || !Y || !workspace)
-        return QG_EINVAL;
+    qg_status st = check_ffn(fmt, gate_up, down, group, E, H, I, X, T, k, seg_off, row_src, slot_row, slot_w, Y,
+                             mode);
+    if (st != QG_OK || T == 0) return st;
+    if (!workspace) return QG_EINVAL;
     if (!aligned(workspace, 256)) return QG_EALIGN;
     if (ws_bytes < qg_moe_ffn_workspace(H, I, T, k, mode)) return QG_EWORKSPACE;
     const int R = T * k;
@@ -346,7 +374,6 @@ qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* d
     w += align256((size_t)R * 2 * I * 4);
     float* O = (float*)w;
     w += align256((size_t)R * H * 4);
-    qg_status st;
     if (mode == QG_FAST) {
         uint16_t* Xh = (uint16_t*)w;
         w += align256((size_t)R * H * 2);
@@ -374,6 +401,20 @@ qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* d
             return st;
     }
     return qg_moe_combine(O, R, slot_row, slot_w, Y, H, T, k, accumulate, stream);
+}
+
+qg_status qg_moe_ffn_noalloc(qg_format fmt, const qg_expert* gate_up, const qg_expert* down, int group, int E,
+                             int H, int I, const float* X, int T, int k, const int32_t* seg_off,
+                             const int32_t* row_src, const int32_t* slot_row, const float* slot_w, float* Y,
+                             int accumulate, qg_mode mode, hipStream_t stream) {
+    qg_status st = check_ffn(fmt, gate_up, down, group, E, H, I, X, T, k, seg_off, row_src, slot_row, slot_w, Y,
+                             mode);
+    if (st != QG_OK || T == 0) return st;
+    if (qg_moe_ffn_workspace(H, I, T, k, mode) > (size_t)QG_NOALLOC_SCRATCH_BYTES) return QG_ESCRATCH;
+    void* ws = nullptr;
+    if (qg::noalloc_scratch(&ws) != hipSuccess) return QG_ELAUNCH;
+    return qg_moe_ffn(fmt, gate_up, down, group, E, H, I, X, T, k, seg_off, row_src, slot_row, slot_w, Y, accumulate,
+                      mode, ws, QG_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -1,11 +1,39 @@
 // qg_misc.hip -- the dequant dump, the per-row f16 scaling, SwiGLU, the weighted combine, the
 // device routing plan and the GGUF block repack.
 #include <algorithm>
+#include <mutex>
 
+#include "qgemm.h"
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
 namespace qg {
+
+// ---- fixed scratch of the no-allocation MoE chain ---------------------------------------------------
+// QG_NOALLOC_SCRATCH_BYTES of device memory in every GPU the library runs on, held until the process
+// ends.  In host code `scratch` is a host-side stand-in, not a device address: host code only ever
+// uses the address hipGetSymbolAddress gives for the current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[QG_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // ---- dequant dump ------------------------------------------------------------------------------
 // One thread per (row, block) of the requested tile.  It runs the same block load and decode the

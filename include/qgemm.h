@@ -61,7 +61,8 @@ typedef enum {
     QG_EUNSUPPORTED = 4, /* a mode / activation type combination the library does not provide */
     QG_ELAUNCH = 5,      /* the HIP launch reported an error (hipGetLastError) */
     QG_EPLAN = 6,        /* a routing plan input is invalid (expert id, non-finite logit) */
-    QG_EWORKSPACE = 7    /* the workspace is smaller than the call needs */
+    QG_EWORKSPACE = 7,   /* the workspace is smaller than the call needs */
+    QG_ESCRATCH = 8      /* the call needs more than the library's fixed scratch memory */
 } qg_status;
 
 typedef enum { QG_X_F32 = 0, QG_X_F16 = 1, QG_X_BF16 = 2 } qg_xtype;
@@ -246,6 +247,27 @@ qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* d
                      const int32_t* row_src, const int32_t* slot_row, const float* slot_w,
                      float* Y, int accumulate, qg_mode mode, void* workspace, size_t ws_bytes,
                      hipStream_t stream);
+
+/* Bytes of the fixed device scratch that qg_moe_ffn_noalloc uses (one copy per GPU). */
+#define QG_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* qg_moe_ffn without a workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * semantics, checks and kernels as qg_moe_ffn; the intermediates live in a fixed scratch array of
+ * QG_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory from its first call on that
+ * GPU (the stream's GPU must be the current device) until the process ends.  Calls on one GPU share
+ * that array: calls that overlap in time on one GPU (two streams, two host threads) race and give
+ * wrong results; calls ordered on one stream are safe.  Nothing in the array has to start at zero
+ * (every intermediate the chain reads it has written first in the same call).  A call whose
+ * qg_moe_ffn_workspace(H, I, T, k, mode) exceeds QG_NOALLOC_SCRATCH_BYTES returns QG_ESCRATCH before
+ * any HIP call (exact mode at H 2048, I 1536 needs 26 624 bytes per routed row: up to 630 rows, 78
+ * tokens at top 8); a failure to find the array's device address returns QG_ELAUNCH.  Allocates
+ * nothing: no hipMalloc / hipFree. */
+qg_status qg_moe_ffn_noalloc(qg_format fmt, const qg_expert* gate_up, const qg_expert* down,
+                             int group, int E, int H, int I, const float* X, int T, int k,
+                             const int32_t* seg_off, const int32_t* row_src,
+                             const int32_t* slot_row, const float* slot_w, float* Y,
+                             int accumulate, qg_mode mode, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert qg.abi_version() == 1
-    for s in range(8):
+    for s in range(9):
         assert qg.strerror(s)
 
 
@@ -191,3 +191,33 @@ def test_pack_q4_round_trip_against_oracle(orc):
     assert np.array_equal(W, nib.astype(np.float64) - 8.0)
     with pytest.raises(ValueError):
         qg.pack_q4(np.full((1, 32), 16, np.uint8))
+
+
+def test_noalloc_ffn_validation_codes():
+    """The no-allocation expert block checks everything before any HIP call: a call whose
+    intermediates exceed the fixed scratch, bad shapes, null and misaligned pointers."""
+    L = qg.lib()
+    args = [0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d, 0, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.qg_moe_ffn_noalloc(*a)
+    assert qg.qg_moe_ffn_workspace(2048, 1536, 32, 8, "exact") <= qg.QG_NOALLOC_SCRATCH_BYTES
+    assert qg.qg_moe_ffn_workspace(2048, 1536, 32, 8, "fast") <= qg.QG_NOALLOC_SCRATCH_BYTES
+    # 4096 tokens x top 8: 32768 routed rows need ~870 MB of intermediates
+    assert call(a8=4096) == qg.QG_ESCRATCH
+    # exact mode at H 2048, I 1536: 26 624 bytes per routed row, 630 rows, so 78 tokens at top 8
+    assert qg.qg_moe_ffn_workspace(2048, 1536, 78, 8, "exact") <= qg.QG_NOALLOC_SCRATCH_BYTES
+    assert call(a8=79, a16=0) == qg.QG_ESCRATCH
+    assert call(a9=129) == qg.QG_ESHAPE                    # k > E
+    assert call(a5=2050) == qg.QG_ESHAPE                   # H % 32
+    assert call(a0=5) == qg.QG_EINVAL
+    assert call(a14=None) == qg.QG_EINVAL
+    assert call(a14=A16d + 4) == qg.QG_EALIGN              # Y: the combine's 16-byte rows
+    assert call(a7=A16c + 8) == qg.QG_EALIGN
+    assert call(a8=0) == qg.QG_OK                          # T = 0: nothing to do, no HIP call
+    # the workspace entry point applies the same checks first
+    assert L.qg_moe_ffn(0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d + 4, 0, 1,
+                        0x100000, 1 << 30, None) == qg.QG_EALIGN
