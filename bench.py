@@ -42,7 +42,7 @@ WORKLOADS = {
     "moe_block_fast": (4, "fast"),
 }
 HEADLINE = "q8_gemv_decode"
-# The headline kernel (gemv1_stream_kernel) and everything it is built from: its file, the device and
+# The headline kernel (gemv1_split_kernel) and everything it is built from: its file, the device and
 # launch headers, and the C entry point that launches it.  A committed traffic figure counts only while
 # these are unchanged.
 KERNEL_SOURCES = ["qg_device.hpp", "qg_internal.hpp", "qg_gemv.hip", "qg_capi.cpp"]
@@ -142,7 +142,7 @@ def setup_dense(ci: int, mode: str, copies: int):
         "name": c.name, "cfg": c, "mode": mode, "flops": 2.0 * c.T * c.N * c.K,
         "bytes": float(wbytes + xbytes + ybytes), "copies": copies, "weights": w,
         "dtype": ("f32" if mode == "exact" else c.xtype),
-        "kernel": (("gemv1_stream_kernel" if c.T == 1 and c.K <= 16384 else
+        "kernel": (("gemv1_split_kernel" if c.T == 1 and c.K <= 16384 else
                     "gemv_ksplit_kernel" if c.T >= 2 and c.K <= (16384 if c.T <= 4 else 8192) else "gemv_kernel")
                    if c.T <= 8
                    else ("gemm_exact_kernel" if mode == "exact" else "gemm_fast_lds_kernel")),
@@ -237,7 +237,7 @@ def measure_batch(steps: int, warmup: int) -> dict:
     nbytes = float(sum(N * (K + K // 32 * 4) + 4 * N for N in Ns) + 4 * K)
     gbs = nbytes / (ms_b * 1e-3) / 1e9
     return {"workload": "q8_batch_qkv_decode", "config": "q8_jobs_N4096_1024_1024_K4096_T1", "mode": "exact",
-            "ms_per_step": ms_b, "us_per_step": ms_b * 1e3, "dtype": "f32", "kernel": "gemv1_batch_kernel",
+            "ms_per_step": ms_b, "us_per_step": ms_b * 1e3, "dtype": "f32", "kernel": "gemv1_split_kernel",
             "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
             "bytes_per_step": nbytes, "us_three_separate_calls": ms_s * 1e3, "keep": (arrs, dev_sets, X)}
 

@@ -22,10 +22,11 @@
 //  * Grouped launches (exact-mode MoE): blockIdx.y is the expert; the workgroup walks the expert's
 //    row segment in chunks of at most 4 rows.
 //
-// Three kernels use this unit layout: gemv1_stream_kernel (one X row, X in LDS, persistent
-// wavefronts streaming whole rows), gemv_ksplit_kernel / gemv_ksplit_grouped_kernel (2..8 X rows or
-// an expert's segment chunk: K split over the wavefronts, each lane's X unit in registers, DPP row
-// sums), and gemv_kernel (the chunked LDS kernel above, for K beyond the K-split limits).
+// Kernels: gemv1_split_kernel (one X row: K split over the workgroup, each lane one 16-byte code
+// chunk of every weight row, its X values in registers; also the batched launch of several matrices),
+// gemv_ksplit_kernel / gemv_ksplit_grouped_kernel (2..8 X rows or an expert's segment chunk: K split
+// over the wavefronts in the unit layout above, each lane's X unit in registers, DPP row sums), and
+// gemv_kernel (the chunked LDS kernel above, for K beyond the K-split limits).
 #include <algorithm>
 
 #include "qg_device.hpp"
@@ -357,62 +358,108 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(DMA ? 3 : 1)
     }
 }
 
-// ---- single X row: streaming kernel ---------------------------------------------------------------
-// Workgroups of 4 wavefronts, up to four resident per CU; each stages X once into LDS (f32) and
-// wavefront w of workgroup b walks rows b * 4 + w + i * (4 * grid).  A row is cut into items of up
-// to 4 steps (4096 values); the loads of a wavefront's next item are issued before the arithmetic
-// of its current item.  The prologue issues the loads of X's first 1024 * XV values into registers,
-// then the first item's weight loads, and only then writes X to LDS and meets the one barrier, so
-// X's latency overlaps the weight stream instead of preceding it.  Measured on MI355X for a 4096 x
-// 4096 Q8 matrix (16 rotating copies), with standalone kernels of this shape: 5.24 us per launch
-// against 5.59 us for 16-wavefront workgroups that stage X before issuing any weight load; a plain
-// read of the same bytes with this geometry takes 4.71 us and an empty launch 2.7 us.  This kernel
-// through the C ABI: 5.4-5.6 us.
-constexpr int kStreamThreads = 256;
-constexpr int kStreamKMax = 16384;  // X in LDS as f32: at most 64 KiB
-constexpr int kStreamSteps = 4;     // steps (64 units each) per item
-constexpr int kStreamWgPerCu = 4;   // resident workgroups per CU when LDS allows
+// Sums of each 16-lane row of the wavefront by DPP row shifts by 1, 2, 4, 8 (lanes without a source
+// add 0): lane 15 of every row ends with its row's sum.
+__device__ __forceinline__ float row16_sum_dpp(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+    return v;
+}
+// ---- single X row: K split over the workgroup --------------------------------------------------
+// Lane c of the workgroup owns chunk c of every weight row: its 16 code bytes (Q8: 16 values, half a
+// block; Q4 / Q4A: 32 values, one block), so every load instruction of a wavefront is one contiguous
+// 1 KiB run of a row, and the chunk's X values stay in registers for the whole launch.  A workgroup
+// of W = ceil(chunks / 64) wavefronts takes R consecutive weight rows: it issues the loads of all R
+// rows, then per row forms the chunk's f32 partial (block scale on the partial, Q4A offset times the
+// chunk's X sum), sums each 16-lane row by DPP, and after one barrier R threads add the W * 4 row
+// sums and store Y.
+//
+// Measured on MI355X, Q8 N = K = 4096, f32 X, 16 rotating weight copies, standalone kernels in one
+// process (the figures of one run): this shape with R = 8 5.03-5.07 us per launch; R = 4 5.19-5.32;
+// R = 16 (one workgroup per CU) 5.8; the previous kernel (one row per wavefront, X staged in LDS per
+// workgroup, 1024 workgroups) 5.43-5.70 through the C ABI.  What the rest is: an empty launch costs
+// 1.58 us on the GPU; a kernel issuing the same loads and only folding the bytes takes 4.16-4.19 us;
+// the row sums, barrier and Y store add 0.35 us to it (0.25 of that is the store: a kernel that
+// leaves output in the L2 caches pays their write-back at its end, whatever the store's scope); the
+// decode (16 conversions and 16 FMAs per lane and row) overlaps the loads only in part, because a
+// wavefront consumes its loads in issue order.  Tried and slower: each lane owning 2 or 4
+// consecutive chunks (a load then covers 2 or 4 KiB with gaps: 5.5-12 us), every load pinned ahead
+// of all arithmetic (5.3-5.6), X loaded after the weights (5.6-5.9), per-lane partials summed from
+// LDS instead of DPP row sums (5.26), nontemporal Y stores (5.23).
+constexpr int kStreamKMax = 16384;  // K limit of the K-split kernels for Q8 (16 wavefronts of 1024 values)
 
-// BATCH: p.N is the total row count of the jobs in bj; a wavefront's row g belongs to the job j
-// with start[j] <= g < start[j+1] (found by a scan over at most 8 wave-uniform entries).
-template <int FMT, int XT, bool BATCH>
-__device__ __forceinline__ void gemv1_body(const GemmParams& p, const BatchJobs& bj) {
-    extern __shared__ __attribute__((aligned(16))) float xs[];  // K floats
-    constexpr int W = kStreamThreads / 64, S = kStreamSteps;
-    constexpr int XV = (XT == XT_F32) ? 4 : 8;  // X values per 16-byte load
-    constexpr int XPRE = 4;                     // 16-byte X loads per thread issued ahead
+template <int FMT>
+struct G1Chunk {
+    static constexpr int values = FMT == FMT_Q8 ? 16 : 32;  // X values per lane chunk (16 code bytes)
+};
+
+// base + off as a wavefront-uniform pointer held in scalar registers (off must be uniform).
+__device__ __forceinline__ const QG_GLOBAL char* uniform_ptr(const void* base, uint64_t off) {
+    const uint64_t a = (uint64_t)(uintptr_t)base + off;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return (const QG_GLOBAL char*)(((uint64_t)hi << 32) | lo);
+}
+
+// BATCH: p.N is the total row count of the jobs in bj; row g belongs to the job j with
+// start[j] <= g < start[j+1] (a scan over at most 8 wave-uniform entries).
+template <int FMT, int XT, int R, bool BATCH, bool RS>
+__global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJobs bj) {
+    constexpr int V = G1Chunk<FMT>::values;
+    __shared__ float part[R * 16 * 4];  // [row][wavefront][4 row sums]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int K = p.K, units = K >> 4;
-    const int items = (units + 64 * S - 1) / (64 * S);  // items per row
+    const int K = p.K, N = p.N, chunks = K / V;
+    const int W = (chunks + 63) >> 6;  // the launch's wavefront count (blockDim.x would be read late)
+    const int c = 64 * wave + lane;
+    const bool on = c < chunks;
+    const int cc = min(c, chunks - 1);
+    const int n0 = (int)blockIdx.x * R;
+    // What the epilogue needs from the arguments is read here and pinned in scalar registers: the
+    // compiler treats argument loads as free to repeat and otherwise reloads them after the barrier,
+    // a memory round trip at the end of every workgroup (0.3-0.5 us per launch measured).
+    QG_GLOBAL float* Yout = gptr_mut<float>(p.Y);
+    int Nout = N;
+    asm volatile("" : "+s"(Yout), "+s"(Nout));
+    float sc = 1.f;
+    if constexpr (RS) sc = p.rs ? p.rs[0] : 1.f;
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Stores XV values of X starting at element e (a 16-byte load q) into xs as f32.
-    auto put_x = [&](int e, const uint4 q) {
-        float4* d = (float4*)(xs + e);
+    // This lane's X values: Q8 elements 16cc..16cc+15; Q4 / Q4A elements 32cc..32cc+31 (x[0..15]
+    // pair with the low nibbles, x[16..31] with the high ones).  Zero for a lane past K.
+    float x[V];
+    {
+        const size_t e0 = (size_t)cc * V;
         if constexpr (XT == XT_F32) {
-            d[0] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
-        } else {
-            const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-            float v[8];
 #pragma unroll
-            for (int h = 0; h < 4; h++) {
-                if constexpr (XT == XT_F16) {
-                    v[2 * h] = f16_to_f32((uint16_t)(w4[h] & 0xFFFFu));
-                    v[2 * h + 1] = f16_to_f32((uint16_t)(w4[h] >> 16));
-                } else {
-                    v[2 * h] = __uint_as_float(w4[h] << 16);
-                    v[2 * h + 1] = __uint_as_float(w4[h] & 0xFFFF0000u);
+            for (int i = 0; i < V / 4; i++) {
+                const float4 a = *(const float4*)((const float*)p.X + e0 + 4 * i);
+                x[4 * i] = a.x;
+                x[4 * i + 1] = a.y;
+                x[4 * i + 2] = a.z;
+                x[4 * i + 3] = a.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V / 8; i++) {
+                const uint4 q = *(const uint4*)((const uint16_t*)p.X + e0 + 8 * i);
+                const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int h = 0; h < 8; h++) {
+                    const uint16_t hv = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
+                    x[8 * i + h] = (XT == XT_F16) ? f16_to_f32(hv) : bf16_to_f32(hv);
                 }
             }
-            d[0] = make_float4(v[0], v[1], v[2], v[3]);
-            d[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
-    };
-    auto x_at = [&](int e) -> uint4 {  // 16 bytes of X from element e (e % XV == 0, e < K)
-        return (XT == XT_F32) ? *(const uint4*)((const float*)p.X + e) : *(const uint4*)((const uint16_t*)p.X + e);
-    };
+#pragma unroll
+        for (int i = 0; i < V; i++) x[i] = on ? x[i] : 0.f;
+    }
+    float sx = 0.f;
+    if constexpr (FMT == FMT_Q4A) {
+#pragma unroll
+        for (int i = 0; i < V; i++) sx += x[i];
+    }
 
-    const int tw = W * (int)gridDim.x;
-    const float sc = p.rs ? p.rs[0] : 1.f;
     auto job_of = [&](int g) {
         int j = 0;
         if constexpr (BATCH) {
@@ -422,108 +469,104 @@ __device__ __forceinline__ void gemv1_body(const GemmParams& p, const BatchJobs&
         }
         return j;
     };
-    auto load_item = [&](int row, int c, Unit<FMT> (&w)[S]) {
+    // Row bases of codes, scales (and offsets) for every row, as wavefront-uniform pointers pinned in
+    // scalar registers before any load: each load is then base + the lane's 32-bit offset, with no
+    // per-lane 64-bit address arithmetic (left to itself the compiler computes half of them per
+    // lane in vector registers; 0.2-0.3 us per launch measured).
+    const QG_GLOBAL char* crow[R];
+    const QG_GLOBAL char* srow[R];
+    const QG_GLOBAL char* orow[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        int n = min(n0 + r, N - 1);
         const void* codes = p.codes;
         const void* scales = p.scales;
         const uint16_t* offs = p.offs;
         if constexpr (BATCH) {
-            const int j = job_of(row);
+            const int j = job_of(n);
             codes = bj.codes[j];
             scales = bj.scales[j];
             offs = bj.offs[j];
-            row -= bj.start[j];
+            n -= bj.start[j];
         }
-#pragma unroll
-        for (int j = 0; j < S; j++) {
-            const int u = min(64 * (S * c + j) + lane, units - 1);
-            w[j] = load_unit<FMT>(codes, scales, offs, p.group, K, row, u);
+        crow[r] = uniform_ptr(codes, (uint64_t)n * (uint64_t)(FMT == FMT_Q8 ? K : K >> 1));
+        srow[r] = uniform_ptr(scales, (uint64_t)n * (uint64_t)((K >> 5) * (FMT == FMT_Q8 ? 4 : 2)));
+        asm volatile("" : "+s"(crow[r]), "+s"(srow[r]));
+        if constexpr (FMT == FMT_Q4A) {
+            orow[r] = uniform_ptr(offs, (uint64_t)n * (uint64_t)((K / p.group) * 2));
+            asm volatile("" : "+s"(orow[r]));
+        }
+    }
+    const uint32_t oc = (uint32_t)(cc * 16);
+    const uint32_t os = FMT == FMT_Q8 ? (uint32_t)((cc >> 1) * 4) : (uint32_t)(cc * 2);
+    const uint32_t oo = FMT == FMT_Q4A ? (uint32_t)(((cc * 32) / p.group) * 2) : 0u;
+    u32x4_t q[R];
+    float d[R], m[R];
+    auto issue = [&](int r) __attribute__((always_inline)) {
+        q[r] = __builtin_nontemporal_load((const QG_GLOBAL u32x4_t*)(crow[r] + oc));
+        if constexpr (FMT == FMT_Q8) {
+            d[r] = *(const QG_GLOBAL float*)(srow[r] + os);
+            m[r] = 0.f;
+        } else {
+            d[r] = 0.0625f * f16_to_f32(*(const QG_GLOBAL uint16_t*)(srow[r] + os));
+            m[r] = FMT == FMT_Q4A ? bf16_to_f32(*(const QG_GLOBAL uint16_t*)(orow[r] + oo)) : 0.f;
         }
     };
-    auto compute_item = [&](int c, const Unit<FMT> (&w)[S], float& acc) {
+    auto row = [&](int r) __attribute__((always_inline)) {
+        const uint32_t w4[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
+        float pr = 0.f;
+        if constexpr (FMT == FMT_Q8) {
 #pragma unroll
-        for (int j = 0; j < S; j++) {
-            const int u = 64 * (S * c + j) + lane;
-            if (u < units) {
-                int e0, e1;
-                unit_runs<FMT>(u, e0, e1);
-                const float4* a = (const float4*)(xs + e0);
-                const float4* b = (const float4*)(xs + e1);
-                const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-                const float x[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                                     b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-                float sx = 0.f;
-                if constexpr (FMT == FMT_Q4A) {
+            for (int i = 0; i < 16; i++) pr = fmaf(sbyte_f32(w4[i >> 2], i & 3), x[i], pr);
+        } else {
+            // signed bytes 16 (nibble - 8): the nibble moved to the byte's high half, top bit flipped
 #pragma unroll
-                    for (int i = 0; i < 16; i++) sx += x[i];
-                }
-                acc += unit_value<FMT>(w[j], unit_partial<FMT>(w[j], x), sx);
+            for (int i = 0; i < 16; i++) pr = fmaf(sbyte_f32(((w4[i >> 2] << 4) & 0xF0F0F0F0u) ^ 0x80808080u, i & 3), x[i], pr);
+#pragma unroll
+            for (int i = 0; i < 16; i++) pr = fmaf(sbyte_f32((w4[i >> 2] & 0xF0F0F0F0u) ^ 0x80808080u, i & 3), x[16 + i], pr);
+        }
+        const float v = row16_sum_dpp(FMT == FMT_Q4A ? fmaf(d[r], pr, m[r] * sx) : d[r] * pr);
+        if ((lane & 15) == 15) part[(r * 16 + wave) * 4 + (lane >> 4)] = v;
+    };
+    // Issue order (pinned by scheduling barriers): X (above), rows [0, A), the arithmetic of row 0,
+    // rows [A, R), the arithmetic of the rest.  Measured (Q8 4096 x 4096, R = 8): A = 3 or 4 5.03
+    // us, A = 2 5.13, A = 1 5.24, the rest issued before row 0's arithmetic 5.23, and the order the
+    // compiler picks by itself 5.05-5.45 depending on the surrounding code.
+    constexpr int A = R >= 8 ? 4 : 1;
+#pragma unroll
+    for (int r = 0; r < A; r++) issue(r);
+    __builtin_amdgcn_sched_barrier(0);
+    row(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = A; r < R; r++) issue(r);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 1; r < R; r++) row(r);
+    __syncthreads();
+    // Row r's W * 4 partials: thread 16 r + w adds wavefront w's four, then a 16-lane DPP sum
+    // (R * 16 <= 64 W threads: R = 8 runs with W >= 4, R = 4 with W >= 1).
+    if ((int)threadIdx.x < R * 16) {
+        const int r = (int)threadIdx.x >> 4, w = (int)threadIdx.x & 15;
+        float sum = 0.f;
+        if (w < W) {
+            const float4 a = *(const float4*)(part + ((int)threadIdx.x) * 4);
+            sum = (a.x + a.y) + (a.z + a.w);
+        }
+        sum = row16_sum_dpp(sum);
+        const int g = n0 + r;
+        if (w == 15 && g < Nout) {
+            if constexpr (BATCH) {
+                const int j = job_of(g);
+                bj.Y[j][g - bj.start[j]] = sum * sc;
+            } else {
+                Yout[g] = sum * sc;
             }
         }
-    };
-    int n = (int)blockIdx.x * W + wave, c = 0;
-    const bool active = n < p.N;  // every wavefront takes part in staging X and the barrier
-    Unit<FMT> wa[S], wb[S];
-
-    // Prologue: X loads for the first XPRE * XV * 256 values, the first item's weight loads, then
-    // X into LDS (the rest of X, if any, loaded directly), one barrier.  No branches: indices past
-    // K are clamped to the last 16 bytes of X (those threads store the same values twice) and an
-    // idle wavefront loads the last row, so the compiler waits for each X load alone before its
-    // LDS store instead of for every load in flight.
-    uint4 xr[XPRE];
-#pragma unroll
-    for (int i = 0; i < XPRE; i++) xr[i] = x_at(min(XV * ((int)threadIdx.x + kStreamThreads * i), K - XV));
-    load_item(min(n, p.N - 1), 0, wa);
-#pragma unroll
-    for (int i = 0; i < XPRE; i++) put_x(min(XV * ((int)threadIdx.x + kStreamThreads * i), K - XV), xr[i]);
-    for (int e = XV * ((int)threadIdx.x + kStreamThreads * XPRE); e < K; e += XV * kStreamThreads) put_x(e, x_at(e));
-    __syncthreads();  // the only barrier: wavefronts may leave independently after it
-    if (!active) return;
-
-    float acc = 0.f;
-    // Item sequence of this wavefront: (row n, chunk c) in row-major order.
-    // One item: issue the next item's loads into `nx`, compute `cu`, finish the row if its last
-    // chunk was just done.  Returns false after the wavefront's last item.
-    auto step = [&](Unit<FMT> (&cu)[S], Unit<FMT> (&nx)[S]) __attribute__((always_inline)) {
-        int n2 = n, c2 = c + 1;
-        if (c2 == items) {
-            c2 = 0;
-            n2 = n + tw;
-        }
-        const bool more = n2 < p.N;
-        if (more) load_item(n2, c2, nx);
-        compute_item(c, cu, acc);
-        if (c + 1 == items) {
-            const float v = wave_sum(acc);
-            if (lane == 0) {
-                if constexpr (BATCH) {
-                    const int j = job_of(n);
-                    bj.Y[j][n - bj.start[j]] = v * sc;
-                } else {
-                    p.Y[n] = v * sc;
-                }
-            }
-            acc = 0.f;
-        }
-        n = n2;
-        c = c2;
-        return more;
-    };
-    while (step(wa, wb) && step(wb, wa)) {
     }
 }
 
-template <int FMT, int XT>
-__global__ __launch_bounds__(kStreamThreads) void gemv1_stream_kernel(GemmParams p) {
-    gemv1_body<FMT, XT, false>(p, BatchJobs{});
-}
-
-template <int FMT, int XT>
-__global__ __launch_bounds__(kStreamThreads) void gemv1_batch_kernel(GemmParams p, BatchJobs bj) {
-    gemv1_body<FMT, XT, true>(p, bj);
-}
-
-// Single X row with K <= kStreamKMax: up to kStreamWgPerCu resident workgroups per CU, fewer when
-// their X copies would not fit in the CU's 160 KiB of LDS.
+// CU count of the current device (cached).
 static int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
@@ -536,17 +579,27 @@ static int device_cus() {
     return cus[dev];
 }
 
+// Single X row: W = ceil(chunks / 64) <= 16 wavefronts (Q8 K <= 16384, Q4 K <= 32768); R = 8 rows per
+// workgroup when W >= 4, else 4 (more workgroups for narrow ones).  False (nothing launched) when K
+// is past the limit.
 template <int FMT, int XT>
 static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = nullptr) {
-    if (p.K > kStreamKMax) return false;
-    constexpr int W = kStreamThreads / 64;
-    const size_t lds = (size_t)p.K * 4;
-    const int per_cu = std::max(1, std::min(kStreamWgPerCu, (int)((160u * 1024u) / lds)));
-    const int grid = std::max(1, std::min((p.N + W - 1) / W, device_cus() * per_cu));
-    if (bj)
-        hipLaunchKernelGGL((gemv1_batch_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p, *bj);
-    else
-        hipLaunchKernelGGL((gemv1_stream_kernel<FMT, XT>), dim3(grid), dim3(kStreamThreads), lds, s, p);
+    const int chunks = p.K / G1Chunk<FMT>::values;
+    const int W = (chunks + 63) / 64;
+    if (W > 16) return false;
+    const BatchJobs none{};
+    const BatchJobs& b = bj ? *bj : none;
+    // variants: rows per workgroup, batched jobs, a row scale (read only when given)
+    auto go = [&](auto kern, int rows) { hipLaunchKernelGGL(kern, dim3((p.N + rows - 1) / rows), dim3(64 * W), 0, s, p, b); };
+    if (W >= 4) {
+        if (bj) go(gemv1_split_kernel<FMT, XT, 8, true, false>, 8);
+        else if (p.rs) go(gemv1_split_kernel<FMT, XT, 8, false, true>, 8);
+        else go(gemv1_split_kernel<FMT, XT, 8, false, false>, 8);
+    } else {
+        if (bj) go(gemv1_split_kernel<FMT, XT, 4, true, false>, 4);
+        else if (p.rs) go(gemv1_split_kernel<FMT, XT, 4, false, true>, 4);
+        else go(gemv1_split_kernel<FMT, XT, 4, false, false>, 4);
+    }
     return true;
 }
 
@@ -565,15 +618,6 @@ static bool gemv1(const GemmParams& p, hipStream_t s, const BatchJobs* bj = null
 // against 14.61, T = 8 14.05 against 17.94.
 constexpr int kSplitRows = 4;  // weight rows per batch
 
-// Sums of each 16-lane row of the wavefront by DPP row shifts by 1, 2, 4, 8 (lanes without a source
-// add 0): lane 15 of every row ends with its row's sum.
-__device__ __forceinline__ float row16_sum_dpp(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
-    return v;
-}
 // One pass of the scheme above: NT X rows xrow[t] (-1 = a zero row) against the weight-row batches
 // b, b + stride, ... < ceil(N / kSplitRows) of one matrix, into Y rows yrow0 + t.  part: LDS of
 // 2 * 16 * kSplitRows * NTS * 4 floats, 16-byte aligned, with a per-wavefront slot of
