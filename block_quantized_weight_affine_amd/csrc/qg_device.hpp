@@ -245,13 +245,13 @@ __device__ __forceinline__ uint32_t value_word(const RawBlock<FMT>& r, int k) {
     }
 }
 
-// Fragment jj (elements 8jj .. 8jj+7) of a block as (1) gives it, c0 from block_c0; no fallback.
+// Eight elements as (1) gives them from their two value-byte words c (elements 4k .. 4k+3 in word
+// k), the block's scale d (dh its f16 bits, used by Q4 into f16) and c0 from block_c0; no fallback.
 template <int FMT, int ST>
-__device__ __forceinline__ short8_t frag16_fast(const RawBlock<FMT>& r, float c0, int jj) {
-    const uint32_t c[2] = {value_word<FMT>(r, 2 * jj), value_word<FMT>(r, 2 * jj + 1)};
+__device__ __forceinline__ short8_t frag16_words(const uint32_t (&c)[2], float d, uint32_t dh, float c0) {
     short8_t f;
     if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
-        const half2_t d2 = __builtin_bit_cast(half2_t, r.dh | (r.dh << 16));
+        const half2_t d2 = __builtin_bit_cast(half2_t, dh | (dh << 16));
         const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
         uint32_t o[4];
 #pragma unroll
@@ -266,7 +266,31 @@ __device__ __forceinline__ short8_t frag16_fast(const RawBlock<FMT>& r, float c0
     } else {
 #pragma unroll
         for (int s = 0; s < 8; s++)
-            f[s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[s >> 2], s & 3), r.d, c0)));
+            f[s] = (short)f32_to_16<ST>(keep_f32(fmaf(byte_f32(c[s >> 2], s & 3), d, c0)));
+    }
+    return f;
+}
+
+// Fragment jj (elements 8jj .. 8jj+7) of a block as (1) gives it, c0 from block_c0; no fallback.
+template <int FMT, int ST>
+__device__ __forceinline__ short8_t frag16_fast(const RawBlock<FMT>& r, float c0, int jj) {
+    const uint32_t c[2] = {value_word<FMT>(r, 2 * jj), value_word<FMT>(r, 2 * jj + 1)};
+    return frag16_words<FMT, ST>(c, r.d, r.dh, c0);
+}
+
+// The same eight elements in the pages' order of operations (the fallback of (1)): (c - 8) d,
+// (c - 128) d or fma(c - 8, d, m) per element, then narrowed to ST.
+template <int FMT, int ST>
+__device__ __forceinline__ short8_t frag16_words_slow(const uint32_t (&c)[2], float d, float m) {
+    short8_t f;
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+        const float cf = byte_f32(c[s >> 2], s & 3);
+        float v;
+        if constexpr (FMT == FMT_Q8) v = (cf - 128.0f) * d;
+        else if constexpr (FMT == FMT_Q4) v = (cf - 8.0f) * d;
+        else v = fmaf(cf - 8.0f, d, m);
+        f[s] = (short)f32_to_16<ST>(keep_f32(v));
     }
     return f;
 }
