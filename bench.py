@@ -191,7 +191,7 @@ def setup_moe(mode: str):
         "bytes": float(used * (gu_b + dn_b) + 2 * T * H * 4), "used_experts": used, "plan_host_ms": plan_ms,
         "plan_device_us": plan_dev_ms * 1e3,
         "copies": 1, "dtype": "f32" if mode == "exact" else "f16",
-        "kernel": "gemv_ksplit_grouped_kernel" if mode == "exact" else "gemm_fast_lds_kernel", "keep": keep,
+        "kernel": "grouped_rows_kernel", "keep": keep,
     }
     return step, info
 

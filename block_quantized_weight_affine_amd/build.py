@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["qg_gemm.hip", "qg_gemv.hip", "qg_misc.hip", "qg_capi.cpp"]
+SOURCES = ["qg_gemm.hip", "qg_gemv.hip", "qg_moe.hip", "qg_misc.hip", "qg_capi.cpp"]
 ARCH = os.environ.get("QG_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -274,7 +274,9 @@ qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, 
     if (!aligned(experts, 8) || !aligned(seg_off, 4) || !aligned(X, 16) || !aligned(Y, 4) ||
         (row_src && !aligned(row_src, 4)) || (rs && !aligned(rs, 4)))
         return QG_EALIGN;
-    if (mode == QG_FAST && xt == QG_X_F32) return QG_EUNSUPPORTED;
+    // fast mode with f32 X: the rows are scaled to f16 inside the expert-row kernel, which takes K up
+    // to 2048 (Q4, Q4A) or 1024 (Q8)
+    if (mode == QG_FAST && xt == QG_X_F32 && !qg::grouped_rows_fits(fmt, K, N, 0)) return QG_EUNSUPPORTED;
     GemmParams p{};
     p.experts = (const qg::ExpertPtr*)experts;
     p.seg_off = seg_off;
@@ -288,13 +290,17 @@ qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, 
     p.K = K;
     p.R = R;
     p.E = E;
-    // Exact mode: short segments (at most 8 rows per expert on average) stream each expert's
-    // weights once through the GEMV; longer ones would make the GEMV re-read them for every 8 rows,
-    // so they take the f32 MFMA tile kernel.
-    if (mode == QG_EXACT) {
-        if (R <= 8 * E) return launched(qg::launch_gemv(fmt, xt, p, true, stream));
-        return launched(qg::launch_gemm_exact(fmt, xt, p, true, stream));
+    // Short segments (at most 8 rows per expert on average) stream each expert's weights once
+    // through the expert-row kernel (f32 arithmetic; fast mode with f16 or f32 X: f16 X through
+    // v_dot2), or the K-split GEMV where K is past that kernel's limit; longer segments would
+    // re-read the weights for every 4 rows, so they take the MFMA tile kernels.
+    const bool fast = mode == QG_FAST;
+    if (fast && xt == QG_X_F32) return launched(qg::launch_grouped_rows(fmt, xt, true, 0, p, stream));
+    if (R <= 8 * E) {
+        if (qg::grouped_rows_fits(fmt, K, N, 0)) return launched(qg::launch_grouped_rows(fmt, xt, fast, 0, p, stream));
+        if (!fast) return launched(qg::launch_gemv(fmt, xt, p, true, stream));
     }
+    if (!fast) return launched(qg::launch_gemm_exact(fmt, xt, p, true, stream));
     return launched(qg::launch_gemm_fast(fmt, xt, p, true, stream));
 }
 
@@ -370,6 +376,35 @@ qg_status qg_moe_ffn(qg_format fmt, const qg_expert* gate_up, const qg_expert* d
     if (ws_bytes < qg_moe_ffn_workspace(H, I, T, k, mode)) return QG_EWORKSPACE;
     const int R = T * k;
     char* w = (char*)workspace;
+    if (R <= 8 * E && qg::grouped_rows_fits(fmt, H, 2 * I, 1) && qg::grouped_rows_fits(fmt, I, H, 0)) {
+        // Short segments: gate|up with SwiGLU in its epilogue (A f32), then down, then the combine;
+        // fast mode scales the f32 rows of X and of A to f16 inside the two matmuls.
+        const bool fast = mode == QG_FAST;
+        float* A = (float*)w;
+        float* O = (float*)(w + align256((size_t)R * I * 4));
+        GemmParams p{};
+        p.experts = (const qg::ExpertPtr*)gate_up;
+        p.seg_off = seg_off;
+        p.row_src = row_src;
+        p.x_rows = T;
+        p.X = X;
+        p.Y = A;
+        p.group = group > 0 ? group : 64;
+        p.N = 2 * I;
+        p.K = H;
+        p.R = R;
+        p.E = E;
+        if ((st = launched(qg::launch_grouped_rows(fmt, QG_X_F32, fast, 1, p, stream))) != QG_OK) return st;
+        p.experts = (const qg::ExpertPtr*)down;
+        p.row_src = nullptr;
+        p.x_rows = R;
+        p.X = A;
+        p.Y = O;
+        p.N = H;
+        p.K = I;
+        if ((st = launched(qg::launch_grouped_rows(fmt, QG_X_F32, fast, 0, p, stream))) != QG_OK) return st;
+        return qg_moe_combine(O, R, slot_row, slot_w, Y, H, T, k, accumulate, stream);
+    }
     float* GU = (float*)w;
     w += align256((size_t)R * 2 * I * 4);
     float* O = (float*)w;

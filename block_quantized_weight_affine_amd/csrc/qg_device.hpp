@@ -40,6 +40,13 @@ __device__ __forceinline__ QG_GLOBAL T* gptr_mut(void* p) {
     return (QG_GLOBAL T*)(p);
 }
 
+// base + off as a wavefront-uniform pointer held in scalar registers (off must be uniform).
+__device__ __forceinline__ const QG_GLOBAL char* uniform_ptr(const void* base, uint64_t off) {
+    const uint64_t a = (uint64_t)(uintptr_t)base + off;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return (const QG_GLOBAL char*)(((uint64_t)hi << 32) | lo);
+}
+
 // Same layout as qg_expert in qgemm.h.
 struct Expert {
     const void* codes;
@@ -387,5 +394,51 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
+
+// Sums of each 16-lane row of the wavefront by DPP row shifts by 1, 2, 4, 8 (lanes without a source
+// add 0): lane 15 of every row ends with its row's sum.
+__device__ __forceinline__ float row16_sum_dpp(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+    return v;
+}
+// Full-wavefront sum: the row sums above, then the row-15 broadcast into rows 1 and 3 and the
+// row-31 broadcast into rows 2 and 3 (lanes of other rows keep their value): lane 63 ends with the
+// sum of all 64 lanes.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    v = row16_sum_dpp(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+// Wavefront maximum of non-negative values by the same steps (identity 0), read back from lane 63
+// into every lane.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Power-of-two row scale (page "oxinfer 0.0.5 src/metal.rs", MMA_SHADER_SRC, row_scale): the
+// largest magnitude lands in [2^13, 2^14); a zero or non-finite amax keeps scale 1.  The caller
+// multiplies the row by 2^e before narrowing to f16 and the result by 2^-e.
+__device__ __forceinline__ int row_scale_exp(float amax) {
+    int e = 0;
+    if (amax > 0.f && isfinite(amax)) {
+        int fe;
+        frexpf(amax, &fe);
+        e = min(max(14 - fe, -100), 100);
+    }
+    return e;
+}
+
+// SwiGLU of one gate / up pair (page section silu_half): a = g / (1 + exp(-g)) * u in f32.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 }  // namespace qg

@@ -696,6 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
     constexpr int WL = (BN * CPR) % (64 * NW) == 0 ? 64 : 32;  // lanes per raw-weight copy
     constexpr int WCH = BN * CPR / (WL * NW);   // raw-weight copies per wavefront and stage
     constexpr int L = XCH + WCH + 2 * MN * (FMT == FMT_Q4A ? 2 : 1);  // loads per wavefront and stage
+    constexpr int LC = XCH + WCH;  // of which copies to LDS
     static_assert(XCH * 8 * NW == BT && WCH * WL * NW == BN * CPR, "tile");
     static_assert(D >= 3 && (D - 2) * L <= 63, "ring depth");
     constexpr int XB = BT * 128, WBY = BN * CPR * 16;  // bytes per slot
@@ -870,8 +871,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
     auto stage = [&](auto uc, int s) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;  // s % D
         // this wavefront's copies of stage s have landed (D - 2 later stages issued since); the
-        // barrier then covers every wavefront's copies and frees slot (s - 1) % D for stage s + D - 1
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 2) * L>());
+        // barrier then covers every wavefront's copies and frees slot (s - 1) % D for stage s + D - 1.
+        // The wait counts the later stages' copies only: copies to LDS complete in issue order among
+        // themselves but not with respect to the scale loads into registers, so the scale loads
+        // issued since may already be done (their own waits the compiler places before their uses).
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 2) * LC>());
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(min(s + D - 1, nstage - 1), std::integral_constant<int, (u + D - 1) % D>{}, scr[(u + D - 1) % D]);

@@ -358,15 +358,6 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(DMA ? 3 : 1)
     }
 }
 
-// Sums of each 16-lane row of the wavefront by DPP row shifts by 1, 2, 4, 8 (lanes without a source
-// add 0): lane 15 of every row ends with its row's sum.
-__device__ __forceinline__ float row16_sum_dpp(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
-    return v;
-}
 // ---- single X row: K split over the workgroup --------------------------------------------------
 // Lane c of the workgroup owns chunk c of every weight row: its 16 code bytes (Q8: 16 values, half a
 // block; Q4 / Q4A: 32 values, one block), so every load instruction of a wavefront is one contiguous
@@ -395,12 +386,6 @@ struct G1Chunk {
     static constexpr int values = FMT == FMT_Q8 ? 16 : 32;  // X values per lane chunk (16 code bytes)
 };
 
-// base + off as a wavefront-uniform pointer held in scalar registers (off must be uniform).
-__device__ __forceinline__ const QG_GLOBAL char* uniform_ptr(const void* base, uint64_t off) {
-    const uint64_t a = (uint64_t)(uintptr_t)base + off;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    return (const QG_GLOBAL char*)(((uint64_t)hi << 32) | lo);
-}
 
 // BATCH: p.N is the total row count of the jobs in bj; row g belongs to the job j with
 // start[j] <= g < start[j+1] (a scan over at most 8 wave-uniform entries).

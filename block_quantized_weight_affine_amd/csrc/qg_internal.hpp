@@ -51,6 +51,12 @@ hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped,
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
 // T = 1, K <= 16384: every job of bj in one launch (p.N = bj.start[bj.J]); false if not applicable.
 bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err);
+// Grouped matmul with short segments streamed per expert row (epi 0: Y = X W^T; epi 1: gate|up
+// matrices of N = 2I rows, Y[r][j] = SiLU(g) * u with pitch I).  fast: f16 X through v_dot2, or f32
+// X scaled to f16 per row in the kernel; otherwise f32 arithmetic.  grouped_rows_fits tells whether
+// the shape is taken.
+bool grouped_rows_fits(int fmt, int K, int N, int epi);
+hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmParams& p, hipStream_t s);
 hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
                                int N, int K, int n0, int k0, int rows, int cols, int staged, void* out,
                                hipStream_t s);

@@ -100,17 +100,6 @@ __device__ __forceinline__ float block_max256(float m, float* red) {
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Power-of-two row scale (page "oxinfer 0.0.5 src/metal.rs", MMA_SHADER_SRC, row_scale): the
-// largest magnitude lands in [2^13, 2^14); a zero or non-finite amax keeps scale 1.
-__device__ __forceinline__ int row_scale_exp(float amax) {
-    int e = 0;
-    if (amax > 0.f && isfinite(amax)) {
-        int fe;
-        frexpf(amax, &fe);
-        e = min(max(14 - fe, -100), 100);
-    }
-    return e;
-}
 
 // ---- x_half: gathered per-row scaling to f16 -----------------------------------------------------
 __global__ __launch_bounds__(256) void x_half_kernel(const float* X, int x_rows, const int32_t* row_src, int K,
@@ -151,7 +140,6 @@ hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int
 }
 
 // ---- SwiGLU (page section silu_half): a = g / (1 + exp(-g)) * u ------------------------------------
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 __global__ __launch_bounds__(256) void swiglu_f32_kernel(const float* GU, int I, float* A) {
     const int r = blockIdx.x;

@@ -209,11 +209,19 @@ qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, i
  * x_r = X[row_src[r]] if row_src is given (row ids outside [0, x_rows) read as zeros) else X[r].
  * experts is a DEVICE array of E qg_expert (all of format fmt, each [N][K]); seg_off is a DEVICE
  * int32 [E+1], non-decreasing, seg_off[0] >= 0, seg_off[E] <= R (rows outside every segment are
- * not written).  QG_EXACT: X f32 / f16 / bf16, f32 arithmetic (f32 FMA when R <= 8 E, i.e. short
- * segments; the f32 MFMA tile kernel otherwise).  QG_FAST: X f16 or bf16 (for f32 rows, first run
- * qg_x_half and pass its Xh and rs), f16 / bf16 MFMA.  Y f32 [R][N].  QG_ESHAPE also when a
- * tile-kernel launch (QG_FAST, or QG_EXACT with R > 8 E) would need more than 65535 row tiles
- * ((R + 31) / 32 + min(E, R)). */
+ * not written).  Kernels: short segments (R <= 8 E) stream each expert's weight rows once through
+ * the expert-row kernel when K <= 2048 (Q4, Q4A) or 1024 (Q8), else through the K-split GEMV
+ * (exact mode) or the MFMA tile kernel (fast mode); R > 8 E takes the MFMA tile kernel of the mode.
+ * QG_EXACT: X f32 / f16 / bf16, f32 arithmetic throughout.  QG_FAST: X f16 or bf16 -- the tile
+ * kernel rounds the decoded weights to that type for f16 / bf16 MFMA; the expert-row kernel keeps
+ * them exact (f16 X: the codes as exact f16 pairs through v_dot2 into an f32 partial per block,
+ * scaled by the block scale; bf16 X: f32 arithmetic).  QG_FAST with f32 X (any R, K within the
+ * expert-row kernel's limit, else QG_EUNSUPPORTED): each gathered row is scaled to f16 inside that
+ * kernel exactly as qg_x_half does and the inverse scale multiplies the outputs (times rs when
+ * given); for R <= 8 E, where the f16 call takes the same kernel, the result equals qg_x_half
+ * followed by the f16 call bit for bit.  Y f32 [R][N].
+ * QG_ESHAPE also when a tile-kernel launch (QG_FAST, or QG_EXACT with R > 8 E) would need more than
+ * 65535 row tiles ((R + 31) / 32 + min(E, R)). */
 qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group,
                             const int32_t* seg_off, const int32_t* row_src, int x_rows,
                             const void* X, qg_xtype xt, const float* rs, float* Y, int N, int K,
@@ -238,7 +246,12 @@ size_t qg_moe_ffn_workspace(int H, int I, int T, int k, qg_mode mode);
 
 /* The whole expert block on the stream (page section Backend::moe): [fast: qg_x_half gather] ->
  * grouped gate|up ([2I][H] per expert) -> qg_swiglu -> grouped down ([H][I] per expert) ->
- * qg_moe_combine into Y f32 [T][H] (accumulate as above).  gate_up / down are DEVICE arrays of E
+ * qg_moe_combine into Y f32 [T][H] (accumulate as above).  With short segments (T k <= 8 E) and
+ * H, I within the expert-row kernel's K limit (qgemm_moe_grouped) this runs as three launches: the
+ * gate|up matmul with SwiGLU in its epilogue (A f32; fast mode scales X rows to f16 inside it),
+ * the down matmul (fast mode scales the rows of A to f16 inside it, as qg_swiglu's f16 output
+ * would be), and the combine -- the same results as the separate calls (qgemm_moe_grouped from f32
+ * rows, qg_swiglu to f32, qgemm_moe_grouped, qg_moe_combine) bit for bit.  gate_up / down are DEVICE arrays of E
  * experts of format fmt; seg_off, row_src, slot_row, slot_w are the device copies of a plan
  * (qg_moe_plan_host) for these T tokens and k slots; X f32 [T][H].  The workspace (device,
  * 256-byte aligned) holds the intermediates; QG_EWORKSPACE if ws_bytes is too small. */

@@ -76,9 +76,13 @@ def test_dump_and_moe_validation_codes():
     assert L.qg_dequant_dump(0, A16, A16b, None, 64, 64, 128, 60, 0, 8, 32, 0, A16c, None) == qg.QG_ESHAPE
     assert L.qg_dequant_dump(0, A16, A16b, None, 64, 64, 128, 0, 96, 1, 64, 0, A16c, None) == qg.QG_ESHAPE
     assert L.qg_dequant_dump(3, A16, A16b, None, 64, 64, 128, 0, 0, 1, 32, 0, A16c, None) == qg.QG_EINVAL
-    # grouped: fast mode needs 16-bit X; E >= 1
-    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 512, 8, 4, 1, None) == \
+    # grouped: fast mode with f32 X only where the expert-row kernel scales the rows itself (K <= 2048
+    # for Q4 / Q4A, 1024 for Q8); E >= 1
+    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 2080, 8, 4, 1, None) == \
         qg.QG_EUNSUPPORTED
+    assert L.qgemm_moe_grouped(2, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 1056, 8, 4, 1, None) == \
+        qg.QG_EUNSUPPORTED
+    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 512, 0, 4, 1, None) == qg.QG_OK
     assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 8, 0, 1, None) == \
         qg.QG_ESHAPE
     assert L.qgemm_moe_grouped(0, None, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 8, 4, 1, None) == \
