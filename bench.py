@@ -10,7 +10,8 @@ torch.cuda.synchronize(); HIP events on the launch stream time it.  Each step is
 of the C entry point (arguments marshalled beforehand), so the host side keeps ahead of the GPU.
 `roofline` relates the dominant kernel's achieved rate to the chip's peak; `cpu_baseline` times the
 CPU oracle on the host cores.
-`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak), the MoE expert block (GB/s), the GGUF
+`also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak; the Q8 prefill shape in both fast modes,
+weights rounded to f16 and kept exact), the MoE expert block (GB/s), the GGUF
 Q4_0 repack of a 4096 x 4096 matrix (GB/s), a batched q / k / v decode step (GB/s, with the time
 of the same three matrices as separate calls) and the Q8 GEMV with T = 4 (GB/s), each on
 its own synthetic workload; `--workload` selects one of them as the headline instead.
@@ -268,6 +269,30 @@ def measure_gemv_t(T: int, steps: int, warmup: int) -> dict:
             "bytes_per_step": nbytes}
 
 
+def measure_q8_prefill(mode: str, steps: int, warmup: int) -> dict:
+    """The prefill GEMM shape with Q8 weights (N = K = 4096, T = 512, f16 X N(0, 0.5)) in the two
+    fast modes: "fast" rounds each decoded weight q d to f16; "fast_wexact" keeps the codes exact in
+    f16 and applies the f32 block scale to each 32-k block's f32 partial.  TFLOP/s vs the f16 MFMA
+    peak."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    N = K = 4096
+    T = 512
+    w = synth.make_dense("q8", N, K, T, "f16", 0.5, 1402)
+    C_, S_ = _dev(w["codes"]), _dev(w["scales"])
+    X = _dev(w["X"])
+    Y = torch.empty((T, N), device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    step = _bound("qgemm_q8", C_.data_ptr(), S_.data_ptr(), X.data_ptr(), qg.QG_X_F16, Y.data_ptr(), N, K, T,
+                  qg.MODE[mode], st)
+    ms, _ = _timed(step, steps, warmup)
+    tf = 2.0 * T * N * K / (ms * 1e-3) / 1e12
+    return {"workload": f"q8_prefill_{mode}", "config": "q8_prefill_N4096_K4096_T512", "mode": mode,
+            "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f16", "kernel": "gemm_fast_ring_kernel",
+            "value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK["f16"], "frac": tf / PEAK["f16"]}
+
+
 def measure_repack(steps: int, warmup: int) -> dict:
     """GGUF Q4_0 -> split-layout repack of a 4096 x 4096 matrix (an upload-time step): GB/s of the
     bytes it reads (18 per block) and writes (16 code bytes and a 2-byte scale per block)."""
@@ -455,6 +480,9 @@ def main():
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         r = measure_gemv_t(4, 512, 50)
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        for mode in ("fast", "fast_wexact"):
+            r = measure_q8_prefill(mode, 128, 20)
+            also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
     c = info["cfg"]
     line = {
         "metric": "TFLOP/s (prefill qgemm) & HBM GB/s (T=1 qgemv), as % of MI355X roofline",

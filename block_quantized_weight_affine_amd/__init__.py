@@ -22,11 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 QG_OK, QG_EINVAL, QG_EALIGN, QG_ESHAPE, QG_EUNSUPPORTED, QG_ELAUNCH, QG_EPLAN, QG_EWORKSPACE, QG_ESCRATCH = range(9)
 QG_NOALLOC_SCRATCH_BYTES = 16 << 20
 QG_X_F32, QG_X_F16, QG_X_BF16 = 0, 1, 2
-QG_EXACT, QG_FAST = 0, 1
+QG_EXACT, QG_FAST, QG_FAST_WEXACT = 0, 1, 2
 QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8 = 0, 1, 2
 
 FMT = {"q4": QG_FMT_Q4, "q4a": QG_FMT_Q4A, "q8": QG_FMT_Q8}
-MODE = {"exact": QG_EXACT, "fast": QG_FAST}
+MODE = {"exact": QG_EXACT, "fast": QG_FAST, "fast_wexact": QG_FAST_WEXACT}
 
 # exported symbols of include/qgemm.h, in declaration order
 SYMBOLS = [

@@ -21,7 +21,7 @@ constexpr int kMaxGridY = 65535;
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8; }
 bool xt_ok(int x) { return x == QG_X_F32 || x == QG_X_F16 || x == QG_X_BF16; }
-bool mode_ok(int m) { return m == QG_EXACT || m == QG_FAST; }
+bool mode_ok(int m) { return m == QG_EXACT || m == QG_FAST || m == QG_FAST_WEXACT; }
 size_t scale_bytes(int fmt) { return fmt == QG_FMT_Q8 ? 4 : 2; }
 
 // Shared checks of the dense matmul / GEMV entry points.
@@ -64,8 +64,10 @@ qg_status run_dense(int fmt, const void* codes, const void* scales, const uint16
     if (gemv_only && T > 8) return QG_ESHAPE;
     if (T == 0) return QG_OK;
     GemmParams p = dense_params(codes, scales, offs, group, X, Y, N, K, T);
+    if (mode == QG_FAST_WEXACT && (fmt == QG_FMT_Q4A || xt != QG_X_F16)) return QG_EUNSUPPORTED;
     if (T <= 8) return launched(qg::launch_gemv(fmt, xt, p, false, s));
     if (mode == QG_EXACT) return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
+    if (mode == QG_FAST_WEXACT) return launched(qg::launch_gemm_fast_wexact(fmt, p, s));
     if (xt == QG_X_F32) return QG_EUNSUPPORTED;
     return launched(qg::launch_gemm_fast(fmt, xt, p, false, s));
 }
@@ -190,6 +192,7 @@ qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const
     }
     if (T == 0) return QG_OK;
     if (T > 8 && mode == QG_FAST && xt == QG_X_F32) return QG_EUNSUPPORTED;
+    if (mode == QG_FAST_WEXACT && (fmt == QG_FMT_Q4A || xt != QG_X_F16)) return QG_EUNSUPPORTED;
     if (T == 1) {
         bool all = true;
         for (int j0 = 0; j0 < J && all; j0 += qg::kMaxBatchJobs) {
@@ -264,6 +267,7 @@ qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, 
                             const int32_t* row_src, int x_rows, const void* X, qg_xtype xt, const float* rs,
                             float* Y, int N, int K, int R, int E, qg_mode mode, hipStream_t stream) {
     if (!fmt_ok(fmt) || !xt_ok(xt) || !mode_ok(mode)) return QG_EINVAL;
+    if (mode == QG_FAST_WEXACT) return QG_EUNSUPPORTED;
     if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || R < 0 || R > kMaxT || E < 1 ||
         E > kMaxGridY || x_rows < 0)
         return QG_ESHAPE;
@@ -345,6 +349,7 @@ qg_status check_ffn(int fmt, const qg_expert* gate_up, const qg_expert* down, in
                     const float* X, int T, int k, const int32_t* seg_off, const int32_t* row_src,
                     const int32_t* slot_row, const float* slot_w, const float* Y, int mode) {
     if (!fmt_ok(fmt) || !mode_ok(mode)) return QG_EINVAL;
+    if (mode == QG_FAST_WEXACT) return QG_EUNSUPPORTED;
     if (E < 1 || E > kMaxGridY || H < 32 || (H % 32) != 0 || H > kMaxK || I < 32 || (I % 32) != 0 || I > kMaxK ||
         T < 0 || T > kMaxGridY || k < 1 || k > E || (int64_t)T * k > kMaxT)
         return QG_ESHAPE;

@@ -388,6 +388,32 @@ __device__ __forceinline__ void x_load8(const void* X, size_t i, float (&v)[8]) 
     }
 }
 
+// Eight codes of a fragment as exact f16 (the W-exact fast path): c holds 8 code bytes, Q4 a nibble
+// per byte (0..15), Q8 q + 128 (the byte with its top bit flipped).  A byte b becomes the f16
+// 1024 + b by a byte permutation into 0x64.., then 1024 + 8 (Q4) or 1024 + 128 (Q8) is subtracted
+// in f16, exactly: nibble - 8 and q are small integers, exact in f16.
+template <int FMT>
+__device__ __forceinline__ short8_t frag16_codes(const uint32_t (&c)[2]) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t off = FMT == FMT_Q8 ? (h2_t){(_Float16)1152.0f, (_Float16)1152.0f}
+                                   : (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, c[j], 0x04010400u)) - off;
+        const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, c[j], 0x04030402u)) - off;
+        w[2 * j] = __builtin_bit_cast(uint32_t, lo);
+        w[2 * j + 1] = __builtin_bit_cast(uint32_t, hi);
+    }
+    short8_t r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        r[2 * j] = (short)(w[j] & 0xFFFFu);
+        r[2 * j + 1] = (short)(w[j] >> 16);
+    }
+    return r;
+}
+
 // ---- wavefront helpers ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

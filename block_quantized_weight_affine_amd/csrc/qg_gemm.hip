@@ -685,8 +685,14 @@ __device__ __forceinline__ uint8_t* ring_slot() {
     return b;
 }
 
-template <int FMT, int ST, int WM, int MT, int MN, int D>
+// WX (W-exact, Q4 and Q8 with f16 X): the fragments hold the codes themselves as exact f16 (Q4
+// nibble - 8, Q8 q), each 32-k block's two MFMA steps accumulate into a block partial from zero,
+// and the block scale of the fragment's weight row (every accumulator of a lane belongs to the
+// lane's column, one weight row) multiplies the partial into the accumulator in f32: the weights are
+// never rounded.
+template <int FMT, int ST, int WM, int MT, int MN, int D, bool WX = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams p) {
+    static_assert(!WX || (FMT != FMT_Q4A && ST == XT_F16), "W-exact: Q4 / Q8 codes, f16 X");
     constexpr int NW = 4;                       // wavefronts
     constexpr int WN = 4 / WM;
     constexpr int BT = 32 * MT * WM;
@@ -818,6 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
         const uint8_t* const wsb = wsl(uc);
         constexpr int NSTEP = 4;
         short8_t A[2][MT], B[2][MN];
+        f32x16_t part[MT][MN];  // WX: the current block's partial
         uint2 raw[2][MN];
         auto decode = [&](int q, const uint2 (&rw)[MN], short8_t (&Bo)[MN]) __attribute__((always_inline)) {
             const int b = q >> 1;
@@ -834,7 +841,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
                     c[0] = keep_u32(rw[mn].x & 0x0F0F0F0Fu);
                     c[1] = keep_u32(rw[mn].y & 0x0F0F0F0Fu);
                 }
-                if constexpr (FAST) Bo[mn] = frag16_words<FMT, ST>(c, d[mn][b], dh[mn][b], c0[mn][b]);
+                if constexpr (WX) Bo[mn] = frag16_codes<FMT>(c);
+                else if constexpr (FAST) Bo[mn] = frag16_words<FMT, ST>(c, d[mn][b], dh[mn][b], c0[mn][b]);
                 else Bo[mn] = frag16_words_slow<FMT, ST>(c, d[mn][b], mm[mn][b]);
             }
         };
@@ -858,10 +866,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
                     if ((q & 1) && q + 1 < NSTEP) read_raw(q + 1, raw[0]);  // next block's chunk
                 }
             }
+            if constexpr (WX) {
+                // block q / 2: its partial from zero over its two steps, then scaled into acc
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
+                for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-                for (int mn = 0; mn < MN; mn++) mfma(A[cur][mt], B[cur][mn], acc[mt][mn]);
+                    for (int mn = 0; mn < MN; mn++) {
+                        if ((q & 1) == 0) {
+                            f32x16_t z;
+#pragma unroll
+                            for (int i = 0; i < 16; i++) z[i] = 0.f;
+                            part[mt][mn] = z;
+                        }
+                        mfma(A[cur][mt], B[cur][mn], part[mt][mn]);
+                        if (q & 1) {
+#pragma unroll
+                            for (int i = 0; i < 16; i++)
+                                acc[mt][mn][i] = fmaf(part[mt][mn][i], d[mn][q >> 1], acc[mt][mn][i]);
+                        }
+                    }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                    for (int mn = 0; mn < MN; mn++) mfma(A[cur][mt], B[cur][mn], acc[mt][mn]);
+            }
             if (q + 1 < NSTEP) {
                 if constexpr (FMT == FMT_Q8) decode(q + 1, raw[nx], B[nx]);
                 else decode(q + 1, raw[0], B[nx]);
@@ -899,7 +928,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
                 c0[mn][b] = block_c0<FMT>(rb, f);
                 if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) fast = fast && (f || !valid);
             }
-        if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
+        if constexpr (WX || (FMT == FMT_Q4 && ST == XT_F16)) {
             body(uc, std::true_type{}, s, d, c0, mm, dh);
         } else {
             if (__all(fast)) body(uc, std::true_type{}, s, d, c0, mm, dh);
@@ -1108,11 +1137,11 @@ static void fast_lds_launch(const GemmParams& p, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN, DP, GR>), grid, dim3(kThreads), 0, s, p);
 }
 
-template <int FMT, int ST, int WM, int MT, int MN, int D>
+template <int FMT, int ST, int WM, int MT, int MN, int D, bool WX = false>
 static void fast_ring_launch(const GemmParams& p, hipStream_t s) {
     constexpr int BT = 32 * MT * WM, BN = 32 * MN * (4 / WM);
     dim3 grid((p.N + BN - 1) / BN, (p.R + BT - 1) / BT);
-    hipLaunchKernelGGL((gemm_fast_ring_kernel<FMT, ST, WM, MT, MN, D>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_fast_ring_kernel<FMT, ST, WM, MT, MN, D, WX>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <int FMT, int ST>
@@ -1133,6 +1162,14 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     // 64 x 128 tiles: the raw-weight ring, wavefronts 1 x 4, six stages (Q4 prefill N = K = 4096,
     // T 512: 32.5 us against 40.1 for the decoded-tile kernel with the same tile)
     return fast_ring_launch<FMT, ST, 1, 2, 1, 6>(p, s);
+}
+
+hipError_t launch_gemm_fast_wexact(int fmt, const GemmParams& p, hipStream_t s) {
+    // 64 x 128 tiles of the raw-weight ring, whatever the shape
+    if (fmt == FMT_Q4) fast_ring_launch<FMT_Q4, XT_F16, 1, 2, 1, 6, true>(p, s);
+    else if (fmt == FMT_Q8) fast_ring_launch<FMT_Q8, XT_F16, 1, 2, 1, 6, true>(p, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s) {

@@ -48,6 +48,9 @@ struct BatchJobs {
 // Kernel launchers; each returns a hipError_t from hipGetLastError after the launch.
 hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s);
 hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
+// Dense fast matmul with the weights kept exact (Q4 / Q8 codes as f16, f16 X, block scale on the f32
+// block partial); hipErrorInvalidValue for another format.
+hipError_t launch_gemm_fast_wexact(int fmt, const GemmParams& p, hipStream_t s);
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
 // T = 1, K <= 16384: every job of bj in one launch (p.N = bj.start[bj.J]); false if not applicable.
 bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err);

@@ -66,7 +66,8 @@ typedef enum {
 } qg_status;
 
 typedef enum { QG_X_F32 = 0, QG_X_F16 = 1, QG_X_BF16 = 2 } qg_xtype;
-typedef enum { QG_EXACT = 0, QG_FAST = 1 } qg_mode;
+/* QG_FAST_WEXACT (dense matmuls only): the fast mode with the weights kept exact -- see below. */
+typedef enum { QG_EXACT = 0, QG_FAST = 1, QG_FAST_WEXACT = 2 } qg_mode;
 typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2 } qg_format;
 /* GGUF block types with the scale inside each block (the values are GGML's type ids). */
 typedef enum { QG_GGUF_Q4_0 = 2, QG_GGUF_Q8_0 = 8 } qg_gguf_type;
@@ -81,7 +82,14 @@ int qg_abi_version(void);
  * T <= 8 runs the wavefront-reduction GEMV (exact f32 arithmetic whatever the mode); larger T
  * runs the MFMA tile kernel of the mode.  QG_FAST needs X in f16 or bf16 (the MFMA operand
  * type); an f32 X in QG_FAST with T > 8 returns QG_EUNSUPPORTED (convert it with qg_x_half and
- * use qgemm_moe_grouped with one expert, or use QG_EXACT).
+ * use qgemm_moe_grouped with one expert, or use QG_EXACT).  QG_FAST stages each decoded weight
+ * rounded to the X type.  QG_FAST_WEXACT (Q4 and Q8, f16 X; else QG_EUNSUPPORTED) keeps the
+ * weights exact instead: the codes (Q4 nibble - 8, Q8 q) enter the f16 MFMA as exact f16 values,
+ * each 32-k block's products are summed into an f32 block partial, and the block scale multiplies
+ * that partial into the f32 result (page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", Pipes,
+ * the q8 pipelines: W exact in half, the scale on the f32 result -- a per-row scale there, constant
+ * over k; here the scale varies per 32-k block, so it is applied per block).  Only the rounding of
+ * X to f16 and the f32 sums remain.
  * Sources: oxinfer src/metal.rs, Backend::matmul (f32 GEMM) and matmul_mma (matrix-unit GEMM).
  */
 qg_status qgemm_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt,

@@ -64,6 +64,15 @@ def test_dense_validation_codes():
     assert L.qgemm_q4a(A16, A16b, None, 64, A16c, 0, A16d, 256, 512, 16, 0, None) == qg.QG_EINVAL
     # q8 scales are f32: 4-byte alignment
     assert L.qgemm_q8(A16, A16b + 2, A16c, 0, A16d, 256, 512, 16, 0, None) == qg.QG_EALIGN
+    # the W-exact fast mode: Q4 and Q8 codes with f16 X only; not for grouped matmuls or the block
+    assert L.qgemm_q4a(A16, A16b, A16, 64, A16c, 1, A16d, 256, 512, 16, qg.QG_FAST_WEXACT, None) == \
+        qg.QG_EUNSUPPORTED
+    assert L.qgemm_q8(A16, A16b, A16c, 0, A16d, 256, 512, 16, qg.QG_FAST_WEXACT, None) == qg.QG_EUNSUPPORTED
+    assert L.qgemm_q8(A16, A16b, A16c, 2, A16d, 256, 512, 16, qg.QG_FAST_WEXACT, None) == qg.QG_EUNSUPPORTED
+    assert L.qgemm_q4(A16, A16b, A16c, 1, A16d, 256, 512, 0, qg.QG_FAST_WEXACT, None) == qg.QG_OK
+    assert L.qgemm_q4(A16, A16b, A16c, 1, A16d, 256, 512, 16, 3, None) == qg.QG_EINVAL
+    assert L.qgemm_moe_grouped(0, A16, 64, A16b, None, 8, A16c, 1, None, A16d, 256, 512, 8, 4,
+                               qg.QG_FAST_WEXACT, None) == qg.QG_EUNSUPPORTED
     # GEMV takes at most 8 rows
     assert L.qgemv_q8(A16, A16b, A16c, 0, A16d, 256, 512, 9, None) == qg.QG_ESHAPE
     assert L.qgemv_q4(A16, A16b, A16c, 0, A16d, 256, 512, 0, None) == qg.QG_OK
@@ -102,6 +111,8 @@ def test_dump_and_moe_validation_codes():
                         0x100000, ws - 1, None) == qg.QG_EWORKSPACE
     assert L.qg_moe_ffn(0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d, 0, 1,
                         0x100010, ws, None) == qg.QG_EALIGN
+    assert L.qg_moe_ffn(0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d, 0,
+                        qg.QG_FAST_WEXACT, 0x100000, ws, None) == qg.QG_EUNSUPPORTED
 
 
 def test_batch_validation_codes():
