@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT = {"q4": 0, "q4a": 1, "q8": 2}
+FMT = {"q4": 0, "q4a": 1, "q8": 2, "q8a": 3}
 XT = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 
 _p = C.c_void_p
@@ -63,6 +63,8 @@ def lib():
         L.orc_gguf_dequant.argtypes = [_i, _p, _i, _i, _p]
         L.orc_gguf_repack.restype = None
         L.orc_gguf_repack.argtypes = [_i, _p, _i, _i, _p, _p]
+        L.orc_gguf_repack_q8a.restype = None
+        L.orc_gguf_repack_q8a.argtypes = [_i, _p, _i, _i, _p, _p, _p]
         L.orc_gemm.restype = _i
         L.orc_gemm.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _i, _p, _p, _i]
         L.orc_x_half.restype = None
@@ -99,6 +101,8 @@ def _c(a, dtype):
 def _weights(fmt, codes, scales, offsets):
     if fmt == "q8":
         return _c(codes, np.int8), _c(scales, np.float32), None
+    if fmt == "q8a":
+        return _c(codes, np.int8), _c(scales, np.float32), _c(offsets, np.float32)
     return _c(codes, np.uint8), _c(scales, np.uint16), (_c(offsets, np.uint16) if fmt == "q4a" else None)
 
 
@@ -264,9 +268,10 @@ def moe_ffn(m: dict, plan: dict, fmt: str = "q4", group: int = 64, threads=None)
     return {"y": y, "b_dn": bdn, "b_gu": bgu, "GU": GU, "A": A, "O": O}
 
 
-# ---- GGUF blocks with in-block scales (Q4_0 = 2, Q8_0 = 8) ----------------------------------------
-GGUF = {"q4_0": 2, "q8_0": 8}
-GGUF_BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+# ---- GGUF blocks with in-block scales (GGML type ids) -------------------------------------------
+GGUF = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12}
+# bytes per 32 elements (Q4_K: 144 per 256)
+GGUF_BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24, "q8_0": 34, "q4_k": 18}
 
 
 def gguf_dequant(gtype, src, N, K) -> np.ndarray:
@@ -289,3 +294,14 @@ def gguf_repack(gtype, src, N, K) -> tuple:
         scales = np.empty(N * K // 32, np.float32)
     lib().orc_gguf_repack(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales))
     return (codes if gtype == "q4_0" else codes.view(np.int8)), scales
+
+
+def gguf_repack_q8a(gtype, src, N, K) -> tuple:
+    """(codes int8 [N*K], scales f32 [N*K/32], offsets f32 [N*K/32]) of the Q8A layout for the
+    affine types Q4_1, Q5_0, Q5_1 and Q4_K."""
+    b = _c(src, np.uint8)
+    codes = np.empty(N * K, np.int8)
+    scales = np.empty(N * K // 32, np.float32)
+    offs = np.empty(N * K // 32, np.float32)
+    lib().orc_gguf_repack_q8a(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales), _ptr(offs))
+    return codes, scales, offs

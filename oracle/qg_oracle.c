@@ -17,6 +17,10 @@
  *     n*(K/group) + floor(k/group), is added (in f32) to every element of the group.
  *   - Q8, SHADER_SRC (struct Q8W, load(Q8W)): int8 code at n*K + k, f32 scale of the
  *     32-element block at n*K/32 + floor(k/32); value = float(q) * scale in f32.
+ *   - Q8A (the split layout the affine GGUF blocks below are repacked into): Q8 plus an f32
+ *     offset m of the block at n*K/32 + floor(k/32); value = (float(q) * scale) + m in f32, two
+ *     roundings as written (the GGUF sources make the product exact, so their single rounding
+ *     at the add is the same).
  *   - Fast-mode staging, MMA_SHADER_SRC (mma_tile): the f32 value is converted to a 16-bit
  *     float as it is written to the tile (round to nearest, ties to even).
  *   - Row scaling to f16, MMA_SHADER_SRC (row_scale, x_half): per row, amax; frexp exponent
@@ -40,7 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_Q4 = 0, ORC_Q4A = 1, ORC_Q8 = 2 };
+enum { ORC_Q4 = 0, ORC_Q4A = 1, ORC_Q8 = 2, ORC_Q8A = 3 };
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_F64 = 3 };
 
 /* ---------------------------------------------------------------------------------------
@@ -136,9 +140,11 @@ double orc_weight_exact(int fmt, const void* codes, const void* scales, const ui
                         int N, int K, int n, int k) {
     (void)N;
     size_t bi = (size_t)n * (K / 32) + k / 32;
-    if (fmt == ORC_Q8) {
+    if (fmt == ORC_Q8 || fmt == ORC_Q8A) {
         int q = ((const int8_t*)codes)[(size_t)n * K + k];
-        return (double)q * (double)((const float*)scales)[bi];
+        double v = (double)q * (double)((const float*)scales)[bi];
+        if (fmt == ORC_Q8A) v += (double)((const float*)(const void*)offs)[bi];
+        return v;
     }
     int nib = q4_nibble((const uint8_t*)codes, K, n, k);
     double v = (double)(nib - 8) * orc_f16_value(((const uint16_t*)scales)[bi]);
@@ -151,10 +157,14 @@ float orc_weight_f32(int fmt, const void* codes, const void* scales, const uint1
                      int N, int K, int n, int k) {
     (void)N;
     size_t bi = (size_t)n * (K / 32) + k / 32;
-    if (fmt == ORC_Q8) {
+    if (fmt == ORC_Q8 || fmt == ORC_Q8A) {
         int q = ((const int8_t*)codes)[(size_t)n * K + k];
         float d = ((const float*)scales)[bi];
         float v = (float)q * d;
+        if (fmt == ORC_Q8A) {
+            float m = ((const float*)(const void*)offs)[bi];
+            v = v + m;
+        }
         return v;
     }
     int nib = q4_nibble((const uint8_t*)codes, K, n, k);
@@ -375,33 +385,127 @@ void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uin
 }
 
 /* ---------------------------------------------------------------------------------------
- * GGUF blocks with the scale inside the block (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC,
- * the GGUF dequantizers Q4_0W and Q8_0W): a row is K/32 consecutive blocks.
- *   Q4_0: 18 bytes = f16 scale d (little-endian), then 16 bytes; byte j holds element j in its
- *         low nibble and element j + 16 in its high nibble; value = (nibble - 8) * d in f32.
- *   Q8_0: 34 bytes = f16 scale d, then 32 signed bytes q; value = float(q) * d in f32.
- * Type ids: 2 = Q4_0, 8 = Q8_0.
+ * GGUF blocks with the scale inside the block (page "oxinfer 0.0.5 src/metal.rs",
+ * GGUF_SHADER_SRC: the loaders Q4_0W, Q8_0W, Q4_1W / Q5_0W / Q5_1W (load_q45) and Q4_KW with
+ * scale_min_k4).  Multi-byte fields are little-endian; h = an f16 field as f32.
+ *   Q4_0 (type 2): 18 bytes per 32 elements = h d, then 16 bytes; byte j holds element j in its
+ *         low nibble and element j + 16 in its high nibble; value = (nibble - 8) * d.
+ *   Q8_0 (type 8): 34 bytes = h d, then 32 signed bytes q; value = float(q) * d.
+ *   Q4_1 (type 3): 20 bytes = h d, h m, 16 nibble bytes as Q4_0; value = nibble * d + m.
+ *   Q5_0 (type 6): 22 bytes = h d, a 32-bit word qh, 16 nibble bytes; element j's code is its
+ *         nibble + 16 * bit j of qh; value = (code - 16) * d + 0.
+ *   Q5_1 (type 7): 24 bytes = h d, h m, qh, 16 nibble bytes; value = code * d + m.
+ *   Q4_K (type 12): 144 bytes per 256 elements = h d, h dmin, 12 scale bytes s, 128 code bytes.
+ *         Sub-block j (elements 32 j .. 32 j + 31) has a 6-bit scale sc and min mn:
+ *         j < 4: sc = s[j] & 63, mn = s[j + 4] & 63; j >= 4: sc = (s[j + 4] & 15) | ((s[j - 4] >> 6)
+ *         << 4), mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4).  d1 = d * sc, m1 = dmin * mn (f32);
+ *         element e of sub-block j is nibble (j % 2 ? high : low) of code byte 32 (j / 2) + e;
+ *         value = nibble * d1 - m1.
+ * Every value is evaluated in f32 in the order written.  A row holds K / 32 blocks (K / 256
+ * super-blocks for Q4_K).
  */
 #define ORC_GGUF_Q4_0 2
+#define ORC_GGUF_Q4_1 3
+#define ORC_GGUF_Q5_0 6
+#define ORC_GGUF_Q5_1 7
 #define ORC_GGUF_Q8_0 8
+#define ORC_GGUF_Q4_K 12
 
-static size_t gguf_block_bytes(int type) { return type == ORC_GGUF_Q4_0 ? 18 : 34; }
+/* Bytes of one row of K elements. */
+static size_t gguf_row_bytes(int type, int K) {
+    switch (type) {
+    case ORC_GGUF_Q4_0: return (size_t)(K / 32) * 18;
+    case ORC_GGUF_Q4_1: return (size_t)(K / 32) * 20;
+    case ORC_GGUF_Q5_0: return (size_t)(K / 32) * 22;
+    case ORC_GGUF_Q5_1: return (size_t)(K / 32) * 24;
+    case ORC_GGUF_Q8_0: return (size_t)(K / 32) * 34;
+    default: return (size_t)(K / 256) * 144;
+    }
+}
 
-/* The f32 value of element (n, k), read from the GGUF bytes. */
-float orc_gguf_weight_f32(int type, const uint8_t* src, int K, int n, int k) {
-    const uint8_t* B = src + (size_t)n * (K / 32) * gguf_block_bytes(type) + (size_t)(k / 32) * gguf_block_bytes(type);
-    uint16_t dh = (uint16_t)(B[0] | (B[1] << 8));
-    float d = (float)orc_f16_value(dh);
+static float gguf_h(const uint8_t* p) { return (float)orc_f16_value((uint16_t)(p[0] | (p[1] << 8))); }
+
+/* Q4_K: the 6-bit scale and min of sub-block j from the 12 scale bytes. */
+static void gguf_k4_scale_min(int j, const uint8_t* s, int* sc, int* mn) {
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *mn = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* The integer code, f32 scale and f32 offset of element (n, k): value = code * scale + offset
+ * in the types' own evaluation order (see gguf_value). */
+static void gguf_element(int type, const uint8_t* src, int K, int n, int k, int* code, float* d, float* m) {
+    const uint8_t* row = src + (size_t)n * gguf_row_bytes(type, K);
     int j = k % 32;
-    if (type == ORC_GGUF_Q4_0) {
-        uint8_t byte = B[2 + (j % 16)];
-        int nib = j < 16 ? (byte & 0xF) : (byte >> 4);
-        float v = (float)(nib - 8) * d;
+    if (type == ORC_GGUF_Q4_K) {
+        const uint8_t* SB = row + (size_t)(k / 256) * 144;
+        int sub = (k % 256) / 32, sc, mn;
+        gguf_k4_scale_min(sub, SB + 4, &sc, &mn);
+        float d1 = gguf_h(SB) * (float)sc;
+        float m1 = gguf_h(SB + 2) * (float)mn;
+        uint8_t byte = SB[16 + 32 * (sub / 2) + j];
+        *code = (sub % 2) ? (byte >> 4) : (byte & 15);
+        *d = d1;
+        *m = m1;
+        return;
+    }
+    int minb = type == ORC_GGUF_Q4_1 || type == ORC_GGUF_Q5_1;
+    int hib = type == ORC_GGUF_Q5_0 || type == ORC_GGUF_Q5_1;
+    size_t bb = gguf_row_bytes(type, 32);
+    const uint8_t* B = row + (size_t)(k / 32) * bb;
+    if (type == ORC_GGUF_Q8_0) {
+        *code = (int8_t)B[2 + j];
+        *d = gguf_h(B);
+        *m = 0.0f;
+        return;
+    }
+    *d = gguf_h(B);
+    *m = minb ? gguf_h(B + 2) : 0.0f;
+    const uint8_t* qs = B + 2 + (minb ? 2 : 0) + (hib ? 4 : 0);
+    uint8_t byte = qs[j % 16];
+    int nib = j < 16 ? (byte & 15) : (byte >> 4);
+    if (hib) {
+        const uint8_t* h = B + 2 + (minb ? 2 : 0);
+        uint32_t qh = (uint32_t)h[0] | ((uint32_t)h[1] << 8) | ((uint32_t)h[2] << 16) | ((uint32_t)h[3] << 24);
+        nib += 16 * (int)((qh >> j) & 1);
+    }
+    *code = nib;
+}
+
+/* The f32 value of element (n, k), as the type's loader evaluates it. */
+float orc_gguf_weight_f32(int type, const uint8_t* src, int K, int n, int k) {
+    int code;
+    float d, m;
+    gguf_element(type, src, K, n, k, &code, &d, &m);
+    switch (type) {
+    case ORC_GGUF_Q4_0: {
+        float v = (float)(code - 8) * d;
         return v;
     }
-    int q = (int8_t)B[2 + j];
-    float v = (float)q * d;
-    return v;
+    case ORC_GGUF_Q8_0: {
+        float v = (float)code * d;
+        return v;
+    }
+    case ORC_GGUF_Q5_0: {
+        float p = (float)(code - 16) * d;
+        float v = p + m;
+        return v;
+    }
+    case ORC_GGUF_Q4_K: {
+        float p = (float)code * d;
+        float v = p - m;
+        return v;
+    }
+    default: { /* Q4_1, Q5_1 */
+        float p = (float)code * d;
+        float v = p + m;
+        return v;
+    }
+    }
 }
 
 void orc_gguf_dequant(int type, const uint8_t* src, int N, int K, float* out) {
@@ -413,7 +517,7 @@ void orc_gguf_dequant(int type, const uint8_t* src, int N, int K, float* out) {
  * block, unchanged) and f16 scales [N][K/32] (the block's 2 scale bytes); Q8_0 -> Q8 codes
  * [N][K] and f32 scales [N][K/32] (the f16 scale widened, exactly). */
 void orc_gguf_repack(int type, const uint8_t* src, int N, int K, uint8_t* codes, void* scales) {
-    size_t bb = gguf_block_bytes(type), nb = (size_t)K / 32;
+    size_t bb = gguf_row_bytes(type, 32), nb = (size_t)K / 32;
     for (int n = 0; n < N; n++)
         for (size_t b = 0; b < nb; b++) {
             const uint8_t* B = src + ((size_t)n * nb + b) * bb;
@@ -425,6 +529,23 @@ void orc_gguf_repack(int type, const uint8_t* src, int N, int K, uint8_t* codes,
                 for (int j = 0; j < 32; j++) codes[(size_t)n * K + 32 * b + j] = B[2 + j];
                 ((float*)scales)[(size_t)n * nb + b] = (float)orc_f16_value(dh);
             }
+        }
+}
+
+/* Q4_1, Q5_0, Q5_1, Q4_K -> the Q8A layout: int8 codes [N][K], f32 scales and f32 offsets
+ * [N][K/32], with q * scale + offset equal to the type's value: Q4_1 / Q5_1 (code, d, m);
+ * Q5_0 (code - 16, d, +0); Q4_K (code, d1, -m1) per 32-element sub-block. */
+void orc_gguf_repack_q8a(int type, const uint8_t* src, int N, int K, int8_t* codes, float* scales, float* offs) {
+    for (int n = 0; n < N; n++)
+        for (int k = 0; k < K; k++) {
+            int code;
+            float d, m;
+            gguf_element(type, src, K, n, k, &code, &d, &m);
+            size_t bi = (size_t)n * (K / 32) + k / 32;
+            if (type == ORC_GGUF_Q5_0) code -= 16;
+            codes[(size_t)n * K + k] = (int8_t)code;
+            scales[bi] = d;
+            offs[bi] = type == ORC_GGUF_Q4_K ? -m : m;
         }
 }
 

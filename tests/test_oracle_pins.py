@@ -580,3 +580,64 @@ def test_moe_chain_brute_force(orc):
     for t in range(T):
         want = sum(plan["slot_w"][t * k + j] * r["O"][plan["slot_row"][t * k + j]] for j in range(k))
         assert np.allclose(r["y"][t], want, rtol=1e-15, atol=0)
+
+
+# ---- affine GGUF blocks (oxinfer src/metal.rs, GGUF_SHADER_SRC: load_q45, Q4_KW / scale_min_k4) ---
+def _golden_affine():
+    with open(os.path.join(GOLD, "gguf_affine_blocks.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _expected_row(spec, n):
+    out = np.full(n, spec["default"], np.float64)
+    for key, v in spec.items():
+        if key != "default":
+            out[int(key)] = v
+    return out
+
+
+@pytest.mark.parametrize("case", _golden_affine(), ids=lambda c: c["name"])
+def test_gguf_affine_hand_blocks(orc, case):
+    """Q4_1, Q5_0, Q5_1 and Q4_K blocks worked by hand (tests/golden/gguf_affine_blocks.json): every
+    element's decoded value, and +0 (not -0) where the value is zero."""
+    src = np.frombuffer(bytes.fromhex("".join(case["fields_hex"])), np.uint8)
+    K = case["K"]
+    w = orc.gguf_dequant(case["type"], src, 1, K)[0].astype(np.float64)
+    if "expected" in case:
+        exp = _expected_row(case["expected"], K)
+    else:
+        exp = np.concatenate([_expected_row(s, 32) for s in case["expected_subblocks"]])
+    assert np.array_equal(w, exp), f"{case['name']}: first mismatch at {np.argmax(w != exp)}"
+    assert not np.any(np.signbit(w) & (w == 0)), "a zero value came out as -0"
+
+
+@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k"])
+def test_gguf_affine_repack_matches_direct_decode(orc, gtype):
+    """The Q8A repack (int8 code, f32 scale, f32 offset per 32 elements), decoded by the Q8A decoder
+    (code * scale, then + offset), gives every element's GGUF value bit for bit -- random blocks with
+    negative scales and mins (the Q8A order of operations equals each type's)."""
+    rng = np.random.default_rng(17)
+    N, K = 3, 512
+    import synth
+    if gtype == "q4_k":
+        nsb = N * K // 256
+        src = rng.integers(0, 256, nsb * 144).astype(np.uint8).reshape(nsb, 144)
+        d = synth.f16_uniform(11, 1, nsb, -0.05, 0.05)
+        dm = synth.f16_uniform(12, 1, nsb, -0.05, 0.05)
+        src[:, 0], src[:, 1], src[:, 2], src[:, 3] = d & 0xFF, d >> 8, dm & 0xFF, dm >> 8
+    else:
+        nb = N * K // 32
+        bb = orc.GGUF_BLOCK_BYTES[gtype]
+        src = rng.integers(0, 256, nb * bb).astype(np.uint8).reshape(nb, bb)
+        d = synth.f16_uniform(11, 1, nb, -0.05, 0.05)
+        src[:, 0], src[:, 1] = d & 0xFF, d >> 8
+        if gtype in ("q4_1", "q5_1"):
+            m = synth.f16_uniform(12, 1, nb, -1.0, 1.0)
+            src[:, 2], src[:, 3] = m & 0xFF, m >> 8
+    src = src.reshape(-1)
+    direct = orc.gguf_dequant(gtype, src, N, K)
+    codes, scales, offs = orc.gguf_repack_q8a(gtype, src, N, K)
+    split = orc.dequant_tile("q8a", codes, scales, offs, 32, N, K, 0, 0, N, K, "f32")
+    assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
+    lo, hi = {"q4_1": (0, 15), "q5_0": (-16, 15), "q5_1": (0, 31), "q4_k": (0, 15)}[gtype]
+    assert codes.min() >= lo and codes.max() <= hi
