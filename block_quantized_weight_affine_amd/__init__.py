@@ -23,17 +23,17 @@ QG_OK, QG_EINVAL, QG_EALIGN, QG_ESHAPE, QG_EUNSUPPORTED, QG_ELAUNCH, QG_EPLAN, Q
 QG_NOALLOC_SCRATCH_BYTES = 16 << 20
 QG_X_F32, QG_X_F16, QG_X_BF16 = 0, 1, 2
 QG_EXACT, QG_FAST, QG_FAST_WEXACT = 0, 1, 2
-QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8 = 0, 1, 2
+QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8, QG_FMT_Q8A = 0, 1, 2, 3
 
-FMT = {"q4": QG_FMT_Q4, "q4a": QG_FMT_Q4A, "q8": QG_FMT_Q8}
+FMT = {"q4": QG_FMT_Q4, "q4a": QG_FMT_Q4A, "q8": QG_FMT_Q8, "q8a": QG_FMT_Q8A}
 MODE = {"exact": QG_EXACT, "fast": QG_FAST, "fast_wexact": QG_FAST_WEXACT}
 
 # exported symbols of include/qgemm.h, in declaration order
 SYMBOLS = [
     "qg_strerror", "qg_abi_version",
-    "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_batch",
-    "qgemv_q4", "qgemv_q4a", "qgemv_q8",
-    "qg_dequant_dump", "qg_repack_gguf",
+    "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_q8a", "qgemm_batch",
+    "qgemv_q4", "qgemv_q4a", "qgemv_q8", "qgemv_q8a",
+    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn", "qg_moe_ffn_noalloc",
 ]
@@ -69,6 +69,9 @@ def lib() -> C.CDLL:
         L.qgemv_q4.argtypes = sig_gemv
         L.qgemv_q8.argtypes = sig_gemv
         L.qgemv_q4a.argtypes = [_p, _p, _p, _i, _p, _i, _p, _i, _i, _i, _p]
+        L.qgemm_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _p]
+        L.qgemv_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _p]
+        L.qg_repack_gguf_q8a.argtypes = [_i, _p, _i, _i, _p, _p, _p, _p]
         L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
         L.qg_moe_plan_host.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
         L.qg_repack_gguf.argtypes = [_i, _p, _i, _i, _p, _p, _p]
@@ -148,6 +151,11 @@ def qgemm_q8(codes, scales, X, Y, N, K, T, mode="exact", xt=None, stream=None):
                           _mode(mode), _stream(stream)), "qgemm_q8")
 
 
+def qgemm_q8a(codes, scales, offsets, X, Y, N, K, T, mode="exact", xt=None, stream=None):
+    _check(lib().qgemm_q8a(_ptr(codes), _ptr(scales), _ptr(offsets), _ptr(X), _xt(X) if xt is None else xt,
+                           _ptr(Y), N, K, T, _mode(mode), _stream(stream)), "qgemm_q8a")
+
+
 def qgemv_q4(codes, scales, X, Y, N, K, T, xt=None, stream=None):
     _check(lib().qgemv_q4(_ptr(codes), _ptr(scales), _ptr(X), _xt(X) if xt is None else xt, _ptr(Y), N, K, T,
                           _stream(stream)), "qgemv_q4")
@@ -163,12 +171,19 @@ def qgemv_q8(codes, scales, X, Y, N, K, T, xt=None, stream=None):
                           _stream(stream)), "qgemv_q8")
 
 
+def qgemv_q8a(codes, scales, offsets, X, Y, N, K, T, xt=None, stream=None):
+    _check(lib().qgemv_q8a(_ptr(codes), _ptr(scales), _ptr(offsets), _ptr(X), _xt(X) if xt is None else xt,
+                           _ptr(Y), N, K, T, _stream(stream)), "qgemv_q8a")
+
+
 def qgemm(fmt, codes, scales, offsets, group, X, Y, N, K, T, mode="exact", stream=None):
-    """Dispatch by format name: 'q4' | 'q4a' | 'q8'."""
+    """Dispatch by format name: 'q4' | 'q4a' | 'q8' | 'q8a'."""
     if fmt == "q4":
         return qgemm_q4(codes, scales, X, Y, N, K, T, mode, stream=stream)
     if fmt == "q4a":
         return qgemm_q4a(codes, scales, offsets, group, X, Y, N, K, T, mode, stream=stream)
+    if fmt == "q8a":
+        return qgemm_q8a(codes, scales, offsets, X, Y, N, K, T, mode, stream=stream)
     return qgemm_q8(codes, scales, X, Y, N, K, T, mode, stream=stream)
 
 
@@ -177,6 +192,8 @@ def qgemv(fmt, codes, scales, offsets, group, X, Y, N, K, T, stream=None):
         return qgemv_q4(codes, scales, X, Y, N, K, T, stream=stream)
     if fmt == "q4a":
         return qgemv_q4a(codes, scales, offsets, group, X, Y, N, K, T, stream=stream)
+    if fmt == "q8a":
+        return qgemv_q8a(codes, scales, offsets, X, Y, N, K, T, stream=stream)
     return qgemv_q8(codes, scales, X, Y, N, K, T, stream=stream)
 
 
@@ -207,14 +224,23 @@ def qgemm_batch(fmt, group, jobs, X, K, T, mode="exact", xt=None, stream=None):
                              _ptr(X), _xt(X) if xt is None else xt, K, T, _mode(mode), _stream(stream)), "qgemm_batch")
 
 
-QG_GGUF_Q4_0, QG_GGUF_Q8_0 = 2, 8
-GGUF = {"q4_0": QG_GGUF_Q4_0, "q8_0": QG_GGUF_Q8_0}
+QG_GGUF_Q4_0, QG_GGUF_Q4_1, QG_GGUF_Q5_0, QG_GGUF_Q5_1, QG_GGUF_Q8_0, QG_GGUF_Q4_K = 2, 3, 6, 7, 8, 12
+GGUF = {"q4_0": QG_GGUF_Q4_0, "q4_1": QG_GGUF_Q4_1, "q5_0": QG_GGUF_Q5_0, "q5_1": QG_GGUF_Q5_1,
+        "q8_0": QG_GGUF_Q8_0, "q4_k": QG_GGUF_Q4_K}
 
 
 def qg_repack_gguf(gtype, src, N, K, codes, scales, stream=None):
     """GGUF Q4_0 / Q8_0 blocks (device uint8 tensor) -> this library's codes and scales (device)."""
     _check(lib().qg_repack_gguf(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K, _ptr(codes),
                                 _ptr(scales), _stream(stream)), "qg_repack_gguf")
+
+
+def qg_repack_gguf_q8a(gtype, src, N, K, codes, scales, offsets, stream=None):
+    """GGUF Q4_1 / Q5_0 / Q5_1 / Q4_K blocks (device uint8 tensor) -> Q8A codes (int8 [N*K]), f32
+    scales and f32 offsets ([N*K/32]), all device tensors."""
+    _check(lib().qg_repack_gguf_q8a(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K,
+                                    _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)),
+           "qg_repack_gguf_q8a")
 
 
 # ---- MoE ----------------------------------------------------------------------------------------

@@ -19,10 +19,15 @@ constexpr int kMaxT = 1 << 21;
 constexpr int kMaxGridY = 65535;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-bool fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8; }
+bool fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8 || f == QG_FMT_Q8A; }
+// formats of the grouped (MoE) entry points
+bool grouped_fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8; }
+// formats with per-block offsets, and the alignment of those offsets
+bool has_offs(int f) { return f == QG_FMT_Q4A || f == QG_FMT_Q8A; }
+size_t offs_bytes(int f) { return f == QG_FMT_Q8A ? 4 : 2; }
 bool xt_ok(int x) { return x == QG_X_F32 || x == QG_X_F16 || x == QG_X_BF16; }
 bool mode_ok(int m) { return m == QG_EXACT || m == QG_FAST || m == QG_FAST_WEXACT; }
-size_t scale_bytes(int fmt) { return fmt == QG_FMT_Q8 ? 4 : 2; }
+size_t scale_bytes(int fmt) { return fmt == QG_FMT_Q8 || fmt == QG_FMT_Q8A ? 4 : 2; }
 
 // Shared checks of the dense matmul / GEMV entry points.
 qg_status check_dense(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
@@ -31,9 +36,9 @@ qg_status check_dense(int fmt, const void* codes, const void* scales, const uint
     if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || T < 0 || T > kMaxT) return QG_ESHAPE;
     if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
     if (T == 0) return QG_OK;
-    if (!codes || !scales || !X || !Y || (fmt == QG_FMT_Q4A && !offs)) return QG_EINVAL;
+    if (!codes || !scales || !X || !Y || (has_offs(fmt) && !offs)) return QG_EINVAL;
     if (!aligned(codes, 16) || !aligned(X, 16) || !aligned(Y, 4) || !aligned(scales, scale_bytes(fmt)) ||
-        (offs && !aligned(offs, 2)))
+        (has_offs(fmt) && !aligned(offs, offs_bytes(fmt))))
         return QG_EALIGN;
     return QG_OK;
 }
@@ -64,7 +69,7 @@ qg_status run_dense(int fmt, const void* codes, const void* scales, const uint16
     if (gemv_only && T > 8) return QG_ESHAPE;
     if (T == 0) return QG_OK;
     GemmParams p = dense_params(codes, scales, offs, group, X, Y, N, K, T);
-    if (mode == QG_FAST_WEXACT && (fmt == QG_FMT_Q4A || xt != QG_X_F16)) return QG_EUNSUPPORTED;
+    if (mode == QG_FAST_WEXACT && ((fmt != QG_FMT_Q4 && fmt != QG_FMT_Q8) || xt != QG_X_F16)) return QG_EUNSUPPORTED;
     if (T <= 8) return launched(qg::launch_gemv(fmt, xt, p, false, s));
     if (mode == QG_EXACT) return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
     if (mode == QG_FAST_WEXACT) return launched(qg::launch_gemm_fast_wexact(fmt, p, s));
@@ -110,6 +115,12 @@ qg_status qgemm_q8(const int8_t* codes, const float* scales_f32, const void* X, 
     return run_dense(QG_FMT_Q8, codes, scales_f32, nullptr, 64, X, xt, Y, N, K, T, mode, false, stream);
 }
 
+qg_status qgemm_q8a(const int8_t* codes, const float* scales_f32, const float* offsets_f32, const void* X,
+                    qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode, hipStream_t stream) {
+    return run_dense(QG_FMT_Q8A, codes, scales_f32, (const uint16_t*)(const void*)offsets_f32, 64, X, xt, Y, N, K, T,
+                     mode, false, stream);
+}
+
 qg_status qgemv_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt, float* Y, int N,
                    int K, int T, hipStream_t stream) {
     return run_dense(QG_FMT_Q4, codes, scales_f16, nullptr, 64, X, xt, Y, N, K, T, QG_EXACT, true, stream);
@@ -125,6 +136,12 @@ qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, 
     return run_dense(QG_FMT_Q8, codes, scales_f32, nullptr, 64, X, xt, Y, N, K, T, QG_EXACT, true, stream);
 }
 
+qg_status qgemv_q8a(const int8_t* codes, const float* scales_f32, const float* offsets_f32, const void* X,
+                    qg_xtype xt, float* Y, int N, int K, int T, hipStream_t stream) {
+    return run_dense(QG_FMT_Q8A, codes, scales_f32, (const uint16_t*)(const void*)offsets_f32, 64, X, xt, Y, N, K, T,
+                     QG_EXACT, true, stream);
+}
+
 qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales, const uint16_t* offsets_bf16,
                           int group, int N, int K, int n0, int k0, int rows, int cols, qg_xtype staged, void* out,
                           hipStream_t stream) {
@@ -134,9 +151,9 @@ qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales, 
     if (rows < 1 || cols < 32 || (cols % 32) != 0 || (k0 % 32) != 0 || n0 < 0 || k0 < 0 || n0 + rows > N ||
         k0 + cols > K)
         return QG_ESHAPE;
-    if (!codes || !scales || !out || (fmt == QG_FMT_Q4A && !offsets_bf16)) return QG_EINVAL;
+    if (!codes || !scales || !out || (has_offs(fmt) && !offsets_bf16)) return QG_EINVAL;
     if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(scales, scale_bytes(fmt)) ||
-        (offsets_bf16 && !aligned(offsets_bf16, 2)))
+        (has_offs(fmt) && !aligned(offsets_bf16, offs_bytes(fmt))))
         return QG_EALIGN;
     return launched(qg::launch_dequant_dump(fmt, codes, scales, offsets_bf16, group, N, K, n0, k0, rows, cols,
                                             staged, out, stream));
@@ -192,7 +209,7 @@ qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const
     }
     if (T == 0) return QG_OK;
     if (T > 8 && mode == QG_FAST && xt == QG_X_F32) return QG_EUNSUPPORTED;
-    if (mode == QG_FAST_WEXACT && (fmt == QG_FMT_Q4A || xt != QG_X_F16)) return QG_EUNSUPPORTED;
+    if (mode == QG_FAST_WEXACT && ((fmt != QG_FMT_Q4 && fmt != QG_FMT_Q8) || xt != QG_X_F16)) return QG_EUNSUPPORTED;
     if (T == 1) {
         bool all = true;
         for (int j0 = 0; j0 < J && all; j0 += qg::kMaxBatchJobs) {
@@ -242,6 +259,19 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
     return launched(qg::launch_repack_gguf(q8 ? 1 : 0, src, nblocks, codes, scales, stream));
 }
 
+qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes, float* scales_f32,
+                             float* offsets_f32, hipStream_t stream) {
+    if (type != QG_GGUF_Q4_1 && type != QG_GGUF_Q5_0 && type != QG_GGUF_Q5_1 && type != QG_GGUF_Q4_K)
+        return QG_EINVAL;
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || (type == QG_GGUF_Q4_K && (K % 256) != 0))
+        return QG_ESHAPE;
+    if (!src || !codes || !scales_f32 || !offsets_f32) return QG_EINVAL;
+    if (!aligned(src, 2) || !aligned(codes, 16) || !aligned(scales_f32, 4) || !aligned(offsets_f32, 4))
+        return QG_EALIGN;
+    const size_t nblocks = (size_t)N * (size_t)(K / 32);
+    return launched(qg::launch_repack_gguf_q8a(type, src, nblocks, codes, scales_f32, offsets_f32, stream));
+}
+
 qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                       int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, hipStream_t stream) {
     if (T < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32 || (long)T * k > 16384) return QG_ESHAPE;
@@ -267,7 +297,7 @@ qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, 
                             const int32_t* row_src, int x_rows, const void* X, qg_xtype xt, const float* rs,
                             float* Y, int N, int K, int R, int E, qg_mode mode, hipStream_t stream) {
     if (!fmt_ok(fmt) || !xt_ok(xt) || !mode_ok(mode)) return QG_EINVAL;
-    if (mode == QG_FAST_WEXACT) return QG_EUNSUPPORTED;
+    if (mode == QG_FAST_WEXACT || !grouped_fmt_ok(fmt)) return QG_EUNSUPPORTED;
     if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || R < 0 || R > kMaxT || E < 1 ||
         E > kMaxGridY || x_rows < 0)
         return QG_ESHAPE;
@@ -349,7 +379,7 @@ qg_status check_ffn(int fmt, const qg_expert* gate_up, const qg_expert* down, in
                     const float* X, int T, int k, const int32_t* seg_off, const int32_t* row_src,
                     const int32_t* slot_row, const float* slot_w, const float* Y, int mode) {
     if (!fmt_ok(fmt) || !mode_ok(mode)) return QG_EINVAL;
-    if (mode == QG_FAST_WEXACT) return QG_EUNSUPPORTED;
+    if (mode == QG_FAST_WEXACT || !grouped_fmt_ok(fmt)) return QG_EUNSUPPORTED;
     if (E < 1 || E > kMaxGridY || H < 32 || (H % 32) != 0 || H > kMaxK || I < 32 || (I % 32) != 0 || I > kMaxK ||
         T < 0 || T > kMaxGridY || k < 1 || k > E || (int64_t)T * k > kMaxT)
         return QG_ESHAPE;

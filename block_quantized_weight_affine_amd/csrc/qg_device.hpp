@@ -16,7 +16,11 @@
 
 namespace qg {
 
-enum { FMT_Q4 = 0, FMT_Q4A = 1, FMT_Q8 = 2 };
+enum { FMT_Q4 = 0, FMT_Q4A = 1, FMT_Q8 = 2, FMT_Q8A = 3 };
+// Q8 and Q8A share the code layout (one int8 per element) and the f32 block scales; Q8A adds an f32
+// offset per 32-element block: value = (float(q) * d) + m, two roundings as written.
+template <int FMT>
+constexpr bool q8_layout = FMT == FMT_Q8 || FMT == FMT_Q8A;
 enum { XT_F32 = 0, XT_F16 = 1, XT_BF16 = 2 };
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -104,6 +108,12 @@ struct RawBlock<FMT_Q8> {
     float d, m;
     uint32_t dh;
 };
+template <>
+struct RawBlock<FMT_Q8A> {
+    uint4 q0, q1;
+    float d, m;
+    uint32_t dh;
+};
 
 // Loads block b of row n (all addresses in bounds: the caller clamps n and b).
 template <int FMT>
@@ -111,13 +121,13 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
                                                     int group, int K, int n, int b) {
     RawBlock<FMT> r;
     const size_t bi = (size_t)n * (size_t)(K >> 5) + (size_t)b;
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         const QG_GLOBAL u32x4_t* p = gptr<u32x4_t>((const int8_t*)codes + (size_t)n * (size_t)K + (size_t)b * 32);
         const u32x4_t a = p[0], c = p[1];
         r.q0 = make_uint4(a.x, a.y, a.z, a.w);
         r.q1 = make_uint4(c.x, c.y, c.z, c.w);
         r.d = gptr<float>(scales)[bi];
-        r.m = 0.f;
+        r.m = FMT == FMT_Q8A ? gptr<float>((const void*)offs)[bi] : 0.f;
         r.dh = 0;
     } else {
         const u32x4_t a = *gptr<u32x4_t>((const uint8_t*)codes + (size_t)n * (size_t)(K >> 1) + (size_t)b * 16);
@@ -146,7 +156,7 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
 // the separate one.  The choice is made for the whole wavefront at once.
 template <int FMT>
 __device__ __forceinline__ void value_bytes(const RawBlock<FMT>& r, uint32_t (&c)[8]) {
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         c[0] = keep_u32(r.q0.x ^ 0x80808080u); c[1] = keep_u32(r.q0.y ^ 0x80808080u);
         c[2] = keep_u32(r.q0.z ^ 0x80808080u); c[3] = keep_u32(r.q0.w ^ 0x80808080u);
         c[4] = keep_u32(r.q1.x ^ 0x80808080u); c[5] = keep_u32(r.q1.y ^ 0x80808080u);
@@ -165,7 +175,10 @@ __device__ __forceinline__ void value_bytes(const RawBlock<FMT>& r, uint32_t (&c
 template <int FMT>
 __device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
     fast = r.d > 0.0f;  // zero or negative scales (and NaN) take the pages' order
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (FMT == FMT_Q8A) {
+        fast = false;  // two roundings (product, then offset): always the written order
+        return -128.0f * r.d;
+    } else if constexpr (FMT == FMT_Q8) {
         return -128.0f * r.d;
     } else if constexpr (FMT == FMT_Q4) {
         return -8.0f * r.d;
@@ -183,7 +196,9 @@ __device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
 // The pages' order of operations for one element (value byte as f32).
 template <int FMT>
 __device__ __forceinline__ float slow_value(const RawBlock<FMT>& r, float cf) {
-    if constexpr (FMT == FMT_Q8)
+    if constexpr (FMT == FMT_Q8A)
+        return keep_f32((cf - 128.0f) * r.d) + r.m;
+    else if constexpr (FMT == FMT_Q8)
         return (cf - 128.0f) * r.d;
     else if constexpr (FMT == FMT_Q4)
         return (cf - 8.0f) * r.d;
@@ -202,11 +217,14 @@ __device__ __forceinline__ float byte_f32(uint32_t word, int i) { return (float)
 // The sign of a zero product is sign(d), as in (nibble - 8) * d.
 template <int FMT>
 __device__ __forceinline__ void block_quad_f32(const RawBlock<FMT>& r, int q, float (&v)[4]) {
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         const uint32_t x = w[q];
 #pragma unroll
-        for (int b = 0; b < 4; b++) v[b] = (float)(int8_t)(x >> (8 * b)) * r.d;
+        for (int b = 0; b < 4; b++) {
+            v[b] = (float)(int8_t)(x >> (8 * b)) * r.d;
+            if constexpr (FMT == FMT_Q8A) v[b] = keep_f32(v[b]) + r.m;
+        }
     } else {
         const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         const uint32_t x = keep_u32(q < 4 ? ((w[q & 3] << 4) & 0xF0F0F0F0u) ^ 0x80808080u
@@ -243,7 +261,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // Value-byte word k (elements 4k .. 4k+3) of a block, as in value_bytes.
 template <int FMT>
 __device__ __forceinline__ uint32_t value_word(const RawBlock<FMT>& r, int k) {
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         return keep_u32(w[k] ^ 0x80808080u);
     } else {
@@ -294,7 +312,8 @@ __device__ __forceinline__ short8_t frag16_words_slow(const uint32_t (&c)[2], fl
     for (int s = 0; s < 8; s++) {
         const float cf = byte_f32(c[s >> 2], s & 3);
         float v;
-        if constexpr (FMT == FMT_Q8) v = (cf - 128.0f) * d;
+        if constexpr (FMT == FMT_Q8A) v = keep_f32((cf - 128.0f) * d) + m;
+        else if constexpr (FMT == FMT_Q8) v = (cf - 128.0f) * d;
         else if constexpr (FMT == FMT_Q4) v = (cf - 8.0f) * d;
         else v = fmaf(cf - 8.0f, d, m);
         f[s] = (short)f32_to_16<ST>(keep_f32(v));
@@ -342,6 +361,7 @@ __device__ __forceinline__ void block_frags16_fixup(const RawBlock<FMT>& r, shor
 // pages' order.
 template <int FMT, int ST>
 __device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_t (&f)[4]) {
+    if constexpr (FMT == FMT_Q8A) return block_frags16_fixup<FMT, ST>(r, f);  // no shortcut applies
     block_to_frags16_fast<FMT, ST>(r, f);
     if (frags16_need_fixup<FMT, ST>(r)) block_frags16_fixup<FMT, ST>(r, f);
 }

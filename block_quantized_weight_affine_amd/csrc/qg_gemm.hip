@@ -90,7 +90,7 @@ template <int FMT, int MN>
 struct LaneRows {
     const QG_GLOBAL uint8_t* codes[MN];
     const QG_GLOBAL uint8_t* scales[MN];  // f16 (Q4, Q4A) or f32 (Q8) scales of the row
-    const QG_GLOBAL uint16_t* offs[MN];   // Q4A offsets of the row
+    const QG_GLOBAL uint16_t* offs[MN];   // Q4A offsets of the row (Q8A: f32, per block)
     int group;
 
     __device__ __forceinline__ void init(const void* c, const void* sc, const uint16_t* of, int grp, int K, int N,
@@ -99,23 +99,25 @@ struct LaneRows {
 #pragma unroll
         for (int mn = 0; mn < MN; mn++) {
             const size_t n = (size_t)min(row0 + 32 * mn, N - 1);
-            const size_t row_bytes = FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1);
+            const size_t row_bytes = q8_layout<FMT> ? (size_t)K : (size_t)(K >> 1);
             codes[mn] = gptr<uint8_t>((const uint8_t*)c + n * row_bytes);
-            scales[mn] = gptr<uint8_t>((const uint8_t*)sc + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
-            offs[mn] = FMT == FMT_Q4A ? gptr<uint16_t>(of + n * (size_t)(K / grp)) : nullptr;
+            scales[mn] = gptr<uint8_t>((const uint8_t*)sc + n * (size_t)(K >> 5) * (q8_layout<FMT> ? 4 : 2));
+            offs[mn] = FMT == FMT_Q4A ? gptr<uint16_t>(of + n * (size_t)(K / grp))
+                       : FMT == FMT_Q8A ? gptr<uint16_t>((const float*)(const void*)of + n * (size_t)(K >> 5))
+                                        : nullptr;
         }
     }
     // Block b (in bounds) of every row.
     __device__ __forceinline__ void load(int b, RawBlock<FMT> (&w)[MN]) const {
 #pragma unroll
         for (int mn = 0; mn < MN; mn++) {
-            if constexpr (FMT == FMT_Q8) {
+            if constexpr (q8_layout<FMT>) {
                 const QG_GLOBAL u32x4_t* q = (const QG_GLOBAL u32x4_t*)(codes[mn] + 32 * b);
                 const u32x4_t a = q[0], c = q[1];
                 w[mn].q0 = make_uint4(a.x, a.y, a.z, a.w);
                 w[mn].q1 = make_uint4(c.x, c.y, c.z, c.w);
                 w[mn].d = ((const QG_GLOBAL float*)scales[mn])[b];
-                w[mn].m = 0.f;
+                w[mn].m = FMT == FMT_Q8A ? ((const QG_GLOBAL float*)offs[mn])[b] : 0.f;
                 w[mn].dh = 0;
             } else {
                 const u32x4_t a = *(const QG_GLOBAL u32x4_t*)(codes[mn] + 16 * b);
@@ -427,21 +429,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
 #pragma unroll
     for (int i = 0; i < WB; i++) {
         const size_t n = (size_t)min(n0 + blk(i) / 2, p.N - 1);
-        wc[i] = gptr<uint8_t>((const uint8_t*)wcodes + n * (FMT == FMT_Q8 ? (size_t)K : (size_t)(K >> 1)));
-        wsc[i] = gptr<uint8_t>((const uint8_t*)wscales + n * (size_t)(K >> 5) * (FMT == FMT_Q8 ? 4 : 2));
-        wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(woffs + n * (size_t)(K / p.group)) : nullptr;
+        wc[i] = gptr<uint8_t>((const uint8_t*)wcodes + n * (q8_layout<FMT> ? (size_t)K : (size_t)(K >> 1)));
+        wsc[i] = gptr<uint8_t>((const uint8_t*)wscales + n * (size_t)(K >> 5) * (q8_layout<FMT> ? 4 : 2));
+        wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(woffs + n * (size_t)(K / p.group))
+                 : FMT == FMT_Q8A ? gptr<uint16_t>((const float*)(const void*)woffs + n * (size_t)(K >> 5))
+                                  : nullptr;
     }
     auto load_w = [&](int st, RawBlock<FMT> (&w)[WB]) {
         const int b = min(2 * st + hsel, nblk - 1);
 #pragma unroll
         for (int i = 0; i < WB; i++) {
-            if constexpr (FMT == FMT_Q8) {
+            if constexpr (q8_layout<FMT>) {
                 const QG_GLOBAL u32x4_t* q = (const QG_GLOBAL u32x4_t*)(wc[i] + 32 * b);
                 const u32x4_t a = q[0], c = q[1];
                 w[i].q0 = make_uint4(a.x, a.y, a.z, a.w);
                 w[i].q1 = make_uint4(c.x, c.y, c.z, c.w);
                 w[i].d = ((const QG_GLOBAL float*)wsc[i])[b];
-                w[i].m = 0.f;
+                w[i].m = FMT == FMT_Q8A ? ((const QG_GLOBAL float*)wof[i])[b] : 0.f;
                 w[i].dh = 0;
             } else {
                 const u32x4_t a = *(const QG_GLOBAL u32x4_t*)(wc[i] + 16 * b);
@@ -692,7 +696,8 @@ __device__ __forceinline__ uint8_t* ring_slot() {
 // never rounded.
 template <int FMT, int ST, int WM, int MT, int MN, int D, bool WX = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams p) {
-    static_assert(!WX || (FMT != FMT_Q4A && ST == XT_F16), "W-exact: Q4 / Q8 codes, f16 X");
+    static_assert(!WX || ((FMT == FMT_Q4 || FMT == FMT_Q8) && ST == XT_F16), "W-exact: Q4 / Q8 codes, f16 X");
+    static_assert(FMT != FMT_Q8A, "Q8A takes the decoded-tile kernels");
     constexpr int NW = 4;                       // wavefronts
     constexpr int WN = 4 / WM;
     constexpr int BT = 32 * MT * WM;
@@ -1160,8 +1165,10 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4, 4>(p, s);
     if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
     // 64 x 128 tiles: the raw-weight ring, wavefronts 1 x 4, six stages (Q4 prefill N = K = 4096,
-    // T 512: 32.5 us against 40.1 for the decoded-tile kernel with the same tile)
-    return fast_ring_launch<FMT, ST, 1, 2, 1, 6>(p, s);
+    // T 512: 32.5 us against 40.1 for the decoded-tile kernel with the same tile); Q8A (its per-block
+    // offsets are not in the ring) the 128 x 128 decoded tiles
+    if constexpr (FMT == FMT_Q8A) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
+    else return fast_ring_launch<FMT, ST, 1, 2, 1, 6>(p, s);
 }
 
 hipError_t launch_gemm_fast_wexact(int fmt, const GemmParams& p, hipStream_t s) {
@@ -1176,10 +1183,12 @@ hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, 
     if (st == XT_F16) {
         if (fmt == FMT_Q4) fast_pick<FMT_Q4, XT_F16>(p, grouped, s);
         else if (fmt == FMT_Q4A) fast_pick<FMT_Q4A, XT_F16>(p, grouped, s);
+        else if (fmt == FMT_Q8A) fast_pick<FMT_Q8A, XT_F16>(p, grouped, s);
         else fast_pick<FMT_Q8, XT_F16>(p, grouped, s);
     } else {
         if (fmt == FMT_Q4) fast_pick<FMT_Q4, XT_BF16>(p, grouped, s);
         else if (fmt == FMT_Q4A) fast_pick<FMT_Q4A, XT_BF16>(p, grouped, s);
+        else if (fmt == FMT_Q8A) fast_pick<FMT_Q8A, XT_BF16>(p, grouped, s);
         else fast_pick<FMT_Q8, XT_BF16>(p, grouped, s);
     }
     return hipGetLastError();
@@ -1213,6 +1222,7 @@ static void exact_xt(int xt, const GemmParams& p, bool grouped, hipStream_t s) {
 hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s) {
     if (fmt == FMT_Q4) exact_xt<FMT_Q4>(xt, p, grouped, s);
     else if (fmt == FMT_Q4A) exact_xt<FMT_Q4A>(xt, p, grouped, s);
+    else if (fmt == FMT_Q8A) exact_xt<FMT_Q8A>(xt, p, grouped, s);
     else exact_xt<FMT_Q8>(xt, p, grouped, s);
     return hipGetLastError();
 }

@@ -60,18 +60,23 @@ struct Unit<FMT_Q8> {
     uint4 q;
     float d, m;
 };
+template <>
+struct Unit<FMT_Q8A> {
+    uint4 q;
+    float d, m;
+};
 
 template <int FMT>
 __device__ __forceinline__ Unit<FMT> load_unit(const void* codes, const void* scales, const uint16_t* offs,
                                                int group, int K, int n, int u) {
     Unit<FMT> r;
     const size_t bi = (size_t)n * (size_t)(K >> 5) + (size_t)(u >> 1);
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         const u32x4_t v =
             __builtin_nontemporal_load((const u32x4_t*)((const int8_t*)codes + (size_t)n * K + (size_t)u * 16));
         r.q = make_uint4(v.x, v.y, v.z, v.w);
         r.d = ((const float*)scales)[bi];
-        r.m = 0.f;
+        r.m = FMT == FMT_Q8A ? ((const float*)(const void*)offs)[bi] : 0.f;
     } else {
         const u32x2_t v =
             __builtin_nontemporal_load((const u32x2_t*)((const uint8_t*)codes + (size_t)n * (K >> 1) + (size_t)u * 8));
@@ -86,7 +91,7 @@ __device__ __forceinline__ Unit<FMT> load_unit(const void* codes, const void* sc
 // Element offsets (within the row) of unit u's two runs of 8 values.
 template <int FMT>
 __device__ __forceinline__ void unit_runs(int u, int& k0, int& k1) {
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         k0 = 16 * u;
         k1 = 16 * u + 8;
     } else {
@@ -103,7 +108,7 @@ __device__ __forceinline__ float sbyte_f32(uint32_t word, int i) { return (float
 template <int FMT>
 __device__ __forceinline__ float unit_partial(const Unit<FMT>& w, const float (&x)[16]) {
     float p = 0.f;
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         const uint32_t ws[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
 #pragma unroll
         for (int i = 0; i < 16; i++) p = fmaf(sbyte_f32(ws[i >> 2], i & 3), x[i], p);
@@ -122,7 +127,7 @@ __device__ __forceinline__ float unit_partial(const Unit<FMT>& w, const float (&
 // several X rows.
 template <int FMT>
 __device__ __forceinline__ void unit_codes(const Unit<FMT>& w, float (&c)[16]) {
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (q8_layout<FMT>) {
         const uint32_t ws[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
 #pragma unroll
         for (int i = 0; i < 16; i++) c[i] = sbyte_f32(ws[i >> 2], i & 3);
@@ -142,6 +147,8 @@ template <int FMT>
 __device__ __forceinline__ float unit_value(const Unit<FMT>& w, float p, float sx) {
     if constexpr (FMT == FMT_Q8)
         return w.d * p;
+    else if constexpr (FMT == FMT_Q8A)
+        return fmaf(w.d, p, w.m * sx);
     else if constexpr (FMT == FMT_Q4)
         return (0.0625f * w.d) * p;
     else
@@ -273,7 +280,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
                         x[8] = b0.x; x[9] = b0.y; x[10] = b0.z; x[11] = b0.w;
                         x[12] = b1.x; x[13] = b1.y; x[14] = b1.z; x[15] = b1.w;
                         float sx = 0.f;
-                        if constexpr (FMT == FMT_Q4A) {
+                        if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
 #pragma unroll
                             for (int i = 0; i < 16; i++) sx += x[i];
                         }
@@ -383,7 +390,7 @@ constexpr int kStreamKMax = 16384;  // K limit of the K-split kernels for Q8 (16
 
 template <int FMT>
 struct G1Chunk {
-    static constexpr int values = FMT == FMT_Q8 ? 16 : 32;  // X values per lane chunk (16 code bytes)
+    static constexpr int values = q8_layout<FMT> ? 16 : 32;  // X values per lane chunk (16 code bytes)
 };
 
 
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
         for (int i = 0; i < V; i++) x[i] = on ? x[i] : 0.f;
     }
     float sx = 0.f;
-    if constexpr (FMT == FMT_Q4A) {
+    if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
 #pragma unroll
         for (int i = 0; i < V; i++) sx += x[i];
     }
@@ -474,24 +481,25 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
             offs = bj.offs[j];
             n -= bj.start[j];
         }
-        crow[r] = uniform_ptr(codes, (uint64_t)n * (uint64_t)(FMT == FMT_Q8 ? K : K >> 1));
-        srow[r] = uniform_ptr(scales, (uint64_t)n * (uint64_t)((K >> 5) * (FMT == FMT_Q8 ? 4 : 2)));
+        crow[r] = uniform_ptr(codes, (uint64_t)n * (uint64_t)(q8_layout<FMT> ? K : K >> 1));
+        srow[r] = uniform_ptr(scales, (uint64_t)n * (uint64_t)((K >> 5) * (q8_layout<FMT> ? 4 : 2)));
         asm volatile("" : "+s"(crow[r]), "+s"(srow[r]));
-        if constexpr (FMT == FMT_Q4A) {
-            orow[r] = uniform_ptr(offs, (uint64_t)n * (uint64_t)((K / p.group) * 2));
+        if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
+            // Q4A: bf16 per group; Q8A: f32 per block, laid out as the scales
+            orow[r] = uniform_ptr(offs, (uint64_t)n * (uint64_t)(FMT == FMT_Q8A ? (K >> 5) * 4 : (K / p.group) * 2));
             asm volatile("" : "+s"(orow[r]));
         }
     }
     const uint32_t oc = (uint32_t)(cc * 16);
-    const uint32_t os = FMT == FMT_Q8 ? (uint32_t)((cc >> 1) * 4) : (uint32_t)(cc * 2);
-    const uint32_t oo = FMT == FMT_Q4A ? (uint32_t)(((cc * 32) / p.group) * 2) : 0u;
+    const uint32_t os = q8_layout<FMT> ? (uint32_t)((cc >> 1) * 4) : (uint32_t)(cc * 2);
+    const uint32_t oo = FMT == FMT_Q4A ? (uint32_t)(((cc * 32) / p.group) * 2) : FMT == FMT_Q8A ? os : 0u;
     u32x4_t q[R];
     float d[R], m[R];
     auto issue = [&](int r) __attribute__((always_inline)) {
         q[r] = __builtin_nontemporal_load((const QG_GLOBAL u32x4_t*)(crow[r] + oc));
-        if constexpr (FMT == FMT_Q8) {
+        if constexpr (q8_layout<FMT>) {
             d[r] = *(const QG_GLOBAL float*)(srow[r] + os);
-            m[r] = 0.f;
+            m[r] = FMT == FMT_Q8A ? *(const QG_GLOBAL float*)(orow[r] + oo) : 0.f;
         } else {
             d[r] = 0.0625f * f16_to_f32(*(const QG_GLOBAL uint16_t*)(srow[r] + os));
             m[r] = FMT == FMT_Q4A ? bf16_to_f32(*(const QG_GLOBAL uint16_t*)(orow[r] + oo)) : 0.f;
@@ -500,7 +508,7 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
     auto row = [&](int r) __attribute__((always_inline)) {
         const uint32_t w4[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
         float pr = 0.f;
-        if constexpr (FMT == FMT_Q8) {
+        if constexpr (q8_layout<FMT>) {
 #pragma unroll
             for (int i = 0; i < 16; i++) pr = fmaf(sbyte_f32(w4[i >> 2], i & 3), x[i], pr);
         } else {
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
 #pragma unroll
             for (int i = 0; i < 16; i++) pr = fmaf(sbyte_f32((w4[i >> 2] & 0xF0F0F0F0u) ^ 0x80808080u, i & 3), x[16 + i], pr);
         }
-        const float v = row16_sum_dpp(FMT == FMT_Q4A ? fmaf(d[r], pr, m[r] * sx) : d[r] * pr);
+        const float v = row16_sum_dpp(FMT == FMT_Q4A || FMT == FMT_Q8A ? fmaf(d[r], pr, m[r] * sx) : d[r] * pr);
         if ((lane & 15) == 15) part[(r * 16 + wave) * 4 + (lane >> 4)] = v;
     };
     // Issue order (pinned by scheduling barriers): X (above), rows [0, A), the arithmetic of row 0,
@@ -655,7 +663,7 @@ __device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* cod
                 }
             }
             sx[t] = 0.f;
-            if constexpr (FMT == FMT_Q4A) {
+            if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
 #pragma unroll
                 for (int i = 0; i < 16; i++) sx[t] += x[t][i];
             }
@@ -884,6 +892,7 @@ bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& b
     bool ok;
     if (fmt == FMT_Q4) ok = gemv1_batch_xt<FMT_Q4>(xt, p, bj, s);
     else if (fmt == FMT_Q4A) ok = gemv1_batch_xt<FMT_Q4A>(xt, p, bj, s);
+    else if (fmt == FMT_Q8A) ok = gemv1_batch_xt<FMT_Q8A>(xt, p, bj, s);
     else ok = gemv1_batch_xt<FMT_Q8>(xt, p, bj, s);
     err = ok ? hipGetLastError() : hipSuccess;
     return ok;
@@ -892,6 +901,7 @@ bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& b
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s) {
     if (fmt == FMT_Q4) gemv_xt<FMT_Q4>(xt, p, grouped, s);
     else if (fmt == FMT_Q4A) gemv_xt<FMT_Q4A>(xt, p, grouped, s);
+    else if (fmt == FMT_Q8A) gemv_xt<FMT_Q8A>(xt, p, grouped, s);
     else gemv_xt<FMT_Q8>(xt, p, grouped, s);
     return hipGetLastError();
 }

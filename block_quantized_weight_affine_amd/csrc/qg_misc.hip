@@ -86,6 +86,7 @@ hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, c
     (void)N;
     if (fmt == FMT_Q4) dump_st<FMT_Q4>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else if (fmt == FMT_Q4A) dump_st<FMT_Q4A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
+    else if (fmt == FMT_Q8A) dump_st<FMT_Q8A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else dump_st<FMT_Q8>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     return hipGetLastError();
 }
@@ -419,6 +420,120 @@ __global__ void repack_gguf_kernel(const uint16_t* src, size_t nblocks, uint8_t*
         else
             ((float*)scales)[b] = f16_to_f32(B[0]);
     }
+}
+
+// ---- GGUF affine blocks -> Q8A ----------------------------------------------------------------------
+// Page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC, the loaders of Q4_1, Q5_0, Q5_1 (load_q45) and
+// Q4_K (with its 6-bit scale / min unpacking).  Each of these types gives element e of a 32-element
+// block (a sub-block for Q4_K) as an integer code times an f32 scale plus an f32 offset, evaluated
+// product first, then the add: Q4_1 nibble * d + m, Q5_0 (code5 - 16) * d (+ 0), Q5_1 code5 * d + m,
+// Q4_K nibble * (d sc) - dmin mn.  Q8A holds exactly that: int8 codes, the scale and the offset in
+// f32 (Q5_0: codes - 16 and offset +0; Q4_K: scale d sc and offset -(dmin mn), both rounded once as
+// the loader rounds them).  Field layout, little-endian, f16 fields as h:
+//   Q4_1 20 B: h d, h m, 16 bytes (byte j: element j low nibble, element j + 16 high nibble)
+//   Q5_0 22 B: h d, 32-bit qh (bit e: 16s bit of element e), 16 nibble bytes as Q4_1
+//   Q5_1 24 B: h d, h m, qh, 16 nibble bytes
+//   Q4_K 144 B per 256 elements: h d, h dmin, 12 scale bytes, 128 code bytes; sub-block j's
+//        elements are the low (j even) or high (j odd) nibbles of code bytes 32 (j / 2) .. + 31.
+// One thread per output block, consecutive threads on consecutive blocks of a row-major [N][K/32]
+// block grid (blocks are 2-byte aligned: read as 16-bit words).
+template <int GT>
+__global__ void repack_gguf_q8a_kernel(const uint16_t* src, size_t nblocks, uint8_t* codes, float* scales,
+                                       float* offs) {
+    for (size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * blockDim.x) {
+        uint8_t nib[32];  // element e's code before any shift
+        float d, m;
+        if constexpr (GT == QG_GGUF_Q4_K) {
+            const uint16_t* SB = src + (b >> 3) * 72;  // 144-byte super-block
+            const int j = (int)(b & 7);
+            uint8_t sb[12];
+#pragma unroll
+            for (int i = 0; i < 6; i++) {
+                sb[2 * i] = (uint8_t)SB[2 + i];
+                sb[2 * i + 1] = (uint8_t)(SB[2 + i] >> 8);
+            }
+            int sc, mn;
+            if (j < 4) {
+                sc = sb[j] & 63;
+                mn = sb[j + 4] & 63;
+            } else {
+                sc = (sb[j + 4] & 15) | ((sb[j - 4] >> 6) << 4);
+                mn = (sb[j + 4] >> 4) | ((sb[j] >> 6) << 4);
+            }
+            d = f16_to_f32(SB[0]) * (float)sc;
+            m = -(f16_to_f32(SB[1]) * (float)mn);
+            const uint16_t* q = SB + 8 + 16 * (j >> 1);
+            const int sh = 4 * (j & 1);
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                nib[2 * i] = (uint8_t)((q[i] >> sh) & 15);
+                nib[2 * i + 1] = (uint8_t)((q[i] >> (8 + sh)) & 15);
+            }
+        } else {
+            constexpr bool has_m = GT == QG_GGUF_Q4_1 || GT == QG_GGUF_Q5_1;
+            constexpr bool has_h = GT == QG_GGUF_Q5_0 || GT == QG_GGUF_Q5_1;
+            constexpr int W = (2 + (has_m ? 2 : 0) + (has_h ? 4 : 0) + 16) / 2;  // 16-bit words per block
+            const uint16_t* B = src + b * W;
+            d = f16_to_f32(B[0]);
+            m = has_m ? f16_to_f32(B[1]) : 0.0f;
+            constexpr int qo = 1 + (has_m ? 1 : 0) + (has_h ? 2 : 0);  // word of the first nibble byte
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint16_t w = B[qo + i];
+                nib[2 * i] = (uint8_t)(w & 15);
+                nib[2 * i + 1] = (uint8_t)((w >> 8) & 15);
+                nib[16 + 2 * i] = (uint8_t)((w >> 4) & 15);
+                nib[17 + 2 * i] = (uint8_t)(w >> 12);
+            }
+            if constexpr (has_h) {
+                constexpr int ho = 1 + (has_m ? 1 : 0);
+                const uint32_t qh = (uint32_t)B[ho] | ((uint32_t)B[ho + 1] << 16);
+#pragma unroll
+                for (int e = 0; e < 32; e++) nib[e] = (uint8_t)(nib[e] + 16 * ((qh >> e) & 1));
+            }
+            if constexpr (GT == QG_GGUF_Q5_0) {
+#pragma unroll
+                for (int e = 0; e < 32; e++) nib[e] = (uint8_t)(nib[e] - 16);  // int8 code - 16
+            }
+        }
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            w[i] = (uint32_t)nib[4 * i] | ((uint32_t)nib[4 * i + 1] << 8) | ((uint32_t)nib[4 * i + 2] << 16) |
+                   ((uint32_t)nib[4 * i + 3] << 24);
+        uint4* dst = (uint4*)(codes + b * 32);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        scales[b] = d;
+        offs[b] = m;
+    }
+}
+
+hipError_t launch_repack_gguf_q8a(int type, const void* src, size_t nblocks, void* codes, float* scales,
+                                  float* offs, hipStream_t s) {
+    const unsigned grid = (unsigned)std::min<size_t>((nblocks + 255) / 256, 65535);
+    const uint16_t* w = (const uint16_t*)src;
+    uint8_t* c = (uint8_t*)codes;
+    switch (type) {
+        case QG_GGUF_Q4_1:
+            hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q4_1>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
+                               scales, offs);
+            break;
+        case QG_GGUF_Q5_0:
+            hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q5_0>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
+                               scales, offs);
+            break;
+        case QG_GGUF_Q5_1:
+            hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q5_1>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
+                               scales, offs);
+            break;
+        case QG_GGUF_Q4_K:
+            hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q4_K>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
+                               scales, offs);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_repack_gguf(int q8, const void* src, size_t nblocks, void* codes, void* scales, hipStream_t s) {

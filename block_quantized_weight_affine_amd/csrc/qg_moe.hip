@@ -12,9 +12,10 @@
 //    rows and streams it on its own, with no barrier: lane c holds 16-byte chunk c of every row (Q4 /
 //    Q4A: one 32-value block; Q8: half a block), so K <= 64 chunks.  The chunk's X values of each
 //    segment row stay in registers for the whole range.
-//  * The weight rows go through a per-wavefront ring in LDS, 4 rows (4 KiB) a stage, 3 stages: the
-//    code bytes are copied by buffer_load ... lds (one instruction per row, no registers held), the
-//    lane's block scale into a register ring; two stages stay in flight while one is computed.
+//  * The weight rows go through a per-wavefront ring in LDS, 4 rows a stage, 3 stages: the code bytes
+//    (one instruction per row) and the block scales and offsets (one instruction for the stage) are
+//    copied by buffer_load ... lds, holding no registers; two stages stay in flight while one is
+//    computed.
 //  * Arithmetic.  F32: the signed codes as f32, f32 FMA with x, then the block scale times the f32
 //    partial (and the Q4A offset times the chunk's x sum).  DOT2 (fast mode with f16 X): two codes
 //    per mask instruction as exact f16 subnormals, v_dot2 with pairs of x into an f32 partial, scaled
@@ -515,7 +516,9 @@ static bool rows_pick(int xt, bool fast, int epi, const GemmParams& p, int gx, h
 
 bool grouped_rows_fits(int fmt, int K, int N, int epi) {
     // byte offsets into an expert's codes are 31-bit buffer offsets
-    return K <= rows_kmax(fmt) && (int64_t)N * K < ((int64_t)1 << 31) && (epi == EPI_PLAIN || (N % 2) == 0);
+    // (Q8A is not a grouped format)
+    return fmt != FMT_Q8A && K <= rows_kmax(fmt) && (int64_t)N * K < ((int64_t)1 << 31) &&
+           (epi == EPI_PLAIN || (N % 2) == 0);
 }
 
 hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmParams& p, hipStream_t s) {
@@ -534,7 +537,7 @@ hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmPa
     bool ok = false;
     if (fmt == FMT_Q4) ok = rows_pick<FMT_Q4>(xt, fast, epi, p, gx, s);
     else if (fmt == FMT_Q4A) ok = rows_pick<FMT_Q4A>(xt, fast, epi, p, gx, s);
-    else ok = rows_pick<FMT_Q8>(xt, fast, epi, p, gx, s);
+    else if (fmt == FMT_Q8) ok = rows_pick<FMT_Q8>(xt, fast, epi, p, gx, s);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -68,9 +68,18 @@ typedef enum {
 typedef enum { QG_X_F32 = 0, QG_X_F16 = 1, QG_X_BF16 = 2 } qg_xtype;
 /* QG_FAST_WEXACT (dense matmuls only): the fast mode with the weights kept exact -- see below. */
 typedef enum { QG_EXACT = 0, QG_FAST = 1, QG_FAST_WEXACT = 2 } qg_mode;
-typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2 } qg_format;
+/* QG_FMT_Q8A: the target layout of the affine GGUF types (see qg_repack_gguf_q8a); dense entry
+ * points, the GEMV, the batched call and the dump only. */
+typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2, QG_FMT_Q8A = 3 } qg_format;
 /* GGUF block types with the scale inside each block (the values are GGML's type ids). */
-typedef enum { QG_GGUF_Q4_0 = 2, QG_GGUF_Q8_0 = 8 } qg_gguf_type;
+typedef enum {
+    QG_GGUF_Q4_0 = 2,
+    QG_GGUF_Q4_1 = 3,
+    QG_GGUF_Q5_0 = 6,
+    QG_GGUF_Q5_1 = 7,
+    QG_GGUF_Q8_0 = 8,
+    QG_GGUF_Q4_K = 12
+} qg_gguf_type;
 
 /* Text for a status code (static storage; never NULL). */
 const char* qg_strerror(qg_status s);
@@ -99,6 +108,15 @@ qg_status qgemm_q4a(const uint8_t* codes, const uint16_t* scales_f16, const uint
                     qg_mode mode, hipStream_t stream);
 qg_status qgemm_q8(const int8_t* codes, const float* scales_f32, const void* X, qg_xtype xt,
                    float* Y, int N, int K, int T, qg_mode mode, hipStream_t stream);
+/* Q8A: int8 codes q [N][K] (16-byte aligned), f32 scales d and f32 offsets m [N][K/32] (4-byte
+ * aligned; offsets NULL gives QG_EINVAL); w(n, k) = fl(fl(q d) + m), the product rounded to f32,
+ * then the add (page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC, the loaders load_q45 and Q4_KW,
+ * which evaluate the affine GGUF types in that order).  Exact mode stages that value; QG_FAST
+ * stages it rounded to the X type; QG_FAST_WEXACT gives QG_EUNSUPPORTED.  Every other rule as
+ * qgemm_q8. */
+qg_status qgemm_q8a(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
+                    const void* X, qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode,
+                    hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * T <= 8 GEMV: one weight row per wavefront group, coalesced 16-byte loads of the packed blocks,
@@ -113,6 +131,8 @@ qg_status qgemv_q4a(const uint8_t* codes, const uint16_t* scales_f16, const uint
                     hipStream_t stream);
 qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, qg_xtype xt,
                    float* Y, int N, int K, int T, hipStream_t stream);
+qg_status qgemv_q8a(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
+                    const void* X, qg_xtype xt, float* Y, int N, int K, int T, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Debug dump of a staged weight tile: out[r][c] = the value the GEMM kernels stage for element
@@ -121,7 +141,8 @@ qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, 
  * staged = QG_X_F32: f32 values (exact mode); QG_X_F16 / QG_X_BF16: 16-bit patterns (fast mode).
  * Needs k0 % 32 == 0, cols % 32 == 0, 0 <= n0, n0 + rows <= N, k0 + cols <= K, rows >= 1;
  * out is [rows][cols] of 4 or 2 bytes, 16-byte aligned.  fmt QG_FMT_Q4 / Q4A take uint16 f16
- * scales, QG_FMT_Q8 f32 scales; offsets are read only for QG_FMT_Q4A.
+ * scales, QG_FMT_Q8 / Q8A f32 scales; offsets are read for QG_FMT_Q4A (bf16 bits) and QG_FMT_Q8A
+ * (f32 values passed through this pointer, 4-byte aligned) only.
  */
 qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales,
                           const uint16_t* offsets_bf16, int group, int N, int K, int n0, int k0,
@@ -143,8 +164,8 @@ typedef struct {
     const uint16_t* offsets;
 } qg_expert;
 
-/* One weight matrix of a batched call: device pointers as in qgemm_q4 / qgemm_q4a / qgemm_q8
- * (offsets used by QG_FMT_Q4A only), Y f32 [T][N]. */
+/* One weight matrix of a batched call: device pointers as in qgemm_q4 / qgemm_q4a / qgemm_q8 /
+ * qgemm_q8a (offsets used by QG_FMT_Q4A and, as f32, QG_FMT_Q8A only), Y f32 [T][N]. */
 typedef struct {
     const void* codes;
     const void* scales;
@@ -177,6 +198,28 @@ qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const
  * QG_EINVAL.  Asynchronous on `stream`; nothing is allocated. */
 qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void* codes, void* scales,
                          hipStream_t stream);
+
+/* Affine GGUF blocks to the Q8A layout, on the device (page "oxinfer 0.0.5 src/metal.rs",
+ * GGUF_SHADER_SRC, the loaders load_q45 for Q4_1 / Q5_0 / Q5_1 and Q4_KW with its 6-bit scale and
+ * min unpacking).  src: N rows of K/32 blocks (K/256 super-blocks for QG_GGUF_Q4_K), row after row,
+ * little-endian, f16 fields as h:
+ *   QG_GGUF_Q4_1 (20 bytes): h d, h m, 16 nibble bytes (byte j: element j in its low nibble,
+ *                element j + 16 in its high nibble); value nibble * d + m.
+ *   QG_GGUF_Q5_0 (22 bytes): h d, a 32-bit qh, 16 nibble bytes; code = nibble + 16 * bit e of qh;
+ *                value (code - 16) * d.
+ *   QG_GGUF_Q5_1 (24 bytes): h d, h m, qh, 16 nibble bytes; value code * d + m.
+ *   QG_GGUF_Q4_K (144 bytes per 256 elements): h d, h dmin, 12 bytes of 6-bit scales sc and mins
+ *                mn of the eight 32-element sub-blocks, 128 code bytes; value nibble * (d sc) -
+ *                dmin mn.
+ * Each value is a product rounded to f32 and then an add, so the Q8A layout holds it exactly: codes
+ * int8 [N][K] (the code; Q5_0 code - 16), scales f32 [N][K/32] (d; Q4_K d sc rounded once) and
+ * offsets f32 [N][K/32] (m; Q5_0 +0; Q4_K -(dmin mn) rounded once), and qgemm_q8a / qgemv_q8a then
+ * compute with the GGUF values.  Device pointers owned by the caller; src 2-byte aligned, codes
+ * 16-byte aligned, scales and offsets 4-byte aligned, else QG_EALIGN; N >= 1, K >= 32, K % 32 == 0
+ * (K % 256 == 0 for Q4_K), else QG_ESHAPE; a type not listed here or a null pointer gives
+ * QG_EINVAL.  Asynchronous on `stream`; nothing is allocated. */
+qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
+                             float* scales_f32, float* offsets_f32, hipStream_t stream);
 
 /* Routing plan, on the HOST (all pointers host memory).  logits f32 [T][E].  For each token:
  * the k largest logits, equal logits in ascending expert index; weight_j = exp(l_j - l_max) /
@@ -229,7 +272,8 @@ qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, i
  * given); for R <= 8 E, where the f16 call takes the same kernel, the result equals qg_x_half
  * followed by the f16 call bit for bit.  Y f32 [R][N].
  * QG_ESHAPE also when a tile-kernel launch (QG_FAST, or QG_EXACT with R > 8 E) would need more than
- * 65535 row tiles ((R + 31) / 32 + min(E, R)). */
+ * 65535 row tiles ((R + 31) / 32 + min(E, R)).  fmt QG_FMT_Q8A gives QG_EUNSUPPORTED here and in
+ * qg_moe_ffn. */
 qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group,
                             const int32_t* seg_off, const int32_t* row_src, int x_rows,
                             const void* X, qg_xtype xt, const float* rs, float* Y, int N, int K,

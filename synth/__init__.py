@@ -188,7 +188,8 @@ def make_dense(fmt: str, N: int, K: int, T: int, xtype: str, x_sigma: float, see
 
     q4 / q4a: codes uint8 [N*K/2], scales f16 bits uint16 [N*K/32] uniform [0.01, 0.05];
     q4a adds offsets bf16 bits uint16 [N*K/group] from N(0, 0.02).
-    q8: codes int8 [N*K] uniform -127..127, scales f32 [N*K/32] uniform [0.002, 0.01].
+    q8: codes int8 [N*K] uniform -127..127, scales f32 [N*K/32] uniform [0.002, 0.01];
+    q8a adds offsets f32 [N*K/32] from N(0, 0.2).
     X: N(0, x_sigma) [T*K] in xtype (f32 / f16 / bf16 bits)."""
     out = {"fmt": fmt, "N": N, "K": K, "T": T, "xtype": xtype, "group": group}
     if fmt in ("q4", "q4a"):
@@ -196,9 +197,11 @@ def make_dense(fmt: str, N: int, K: int, T: int, xtype: str, x_sigma: float, see
         out["scales"] = f16_uniform(seed, STREAM_SCALES, N * K // 32, 0.01, 0.05)
         if fmt == "q4a":
             out["offsets"] = normal_as(seed, STREAM_OFFS, N * K // group, 0.0, 0.02, "bf16")
-    elif fmt == "q8":
+    elif fmt in ("q8", "q8a"):
         out["codes"] = q8_codes(seed, STREAM_CODES, N * K)
         out["scales"] = f32_uniform(seed, STREAM_SCALES, N * K // 32, 0.002, 0.01)
+        if fmt == "q8a":
+            out["offsets"] = normal_as(seed, STREAM_OFFS, N * K // 32, 0.0, 0.2, "f32")
     else:
         raise ValueError(fmt)
     out["X"] = normal_as(seed, STREAM_X, T * K, 0.0, x_sigma, xtype)

@@ -154,6 +154,49 @@ def test_repack_gguf_validation_codes():
     assert call(t=qg.QG_GGUF_Q8_0, scales=A16c + 2) == qg.QG_EALIGN
 
 
+def test_q8a_validation_codes():
+    """Q8A: offsets required and 4-byte aligned (f32), W-exact unsupported, no grouped or expert-block
+    calls; the GGUF -> Q8A repack checks type, sizes, pointers and alignment."""
+    L = qg.lib()
+
+    def gemm(codes=A16, scales=A16b, offs=A16, xt=qg.QG_X_F32, T=16, mode=qg.QG_EXACT):
+        return L.qgemm_q8a(codes, scales, offs, A16c, xt, A16d, 256, 512, T, mode, None)
+
+    assert gemm(offs=None) == qg.QG_EINVAL
+    assert gemm(offs=A16 + 2) == qg.QG_EALIGN
+    assert gemm(scales=A16b + 2) == qg.QG_EALIGN
+    assert gemm(codes=A16 + 4) == qg.QG_EALIGN
+    assert gemm(T=0, offs=None) == qg.QG_OK
+    assert gemm(xt=qg.QG_X_F16, mode=qg.QG_FAST_WEXACT) == qg.QG_EUNSUPPORTED
+    assert gemm(xt=qg.QG_X_F32, mode=qg.QG_FAST) == qg.QG_EUNSUPPORTED
+    assert L.qgemv_q8a(A16, A16b, A16, A16c, 0, A16d, 256, 512, 9, None) == qg.QG_ESHAPE
+    assert L.qgemv_q8a(A16, A16b, None, A16c, 0, A16d, 256, 512, 1, None) == qg.QG_EINVAL
+    assert L.qg_dequant_dump(qg.QG_FMT_Q8A, A16, A16b, A16 + 2, 64, 64, 256, 0, 0, 8, 64, 0, A16c, None) == \
+        qg.QG_EALIGN
+    assert L.qg_dequant_dump(qg.QG_FMT_Q8A, A16, A16b, None, 64, 64, 256, 0, 0, 8, 64, 0, A16c, None) == \
+        qg.QG_EINVAL
+    assert L.qgemm_moe_grouped(qg.QG_FMT_Q8A, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 512, 8, 4,
+                               qg.QG_EXACT, None) == qg.QG_EUNSUPPORTED
+    assert L.qg_moe_ffn(qg.QG_FMT_Q8A, A16, A16b, 64, 4, 256, 256, A16c, 2, 2, A16, A16, A16, A16, A16d, 0,
+                        qg.QG_EXACT, A16, 0x1000000, None) == qg.QG_EUNSUPPORTED
+
+    def rep(t=qg.QG_GGUF_Q4_K, src=A16, N=8, K=512, codes=A16b, scales=A16c, offs=A16d):
+        return L.qg_repack_gguf_q8a(t, src, N, K, codes, scales, offs, None)
+
+    assert rep(t=qg.QG_GGUF_Q4_0) == qg.QG_EINVAL     # not an affine type
+    assert rep(t=qg.QG_GGUF_Q8_0) == qg.QG_EINVAL
+    assert rep(t=5) == qg.QG_EINVAL
+    assert rep(K=288) == qg.QG_ESHAPE                 # Q4_K needs K % 256 == 0
+    assert rep(N=0) == qg.QG_ESHAPE
+    assert rep(t=qg.QG_GGUF_Q4_1, K=48) == qg.QG_ESHAPE
+    assert rep(offs=None) == qg.QG_EINVAL
+    assert rep(src=None) == qg.QG_EINVAL
+    assert rep(src=A16 + 1) == qg.QG_EALIGN
+    assert rep(codes=A16b + 8) == qg.QG_EALIGN
+    assert rep(scales=A16c + 2) == qg.QG_EALIGN
+    assert rep(offs=A16d + 2) == qg.QG_EALIGN
+
+
 def test_device_plan_validation_codes():
     """qg_moe_plan checks its sizes and pointers on the host, before any HIP call."""
     L = qg.lib()

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 STAGED = {"f32": qg.QG_X_F32, "f16": qg.QG_X_F16, "bf16": qg.QG_X_BF16}
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
+@pytest.mark.parametrize("fmt", ["q4", "q4a", "q8", "q8a"])
 @pytest.mark.parametrize("staged", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", [(64, 256, 5, 64, 37, 128), (48, 96, 0, 0, 48, 96), (4096, 4096, 4000, 3968, 96, 128)])
 def test_dump_bit_exact(orc, fmt, staged, shape):
@@ -21,7 +21,7 @@ def test_dump_bit_exact(orc, fmt, staged, shape):
     w = synth.make_dense(fmt, N, K, 1, "f32", 1.0, 77 + N, group=32 if K == 96 else 64)
     group = w["group"]
     codes, scales = dev(w["codes"]), dev(w["scales"])
-    offs = dev(w["offsets"]) if fmt == "q4a" else None
+    offs = dev(w["offsets"]) if fmt in ("q4a", "q8a") else None
     out = torch.empty((rows, cols), dtype=torch.float32 if staged == "f32" else torch.int16, device="cuda")
     qg.qg_dequant_dump(fmt, codes, scales, offs, group, N, K, n0, k0, rows, cols, STAGED[staged], out)
     torch.cuda.synchronize()
