@@ -43,15 +43,20 @@ WORKLOADS = {
     "moe_block_fast": (4, "fast"),
 }
 HEADLINE = "q8_gemv_decode"
-# The headline kernel (gemv1_split_kernel) and everything it is built from: its file, the device and
-# launch headers, and the C entry point that launches it.  A committed traffic figure counts only while
+# The sources each workload's kernels are built from: the kernel files, the device and launch headers,
+# and the C entry point that picks and launches them.  A committed traffic figure counts only while
 # these are unchanged.
-KERNEL_SOURCES = ["qg_device.hpp", "qg_internal.hpp", "qg_gemv.hip", "qg_capi.cpp"]
+_BASE_SOURCES = ["qg_device.hpp", "qg_internal.hpp", "qg_capi.cpp"]
+KERNEL_SOURCES = {
+    "q8_gemv_decode": _BASE_SOURCES + ["qg_gemv.hip"],
+    "moe_block_exact": _BASE_SOURCES + ["qg_moe.hip", "qg_misc.hip"],
+    "moe_block_fast": _BASE_SOURCES + ["qg_moe.hip", "qg_misc.hip"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(name: str = HEADLINE) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES.get(name, _BASE_SOURCES + ["qg_gemm.hip", "qg_gemv.hip"]):
         with open(os.path.join(ROOT, "block_quantized_weight_affine_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -80,6 +85,21 @@ def _timed(fn, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return s.elapsed_time(e) / steps, wall
+
+
+def _bracketed(fn, n: int, first: int) -> float:
+    """Mean duration (us) of n single launches, each bracketed by its own pair of events on the launch
+    stream (an event between every two launches): the figure to set beside a profiler's per-dispatch
+    durations, which likewise separate the launches."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(first + i)
+        b.record()
+    torch.cuda.synchronize()
+    return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / n
 
 
 def _bound(name: str, *args):
@@ -112,6 +132,17 @@ def _bound(name: str, *args):
 
 
 # ---------------------------------------------------------------------------------------------------
+def _fast_kernel(fmt: str, N: int, T: int) -> str:
+    """The kernel the fast-mode dispatcher picks for a dense call: decoded tiles (256 x 256, 128 x 256
+    or 128 x 128 rows x tokens) while they still give about 200 workgroups, else the raw-weight ring
+    with 64 x 128 tiles (Q8A: 128 x 128 decoded tiles)."""
+    def wgs(bt, bn):
+        return ((N + bn - 1) // bn) * ((T + bt - 1) // bt)
+    if wgs(256, 256) >= 200 or wgs(128, 256) >= 200 or wgs(128, 128) >= 200 or fmt == "q8a":
+        return "gemm_fast_lds_kernel"
+    return "gemm_fast_ring_kernel"
+
+
 def setup_dense(ci: int, mode: str, copies: int):
     import torch
     import block_quantized_weight_affine_amd as qg
@@ -146,7 +177,7 @@ def setup_dense(ci: int, mode: str, copies: int):
         "kernel": (("gemv1_split_kernel" if c.T == 1 and c.K <= 16384 else
                     "gemv_ksplit_kernel" if c.T >= 2 and c.K <= (16384 if c.T <= 4 else 8192) else "gemv_kernel")
                    if c.T <= 8
-                   else ("gemm_exact_kernel" if mode == "exact" else "gemm_fast_lds_kernel")),
+                   else ("gemm_exact_kernel" if mode == "exact" else _fast_kernel(c.fmt, c.N, c.T))),
         "keep": (codes, scales, offs, X, Y),
     }
     return step, info
@@ -317,12 +348,14 @@ def measure_repack(steps: int, warmup: int) -> dict:
             "bytes_per_step": nbytes}
 
 
-def measure(name: str, steps: int, warmup: int) -> dict:
+def measure(name: str, steps: int, warmup: int, bracketed: int = 0) -> dict:
     step, info = setup(name)
     ms, wall = _timed(step, steps, warmup)
     c = info["cfg"]
     out = {"workload": name, "config": info["name"], "mode": info["mode"], "ms_per_step": ms,
            "us_per_step": ms * 1e3, "dtype": info["dtype"], "kernel": info["kernel"]}
+    if bracketed:
+        out["launch_us_bracketed"] = _bracketed(step, bracketed, warmup + steps)
     if c.index in (1, 4):
         gbs = info["bytes"] / (ms * 1e-3) / 1e9
         out.update({"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
@@ -418,7 +451,7 @@ def traffic_for(name: str, info: dict, ms: float) -> float | None:
         t = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(name):
         return None
     return float(t["hbm_bytes_per_launch"])
 
@@ -454,12 +487,15 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "copies": args.steps}))
         return
 
-    head = measure(args.workload, args.steps, args.warmup)
+    head = measure(args.workload, args.steps, args.warmup, bracketed=200)
     info = head.pop("_info")
     roofline = {"bound": head["bound"], "achieved": head["value"], "peak": head["peak"],
                 "unit": head["unit"], "frac": head["frac"], "traffic": traffic_for(args.workload, info,
                                                                                  head["ms_per_step"]),
-                "kernel": head["kernel"], "per_launch": (info["bytes"] if head["unit"] == "GB/s" else info["flops"])}
+                "kernel": head["kernel"], "per_launch": (info["bytes"] if head["unit"] == "GB/s" else info["flops"]),
+                # one launch per step: the timed region's mean step is the mean launch duration; the
+                # bracketed figure separates every launch by events, as a profiler's trace does
+                "launch_us_timed": head["ms_per_step"] * 1e3, "launch_us_bracketed": head["launch_us_bracketed"]}
     cpu = None
     if not args.no_cpu and info["cfg"].index != 4:
         cpu = cpu_baseline(info)
@@ -470,7 +506,9 @@ def main():
                 continue
             st = 128 if "moe" in name or "prefill" in name or "upproj" in name else 512
             r = measure(name, st, 20)
-            r.pop("_info")
+            r_info = r.pop("_info")
+            if r["unit"] == "GB/s":
+                r["traffic"] = traffic_for(name, r_info, r["ms_per_step"])
             also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
             torch.cuda.empty_cache()
         r = measure_repack(256, 20)
