@@ -86,6 +86,13 @@ def lib():
             getattr(L, name).argtypes = [_p, _sz, _p]
         L.orc_dequant_exact.restype = None
         L.orc_dequant_exact.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p]
+        L.orc_conv_stats.restype = None
+        L.orc_conv_stats.argtypes = [_p, _i, _i, _i, C.c_double, _p]
+        L.orc_conv_gather.restype = None
+        L.orc_conv_gather.argtypes = [_p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p, _p]
+        L.orc_conv2d.restype = _i
+        L.orc_conv2d.argtypes = [_i, _p, _p, _p, _i, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p,
+                                 _i, _p, _p, _i]
         _lib = L
     return _lib
 
@@ -305,3 +312,62 @@ def gguf_repack_q8a(gtype, src, N, K) -> tuple:
     offs = np.empty(N * K // 32, np.float32)
     lib().orc_gguf_repack_q8a(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales), _ptr(offs))
     return codes, scales, offs
+
+
+# ---- convolution (implicit GEMM over the same weights) -----------------------------------------
+NORM = {None: 0, "none": 0, "group": 1, "layer": 2}
+
+
+def conv_out_size(H, W, ksz, stride):
+    """(oh, ow) with pad = ksz // 2."""
+    pad = ksz // 2
+    return (H + 2 * pad - ksz) // stride + 1, (W + 2 * pad - ksz) // stride + 1
+
+
+def conv_stats(X, npix, cin, groups, eps) -> np.ndarray:
+    """f64 [n][2] (mean, rstd): groups > 0 -> per group of cin / groups channels over all pixels;
+    groups == 0 -> per pixel over its cin channels."""
+    x = _c(X, np.float32)
+    n = groups if groups > 0 else npix
+    out = np.empty((n, 2), np.float64)
+    lib().orc_conv_stats(_ptr(x), npix, cin, groups, float(eps), _ptr(out))
+    return out
+
+
+def conv_gather(X, H, W, cin, ksz, stride, norm=None, groups=0, stats=None, gb=None, silu=False, ps=None):
+    """(A, M) f64 [len(ps)][ksz*ksz*cin]: the implicit GEMM's gathered input rows and their error
+    magnitudes (see orc_conv_gather)."""
+    x = _c(X, np.float32)
+    oh, ow = conv_out_size(H, W, ksz, stride)
+    psa = _c(np.arange(oh * ow) if ps is None else ps, np.int32)
+    K = ksz * ksz * cin
+    A = np.empty((psa.size, K), np.float64)
+    M = np.empty((psa.size, K), np.float64)
+    cpg = cin // groups if groups else 1
+    lib().orc_conv_gather(_ptr(x), H, W, cin, ksz, stride, NORM[norm], cpg, _ptr(_c(stats, np.float32)),
+                          _ptr(_c(gb, np.float32)), int(bool(silu)), _ptr(psa), psa.size, _ptr(A), _ptr(M))
+    return A, M
+
+
+def conv2d(fmt, codes, scales, offsets, group, n_out, X, H, W, cin, ksz, stride, norm=None, groups=0, stats=None,
+           gb=None, silu=False, ps=None, os_=None, threads=None):
+    """(Y, S) f64 [len(ps)][len(os)] (all output pixels / channels by default): Y[p][o] = the
+    convolution of the (normalised, activated) image with weight row o; S the error magnitude
+    sum_k M |v32|.  stats: f32 [n][2] (mean, rstd) as the convolution uses them."""
+    c, s, o = _weights(fmt, codes, scales, offsets)
+    x = _c(X, np.float32)
+    oh, ow = conv_out_size(H, W, ksz, stride)
+    psa = None if ps is None else _c(ps, np.int32)
+    osa = None if os_ is None else _c(os_, np.int32)
+    np_ = oh * ow if psa is None else psa.size
+    no = n_out if osa is None else osa.size
+    Y = np.empty((np_, no), np.float64)
+    S = np.empty((np_, no), np.float64)
+    cpg = cin // groups if groups else 1
+    if threads is None:
+        threads = default_threads()
+    lib().orc_conv2d(FMT[fmt], _ptr(c), _ptr(s), _ptr(o), group, n_out, _ptr(x), H, W, cin, ksz, stride, NORM[norm],
+                     cpg, _ptr(_c(stats, np.float32)), _ptr(_c(gb, np.float32)), int(bool(silu)), _ptr(psa),
+                     0 if psa is None else psa.size, _ptr(osa), 0 if osa is None else osa.size, _ptr(Y), _ptr(S),
+                     int(threads))
+    return Y, S

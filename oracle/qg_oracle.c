@@ -631,3 +631,126 @@ int orc_moe_ffn(int fmt, const void* const* gu_codes, const void* const* gu_scal
     free(o_all);
     return R;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Convolution as an implicit GEMM over the same quantized weights (page "oxinfer 0.0.5
+ * src/metal.rs": SHADER_SRC conv_body / CONV / norm4, group_stats and row_stats, and
+ * Backend::conv2d).
+ *   - X is one image [H][W][cin] (f32, channels innermost); the output has one row per output
+ *     pixel p = oy * ow + ox and one column per output channel o: Y[p][o].
+ *   - The weight row o has K = ksz * ksz * cin elements in the order (ky, kx, ci): element
+ *     k = (ky * ksz + kx) * cin + ci, decoded exactly as for the GEMM (v32).
+ *   - pad = ksz / 2; the input pixel of tap (ky, kx) is (oy * stride + ky - pad,
+ *     ox * stride + kx - pad); taps outside the image contribute 0 (they are not normalised).
+ *     Output size: oh = (H + 2 pad - ksz) / stride + 1, likewise ow (the page takes oh / ow
+ *     from its geometry record; this is the usual definition with that padding).
+ *   - Optional normalisation of each gathered input value v of channel c at input pixel q:
+ *     y = (v - mean) * rstd * gamma[c] + beta[c], with (mean, rstd) = stats[c / cpg] (group
+ *     norm, cpg channels per group) or stats[q] (layer norm over the cin channels of pixel q);
+ *     then optionally SiLU: y / (1 + exp(-y)).
+ *   - Statistics (group_stats / row_stats): two passes, mean = sum x / n, then
+ *     var = sum (x - mean)^2 / n, rstd = 1 / sqrt(var + eps), over the n values of the group
+ *     (all pixels, its cpg channels) or of the pixel (its cin channels).
+ * Arithmetic here: f64 throughout; the statistics the convolution uses are passed in as f32
+ * (the precision the device computes them in), widened exactly.
+ */
+
+/* (mean, rstd) pairs: groups > 0 -> one per group; groups == 0 -> one per pixel. */
+void orc_conv_stats(const float* X, int npix, int cin, int groups, double eps, double* out) {
+    if (groups > 0) {
+        const int cpg = cin / groups;
+        const double n = (double)npix * cpg;
+        for (int g = 0; g < groups; g++) {
+            double s = 0.0, v = 0.0;
+            for (int q = 0; q < npix; q++)
+                for (int c = g * cpg; c < (g + 1) * cpg; c++) s += (double)X[(size_t)q * cin + c];
+            const double mean = s / n;
+            for (int q = 0; q < npix; q++)
+                for (int c = g * cpg; c < (g + 1) * cpg; c++) {
+                    const double d = (double)X[(size_t)q * cin + c] - mean;
+                    v += d * d;
+                }
+            out[2 * g] = mean;
+            out[2 * g + 1] = 1.0 / sqrt(v / n + eps);
+        }
+    } else {
+        for (int q = 0; q < npix; q++) {
+            double s = 0.0, v = 0.0;
+            for (int c = 0; c < cin; c++) s += (double)X[(size_t)q * cin + c];
+            const double mean = s / cin;
+            for (int c = 0; c < cin; c++) {
+                const double d = (double)X[(size_t)q * cin + c] - mean;
+                v += d * d;
+            }
+            out[2 * q] = mean;
+            out[2 * q + 1] = 1.0 / sqrt(v / cin + eps);
+        }
+    }
+}
+
+/* The gathered input rows of the implicit GEMM for the output pixels ps[0..np-1]:
+ * A[i][k] = the (normalised, activated) input value of tap k for pixel ps[i], and
+ * M[i][k] = a magnitude that bounds the error of evaluating it in f32: |A| plus, when
+ * normalising, |v - mean| |rstd| |gamma| + |beta| + |y| (every term an f32 rounding touches). */
+void orc_conv_gather(const float* X, int H, int W, int cin, int ksz, int stride, int norm, int cpg,
+                     const float* stats, const float* gb, int silu, const int* ps, int np, double* A, double* M) {
+    const int pad = ksz / 2, ow = (W + 2 * pad - ksz) / stride + 1, K = ksz * ksz * cin;
+    for (int i = 0; i < np; i++) {
+        const int p = ps[i], oy = p / ow, ox = p % ow;
+        for (int ky = 0; ky < ksz; ky++)
+            for (int kx = 0; kx < ksz; kx++) {
+                const int iy = oy * stride + ky - pad, ix = ox * stride + kx - pad;
+                const int inside = iy >= 0 && iy < H && ix >= 0 && ix < W;
+                for (int c = 0; c < cin; c++) {
+                    const size_t k = (size_t)(ky * ksz + kx) * cin + c;
+                    double a = 0.0, m = 0.0;
+                    if (inside) {
+                        const double v = (double)X[((size_t)iy * W + ix) * cin + c];
+                        a = v;
+                        if (norm) {
+                            const int si = norm == 1 ? c / cpg : iy * W + ix;
+                            const double mean = (double)stats[2 * si], rstd = (double)stats[2 * si + 1];
+                            const double g = (double)gb[c], b = (double)gb[cin + c];
+                            const double y = (v - mean) * rstd * g + b;
+                            a = silu ? y / (1.0 + exp(-y)) : y;
+                            m = fabs(v - mean) * fabs(rstd) * fabs(g) + fabs(b) + fabs(y);
+                        }
+                        m += fabs(a);
+                    }
+                    A[(size_t)i * K + k] = a;
+                    M[(size_t)i * K + k] = m;
+                }
+            }
+    }
+}
+
+/* Y[i][j] = sum_k A[i][k] v32[os[j]][k] and S[i][j] = sum_k M[i][k] |v32[os[j]][k]| for the
+ * output pixels ps and output channels os (all of them when a list is NULL). */
+int orc_conv2d(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group, int n_out,
+               const float* X, int H, int W, int cin, int ksz, int stride, int norm, int cpg,
+               const float* stats, const float* gb, int silu, const int* ps, int np, const int* os, int nos,
+               double* Y, double* S, int nthreads) {
+    const int pad = ksz / 2;
+    const int oh = (H + 2 * pad - ksz) / stride + 1, ow = (W + 2 * pad - ksz) / stride + 1;
+    const int K = ksz * ksz * cin;
+    int* all = NULL;
+    if (!ps) {
+        np = oh * ow;
+        all = (int*)malloc(sizeof(int) * (size_t)np);
+        for (int i = 0; i < np; i++) all[i] = i;
+        ps = all;
+    }
+    double* A = (double*)malloc(sizeof(double) * (size_t)np * K);
+    double* M = (double*)malloc(sizeof(double) * (size_t)np * K);
+    orc_conv_gather(X, H, W, cin, ksz, stride, norm, cpg, stats, gb, silu, ps, np, A, M);
+    const int nn = os ? nos : n_out;
+    double* junk = (double*)malloc(sizeof(double) * (size_t)np * nn);
+    int used = orc_gemm(fmt, codes, scales, offs, group, n_out, K, A, ORC_F64, np, os, nos, NULL, 0, Y, NULL,
+                        nthreads);
+    orc_gemm(fmt, codes, scales, offs, group, n_out, K, M, ORC_F64, np, os, nos, NULL, 0, junk, S, nthreads);
+    free(junk);
+    free(M);
+    free(A);
+    free(all);
+    return used;
+}

@@ -641,3 +641,136 @@ def test_gguf_affine_repack_matches_direct_decode(orc, gtype):
     assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
     lo, hi = {"q4_1": (0, 15), "q5_0": (-16, 15), "q5_1": (0, 31), "q4_k": (0, 15)}[gtype]
     assert codes.min() >= lo and codes.max() <= hi
+
+
+# ---- convolution as an implicit GEMM (oxinfer src/metal.rs, SHADER_SRC conv_body / norm4,
+# group_stats / row_stats, Backend::conv2d) --------------------------------------------------------
+def _q8_onehot(n_out, K, entries):
+    """Q8 weights [n_out][K], scale 1, code q at (o, k) for (o, k, q) in entries, else 0."""
+    codes = np.zeros((n_out, K), np.int8)
+    for o, k, q in entries:
+        codes[o, k] = q
+    return codes.reshape(-1), np.ones(n_out * K // 32, np.float32)
+
+
+def test_conv_1x1_is_the_gemm_over_pixels(orc):
+    """A 1 x 1 convolution with stride 1 is the GEMM with the pixels as tokens, bit for bit."""
+    import synth
+    H, W, cin, n_out = 3, 5, 64, 40
+    w = synth.make_dense("q4", n_out, cin, H * W, "f32", 1.0, 61)
+    Yc, Sc = orc.conv2d("q4", w["codes"], w["scales"], None, 64, n_out, w["X"], H, W, cin, 1, 1)
+    Yg, Sg, _ = orc.gemm("q4", w["codes"], w["scales"], None, 64, n_out, cin, w["X"], "f32", H * W)
+    assert np.array_equal(Yc, Yg) and np.array_equal(Sc, Sg)
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_conv_one_hot_taps_and_zero_padding(orc, stride):
+    """Output channel o = (ky, kx, c) picks input channel c at tap (ky, kx): y[oy][ox] =
+    x[oy*s + ky - 1][ox*s + kx - 1][c], or 0 outside the image (3 x 3 kernel, pad 1).  Pins the
+    (ky, kx, ci) order of K, the sign of the tap offset, the padding and the output size."""
+    H, W, cin, ksz = 4, 5, 32, 3
+    K = ksz * ksz * cin
+    taps = [(ky, kx, c) for ky in range(3) for kx in range(3) for c in (0, 7, 31)]
+    codes, scales = _q8_onehot(len(taps), K, [(o, (ky * 3 + kx) * cin + c, 1) for o, (ky, kx, c) in enumerate(taps)])
+    X = (np.arange(H * W * cin, dtype=np.float32) + 1.0)         # distinct, exact values
+    Y, _ = orc.conv2d("q8", codes, scales, None, 64, len(taps), X, H, W, cin, ksz, stride)
+    oh, ow = (H - 1) // stride + 1, (W - 1) // stride + 1
+    assert orc.conv_out_size(H, W, ksz, stride) == (oh, ow) and Y.shape == (oh * ow, len(taps))
+    x = X.reshape(H, W, cin)
+    for oy in range(oh):
+        for ox in range(ow):
+            for o, (ky, kx, c) in enumerate(taps):
+                iy, ix = oy * stride + ky - 1, ox * stride + kx - 1
+                want = x[iy, ix, c] if 0 <= iy < H and 0 <= ix < W else 0.0
+                assert Y[oy * ow + ox, o] == want
+
+
+def test_conv_even_kernel_geometry(orc):
+    """ksz = 2: pad 1, output (H + 1) x (W + 1); tap (ky, kx) of pixel (oy, ox) reads x[oy + ky - 1][ox + kx - 1]."""
+    H, W, cin = 3, 2, 32
+    K = 4 * cin
+    codes, scales = _q8_onehot(4, K, [(o, o * cin + 5, 1) for o in range(4)])
+    X = np.arange(H * W * cin, dtype=np.float32) + 1.0
+    Y, _ = orc.conv2d("q8", codes, scales, None, 64, 4, X, H, W, cin, 2, 1)
+    assert orc.conv_out_size(H, W, 2, 1) == (4, 3)
+    x = X.reshape(H, W, cin)
+    for oy in range(4):
+        for ox in range(3):
+            for o in range(4):
+                iy, ix = oy + o // 2 - 1, ox + o % 2 - 1
+                want = x[iy, ix, 5] if 0 <= iy < H and 0 <= ix < W else 0.0
+                assert Y[oy * 3 + ox, o] == want
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_conv_matches_scipy_correlate(orc, stride):
+    """Random Q8 weights, 3 x 3 and 5 x 5 kernels: the sum over input channels of scipy's 2-D
+    cross-correlation ('same', zero fill) of each channel with the decoded kernel slice, taken at
+    every stride-th pixel."""
+    from scipy.signal import correlate2d
+    import synth
+    rng = np.random.default_rng(3 + stride)
+    for ksz in (3, 5):
+        H, W, cin, n_out = 7, 6, 32, 3
+        K = ksz * ksz * cin
+        w = synth.make_dense("q8", n_out, K, 1, "f32", 1.0, 70 + ksz)
+        X = rng.standard_normal(H * W * cin).astype(np.float32)
+        Y, _ = orc.conv2d("q8", w["codes"], w["scales"], None, 64, n_out, X, H, W, cin, ksz, stride)
+        Wd = orc.dequant_tile("q8", w["codes"], w["scales"], None, 64, n_out, K, 0, 0, n_out, K, "f32")
+        Wd = Wd.astype(np.float64).reshape(n_out, ksz, ksz, cin)
+        x = X.reshape(H, W, cin).astype(np.float64)
+        oh, ow = orc.conv_out_size(H, W, ksz, stride)
+        for o in range(n_out):
+            ref = sum(correlate2d(x[:, :, c], Wd[o, :, :, c], mode="same", boundary="fill") for c in range(cin))
+            ref = ref[::stride, ::stride]
+            assert ref.shape == (oh, ow)
+            np.testing.assert_allclose(Y[:, o].reshape(oh, ow), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_conv_stats_against_numpy(orc):
+    """Group statistics over (all pixels, the group's channels) and per-pixel statistics over the
+    channels: mean and 1 / sqrt(var + eps) with the population variance, as numpy computes them."""
+    rng = np.random.default_rng(9)
+    npix, cin, groups, eps = 37, 64, 8, 1e-5
+    X = (rng.standard_normal(npix * cin) * 3 + 1).astype(np.float32)
+    x = X.reshape(npix, cin).astype(np.float64)
+    g = orc.conv_stats(X, npix, cin, groups, eps)
+    xg = x.reshape(npix, groups, cin // groups)
+    np.testing.assert_allclose(g[:, 0], xg.mean(axis=(0, 2)), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(g[:, 1], 1 / np.sqrt(xg.var(axis=(0, 2)) + eps), rtol=1e-12)
+    l = orc.conv_stats(X, npix, cin, 0, eps)
+    np.testing.assert_allclose(l[:, 0], x.mean(axis=1), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l[:, 1], 1 / np.sqrt(x.var(axis=1) + eps), rtol=1e-12)
+    c = orc.conv_stats(np.full(npix * cin, 2.5, np.float32), npix, cin, 4, 0.25)   # constant image
+    assert np.all(c[:, 0] == 2.5) and np.all(c[:, 1] == 2.0)
+
+
+def test_conv_normalised_gather_closed_forms(orc):
+    """The gathered value of a normalised tap: y = (v - mean) rstd gamma + beta, then SiLU; padding
+    taps stay 0 (not beta); group norm takes stats[c // cpg], layer norm stats[input pixel]."""
+    H, W, cin = 1, 2, 32
+    X = np.zeros(H * W * cin, np.float32)
+    X[0 * cin + 3] = 2.0          # pixel 0, channel 3
+    X[1 * cin + 3] = 5.0          # pixel 1, channel 3
+    gb = np.zeros(2 * cin, np.float32)
+    gb[3], gb[cin + 3] = 3.0, -1.0                 # gamma 3, beta -1 on channel 3
+    # group norm, 4 groups of 8 channels: channel 3 -> group 0 (mean 1, rstd 2)
+    st = np.array([[1.0, 2.0], [9.0, 9.0], [9.0, 9.0], [9.0, 9.0]], np.float32)
+    A, M = orc.conv_gather(X, H, W, cin, 3, 1, "group", 4, st, gb, False, ps=[0])
+    # pixel 0's centre tap (ky = kx = 1) reads pixel 0; tap (1, 2) reads pixel 1; tap (0, 0) is padding
+    centre, right, pad = (1 * 3 + 1) * cin + 3, (1 * 3 + 2) * cin + 3, 3
+    assert A[0, centre] == (2.0 - 1.0) * 2.0 * 3.0 - 1.0 == 5.0
+    assert A[0, right] == (5.0 - 1.0) * 2.0 * 3.0 - 1.0
+    assert A[0, pad] == 0.0 and M[0, pad] == 0.0
+    assert A[0, centre + 1] == (0.0 - 9.0) * 9.0 * 0.0 + 0.0      # gamma 0, beta 0 on channel 4
+    As, _ = orc.conv_gather(X, H, W, cin, 3, 1, "group", 4, st, gb, True, ps=[0])
+    assert As[0, centre] == 5.0 / (1.0 + math.exp(-5.0))
+    assert As[0, centre + 1] == 0.0                                 # SiLU(0) = 0
+    # layer norm: stats per input pixel
+    sl = np.array([[1.0, 2.0], [4.0, 0.5]], np.float32)
+    Al, Ml = orc.conv_gather(X, H, W, cin, 3, 1, "layer", 0, sl, gb, False, ps=[0])
+    assert Al[0, centre] == (2.0 - 1.0) * 2.0 * 3.0 - 1.0
+    assert Al[0, right] == (5.0 - 4.0) * 0.5 * 3.0 - 1.0
+    assert np.all(Ml >= np.abs(Al))
+    A0, M0 = orc.conv_gather(X, H, W, cin, 3, 1)
+    assert np.array_equal(M0, np.abs(A0))
