@@ -12,7 +12,7 @@ of the C entry point (arguments marshalled beforehand), so the host side keeps a
 CPU oracle on the host cores.
 `also` lists the prefill GEMMs (TFLOP/s vs the MFMA peak; the Q8 prefill shape in both fast modes,
 weights rounded to f16 and kept exact), the MoE expert block (GB/s), the GGUF
-Q4_0 repack of a 4096 x 4096 matrix (GB/s), a batched q / k / v decode step (GB/s, with the time
+Q4_0 repack of a 4096 x 4096 matrix (GB/s), a 3 x 3 convolution with group norm and SiLU (TFLOP/s), a batched q / k / v decode step (GB/s, with the time
 of the same three matrices as separate calls) and the Q8 GEMV with T = 4 (GB/s), each on
 its own synthetic workload; `--workload` selects one of them as the headline instead.
 """
@@ -324,6 +324,41 @@ def measure_q8_prefill(mode: str, steps: int, warmup: int) -> dict:
             "value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK["f16"], "frac": tf / PEAK["f16"]}
 
 
+def measure_conv(steps: int, warmup: int) -> dict:
+    """A 3 x 3 convolution over a 64 x 64 image with 256 input and 256 output channels, Q4 weights
+    (N(0, 1) f32 input, group norm over 32 groups with SiLU on the gathered input, exact mode): one step
+    is the normalisation statistics (qg_conv_stats) and the implicit-GEMM convolution (qg_conv2d).
+    TFLOP/s of the convolution's 2 * pixels * n_out * K flop against the f32 MFMA peak."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    H = W = 64
+    cin, n_out, ksz, groups = 256, 256, 3, 32
+    K = ksz * ksz * cin
+    w = synth.make_dense("q4", n_out, K, 1, "f32", 1.0, 1501)
+    X = _dev(synth.normal_as(1501, synth.STREAM_X, H * W * cin, 0.0, 1.0, "f32"))
+    gb = _dev(np.concatenate([np.ones(cin, np.float32), np.zeros(cin, np.float32)]))
+    C_, S_ = _dev(w["codes"]), _dev(w["scales"])
+    st_buf = torch.empty((groups, 2), device="cuda")
+    Y = torch.empty((H * W, n_out), device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    stats = _bound("qg_conv_stats", X.data_ptr(), H * W, cin, groups, 1e-5, st_buf.data_ptr(), st)
+    conv = _bound("qg_conv2d", qg.QG_FMT_Q4, C_.data_ptr(), S_.data_ptr(), X.data_ptr(), H, W, cin, ksz, 1, n_out, 1,
+                  groups, st_buf.data_ptr(), gb.data_ptr(), 1, Y.data_ptr(), qg.QG_EXACT, st)
+
+    def step(i):
+        stats(i)
+        conv(i)
+    ms, _ = _timed(step, steps, warmup)
+    ms_conv, _ = _timed(conv, steps, warmup)
+    flops = 2.0 * H * W * n_out * K
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "conv3x3_q4_gn_silu", "config": "conv_q4_H64_W64_cin256_k3_nout256_group32_silu",
+            "mode": "exact", "ms_per_step": ms, "us_per_step": ms * 1e3, "us_conv_only": ms_conv * 1e3,
+            "dtype": "f32", "kernel": "gemm_exact_kernel (tap gather)", "value": tf, "unit": "TFLOP/s",
+            "bound": "mfma", "peak": PEAK["f32"], "frac": tf / PEAK["f32"], "flops_per_step": flops}
+
+
 def measure_repack(steps: int, warmup: int) -> dict:
     """GGUF Q4_0 -> split-layout repack of a 4096 x 4096 matrix (an upload-time step): GB/s of the
     bytes it reads (18 per block) and writes (16 code bytes and a 2-byte scale per block)."""
@@ -512,6 +547,8 @@ def main():
             also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
             torch.cuda.empty_cache()
         r = measure_repack(256, 20)
+        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        r = measure_conv(128, 20)
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         r = measure_batch(512, 50)
         r.pop("keep")

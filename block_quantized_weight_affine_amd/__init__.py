@@ -33,7 +33,7 @@ SYMBOLS = [
     "qg_strerror", "qg_abi_version",
     "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_q8a", "qgemm_batch",
     "qgemv_q4", "qgemv_q4a", "qgemv_q8", "qgemv_q8a",
-    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a",
+    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a", "qg_conv_stats", "qg_conv2d",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn", "qg_moe_ffn_noalloc",
 ]
@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
         L.qgemm_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _p]
         L.qgemv_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _p]
         L.qg_repack_gguf_q8a.argtypes = [_i, _p, _i, _i, _p, _p, _p, _p]
+        L.qg_conv_stats.argtypes = [_p, _i, _i, _i, C.c_float, _p, _p]
+        L.qg_conv2d.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p]
         L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
         L.qg_moe_plan_host.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p]
         L.qg_repack_gguf.argtypes = [_i, _p, _i, _i, _p, _p, _p]
@@ -241,6 +243,33 @@ def qg_repack_gguf_q8a(gtype, src, N, K, codes, scales, offsets, stream=None):
     _check(lib().qg_repack_gguf_q8a(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K,
                                     _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)),
            "qg_repack_gguf_q8a")
+
+
+# ---- convolution ------------------------------------------------------------------------------------
+CONV_NORM = {None: 0, "none": 0, "group": 1, "layer": 2}
+
+
+def conv_out_size(H, W, ksize, stride):
+    """(oh, ow) of qg_conv2d: pad = ksize // 2."""
+    pad = ksize // 2
+    return (H + 2 * pad - ksize) // stride + 1, (W + 2 * pad - ksize) // stride + 1
+
+
+def qg_conv_stats(X, npix, cin, groups, eps, stats, stream=None):
+    """(mean, rstd) f32 pairs of the image X [npix][cin] into stats (device): per group of
+    cin / groups channels (groups > 0) or per pixel (groups == 0)."""
+    _check(lib().qg_conv_stats(_ptr(X), npix, cin, groups, float(eps), _ptr(stats), _stream(stream)),
+           "qg_conv_stats")
+
+
+def qg_conv2d(fmt, codes, scales, X, H, W, cin, ksize, stride, n_out, Y, norm=None, groups=0, stats=None,
+              gamma_beta=None, silu=False, mode="exact", stream=None):
+    """Implicit-GEMM convolution of the image X [H][W][cin] (f32) with the quantized weight matrix
+    [n_out][ksize * ksize * cin] into Y [oh * ow][n_out] (device tensors)."""
+    _check(lib().qg_conv2d(FMT[fmt] if isinstance(fmt, str) else fmt, _ptr(codes), _ptr(scales), _ptr(X), H, W, cin,
+                           ksize, stride, n_out, CONV_NORM[norm] if not isinstance(norm, int) else norm, groups,
+                           _ptr(stats), _ptr(gamma_beta), int(bool(silu)), _ptr(Y), _mode(mode), _stream(stream)),
+           "qg_conv2d")
 
 
 # ---- MoE ----------------------------------------------------------------------------------------

@@ -272,6 +272,53 @@ qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, i
     return launched(qg::launch_repack_gguf_q8a(type, src, nblocks, codes, scales_f32, offsets_f32, stream));
 }
 
+qg_status qg_conv_stats(const float* X, int npix, int cin, int groups, float eps, float* stats, hipStream_t stream) {
+    if (npix < 1 || npix > (1 << 26) || cin < 1 || cin > kMaxK || groups < 0 || groups > kMaxGridY ||
+        (groups > 0 && (cin % groups) != 0) || (int64_t)npix * cin >= ((int64_t)1 << 31))
+        return QG_ESHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return QG_EINVAL;
+    if (!X || !stats) return QG_EINVAL;
+    if (!aligned(X, 4) || !aligned(stats, 4)) return QG_EALIGN;
+    return launched(qg::launch_conv_stats(X, npix, cin, groups, eps, stats, stream));
+}
+
+qg_status qg_conv2d(qg_format fmt, const void* codes, const void* scales, const float* X, int H, int W, int cin,
+                    int ksize, int stride, int n_out, int norm, int groups, const float* stats,
+                    const float* gamma_beta, int silu, float* Y, qg_mode mode, hipStream_t stream) {
+    if (!fmt_ok(fmt) || !mode_ok(mode) || norm < 0 || norm > 2 || (silu != 0 && silu != 1)) return QG_EINVAL;
+    if (silu && norm == 0) return QG_EINVAL;
+    if ((fmt != QG_FMT_Q4 && fmt != QG_FMT_Q8) || mode != QG_EXACT) return QG_EUNSUPPORTED;
+    if (H < 1 || W < 1 || (int64_t)H * W > ((int64_t)1 << 26) || cin < 32 || (cin % 32) != 0 || ksize < 1 ||
+        ksize > 64 || stride < 1 || n_out < 1 || n_out > kMaxN || (int64_t)H * W * cin >= ((int64_t)1 << 31))
+        return QG_ESHAPE;
+    const int64_t K = (int64_t)ksize * ksize * cin;
+    if (K > kMaxK) return QG_ESHAPE;
+    const int pad = ksize / 2;
+    const int oh = (H + 2 * pad - ksize) / stride + 1, ow = (W + 2 * pad - ksize) / stride + 1;
+    const int64_t R = (int64_t)oh * ow;
+    if (R > kMaxT || (R + 31) / 32 > kMaxGridY) return QG_ESHAPE;
+    if (norm == 1 && (groups < 1 || (cin % groups) != 0)) return QG_ESHAPE;
+    if (!codes || !scales || !X || !Y || (norm && (!stats || !gamma_beta))) return QG_EINVAL;
+    if (!aligned(codes, 16) || !aligned(scales, scale_bytes(fmt)) || !aligned(X, 16) || !aligned(Y, 4) ||
+        (norm && (!aligned(stats, 4) || !aligned(gamma_beta, 4))))
+        return QG_EALIGN;
+    GemmParams p = dense_params(codes, scales, nullptr, 64, X, Y, n_out, (int)K, (int)R);
+    qg::ConvParams cv{};
+    cv.H = H;
+    cv.W = W;
+    cv.cin = cin;
+    cv.ksz = ksize;
+    cv.stride = stride;
+    cv.pad = pad;
+    cv.ow = ow;
+    cv.norm = norm;
+    cv.cpg = norm == 1 ? cin / groups : 1;
+    cv.silu = silu;
+    cv.stats = stats;
+    cv.gb = gamma_beta;
+    return launched(qg::launch_conv_exact(fmt, p, cv, stream));
+}
+
 qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                       int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, hipStream_t stream) {
     if (T < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32 || (long)T * k > 16384) return QG_ESHAPE;

@@ -968,8 +968,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
 
 // ================================================================================================
 // Exact mode: f32 MFMA (v_mfma_f32_32x32x2_f32), f32 accumulation; X f32, f16 or bf16 widened.
-template <int FMT, int XT, int MT, int MN>
-__global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool grouped) {
+// CV: the convolution (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC conv_body and norm4): the X tile
+// of output pixel r and 8 values of K starting at k is the image's channel slice ci .. ci + 7 of tap
+// (ky, kx) = divmod(k / cin, ksz) (cin % 32 == 0, so a slice never crosses a tap) at input pixel
+// (oy * stride + ky - pad, ox * stride + kx - pad), zeros outside the image; with normalisation the
+// loaded values are normalised (and SiLU applied) when they are stored to LDS, after the stage's
+// MFMAs, so the loads keep their latency hidden as in the GEMM.
+// Per-channel normalisation parameters of the convolution in LDS (cin <= kConvLdsCin): group norm
+// keeps mean_c, rstd_c * gamma_c and beta_c; layer norm gamma_c and beta_c (its (mean, rstd) pair
+// is per input pixel and travels with the chunk's loads).
+constexpr int kConvLdsCin = 1024;
+__device__ __forceinline__ float* conv_norm_lds() {
+    __shared__ __attribute__((aligned(16))) float b[3 * kConvLdsCin];
+    return b;
+}
+
+// SiLU as y / (1 + exp(-y)) with the hardware exponential and reciprocal (a few ulp of the result;
+// large negative y give exp = inf and the result -0).
+__device__ __forceinline__ float conv_silu(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
+
+template <int FMT, int XT, int MT, int MN, bool CV = false>
+__global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool grouped, ConvParams cv) {
     constexpr int BT = 32 * MT;
     constexpr int BN = 4 * 32 * MN;
     constexpr int PITCH = 68;  // floats per LDS row: 64 + 4 (16-byte pad)
@@ -993,27 +1012,110 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
     // X staging in 8-element chunks: chunk c -> tile row c / 8, columns 8 * (c % 8) .. +7.
     constexpr int XCH = BT * 8 / kThreads;
     int xrow[XCH];
+    int cy[XCH], cx[XCH];  // CV: input position of tap (0, 0) for the chunk's output pixel
+    int cq[XCH], cc[XCH];  // CV: input pixel and channel of the chunk loaded last (cq < 0: zeros)
+    float cm[XCH], cr[XCH];  // CV, layer norm: (mean, rstd) of that input pixel
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
         const int c = tid + i * kThreads;
         xrow[i] = x_row_of(p, min(r0 + c / 8, r1 - 1));
+        if constexpr (CV) {
+            const int oy = xrow[i] / cv.ow, ox = xrow[i] - oy * cv.ow;
+            cy[i] = oy * cv.stride - cv.pad;
+            cx[i] = ox * cv.stride - cv.pad;
+        }
+    }
+    // CV with normalisation and cin <= kConvLdsCin: the per-channel parameters once per workgroup
+    bool norm_lds = false;
+    float* nl = nullptr;
+    if constexpr (CV) {
+        norm_lds = cv.norm != 0 && cv.cin <= kConvLdsCin;
+        if (norm_lds) {
+            nl = conv_norm_lds();
+            for (int ch = tid; ch < cv.cin; ch += kThreads) {
+                if (cv.norm == 1) {
+                    const int sg = ch / cv.cpg;
+                    nl[ch] = cv.stats[2 * sg];
+                    nl[kConvLdsCin + ch] = cv.stats[2 * sg + 1] * cv.gb[ch];
+                } else {
+                    nl[kConvLdsCin + ch] = cv.gb[ch];
+                }
+                nl[2 * kConvLdsCin + ch] = cv.gb[cv.cin + ch];
+            }
+            __syncthreads();
+        }
     }
     auto load_x = [&](int s, float (&v)[XCH][8]) {
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * kThreads;
             const int k = s * 64 + 8 * (c & 7);
-            if (xrow[i] >= 0 && k < K)
-                x_load8<XT>(p.X, (size_t)xrow[i] * K + k, v[i]);
-            else
+            if constexpr (CV) {
+                cq[i] = -1;
+                if (xrow[i] >= 0 && k < K) {
+                    const int tap = k / cv.cin, ci = k - tap * cv.cin;
+                    const int ky = tap / cv.ksz, kx = tap - ky * cv.ksz;
+                    const int iy = cy[i] + ky, ix = cx[i] + kx;
+                    if ((unsigned)iy < (unsigned)cv.H && (unsigned)ix < (unsigned)cv.W) {
+                        cq[i] = iy * cv.W + ix;
+                        cc[i] = ci;
+                    }
+                }
+                if (cq[i] >= 0 && cv.norm == 2) {
+                    cm[i] = cv.stats[2 * cq[i]];
+                    cr[i] = cv.stats[2 * cq[i] + 1];
+                }
+                if (cq[i] >= 0)
+                    x_load8<XT_F32>(p.X, (size_t)cq[i] * cv.cin + cc[i], v[i]);
+                else
 #pragma unroll
-                for (int j = 0; j < 8; j++) v[i][j] = 0.f;
+                    for (int j = 0; j < 8; j++) v[i][j] = 0.f;
+            } else {
+                if (xrow[i] >= 0 && k < K)
+                    x_load8<XT>(p.X, (size_t)xrow[i] * K + k, v[i]);
+                else
+#pragma unroll
+                    for (int j = 0; j < 8; j++) v[i][j] = 0.f;
+            }
         }
     };
-    auto store_x = [&](int buf, const float (&v)[XCH][8]) {
+    auto store_x = [&](int buf, float (&v)[XCH][8]) {
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * kThreads;
+            if constexpr (CV) {
+                // norm4: y = (v - mean) * rstd * gamma + beta, then SiLU; padding taps stay zero
+                if (norm_lds && cq[i] >= 0) {
+                    const float* pa = nl + kConvLdsCin + cc[i];
+                    const float* pb = nl + 2 * kConvLdsCin + cc[i];
+                    const float4 a0 = *(const float4*)pa, a1 = *(const float4*)(pa + 4);
+                    const float4 b0 = *(const float4*)pb, b1 = *(const float4*)(pb + 4);
+                    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                    if (cv.norm == 1) {
+                        const float4 m0 = *(const float4*)(nl + cc[i]), m1 = *(const float4*)(nl + cc[i] + 4);
+                        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+                        for (int j = 0; j < 8; j++) v[i][j] = fmaf(v[i][j] - mv[j], av[j], bv[j]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; j++) v[i][j] = fmaf((v[i][j] - cm[i]) * cr[i], av[j], bv[j]);
+                    }
+                    if (cv.silu)
+#pragma unroll
+                        for (int j = 0; j < 8; j++) v[i][j] = conv_silu(v[i][j]);
+                } else if (cv.norm && cq[i] >= 0) {
+                    // cin past the LDS staging: parameters straight from memory
+#pragma unroll
+                    for (int j = 0; j < 8; j++) {
+                        const int ch = cc[i] + j;
+                        const int si = cv.norm == 1 ? ch / cv.cpg : cq[i];
+                        const float y = fmaf((v[i][j] - cv.stats[2 * si]) * cv.stats[2 * si + 1], cv.gb[ch],
+                                             cv.gb[cv.cin + ch]);
+                        v[i][j] = cv.silu ? conv_silu(y) : y;
+                    }
+                }
+            }
             float4* d = (float4*)(&xs[buf][(c >> 3) * PITCH + 8 * (c & 7)]);
             d[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
             d[1] = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
@@ -1197,7 +1299,7 @@ hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, 
 template <int FMT, int XT, int MT, int MN>
 static void exact_launch(const GemmParams& p, bool grouped, hipStream_t s) {
     dim3 grid((p.N + 128 * MN - 1) / (128 * MN), grid_rows(p, grouped, 32 * MT));
-    hipLaunchKernelGGL((gemm_exact_kernel<FMT, XT, MT, MN>), grid, dim3(kThreads), 0, s, p, grouped);
+    hipLaunchKernelGGL((gemm_exact_kernel<FMT, XT, MT, MN>), grid, dim3(kThreads), 0, s, p, grouped, ConvParams{});
 }
 
 template <int FMT, int XT>
@@ -1217,6 +1319,26 @@ static void exact_xt(int xt, const GemmParams& p, bool grouped, hipStream_t s) {
     if (xt == XT_F32) exact_pick<FMT, XT_F32>(p, grouped, s);
     else if (xt == XT_F16) exact_pick<FMT, XT_F16>(p, grouped, s);
     else exact_pick<FMT, XT_BF16>(p, grouped, s);
+}
+
+template <int FMT>
+static void conv_pick(const GemmParams& p, const ConvParams& cv, hipStream_t s) {
+    // the exact kernel's tile rule
+    const long mid = (long)((p.N + 127) / 128) * ((p.R + 63) / 64);
+    if (mid >= 1024) {
+        dim3 grid((p.N + 127) / 128, (p.R + 63) / 64);
+        hipLaunchKernelGGL((gemm_exact_kernel<FMT, XT_F32, 2, 1, true>), grid, dim3(kThreads), 0, s, p, false, cv);
+    } else {
+        dim3 grid((p.N + 127) / 128, (p.R + 31) / 32);
+        hipLaunchKernelGGL((gemm_exact_kernel<FMT, XT_F32, 1, 1, true>), grid, dim3(kThreads), 0, s, p, false, cv);
+    }
+}
+
+hipError_t launch_conv_exact(int fmt, const GemmParams& p, const ConvParams& cv, hipStream_t s) {
+    if (fmt == FMT_Q4) conv_pick<FMT_Q4>(p, cv, s);
+    else if (fmt == FMT_Q8) conv_pick<FMT_Q8>(p, cv, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s) {

@@ -32,6 +32,17 @@ struct GemmParams {
     int x_rows;                  // rows of X (bounds for row_src)
 };
 
+// Convolution as an implicit GEMM (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC conv_body / CP):
+// output row r of the GEMM is output pixel r = oy * ow + ox, K runs over (ky, kx, ci), and X is the
+// image [H][W][cin] in f32.  norm 1: group norm with stats[c / cpg]; 2: layer norm with stats[input
+// pixel]; stats are (mean, rstd) f32 pairs, gb gamma[cin] then beta[cin]; silu applies SiLU after.
+struct ConvParams {
+    int H, W, cin, ksz, stride, pad, ow;
+    int norm, cpg, silu;
+    const float* stats;
+    const float* gb;
+};
+
 // Several weight matrices sharing one X row in one T = 1 launch: job j owns the global output rows
 // [start[j], start[j+1]) and writes them to Y[j] (page "oxinfer 0.0.5 src/metal.rs",
 // Backend::matmul, whose jobs share X).  Passed by value in the kernel arguments.
@@ -48,6 +59,12 @@ struct BatchJobs {
 // Kernel launchers; each returns a hipError_t from hipGetLastError after the launch.
 hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, hipStream_t s);
 hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
+// The convolution through the exact kernel (f32 X gathered per tap; Q4 / Q8 weights); p.R = oh * ow
+// output pixels, p.N output channels, p.K = ksz * ksz * cin.
+hipError_t launch_conv_exact(int fmt, const GemmParams& p, const ConvParams& cv, hipStream_t s);
+// (mean, rstd) pairs of the image [npix][cin]: groups > 0 per group (all pixels, cin / groups
+// channels), groups == 0 per pixel.
+hipError_t launch_conv_stats(const float* X, int npix, int cin, int groups, float eps, float* stats, hipStream_t s);
 // Dense fast matmul with the weights kept exact (Q4 / Q8 codes as f16, f16 X, block scale on the f32
 // block partial); hipErrorInvalidValue for another format.
 hipError_t launch_gemm_fast_wexact(int fmt, const GemmParams& p, hipStream_t s);

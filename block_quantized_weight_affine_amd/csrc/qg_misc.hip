@@ -422,6 +422,94 @@ __global__ void repack_gguf_kernel(const uint16_t* src, size_t nblocks, uint8_t*
     }
 }
 
+// ---- normalisation statistics of the convolution input ---------------------------------------------
+// Page "oxinfer 0.0.5 src/metal.rs", group_stats and row_stats: two passes, the mean first, then the
+// mean squared deviation from it; rstd = 1 / sqrt(var + eps).  Group statistics: one workgroup of
+// 1024 threads per group walks the group's npix x cpg values (consecutive threads on consecutive
+// values: a pixel's cpg channels are contiguous), the (pixel, channel) position advanced by
+// additions instead of a division per value; per-pixel statistics: one wavefront per pixel over its
+// cin channels.  f32 sums: each thread strided, then the wavefront by xor shuffles, then the
+// wavefronts through LDS in a fixed order.
+constexpr int kStatsThreads = 1024;
+
+__device__ __forceinline__ float block_sum_stats(float v, float* red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStatsThreads / 64; w++) t += red[w];
+    return t;
+}
+
+template <bool DEV>
+__device__ __forceinline__ float group_pass(const float* X, int npix, int cin, int cpg, int g, float mean) {
+    // thread t starts at value t of the group: pixel t / cpg, channel t % cpg, and steps by 1024
+    const int dq = kStatsThreads / cpg, dj = kStatsThreads % cpg;
+    int q = threadIdx.x / cpg, j = threadIdx.x % cpg;
+    float s = 0.f;
+    const float* base = X + (size_t)g * cpg;
+    while (q < npix) {
+        const float x = base[(size_t)q * cin + j];
+        if constexpr (DEV) {
+            const float d = x - mean;
+            s += d * d;
+        } else {
+            s += x;
+        }
+        q += dq;
+        j += dj;
+        if (j >= cpg) {
+            j -= cpg;
+            q += 1;
+        }
+    }
+    return s;
+}
+
+__global__ __launch_bounds__(kStatsThreads) void conv_group_stats_kernel(const float* X, int npix, int cin, int cpg,
+                                                                         float eps, float* stats) {
+    __shared__ float red[kStatsThreads / 64];
+    const int g = blockIdx.x;
+    const float total = (float)npix * (float)cpg;
+    const float mean = block_sum_stats(group_pass<false>(X, npix, cin, cpg, g, 0.f), red) / total;
+    const float var = block_sum_stats(group_pass<true>(X, npix, cin, cpg, g, mean), red) / total;
+    if (threadIdx.x == 0) {
+        stats[2 * g] = mean;
+        stats[2 * g + 1] = 1.0f / sqrtf(var + eps);
+    }
+}
+
+__global__ __launch_bounds__(256) void conv_pixel_stats_kernel(const float* X, int npix, int cin, float eps,
+                                                               float* stats) {
+    const int q = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (q >= npix) return;  // wave-uniform: the wavefront's pixel
+    const float* row = X + (size_t)q * cin;
+    float s = 0.f;
+    for (int c = lane; c < cin; c += 64) s += row[c];
+    const float mean = wave_sum(s) / (float)cin;
+    float v = 0.f;
+    for (int c = lane; c < cin; c += 64) {
+        const float d = row[c] - mean;
+        v += d * d;
+    }
+    const float var = wave_sum(v) / (float)cin;
+    if (lane == 0) {
+        stats[2 * q] = mean;
+        stats[2 * q + 1] = 1.0f / sqrtf(var + eps);
+    }
+}
+
+hipError_t launch_conv_stats(const float* X, int npix, int cin, int groups, float eps, float* stats, hipStream_t s) {
+    if (groups > 0)
+        hipLaunchKernelGGL(conv_group_stats_kernel, dim3(groups), dim3(kStatsThreads), 0, s, X, npix, cin,
+                           cin / groups, eps, stats);
+    else
+        hipLaunchKernelGGL(conv_pixel_stats_kernel, dim3((npix + 3) / 4), dim3(256), 0, s, X, npix, cin, eps, stats);
+    return hipGetLastError();
+}
+
 // ---- GGUF affine blocks -> Q8A ----------------------------------------------------------------------
 // Page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC, the loaders of Q4_1, Q5_0, Q5_1 (load_q45) and
 // Q4_K (with its 6-bit scale / min unpacking).  Each of these types gives element e of a 32-element

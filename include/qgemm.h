@@ -221,6 +221,45 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
 qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
                              float* scales_f32, float* offsets_f32, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Convolution as an implicit GEMM over the same quantized weights (page "oxinfer 0.0.5
+ * src/metal.rs": SHADER_SRC conv_body / CONV / norm4, group_stats and row_stats, and
+ * Backend::conv2d).
+ *
+ * qg_conv2d: X is one image [H][W][cin] f32 (channels innermost, 16-byte aligned); the weights are
+ * a Q4 (uint16 f16 scales) or Q8 (f32 scales) matrix [n_out][K] in this library's layout with
+ * K = ksize * ksize * cin in the order (ky, kx, ci).  pad = ksize / 2; oh = (H + 2 pad - ksize) /
+ * stride + 1, likewise ow; Y f32 [oh * ow][n_out] (output pixel oy * ow + ox, then channel):
+ *     Y[p][o] = sum_{ky, kx, ci} w(o, (ky * ksize + kx) * cin + ci) * x'(oy*stride + ky - pad,
+ *                                                                       ox*stride + kx - pad, ci),
+ * where x' is 0 outside the image and otherwise the input value, normalised when norm != 0:
+ * y = (x - mean) * rstd * gamma[ci] + beta[ci] with (mean, rstd) = stats[ci / (cin / groups)]
+ * (norm 1, group norm) or stats[iy * W + ix] (norm 2, per-pixel layer norm), then SiLU
+ * y / (1 + exp(-y)) when silu = 1 (silu needs norm != 0, as on the page).  stats f32 pairs
+ * (mean, rstd) [groups or H*W][2] (qg_conv_stats), gamma_beta f32 [2 * cin] (gamma then beta);
+ * both read only when norm != 0.  Exact mode only (f32 MFMA, the exact GEMM kernel with the tap
+ * gather in its X staging; QG_FAST / QG_FAST_WEXACT give QG_EUNSUPPORTED), Q4 / Q8 only (affine
+ * formats give QG_EUNSUPPORTED, as the page has no affine convolution kernel).  Tolerance as the
+ * dense matmul in exact mode.  Checks, before any HIP call: cin % 32 == 0, cin >= 32, ksize 1..64,
+ * stride >= 1, H * W <= 2^26, H * W * cin < 2^31, K <= 2^20, oh * ow <= 2^21 (else QG_ESHAPE);
+ * norm 1 needs groups >= 1 dividing cin (QG_ESHAPE); a null pointer, an unknown norm or silu
+ * without norm give QG_EINVAL; codes and X 16-byte, scales 2 / 4-byte, Y, stats and gamma_beta
+ * 4-byte aligned (QG_EALIGN).  Asynchronous on `stream`; nothing is allocated.
+ *
+ * qg_conv_stats: the page's two-pass statistics of X [npix][cin] in f32: mean = sum x / n, then
+ * var = sum (x - mean)^2 / n and rstd = 1 / sqrt(var + eps), written as (mean, rstd) to
+ * stats[j][2]: groups > 0 -> one pair per group j of cin / groups channels over all npix pixels
+ * (groups must divide cin); groups == 0 -> one pair per pixel over its cin channels.  Each sum is an
+ * f32 sum in a fixed order (error at most (n / 1024 + 24) 2^-24 of sum |x| for the group
+ * statistics, (n / 64 + 8) 2^-24 per pixel).  npix >= 1, cin >= 1, npix * cin < 2^31 (QG_ESHAPE);
+ * eps finite and >= 0, X and stats non-null (QG_EINVAL); 4-byte aligned (QG_EALIGN). */
+qg_status qg_conv_stats(const float* X, int npix, int cin, int groups, float eps, float* stats,
+                        hipStream_t stream);
+qg_status qg_conv2d(qg_format fmt, const void* codes, const void* scales, const float* X, int H, int W,
+                    int cin, int ksize, int stride, int n_out, int norm, int groups,
+                    const float* stats, const float* gamma_beta, int silu, float* Y, qg_mode mode,
+                    hipStream_t stream);
+
 /* Routing plan, on the HOST (all pointers host memory).  logits f32 [T][E].  For each token:
  * the k largest logits, equal logits in ascending expert index; weight_j = exp(l_j - l_max) /
  * sum over the k kept of exp(l_i - l_max).  Outputs: seg_off [E+1] (expert e's gathered rows are

@@ -197,6 +197,49 @@ def test_q8a_validation_codes():
     assert rep(offs=A16d + 2) == qg.QG_EALIGN
 
 
+def test_conv_validation_codes():
+    """qg_conv2d / qg_conv_stats check formats, modes, shapes, pointers and alignment on the host."""
+    L = qg.lib()
+
+    def conv(fmt=qg.QG_FMT_Q4, codes=A16, scales=A16b, X=A16c, H=8, W=8, cin=64, k=3, stride=1, n_out=32,
+             norm=0, groups=0, stats=None, gb=None, silu=0, Y=A16d, mode=qg.QG_EXACT):
+        return L.qg_conv2d(fmt, codes, scales, X, H, W, cin, k, stride, n_out, norm, groups, stats, gb, silu, Y,
+                           mode, None)
+
+    assert conv(fmt=qg.QG_FMT_Q4A) == qg.QG_EUNSUPPORTED      # no affine convolution
+    assert conv(fmt=qg.QG_FMT_Q8A) == qg.QG_EUNSUPPORTED
+    assert conv(fmt=9) == qg.QG_EINVAL
+    assert conv(mode=qg.QG_FAST) == qg.QG_EUNSUPPORTED
+    assert conv(cin=48) == qg.QG_ESHAPE
+    assert conv(cin=0) == qg.QG_ESHAPE
+    assert conv(k=0) == qg.QG_ESHAPE
+    assert conv(stride=0) == qg.QG_ESHAPE
+    assert conv(n_out=0) == qg.QG_ESHAPE
+    assert conv(H=0) == qg.QG_ESHAPE
+    assert conv(norm=1, groups=3, stats=A16, gb=A16) == qg.QG_ESHAPE   # groups must divide cin
+    assert conv(norm=1, groups=0, stats=A16, gb=A16) == qg.QG_ESHAPE
+    assert conv(norm=3) == qg.QG_EINVAL
+    assert conv(silu=1) == qg.QG_EINVAL                        # SiLU only with a normalisation
+    assert conv(norm=2, stats=None, gb=A16) == qg.QG_EINVAL
+    assert conv(norm=2, stats=A16, gb=None) == qg.QG_EINVAL
+    assert conv(codes=None) == qg.QG_EINVAL
+    assert conv(X=A16c + 4) == qg.QG_EALIGN
+    assert conv(codes=A16 + 8) == qg.QG_EALIGN
+    assert conv(norm=2, stats=A16 + 2, gb=A16) == qg.QG_EALIGN
+    assert conv(fmt=qg.QG_FMT_Q8, scales=A16b + 2) == qg.QG_EALIGN
+
+    def stats(X=A16, npix=64, cin=64, groups=8, eps=1e-5, out=A16b):
+        return L.qg_conv_stats(X, npix, cin, groups, eps, out, None)
+
+    assert stats(groups=3) == qg.QG_ESHAPE
+    assert stats(npix=0) == qg.QG_ESHAPE
+    assert stats(groups=-1) == qg.QG_ESHAPE
+    assert stats(eps=-1.0) == qg.QG_EINVAL
+    assert stats(eps=float("nan")) == qg.QG_EINVAL
+    assert stats(X=None) == qg.QG_EINVAL
+    assert stats(out=A16b + 2) == qg.QG_EALIGN
+
+
 def test_device_plan_validation_codes():
     """qg_moe_plan checks its sizes and pointers on the host, before any HIP call."""
     L = qg.lib()
