@@ -266,12 +266,31 @@ def measure_batch(steps: int, warmup: int) -> dict:
             f(i)
     ms_b, _ = _timed(batch, steps, warmup)
     ms_s, _ = _timed(separate, steps, warmup)
+    # the same three matrices with T = 4 rows of X (the K-split GEMV: one launch for the three jobs,
+    # against three)
+    X4 = _dev(synth.normal_as(1001, synth.STREAM_X, 4 * K, 0.0, 1.0, "f32").reshape(4, K))
+    y4 = [[torch.empty((4, N), device="cuda") for N in Ns] for _ in range(copies)]
+    arrs4 = [qg.job_array([(c_, s_, None, y, N) for (c_, s_, _, N), y in zip(js, ys)])
+             for js, ys in zip(dev_sets, y4)]
+    batch4 = _bound("qgemm_batch", qg.QG_FMT_Q8, 64, [C.cast(a, C.c_void_p).value for a in arrs4], 3,
+                    X4.data_ptr(), qg.QG_X_F32, K, 4, qg.QG_EXACT, st)
+    singles4 = [_bound("qgemv_q8", [js[i][0].data_ptr() for js in dev_sets], [js[i][1].data_ptr() for js in dev_sets],
+                       X4.data_ptr(), qg.QG_X_F32, [ys[i].data_ptr() for ys in y4], Ns[i], K, 4, st)
+                for i in range(3)]
+
+    def separate4(i):
+        for f in singles4:
+            f(i)
+    ms_b4, _ = _timed(batch4, steps, warmup)
+    ms_s4, _ = _timed(separate4, steps, warmup)
     nbytes = float(sum(N * (K + K // 32 * 4) + 4 * N for N in Ns) + 4 * K)
     gbs = nbytes / (ms_b * 1e-3) / 1e9
     return {"workload": "q8_batch_qkv_decode", "config": "q8_jobs_N4096_1024_1024_K4096_T1", "mode": "exact",
             "ms_per_step": ms_b, "us_per_step": ms_b * 1e3, "dtype": "f32", "kernel": "gemv1_split_kernel",
             "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
-            "bytes_per_step": nbytes, "us_three_separate_calls": ms_s * 1e3, "keep": (arrs, dev_sets, X)}
+            "bytes_per_step": nbytes, "us_three_separate_calls": ms_s * 1e3,
+            "us_T4_batched": ms_b4 * 1e3, "us_T4_three_separate_calls": ms_s4 * 1e3,
+            "keep": (arrs, dev_sets, X, arrs4, y4, X4)}
 
 
 def measure_gemv_t(T: int, steps: int, warmup: int) -> dict:

@@ -210,7 +210,8 @@ qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const
     if (T == 0) return QG_OK;
     if (T > 8 && mode == QG_FAST && xt == QG_X_F32) return QG_EUNSUPPORTED;
     if (mode == QG_FAST_WEXACT && ((fmt != QG_FMT_Q4 && fmt != QG_FMT_Q8) || xt != QG_X_F16)) return QG_EUNSUPPORTED;
-    if (T == 1) {
+    if (T <= 8) {
+        // T = 1: the streaming GEMV; T = 2..8: the K-split GEMV with one launch column per job
         bool all = true;
         for (int j0 = 0; j0 < J && all; j0 += qg::kMaxBatchJobs) {
             qg::BatchJobs bj{};
@@ -223,10 +224,12 @@ qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const
                 bj.offs[i] = b.offsets;
                 bj.Y[i] = b.Y;
             }
-            GemmParams p = dense_params(nullptr, nullptr, nullptr, group, X, nullptr, bj.start[bj.J], K, 1);
+            GemmParams p = dense_params(nullptr, nullptr, nullptr, group, X, nullptr, bj.start[bj.J], K, T);
             hipError_t err = hipSuccess;
-            if (!qg::launch_gemv1_batch(fmt, xt, p, bj, stream, err)) {
-                all = false;  // K beyond the streaming kernel: nothing was launched for this group
+            const bool ok = T == 1 ? qg::launch_gemv1_batch(fmt, xt, p, bj, stream, err)
+                                   : qg::launch_gemv_batch(fmt, xt, p, bj, stream, err);
+            if (!ok) {
+                all = false;  // K beyond the batched kernel: nothing was launched for this group
                 for (int j = j0; j < J; j++) {
                     const qg_job& b = jobs[j];
                     const qg_status st = run_dense(fmt, b.codes, b.scales, b.offsets, group, X, xt, b.Y, b.N, K, T,

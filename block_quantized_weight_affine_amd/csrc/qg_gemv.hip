@@ -728,6 +728,27 @@ __global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_kernel(GemmP
     ksplit_pass<FMT, XT, NT>(p, p.codes, p.scales, p.offs, xrow, 0, (int)blockIdx.x, (int)gridDim.x, part, par);
 }
 
+// Several matrices sharing the NT X rows (qgemm_batch, T = 2..8): blockIdx.y is the job, whose rows
+// the workgroups of that column take in batches with stride gridDim.x, as the dense launch does.
+template <int FMT, int XT, int NT>
+__global__ __launch_bounds__(NT <= 4 ? 1024 : 512) void gemv_ksplit_batch_kernel(GemmParams p, BatchJobs bj) {
+    __shared__ __attribute__((aligned(16))) float part[2 * 16 * kSplitRows * NT * 4];
+    const int j = blockIdx.y;
+    if (j >= bj.J) return;  // uniform over the workgroup
+    GemmParams q = p;
+    q.codes = bj.codes[j];
+    q.scales = bj.scales[j];
+    q.offs = bj.offs[j];
+    q.Y = bj.Y[j];
+    q.N = bj.start[j + 1] - bj.start[j];
+    if ((int)blockIdx.x * kSplitRows >= q.N) return;  // uniform over the workgroup
+    int xrow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) xrow[t] = t;
+    int par = 0;
+    ksplit_pass<FMT, XT, NT>(q, q.codes, q.scales, q.offs, xrow, 0, (int)blockIdx.x, (int)gridDim.x, part, par);
+}
+
 // Grouped launches (exact-mode MoE): blockIdx.y is the expert; the workgroup walks the expert's row
 // segment in chunks of at most 4 X rows (gathered through row_src when given; ids outside X read as
 // zero rows), each chunk one pass over its share of the expert's weight-row batches.
@@ -886,6 +907,58 @@ static bool gemv1_batch_xt(int xt, const GemmParams& p, const BatchJobs& bj, hip
     if (xt == XT_F32) return gemv1<FMT, XT_F32>(p, s, &bj);
     if (xt == XT_F16) return gemv1<FMT, XT_F16>(p, s, &bj);
     return gemv1<FMT, XT_BF16>(p, s, &bj);
+}
+
+// T = 2..8 X rows, every job of bj in one launch: the K-split kernel with blockIdx.y the job and the
+// column count sized like the dense launch's resident round, shared out in proportion to the largest
+// job's rows (smaller jobs' extra workgroups exit at once).  False when K is past the kernel's limit.
+template <int FMT, int XT, int NT>
+static bool gemv_ksplit_batch(const GemmParams& p, const BatchJobs& bj, hipStream_t s) {
+    if (p.K > (NT <= 4 ? kStreamKMax : kStreamKMax / 2)) return false;
+    const int W = (p.K / 16 + 63) / 64;
+    int nb_max = 1;
+    long nb_tot = 0;
+    for (int j = 0; j < bj.J; j++) {
+        const int nb = (bj.start[j + 1] - bj.start[j] + kSplitRows - 1) / kSplitRows;
+        nb_max = std::max(nb_max, nb);
+        nb_tot += nb;
+    }
+    const int per_cu = std::max(1, (NT >= 4 ? 8 : 16) / W);
+    const long round = (long)device_cus() * per_cu;
+    const int gx = (int)std::max(1L, std::min((long)nb_max, (round * nb_max + nb_tot - 1) / std::max(1L, nb_tot)));
+    hipLaunchKernelGGL((gemv_ksplit_batch_kernel<FMT, XT, NT>), dim3(gx, bj.J), dim3(64 * W), 0, s, p, bj);
+    return true;
+}
+
+template <int FMT, int XT>
+static bool gemv_batch_t(const GemmParams& p, const BatchJobs& bj, hipStream_t s) {
+    switch (p.R) {
+        case 2: return gemv_ksplit_batch<FMT, XT, 2>(p, bj, s);
+        case 3: return gemv_ksplit_batch<FMT, XT, 3>(p, bj, s);
+        case 4: return gemv_ksplit_batch<FMT, XT, 4>(p, bj, s);
+        case 5: return gemv_ksplit_batch<FMT, XT, 5>(p, bj, s);
+        case 6: return gemv_ksplit_batch<FMT, XT, 6>(p, bj, s);
+        case 7: return gemv_ksplit_batch<FMT, XT, 7>(p, bj, s);
+        case 8: return gemv_ksplit_batch<FMT, XT, 8>(p, bj, s);
+        default: return false;
+    }
+}
+
+template <int FMT>
+static bool gemv_batch_xt(int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s) {
+    if (xt == XT_F32) return gemv_batch_t<FMT, XT_F32>(p, bj, s);
+    if (xt == XT_F16) return gemv_batch_t<FMT, XT_F16>(p, bj, s);
+    return gemv_batch_t<FMT, XT_BF16>(p, bj, s);
+}
+
+bool launch_gemv_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err) {
+    bool ok;
+    if (fmt == FMT_Q4) ok = gemv_batch_xt<FMT_Q4>(xt, p, bj, s);
+    else if (fmt == FMT_Q4A) ok = gemv_batch_xt<FMT_Q4A>(xt, p, bj, s);
+    else if (fmt == FMT_Q8A) ok = gemv_batch_xt<FMT_Q8A>(xt, p, bj, s);
+    else ok = gemv_batch_xt<FMT_Q8>(xt, p, bj, s);
+    err = ok ? hipGetLastError() : hipSuccess;
+    return ok;
 }
 
 bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err) {

@@ -71,6 +71,9 @@ hipError_t launch_gemm_fast_wexact(int fmt, const GemmParams& p, hipStream_t s);
 hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipStream_t s);
 // T = 1, K <= 16384: every job of bj in one launch (p.N = bj.start[bj.J]); false if not applicable.
 bool launch_gemv1_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err);
+// T = p.R = 2..8, K within the K-split kernel's limit: every job of bj in one launch; false if not
+// applicable.
+bool launch_gemv_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj, hipStream_t s, hipError_t& err);
 // Grouped matmul with short segments streamed per expert row (epi 0: Y = X W^T; epi 1: gate|up
 // matrices of N = 2I rows, Y[r][j] = SiLU(g) * u with pitch I).  fast: f16 X through v_dot2, or f32
 // X scaled to f16 per row in the kernel; otherwise f32 arithmetic.  grouped_rows_fits tells whether

@@ -179,7 +179,9 @@ typedef struct {
  * the single-matrix entry points (format fmt and group for all jobs, X [T][K] of type xt, mode).
  * jobs is a HOST array (read during the call, not kept); its pointers are device memory.  T = 1
  * with K <= 16384 runs every 8 jobs in one launch of the streaming GEMV (the jobs' rows walked as one
- * matrix), which saves a launch per job in decode; other shapes run one call per job.  Every job is
+ * matrix); T = 2..8 with K <= 16384 (8192 for T > 4) every 8 jobs in one launch of the K-split GEMV
+ * (one column of workgroups per job), which saves a launch per job in decode; other shapes (T > 8,
+ * where each job's tile launch fills the chip on its own, or longer K) run one call per job.  Every job is
  * validated before anything is launched (the first failing job's status is returned, with the
  * codes of qgemm_q4 / qgemm_q8); 1 <= J <= 64 else QG_ESHAPE; jobs NULL gives QG_EINVAL. */
 qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const void* X, qg_xtype xt,

@@ -1,7 +1,7 @@
 """Several weight matrices sharing one X (qgemm_batch) on the GPU: every job's Y against the oracle,
-for T = 1 (the jobs' rows walked by one streaming GEMV launch per 8 jobs), T = 3 (the GEMV per job)
-and T = 40 (the tile kernels per job); the batched T = 1 rows also equal single-matrix calls bit for
-bit (the same per-row arithmetic)."""
+for T = 1 (the jobs' rows walked by one streaming GEMV launch per 8 jobs), T = 2..8 (one K-split GEMV
+launch per 8 jobs, a column of workgroups per job) and T = 40 (the tile kernels per job); the batched
+rows at T <= 8 also equal single-matrix calls bit for bit (the same per-row arithmetic)."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +21,7 @@ def _jobs(fmt, Ns, K, seed):
 
 @pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
 @pytest.mark.parametrize("case", [(1, [96, 160, 32, 48]), (1, [64] * 7 + [32, 96, 16]), (3, [96, 160, 32]),
+                                  (2, [4096, 1024, 1024]), (5, [64] * 9 + [34]), (8, [200, 40]),
                                   (40, [128, 64])], ids=lambda c: f"T{c[0]}-J{len(c[1])}")
 def test_batch_matches_oracle(orc, fmt, case):
     T, Ns = case
@@ -34,25 +35,27 @@ def test_batch_matches_oracle(orc, fmt, case):
     for i, (w, y, N) in enumerate(zip(ws, Ys, Ns)):
         Yr, S, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), 64, N, K, X, "f32", T)
         check_tol(y.cpu().numpy(), Yr, S, TAU["exact"], f"job {i} (N {N})")
-    if T == 1:
+    if T <= 8:
         for (c, s, o), y, N in zip(dw, Ys, Ns):
-            y1 = torch.full((1, N), float("nan"), device="cuda")
+            y1 = torch.full((T, N), float("nan"), device="cuda")
             if fmt == "q4":
-                qg.qgemm_q4(c, s, dev(X), y1, N, K, 1, "exact")
+                qg.qgemm_q4(c, s, dev(X), y1, N, K, T, "exact")
             elif fmt == "q4a":
-                qg.qgemm_q4a(c, s, o, 64, dev(X), y1, N, K, 1, "exact")
+                qg.qgemm_q4a(c, s, o, 64, dev(X), y1, N, K, T, "exact")
             else:
-                qg.qgemm_q8(c, s, dev(X), y1, N, K, 1, "exact")
+                qg.qgemm_q8(c, s, dev(X), y1, N, K, T, "exact")
             torch.cuda.synchronize()
             assert np.array_equal(y1.cpu().numpy().view(np.uint32), y.cpu().numpy().view(np.uint32))
 
 
 @pytest.mark.parametrize("case", [("q4", 1, 576, "f16", "exact"), ("q8", 1, 576, "bf16", "exact"),
-                                  ("q4a", 40, 576, "bf16", "fast"), ("q8", 1, 16416, "f32", "exact")],
+                                  ("q4a", 40, 576, "bf16", "fast"), ("q8", 1, 16416, "f32", "exact"),
+                                  ("q4", 4, 576, "f16", "exact"), ("q8a", 6, 1024, "bf16", "exact"),
+                                  ("q8", 5, 8224, "f32", "exact")],
                          ids=lambda c: f"{c[0]}-T{c[1]}-K{c[2]}-{c[3]}-{c[4]}")
 def test_batch_other_paths(orc, case):
-    """16-bit X in the batched T = 1 kernel, fast mode through the per-job tile kernels, and K past
-    the streaming kernel's LDS copy (every job then runs the chunked GEMV)."""
+    """16-bit X in the batched T = 1 and T = 2..8 kernels, Q8A jobs, fast mode through the per-job
+    tile kernels, and K past the batched kernels' limits (every job then runs the chunked GEMV)."""
     fmt, T, K, xt, mode = case
     Ns = [64, 96, 32]
     ws, dw = _jobs(fmt, Ns, K, 5100)
