@@ -243,8 +243,12 @@ namespace qg {
 //  3. one wavefront per expert walks the slots in token order, 64 at a time: the ballot of slots
 //     that picked it and their popcount ranks give each slot its gathered row, in ascending token
 //     order; row_src[row] = token, slot_row[slot] = row.
+// The kernel is instantiated for NPL = 1, 2, 4, 8, 16 logits per lane (E <= 64 NPL): each top-k
+// round scans only the lane's NPL candidates (the rounds run on one CU's VALUs, so a fixed 16 cost
+// E = 128 most of its time).  In step 3 a wavefront skips experts without slots and stops an
+// expert's walk once its count is reached.
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanNpl = 16;         // logits per lane: E <= 1024
+constexpr int kPlanNplMax = 16;      // logits per lane: E <= 1024
 constexpr int kPlanSlots = 16384;    // T * k: the picks live in LDS (32 KiB)
 
 // Order-preserving 32-bit image of a logit (larger value, larger key; -0 taken as +0 so that equal
@@ -278,11 +282,12 @@ __device__ __forceinline__ uint32_t wave_umin32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+template <int NPL>
 __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* logits, int T, int E, int k,
                                                                 int32_t* seg_off, int32_t* row_src, int32_t* slot_row,
                                                                 float* slot_w, int32_t* slot_expert, int32_t* status,
                                                                 int32_t err_code) {
-    __shared__ int cnt[kPlanNpl * 64 + 1];
+    __shared__ int cnt[NPL * 64 + 1];
     __shared__ uint16_t pick[kPlanSlots];
     __shared__ int bad;
     constexpr int W = kPlanThreads / 64;
@@ -294,11 +299,11 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
 
     for (int t = wave; t < T; t += W) {
         const float* row = logits + (size_t)t * E;
-        float v[kPlanNpl];
+        float v[NPL];
         uint32_t taken = 0;  // bit i: candidate lane + 64 i is gone (picked, or past E)
         bool nan_seen = false;
 #pragma unroll
-        for (int i = 0; i < kPlanNpl; i++) {
+        for (int i = 0; i < NPL; i++) {
             const int e = lane + 64 * i;
             v[i] = -INFINITY;
             if (e < E) {
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
             uint32_t bk = 0;
             int bi = 0x7fffffff;
 #pragma unroll
-            for (int i = 0; i < kPlanNpl; i++) {
+            for (int i = 0; i < NPL; i++) {
                 const uint32_t key = ((taken >> i) & 1u) ? 0u : plan_key(v[i]);
                 if (key > bk) {
                     bk = key;
@@ -371,7 +376,8 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
 
     for (int e = wave; e < E; e += W) {
         int base = cnt[e];
-        for (int c = 0; c < tk; c += 64) {
+        const int end = cnt[e + 1];
+        for (int c = 0; c < tk && base < end; c += 64) {
             const int i = c + lane;
             const bool match = i < tk && pick[i] == e;
             const uint64_t mask = __ballot(match);
@@ -388,8 +394,15 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const float* log
 hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                            int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, int err_code,
                            hipStream_t s) {
-    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, logits, T, E, k, seg_off, row_src,
-                       slot_row, slot_w, slot_expert, status, err_code);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(1), dim3(kPlanThreads), 0, s, logits, T, E, k, seg_off, row_src, slot_row,
+                           slot_w, slot_expert, status, err_code);
+    };
+    if (E <= 64) go(moe_plan_kernel<1>);
+    else if (E <= 128) go(moe_plan_kernel<2>);
+    else if (E <= 256) go(moe_plan_kernel<4>);
+    else if (E <= 512) go(moe_plan_kernel<8>);
+    else go(moe_plan_kernel<kPlanNplMax>);
     return hipGetLastError();
 }
 
