@@ -967,6 +967,270 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
 }
 
 // ================================================================================================
+// Fast GEMM with K split over the wavefronts (Q4 / Q4A): a workgroup owns a 64-token x 128-row output
+// tile; each of its 4 wavefronts computes the whole tile over its own quarter of the 64-k stages, from
+// a ring in LDS that only it writes and reads -- X (64 rows x 64 k of the stage, XOR-swizzled as in
+// the ring kernel) and the raw code chunks of the 128 weight rows (32 bytes a row and stage), copied
+// by buffer_load ... lds -- so the main loop has no barrier.  Per stage a wavefront reads 8 KiB of X
+// fragments and 4 KiB of raw codes for 32 MFMAs (the 64 x 128 ring kernel: 9 KiB for 8), decodes
+// each B fragment once (frag16_words), and the four 64 x 128 f32 partials are added through LDS at
+// the end in wavefront order.
+// Tile 32 MT tokens x 32 MN weight rows; per wavefront and stage BT x 128 bytes of X and BN x 32 bytes
+// of codes.
+template <int SLOT, int I>
+__device__ __forceinline__ uint8_t* kz_slot() {
+    __shared__ __attribute__((aligned(16))) uint8_t b[4 * SLOT];
+    return b;
+}
+
+template <int FMT, int ST, int MT, int MN, int D>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fast_kz_kernel(GemmParams p) {
+    static_assert(FMT == FMT_Q4 || FMT == FMT_Q4A, "Q4 / Q4A codes");
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    constexpr int BT = 32 * MT, BN = 32 * MN;
+    constexpr int XB = BT * 128, WB = BN * 32, SLOT = XB + WB;  // per wavefront and stage
+    static_assert(D * 4 * SLOT <= 160 * 1024, "LDS");
+    constexpr int XCH = BT / 8;     // X copies (8 rows each) per stage
+    constexpr int WCH = BN / 32;    // raw-code copies (64 lanes x 16 bytes) per stage
+    constexpr int LC = XCH + WCH;   // copies to LDS per stage
+    static_assert((D - 1) * LC <= 63, "vmcnt range");
+    const int r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
+    const int n0 = blockIdx.x * BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, li = lane & 31;
+    const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
+    const int s0 = (wave * nstage) >> 2, s1 = ((wave + 1) * nstage) >> 2;  // this wavefront's stages
+    const int rows = min(BN, p.N - n0);
+
+    uint16_t* const xbase = (uint16_t*)p.X + (size_t)r0 * K;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(xbase, 0, (r1 - r0) * K * 2, 0x00020000);
+    // X copy i: rows 8 i .. 8 i + 7; lane at row 8 i + lane / 8, position lane % 8 holding chunk
+    // (lane % 8) ^ ((row / 2) % 8) = (lane % 8) ^ ((4 i + lane / 16) % 8)
+    int xoff[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; i++) {
+        const int row = 8 * i + (lane >> 3);
+        xoff[i] = row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+    }
+    const int rowb = K >> 1;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.codes + (size_t)n0 * rowb), 0, rows * rowb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.scales + (size_t)n0 * nblk * 2), 0, rows * nblk * 2, 0x00020000);
+    const int ngr = FMT == FMT_Q4A ? K / p.group : 1;
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(FMT == FMT_Q4A ? (const uint8_t*)p.offs + (size_t)n0 * ngr * 2 : (const uint8_t*)p.scales), 0,
+        FMT == FMT_Q4A ? rows * ngr * 2 : 0, 0x00020000);
+    // raw copy i: slots 64 i + lane -> tile row n = slot / 2, chunk position cs = slot % 2, holding
+    // the row's chunk cs ^ ((n / 8) % 2) of the stage
+    int woff[WCH];
+#pragma unroll
+    for (int i = 0; i < WCH; i++) {
+        const int slot = 64 * i + lane;
+        const int n = slot >> 1, cs = slot & 1;
+        woff[i] = n * rowb + 16 * (cs ^ ((n >> 3) & 1));
+    }
+    int soff[MN], ooff[MN];
+#pragma unroll
+    for (int mn = 0; mn < MN; mn++) {
+        soff[mn] = (32 * mn + li) * nblk * 2;
+        ooff[mn] = (32 * mn + li) * ngr * 2;
+    }
+    struct Scales {
+        uint32_t d[MN][2];
+        uint32_t m[MN][2];
+    };
+    auto issue = [&](auto slotc, int st, Scales& sc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slotc)::value;
+        asm volatile("" ::: "memory");
+        uint8_t* const xd = kz_slot<SLOT, sl>() + wave * SLOT;
+        uint8_t* const wd = xd + XB;
+        const int sr = min(st, s1 - 1);  // stages past the wavefront's last repeat it
+        const int koff = sr * 64 < K ? sr * 128 : 0x40000000;
+#pragma unroll
+        for (int i = 0; i < XCH; i++) buffer_copy16_lds(xrs, xd + 1024 * i, xoff[i] + koff);
+#pragma unroll
+        for (int i = 0; i < WCH; i++) buffer_copy16_lds(crs, wd + 1024 * i, woff[i] + 32 * sr);
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++)
+#pragma unroll
+            for (int b = 0; b < 2; b++) {
+                const int blk = 2 * sr + b;
+                sc.d[mn][b] = __builtin_amdgcn_raw_buffer_load_b16(srs, soff[mn], 2 * blk, 0);
+                if constexpr (FMT == FMT_Q4A)
+                    sc.m[mn][b] = __builtin_amdgcn_raw_buffer_load_b16(ors, ooff[mn], 2 * ((32 * blk) / p.group), 0);
+            }
+    };
+
+    f32x16_t acc[MT][MN];
+#pragma unroll
+    for (int a = 0; a < MT; a++)
+#pragma unroll
+        for (int b = 0; b < MN; b++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+
+    auto mfma = [&](const short8_t& a, const short8_t& b, f32x16_t& c) {
+        if constexpr (ST == XT_F16)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    };
+    Scales scr[D];
+
+    // The four MFMA steps of a stage; step j: X columns 16 j .. 16 j + 15, block j / 2 of every row,
+    // low nibbles for even j, high for odd j.
+    auto body = [&](auto uc, auto fastc, int s, const float (&d)[MN][2], const float (&c0)[MN][2],
+                    const float (&mm)[MN][2], const uint32_t (&dh)[MN][2]) __attribute__((always_inline)) {
+        constexpr bool FAST = decltype(fastc)::value;
+        const uint8_t* const xb = kz_slot<SLOT, decltype(uc)::value>() + wave * SLOT;
+        const uint16_t* const xsb = (const uint16_t*)xb;
+        const uint8_t* const wsb = xb + XB;
+        short8_t A[2][MT], B[2][MN];
+        uint2 raw[MN];
+        auto frags_a = [&](int j, short8_t (&Ao)[MT]) __attribute__((always_inline)) {
+            const uint16_t* xa = xsb + li * 64 + 8 * ((2 * j + g) ^ ((li >> 1) & 7));
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) Ao[mt] = *(const short8_t*)(xa + mt * 32 * 64);
+        };
+        auto read_raw = [&](int blk) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mn = 0; mn < MN; mn++) {
+                const int n = 32 * mn + li;
+                raw[mn] = *(const uint2*)(wsb + 16 * (2 * n + (blk ^ ((n >> 3) & 1))) + 8 * g);
+            }
+        };
+        auto decode = [&](int q, short8_t (&Bo)[MN]) __attribute__((always_inline)) {
+            const int b = q >> 1;
+#pragma unroll
+            for (int mn = 0; mn < MN; mn++) {
+                uint32_t c[2];
+                if (q & 1) {
+                    c[0] = keep_u32((raw[mn].x >> 4) & 0x0F0F0F0Fu);
+                    c[1] = keep_u32((raw[mn].y >> 4) & 0x0F0F0F0Fu);
+                } else {
+                    c[0] = keep_u32(raw[mn].x & 0x0F0F0F0Fu);
+                    c[1] = keep_u32(raw[mn].y & 0x0F0F0F0Fu);
+                }
+                if constexpr (FAST) Bo[mn] = frag16_words<FMT, ST>(c, d[mn][b], dh[mn][b], c0[mn][b]);
+                else Bo[mn] = frag16_words_slow<FMT, ST>(c, d[mn][b], mm[mn][b]);
+            }
+        };
+        frags_a(0, A[0]);
+        read_raw(0);
+        decode(0, B[0]);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int cur = q & 1, nx = cur ^ 1;
+            if (q + 1 < 4) {
+                frags_a(q + 1, A[nx]);
+                if (q == 1) read_raw(1);  // the second block's chunks
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int mn = 0; mn < MN; mn++) mfma(A[cur][mt], B[cur][mn], acc[mt][mn]);
+            if (q + 1 < 4) decode(q + 1, B[nx]);
+        }
+    };
+    auto stage = [&](auto uc, int s) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;  // (s - s0) % D
+        issue(std::integral_constant<int, (u + D - 1) % D>{}, s + D - 1, scr[(u + D - 1) % D]);
+        // this stage's copies have landed: D - 1 later stages' copies were issued since (copies to LDS
+        // complete in issue order among themselves; the scale loads into registers are not counted)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * LC>());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        float d[MN][2], c0[MN][2], mm[MN][2];
+        uint32_t dh[MN][2];
+        bool fast = true;
+#pragma unroll
+        for (int mn = 0; mn < MN; mn++)
+#pragma unroll
+            for (int b = 0; b < 2; b++) {
+                const bool valid = 2 * s + b < nblk;  // a K tail block decodes as zeros
+                const uint32_t db = valid ? scr[u].d[mn][b] : 0u;
+                dh[mn][b] = db & 0xFFFFu;
+                d[mn][b] = f16_to_f32((uint16_t)db);
+                mm[mn][b] = FMT == FMT_Q4A ? (valid ? bf16_to_f32((uint16_t)scr[u].m[mn][b]) : 0.f) : 0.f;
+                RawBlock<FMT> rb{};
+                rb.d = d[mn][b];
+                rb.m = mm[mn][b];
+                bool f;
+                c0[mn][b] = block_c0<FMT>(rb, f);
+                if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) fast = fast && (f || !valid);
+            }
+        if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
+            body(uc, std::true_type{}, s, d, c0, mm, dh);
+        } else {
+            if (__all(fast)) body(uc, std::true_type{}, s, d, c0, mm, dh);
+            else body(uc, std::false_type{}, s, d, c0, mm, dh);
+        }
+    };
+    if (s1 > s0) {
+        auto prologue = [&](auto tc) __attribute__((always_inline)) {
+            constexpr int t = decltype(tc)::value;
+            issue(tc, s0 + t, scr[t]);
+        };
+        run_stages_c<0, D - 1>(prologue);
+        int s = s0;
+        for (; s + D <= s1; s += D) run_stages<0, D>(stage, s);
+        // the remaining s1 - s < D stages keep their slot numbering (slot (s - s0) % D)
+        run_tail_stages<0, D + 1>(stage, s, s1);
+    }
+
+    // The four partial tiles added in wavefront order through slot 0, RT accumulator tiles a round:
+    // every wavefront writes its partials of the round's tiles, then wavefront w adds and stores the
+    // round's tiles t with t % 4 == w.
+    __builtin_amdgcn_s_waitcnt(0);  // the ring's last (repeated) copies have landed before slot 0 is reused
+    __syncthreads();
+    constexpr int NT = MT * MN;
+    constexpr int RT = (4 * SLOT) / (4 * 4096) < NT ? (4 * SLOT) / (4 * 4096) : NT;  // 4 KiB per tile and wavefront
+    static_assert(RT >= 1, "reduction round");
+    float* const red = (float*)kz_slot<SLOT, 0>();
+    QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
+#pragma unroll
+    for (int t0 = 0; t0 < NT; t0 += RT) {
+#pragma unroll
+        for (int t = t0; t < t0 + RT && t < NT; t++)
+#pragma unroll
+            for (int i = 0; i < 16; i += 4)
+                *(float4*)(red + (((wave * RT + (t - t0)) * 4 + i / 4) * 64 + lane) * 4) =
+                    make_float4(acc[t / MN][t % MN][i], acc[t / MN][t % MN][i + 1], acc[t / MN][t % MN][i + 2],
+                                acc[t / MN][t % MN][i + 3]);
+        __syncthreads();
+#pragma unroll
+        for (int t = t0; t < t0 + RT && t < NT; t++) {
+            if (t % 4 != wave) continue;
+            const int mt = t / MN, mn = t % MN;
+            const int n = n0 + 32 * mn + li;
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                float4 v = *(const float4*)(red + (((0 * RT + (t - t0)) * 4 + i / 4) * 64 + lane) * 4);
+#pragma unroll
+                for (int w = 1; w < 4; w++) {
+                    const float4 q = *(const float4*)(red + (((w * RT + (t - t0)) * 4 + i / 4) * 64 + lane) * 4);
+                    v.x += q.x;
+                    v.y += q.y;
+                    v.z += q.z;
+                    v.w += q.w;
+                }
+                const float tv[4] = {v.x, v.y, v.z, v.w};
+                if (n < p.N) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int r = r0 + mt * 32 + 8 * ((i + j) >> 2) + 4 * g + ((i + j) & 3);
+                        if (r < r1) Y[(size_t)r * p.N + n] = tv[j];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ================================================================================================
 // Exact mode: f32 MFMA (v_mfma_f32_32x32x2_f32), f32 accumulation; X f32, f16 or bf16 widened.
 // CV: the convolution (page "oxinfer 0.0.5 src/metal.rs", SHADER_SRC conv_body and norm4): the X tile
 // of output pixel r and 8 values of K starting at k is the image's channel slice ci .. ci + 7 of tap
@@ -1251,6 +1515,12 @@ static void fast_ring_launch(const GemmParams& p, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fast_ring_kernel<FMT, ST, WM, MT, MN, D, WX>), grid, dim3(kThreads), 0, s, p);
 }
 
+template <int FMT, int ST, int MT, int MN, int D>
+static void fast_kz_launch(const GemmParams& p, hipStream_t s) {
+    dim3 grid((p.N + 32 * MN - 1) / (32 * MN), (p.R + 32 * MT - 1) / (32 * MT));
+    hipLaunchKernelGGL((gemm_fast_kz_kernel<FMT, ST, MT, MN, D>), grid, dim3(kThreads), 0, s, p);
+}
+
 template <int FMT, int ST>
 static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     // Grouped launches: 32-row tiles (MoE segments are short), 128 weight rows (three workgroups
@@ -1266,10 +1536,13 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (wgs(256, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 4, 4, 1>(p, s);
     if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4, 4>(p, s);
     if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
-    // 64 x 128 tiles: the raw-weight ring, wavefronts 1 x 4, six stages (Q4 prefill N = K = 4096,
-    // T 512: 32.5 us against 40.1 for the decoded-tile kernel with the same tile); Q8A (its per-block
-    // offsets are not in the ring) the 128 x 128 decoded tiles
+    // Smaller shapes: Q4 / Q4A 128 x 64 tiles with K split over the wavefronts (Q4 prefill N = K =
+    // 4096, T 512: 31.8 us against 34.5 for the ring kernel below and 39.1 for the same kernel with
+    // 64 x 128 tiles, whose decode costs twice the VALU work per MFMA); Q8 the raw-weight ring, 64 x 128
+    // tiles, wavefronts 1 x 4, six stages (Q8 codes are twice the bytes: the k-split rings would not
+    // fit); Q8A (its per-block offsets are not in the ring) the 128 x 128 decoded tiles
     if constexpr (FMT == FMT_Q8A) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
+    else if constexpr (FMT == FMT_Q4 || FMT == FMT_Q4A) return fast_kz_launch<FMT, ST, 4, 2, 2>(p, s);
     else return fast_ring_launch<FMT, ST, 1, 2, 1, 6>(p, s);
 }
 
