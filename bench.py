@@ -87,21 +87,6 @@ def _timed(fn, steps: int, warmup: int):
     return s.elapsed_time(e) / steps, wall
 
 
-def _bracketed(fn, n: int, first: int) -> float:
-    """Mean duration (us) of n single launches, each bracketed by its own pair of events on the launch
-    stream (an event between every two launches): the figure to set beside a profiler's per-dispatch
-    durations, which likewise separate the launches."""
-    import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        fn(first + i)
-        b.record()
-    torch.cuda.synchronize()
-    return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / n
-
-
 def _bound(name: str, *args):
     """A step function calling the C entry point `name` with pre-marshalled integer arguments;
     args may hold per-step lists (indexed by the step number modulo their length)."""
@@ -402,14 +387,12 @@ def measure_repack(steps: int, warmup: int) -> dict:
             "bytes_per_step": nbytes}
 
 
-def measure(name: str, steps: int, warmup: int, bracketed: int = 0) -> dict:
+def measure(name: str, steps: int, warmup: int) -> dict:
     step, info = setup(name)
     ms, wall = _timed(step, steps, warmup)
     c = info["cfg"]
     out = {"workload": name, "config": info["name"], "mode": info["mode"], "ms_per_step": ms,
            "us_per_step": ms * 1e3, "dtype": info["dtype"], "kernel": info["kernel"]}
-    if bracketed:
-        out["launch_us_bracketed"] = _bracketed(step, bracketed, warmup + steps)
     if c.index in (1, 4):
         gbs = info["bytes"] / (ms * 1e-3) / 1e9
         out.update({"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
@@ -541,15 +524,14 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "copies": args.steps}))
         return
 
-    head = measure(args.workload, args.steps, args.warmup, bracketed=200)
+    head = measure(args.workload, args.steps, args.warmup)
     info = head.pop("_info")
     roofline = {"bound": head["bound"], "achieved": head["value"], "peak": head["peak"],
                 "unit": head["unit"], "frac": head["frac"], "traffic": traffic_for(args.workload, info,
                                                                                  head["ms_per_step"]),
                 "kernel": head["kernel"], "per_launch": (info["bytes"] if head["unit"] == "GB/s" else info["flops"]),
-                # one launch per step: the timed region's mean step is the mean launch duration; the
-                # bracketed figure separates every launch by events, as a profiler's trace does
-                "launch_us_timed": head["ms_per_step"] * 1e3, "launch_us_bracketed": head["launch_us_bracketed"]}
+                # one launch per step: the timed region's mean step is the mean launch duration
+                "launch_us_timed": head["ms_per_step"] * 1e3}
     cpu = None
     if not args.no_cpu and info["cfg"].index != 4:
         cpu = cpu_baseline(info)
