@@ -276,9 +276,9 @@ def moe_ffn(m: dict, plan: dict, fmt: str = "q4", group: int = 64, threads=None)
 
 
 # ---- GGUF blocks with in-block scales (GGML type ids) -------------------------------------------
-GGUF = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12}
-# bytes per 32 elements (Q4_K: 144 per 256)
-GGUF_BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24, "q8_0": 34, "q4_k": 18}
+GGUF = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12, "q5_k": 13}
+# bytes per 32 elements (Q4_K: 144 per 256, Q5_K: 176 per 256)
+GGUF_BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24, "q8_0": 34, "q4_k": 18, "q5_k": 22}
 
 
 def gguf_dequant(gtype, src, N, K) -> np.ndarray:
@@ -305,7 +305,7 @@ def gguf_repack(gtype, src, N, K) -> tuple:
 
 def gguf_repack_q8a(gtype, src, N, K) -> tuple:
     """(codes int8 [N*K], scales f32 [N*K/32], offsets f32 [N*K/32]) of the Q8A layout for the
-    affine types Q4_1, Q5_0, Q5_1 and Q4_K."""
+    affine types Q4_1, Q5_0, Q5_1, Q4_K and Q5_K."""
     b = _c(src, np.uint8)
     codes = np.empty(N * K, np.int8)
     scales = np.empty(N * K // 32, np.float32)

@@ -401,6 +401,10 @@ void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uin
  *         << 4), mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4).  d1 = d * sc, m1 = dmin * mn (f32);
  *         element e of sub-block j is nibble (j % 2 ? high : low) of code byte 32 (j / 2) + e;
  *         value = nibble * d1 - m1.
+ *   Q5_K (type 13, loader Q5_KW): 176 bytes per 256 elements = h d, h dmin, the 12 scale bytes of
+ *         Q4_K, 32 bytes qh, 128 code bytes; sub-block j as Q4_K (code bytes 48 + 32 (j / 2) + e,
+ *         the same scale / min unpacking) with a fifth bit: code = nibble | (bit j of qh[e]) << 4;
+ *         value = code * d1 - m1.
  * Every value is evaluated in f32 in the order written.  A row holds K / 32 blocks (K / 256
  * super-blocks for Q4_K).
  */
@@ -410,6 +414,7 @@ void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uin
 #define ORC_GGUF_Q5_1 7
 #define ORC_GGUF_Q8_0 8
 #define ORC_GGUF_Q4_K 12
+#define ORC_GGUF_Q5_K 13
 
 /* Bytes of one row of K elements. */
 static size_t gguf_row_bytes(int type, int K) {
@@ -419,6 +424,7 @@ static size_t gguf_row_bytes(int type, int K) {
     case ORC_GGUF_Q5_0: return (size_t)(K / 32) * 22;
     case ORC_GGUF_Q5_1: return (size_t)(K / 32) * 24;
     case ORC_GGUF_Q8_0: return (size_t)(K / 32) * 34;
+    case ORC_GGUF_Q5_K: return (size_t)(K / 256) * 176;
     default: return (size_t)(K / 256) * 144;
     }
 }
@@ -441,6 +447,19 @@ static void gguf_k4_scale_min(int j, const uint8_t* s, int* sc, int* mn) {
 static void gguf_element(int type, const uint8_t* src, int K, int n, int k, int* code, float* d, float* m) {
     const uint8_t* row = src + (size_t)n * gguf_row_bytes(type, K);
     int j = k % 32;
+    if (type == ORC_GGUF_Q5_K) {
+        const uint8_t* SB = row + (size_t)(k / 256) * 176;
+        int sub = (k % 256) / 32, sc, mn;
+        gguf_k4_scale_min(sub, SB + 4, &sc, &mn);
+        float d1 = gguf_h(SB) * (float)sc;
+        float m1 = gguf_h(SB + 2) * (float)mn;
+        uint8_t byte = SB[48 + 32 * (sub / 2) + j];
+        int nib = (sub % 2) ? (byte >> 4) : (byte & 15);
+        *code = nib | (((SB[16 + j] >> sub) & 1) << 4);
+        *d = d1;
+        *m = m1;
+        return;
+    }
     if (type == ORC_GGUF_Q4_K) {
         const uint8_t* SB = row + (size_t)(k / 256) * 144;
         int sub = (k % 256) / 32, sc, mn;
@@ -495,7 +514,8 @@ float orc_gguf_weight_f32(int type, const uint8_t* src, int K, int n, int k) {
         float v = p + m;
         return v;
     }
-    case ORC_GGUF_Q4_K: {
+    case ORC_GGUF_Q4_K:
+    case ORC_GGUF_Q5_K: {
         float p = (float)code * d;
         float v = p - m;
         return v;
@@ -532,9 +552,9 @@ void orc_gguf_repack(int type, const uint8_t* src, int N, int K, uint8_t* codes,
         }
 }
 
-/* Q4_1, Q5_0, Q5_1, Q4_K -> the Q8A layout: int8 codes [N][K], f32 scales and f32 offsets
+/* Q4_1, Q5_0, Q5_1, Q4_K, Q5_K -> the Q8A layout: int8 codes [N][K], f32 scales and f32 offsets
  * [N][K/32], with q * scale + offset equal to the type's value: Q4_1 / Q5_1 (code, d, m);
- * Q5_0 (code - 16, d, +0); Q4_K (code, d1, -m1) per 32-element sub-block. */
+ * Q5_0 (code - 16, d, +0); Q4_K / Q5_K (code, d1, -m1) per 32-element sub-block. */
 void orc_gguf_repack_q8a(int type, const uint8_t* src, int N, int K, int8_t* codes, float* scales, float* offs) {
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++) {
@@ -545,7 +565,7 @@ void orc_gguf_repack_q8a(int type, const uint8_t* src, int N, int K, int8_t* cod
             if (type == ORC_GGUF_Q5_0) code -= 16;
             codes[(size_t)n * K + k] = (int8_t)code;
             scales[bi] = d;
-            offs[bi] = type == ORC_GGUF_Q4_K ? -m : m;
+            offs[bi] = (type == ORC_GGUF_Q4_K || type == ORC_GGUF_Q5_K) ? -m : m;
         }
 }
 

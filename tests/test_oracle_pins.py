@@ -598,7 +598,7 @@ def _expected_row(spec, n):
 
 @pytest.mark.parametrize("case", _golden_affine(), ids=lambda c: c["name"])
 def test_gguf_affine_hand_blocks(orc, case):
-    """Q4_1, Q5_0, Q5_1 and Q4_K blocks worked by hand (tests/golden/gguf_affine_blocks.json): every
+    """Q4_1, Q5_0, Q5_1, Q4_K and Q5_K blocks worked by hand (tests/golden/gguf_affine_blocks.json): every
     element's decoded value, and +0 (not -0) where the value is zero."""
     src = np.frombuffer(bytes.fromhex("".join(case["fields_hex"])), np.uint8)
     K = case["K"]
@@ -611,7 +611,7 @@ def test_gguf_affine_hand_blocks(orc, case):
     assert not np.any(np.signbit(w) & (w == 0)), "a zero value came out as -0"
 
 
-@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k"])
+@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k", "q5_k"])
 def test_gguf_affine_repack_matches_direct_decode(orc, gtype):
     """The Q8A repack (int8 code, f32 scale, f32 offset per 32 elements), decoded by the Q8A decoder
     (code * scale, then + offset), gives every element's GGUF value bit for bit -- random blocks with
@@ -619,9 +619,10 @@ def test_gguf_affine_repack_matches_direct_decode(orc, gtype):
     rng = np.random.default_rng(17)
     N, K = 3, 512
     import synth
-    if gtype == "q4_k":
+    if gtype in ("q4_k", "q5_k"):
         nsb = N * K // 256
-        src = rng.integers(0, 256, nsb * 144).astype(np.uint8).reshape(nsb, 144)
+        sbb = 144 if gtype == "q4_k" else 176
+        src = rng.integers(0, 256, nsb * sbb).astype(np.uint8).reshape(nsb, sbb)
         d = synth.f16_uniform(11, 1, nsb, -0.05, 0.05)
         dm = synth.f16_uniform(12, 1, nsb, -0.05, 0.05)
         src[:, 0], src[:, 1], src[:, 2], src[:, 3] = d & 0xFF, d >> 8, dm & 0xFF, dm >> 8
@@ -639,7 +640,7 @@ def test_gguf_affine_repack_matches_direct_decode(orc, gtype):
     codes, scales, offs = orc.gguf_repack_q8a(gtype, src, N, K)
     split = orc.dequant_tile("q8a", codes, scales, offs, 32, N, K, 0, 0, N, K, "f32")
     assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
-    lo, hi = {"q4_1": (0, 15), "q5_0": (-16, 15), "q5_1": (0, 31), "q4_k": (0, 15)}[gtype]
+    lo, hi = {"q4_1": (0, 15), "q5_0": (-16, 15), "q5_1": (0, 31), "q4_k": (0, 15), "q5_k": (0, 31)}[gtype]
     assert codes.min() >= lo and codes.max() <= hi
 
 
