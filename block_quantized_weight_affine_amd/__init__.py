@@ -226,9 +226,9 @@ def qgemm_batch(fmt, group, jobs, X, K, T, mode="exact", xt=None, stream=None):
                              _ptr(X), _xt(X) if xt is None else xt, K, T, _mode(mode), _stream(stream)), "qgemm_batch")
 
 
-QG_GGUF_Q4_0, QG_GGUF_Q4_1, QG_GGUF_Q5_0, QG_GGUF_Q5_1, QG_GGUF_Q8_0, QG_GGUF_Q4_K = 2, 3, 6, 7, 8, 12
+QG_GGUF_Q4_0, QG_GGUF_Q4_1, QG_GGUF_Q5_0, QG_GGUF_Q5_1, QG_GGUF_Q8_0, QG_GGUF_Q4_K, QG_GGUF_Q5_K = 2, 3, 6, 7, 8, 12, 13
 GGUF = {"q4_0": QG_GGUF_Q4_0, "q4_1": QG_GGUF_Q4_1, "q5_0": QG_GGUF_Q5_0, "q5_1": QG_GGUF_Q5_1,
-        "q8_0": QG_GGUF_Q8_0, "q4_k": QG_GGUF_Q4_K}
+        "q8_0": QG_GGUF_Q8_0, "q4_k": QG_GGUF_Q4_K, "q5_k": QG_GGUF_Q5_K}
 
 
 def qg_repack_gguf(gtype, src, N, K, codes, scales, stream=None):
@@ -238,7 +238,7 @@ def qg_repack_gguf(gtype, src, N, K, codes, scales, stream=None):
 
 
 def qg_repack_gguf_q8a(gtype, src, N, K, codes, scales, offsets, stream=None):
-    """GGUF Q4_1 / Q5_0 / Q5_1 / Q4_K blocks (device uint8 tensor) -> Q8A codes (int8 [N*K]), f32
+    """GGUF Q4_1 / Q5_0 / Q5_1 / Q4_K / Q5_K blocks (device uint8 tensor) -> Q8A codes (int8 [N*K]), f32
     scales and f32 offsets ([N*K/32]), all device tensors."""
     _check(lib().qg_repack_gguf_q8a(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K,
                                     _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)),

@@ -264,10 +264,11 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
 
 qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes, float* scales_f32,
                              float* offsets_f32, hipStream_t stream) {
-    if (type != QG_GGUF_Q4_1 && type != QG_GGUF_Q5_0 && type != QG_GGUF_Q5_1 && type != QG_GGUF_Q4_K)
+    if (type != QG_GGUF_Q4_1 && type != QG_GGUF_Q5_0 && type != QG_GGUF_Q5_1 && type != QG_GGUF_Q4_K &&
+        type != QG_GGUF_Q5_K)
         return QG_EINVAL;
-    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || (type == QG_GGUF_Q4_K && (K % 256) != 0))
-        return QG_ESHAPE;
+    const bool kq = type == QG_GGUF_Q4_K || type == QG_GGUF_Q5_K;  // 256-element super-blocks
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || (kq && (K % 256) != 0)) return QG_ESHAPE;
     if (!src || !codes || !scales_f32 || !offsets_f32) return QG_EINVAL;
     if (!aligned(src, 2) || !aligned(codes, 16) || !aligned(scales_f32, 4) || !aligned(offsets_f32, 4))
         return QG_EALIGN;

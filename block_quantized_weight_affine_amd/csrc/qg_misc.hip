@@ -536,6 +536,8 @@ hipError_t launch_conv_stats(const float* X, int npix, int cin, int groups, floa
 //   Q5_1 24 B: h d, h m, qh, 16 nibble bytes
 //   Q4_K 144 B per 256 elements: h d, h dmin, 12 scale bytes, 128 code bytes; sub-block j's
 //        elements are the low (j even) or high (j odd) nibbles of code bytes 32 (j / 2) .. + 31.
+//   Q5_K 176 B per 256 elements (loader Q5_KW): h d, h dmin, the 12 scale bytes, 32 bytes qh, 128 code
+//        bytes; as Q4_K with a fifth code bit, bit j of qh[e] for element e of sub-block j.
 // One thread per output block, consecutive threads on consecutive blocks of a row-major [N][K/32]
 // block grid (blocks are 2-byte aligned: read as 16-bit words).
 template <int GT>
@@ -544,8 +546,9 @@ __global__ void repack_gguf_q8a_kernel(const uint16_t* src, size_t nblocks, uint
     for (size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * blockDim.x) {
         uint8_t nib[32];  // element e's code before any shift
         float d, m;
-        if constexpr (GT == QG_GGUF_Q4_K) {
-            const uint16_t* SB = src + (b >> 3) * 72;  // 144-byte super-block
+        if constexpr (GT == QG_GGUF_Q4_K || GT == QG_GGUF_Q5_K) {
+            constexpr bool q5 = GT == QG_GGUF_Q5_K;
+            const uint16_t* SB = src + (b >> 3) * (q5 ? 88 : 72);  // 176- / 144-byte super-block
             const int j = (int)(b & 7);
             uint8_t sb[12];
 #pragma unroll
@@ -563,12 +566,20 @@ __global__ void repack_gguf_q8a_kernel(const uint16_t* src, size_t nblocks, uint
             }
             d = f16_to_f32(SB[0]) * (float)sc;
             m = -(f16_to_f32(SB[1]) * (float)mn);
-            const uint16_t* q = SB + 8 + 16 * (j >> 1);
+            const uint16_t* q = SB + (q5 ? 24 : 8) + 16 * (j >> 1);
             const int sh = 4 * (j & 1);
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 nib[2 * i] = (uint8_t)((q[i] >> sh) & 15);
                 nib[2 * i + 1] = (uint8_t)((q[i] >> (8 + sh)) & 15);
+            }
+            if constexpr (q5) {
+                const uint16_t* qh = SB + 8;  // bytes 16 .. 47
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    nib[2 * i] = (uint8_t)(nib[2 * i] | (((qh[i] >> j) & 1) << 4));
+                    nib[2 * i + 1] = (uint8_t)(nib[2 * i + 1] | (((qh[i] >> (8 + j)) & 1) << 4));
+                }
             }
         } else {
             constexpr bool has_m = GT == QG_GGUF_Q4_1 || GT == QG_GGUF_Q5_1;
@@ -630,6 +641,10 @@ hipError_t launch_repack_gguf_q8a(int type, const void* src, size_t nblocks, voi
             break;
         case QG_GGUF_Q4_K:
             hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q4_K>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
+                               scales, offs);
+            break;
+        case QG_GGUF_Q5_K:
+            hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q5_K>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
                                scales, offs);
             break;
         default: return hipErrorInvalidValue;

@@ -78,7 +78,8 @@ typedef enum {
     QG_GGUF_Q5_0 = 6,
     QG_GGUF_Q5_1 = 7,
     QG_GGUF_Q8_0 = 8,
-    QG_GGUF_Q4_K = 12
+    QG_GGUF_Q4_K = 12,
+    QG_GGUF_Q5_K = 13
 } qg_gguf_type;
 
 /* Text for a status code (static storage; never NULL). */
@@ -202,8 +203,8 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
                          hipStream_t stream);
 
 /* Affine GGUF blocks to the Q8A layout, on the device (page "oxinfer 0.0.5 src/metal.rs",
- * GGUF_SHADER_SRC, the loaders load_q45 for Q4_1 / Q5_0 / Q5_1 and Q4_KW with its 6-bit scale and
- * min unpacking).  src: N rows of K/32 blocks (K/256 super-blocks for QG_GGUF_Q4_K), row after row,
+ * GGUF_SHADER_SRC, the loaders load_q45 for Q4_1 / Q5_0 / Q5_1, and Q4_KW / Q5_KW with their 6-bit
+ * scale and min unpacking).  src: N rows of K/32 blocks (K/256 super-blocks for QG_GGUF_Q4_K), row after row,
  * little-endian, f16 fields as h:
  *   QG_GGUF_Q4_1 (20 bytes): h d, h m, 16 nibble bytes (byte j: element j in its low nibble,
  *                element j + 16 in its high nibble); value nibble * d + m.
@@ -213,12 +214,15 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
  *   QG_GGUF_Q4_K (144 bytes per 256 elements): h d, h dmin, 12 bytes of 6-bit scales sc and mins
  *                mn of the eight 32-element sub-blocks, 128 code bytes; value nibble * (d sc) -
  *                dmin mn.
+ *   QG_GGUF_Q5_K (176 bytes per 256 elements, loader Q5_KW): h d, h dmin, the 12 scale bytes, 32
+ *                bytes qh, 128 code bytes; code = nibble | (bit j of qh[e]) << 4 for element e of
+ *                sub-block j; value code * (d sc) - dmin mn.
  * Each value is a product rounded to f32 and then an add, so the Q8A layout holds it exactly: codes
  * int8 [N][K] (the code; Q5_0 code - 16), scales f32 [N][K/32] (d; Q4_K d sc rounded once) and
- * offsets f32 [N][K/32] (m; Q5_0 +0; Q4_K -(dmin mn) rounded once), and qgemm_q8a / qgemv_q8a then
+ * offsets f32 [N][K/32] (m; Q5_0 +0; Q4_K / Q5_K -(dmin mn) rounded once), and qgemm_q8a / qgemv_q8a then
  * compute with the GGUF values.  Device pointers owned by the caller; src 2-byte aligned, codes
  * 16-byte aligned, scales and offsets 4-byte aligned, else QG_EALIGN; N >= 1, K >= 32, K % 32 == 0
- * (K % 256 == 0 for Q4_K), else QG_ESHAPE; a type not listed here or a null pointer gives
+ * (K % 256 == 0 for Q4_K and Q5_K), else QG_ESHAPE; a type not listed here or a null pointer gives
  * QG_EINVAL.  Asynchronous on `stream`; nothing is allocated. */
 qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
                              float* scales_f32, float* offsets_f32, hipStream_t stream);

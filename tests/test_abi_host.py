@@ -187,6 +187,7 @@ def test_q8a_validation_codes():
     assert rep(t=qg.QG_GGUF_Q8_0) == qg.QG_EINVAL
     assert rep(t=5) == qg.QG_EINVAL
     assert rep(K=288) == qg.QG_ESHAPE                 # Q4_K needs K % 256 == 0
+    assert rep(t=qg.QG_GGUF_Q5_K, K=288) == qg.QG_ESHAPE
     assert rep(N=0) == qg.QG_ESHAPE
     assert rep(t=qg.QG_GGUF_Q4_1, K=48) == qg.QG_ESHAPE
     assert rep(offs=None) == qg.QG_EINVAL

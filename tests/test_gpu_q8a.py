@@ -1,5 +1,5 @@
 """Q8A (int8 codes, f32 scale and f32 offset per 32-k block; w = fl(fl(q d) + m)) on the GPU, and the
-affine GGUF types that map onto it (Q4_1, Q5_0, Q5_1, Q4_K):
+affine GGUF types that map onto it (Q4_1, Q5_0, Q5_1, Q4_K, Q5_K):
 
   * the device repack GGUF -> Q8A against the oracle's repack, bit for bit (the oracle's repack is
     pinned on the CPU to decode every element as the oracle's direct GGUF decoder does);
@@ -18,20 +18,20 @@ from helpers import TAU, check_tol, dev, sample_idx
 
 pytestmark = pytest.mark.gpu
 
-BB = {"q4_1": 20, "q5_0": 22, "q5_1": 24, "q4_k": 144}
+BB = {"q4_1": 20, "q5_0": 22, "q5_1": 24, "q4_k": 144, "q5_k": 176}
 STAGED = {"f32": qg.QG_X_F32, "f16": qg.QG_X_F16, "bf16": qg.QG_X_BF16}
 
 
 def _gguf_bytes(gtype, N, K, seed):
     """Random field bytes; the f16 fields drawn from seeded uniforms (both signs, a few subnormal)."""
-    per = 256 if gtype == "q4_k" else 32
+    per = 256 if gtype in ("q4_k", "q5_k") else 32
     nb = N * K // per
     rng = np.random.default_rng(seed)
     src = rng.integers(0, 256, nb * BB[gtype]).astype(np.uint8).reshape(nb, BB[gtype])
     d = synth.f16_uniform(seed, 1, nb, -0.05, 0.05)
     d[::97] = 0x0003
     src[:, 0], src[:, 1] = d & 0xFF, d >> 8
-    if gtype in ("q4_1", "q5_1", "q4_k"):
+    if gtype in ("q4_1", "q5_1", "q4_k", "q5_k"):
         m = synth.f16_uniform(seed, 2, nb, -0.5, 0.5)
         src[:, 2], src[:, 3] = m & 0xFF, m >> 8
     return src.reshape(-1)
@@ -47,7 +47,7 @@ def _repack_dev(gtype, src, N, K):
     return codes, scales, offs
 
 
-@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k"])
+@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k", "q5_k"])
 @pytest.mark.parametrize("NK", [(64, 512), (3, 256), (517, 1024)])
 def test_repack_q8a_bit_exact(orc, gtype, NK):
     N, K = NK
@@ -142,7 +142,7 @@ def test_q8a_dump_extreme_fields(orc):
             assert np.array_equal(got.view(np.uint16), ref), staged
 
 
-@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k"])
+@pytest.mark.parametrize("gtype", ["q4_1", "q5_0", "q5_1", "q4_k", "q5_k"])
 @pytest.mark.parametrize("case", [("exact", 1, "f32"), ("exact", 40, "f32"), ("fast", 96, "f16")],
                          ids=lambda c: f"{c[0]}-T{c[1]}-{c[2]}")
 def test_matmul_through_repacked_gguf(orc, gtype, case):
