@@ -119,13 +119,13 @@ def _bound(name: str, *args):
 # ---------------------------------------------------------------------------------------------------
 def _fast_kernel(fmt: str, N: int, T: int) -> str:
     """The kernel the fast-mode dispatcher picks for a dense call: decoded tiles (256 x 256, 128 x 256
-    or 128 x 128 rows x tokens) while they still give about 200 workgroups, else the raw-weight ring
-    with 64 x 128 tiles (Q8A: 128 x 128 decoded tiles)."""
+    or 128 x 128 rows x tokens) while they still give about 200 workgroups, else 128 x 64 tiles with K
+    split over the wavefronts (Q8A: 128 x 128 decoded tiles)."""
     def wgs(bt, bn):
         return ((N + bn - 1) // bn) * ((T + bt - 1) // bt)
     if wgs(256, 256) >= 200 or wgs(128, 256) >= 200 or wgs(128, 128) >= 200 or fmt == "q8a":
         return "gemm_fast_lds_kernel"
-    return "gemm_fast_ring_kernel"
+    return "gemm_fast_kz_kernel"
 
 
 def setup_dense(ci: int, mode: str, copies: int):
@@ -324,7 +324,7 @@ def measure_q8_prefill(mode: str, steps: int, warmup: int) -> dict:
     ms, _ = _timed(step, steps, warmup)
     tf = 2.0 * T * N * K / (ms * 1e-3) / 1e12
     return {"workload": f"q8_prefill_{mode}", "config": "q8_prefill_N4096_K4096_T512", "mode": mode,
-            "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f16", "kernel": "gemm_fast_ring_kernel",
+            "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f16", "kernel": "gemm_fast_kz_kernel",
             "value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK["f16"], "frac": tf / PEAK["f16"]}
 
 

@@ -638,39 +638,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
         }
 }
 
-// ================================================================================================
-// Dense fast mode, raw-weight ring: gemm_fast_ring_kernel (64 x 128 tiles, the tile that fills 256
-// CUs for a 512-token, 4096-row prefill).
-//
-// Per 64-k stage the workgroup copies the X tile (BT rows x 128 bytes, the XOR-swizzled slab of the
-// LDS kernel above) and the RAW code bytes of its BN weight rows (CPR 16-byte chunks per row: 2 for
-// Q4 / Q4A, 4 for Q8) straight from memory into LDS with buffer_load ... lds, and each wavefront
-// decodes its own B fragments from those bytes in registers: no decoded tile is written to LDS and
-// a weight byte is read from LDS as a byte, not as two 16-bit values.  Wavefronts sit 1 x 4 along
-// the weight rows, so every fragment is decoded once.  The LDS holds a ring of D stages (one LDS
-// array per slot, so the compiler can see that a copy into one slot never aliases the reads of
-// another); the copies and the block-scale loads (into registers, the same ring) of stage s + D - 1
-// are issued at stage s, so D - 1 stages of loads are in flight.  One barrier per stage, preceded by
-// a wait for this wavefront's copies of the current stage only (vmcnt counts loads in issue order).
-//
-// Raw-chunk layout: chunk c of tile row n sits at slot CPR n + (c ^ ((n / (16 / CPR)) % CPR)), so
-// the 8-byte fragment reads of 16 consecutive rows hit 16 different bank pairs.  Lane (li, g) of a
-// wavefront reads, for its tile row n = wn 32 MN + 32 mn + li, bytes 8g .. 8g+7 of the chunk of
-// MFMA step j: Q4 / Q4A chunk j / 2 (block j / 2; low nibbles for even j, high for odd j); Q8
-// chunk j (block j / 2, half j % 2).
-//
-// Measured on the Q4 prefill (N = K = 4096, T 512, f16): 32.5 us against 40.1 us for the
-// decoded-tile kernel with the same tile.  Timing-only copies of this kernel with parts removed:
-// 29-31 us whole, 12.6 us with only the X and raw-weight fragment reads left (each of the four
-// wavefronts reads the whole 64 x 64 X tile of a stage: 32 KiB of LDS reads per stage and CU),
-// 18.3 us with the MFMAs added, 24 us without the copies, and the decode and the barrier each
-// within 1-2 us once the MFMAs are there -- so the bound is the LDS read traffic of the A operand,
-// which the tile shape fixes.  Also measured and slower: wavefronts 2 x 2 (every fragment decoded
-// twice: 43-47 us), 8 wavefronts with the stage's two blocks split between two groups of four and
-// the partial sums added through LDS (37 us), two 32 x 128 workgroups per CU (53 us), explicit
-// MFMA / read / decode interleaving with sched_group_barrier (33-35 us), and, for the 14336-row
-// up-projection, 128 x 256 and 128 x 128 rings (227-262 us against 150 for the 256 x 256 decoded
-// tile).
 // s_waitcnt immediate that waits for at most N outstanding vector-memory loads and leaves the LDS /
 // scalar and export counters unconstrained (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8).
@@ -680,61 +647,69 @@ constexpr int vmcnt_only() {
     return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
-// Ring slot I of one kind (TAG) as its own LDS array: with a distinct object per slot the compiler
-// can see that the copies into one slot never alias the reads of another, and does not wait for
-// every copy in flight before an LDS read.
-template <int TAG, int I, int BYTES>
-__device__ __forceinline__ uint8_t* ring_slot() {
-    __shared__ __attribute__((aligned(16))) uint8_t b[BYTES];
+// ================================================================================================
+// Fast GEMM with K split over the wavefronts (Q4 / Q4A / Q8), for shapes too small for the decoded
+// tiles: a workgroup owns a 32 MT-token x 32 MN-row output tile (launched with 128 x 64); each of its 4
+// wavefronts computes the whole tile over its own quarter of the 64-k stages, from a ring in LDS that
+// only it writes and reads -- X (BT rows x 64 k of the stage; chunk c of row r at position
+// c ^ ((r / 2) % 8), so the 16-byte fragment reads of 32 rows hit distinct bank quads) and the raw
+// code chunks of its weight rows (chunk c of row n at position c ^ ((n / (16 / CPR)) % CPR)), both
+// copied by buffer_load ... lds -- so the main loop has no barrier, and the wait before a stage
+// counts only this wavefront's copies.  Each B fragment is decoded once in registers (frag16_words,
+// or frag16_codes for W-exact) and serves the MT MFMA row tiles; the four f32 partials are added
+// through LDS at the end in wavefront order.
+//
+// Measured on the Q4 prefill (N = K = 4096, T 512, f16): 31.8-33.4 us at 128 x 64, 39-43 us at
+// 64 x 128 (two row tiles per decoded fragment: counters showed 369 VALU instructions per wavefront
+// and stage for 32 MFMAs, nearly all decode); the 64 x 128 ring kernel it replaces (X and raw codes
+// shared by the 4 wavefronts of a 6-stage ring, one barrier per stage, each wavefront on its own
+// 32 rows over every stage) ran 32.5-34.5 us, and its Q8 and W-exact launches 46.9 and 49.5 us
+// against 39.2 and 44.7 here.  The 14336-row up-projection keeps the 256 x 256 decoded tiles (236 us
+// through this kernel against 129).
+// Tile 32 MT tokens x 32 MN weight rows; per wavefront and stage BT x 128 bytes of X and BN x 32 (Q8:
+// 64) bytes of codes.
+template <int SLOT, int I>
+__device__ __forceinline__ uint8_t* kz_slot() {
+    __shared__ __attribute__((aligned(16))) uint8_t b[4 * SLOT];
     return b;
 }
 
-// WX (W-exact, Q4 and Q8 with f16 X): the fragments hold the codes themselves as exact f16 (Q4
-// nibble - 8, Q8 q), each 32-k block's two MFMA steps accumulate into a block partial from zero,
-// and the block scale of the fragment's weight row (every accumulator of a lane belongs to the
-// lane's column, one weight row) multiplies the partial into the accumulator in f32: the weights are
-// never rounded.
-template <int FMT, int ST, int WM, int MT, int MN, int D, bool WX = false>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams p) {
-    static_assert(!WX || ((FMT == FMT_Q4 || FMT == FMT_Q8) && ST == XT_F16), "W-exact: Q4 / Q8 codes, f16 X");
-    static_assert(FMT != FMT_Q8A, "Q8A takes the decoded-tile kernels");
-    constexpr int NW = 4;                       // wavefronts
-    constexpr int WN = 4 / WM;
-    constexpr int BT = 32 * MT * WM;
-    constexpr int BN = 32 * MN * WN;
+// WX (W-exact, Q4 and Q8 with f16 X): the fragments hold the codes as exact f16 and each block's two
+// MFMA steps accumulate into a partial from zero, which the block scale of the lane's weight row
+// multiplies into the accumulator in f32.
+template <int FMT, int ST, int MT, int MN, int D, bool WX = false>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fast_kz_kernel(GemmParams p) {
+    static_assert(FMT == FMT_Q4 || FMT == FMT_Q4A || FMT == FMT_Q8, "Q4 / Q4A / Q8 codes");
+    static_assert(!WX || (FMT != FMT_Q4A && ST == XT_F16), "W-exact: Q4 / Q8 codes, f16 X");
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    constexpr int BT = 32 * MT, BN = 32 * MN;
     constexpr int CPR = FMT == FMT_Q8 ? 4 : 2;  // 16-byte code chunks per row and stage
-    constexpr int XCH = BT / (8 * NW);          // X copies (8 rows each) per wavefront and stage
-    constexpr int WL = (BN * CPR) % (64 * NW) == 0 ? 64 : 32;  // lanes per raw-weight copy
-    constexpr int WCH = BN * CPR / (WL * NW);   // raw-weight copies per wavefront and stage
-    constexpr int L = XCH + WCH + 2 * MN * (FMT == FMT_Q4A ? 2 : 1);  // loads per wavefront and stage
-    constexpr int LC = XCH + WCH;  // of which copies to LDS
-    static_assert(XCH * 8 * NW == BT && WCH * WL * NW == BN * CPR, "tile");
-    static_assert(D >= 3 && (D - 2) * L <= 63, "ring depth");
-    constexpr int XB = BT * 128, WBY = BN * CPR * 16;  // bytes per slot
-    auto xsl = [](auto ic) -> uint16_t* { return (uint16_t*)ring_slot<0, decltype(ic)::value, XB>(); };
-    auto wsl = [](auto ic) -> uint8_t* { return ring_slot<1, decltype(ic)::value, WBY>(); };
-
+    constexpr int ESZ = FMT == FMT_Q8 ? 4 : 2;  // scale bytes
+    constexpr int XB = BT * 128, WB = BN * CPR * 16, SLOT = XB + WB;  // per wavefront and stage
+    static_assert(D * 4 * SLOT <= 160 * 1024, "LDS");
+    constexpr int XCH = BT / 8;     // X copies (8 rows each) per stage
+    constexpr int WCH = BN * CPR / 64;  // raw-code copies (64 lanes x 16 bytes) per stage
+    constexpr int LC = XCH + WCH;   // copies to LDS per stage
+    static_assert((D - 1) * LC <= 63, "vmcnt range");
     const int r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
     const int n0 = blockIdx.x * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
     const int g = lane >> 5, li = lane & 31;
     const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
-    const int rows = min(BN, p.N - n0);  // weight rows of the tile that exist
+    const int s0 = (wave * nstage) >> 2, s1 = ((wave + 1) * nstage) >> 2;  // this wavefront's stages
+    const int rows = min(BN, p.N - n0);
 
-    // X: rows r0 .. r1-1; offsets past the end (rows past the tile, columns past K) read as zero.
-    // Copy i of wavefront w: rows 8 (NW i + w) .. +7 of the slab, lane at row 8 (NW i + w) + lane / 8,
-    // position lane % 8 holding chunk (lane % 8) ^ ((row / 2) % 8) (= 4 (w % 2) + lane / 16).
     uint16_t* const xbase = (uint16_t*)p.X + (size_t)r0 * K;
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(xbase, 0, (r1 - r0) * K * 2, 0x00020000);
-    const int xc = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    // X copy i: rows 8 i .. 8 i + 7; lane at row 8 i + lane / 8, position lane % 8 holding chunk
+    // (lane % 8) ^ ((row / 2) % 8) = (lane % 8) ^ ((4 i + lane / 16) % 8)
     int xoff[XCH];
 #pragma unroll
-    for (int i = 0; i < XCH; i++) xoff[i] = (8 * (NW * i + wave) + (lane >> 3)) * K * 2 + 16 * xc;
-
-    // Raw codes, scales and offsets of rows n0 .. n0+rows-1 (past them: zero).
-    constexpr int ESZ = FMT == FMT_Q8 ? 4 : 2;  // scale bytes
+    for (int i = 0; i < XCH; i++) {
+        const int row = 8 * i + (lane >> 3);
+        xoff[i] = row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+    }
     const int rowb = FMT == FMT_Q8 ? K : K >> 1;
     const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)p.codes + (size_t)n0 * rowb), 0, rows * rowb, 0x00020000);
@@ -744,45 +719,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(FMT == FMT_Q4A ? (const uint8_t*)p.offs + (size_t)n0 * ngr * 2 : (const uint8_t*)p.scales), 0,
         FMT == FMT_Q4A ? rows * ngr * 2 : 0, 0x00020000);
-    // raw copy i of this wavefront: slots WL (NW i + wave) + lane; slot -> (row, chunk) as above
+    // raw copy i: slots 64 i + lane -> tile row n = slot / CPR, chunk position cs = slot % CPR, holding
+    // the row's chunk cs ^ ((n / (16 / CPR)) % CPR) of the stage
+    auto swz = [](int n) { return (n / (16 / CPR)) % CPR; };
     int woff[WCH];
 #pragma unroll
     for (int i = 0; i < WCH; i++) {
-        const int slot = WL * (NW * i + wave) + (lane & (WL - 1));
+        const int slot = 64 * i + lane;
         const int n = slot / CPR, cs = slot % CPR;
-        const int c = cs ^ ((n / (16 / CPR)) % CPR);
-        woff[i] = n * rowb + 16 * c;
+        woff[i] = n * rowb + 16 * (cs ^ swz(n));
     }
-    // this lane's weight rows (tile-relative), one per mn; per-lane parts of the scale offsets
-    int brow[MN], soff[MN], ooff[MN];
+    int soff[MN], ooff[MN];
 #pragma unroll
     for (int mn = 0; mn < MN; mn++) {
-        brow[mn] = wn * 32 * MN + 32 * mn + li;
-        soff[mn] = brow[mn] * nblk * ESZ;
-        ooff[mn] = brow[mn] * ngr * 2;
+        soff[mn] = (32 * mn + li) * nblk * ESZ;
+        ooff[mn] = (32 * mn + li) * ngr * 2;
     }
-
-    // Scales (and offsets) of a stage's two blocks 2 st + b for this lane's rows, raw bits.
     struct Scales {
         uint32_t d[MN][2];
         uint32_t m[MN][2];
     };
-    auto issue = [&](int st, auto slotc, Scales& sc) __attribute__((always_inline)) {
-        const int koff = st * 64 < K ? st * 128 : 0x40000000;  // X columns of the stage (past K: zero)
-        uint16_t* const xd = xsl(slotc);
-        uint8_t* const wd = wsl(slotc);
+    auto issue = [&](auto slotc, int st, Scales& sc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slotc)::value;
+        asm volatile("" ::: "memory");
+        uint8_t* const xd = kz_slot<SLOT, sl>() + wave * SLOT;
+        uint8_t* const wd = xd + XB;
+        const int sr = min(st, s1 - 1);  // stages past the wavefront's last repeat it
+        const int koff = sr * 64 < K ? sr * 128 : 0x40000000;
 #pragma unroll
-        for (int i = 0; i < XCH; i++) buffer_copy16_lds(xrs, xd + 8 * (NW * i + wave) * 64, xoff[i] + koff);
+        for (int i = 0; i < XCH; i++) buffer_copy16_lds(xrs, xd + 1024 * i, xoff[i] + koff);
 #pragma unroll
-        for (int i = 0; i < WCH; i++) {
-            if (WL == 64 || lane < 32)
-                buffer_copy16_lds(crs, wd + 16 * WL * (NW * i + wave), woff[i] + st * (16 * CPR));
-        }
+        for (int i = 0; i < WCH; i++) buffer_copy16_lds(crs, wd + 1024 * i, woff[i] + 16 * CPR * sr);
 #pragma unroll
         for (int mn = 0; mn < MN; mn++)
 #pragma unroll
             for (int b = 0; b < 2; b++) {
-                const int blk = 2 * st + b;
+                const int blk = 2 * sr + b;
                 if constexpr (FMT == FMT_Q8)
                     sc.d[mn][b] = __builtin_amdgcn_raw_buffer_load_b32(srs, soff[mn], 4 * blk, 0);
                 else
@@ -800,79 +772,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
 #pragma unroll
             for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-    auto frags_a = [&](const uint16_t* xsb, int j, short8_t (&A)[MT]) {
-        const uint16_t* xa = xsb + (wm * 32 * MT + li) * 64 + 8 * ((2 * j + g) ^ ((li >> 1) & 7));
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) A[mt] = *(const short8_t*)(xa + mt * 32 * 64);
-    };
-    // bytes 8g .. 8g+7 of chunk c of this lane's row mn
-    auto raw_read = [&](const uint8_t* wsb, int mn, int c) -> uint2 {
-        const int n = brow[mn];
-        const int cs = c ^ ((n / (16 / CPR)) % CPR);
-        return *(const uint2*)(wsb + 16 * (CPR * n + cs) + 8 * g);
-    };
     auto mfma = [&](const short8_t& a, const short8_t& b, f32x16_t& c) {
         if constexpr (ST == XT_F16)
             c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
         else
             c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     };
-
     Scales scr[D];
-    // The four MFMA steps of stage s (slot u); FAST: every block decodes by (1).  Step j uses block
-    // j / 2: Q4 / Q4A one raw chunk per block (low nibbles for even j, high for odd j); Q8 one chunk
-    // per step.
+
+    // The four MFMA steps of a stage; step j: X columns 16 j .. 16 j + 15, block j / 2 of every row
+    // (Q4 / Q4A: one 16-byte chunk per block, low nibbles for even j, high for odd j; Q8: chunk j).
     auto body = [&](auto uc, auto fastc, int s, const float (&d)[MN][2], const float (&c0)[MN][2],
                     const float (&mm)[MN][2], const uint32_t (&dh)[MN][2]) __attribute__((always_inline)) {
         constexpr bool FAST = decltype(fastc)::value;
-        const uint16_t* const xsb = xsl(uc);
-        const uint8_t* const wsb = wsl(uc);
-        constexpr int NSTEP = 4;
+        const uint8_t* const xb = kz_slot<SLOT, decltype(uc)::value>() + wave * SLOT;
+        const uint16_t* const xsb = (const uint16_t*)xb;
+        const uint8_t* const wsb = xb + XB;
         short8_t A[2][MT], B[2][MN];
+        uint2 raw[MN];
         f32x16_t part[MT][MN];  // WX: the current block's partial
-        uint2 raw[2][MN];
-        auto decode = [&](int q, const uint2 (&rw)[MN], short8_t (&Bo)[MN]) __attribute__((always_inline)) {
+        auto frags_a = [&](int j, short8_t (&Ao)[MT]) __attribute__((always_inline)) {
+            const uint16_t* xa = xsb + li * 64 + 8 * ((2 * j + g) ^ ((li >> 1) & 7));
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) Ao[mt] = *(const short8_t*)(xa + mt * 32 * 64);
+        };
+        auto read_raw = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mn = 0; mn < MN; mn++) {
+                const int n = 32 * mn + li;
+                raw[mn] = *(const uint2*)(wsb + 16 * (CPR * n + (ch ^ swz(n))) + 8 * g);
+            }
+        };
+        auto decode = [&](int q, short8_t (&Bo)[MN]) __attribute__((always_inline)) {
             const int b = q >> 1;
 #pragma unroll
             for (int mn = 0; mn < MN; mn++) {
                 uint32_t c[2];
                 if constexpr (FMT == FMT_Q8) {
-                    c[0] = keep_u32(rw[mn].x ^ 0x80808080u);
-                    c[1] = keep_u32(rw[mn].y ^ 0x80808080u);
+                    c[0] = keep_u32(raw[mn].x ^ 0x80808080u);
+                    c[1] = keep_u32(raw[mn].y ^ 0x80808080u);
                 } else if (q & 1) {
-                    c[0] = keep_u32((rw[mn].x >> 4) & 0x0F0F0F0Fu);
-                    c[1] = keep_u32((rw[mn].y >> 4) & 0x0F0F0F0Fu);
+                    c[0] = keep_u32((raw[mn].x >> 4) & 0x0F0F0F0Fu);
+                    c[1] = keep_u32((raw[mn].y >> 4) & 0x0F0F0F0Fu);
                 } else {
-                    c[0] = keep_u32(rw[mn].x & 0x0F0F0F0Fu);
-                    c[1] = keep_u32(rw[mn].y & 0x0F0F0F0Fu);
+                    c[0] = keep_u32(raw[mn].x & 0x0F0F0F0Fu);
+                    c[1] = keep_u32(raw[mn].y & 0x0F0F0F0Fu);
                 }
                 if constexpr (WX) Bo[mn] = frag16_codes<FMT>(c);
                 else if constexpr (FAST) Bo[mn] = frag16_words<FMT, ST>(c, d[mn][b], dh[mn][b], c0[mn][b]);
                 else Bo[mn] = frag16_words_slow<FMT, ST>(c, d[mn][b], mm[mn][b]);
             }
         };
-        // raw chunk of step q (Q4: one chunk per block; Q8: one per step)
-        auto read_raw = [&](int q, uint2 (&rw)[MN]) __attribute__((always_inline)) {
+        frags_a(0, A[0]);
+        read_raw(0);
+        decode(0, B[0]);
 #pragma unroll
-            for (int mn = 0; mn < MN; mn++) rw[mn] = raw_read(wsb, mn, FMT == FMT_Q8 ? q : (q >> 1));
-        };
-        frags_a(xsb, 0, A[0]);
-        read_raw(0, raw[0]);
-        if constexpr (FMT == FMT_Q8) read_raw(1, raw[1]);
-        decode(0, raw[0], B[0]);
-#pragma unroll
-        for (int q = 0; q < NSTEP; q++) {
+        for (int q = 0; q < 4; q++) {
             const int cur = q & 1, nx = cur ^ 1;
-            if (q + 1 < NSTEP) {
-                frags_a(xsb, q + 1, A[nx]);
-                if constexpr (FMT == FMT_Q8) {
-                    if (q + 2 < NSTEP) read_raw(q + 2, raw[cur]);
-                } else {
-                    if ((q & 1) && q + 1 < NSTEP) read_raw(q + 1, raw[0]);  // next block's chunk
-                }
+            if (q + 1 < 4) {
+                frags_a(q + 1, A[nx]);
+                if constexpr (FMT == FMT_Q8) read_raw(q + 1);  // each step its own chunk
+                else if (q == 1) read_raw(1);                  // the second block's chunks
             }
             if constexpr (WX) {
-                // block q / 2: its partial from zero over its two steps, then scaled into acc
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -896,241 +858,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_ring_kernel(GemmParams 
 #pragma unroll
                     for (int mn = 0; mn < MN; mn++) mfma(A[cur][mt], B[cur][mn], acc[mt][mn]);
             }
-            if (q + 1 < NSTEP) {
-                if constexpr (FMT == FMT_Q8) decode(q + 1, raw[nx], B[nx]);
-                else decode(q + 1, raw[0], B[nx]);
-            }
-        }
-    };
-    auto stage = [&](auto uc, int s) __attribute__((always_inline)) {
-        constexpr int u = decltype(uc)::value;  // s % D
-        // this wavefront's copies of stage s have landed (D - 2 later stages issued since); the
-        // barrier then covers every wavefront's copies and frees slot (s - 1) % D for stage s + D - 1.
-        // The wait counts the later stages' copies only: copies to LDS complete in issue order among
-        // themselves but not with respect to the scale loads into registers, so the scale loads
-        // issued since may already be done (their own waits the compiler places before their uses).
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 2) * LC>());
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(min(s + D - 1, nstage - 1), std::integral_constant<int, (u + D - 1) % D>{}, scr[(u + D - 1) % D]);
-        // block scales of this stage: c0 of (1) and whether (1) is the pages' rounding
-        float d[MN][2], c0[MN][2], mm[MN][2];
-        uint32_t dh[MN][2];
-        bool fast = true;
-#pragma unroll
-        for (int mn = 0; mn < MN; mn++)
-#pragma unroll
-            for (int b = 0; b < 2; b++) {
-                const bool valid = 2 * s + b < nblk;  // a K tail block decodes as zeros
-                const uint32_t db = valid ? scr[u].d[mn][b] : 0u;
-                dh[mn][b] = db & 0xFFFFu;
-                d[mn][b] = FMT == FMT_Q8 ? __uint_as_float(db) : f16_to_f32((uint16_t)db);
-                mm[mn][b] = FMT == FMT_Q4A ? (valid ? bf16_to_f32((uint16_t)scr[u].m[mn][b]) : 0.f) : 0.f;
-                RawBlock<FMT> rb{};
-                rb.d = d[mn][b];
-                rb.m = mm[mn][b];
-                bool f;
-                c0[mn][b] = block_c0<FMT>(rb, f);
-                if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) fast = fast && (f || !valid);
-            }
-        if constexpr (WX || (FMT == FMT_Q4 && ST == XT_F16)) {
-            body(uc, std::true_type{}, s, d, c0, mm, dh);
-        } else {
-            if (__all(fast)) body(uc, std::true_type{}, s, d, c0, mm, dh);
-            else body(uc, std::false_type{}, s, d, c0, mm, dh);
-        }
-    };
-
-    // prologue: stages 0 .. D-2 in flight
-    auto prologue = [&](auto tc) __attribute__((always_inline)) {
-        constexpr int t = decltype(tc)::value;
-        issue(min(t, nstage - 1), tc, scr[t]);
-    };
-    run_stages_c<0, D - 1>(prologue);
-    int s = 0;
-    for (; s + D - 1 < nstage; s += D) run_stages<0, D>(stage, s);
-    run_tail_stages<0, D>(stage, s, nstage);
-
-    QG_GLOBAL float* Y = gptr_mut<float>(p.Y);
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int mn = 0; mn < MN; mn++) {
-            const int n = n0 + wn * 32 * MN + 32 * mn + li;
-            if (n >= p.N) continue;
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = r0 + wm * 32 * MT + mt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (r < r1) Y[(size_t)r * p.N + n] = acc[mt][mn][i];
-            }
-        }
-}
-
-// ================================================================================================
-// Fast GEMM with K split over the wavefronts (Q4 / Q4A): a workgroup owns a 64-token x 128-row output
-// tile; each of its 4 wavefronts computes the whole tile over its own quarter of the 64-k stages, from
-// a ring in LDS that only it writes and reads -- X (64 rows x 64 k of the stage, XOR-swizzled as in
-// the ring kernel) and the raw code chunks of the 128 weight rows (32 bytes a row and stage), copied
-// by buffer_load ... lds -- so the main loop has no barrier.  Per stage a wavefront reads 8 KiB of X
-// fragments and 4 KiB of raw codes for 32 MFMAs (the 64 x 128 ring kernel: 9 KiB for 8), decodes
-// each B fragment once (frag16_words), and the four 64 x 128 f32 partials are added through LDS at
-// the end in wavefront order.
-// Tile 32 MT tokens x 32 MN weight rows; per wavefront and stage BT x 128 bytes of X and BN x 32 bytes
-// of codes.
-template <int SLOT, int I>
-__device__ __forceinline__ uint8_t* kz_slot() {
-    __shared__ __attribute__((aligned(16))) uint8_t b[4 * SLOT];
-    return b;
-}
-
-template <int FMT, int ST, int MT, int MN, int D>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fast_kz_kernel(GemmParams p) {
-    static_assert(FMT == FMT_Q4 || FMT == FMT_Q4A, "Q4 / Q4A codes");
-    static_assert(D >= 2 && D <= 4, "ring depth");
-    constexpr int BT = 32 * MT, BN = 32 * MN;
-    constexpr int XB = BT * 128, WB = BN * 32, SLOT = XB + WB;  // per wavefront and stage
-    static_assert(D * 4 * SLOT <= 160 * 1024, "LDS");
-    constexpr int XCH = BT / 8;     // X copies (8 rows each) per stage
-    constexpr int WCH = BN / 32;    // raw-code copies (64 lanes x 16 bytes) per stage
-    constexpr int LC = XCH + WCH;   // copies to LDS per stage
-    static_assert((D - 1) * LC <= 63, "vmcnt range");
-    const int r0 = blockIdx.y * BT, r1 = min(p.R, r0 + BT);
-    const int n0 = blockIdx.x * BN;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 5, li = lane & 31;
-    const int K = p.K, nblk = K >> 5, nstage = (K + 63) >> 6;
-    const int s0 = (wave * nstage) >> 2, s1 = ((wave + 1) * nstage) >> 2;  // this wavefront's stages
-    const int rows = min(BN, p.N - n0);
-
-    uint16_t* const xbase = (uint16_t*)p.X + (size_t)r0 * K;
-    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(xbase, 0, (r1 - r0) * K * 2, 0x00020000);
-    // X copy i: rows 8 i .. 8 i + 7; lane at row 8 i + lane / 8, position lane % 8 holding chunk
-    // (lane % 8) ^ ((row / 2) % 8) = (lane % 8) ^ ((4 i + lane / 16) % 8)
-    int xoff[XCH];
-#pragma unroll
-    for (int i = 0; i < XCH; i++) {
-        const int row = 8 * i + (lane >> 3);
-        xoff[i] = row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
-    }
-    const int rowb = K >> 1;
-    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)p.codes + (size_t)n0 * rowb), 0, rows * rowb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)p.scales + (size_t)n0 * nblk * 2), 0, rows * nblk * 2, 0x00020000);
-    const int ngr = FMT == FMT_Q4A ? K / p.group : 1;
-    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(FMT == FMT_Q4A ? (const uint8_t*)p.offs + (size_t)n0 * ngr * 2 : (const uint8_t*)p.scales), 0,
-        FMT == FMT_Q4A ? rows * ngr * 2 : 0, 0x00020000);
-    // raw copy i: slots 64 i + lane -> tile row n = slot / 2, chunk position cs = slot % 2, holding
-    // the row's chunk cs ^ ((n / 8) % 2) of the stage
-    int woff[WCH];
-#pragma unroll
-    for (int i = 0; i < WCH; i++) {
-        const int slot = 64 * i + lane;
-        const int n = slot >> 1, cs = slot & 1;
-        woff[i] = n * rowb + 16 * (cs ^ ((n >> 3) & 1));
-    }
-    int soff[MN], ooff[MN];
-#pragma unroll
-    for (int mn = 0; mn < MN; mn++) {
-        soff[mn] = (32 * mn + li) * nblk * 2;
-        ooff[mn] = (32 * mn + li) * ngr * 2;
-    }
-    struct Scales {
-        uint32_t d[MN][2];
-        uint32_t m[MN][2];
-    };
-    auto issue = [&](auto slotc, int st, Scales& sc) __attribute__((always_inline)) {
-        constexpr int sl = decltype(slotc)::value;
-        asm volatile("" ::: "memory");
-        uint8_t* const xd = kz_slot<SLOT, sl>() + wave * SLOT;
-        uint8_t* const wd = xd + XB;
-        const int sr = min(st, s1 - 1);  // stages past the wavefront's last repeat it
-        const int koff = sr * 64 < K ? sr * 128 : 0x40000000;
-#pragma unroll
-        for (int i = 0; i < XCH; i++) buffer_copy16_lds(xrs, xd + 1024 * i, xoff[i] + koff);
-#pragma unroll
-        for (int i = 0; i < WCH; i++) buffer_copy16_lds(crs, wd + 1024 * i, woff[i] + 32 * sr);
-#pragma unroll
-        for (int mn = 0; mn < MN; mn++)
-#pragma unroll
-            for (int b = 0; b < 2; b++) {
-                const int blk = 2 * sr + b;
-                sc.d[mn][b] = __builtin_amdgcn_raw_buffer_load_b16(srs, soff[mn], 2 * blk, 0);
-                if constexpr (FMT == FMT_Q4A)
-                    sc.m[mn][b] = __builtin_amdgcn_raw_buffer_load_b16(ors, ooff[mn], 2 * ((32 * blk) / p.group), 0);
-            }
-    };
-
-    f32x16_t acc[MT][MN];
-#pragma unroll
-    for (int a = 0; a < MT; a++)
-#pragma unroll
-        for (int b = 0; b < MN; b++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
-
-    auto mfma = [&](const short8_t& a, const short8_t& b, f32x16_t& c) {
-        if constexpr (ST == XT_F16)
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-        else
-            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    };
-    Scales scr[D];
-
-    // The four MFMA steps of a stage; step j: X columns 16 j .. 16 j + 15, block j / 2 of every row,
-    // low nibbles for even j, high for odd j.
-    auto body = [&](auto uc, auto fastc, int s, const float (&d)[MN][2], const float (&c0)[MN][2],
-                    const float (&mm)[MN][2], const uint32_t (&dh)[MN][2]) __attribute__((always_inline)) {
-        constexpr bool FAST = decltype(fastc)::value;
-        const uint8_t* const xb = kz_slot<SLOT, decltype(uc)::value>() + wave * SLOT;
-        const uint16_t* const xsb = (const uint16_t*)xb;
-        const uint8_t* const wsb = xb + XB;
-        short8_t A[2][MT], B[2][MN];
-        uint2 raw[MN];
-        auto frags_a = [&](int j, short8_t (&Ao)[MT]) __attribute__((always_inline)) {
-            const uint16_t* xa = xsb + li * 64 + 8 * ((2 * j + g) ^ ((li >> 1) & 7));
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) Ao[mt] = *(const short8_t*)(xa + mt * 32 * 64);
-        };
-        auto read_raw = [&](int blk) __attribute__((always_inline)) {
-#pragma unroll
-            for (int mn = 0; mn < MN; mn++) {
-                const int n = 32 * mn + li;
-                raw[mn] = *(const uint2*)(wsb + 16 * (2 * n + (blk ^ ((n >> 3) & 1))) + 8 * g);
-            }
-        };
-        auto decode = [&](int q, short8_t (&Bo)[MN]) __attribute__((always_inline)) {
-            const int b = q >> 1;
-#pragma unroll
-            for (int mn = 0; mn < MN; mn++) {
-                uint32_t c[2];
-                if (q & 1) {
-                    c[0] = keep_u32((raw[mn].x >> 4) & 0x0F0F0F0Fu);
-                    c[1] = keep_u32((raw[mn].y >> 4) & 0x0F0F0F0Fu);
-                } else {
-                    c[0] = keep_u32(raw[mn].x & 0x0F0F0F0Fu);
-                    c[1] = keep_u32(raw[mn].y & 0x0F0F0F0Fu);
-                }
-                if constexpr (FAST) Bo[mn] = frag16_words<FMT, ST>(c, d[mn][b], dh[mn][b], c0[mn][b]);
-                else Bo[mn] = frag16_words_slow<FMT, ST>(c, d[mn][b], mm[mn][b]);
-            }
-        };
-        frags_a(0, A[0]);
-        read_raw(0);
-        decode(0, B[0]);
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int cur = q & 1, nx = cur ^ 1;
-            if (q + 1 < 4) {
-                frags_a(q + 1, A[nx]);
-                if (q == 1) read_raw(1);  // the second block's chunks
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-                for (int mn = 0; mn < MN; mn++) mfma(A[cur][mt], B[cur][mn], acc[mt][mn]);
             if (q + 1 < 4) decode(q + 1, B[nx]);
         }
     };
@@ -1152,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kz_kernel(GemmParams p)
                 const bool valid = 2 * s + b < nblk;  // a K tail block decodes as zeros
                 const uint32_t db = valid ? scr[u].d[mn][b] : 0u;
                 dh[mn][b] = db & 0xFFFFu;
-                d[mn][b] = f16_to_f32((uint16_t)db);
+                d[mn][b] = FMT == FMT_Q8 ? __uint_as_float(db) : f16_to_f32((uint16_t)db);
                 mm[mn][b] = FMT == FMT_Q4A ? (valid ? bf16_to_f32((uint16_t)scr[u].m[mn][b]) : 0.f) : 0.f;
                 RawBlock<FMT> rb{};
                 rb.d = d[mn][b];
@@ -1161,7 +888,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kz_kernel(GemmParams p)
                 c0[mn][b] = block_c0<FMT>(rb, f);
                 if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) fast = fast && (f || !valid);
             }
-        if constexpr (FMT == FMT_Q4 && ST == XT_F16) {
+        if constexpr (WX || (FMT == FMT_Q4 && ST == XT_F16)) {
             body(uc, std::true_type{}, s, d, c0, mm, dh);
         } else {
             if (__all(fast)) body(uc, std::true_type{}, s, d, c0, mm, dh);
@@ -1508,17 +1235,11 @@ static void fast_lds_launch(const GemmParams& p, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fast_lds_kernel<FMT, ST, WM, MT, MN, DP, GR>), grid, dim3(kThreads), 0, s, p);
 }
 
-template <int FMT, int ST, int WM, int MT, int MN, int D, bool WX = false>
-static void fast_ring_launch(const GemmParams& p, hipStream_t s) {
-    constexpr int BT = 32 * MT * WM, BN = 32 * MN * (4 / WM);
-    dim3 grid((p.N + BN - 1) / BN, (p.R + BT - 1) / BT);
-    hipLaunchKernelGGL((gemm_fast_ring_kernel<FMT, ST, WM, MT, MN, D, WX>), grid, dim3(kThreads), 0, s, p);
-}
 
-template <int FMT, int ST, int MT, int MN, int D>
+template <int FMT, int ST, int MT, int MN, int D, bool WX = false>
 static void fast_kz_launch(const GemmParams& p, hipStream_t s) {
     dim3 grid((p.N + 32 * MN - 1) / (32 * MN), (p.R + 32 * MT - 1) / (32 * MT));
-    hipLaunchKernelGGL((gemm_fast_kz_kernel<FMT, ST, MT, MN, D>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_fast_kz_kernel<FMT, ST, MT, MN, D, WX>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <int FMT, int ST>
@@ -1536,20 +1257,17 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     if (wgs(256, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 4, 4, 1>(p, s);
     if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4, 4>(p, s);
     if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
-    // Smaller shapes: Q4 / Q4A 128 x 64 tiles with K split over the wavefronts (Q4 prefill N = K =
-    // 4096, T 512: 31.8 us against 34.5 for the ring kernel below and 39.1 for the same kernel with
-    // 64 x 128 tiles, whose decode costs twice the VALU work per MFMA); Q8 the raw-weight ring, 64 x 128
-    // tiles, wavefronts 1 x 4, six stages (Q8 codes are twice the bytes: the k-split rings would not
-    // fit); Q8A (its per-block offsets are not in the ring) the 128 x 128 decoded tiles
+    // Smaller shapes: 128 x 64 tiles with K split over the wavefronts (Q4 prefill N = K = 4096, T 512:
+    // 31.8 us; Q8 39.2 us); Q8A (its per-block offsets are not in that kernel's ring) the 128 x 128
+    // decoded tiles
     if constexpr (FMT == FMT_Q8A) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
-    else if constexpr (FMT == FMT_Q4 || FMT == FMT_Q4A) return fast_kz_launch<FMT, ST, 4, 2, 2>(p, s);
-    else return fast_ring_launch<FMT, ST, 1, 2, 1, 6>(p, s);
+    else return fast_kz_launch<FMT, ST, 4, 2, 2>(p, s);
 }
 
 hipError_t launch_gemm_fast_wexact(int fmt, const GemmParams& p, hipStream_t s) {
-    // 64 x 128 tiles of the raw-weight ring, whatever the shape
-    if (fmt == FMT_Q4) fast_ring_launch<FMT_Q4, XT_F16, 1, 2, 1, 6, true>(p, s);
-    else if (fmt == FMT_Q8) fast_ring_launch<FMT_Q8, XT_F16, 1, 2, 1, 6, true>(p, s);
+    // 128 x 64 tiles with K split over the wavefronts, whatever the shape
+    if (fmt == FMT_Q4) fast_kz_launch<FMT_Q4, XT_F16, 4, 2, 2, true>(p, s);
+    else if (fmt == FMT_Q8) fast_kz_launch<FMT_Q8, XT_F16, 4, 2, 2, true>(p, s);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
