@@ -73,3 +73,24 @@ def test_batch_other_paths(orc, case):
     for i, (w, y, N) in enumerate(zip(ws, Ys, Ns)):
         Yr, S, _ = orc.gemm(fmt, w["codes"], w["scales"], w.get("offsets"), 64, N, K, xo, xt, T)
         check_tol(y.cpu().numpy(), Yr, S, TAU[mode], f"job {i} (N {N})")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_batch_qkv_decode_shape_sampled(orc, T):
+    """The benchmark's batched q / k / v step (Q8, N 4096 + 1024 + 1024, K 4096, f32 X) at T = 1 and
+    T = 4, in its launch configuration: sampled outputs of every job against the oracle."""
+    from helpers import sample_idx
+    K, Ns = 4096, (4096, 1024, 1024)
+    ws = [synth.make_dense("q8", N, K, T, "f32", 1.0, 1001 + 10 * i) for i, N in enumerate(Ns)]
+    X = synth.normal_as(1001, synth.STREAM_X, T * K, 0.0, 1.0, "f32").reshape(T, K)
+    dw = [(dev(w["codes"]), dev(w["scales"])) for w in ws]
+    Ys = [torch.full((T, N), float("nan"), device="cuda") for N in Ns]
+    print(f"batch qkv T={T}", flush=True)
+    qg.qgemm_batch("q8", 64, [(c, s, None, y, N) for (c, s), y, N in zip(dw, Ys, Ns)], dev(X), K, T, "exact")
+    torch.cuda.synchronize()
+    for i, (w, y, N) in enumerate(zip(ws, Ys, Ns)):
+        ns = sample_idx(N, 96, 20 + i)
+        Yr, S, _ = orc.gemm("q8", w["codes"], w["scales"], None, 64, N, K, X, "f32", T, ns=ns)
+        yy = y.cpu().numpy()
+        check_tol(yy[:, ns], Yr, S, TAU["exact"], f"job {i} (N {N})")
+        assert np.all(np.isfinite(yy))

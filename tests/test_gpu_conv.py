@@ -144,3 +144,28 @@ def test_conv_1x1_equals_dense_exact_gemm():
     qg.qgemm_q8(c, s, x, Yg, n_out, cin, H * W, "exact")
     torch.cuda.synchronize()
     assert torch.equal(Yc, Yg)
+
+
+def test_conv_bench_shape_sampled(orc):
+    """The benchmark's convolution in its launch configuration: 64 x 64 pixels, 256 -> 256 channels,
+    3 x 3 taps, Q4 weights, group norm over 32 groups with SiLU, statistics from the device (sampled
+    outputs against the oracle's statistics and convolution)."""
+    H = W = 64
+    cin, n_out, ksz, groups = 256, 256, 3, 32
+    K = ksz * ksz * cin
+    w = synth.make_dense("q4", n_out, K, 1, "f32", 1.0, 1501)
+    X = synth.normal_as(1501, synth.STREAM_X, H * W * cin, 0.0, 1.0, "f32")
+    gb = np.concatenate([np.ones(cin, np.float32), np.zeros(cin, np.float32)])
+    Xd = dev(X)
+    sdev = torch.empty((groups, 2), device="cuda")
+    qg.qg_conv_stats(Xd, H * W, cin, groups, 1e-5, sdev)
+    Y = torch.full((H * W, n_out), float("nan"), device="cuda")
+    qg.qg_conv2d("q4", dev(w["codes"]), dev(w["scales"]), Xd, H, W, cin, ksz, 1, n_out, Y, norm="group",
+                 groups=groups, stats=sdev, gamma_beta=dev(gb), silu=True)
+    torch.cuda.synchronize()
+    st = orc.conv_stats(X, H * W, cin, groups, 1e-5).astype(np.float32)
+    ps, os_ = sample_idx(H * W, 200, 11), sample_idx(n_out, 32, 12)
+    Yr, S = orc.conv2d("q4", w["codes"], w["scales"], None, 64, n_out, X, H, W, cin, ksz, 1, "group", groups, st,
+                       gb, True, ps=ps, os_=os_)
+    check_tol(Y.cpu().numpy()[np.ix_(ps, os_)], Yr, S, TAU["exact"], "conv bench shape")
+    assert np.all(np.isfinite(Y.cpu().numpy()))
