@@ -458,11 +458,28 @@ __device__ __forceinline__ float block_sum_stats(float v, float* red) {
 
 template <bool DEV>
 __device__ __forceinline__ float group_pass(const float* X, int npix, int cin, int cpg, int g, float mean) {
+    const float* base = X + (size_t)g * cpg;
+    if (kStatsThreads % cpg == 0) {
+        // cpg divides the thread count: every thread keeps one channel and strides over the pixels,
+        // so its loads are independent and go out eight at a time
+        const int P = kStatsThreads / cpg, j = threadIdx.x % cpg;
+        float s = 0.f;
+#pragma unroll 8
+        for (int q = threadIdx.x / cpg; q < npix; q += P) {
+            const float x = base[(size_t)q * cin + j];
+            if constexpr (DEV) {
+                const float d = x - mean;
+                s += d * d;
+            } else {
+                s += x;
+            }
+        }
+        return s;
+    }
     // thread t starts at value t of the group: pixel t / cpg, channel t % cpg, and steps by 1024
     const int dq = kStatsThreads / cpg, dj = kStatsThreads % cpg;
     int q = threadIdx.x / cpg, j = threadIdx.x % cpg;
     float s = 0.f;
-    const float* base = X + (size_t)g * cpg;
     while (q < npix) {
         const float x = base[(size_t)q * cin + j];
         if constexpr (DEV) {
