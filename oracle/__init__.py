@@ -69,6 +69,8 @@ def lib():
         L.orc_gemm.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _i, _p, _p, _i]
         L.orc_x_half.restype = None
         L.orc_x_half.argtypes = [_p, _i, _p, _i, _p, _p]
+        L.orc_x_half_guard.restype = None
+        L.orc_x_half_guard.argtypes = [_p, _i, _i, _p, _i, _i, _p, _p]
         L.orc_swiglu.restype = None
         L.orc_swiglu.argtypes = [_p, _p, _sz, _p]
         L.orc_moe_plan.restype = _i
@@ -197,6 +199,20 @@ def x_half(X, K, src=None, R=None):
     xh = np.empty((R, K), np.uint16)
     rs = np.empty(R, np.float32)
     lib().orc_x_half(_ptr(x), K, _ptr(srca), R, _ptr(xh), _ptr(rs))
+    return xh, rs
+
+
+def x_half_guard(X, K, shift, src=None, R=None, x_rows=None):
+    """(xh f16 bits [R, K], rs f32 [R]) of the fixed power-of-two range guard: x * 2^-shift to f16."""
+    x = _c(X, np.float32)
+    srca = None if src is None else _c(src, np.int32)
+    if x_rows is None:
+        x_rows = x.size // K
+    if R is None:
+        R = srca.size if srca is not None else x_rows
+    xh = np.empty((R, K), np.uint16)
+    rs = np.empty(R, np.float32)
+    lib().orc_x_half_guard(_ptr(x), x_rows, K, _ptr(srca), R, int(shift), _ptr(xh), _ptr(rs))
     return xh, rs
 
 

@@ -288,6 +288,27 @@ void orc_x_half(const float* X, int K, const int* src, int R, uint16_t* xh, floa
     }
 }
 
+/* ---------------------------------------------------------------------------------------
+ * Power-of-two range guard (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs", Guards and p2):
+ * a half site stores x * 2^-s for a fixed shift s of the site, 0 <= s <= 14, and the matmul
+ * that reads it multiplies its result by 2^s.  Row r of the output is source row src[r] (or r);
+ * a source outside [0, x_rows) reads as zeros.  xh gets the f16 bits of x * 2^-s (product in
+ * f32, then nearest-even, overflow to infinity), rs the factor 2^s.
+ */
+void orc_x_half_guard(const float* X, int x_rows, int K, const int* src, int R, int shift, uint16_t* xh,
+                      float* rs) {
+    const float s = ldexpf(1.0f, -shift);
+    for (int r = 0; r < R; r++) {
+        const int sr = src ? src[r] : r;
+        const int ok = sr >= 0 && sr < x_rows;
+        for (int k = 0; k < K; k++) {
+            float v = ok ? X[(size_t)sr * K + k] * s : 0.0f;
+            xh[(size_t)r * K + k] = orc_f32_to_f16(v);
+        }
+        rs[r] = ldexpf(1.0f, shift);
+    }
+}
+
 /* a = SiLU(g) * u = g / (1 + exp(-g)) * u, f64, elementwise. */
 void orc_swiglu(const double* G, const double* U, size_t n, double* A) {
     for (size_t i = 0; i < n; i++) A[i] = G[i] / (1.0 + exp(-G[i])) * U[i];

@@ -340,6 +340,51 @@ def test_x_half_range_random(orc):
     assert np.all(np.abs(back - X) <= 2.0**-11 * np.abs(X) + 1e-300)
 
 
+def test_x_half_guard_closed_forms(orc):
+    """The fixed power-of-two guard (page cortiq-engine 0.8.3 qi21.rs, Guards / p2): x 2^-s to f16,
+    nearest-even, overflow to infinity, factor 2^s.  Values worked by hand for s = 4."""
+    K = 8
+    X = np.array([
+        [1.0, -3.0, 65504.0 * 16, 65520.0 * 16, 2.0**-20, 3.0 * 2.0**-21, 0.0, -0.0],
+        [1e30, -1e30, 3.0 * 2.0**-26, 2.0**-21, 0.5, 6.0, 7.0, 8.0],
+    ], np.float32)
+    xh, rs = orc.x_half_guard(X, K, 4)
+    assert list(rs) == [16.0, 16.0]
+    want0 = [0x2C00,   # 2^-4
+             0xB200,   # -0.1875 = -1.5 2^-3
+             0x7BFF,   # 65504, the largest f16
+             0x7C00,   # 65520 is halfway to 65536: nearest-even gives 2^16, infinity
+             0x0001,   # 2^-24, the smallest subnormal
+             0x0002,   # 1.5 2^-24: a tie, to the even subnormal 2
+             0x0000, 0x8000]
+    want1 = [0x7C00, 0xFC00,
+             0x0000,   # 3 2^-30 < 2^-25: rounds to zero
+             0x0000,   # 2^-25, halfway to the smallest subnormal: a tie to even zero
+             0x2800,   # 2^-5
+             0x3600,   # 0.375 = 1.5 2^-2
+             0x3700,   # 0.4375 = 1.75 2^-2
+             0x3800]   # 0.5
+    assert list(xh[0]) == want0 and list(xh[1]) == want1
+    # shift 0 is the plain conversion; the gather reads zeros outside [0, x_rows)
+    xh0, rs0 = orc.x_half_guard(X[:, 4:], 4, 0)
+    assert xh0[1, 0] == 0x3800 and list(rs0) == [1.0, 1.0]
+    xg, rg = orc.x_half_guard(X, K, 4, src=np.array([1, -1, 2, 0]), x_rows=2)
+    assert np.array_equal(xg[0], xh[1]) and np.array_equal(xg[3], xh[0])
+    assert not xg[1].any() and not xg[2].any() and list(rg) == [16.0] * 4
+
+
+def test_x_half_guard_matches_row_scaling(orc):
+    """When a row's own power-of-two scale is 2^-s (amax in [2^(13+s), 2^(14+s))), the guard and the
+    per-row scaling store the same f16 values and the same factor."""
+    rng = np.random.default_rng(5)
+    for s in (0, 3, 9, 14):
+        X = rng.uniform(-1, 1, (6, 64)).astype(np.float32) * np.float32(2.0 ** (13 + s))
+        X[:, 0] = np.float32(1.5 * 2.0 ** (13 + s))
+        xg, rg = orc.x_half_guard(X, 64, s)
+        xr, rr = orc.x_half(X, 64)
+        assert np.array_equal(xg, xr) and np.array_equal(rg, rr), s
+
+
 def test_swiglu_closed_forms(orc):
     g = np.array([0.0, math.log(3.0), -50.0, 2.0])
     u = np.array([5.0, 2.0, 3.0, 1.0])
