@@ -34,7 +34,7 @@ SYMBOLS = [
     "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_q8a", "qgemm_batch",
     "qgemv_q4", "qgemv_q4a", "qgemv_q8", "qgemv_q8a",
     "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a", "qg_conv_stats", "qg_conv2d",
-    "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
+    "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qg_x_half_guard", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn", "qg_moe_ffn_noalloc",
 ]
 
@@ -80,6 +80,7 @@ def lib() -> C.CDLL:
         L.qgemm_batch.argtypes = [_i, _i, _p, _i, _p, _i, _i, _i, _i, _p]
         L.qg_moe_plan.argtypes = [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
         L.qg_x_half.argtypes = [_p, _i, _p, _i, _i, _p, _p, _p]
+        L.qg_x_half_guard.argtypes = [_p, _i, _p, _i, _i, _i, _p, _p, _p]
         L.qgemm_moe_grouped.argtypes = [_i, _p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]
         L.qg_swiglu.argtypes = [_p, _i, _i, _p, _i, _p, _p]
         L.qg_moe_combine.argtypes = [_p, _i, _p, _p, _p, _i, _i, _i, _i, _p]
@@ -294,6 +295,11 @@ def qg_moe_plan(logits, T, E, k, seg_off, row_src, slot_row, slot_w, slot_expert
 
 def qg_x_half(X, x_rows, row_src, R, K, Xh, rs, stream=None):
     _check(lib().qg_x_half(_ptr(X), x_rows, _ptr(row_src), R, K, _ptr(Xh), _ptr(rs), _stream(stream)), "qg_x_half")
+
+
+def qg_x_half_guard(X, x_rows, row_src, R, K, shift, Xh, rs=None, stream=None):
+    _check(lib().qg_x_half_guard(_ptr(X), x_rows, _ptr(row_src), R, K, int(shift), _ptr(Xh), _ptr(rs), _stream(stream)),
+           "qg_x_half_guard")
 
 
 def qgemm_moe_grouped(fmt, experts, group, seg_off, row_src, x_rows, X, rs, Y, N, K, R, E, mode="exact", xt=None,

@@ -341,7 +341,18 @@ qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, i
     if (!X || !Xh || !rs) return QG_EINVAL;
     if (!aligned(X, 16) || !aligned(Xh, 16) || !aligned(rs, 4) || (row_src && !aligned(row_src, 4)))
         return QG_EALIGN;
-    return launched(qg::launch_x_half(X, x_rows, row_src, R, K, Xh, rs, stream));
+    return launched(qg::launch_x_half(X, x_rows, row_src, R, K, -1, Xh, rs, stream));
+}
+
+qg_status qg_x_half_guard(const float* X, int x_rows, const int32_t* row_src, int R, int K, int shift, uint16_t* Xh,
+                          float* rs, hipStream_t stream) {
+    if (shift < 0 || shift > 14) return QG_EINVAL;
+    if (R < 0 || R > kMaxT || K < 8 || K > kMaxK || (K % 8) != 0 || x_rows < 0) return QG_ESHAPE;
+    if (R == 0) return QG_OK;
+    if (!X || !Xh) return QG_EINVAL;
+    if (!aligned(X, 16) || !aligned(Xh, 16) || (rs && !aligned(rs, 4)) || (row_src && !aligned(row_src, 4)))
+        return QG_EALIGN;
+    return launched(qg::launch_x_half(X, x_rows, row_src, R, K, shift, Xh, rs, stream));
 }
 
 qg_status qgemm_moe_grouped(qg_format fmt, const qg_expert* experts, int group, const int32_t* seg_off,

@@ -83,8 +83,8 @@ hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmPa
 hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
                                int N, int K, int n0, int k0, int rows, int cols, int staged, void* out,
                                hipStream_t s);
-hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh, float* rs,
-                         hipStream_t s);
+hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, int guard, uint16_t* Xh,
+                         float* rs, hipStream_t s);
 hipError_t launch_swiglu(const float* GU, int R, int I, void* A, int at, float* rs, hipStream_t s);
 hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off, int32_t* row_src,
                            int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, int err_code,

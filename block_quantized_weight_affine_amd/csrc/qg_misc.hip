@@ -103,22 +103,28 @@ __device__ __forceinline__ float block_max256(float m, float* red) {
 
 
 // ---- x_half: gathered per-row scaling to f16 -----------------------------------------------------
+// guard < 0: the row's own power-of-two scale (page "oxinfer 0.0.5 src/metal.rs", row_scale /
+// x_half); guard = s >= 0: the fixed scale 2^-s of a guarded half site (page "cortiq-engine 0.8.3
+// src/gpu_metal/qi21.rs", Guards), with no pass over the row for its maximum.
 __global__ __launch_bounds__(256) void x_half_kernel(const float* X, int x_rows, const int32_t* row_src, int K,
-                                                      uint16_t* Xh, float* rs) {
+                                                      int guard, uint16_t* Xh, float* rs) {
     __shared__ float red[4];
     const int r = blockIdx.x;
     int s = row_src ? row_src[r] : r;
     const bool valid = s >= 0 && s < x_rows;
     const float4* row = (const float4*)(X + (size_t)(valid ? s : 0) * K);
     const int n4 = K >> 2;
-    float m = 0.f;
-    if (valid)
-        for (int i = threadIdx.x; i < n4; i += 256) {
-            const float4 v = row[i];
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
-    m = block_max256(m, red);
-    const int e = row_scale_exp(m);
+    int e = -guard;
+    if (guard < 0) {  // uniform over the workgroup
+        float m = 0.f;
+        if (valid)
+            for (int i = threadIdx.x; i < n4; i += 256) {
+                const float4 v = row[i];
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+        m = block_max256(m, red);
+        e = row_scale_exp(m);
+    }
     const float sc = ldexpf(1.0f, e);
     uint2* out = (uint2*)(Xh + (size_t)r * K);
     for (int i = threadIdx.x; i < n4; i += 256) {
@@ -131,12 +137,12 @@ __global__ __launch_bounds__(256) void x_half_kernel(const float* X, int x_rows,
                            ((uint32_t)f32_to_f16_bits(keep_f32(v.w * sc)) << 16);
         out[i] = make_uint2(a, b);
     }
-    if (threadIdx.x == 0) rs[r] = ldexpf(1.0f, -e);
+    if (threadIdx.x == 0 && rs) rs[r] = ldexpf(1.0f, -e);
 }
 
-hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh, float* rs,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(x_half_kernel, dim3(R), dim3(256), 0, s, X, x_rows, row_src, K, Xh, rs);
+hipError_t launch_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, int guard, uint16_t* Xh,
+                         float* rs, hipStream_t s) {
+    hipLaunchKernelGGL(x_half_kernel, dim3(R), dim3(256), 0, s, X, x_rows, row_src, K, guard, Xh, rs);
     return hipGetLastError();
 }
 

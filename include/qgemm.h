@@ -300,6 +300,16 @@ qg_status qg_moe_plan(const float* logits, int T, int E, int k, int32_t* seg_off
 qg_status qg_x_half(const float* X, int x_rows, const int32_t* row_src, int R, int K, uint16_t* Xh,
                     float* rs, hipStream_t stream);
 
+/* Power-of-two range guard of a half site (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs",
+ * Guards and p2: the site stores x 2^-s, the matmul reading it multiplies by 2^s): as qg_x_half
+ * with the fixed scale 2^-shift for every row, Xh[r][:] = f16(X[s][:] * 2^-shift) (nearest-even;
+ * magnitudes past the f16 range become infinities), rs[r] = 2^shift when rs is not NULL.  Passing
+ * rs to qgemm_moe_grouped with Xh as its f16 X undoes the guard in the matmul's epilogue.
+ * 0 <= shift <= 14 (the pages' range), else QG_EINVAL; shapes and alignment as qg_x_half.
+ * Asynchronous; nothing is allocated. */
+qg_status qg_x_half_guard(const float* X, int x_rows, const int32_t* row_src, int R, int K, int shift,
+                          uint16_t* Xh, float* rs, hipStream_t stream);
+
 /* Ragged grouped matmul over experts: for every expert e < E and every gathered row r in
  * [seg_off[e], seg_off[e+1]), Y[r][n] = (rs ? rs[r] : 1) * sum_k x_r[k] * w_e(n, k), n < N, where
  * x_r = X[row_src[r]] if row_src is given (row ids outside [0, x_rows) read as zeros) else X[r].

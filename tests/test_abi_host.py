@@ -105,6 +105,12 @@ def test_dump_and_moe_validation_codes():
     assert L.qg_moe_combine(A16, 8, A16b, A16c, A16d, 6, 2, 2, 0, None) == qg.QG_ESHAPE
     assert L.qg_moe_combine(A16, 8, A16b, A16c, A16d + 8, 8, 2, 2, 0, None) == qg.QG_EALIGN
     assert L.qg_x_half(A16, 4, None, 4, 12, A16b, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_x_half_guard(A16, 4, None, 4, 16, 15, A16b, A16c, None) == qg.QG_EINVAL
+    assert L.qg_x_half_guard(A16, 4, None, 4, 16, -1, A16b, A16c, None) == qg.QG_EINVAL
+    assert L.qg_x_half_guard(A16, 4, None, 4, 12, 4, A16b, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_x_half_guard(A16, 4, None, 4, 16, 4, A16b + 8, None, None) == qg.QG_EALIGN
+    assert L.qg_x_half_guard(None, 4, None, 4, 16, 4, A16b, None, None) == qg.QG_EINVAL
+    assert L.qg_x_half_guard(None, 4, None, 0, 16, 4, None, None, None) == qg.QG_OK
     ws = qg.qg_moe_ffn_workspace(2048, 1536, 32, 8, "fast")
     assert ws >= 256 * (3072 * 4 + 2048 * 4 + 2048 * 2 + 1536 * 2)
     assert L.qg_moe_ffn(0, A16, A16b, 64, 128, 2048, 1536, A16c, 32, 8, A16d, A16d, A16d, A16d, A16d, 0, 1,
