@@ -70,6 +70,10 @@ def lib():
         L.orc_x_half.restype = None
         L.orc_x_half.argtypes = [_p, _i, _p, _i, _p, _p]
         L.orc_x_half_guard.restype = None
+        L.orc_q8f_fields.restype = None
+        L.orc_q8f_fields.argtypes = [_p, _i, _i, _i, _p, _p]
+        L.orc_q8f_gemm.restype = None
+        L.orc_q8f_gemm.argtypes = [_p, _i, _i, _i, _p, _i, _i, _p, _p]
         L.orc_x_half_guard.argtypes = [_p, _i, _i, _p, _i, _i, _p, _p]
         L.orc_swiglu.restype = None
         L.orc_swiglu.argtypes = [_p, _p, _sz, _p]
@@ -200,6 +204,29 @@ def x_half(X, K, src=None, R=None):
     rs = np.empty(R, np.float32)
     lib().orc_x_half(_ptr(x), K, _ptr(srca), R, _ptr(xh), _ptr(rs))
     return xh, rs
+
+
+def q8f_fields(blob, N, K, has_col):
+    """(rs f64 [N], col f64 [K]) of a q8_2f (has_col) or q8_row tensor blob (int8 codes [N][K], then
+    the f16 row scales, then the f16 column field)."""
+    b = _c(blob, np.uint8)
+    rs = np.empty(N, np.float64)
+    col = np.empty(K, np.float64)
+    lib().orc_q8f_fields(_ptr(b), int(bool(has_col)), N, K, _ptr(rs), _ptr(col))
+    return rs, col
+
+
+def q8f_gemm(blob, N, K, has_col, X, xtype, T):
+    """(Y, S) f64 [T, N] of the q8_2f / q8_row matmul: w = q col[k] rs[n]."""
+    b = _c(blob, np.uint8)
+    xdt = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64}[xtype]
+    if xtype == "f16" and np.asarray(X).dtype == np.float16:
+        X = np.asarray(X).view(np.uint16)
+    x = _c(X, xdt)
+    Y = np.empty((T, N), np.float64)
+    S = np.empty((T, N), np.float64)
+    lib().orc_q8f_gemm(_ptr(b), int(bool(has_col)), N, K, _ptr(x), XT[xtype], T, _ptr(Y), _ptr(S))
+    return Y, S
 
 
 def x_half_guard(X, K, shift, src=None, R=None, x_rows=None):

@@ -289,6 +289,46 @@ void orc_x_half(const float* X, int K, const int* src, int R, uint16_t* xh, floa
 }
 
 /* ---------------------------------------------------------------------------------------
+ * q8_2f and q8_row (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs", the block loader's codec
+ * match: a q8_2f tensor of N rows and K columns is N*K int8 codes, row-major, then N f16 row
+ * scales, then K f16 column-field values; a q8_row tensor stops after the row scales and its
+ * column field is 1.  Page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", q8mm: the column field
+ * multiplies X, the row scale the result.)  The weight is w[n][k] = q[n][k] col[k] rs[n], exact in
+ * f64 (30 significant bits at most).  The 16-bit fields are read byte by byte, little-endian.
+ */
+static uint16_t orc_le16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+void orc_q8f_fields(const void* blob, int has_col, int N, int K, double* rs, double* col) {
+    const uint8_t* b = (const uint8_t*)blob;
+    for (int n = 0; n < N; n++) rs[n] = orc_f16_value(orc_le16(b + (size_t)N * K + 2 * (size_t)n));
+    for (int k = 0; k < K; k++)
+        col[k] = has_col ? orc_f16_value(orc_le16(b + (size_t)N * K + 2 * (size_t)N + 2 * (size_t)k)) : 1.0;
+}
+
+/* Y[t][n] = sum_k x[t][k] w[n][k] and S[t][n] = sum_k |x[t][k] w[n][k]|, f64, ascending k. */
+void orc_q8f_gemm(const void* blob, int has_col, int N, int K, const void* X, int xtype, int T, double* Y,
+                  double* S) {
+    const int8_t* q = (const int8_t*)blob;
+    double* rs = (double*)malloc(sizeof(double) * (size_t)N);
+    double* col = (double*)malloc(sizeof(double) * (size_t)K);
+    orc_q8f_fields(blob, has_col, N, K, rs, col);
+    for (int t = 0; t < T; t++)
+        for (int n = 0; n < N; n++) {
+            double y = 0.0, a = 0.0;
+            for (int k = 0; k < K; k++) {
+                const double w = (double)q[(size_t)n * K + k] * col[k] * rs[n];
+                const double p = orc_x_value(X, xtype, (size_t)t * K + k) * w;
+                y += p;
+                a += fabs(p);
+            }
+            Y[(size_t)t * N + n] = y;
+            S[(size_t)t * N + n] = a;
+        }
+    free(rs);
+    free(col);
+}
+
+/* ---------------------------------------------------------------------------------------
  * Power-of-two range guard (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs", Guards and p2):
  * a half site stores x * 2^-s for a fixed shift s of the site, 0 <= s <= 14, and the matmul
  * that reads it multiplies its result by 2^s.  Row r of the output is source row src[r] (or r);

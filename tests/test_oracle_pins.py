@@ -12,6 +12,8 @@ import numpy as np
 import pytest
 import torch
 
+import synth
+
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -340,6 +342,55 @@ def test_x_half_range_random(orc):
     assert np.all(np.abs(back - X) <= 2.0**-11 * np.abs(X) + 1e-300)
 
 
+# ---- q8_2f / q8_row -----------------------------------------------------------------------------------
+
+def _q8f_blob(codes, rs_bits, col_bits=None):
+    parts = [np.asarray(codes, np.int8).view(np.uint8).ravel(), np.asarray(rs_bits, "<u2").view(np.uint8)]
+    if col_bits is not None:
+        parts.append(np.asarray(col_bits, "<u2").view(np.uint8))
+    return np.concatenate(parts)
+
+
+def test_q8f_hand_worked(orc):
+    """A 2 x 4 q8_2f tensor worked by hand (page cortiq-engine 0.8.3 qi21.rs, the codec match: codes,
+    then f16 row scales, then the f16 column field): w = q col[k] rs[n]."""
+    codes = [[3, -2, 0, 127], [-128, 1, 5, -1]]
+    rs = [0x3800, 0xC000]                     # 0.5, -2
+    col = [0x3C00, 0x3400, 0x4200, 0x0001]    # 1, 0.25, 3, 2^-24
+    X = np.array([[2.0, 4.0, 1.0, 2.0**20]], np.float32)
+    blob = _q8f_blob(codes, rs, col)
+    r, c = orc.q8f_fields(blob, 2, 4, True)
+    assert list(r) == [0.5, -2.0] and list(c) == [1.0, 0.25, 3.0, 2.0**-24]
+    Y, S = orc.q8f_gemm(blob, 2, 4, True, X, "f32", 1)
+    # row 0: 2*1.5 + 4*(-0.25) + 0 + 2^20 * 127 * 2^-25;  row 1: 2*256 + 4*(-0.5) + 1*(-30) + 2^20 * 2^-23
+    assert list(Y[0]) == [5.96875, 480.125] and list(S[0]) == [7.96875, 544.125]
+    # q8_row: the same codes and row scales, no column field
+    Yr, Sr = orc.q8f_gemm(_q8f_blob(codes, rs), 2, 4, False, X, "f32", 1)
+    # row 0: w = 1.5, -1, 0, 63.5;  row 1: w = 256, -2, -10, 2
+    assert list(Yr[0]) == [2 * 1.5 - 4 * 1.0 + 2.0**20 * 63.5, 2 * 256.0 - 4 * 2.0 - 10.0 + 2.0**21]
+    assert list(Sr[0]) == [3 + 4 + 2.0**20 * 63.5, 512 + 8 + 10 + 2.0**21]
+
+
+def test_q8f_reduces_to_q8(orc):
+    """q8_row is Q8 with the row scale in every block (bit for bit, Y and S), and q8_2f is q8_row over
+    X times the column field (each product is the exact product rounded once in f64)."""
+    rng = np.random.default_rng(21)
+    N, K, T = 5, 96, 3
+    codes = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    rs = synth.f16_uniform(22, 1, N, -2.0, 2.0)
+    col = synth.f16_uniform(22, 2, K, 0.0, 4.0)
+    X = rng.normal(0, 1, (T, K)).astype(np.float32)
+    Yr, Sr = orc.q8f_gemm(_q8f_blob(codes, rs), N, K, False, X, "f32", T)
+    rsv, _ = orc.q8f_fields(_q8f_blob(codes, rs), N, K, False)
+    scales = np.repeat(rsv.astype(np.float32), K // 32)
+    Yq, Sq, _ = orc.gemm("q8", codes, scales, None, 64, N, K, X, "f32", T)
+    assert np.array_equal(Yr, Yq) and np.array_equal(Sr, Sq)
+    _, colv = orc.q8f_fields(_q8f_blob(codes, rs, col), N, K, True)
+    Yf, Sf = orc.q8f_gemm(_q8f_blob(codes, rs, col), N, K, True, X, "f32", T)
+    Yc, Sc = orc.q8f_gemm(_q8f_blob(codes, rs), N, K, False, X.astype(np.float64) * colv, "f64", T)
+    assert np.array_equal(Yf, Yc) and np.array_equal(Sf, Sc)
+
+
 def test_x_half_guard_closed_forms(orc):
     """The fixed power-of-two guard (page cortiq-engine 0.8.3 qi21.rs, Guards / p2): x 2^-s to f16,
     nearest-even, overflow to infinity, factor 2^s.  Values worked by hand for s = 4."""
@@ -479,7 +530,6 @@ def test_gguf_repack_matches_direct_decode(orc, gtype):
     nb = N * K // 32
     bb = orc.GGUF_BLOCK_BYTES[gtype]
     src = rng.integers(0, 256, nb * bb).astype(np.uint8).reshape(nb, bb)
-    import synth
     d = synth.f16_uniform(9, 1, nb, -0.05, 0.05)                # negative scales too
     src[:, 0], src[:, 1] = d & 0xFF, d >> 8
     src = src.reshape(-1)
