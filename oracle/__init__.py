@@ -73,6 +73,8 @@ def lib():
         L.orc_q8f_fields.restype = None
         L.orc_q8f_fields.argtypes = [_p, _i, _i, _i, _p, _p]
         L.orc_q8f_gemm.restype = None
+        L.orc_col_scale.restype = None
+        L.orc_col_scale.argtypes = [_p, _i, _i, _i, _p, _i, _p]
         L.orc_q8f_gemm.argtypes = [_p, _i, _i, _i, _p, _i, _i, _p, _p]
         L.orc_x_half_guard.argtypes = [_p, _i, _i, _p, _i, _i, _p, _p]
         L.orc_swiglu.restype = None
@@ -227,6 +229,19 @@ def q8f_gemm(blob, N, K, has_col, X, xtype, T):
     S = np.empty((T, N), np.float64)
     lib().orc_q8f_gemm(_ptr(b), int(bool(has_col)), N, K, _ptr(x), XT[xtype], T, _ptr(Y), _ptr(S))
     return Y, S
+
+
+def col_scale(X, xtype, T, K, col, out_type):
+    """X times the column field, the f32 product rounded to out_type ("f32" -> float32, "f16" /
+    "bf16" -> uint16 bits), [T, K]."""
+    xdt = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16}[xtype]
+    if xtype == "f16" and np.asarray(X).dtype == np.float16:
+        X = np.asarray(X).view(np.uint16)
+    x = _c(X, xdt)
+    c = _c(col, np.float32)
+    out = np.empty((T, K), np.float32 if out_type == "f32" else np.uint16)
+    lib().orc_col_scale(_ptr(x), XT[xtype], T, K, _ptr(c), XT[out_type], _ptr(out))
+    return out
 
 
 def x_half_guard(X, K, shift, src=None, R=None, x_rows=None):

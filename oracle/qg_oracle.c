@@ -328,6 +328,18 @@ void orc_q8f_gemm(const void* blob, int has_col, int N, int K, const void* X, in
     free(col);
 }
 
+/* The column field on X (page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", q8mm: applied to X
+ * as it is staged): out[t][k] = x[t][k] * col[k], the product in f32 (round to nearest), then for
+ * a 16-bit output type nearest-even narrowing; out is f32 or 16-bit bits by out_type. */
+void orc_col_scale(const void* X, int xtype, int T, int K, const float* col, int out_type, void* out) {
+    for (size_t i = 0; i < (size_t)T * K; i++) {
+        const float v = (float)orc_x_value(X, xtype, i) * col[i % (size_t)K];
+        if (out_type == ORC_F32) ((float*)out)[i] = v;
+        else if (out_type == ORC_F16) ((uint16_t*)out)[i] = orc_f32_to_f16(v);
+        else ((uint16_t*)out)[i] = orc_f32_to_bf16(v);
+    }
+}
+
 /* ---------------------------------------------------------------------------------------
  * Power-of-two range guard (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs", Guards and p2):
  * a half site stores x * 2^-s for a fixed shift s of the site, 0 <= s <= 14, and the matmul

@@ -391,6 +391,26 @@ def test_q8f_reduces_to_q8(orc):
     assert np.array_equal(Yf, Yc) and np.array_equal(Sf, Sc)
 
 
+def test_col_scale_closed_forms(orc):
+    """The column field on X: the f32 product (IEEE round to nearest), then nearest-even narrowing."""
+    X = np.array([[3.0, 1 + 2.0**-10, 1 + 2.0**-23, -2.0, 65504.0, 1e-8, 0.0, -0.0]], np.float32)
+    col = np.array([0.5, 1 + 2.0**-11, 1 + 2.0**-23, 0.25, 2.0, 1.0, 5.0, 5.0], np.float32)
+    f = orc.col_scale(X, "f32", 1, 8, col, "f32")[0]
+    # (1 + 2^-10)(1 + 2^-11) is exact in f32; (1 + 2^-23)^2 = 1 + 2^-22 + 2^-46 rounds to 1 + 2^-22
+    assert list(f) == [1.5, 1 + 2.0**-10 + 2.0**-11 + 2.0**-21, 1 + 2.0**-22, -0.5, 131008.0,
+                       float(np.float32(1e-8)), 0.0, 0.0]
+    assert np.signbit(f[7]) and not np.signbit(f[6])
+    h = orc.col_scale(X, "f32", 1, 8, col, "f16")[0]
+    # 1 + 1.5 2^-10 + 2^-21 is past the midpoint: up to 1 + 2^-9; 131008 overflows; 1e-8 < 2^-25
+    assert [int(v) for v in h] == [0x3E00, 0x3C02, 0x3C00, 0xB800, 0x7C00, 0x0000, 0x0000, 0x8000]
+    b = orc.col_scale(X, "f32", 1, 8, col, "bf16")[0]
+    # bf16 keeps 7 fraction bits: 131008 = 0x47FFE000 rounds up to 0x4800; 1e-8 = 0x322BCC77 to 0x322C
+    assert [int(v) for v in b] == [0x3FC0, 0x3F80, 0x3F80, 0xBF00, 0x4800, 0x322C, 0x0000, 0x8000]
+    # f16 input: the f16 value is exact in f32
+    xh = np.array([[0x3C01, 0xC000]], np.uint16)          # 1 + 2^-10, -2
+    assert list(orc.col_scale(xh, "f16", 1, 2, np.array([2.0, 0.5], np.float32), "f32")[0]) == [2 + 2.0**-9, -1.0]
+
+
 def test_x_half_guard_closed_forms(orc):
     """The fixed power-of-two guard (page cortiq-engine 0.8.3 qi21.rs, Guards / p2): x 2^-s to f16,
     nearest-even, overflow to infinity, factor 2^s.  Values worked by hand for s = 4."""
