@@ -33,7 +33,8 @@ SYMBOLS = [
     "qg_strerror", "qg_abi_version",
     "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_q8a", "qgemm_batch",
     "qgemv_q4", "qgemv_q4a", "qgemv_q8", "qgemv_q8a",
-    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a", "qg_conv_stats", "qg_conv2d",
+    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a", "qg_repack_q8f", "qg_col_scale", "qg_conv_stats",
+    "qg_conv2d",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qg_x_half_guard", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn", "qg_moe_ffn_noalloc",
 ]
@@ -72,6 +73,8 @@ def lib() -> C.CDLL:
         L.qgemm_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _p]
         L.qgemv_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _p]
         L.qg_repack_gguf_q8a.argtypes = [_i, _p, _i, _i, _p, _p, _p, _p]
+        L.qg_repack_q8f.argtypes = [_p, _i, _i, _i, _p, _p, _p]
+        L.qg_col_scale.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p]
         L.qg_conv_stats.argtypes = [_p, _i, _i, _i, C.c_float, _p, _p]
         L.qg_conv2d.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p]
         L.qg_dequant_dump.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]
@@ -244,6 +247,18 @@ def qg_repack_gguf_q8a(gtype, src, N, K, codes, scales, offsets, stream=None):
     _check(lib().qg_repack_gguf_q8a(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K,
                                     _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)),
            "qg_repack_gguf_q8a")
+
+
+def qg_repack_q8f(blob, N, K, has_col, scales, col=None, stream=None):
+    """q8_2f (has_col) / q8_row tensor blob (device uint8: int8 codes [N][K], f16 row scales, f16 column
+    field) -> f32 Q8 block scales [N*K/32] and the f32 column field [K]; the blob is the Q8 codes."""
+    _check(lib().qg_repack_q8f(_ptr(blob), N, K, int(bool(has_col)), _ptr(scales), _ptr(col), _stream(stream)),
+           "qg_repack_q8f")
+
+
+def qg_col_scale(X, T, K, col, Xs, stream=None):
+    """Xs = X * col[k] (types from the tensors' dtypes)."""
+    _check(lib().qg_col_scale(_ptr(X), _xt(X), T, K, _ptr(col), _ptr(Xs), _xt(Xs), _stream(stream)), "qg_col_scale")
 
 
 # ---- convolution ------------------------------------------------------------------------------------

@@ -276,6 +276,23 @@ qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, i
     return launched(qg::launch_repack_gguf_q8a(type, src, nblocks, codes, scales_f32, offsets_f32, stream));
 }
 
+qg_status qg_repack_q8f(const void* blob, int N, int K, int has_col, float* scales, float* col, hipStream_t stream) {
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0) return QG_ESHAPE;
+    if (!blob || !scales || (has_col && !col)) return QG_EINVAL;
+    if (!aligned(blob, 16) || !aligned(scales, 4) || (has_col && !aligned(col, 16))) return QG_EALIGN;
+    return launched(qg::launch_repack_q8f(blob, N, K, has_col != 0, scales, has_col ? col : nullptr, stream));
+}
+
+qg_status qg_col_scale(const void* X, qg_xtype xt, int T, int K, const float* col, void* Xs, qg_xtype st,
+                       hipStream_t stream) {
+    if (!xt_ok(xt) || !xt_ok(st)) return QG_EINVAL;
+    if (T < 0 || T > kMaxT || K < 8 || K > kMaxK || (K % 8) != 0) return QG_ESHAPE;
+    if (T == 0) return QG_OK;
+    if (!X || !col || !Xs) return QG_EINVAL;
+    if (!aligned(X, 16) || !aligned(col, 16) || !aligned(Xs, 16)) return QG_EALIGN;
+    return launched(qg::launch_col_scale(X, (int)xt, T, K, col, Xs, (int)st, stream));
+}
+
 qg_status qg_conv_stats(const float* X, int npix, int cin, int groups, float eps, float* stats, hipStream_t stream) {
     if (npix < 1 || npix > (1 << 26) || cin < 1 || cin > kMaxK || groups < 0 || groups > kMaxGridY ||
         (groups > 0 && (cin % groups) != 0) || (int64_t)npix * cin >= ((int64_t)1 << 31))

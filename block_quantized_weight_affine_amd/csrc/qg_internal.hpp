@@ -90,6 +90,8 @@ hipError_t launch_moe_plan(const float* logits, int T, int E, int k, int32_t* se
                            int32_t* slot_row, float* slot_w, int32_t* slot_expert, int32_t* status, int err_code,
                            hipStream_t s);
 hipError_t launch_repack_gguf(int q8, const void* src, size_t nblocks, void* codes, void* scales, hipStream_t s);
+hipError_t launch_repack_q8f(const void* blob, int N, int K, bool has_col, float* scales, float* col, hipStream_t s);
+hipError_t launch_col_scale(const void* X, int xt, int T, int K, const float* col, void* Xs, int st, hipStream_t s);
 hipError_t launch_repack_gguf_q8a(int type, const void* src, size_t nblocks, void* codes, float* scales,
                                   float* offs, hipStream_t s);
 // Device address of this GPU's copy of the fixed scratch array (qg_moe_ffn_noalloc), looked up once

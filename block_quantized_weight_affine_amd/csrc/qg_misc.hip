@@ -675,6 +675,88 @@ hipError_t launch_repack_gguf_q8a(int type, const void* src, size_t nblocks, voi
     return hipGetLastError();
 }
 
+// ---- q8_2f / q8_row: row scale into Q8 block scales; the column field applied to X ---------------
+// Page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs" (the block loader's codec match: int8 codes
+// [N][K], then f16 row scales [N], then, for q8_2f, the f16 column field [K]) and page
+// "cortiq-engine 0.8.41 src/gpu_metal/clover.rs" (q8mm: the column field multiplies X as it is
+// staged, the row scale multiplies the result).  The codes stay where they are (they already are the
+// Q8 code layout); block scale (n, b) becomes the f32 row scale of row n, so the Q8 kernels apply
+// it per block; the column field goes to f32 for qg_col_scale.
+__global__ __launch_bounds__(256) void repack_q8f_kernel(const uint16_t* rs, const uint16_t* col, int N, int nb,
+                                                         int K, float* scales, float* colf) {
+    const size_t total = (size_t)N * nb;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total + (col ? (size_t)K : 0);
+         i += (size_t)gridDim.x * 256) {
+        if (i < total) scales[i] = f16_to_f32(rs[i / nb]);
+        else colf[i - total] = f16_to_f32(col[i - total]);
+    }
+}
+
+hipError_t launch_repack_q8f(const void* blob, int N, int K, bool has_col, float* scales, float* col, hipStream_t s) {
+    const uint8_t* b = (const uint8_t*)blob;
+    const uint16_t* rs = (const uint16_t*)(b + (size_t)N * K);
+    const uint16_t* cf = has_col ? rs + N : nullptr;
+    const size_t total = (size_t)N * (K / 32) + (has_col ? K : 0);
+    const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65535);
+    hipLaunchKernelGGL(repack_q8f_kernel, dim3(grid), dim3(256), 0, s, rs, cf, N, K / 32, K, scales, col);
+    return hipGetLastError();
+}
+
+// Xs[t][k] = x[t][k] col[k]: the f32 product, then (f16 / bf16 output) nearest-even narrowing.
+// Eight values per thread and step (16-byte loads of f16 / bf16 X, two of f32).
+template <int XT, int ST>
+__global__ __launch_bounds__(256) void col_scale_kernel(const void* X, const float* col, int K, size_t n8,
+                                                        void* Xs) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+        const int k0 = (int)((i * 8) % (size_t)K);
+        float v[8];
+        if constexpr (XT == XT_F32) {
+            const float4 a = ((const float4*)X)[2 * i], b = ((const float4*)X)[2 * i + 1];
+            v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+        } else {
+            const uint4 q = ((const uint4*)X)[i];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint16_t h = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+                v[j] = XT == XT_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+            }
+        }
+        const float4 c0 = *(const float4*)(col + k0), c1 = *(const float4*)(col + k0 + 4);
+        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = keep_f32(v[j] * c[j]);
+        if constexpr (ST == XT_F32) {
+            ((float4*)Xs)[2 * i] = make_float4(v[0], v[1], v[2], v[3]);
+            ((float4*)Xs)[2 * i + 1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                o[j] = (uint32_t)f32_to_16<ST>(v[2 * j]) | ((uint32_t)f32_to_16<ST>(v[2 * j + 1]) << 16);
+            ((uint4*)Xs)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+template <int XT>
+static void col_scale_st(const void* X, const float* col, int K, size_t n8, void* Xs, int st, unsigned grid,
+                         hipStream_t s) {
+    if (st == XT_F32) hipLaunchKernelGGL((col_scale_kernel<XT, XT_F32>), dim3(grid), dim3(256), 0, s, X, col, K, n8, Xs);
+    else if (st == XT_F16)
+        hipLaunchKernelGGL((col_scale_kernel<XT, XT_F16>), dim3(grid), dim3(256), 0, s, X, col, K, n8, Xs);
+    else hipLaunchKernelGGL((col_scale_kernel<XT, XT_BF16>), dim3(grid), dim3(256), 0, s, X, col, K, n8, Xs);
+}
+
+hipError_t launch_col_scale(const void* X, int xt, int T, int K, const float* col, void* Xs, int st, hipStream_t s) {
+    const size_t n8 = (size_t)T * K / 8;
+    const unsigned grid = (unsigned)std::min<size_t>((n8 + 255) / 256, 8192);
+    if (xt == XT_F32) col_scale_st<XT_F32>(X, col, K, n8, Xs, st, grid, s);
+    else if (xt == XT_F16) col_scale_st<XT_F16>(X, col, K, n8, Xs, st, grid, s);
+    else col_scale_st<XT_BF16>(X, col, K, n8, Xs, st, grid, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_repack_gguf(int q8, const void* src, size_t nblocks, void* codes, void* scales, hipStream_t s) {
     const unsigned grid = (unsigned)std::min<size_t>((nblocks + 255) / 256, 65535);
     if (q8)

@@ -227,6 +227,27 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
 qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
                              float* scales_f32, float* offsets_f32, hipStream_t stream);
 
+/* q8_2f and q8_row tensors (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs", the block loader's
+ * codec match; page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", q8mm): blob is N*K int8 codes
+ * (row-major [N][K]), then N f16 row scales rs, then, for q8_2f (has_col != 0), K f16 column-field
+ * values col; q8_row has no column field (col = 1).  The weight is w[n][k] = q[n][k] col[k] rs[n].
+ * The codes are used in place: blob itself is the codes argument of the Q8 calls (qgemm_q8,
+ * qgemv_q8, qgemm_batch).  This call writes scales f32 [N][K/32], every block of row n holding
+ * f32(rs[n]) (exact), and for q8_2f col f32 [K] (exact); the column field is then applied to X by
+ * qg_col_scale.  The matmul of the pages is thus qg_col_scale (q8_2f only) followed by a Q8 call:
+ * QG_EXACT with f32 Xs (tau_exact), or, as the pages' half path (W exact in f16, the row scale on
+ * the f32 result), QG_FAST_WEXACT with f16 Xs.  K % 32 == 0, else QG_ESHAPE; blob 16-byte aligned
+ * (its codes feed the Q8 kernels), scales 4, col 16, else QG_EALIGN.  Asynchronous; nothing is
+ * allocated. */
+qg_status qg_repack_q8f(const void* blob, int N, int K, int has_col, float* scales, float* col,
+                        hipStream_t stream);
+
+/* The column field on X: Xs[t][k] = x[t][k] col[k], the f32 product, rounded to nearest-even when
+ * st is f16 or bf16 (X of any qg_xtype, col f32 [K], Xs [T][K] of type st).  K % 8 == 0, else
+ * QG_ESHAPE; X, col and Xs 16-byte aligned, else QG_EALIGN.  Asynchronous; nothing is allocated. */
+qg_status qg_col_scale(const void* X, qg_xtype xt, int T, int K, const float* col, void* Xs, qg_xtype st,
+                       hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Convolution as an implicit GEMM over the same quantized weights (page "oxinfer 0.0.5
  * src/metal.rs": SHADER_SRC conv_body / CONV / norm4, group_stats and row_stats, and

@@ -160,6 +160,24 @@ def test_repack_gguf_validation_codes():
     assert call(t=qg.QG_GGUF_Q8_0, scales=A16c + 2) == qg.QG_EALIGN
 
 
+def test_q8f_validation_codes():
+    """q8_2f / q8_row repack and the column-field step: sizes, pointers and alignment are checked
+    before any launch (no GPU needed for a rejected call)."""
+    L = qg.lib()
+    assert L.qg_repack_q8f(A16, 64, 48, 1, A16b, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_repack_q8f(A16, 0, 64, 1, A16b, A16c, None) == qg.QG_ESHAPE
+    assert L.qg_repack_q8f(None, 64, 64, 1, A16b, A16c, None) == qg.QG_EINVAL
+    assert L.qg_repack_q8f(A16, 64, 64, 1, A16b, None, None) == qg.QG_EINVAL
+    assert L.qg_repack_q8f(A16 + 8, 64, 64, 0, A16b, None, None) == qg.QG_EALIGN
+    assert L.qg_repack_q8f(A16, 64, 64, 1, A16b, A16c + 4, None) == qg.QG_EALIGN
+    assert L.qg_col_scale(A16, 0, 4, 12, A16b, A16c, 1, None) == qg.QG_ESHAPE
+    assert L.qg_col_scale(A16, 3, 4, 16, A16b, A16c, 1, None) == qg.QG_EINVAL
+    assert L.qg_col_scale(A16, 0, 4, 16, A16b, A16c, 5, None) == qg.QG_EINVAL
+    assert L.qg_col_scale(A16, 0, 4, 16, A16b + 4, A16c, 1, None) == qg.QG_EALIGN
+    assert L.qg_col_scale(A16, 0, 4, 16, None, A16c, 1, None) == qg.QG_EINVAL
+    assert L.qg_col_scale(None, 0, 0, 16, None, None, 1, None) == qg.QG_OK
+
+
 def test_q8a_validation_codes():
     """Q8A: offsets required and 4-byte aligned (f32), W-exact unsupported, no grouped or expert-block
     calls; the GGUF -> Q8A repack checks type, sizes, pointers and alignment."""
