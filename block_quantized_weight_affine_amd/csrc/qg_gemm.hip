@@ -354,11 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     constexpr int BT = 32 * MT * WM;
     constexpr int BN = 32 * MN * WN;
     constexpr int PITCH = 72;               // halves per weight-tile row: 64 + 8 (16-byte pad)
-    // 8-value fragments decoded per thread per stage; a 224-row tile is decoded as 256 rows (the last
-    // 32 are the next tile's, decoded into rows of the weight buffer the MFMAs never read): whole
-    // blocks per thread keep every block one 16-byte load
-    constexpr int FPT = BN == 224 ? 8 : BN / 32;
-    constexpr int BND = 32 * FPT;           // weight rows decoded per stage
+    constexpr int FPT = BN / 32;            // 8-value fragments decoded per thread per stage
     constexpr int FPB = FPT < 4 ? FPT : 4;  // fragments of one block a thread decodes
     constexpr int TPB = 4 / FPB;            // threads sharing one block
     constexpr int WB = FPT / FPB;           // blocks per thread per stage
@@ -368,8 +364,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     __shared__ __attribute__((aligned(16))) uint16_t xs1[BT * 64];
     // The last row's pad is never touched: leaving it out keeps two 32 x 256 grouped workgroups
     // (and their tile lookup slot) within one CU's 160 KiB.
-    __shared__ __attribute__((aligned(16))) uint16_t ws0[BND * PITCH - 8];
-    __shared__ __attribute__((aligned(16))) uint16_t ws1[BND * PITCH - 8];
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[BN * PITCH - 8];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[BN * PITCH - 8];
 
     // Grouped (MoE) launches: blockIdx.y enumerates the row tiles of every expert's segment
     // (find_tile); the tile's weights are its expert's.  X rows are rows r0 .. r1-1 of p.X either way.
@@ -527,7 +523,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     constexpr int CPS = FPT >= 4 ? FPT / 4 : 1;
     constexpr int NCH = 4 * CPS;
     constexpr int MPC = MT * MN / CPS;
-    constexpr int QPF = NCH / FPT;  // chunks per decoded fragment
     static_assert(MPC * CPS == MT * MN && (CPS == 1 || CPS == 2) && NCH % FPT == 0, "chunking");
 
     // Raw weights of stage t live in register set (t - 1) % NS and load NS stages ahead; with
@@ -580,8 +575,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
                 const int idx = part * MPC + m;
                 mfma(A[j & 1][idx / MN], B[j & 1][idx % MN], acc[idx / MN][idx % MN]);
             }
-            if (q % QPF == 0) {
-                const int f = q / QPF;  // fragment index of this thread: block f % WB, fragment f / WB
+            if (q % (NCH / FPT) == 0) {
+                const int f = q / (NCH / FPT);  // fragment index of this thread: block f % WB, fragment f / WB
                 const int i = f % WB, jj = fb + f / WB;
                 *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_fast<FMT, ST>(r[i], c0[i], jj);
             }
@@ -1270,15 +1265,7 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     // The largest tile that still gives about one workgroup per CU: big tiles amortize each
     // decoded weight over more tokens and each staged X row over more weight rows.
     auto wgs = [&](int bt, int bn) { return (long)((p.N + bn - 1) / bn) * ((p.R + bt - 1) / bt); };
-    if (wgs(256, 256) >= 200) {
-        // 256 x 224 tiles (4 wavefronts along the tokens, 7 fragment tiles along the weight rows)
-        // where they take fewer tile-rounds times tile area over the CUs: the 14336-row
-        // up-projection gets 256 workgroups for 256 CUs instead of 224
-        const long cus = device_cus();
-        const long r256 = (wgs(256, 256) + cus - 1) / cus * 256, r224 = (wgs(256, 224) + cus - 1) / cus * 224;
-        if (r224 < r256) return fast_lds_launch<FMT, ST, 4, 2, 7, 1>(p, s);
-        return fast_lds_launch<FMT, ST, 2, 4, 4, 1>(p, s);
-    }
+    if (wgs(256, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 4, 4, 1>(p, s);
     if (wgs(128, 256) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 4, 4>(p, s);
     if (wgs(128, 128) >= 200) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
     // Smaller shapes: 128 x 64 tiles with K split over the wavefronts (Q4 prefill N = K = 4096, T 512:

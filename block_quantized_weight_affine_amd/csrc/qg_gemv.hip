@@ -560,7 +560,7 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
 }
 
 // CU count of the current device (cached).
-int device_cus() {
+static int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

@@ -79,8 +79,6 @@ bool launch_gemv_batch(int fmt, int xt, const GemmParams& p, const BatchJobs& bj
 // X scaled to f16 per row in the kernel; otherwise f32 arithmetic.  grouped_rows_fits tells whether
 // the shape is taken.
 bool grouped_rows_fits(int fmt, int K, int N, int epi);
-// CU count of the current device (cached per device).
-int device_cus();
 hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmParams& p, hipStream_t s);
 hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
                                int N, int K, int n0, int k0, int rows, int cols, int staged, void* out,

@@ -118,8 +118,7 @@ def test_zero_weights_give_exact_zero(orc):
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
-@pytest.mark.parametrize("shape", [(200, 320, 40), (512, 1024, 300), (3500, 128, 4000)],
-                         ids=["small-tiles", "128x128-tiles", "256x224-tiles"])
+@pytest.mark.parametrize("shape", [(200, 320, 40), (512, 1024, 300)], ids=["small-tiles", "128x128-tiles"])
 def test_fast_blocks_needing_pages_order(orc, fmt, shape):
     """Fast mode through blocks whose one-FMA decode is not the pages' rounding: negative and zero
     scales, and (Q4A) offsets next to scales so large that m - 8d is inexact in f32; every third
@@ -145,14 +144,8 @@ def test_fast_blocks_needing_pages_order(orc, fmt, shape):
         w["offsets"] = off
     xt = "bf16" if fmt == "q4a" else "f16"
     Y, _ = _run(fmt, w, w["X"], xt, N, K, T, "fast")
-    if N * T > 2_000_000:  # sampled outputs at the large tile
-        ns, ts = sample_idx(N, 200, 5), sample_idx(T, 40, 6)
-        Yr, S = _ref(orc, fmt, w, w["X"], xt, N, K, T, ns=ns, ts=ts)
-        check_tol(Y[np.ix_(ts, ns)], Yr, S, TAU["fast"], f"fixup {fmt} {shape}")
-        assert np.all(np.isfinite(Y))
-    else:
-        Yr, S = _ref(orc, fmt, w, w["X"], xt, N, K, T)
-        check_tol(Y, Yr, S, TAU["fast"], f"fixup {fmt} {shape}")
+    Yr, S = _ref(orc, fmt, w, w["X"], xt, N, K, T)
+    check_tol(Y, Yr, S, TAU["fast"], f"fixup {fmt} {shape}")
 
 
 @pytest.mark.parametrize("T,K", [(2, 10240), (4, 5120), (4, 5248), (8, 2560), (3, 6912)])
@@ -207,17 +200,11 @@ def test_gemv_single_row_long_k(orc, K):
 
 # Shapes that reach each fast tile configuration (sampled outputs): 128 x 256 and 128 x 128 tiles
 # with the 4-deep register prefetch, and 64 x 128 tiles over a long K; the stage counts 15, 10 and
-# 33 leave 3, 2 and 1 stages after the 4-way unrolled loop.  Then the 256 x 224 tiles (224 tiles of
-# 256 x 256 would leave CUs idle where 256 of 256 x 224 fill them): ragged weight rows and tokens, a
-# K tail block (K % 64 == 32), an odd stage count, every format.
+# 33 leave 3, 2 and 1 stages after the 4-way unrolled loop.
 TILE_SHAPES = [
     ("q4", 6400, 928, 1024, "f16"),
     ("q4a", 3200, 640, 1000, "bf16"),
     ("q8", 4096, 2080, 512, "bf16"),
-    ("q4a", 3500, 256, 4000, "bf16"),
-    ("q4", 3584, 288, 4096, "f16"),
-    ("q8", 3584, 320, 4096, "f16"),
-    ("q8a", 3500, 256, 4000, "f16"),
 ]
 
 
