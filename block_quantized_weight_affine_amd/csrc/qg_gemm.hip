@@ -1017,6 +1017,9 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
     int cy[XCH], cx[XCH];  // CV: input position of tap (0, 0) for the chunk's output pixel
     int cq[XCH], cc[XCH];  // CV: input pixel and channel of the chunk loaded last (cq < 0: zeros)
     float cm[XCH], cr[XCH];  // CV, layer norm: (mean, rstd) of that input pixel
+    // CV: tap (ky, kx) and channel ci of the chunk's k in the stage load_x takes next; load_x runs
+    // for stages 0, 1, 2, ... in order, so they advance by 64 channels a call with no division
+    int tky[XCH], tkx[XCH], tci[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
         const int c = tid + i * kThreads;
@@ -1025,6 +1028,10 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
             const int oy = xrow[i] / cv.ow, ox = xrow[i] - oy * cv.ow;
             cy[i] = oy * cv.stride - cv.pad;
             cx[i] = ox * cv.stride - cv.pad;
+            const int k0 = 8 * (c & 7), tap = k0 / cv.cin;
+            tci[i] = k0 - tap * cv.cin;
+            tky[i] = tap / cv.ksz;
+            tkx[i] = tap - tky[i] * cv.ksz;
         }
     }
     // CV with normalisation and cin <= kConvLdsCin: the per-channel parameters once per workgroup
@@ -1055,14 +1062,23 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
             if constexpr (CV) {
                 cq[i] = -1;
                 if (xrow[i] >= 0 && k < K) {
-                    const int tap = k / cv.cin, ci = k - tap * cv.cin;
-                    const int ky = tap / cv.ksz, kx = tap - ky * cv.ksz;
-                    const int iy = cy[i] + ky, ix = cx[i] + kx;
+                    const int iy = cy[i] + tky[i], ix = cx[i] + tkx[i];
                     if ((unsigned)iy < (unsigned)cv.H && (unsigned)ix < (unsigned)cv.W) {
                         cq[i] = iy * cv.W + ix;
-                        cc[i] = ci;
+                        cc[i] = tci[i];
                     }
                 }
+                // the next stage: 64 channels on, past at most two taps (cin >= 32)
+                tci[i] += 64;
+#pragma unroll
+                for (int w = 0; w < 2; w++)
+                    if (tci[i] >= cv.cin) {
+                        tci[i] -= cv.cin;
+                        if (++tkx[i] == cv.ksz) {
+                            tkx[i] = 0;
+                            ++tky[i];
+                        }
+                    }
                 if (cq[i] >= 0 && cv.norm == 2) {
                     cm[i] = cv.stats[2 * cq[i]];
                     cr[i] = cv.stats[2 * cq[i] + 1];
