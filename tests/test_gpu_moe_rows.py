@@ -41,16 +41,16 @@ def _check_experts(orc, fmt, y, seg, ws, N, K, Xo, xt, tau, what):
 
 @pytest.mark.parametrize("fmt", ["q4", "q4a", "q8"])
 @pytest.mark.parametrize("path", ["exact_f32", "exact_f16", "exact_bf16", "fast_f16", "fast_bf16", "fast_f32"])
-@pytest.mark.parametrize("kcase", ["k320", "k96"])
+@pytest.mark.parametrize("kcase", ["k320", "k96", "k1024"])
 def test_rows_grouped_matches_oracle(orc, fmt, path, kcase):
     """Short segments (R = 31 <= 8 E): N = 198 (a ragged last batch of weight rows), K = 320 (16-byte
-    lane chunks, lanes past K idle) or a multiple of 96 (Q4 / Q4A: K 1152, 12-byte lane chunks over two
-    blocks, 48 lanes busy; Q8: K 768), rows gathered through row_src with two ids outside X (zero rows)
+    lane chunks, lanes past K idle), a multiple of 96 (Q4 / Q4A: K 1152, 12-byte lane chunks over two
+    blocks, 48 lanes busy; Q8: K 768) or 1024 (exact mode: the f32 matrix-core kernel), rows gathered through row_src with two ids outside X (zero rows)
     and one row scaled by 1e-4.  Exact paths at tau_exact against X as stored; fast f16 / bf16 against
     X as stored, fast f32 (rows scaled to f16 in the kernel) against the f32 rows, both at tau_fast."""
     mode, xt = path.split("_")
     N, x_rows = 198, 23
-    K = 320 if kcase == "k320" else 768 if fmt == "q8" else 1152
+    K = 320 if kcase == "k320" else 1024 if kcase == "k1024" else 768 if fmt == "q8" else 1152
     E, seg, R, ws, dw, table, row_src = _grouped_case(fmt, N, K, x_rows, 900 + len(path))
     row_src[[2, 17]] = [-1, x_rows]                      # outside X: zero rows
     X = synth.normal_as(61, synth.STREAM_X, x_rows * K, 0.0, 1.0, xt).reshape(x_rows, K)
