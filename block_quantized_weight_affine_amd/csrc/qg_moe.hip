@@ -34,7 +34,10 @@
 // Measured on the 128-expert top-8 block (32 tokens, H 2048, I 1536, Q4), whole block in exact / fast
 // mode: the K-split GEMV and the MFMA tile kernel it replaces 259 / 228 us; rows through registers
 // one batch ahead 234 / 205 us; the LDS ring 217 / 187 us (depth 4) and 214 / 186 (depth 3, kept),
-// 221 / 190 at depth 5; about 6 resident rounds of workgroups is best (3: 241 / 190, 10: 239 / 221).
+// 221 / 190 at depth 5.  Workgroups per expert: about 4 resident rounds (19 per expert on this block)
+// measured best, 207 / 181 us against 211 / 193 at 6 rounds, 220 / 187 at 3.5, 215 / 188 at 4.5 and
+// 217 / 193 at 5 (one box, one process each): more workgroups repeat the fused X scaling of every
+// segment row in more wavefronts.
 
 #include <algorithm>
 #include <type_traits>
@@ -629,7 +632,7 @@ bool grouped_rows_fits(int fmt, int K, int N, int epi) {
 
 hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmParams& p, hipStream_t s) {
     if (!grouped_rows_fits(fmt, p.K, p.N, epi)) return hipErrorInvalidValue;
-    // workgroups per expert: about six rounds of eight resident wavefronts per CU over the experts
+    // workgroups per expert: about four rounds of eight resident wavefronts per CU over the experts
     // that have rows
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -639,7 +642,7 @@ hipError_t launch_grouped_rows(int fmt, int xt, bool fast, int epi, const GemmPa
     const int used = std::max(1, std::min(p.E, p.R));
     const int units = epi == EPI_SWIGLU ? p.N / 2 : p.N;
     const int max_gx = std::max(1, (units + kRowsBatch - 1) / kRowsBatch / kRowsWaves);
-    const int gx = std::max(1, std::min(max_gx, (6 * cus * 8 / kRowsWaves + used - 1) / used));
+    const int gx = std::max(1, std::min(max_gx, (4 * cus * 8 / kRowsWaves + used - 1) / used));
     bool ok = false;
     if (fmt == FMT_Q4) ok = rows_pick<FMT_Q4>(xt, fast, epi, p, gx, s);
     else if (fmt == FMT_Q4A) ok = rows_pick<FMT_Q4A>(xt, fast, epi, p, gx, s);
