@@ -29,6 +29,11 @@
 //    (the wavefront's maximum over the row, a power of two putting it in [2^13, 2^14)), rounded to
 //    f16, and the inverse scale is applied to the outputs -- what x_half followed by the f16-X
 //    launch computes, without the f16 copy of X.
+//  * In fast mode (Q4 / Q8) each X row of a chunk is converted once per workgroup: wavefront t
+//    converts row t into LDS and, after one barrier, every wavefront reads all rows.  Per wavefront
+//    this cut the block from 180 to 157 us (the conversion had been repeated by every wavefront of
+//    every workgroup of the expert).  A wavefront with no rows of its own still takes part in the
+//    barriers.
 //  * SwiGLU epilogue (gate|up matrices of 2I rows): the wavefront takes gate row j and up row I + j
 //    together and stores a = g / (1 + exp(-g)) * u, so the 2I-wide intermediate is never written.
 // Measured on the 128-expert top-8 block (32 tokens, H 2048, I 1536, Q4), whole block in exact / fast
@@ -233,12 +238,25 @@ struct RowsArgs {
 // rows' block scales and (Q4A) offsets, 640 bytes each (two runs of at most 2 x 128 bytes, or one of
 // 4 x 128, each from a 16-byte boundary).
 constexpr int kRowsSBytes = 640;
-constexpr int kRowsWaveBytes = kRowsBatch * 1024 + 2 * kRowsSBytes;
-template <int I>
+template <int FMT>
+constexpr int rows_wave_bytes() { return kRowsBatch * 1024 + (FMT == FMT_Q4A ? 2 : 1) * kRowsSBytes; }
+template <int FMT, int I>
 __device__ __forceinline__ uint8_t* rows_slot() {
-    __shared__ __attribute__((aligned(16))) uint8_t b[kRowsWaves * kRowsWaveBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t b[kRowsWaves * rows_wave_bytes<FMT>()];
     return b;
 }
+// X rows of a segment chunk shared by the workgroup's wavefronts (fast mode, Q4 / Q8): row t, word w
+// of lane l at [(t * (XHW + 2) + w) * 64 + l]; words XHW and XHW + 1 hold the row's x sum of the
+// lane and its output scale.
+template <int XHW>
+__device__ __forceinline__ uint32_t* rows_xshare() {
+    __shared__ __attribute__((aligned(16))) uint32_t b[kRowsSeg * (XHW + 2) * 64];
+    return b;
+}
+// Fast-mode Q4 / Q8 chunks convert each X row once per workgroup (wavefront t converts row t into
+// LDS, then every wavefront reads all rows) instead of once per wavefront.
+template <int FMT, int AR, int CW>
+constexpr bool rows_share_x() { return AR == AR_DOT2 && FMT != FMT_Q4A && CW == 4; }
 
 // One segment chunk: NT X rows starting at gathered row c, against the wavefront's units.
 template <int FMT, int XT, int AR, bool XH, int EPI, int NT, int CW>
@@ -269,8 +287,8 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
     uint32_t xh[NT][XHW];
     float sx[NT], sxb[NT];  // x sums over the values of blocks A and B
     float osc[NT];  // output scale per X row: the fused x_half inverse scale times rs
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
+    auto conv_row = [&](int t, float (&xfo)[XF], uint32_t (&xho)[XHW], float& sxo, float& sxbo, float& osco)
+                        __attribute__((always_inline)) {
         int s = c + t;
         if (p.row_src) s = p.row_src[c + t];
         const bool valid = s >= 0 && s < p.x_rows;  // uniform over the wavefront
@@ -338,16 +356,16 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
             sc = ldexpf(1.0f, e);
             inv = ldexpf(1.0f, -e);
         }
-        osc[t] = inv * (p.rs ? p.rs[c + t] : 1.f);
-        sx[t] = sxb[t] = 0.f;
+        osco = inv * (p.rs ? p.rs[c + t] : 1.f);
+        sxo = sxbo = 0.f;
         // value i belongs to word (i % (4 CW)) / 4
         if constexpr (AR == AR_F32) {
 #pragma unroll
             for (int i = 0; i < V; i++) {
-                xf[t][i] = v[i];
+                xfo[i] = v[i];
                 if constexpr (FMT == FMT_Q4A) {
-                    if (in_a((i % (4 * CW)) >> 2)) sx[t] += v[i];
-                    else sxb[t] += v[i];
+                    if (in_a((i % (4 * CW)) >> 2)) sxo += v[i];
+                    else sxbo += v[i];
                 }
             }
         } else {
@@ -357,24 +375,53 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
                 // fused scaling: f32 product, then nearest-even narrowing (as x_half does); f16 X: an
                 // exact round trip
                 hv[i] = XH ? f32_to_f16_bits(keep_f32(v[i] * sc)) : f32_to_f16_bits(v[i]);
-                sx[t] += f16_to_f32(hv[i]);
+                sxo += f16_to_f32(hv[i]);
             }
             auto pk = [&](int i0, int i1) { return (uint32_t)hv[i0] | ((uint32_t)hv[i1] << 16); };
 #pragma unroll
             for (int j = 0; j < CW; j++) {
                 if constexpr (FMT == FMT_Q8) {
-                    xh[t][2 * j] = pk(4 * j, 4 * j + 2);
-                    xh[t][2 * j + 1] = pk(4 * j + 1, 4 * j + 3);
+                    xho[2 * j] = pk(4 * j, 4 * j + 2);
+                    xho[2 * j + 1] = pk(4 * j + 1, 4 * j + 3);
                 } else {
-                    xh[t][4 * j] = pk(4 * j, 4 * j + 2);
-                    xh[t][4 * j + 1] = pk(4 * j + 1, 4 * j + 3);
-                    xh[t][4 * j + 2] = pk(4 * CW + 4 * j, 4 * CW + 4 * j + 2);
-                    xh[t][4 * j + 3] = pk(4 * CW + 4 * j + 1, 4 * CW + 4 * j + 3);
+                    xho[4 * j] = pk(4 * j, 4 * j + 2);
+                    xho[4 * j + 1] = pk(4 * j + 1, 4 * j + 3);
+                    xho[4 * j + 2] = pk(4 * CW + 4 * j, 4 * CW + 4 * j + 2);
+                    xho[4 * j + 3] = pk(4 * CW + 4 * j + 1, 4 * CW + 4 * j + 3);
                 }
             }
         }
-        // one X row at a time: its raw values are dead before the next row's loads go out
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr bool SHARE = rows_share_x<FMT, AR, CW>();
+    if constexpr (SHARE) {
+        // wavefront t converts row t; one barrier; every wavefront reads every row
+        uint32_t* const xs = rows_xshare<XHW>();
+        if (a.wave < NT) {
+            float xfr[XF];
+            uint32_t xhr[XHW];
+            float sxr, sxbr, oscr;
+            conv_row(a.wave, xfr, xhr, sxr, sxbr, oscr);
+#pragma unroll
+            for (int i = 0; i < XHW; i++) xs[(a.wave * (XHW + 2) + i) * 64 + lane] = xhr[i];
+            xs[(a.wave * (XHW + 2) + XHW) * 64 + lane] = __float_as_uint(sxr);
+            xs[(a.wave * (XHW + 2) + XHW + 1) * 64 + lane] = __float_as_uint(oscr);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+#pragma unroll
+            for (int i = 0; i < XHW; i++) xh[t][i] = xs[(t * (XHW + 2) + i) * 64 + lane];
+            sx[t] = __uint_as_float(xs[(t * (XHW + 2) + XHW) * 64 + lane]);
+            osc[t] = __uint_as_float(xs[(t * (XHW + 2) + XHW + 1) * 64 + lane]);
+            sxb[t] = 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            conv_row(t, xf[t], xh[t], sx[t], sxb[t], osc[t]);
+            // one X row at a time: its raw values are dead before the next row's loads go out
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // Weight rows of the wavefront's batches, all copied by buffer_load ... lds into the wavefront's
@@ -397,7 +444,7 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
     const int os = blkA * ESZ, osb = blkB * ESZ;
     const int oo = FMT == FMT_Q4A ? ((blkA * 32) / p.group) * 2 : 0;
     const int oob = FMT == FMT_Q4A ? ((blkB * 32) / p.group) * 2 : 0;
-    const int wbase = a.wave * kRowsWaveBytes;
+    const int wbase = a.wave * rows_wave_bytes<FMT>();
     constexpr int SOFF = kRowsBatch * 1024, OOFF = SOFF + kRowsSBytes;  // scale / offset parts
     constexpr int RL = 8 * RB + 1;                                     // lanes per run
     static_assert(RU * RL * 16 <= kRowsSBytes && RB * 128 + 16 <= RL * 16, "scale part");
@@ -411,7 +458,7 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
         // the copies into the slot go out after the reads of its previous stage (a compiler
         // memory barrier: the compiler does not see that a copy writes every lane's bytes)
         asm volatile("" ::: "memory");
-        uint8_t* const dst = rows_slot<sl>() + wbase;
+        uint8_t* const dst = rows_slot<FMT, sl>() + wbase;
         const int sr = min(st, nstage - 1);
 #pragma unroll
         for (int i = 0; i < kRowsBatch; i++) {
@@ -449,9 +496,9 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         // a copy to LDS puts lane l's bytes at 16 l whatever its size (12-byte copies leave 4-byte gaps)
-        const uint8_t* const src = rows_slot<sl>() + wbase + 16 * cc;
-        const uint8_t* const ssrc = rows_slot<sl>() + wbase + SOFF;
-        const uint8_t* const osrc = rows_slot<sl>() + wbase + OOFF;
+        const uint8_t* const src = rows_slot<FMT, sl>() + wbase + 16 * cc;
+        const uint8_t* const ssrc = rows_slot<FMT, sl>() + wbase + SOFF;
+        const uint8_t* const osrc = rows_slot<FMT, sl>() + wbase + OOFF;
         int sbase[RU], obase[RU];  // a run's first row within the scale / offset part
 #pragma unroll
         for (int ru = 0; ru < RU; ru++) {
@@ -541,15 +588,19 @@ __device__ __forceinline__ void rows_chunk(const GemmParams& p, const RowsArgs& 
     // Ring: stages 0 .. D-2 in flight, then per stage s the copies of stage s + D - 1 (into the slot
     // stage s - 1 used, whose reads are done) go out before stage s is computed.
     auto prologue = [&](auto tc) __attribute__((always_inline)) { issue(tc, decltype(tc)::value); };
-    rows_run<0, D - 1>(prologue);
     auto stage = [&](auto uc, int st) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         issue(std::integral_constant<int, (u + D - 1) % D>{}, st + D - 1);
         compute(uc, st);
     };
-    int st = 0;
-    for (; st + D <= nstage; st += D) rows_run_from<0, D>(stage, st);
-    rows_run_tail<0, D>(stage, st, nstage);
+    if (a.u0 < a.u1) {  // uniform over the wavefront (an empty range only takes part in the X sharing)
+        rows_run<0, D - 1>(prologue);
+        int st = 0;
+        for (; st + D <= nstage; st += D) rows_run_from<0, D>(stage, st);
+        rows_run_tail<0, D>(stage, st, nstage);
+    }
+    // every wavefront has read the shared X rows before the next chunk writes them
+    if constexpr (SHARE) __syncthreads();
 }
 
 // Grid: (gx, E) workgroups of kRowsWaves wavefronts; the gx * kRowsWaves wavefronts of expert e split
@@ -568,7 +619,8 @@ __global__ __launch_bounds__(64 * kRowsWaves) void grouped_rows_kernel(GemmParam
     RowsArgs a;
     a.u0 = RB * (int)(((int64_t)nb * gw) / GW);
     a.u1 = min(units, RB * (int)(((int64_t)nb * (gw + 1)) / GW));
-    if (a.u0 >= a.u1) return;  // uniform over the wavefront
+    // uniform over the wavefront; with shared X rows it still takes part in every chunk's barriers
+    if (a.u0 >= a.u1 && !rows_share_x<FMT, AR, CW>()) return;
     a.lane = threadIdx.x & 63;
     a.wave = wave;
     const Expert ex = ((const Expert*)p.experts)[e];
