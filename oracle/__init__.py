@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT = {"q4": 0, "q4a": 1, "q8": 2, "q8a": 3}
+FMT = {"q4": 0, "q4a": 1, "q8": 2, "q8a": 3, "q8a16": 4}
 XT = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 
 _p = C.c_void_p
@@ -65,6 +65,8 @@ def lib():
         L.orc_gguf_repack.argtypes = [_i, _p, _i, _i, _p, _p]
         L.orc_gguf_repack_q8a.restype = None
         L.orc_gguf_repack_q8a.argtypes = [_i, _p, _i, _i, _p, _p, _p]
+        L.orc_gguf_repack_q8a16.restype = None
+        L.orc_gguf_repack_q8a16.argtypes = [_i, _p, _i, _i, _p, _p, _p]
         L.orc_gemm.restype = _i
         L.orc_gemm.argtypes = [_i, _p, _p, _p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _i, _p, _p, _i]
         L.orc_x_half.restype = None
@@ -116,7 +118,7 @@ def _c(a, dtype):
 def _weights(fmt, codes, scales, offsets):
     if fmt == "q8":
         return _c(codes, np.int8), _c(scales, np.float32), None
-    if fmt == "q8a":
+    if fmt in ("q8a", "q8a16"):
         return _c(codes, np.int8), _c(scales, np.float32), _c(offsets, np.float32)
     return _c(codes, np.uint8), _c(scales, np.uint16), (_c(offsets, np.uint16) if fmt == "q4a" else None)
 
@@ -334,9 +336,12 @@ def moe_ffn(m: dict, plan: dict, fmt: str = "q4", group: int = 64, threads=None)
 
 
 # ---- GGUF blocks with in-block scales (GGML type ids) -------------------------------------------
-GGUF = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12, "q5_k": 13}
+GGUF = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q4_k": 12, "q5_k": 13, "q6_k": 14, "q3_k": 11,
+        "q2_k": 10}
 # bytes per 32 elements (Q4_K: 144 per 256, Q5_K: 176 per 256)
 GGUF_BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24, "q8_0": 34, "q4_k": 18, "q5_k": 22}
+# bytes per 256-element super-block of the K-quants with a scale per 16 elements
+GGUF_SUPER_BYTES = {"q6_k": 210, "q3_k": 110, "q2_k": 84}
 
 
 def gguf_dequant(gtype, src, N, K) -> np.ndarray:
@@ -369,6 +374,17 @@ def gguf_repack_q8a(gtype, src, N, K) -> tuple:
     scales = np.empty(N * K // 32, np.float32)
     offs = np.empty(N * K // 32, np.float32)
     lib().orc_gguf_repack_q8a(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales), _ptr(offs))
+    return codes, scales, offs
+
+
+def gguf_repack_q8a16(gtype, src, N, K) -> tuple:
+    """(codes int8 [N*K], scales f32 [N*K/16], offsets f32 [N*K/16]) of the Q8A16 layout for the
+    K-quants with a scale per 16 elements (Q6_K, Q3_K, Q2_K)."""
+    b = _c(src, np.uint8)
+    codes = np.empty(N * K, np.int8)
+    scales = np.empty(N * K // 16, np.float32)
+    offs = np.empty(N * K // 16, np.float32)
+    lib().orc_gguf_repack_q8a16(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales), _ptr(offs))
     return codes, scales, offs
 
 

@@ -21,6 +21,8 @@
  *     offset m of the block at n*K/32 + floor(k/32); value = (float(q) * scale) + m in f32, two
  *     roundings as written (the GGUF sources make the product exact, so their single rounding
  *     at the add is the same).
+ *   - Q8A16 (the split layout Q6_K, Q3_K and Q2_K below are repacked into): Q8A with one scale
+ *     and one offset per 16-element block, entry n*K/16 + floor(k/16); the same two roundings.
  *   - Fast-mode staging, MMA_SHADER_SRC (mma_tile): the f32 value is converted to a 16-bit
  *     float as it is written to the tile (round to nearest, ties to even).
  *   - Row scaling to f16, MMA_SHADER_SRC (row_scale, x_half): per row, amax; frexp exponent
@@ -44,7 +46,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_Q4 = 0, ORC_Q4A = 1, ORC_Q8 = 2, ORC_Q8A = 3 };
+enum { ORC_Q4 = 0, ORC_Q4A = 1, ORC_Q8 = 2, ORC_Q8A = 3, ORC_Q8A16 = 4 };
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_F64 = 3 };
 
 /* ---------------------------------------------------------------------------------------
@@ -139,11 +141,11 @@ static int q4_nibble(const uint8_t* codes, int K, int n, int k) {
 double orc_weight_exact(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
                         int N, int K, int n, int k) {
     (void)N;
-    size_t bi = (size_t)n * (K / 32) + k / 32;
-    if (fmt == ORC_Q8 || fmt == ORC_Q8A) {
+    size_t bi = fmt == ORC_Q8A16 ? (size_t)n * (K / 16) + k / 16 : (size_t)n * (K / 32) + k / 32;
+    if (fmt == ORC_Q8 || fmt == ORC_Q8A || fmt == ORC_Q8A16) {
         int q = ((const int8_t*)codes)[(size_t)n * K + k];
         double v = (double)q * (double)((const float*)scales)[bi];
-        if (fmt == ORC_Q8A) v += (double)((const float*)(const void*)offs)[bi];
+        if (fmt != ORC_Q8) v += (double)((const float*)(const void*)offs)[bi];
         return v;
     }
     int nib = q4_nibble((const uint8_t*)codes, K, n, k);
@@ -156,12 +158,12 @@ double orc_weight_exact(int fmt, const void* codes, const void* scales, const ui
 float orc_weight_f32(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
                      int N, int K, int n, int k) {
     (void)N;
-    size_t bi = (size_t)n * (K / 32) + k / 32;
-    if (fmt == ORC_Q8 || fmt == ORC_Q8A) {
+    size_t bi = fmt == ORC_Q8A16 ? (size_t)n * (K / 16) + k / 16 : (size_t)n * (K / 32) + k / 32;
+    if (fmt == ORC_Q8 || fmt == ORC_Q8A || fmt == ORC_Q8A16) {
         int q = ((const int8_t*)codes)[(size_t)n * K + k];
         float d = ((const float*)scales)[bi];
         float v = (float)q * d;
-        if (fmt == ORC_Q8A) {
+        if (fmt != ORC_Q8) {
             float m = ((const float*)(const void*)offs)[bi];
             v = v + m;
         }
@@ -478,8 +480,23 @@ void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uin
  *         Q4_K, 32 bytes qh, 128 code bytes; sub-block j as Q4_K (code bytes 48 + 32 (j / 2) + e,
  *         the same scale / min unpacking) with a fifth bit: code = nibble | (bit j of qh[e]) << 4;
  *         value = code * d1 - m1.
+ * The K-quants with a scale per 16 elements (loaders Q6_KW, Q3_KW, Q2_KW): 256 elements per
+ * super-block; sub-block j = (k % 256) / 32 of it has half n = j / 4 and position jj = j % 4;
+ * element e = k % 32 of the sub-block has 16-element index s16 = 8 n + 2 jj + e / 16.
+ *   Q6_K (type 14): 210 bytes = 128 bytes ql, 64 bytes qh, 16 signed scale bytes sc, h d.
+ *         Low four bits: nibble (jj >= 2 ? high : low) of ql[64 n + 32 (jj % 2) + e]; high two
+ *         bits: bits 2 jj, 2 jj + 1 of qh[32 n + e]; q = low | high << 4 (0..63).
+ *         dl = d * sc[s16] (f32); value = (q - 32) * dl.
+ *   Q3_K (type 11): 110 bytes = 32 bytes hmask, 64 bytes qs, 12 scale bytes, h d.  q = bits
+ *         2 jj, 2 jj + 1 of qs[32 n + e]; it is lowered by 4 unless bit 4 n + jj of hmask[e] is
+ *         set.  The 6-bit scale of s16: low four bits = (s16 < 8 ? scales[s16] & 15 :
+ *         scales[s16 - 8] >> 4), high two bits = bits 2 (s16 / 4), +1 of scales[8 + s16 % 4];
+ *         dl = d * (that - 32) (f32); value = code * dl.
+ *   Q2_K (type 10): 84 bytes = 16 scale bytes s, 64 bytes qs, h d, h dmin.  q = bits 2 jj,
+ *         2 jj + 1 of qs[32 n + e]; dl = d * (s[s16] & 15), ml = dmin * (s[s16] >> 4) (f32);
+ *         value = q * dl - ml.
  * Every value is evaluated in f32 in the order written.  A row holds K / 32 blocks (K / 256
- * super-blocks for Q4_K).
+ * super-blocks for the K-quants).
  */
 #define ORC_GGUF_Q4_0 2
 #define ORC_GGUF_Q4_1 3
@@ -488,6 +505,9 @@ void orc_dequant_exact(int fmt, const void* codes, const void* scales, const uin
 #define ORC_GGUF_Q8_0 8
 #define ORC_GGUF_Q4_K 12
 #define ORC_GGUF_Q5_K 13
+#define ORC_GGUF_Q2_K 10
+#define ORC_GGUF_Q3_K 11
+#define ORC_GGUF_Q6_K 14
 
 /* Bytes of one row of K elements. */
 static size_t gguf_row_bytes(int type, int K) {
@@ -498,6 +518,9 @@ static size_t gguf_row_bytes(int type, int K) {
     case ORC_GGUF_Q5_1: return (size_t)(K / 32) * 24;
     case ORC_GGUF_Q8_0: return (size_t)(K / 32) * 34;
     case ORC_GGUF_Q5_K: return (size_t)(K / 256) * 176;
+    case ORC_GGUF_Q6_K: return (size_t)(K / 256) * 210;
+    case ORC_GGUF_Q3_K: return (size_t)(K / 256) * 110;
+    case ORC_GGUF_Q2_K: return (size_t)(K / 256) * 84;
     default: return (size_t)(K / 256) * 144;
     }
 }
@@ -520,6 +543,34 @@ static void gguf_k4_scale_min(int j, const uint8_t* s, int* sc, int* mn) {
 static void gguf_element(int type, const uint8_t* src, int K, int n, int k, int* code, float* d, float* m) {
     const uint8_t* row = src + (size_t)n * gguf_row_bytes(type, K);
     int j = k % 32;
+    if (type == ORC_GGUF_Q6_K || type == ORC_GGUF_Q3_K || type == ORC_GGUF_Q2_K) {
+        int sub = (k % 256) / 32, half = sub / 4, pos = sub % 4, s16 = 8 * half + 2 * pos + j / 16;
+        if (type == ORC_GGUF_Q6_K) {
+            const uint8_t* SB = row + (size_t)(k / 256) * 210;
+            uint8_t lb = SB[64 * half + 32 * (pos % 2) + j];
+            int low = pos >= 2 ? (lb >> 4) : (lb & 15);
+            int high = (SB[128 + 32 * half + j] >> (2 * pos)) & 3;
+            *code = (low | (high << 4)) - 32;
+            *d = gguf_h(SB + 208) * (float)(int8_t)SB[192 + s16];
+            *m = 0.0f;
+        } else if (type == ORC_GGUF_Q3_K) {
+            const uint8_t* SB = row + (size_t)(k / 256) * 110;
+            int q = (SB[32 + 32 * half + j] >> (2 * pos)) & 3;
+            if (!((SB[j] >> (4 * half + pos)) & 1)) q -= 4;
+            int lo = s16 < 8 ? (SB[96 + s16] & 15) : (SB[96 + s16 - 8] >> 4);
+            int hi = (SB[104 + s16 % 4] >> (2 * (s16 / 4))) & 3;
+            *code = q;
+            *d = gguf_h(SB + 108) * (float)((lo | (hi << 4)) - 32);
+            *m = 0.0f;
+        } else {
+            const uint8_t* SB = row + (size_t)(k / 256) * 84;
+            uint8_t sc = SB[s16];
+            *code = (SB[16 + 32 * half + j] >> (2 * pos)) & 3;
+            *d = gguf_h(SB + 80) * (float)(sc & 15);
+            *m = gguf_h(SB + 82) * (float)(sc >> 4);
+        }
+        return;
+    }
     if (type == ORC_GGUF_Q5_K) {
         const uint8_t* SB = row + (size_t)(k / 256) * 176;
         int sub = (k % 256) / 32, sc, mn;
@@ -588,9 +639,15 @@ float orc_gguf_weight_f32(int type, const uint8_t* src, int K, int n, int k) {
         return v;
     }
     case ORC_GGUF_Q4_K:
-    case ORC_GGUF_Q5_K: {
+    case ORC_GGUF_Q5_K:
+    case ORC_GGUF_Q2_K: {
         float p = (float)code * d;
         float v = p - m;
+        return v;
+    }
+    case ORC_GGUF_Q6_K:
+    case ORC_GGUF_Q3_K: {
+        float v = (float)code * d;
         return v;
     }
     default: { /* Q4_1, Q5_1 */
@@ -846,4 +903,20 @@ int orc_conv2d(int fmt, const void* codes, const void* scales, const uint16_t* o
     free(A);
     free(all);
     return used;
+}
+
+/* Q6_K, Q3_K, Q2_K -> the Q8A16 layout: int8 codes [N][K], f32 scales and f32 offsets [N][K/16],
+ * with fl(fl(code * scale) + offset) equal to the type's value: Q6_K and Q3_K (code, dl, -0)
+ * (adding -0 leaves every value, a zero's sign included, unchanged); Q2_K (code, dl, -ml). */
+void orc_gguf_repack_q8a16(int type, const uint8_t* src, int N, int K, int8_t* codes, float* scales, float* offs) {
+    for (int n = 0; n < N; n++)
+        for (int k = 0; k < K; k++) {
+            int code;
+            float d, m;
+            gguf_element(type, src, K, n, k, &code, &d, &m);
+            size_t bi = (size_t)n * (K / 16) + k / 16;
+            codes[(size_t)n * K + k] = (int8_t)code;
+            scales[bi] = d;
+            offs[bi] = -m;
+        }
 }

@@ -890,3 +890,102 @@ def test_conv_normalised_gather_closed_forms(orc):
     assert np.all(Ml >= np.abs(Al))
     A0, M0 = orc.conv_gather(X, H, W, cin, 3, 1)
     assert np.array_equal(M0, np.abs(A0))
+
+
+# ---- the K-quants with a scale per 16 elements (oxinfer src/metal.rs, GGUF_SHADER_SRC: the loaders
+# Q6_KW, Q3_KW, Q2_KW) and the Q8A16 layout they are repacked into ----------------------------------
+def _kquant_block(nbytes, sets):
+    b = np.zeros(nbytes, np.uint8)
+    for i, v in sets.items():
+        b[i] = v
+    return b
+
+
+def test_gguf_q6_k_hand_block(orc):
+    """Q6_K: ql, qh, 16 signed scales, f16 d at byte 208 (d = 0.5).  Element 0: low nibble of ql[0]
+    (10) with bits 0-1 of qh[0] (2) -> q 42, scale 0 (3): (42 - 32) * 1.5 = 15.  Element 71
+    (sub-block 2, 16-block 4): high nibble of ql[7] (12), bits 4-5 of qh[7] (3) -> q 60, scale 2:
+    28 * 1.0 = 28.  Element 245 (sub-block 7, 16-block 15): high nibble of ql[64 + 32 + 21] (3), bits
+    6-7 of qh[32 + 21] (1) -> q 19, scale -5: -13 * -2.5 = 32.5."""
+    src = _kquant_block(210, {0: 0x7A, 128: 0x02, 7: 0xC1, 135: 0x30, 117: 0x3F, 181: 0x40,
+                              192: 3, 196: 2, 207: 0xFB, 208: 0x00, 209: 0x38})
+    w = orc.gguf_dequant("q6_k", src, 1, 256)[0]
+    assert (w[0], w[71], w[245]) == (15.0, 28.0, 32.5)
+    # an all-zero code byte pattern gives q = 0: (0 - 32) * d * scale
+    assert w[1] == -32 * 1.5 and w[16] == 0.0       # element 16 is 16-block 1, scale 0
+
+
+def test_gguf_q3_k_hand_block(orc):
+    """Q3_K: hmask, qs, 12 scale bytes, f16 d at byte 108 (d = 2).  Element 0: bits 0-1 of qs[0]
+    (3), hmask[0] bit 0 clear -> code -1; 6-bit scale 0: low (scales[0] & 15) 5, high (bits 0-1 of
+    scales[8]) 2 -> 37 - 32 = 5: -1 * 10 = -10.  Element 100 (sub-block 3, 16-block 6): bits 6-7 of
+    qs[4] (1), hmask[4] bit 3 set -> code 1; scale: low (scales[6] & 15) 15, high (bits 2-3 of
+    scales[10]) 3 -> 63 - 32 = 31: 62.  Element 245 (16-block 15): bits 6-7 of qs[32 + 21] (2),
+    hmask[21] bit 7 set -> code 2; scale: low (scales[7] >> 4) 14, high (bits 6-7 of scales[11]) 0
+    -> -18: 2 * -36 = -72."""
+    src = _kquant_block(110, {32: 0x03, 96: 0x05, 104: 0x02, 36: 0x40, 4: 0x08, 102: 0x0F, 106: 0x0C,
+                              85: 0x80, 21: 0x80, 103: 0xE0, 108: 0x00, 109: 0x40})
+    w = orc.gguf_dequant("q3_k", src, 1, 256)[0]
+    assert (w[0], w[100], w[245]) == (-10.0, 62.0, -72.0)
+
+
+def test_gguf_q2_k_hand_block(orc):
+    """Q2_K: 16 scale bytes, qs, f16 d and dmin at bytes 80, 82 (d = 1, dmin = 0.5).  Element 0:
+    bits 0-1 of qs[0] (3), scale byte 0x27: 3 * 7 - 0.5 * 2 = 20.  Element 50 (sub-block 1,
+    16-block 3): bits 2-3 of qs[18] (2), scale byte 0x09: 2 * 9 - 0 = 18.  Element 245 (16-block
+    15): bits 6-7 of qs[32 + 21] (1), scale byte 0xF3: 1 * 3 - 0.5 * 15 = -4.5."""
+    src = _kquant_block(84, {16: 0x03, 0: 0x27, 34: 0x08, 3: 0x09, 69: 0x40, 15: 0xF3,
+                             80: 0x00, 81: 0x3C, 82: 0x00, 83: 0x38})
+    w = orc.gguf_dequant("q2_k", src, 1, 256)[0]
+    assert (w[0], w[50], w[245]) == (20.0, 18.0, -4.5)
+
+
+def _random_kquant(orc, gtype, N, K, seed):
+    rng = np.random.default_rng(seed)
+    nsb = N * K // 256
+    sbb = orc.GGUF_SUPER_BYTES[gtype]
+    src = rng.integers(0, 256, nsb * sbb).astype(np.uint8).reshape(nsb, sbb)
+    d = synth.f16_uniform(seed, 1, nsb, -0.05, 0.05)            # negative scales too
+    if gtype == "q2_k":
+        dm = synth.f16_uniform(seed, 2, nsb, -0.05, 0.05)
+        src[:, 80], src[:, 81], src[:, 82], src[:, 83] = d & 0xFF, d >> 8, dm & 0xFF, dm >> 8
+    else:
+        at = sbb - 2
+        src[:, at], src[:, at + 1] = d & 0xFF, d >> 8
+    return src.reshape(-1)
+
+
+@pytest.mark.parametrize("gtype", ["q6_k", "q3_k", "q2_k"])
+def test_gguf_q8a16_repack_matches_direct_decode(orc, gtype):
+    """The Q8A16 repack, decoded by the split-layout decoder, gives every element's value bit for bit
+    (zeros' signs included) -- the in-block loader and the split decoder are independent paths --
+    and the codes stay in the type's range."""
+    N, K = 3, 768
+    src = _random_kquant(orc, gtype, N, K, 21)
+    direct = orc.gguf_dequant(gtype, src, N, K)
+    codes, scales, offs = orc.gguf_repack_q8a16(gtype, src, N, K)
+    split = orc.dequant_tile("q8a16", codes, scales, offs, 32, N, K, 0, 0, N, K, "f32")
+    assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
+    assert np.any(direct.view(np.uint32) == 0x80000000) or gtype == "q2_k"
+    lo, hi = {"q6_k": (-32, 31), "q3_k": (-4, 3), "q2_k": (0, 3)}[gtype]
+    assert codes.min() >= lo and codes.max() <= hi
+
+
+def test_q8a16_reduces_to_q8a(orc):
+    """Q8A16 whose two 16-element halves of every 32-element block share one scale and offset is
+    the Q8A matrix with those blocks: the same Y and S, bit for bit."""
+    rng = np.random.default_rng(4)
+    N, K, T = 7, 96, 3
+    codes = rng.integers(-128, 128, N * K).astype(np.int8)
+    s32 = rng.uniform(-0.1, 0.1, N * K // 32).astype(np.float32)
+    o32 = rng.uniform(-1, 1, N * K // 32).astype(np.float32)
+    X = rng.standard_normal(T * K).astype(np.float32)
+    Ya, Sa, _ = orc.gemm("q8a", codes, s32, o32, 32, N, K, X, "f32", T)
+    Yb, Sb, _ = orc.gemm("q8a16", codes, np.repeat(s32, 2), np.repeat(o32, 2), 32, N, K, X, "f32", T)
+    assert np.array_equal(Ya, Yb) and np.array_equal(Sa, Sb)
+    # and a scale change in one half moves exactly that half's elements
+    s16 = np.repeat(s32, 2)
+    s16[1] *= 2
+    w = orc.dequant_tile("q8a16", codes, s16, np.repeat(o32, 2), 32, N, K, 0, 0, 1, 32, "f32")[0]
+    w0 = orc.dequant_tile("q8a", codes, s32, o32, 32, N, K, 0, 0, 1, 32, "f32")[0]
+    assert np.array_equal(w[:16], w0[:16]) and not np.array_equal(w[16:], w0[16:])
