@@ -23,17 +23,17 @@ QG_OK, QG_EINVAL, QG_EALIGN, QG_ESHAPE, QG_EUNSUPPORTED, QG_ELAUNCH, QG_EPLAN, Q
 QG_NOALLOC_SCRATCH_BYTES = 16 << 20
 QG_X_F32, QG_X_F16, QG_X_BF16 = 0, 1, 2
 QG_EXACT, QG_FAST, QG_FAST_WEXACT = 0, 1, 2
-QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8, QG_FMT_Q8A = 0, 1, 2, 3
+QG_FMT_Q4, QG_FMT_Q4A, QG_FMT_Q8, QG_FMT_Q8A, QG_FMT_Q8A16 = 0, 1, 2, 3, 4
 
-FMT = {"q4": QG_FMT_Q4, "q4a": QG_FMT_Q4A, "q8": QG_FMT_Q8, "q8a": QG_FMT_Q8A}
+FMT = {"q4": QG_FMT_Q4, "q4a": QG_FMT_Q4A, "q8": QG_FMT_Q8, "q8a": QG_FMT_Q8A, "q8a16": QG_FMT_Q8A16}
 MODE = {"exact": QG_EXACT, "fast": QG_FAST, "fast_wexact": QG_FAST_WEXACT}
 
 # exported symbols of include/qgemm.h, in declaration order
 SYMBOLS = [
     "qg_strerror", "qg_abi_version",
-    "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_q8a", "qgemm_batch",
-    "qgemv_q4", "qgemv_q4a", "qgemv_q8", "qgemv_q8a",
-    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a", "qg_repack_q8f", "qg_col_scale", "qg_conv_stats",
+    "qgemm_q4", "qgemm_q4a", "qgemm_q8", "qgemm_q8a", "qgemm_q8a16", "qgemm_batch",
+    "qgemv_q4", "qgemv_q4a", "qgemv_q8", "qgemv_q8a", "qgemv_q8a16",
+    "qg_dequant_dump", "qg_repack_gguf", "qg_repack_gguf_q8a", "qg_repack_gguf_q8a16", "qg_repack_q8f", "qg_col_scale", "qg_conv_stats",
     "qg_conv2d",
     "qg_moe_plan_host", "qg_moe_plan", "qg_x_half", "qg_x_half_guard", "qgemm_moe_grouped", "qg_swiglu", "qg_moe_combine",
     "qg_moe_ffn_workspace", "qg_moe_ffn", "qg_moe_ffn_noalloc",
@@ -73,6 +73,9 @@ def lib() -> C.CDLL:
         L.qgemm_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _p]
         L.qgemv_q8a.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _p]
         L.qg_repack_gguf_q8a.argtypes = [_i, _p, _i, _i, _p, _p, _p, _p]
+        L.qgemm_q8a16.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _p]
+        L.qgemv_q8a16.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _p]
+        L.qg_repack_gguf_q8a16.argtypes = [_i, _p, _i, _i, _p, _p, _p, _p]
         L.qg_repack_q8f.argtypes = [_p, _i, _i, _i, _p, _p, _p]
         L.qg_col_scale.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p]
         L.qg_conv_stats.argtypes = [_p, _i, _i, _i, C.c_float, _p, _p]
@@ -177,13 +180,25 @@ def qgemv_q8(codes, scales, X, Y, N, K, T, xt=None, stream=None):
                           _stream(stream)), "qgemv_q8")
 
 
+def qgemm_q8a16(codes, scales, offsets, X, Y, N, K, T, mode="exact", xt=None, stream=None):
+    _check(lib().qgemm_q8a16(_ptr(codes), _ptr(scales), _ptr(offsets), _ptr(X), _xt(X) if xt is None else xt,
+                             _ptr(Y), N, K, T, _mode(mode), _stream(stream)), "qgemm_q8a16")
+
+
+def qgemv_q8a16(codes, scales, offsets, X, Y, N, K, T, xt=None, stream=None):
+    _check(lib().qgemv_q8a16(_ptr(codes), _ptr(scales), _ptr(offsets), _ptr(X), _xt(X) if xt is None else xt,
+                             _ptr(Y), N, K, T, _stream(stream)), "qgemv_q8a16")
+
+
 def qgemv_q8a(codes, scales, offsets, X, Y, N, K, T, xt=None, stream=None):
     _check(lib().qgemv_q8a(_ptr(codes), _ptr(scales), _ptr(offsets), _ptr(X), _xt(X) if xt is None else xt,
                            _ptr(Y), N, K, T, _stream(stream)), "qgemv_q8a")
 
 
 def qgemm(fmt, codes, scales, offsets, group, X, Y, N, K, T, mode="exact", stream=None):
-    """Dispatch by format name: 'q4' | 'q4a' | 'q8' | 'q8a'."""
+    """Dispatch by format name: 'q4' | 'q4a' | 'q8' | 'q8a' | 'q8a16'."""
+    if fmt == "q8a16":
+        return qgemm_q8a16(codes, scales, offsets, X, Y, N, K, T, mode, stream=stream)
     if fmt == "q4":
         return qgemm_q4(codes, scales, X, Y, N, K, T, mode, stream=stream)
     if fmt == "q4a":
@@ -194,6 +209,8 @@ def qgemm(fmt, codes, scales, offsets, group, X, Y, N, K, T, mode="exact", strea
 
 
 def qgemv(fmt, codes, scales, offsets, group, X, Y, N, K, T, stream=None):
+    if fmt == "q8a16":
+        return qgemv_q8a16(codes, scales, offsets, X, Y, N, K, T, stream=stream)
     if fmt == "q4":
         return qgemv_q4(codes, scales, X, Y, N, K, T, stream=stream)
     if fmt == "q4a":
@@ -231,8 +248,10 @@ def qgemm_batch(fmt, group, jobs, X, K, T, mode="exact", xt=None, stream=None):
 
 
 QG_GGUF_Q4_0, QG_GGUF_Q4_1, QG_GGUF_Q5_0, QG_GGUF_Q5_1, QG_GGUF_Q8_0, QG_GGUF_Q4_K, QG_GGUF_Q5_K = 2, 3, 6, 7, 8, 12, 13
+QG_GGUF_Q2_K, QG_GGUF_Q3_K, QG_GGUF_Q6_K = 10, 11, 14
 GGUF = {"q4_0": QG_GGUF_Q4_0, "q4_1": QG_GGUF_Q4_1, "q5_0": QG_GGUF_Q5_0, "q5_1": QG_GGUF_Q5_1,
-        "q8_0": QG_GGUF_Q8_0, "q4_k": QG_GGUF_Q4_K, "q5_k": QG_GGUF_Q5_K}
+        "q8_0": QG_GGUF_Q8_0, "q4_k": QG_GGUF_Q4_K, "q5_k": QG_GGUF_Q5_K, "q2_k": QG_GGUF_Q2_K,
+        "q3_k": QG_GGUF_Q3_K, "q6_k": QG_GGUF_Q6_K}
 
 
 def qg_repack_gguf(gtype, src, N, K, codes, scales, stream=None):
@@ -380,3 +399,11 @@ def expert_table(experts, device="cuda"):
     rows = [[_ptr(c), _ptr(s), _ptr(o) if o is not None else 0] for (c, s, o) in experts]
     host = torch.tensor(np.array(rows, dtype=np.uint64).view(np.int64), dtype=torch.int64)
     return host.to(device)
+
+
+def qg_repack_gguf_q8a16(gtype, src, N, K, codes, scales, offsets, stream=None):
+    """GGUF Q6_K / Q3_K / Q2_K super-blocks (device uint8 tensor) -> Q8A16 codes (int8 [N*K]), f32 scales
+    and f32 offsets ([N*K/16]), all device tensors."""
+    _check(lib().qg_repack_gguf_q8a16(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K,
+                                      _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)),
+           "qg_repack_gguf_q8a16")

@@ -19,15 +19,17 @@ constexpr int kMaxT = 1 << 21;
 constexpr int kMaxGridY = 65535;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-bool fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8 || f == QG_FMT_Q8A; }
+bool fmt_ok(int f) {
+    return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8 || f == QG_FMT_Q8A || f == QG_FMT_Q8A16;
+}
 // formats of the grouped (MoE) entry points
 bool grouped_fmt_ok(int f) { return f == QG_FMT_Q4 || f == QG_FMT_Q4A || f == QG_FMT_Q8; }
 // formats with per-block offsets, and the alignment of those offsets
-bool has_offs(int f) { return f == QG_FMT_Q4A || f == QG_FMT_Q8A; }
-size_t offs_bytes(int f) { return f == QG_FMT_Q8A ? 4 : 2; }
+bool has_offs(int f) { return f == QG_FMT_Q4A || f == QG_FMT_Q8A || f == QG_FMT_Q8A16; }
+size_t offs_bytes(int f) { return f == QG_FMT_Q4A ? 2 : 4; }
 bool xt_ok(int x) { return x == QG_X_F32 || x == QG_X_F16 || x == QG_X_BF16; }
 bool mode_ok(int m) { return m == QG_EXACT || m == QG_FAST || m == QG_FAST_WEXACT; }
-size_t scale_bytes(int fmt) { return fmt == QG_FMT_Q8 || fmt == QG_FMT_Q8A ? 4 : 2; }
+size_t scale_bytes(int fmt) { return fmt == QG_FMT_Q4 || fmt == QG_FMT_Q4A ? 2 : 4; }
 
 // Shared checks of the dense matmul / GEMV entry points.
 qg_status check_dense(int fmt, const void* codes, const void* scales, const uint16_t* offs, int group,
@@ -71,7 +73,8 @@ qg_status run_dense(int fmt, const void* codes, const void* scales, const uint16
     GemmParams p = dense_params(codes, scales, offs, group, X, Y, N, K, T);
     if (mode == QG_FAST_WEXACT && ((fmt != QG_FMT_Q4 && fmt != QG_FMT_Q8) || xt != QG_X_F16)) return QG_EUNSUPPORTED;
     if (T <= 8) return launched(qg::launch_gemv(fmt, xt, p, false, s));
-    if (mode == QG_EXACT) return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
+    // 16-element blocks: the exact kernel in both modes (its result is well inside the fast tolerance)
+    if (mode == QG_EXACT || fmt == QG_FMT_Q8A16) return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
     if (mode == QG_FAST_WEXACT) return launched(qg::launch_gemm_fast_wexact(fmt, p, s));
     if (xt == QG_X_F32) return QG_EUNSUPPORTED;
     return launched(qg::launch_gemm_fast(fmt, xt, p, false, s));
@@ -121,6 +124,18 @@ qg_status qgemm_q8a(const int8_t* codes, const float* scales_f32, const float* o
                      mode, false, stream);
 }
 
+qg_status qgemm_q8a16(const int8_t* codes, const float* scales_f32, const float* offsets_f32, const void* X,
+                      qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode, hipStream_t stream) {
+    return run_dense(QG_FMT_Q8A16, codes, scales_f32, (const uint16_t*)(const void*)offsets_f32, 64, X, xt, Y, N, K,
+                     T, mode, false, stream);
+}
+
+qg_status qgemv_q8a16(const int8_t* codes, const float* scales_f32, const float* offsets_f32, const void* X,
+                      qg_xtype xt, float* Y, int N, int K, int T, hipStream_t stream) {
+    return run_dense(QG_FMT_Q8A16, codes, scales_f32, (const uint16_t*)(const void*)offsets_f32, 64, X, xt, Y, N, K,
+                     T, QG_EXACT, true, stream);
+}
+
 qg_status qgemv_q4(const uint8_t* codes, const uint16_t* scales_f16, const void* X, qg_xtype xt, float* Y, int N,
                    int K, int T, hipStream_t stream) {
     return run_dense(QG_FMT_Q4, codes, scales_f16, nullptr, 64, X, xt, Y, N, K, T, QG_EXACT, true, stream);
@@ -146,6 +161,7 @@ qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales, 
                           int group, int N, int K, int n0, int k0, int rows, int cols, qg_xtype staged, void* out,
                           hipStream_t stream) {
     if (!fmt_ok(fmt) || !xt_ok(staged)) return QG_EINVAL;
+    if (fmt == QG_FMT_Q8A16 && staged != QG_X_F32) return QG_EUNSUPPORTED;
     if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0) return QG_ESHAPE;
     if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
     if (rows < 1 || cols < 32 || (cols % 32) != 0 || (k0 % 32) != 0 || n0 < 0 || k0 < 0 || n0 + rows > N ||
@@ -202,6 +218,7 @@ qg_status qgemm_batch(qg_format fmt, int group, const qg_job* jobs, int J, const
                       int T, qg_mode mode, hipStream_t stream) {
     if (!jobs) return QG_EINVAL;
     if (J < 1 || J > 64) return QG_ESHAPE;
+    if (fmt == QG_FMT_Q8A16) return QG_EUNSUPPORTED;
     for (int j = 0; j < J; j++) {
         const qg_job& b = jobs[j];
         const qg_status st = check_dense(fmt, b.codes, b.scales, b.offsets, group, X, xt, b.Y, b.N, K, T, mode);
@@ -274,6 +291,17 @@ qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, i
         return QG_EALIGN;
     const size_t nblocks = (size_t)N * (size_t)(K / 32);
     return launched(qg::launch_repack_gguf_q8a(type, src, nblocks, codes, scales_f32, offsets_f32, stream));
+}
+
+qg_status qg_repack_gguf_q8a16(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
+                               float* scales_f32, float* offsets_f32, hipStream_t stream) {
+    if (type != QG_GGUF_Q6_K && type != QG_GGUF_Q3_K && type != QG_GGUF_Q2_K) return QG_EINVAL;
+    if (N < 1 || N > kMaxN || K < 256 || K > kMaxK || (K % 256) != 0) return QG_ESHAPE;
+    if (!src || !codes || !scales_f32 || !offsets_f32) return QG_EINVAL;
+    if (!aligned(src, 2) || !aligned(codes, 16) || !aligned(scales_f32, 4) || !aligned(offsets_f32, 4))
+        return QG_EALIGN;
+    const size_t nblk16 = (size_t)N * (size_t)(K / 16);
+    return launched(qg::launch_repack_gguf_q8a16(type, src, nblk16, codes, scales_f32, offsets_f32, stream));
 }
 
 qg_status qg_repack_q8f(const void* blob, int N, int K, int has_col, float* scales, float* col, hipStream_t stream) {

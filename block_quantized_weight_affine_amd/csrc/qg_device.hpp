@@ -16,11 +16,15 @@
 
 namespace qg {
 
-enum { FMT_Q4 = 0, FMT_Q4A = 1, FMT_Q8 = 2, FMT_Q8A = 3 };
+enum { FMT_Q4 = 0, FMT_Q4A = 1, FMT_Q8 = 2, FMT_Q8A = 3, FMT_Q8A16 = 4 };
 // Q8 and Q8A share the code layout (one int8 per element) and the f32 block scales; Q8A adds an f32
-// offset per 32-element block: value = (float(q) * d) + m, two roundings as written.
+// offset per 32-element block: value = (float(q) * d) + m, two roundings as written.  Q8A16 is Q8A
+// with a scale and an offset per 16-element block (the GGUF K-quants Q6_K, Q3_K, Q2_K repacked).
 template <int FMT>
-constexpr bool q8_layout = FMT == FMT_Q8 || FMT == FMT_Q8A;
+constexpr bool q8_layout = FMT == FMT_Q8 || FMT == FMT_Q8A || FMT == FMT_Q8A16;
+// 16-element blocks: scale / offset index n * K / 16 + k / 16
+template <int FMT>
+constexpr bool blk16 = FMT == FMT_Q8A16;
 enum { XT_F32 = 0, XT_F16 = 1, XT_BF16 = 2 };
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -114,6 +118,25 @@ struct RawBlock<FMT_Q8A> {
     float d, m;
     uint32_t dh;
 };
+// d, m: elements 0..15; d2, m2: elements 16..31
+template <>
+struct RawBlock<FMT_Q8A16> {
+    uint4 q0, q1;
+    float d, m;
+    uint32_t dh;
+    float d2, m2;
+};
+
+// Blocks past K decode to zeros: every scale and offset of the block cleared.
+template <int FMT>
+__device__ __forceinline__ void block_clear_if(RawBlock<FMT>& r, bool valid) {
+    r.d = valid ? r.d : 0.f;
+    r.m = valid ? r.m : 0.f;
+    if constexpr (blk16<FMT>) {
+        r.d2 = valid ? r.d2 : 0.f;
+        r.m2 = valid ? r.m2 : 0.f;
+    }
+}
 
 // Loads block b of row n (all addresses in bounds: the caller clamps n and b).
 template <int FMT>
@@ -126,9 +149,17 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
         const u32x4_t a = p[0], c = p[1];
         r.q0 = make_uint4(a.x, a.y, a.z, a.w);
         r.q1 = make_uint4(c.x, c.y, c.z, c.w);
-        r.d = gptr<float>(scales)[bi];
-        r.m = FMT == FMT_Q8A ? gptr<float>((const void*)offs)[bi] : 0.f;
         r.dh = 0;
+        if constexpr (blk16<FMT>) {
+            const size_t b16 = (size_t)n * (size_t)(K >> 4) + 2 * (size_t)b;
+            r.d = gptr<float>(scales)[b16];
+            r.m = gptr<float>((const void*)offs)[b16];
+            r.d2 = gptr<float>(scales)[b16 + 1];
+            r.m2 = gptr<float>((const void*)offs)[b16 + 1];
+        } else {
+            r.d = gptr<float>(scales)[bi];
+            r.m = FMT == FMT_Q8A ? gptr<float>((const void*)offs)[bi] : 0.f;
+        }
     } else {
         const u32x4_t a = *gptr<u32x4_t>((const uint8_t*)codes + (size_t)n * (size_t)(K >> 1) + (size_t)b * 16);
         r.q = make_uint4(a.x, a.y, a.z, a.w);
@@ -174,6 +205,7 @@ __device__ __forceinline__ void value_bytes(const RawBlock<FMT>& r, uint32_t (&c
 // c0 of (1) and whether (1) gives the pages' bits for this block.
 template <int FMT>
 __device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
+    static_assert(!blk16<FMT>, "16-element blocks are staged in f32 only");
     fast = r.d > 0.0f;  // zero or negative scales (and NaN) take the pages' order
     if constexpr (FMT == FMT_Q8A) {
         fast = false;  // two roundings (product, then offset): always the written order
@@ -196,6 +228,7 @@ __device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
 // The pages' order of operations for one element (value byte as f32).
 template <int FMT>
 __device__ __forceinline__ float slow_value(const RawBlock<FMT>& r, float cf) {
+    static_assert(!blk16<FMT>, "16-element blocks are staged in f32 only");
     if constexpr (FMT == FMT_Q8A)
         return keep_f32((cf - 128.0f) * r.d) + r.m;
     else if constexpr (FMT == FMT_Q8)
@@ -220,10 +253,15 @@ __device__ __forceinline__ void block_quad_f32(const RawBlock<FMT>& r, int q, fl
     if constexpr (q8_layout<FMT>) {
         const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         const uint32_t x = w[q];
+        float d = r.d, m = r.m;
+        if constexpr (blk16<FMT>) {
+            d = q < 4 ? r.d : r.d2;
+            m = q < 4 ? r.m : r.m2;
+        }
 #pragma unroll
         for (int b = 0; b < 4; b++) {
-            v[b] = (float)(int8_t)(x >> (8 * b)) * r.d;
-            if constexpr (FMT == FMT_Q8A) v[b] = keep_f32(v[b]) + r.m;
+            v[b] = (float)(int8_t)(x >> (8 * b)) * d;
+            if constexpr (FMT == FMT_Q8A || FMT == FMT_Q8A16) v[b] = keep_f32(v[b]) + m;
         }
     } else {
         const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};

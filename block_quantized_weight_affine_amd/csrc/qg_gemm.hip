@@ -88,6 +88,7 @@ __device__ __forceinline__ int x_row_of(const GemmParams& p, int r) {
 // Weight rows of one lane: row pointers into the codes, scales and offsets of the lane's rows.
 template <int FMT, int MN>
 struct LaneRows {
+    static_assert(!blk16<FMT>, "16-element blocks: exact kernel only");
     const QG_GLOBAL uint8_t* codes[MN];
     const QG_GLOBAL uint8_t* scales[MN];  // f16 (Q4, Q4A) or f32 (Q8) scales of the row
     const QG_GLOBAL uint16_t* offs[MN];   // Q4A offsets of the row (Q8A: f32, per block)
@@ -1170,8 +1171,7 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
         const bool valid0 = g < nblk;
 #pragma unroll
         for (int mn = 0; mn < MN; mn++) {
-            w0[mn].d = valid0 ? w0[mn].d : 0.f;
-            w0[mn].m = valid0 ? w0[mn].m : 0.f;
+            block_clear_if<FMT>(w0[mn], valid0);
             block_to_f32<FMT>(w0[mn], wv[mn]);
         }
     }
@@ -1189,8 +1189,7 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_kernel(GemmParams p, bool
 #pragma unroll
         for (int mn = 0; mn < MN; mn++) {
             rn[mn] = wr[mn];
-            rn[mn].d = valid ? rn[mn].d : 0.f;
-            rn[mn].m = valid ? rn[mn].m : 0.f;
+            block_clear_if<FMT>(rn[mn], valid);
         }
         float wnv[MN][32];
 #pragma unroll
@@ -1363,6 +1362,7 @@ hipError_t launch_gemm_exact(int fmt, int xt, const GemmParams& p, bool grouped,
     if (fmt == FMT_Q4) exact_xt<FMT_Q4>(xt, p, grouped, s);
     else if (fmt == FMT_Q4A) exact_xt<FMT_Q4A>(xt, p, grouped, s);
     else if (fmt == FMT_Q8A) exact_xt<FMT_Q8A>(xt, p, grouped, s);
+    else if (fmt == FMT_Q8A16) exact_xt<FMT_Q8A16>(xt, p, grouped, s);
     else exact_xt<FMT_Q8>(xt, p, grouped, s);
     return hipGetLastError();
 }

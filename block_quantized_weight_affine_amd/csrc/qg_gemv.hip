@@ -65,18 +65,27 @@ struct Unit<FMT_Q8A> {
     uint4 q;
     float d, m;
 };
+// a unit of 16 Q8 values is exactly one 16-element block
+template <>
+struct Unit<FMT_Q8A16> {
+    uint4 q;
+    float d, m;
+};
+// formats with an offset term (the partial then needs the unit's x sum)
+template <int FMT>
+constexpr bool has_offs = FMT == FMT_Q4A || FMT == FMT_Q8A || FMT == FMT_Q8A16;
 
 template <int FMT>
 __device__ __forceinline__ Unit<FMT> load_unit(const void* codes, const void* scales, const uint16_t* offs,
                                                int group, int K, int n, int u) {
     Unit<FMT> r;
-    const size_t bi = (size_t)n * (size_t)(K >> 5) + (size_t)(u >> 1);
+    const size_t bi = blk16<FMT> ? (size_t)n * (size_t)(K >> 4) + (size_t)u : (size_t)n * (size_t)(K >> 5) + (size_t)(u >> 1);
     if constexpr (q8_layout<FMT>) {
         const u32x4_t v =
             __builtin_nontemporal_load((const u32x4_t*)((const int8_t*)codes + (size_t)n * K + (size_t)u * 16));
         r.q = make_uint4(v.x, v.y, v.z, v.w);
         r.d = ((const float*)scales)[bi];
-        r.m = FMT == FMT_Q8A ? ((const float*)(const void*)offs)[bi] : 0.f;
+        r.m = has_offs<FMT> ? ((const float*)(const void*)offs)[bi] : 0.f;
     } else {
         const u32x2_t v =
             __builtin_nontemporal_load((const u32x2_t*)((const uint8_t*)codes + (size_t)n * (K >> 1) + (size_t)u * 8));
@@ -147,7 +156,7 @@ template <int FMT>
 __device__ __forceinline__ float unit_value(const Unit<FMT>& w, float p, float sx) {
     if constexpr (FMT == FMT_Q8)
         return w.d * p;
-    else if constexpr (FMT == FMT_Q8A)
+    else if constexpr (FMT == FMT_Q8A || FMT == FMT_Q8A16)
         return fmaf(w.d, p, w.m * sx);
     else if constexpr (FMT == FMT_Q4)
         return (0.0625f * w.d) * p;
@@ -280,7 +289,7 @@ __device__ __forceinline__ void gemv_rows(const GemmParams& p, const void* codes
                         x[8] = b0.x; x[9] = b0.y; x[10] = b0.z; x[11] = b0.w;
                         x[12] = b1.x; x[13] = b1.y; x[14] = b1.z; x[15] = b1.w;
                         float sx = 0.f;
-                        if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
+                        if constexpr (has_offs<FMT>) {
 #pragma unroll
                             for (int i = 0; i < 16; i++) sx += x[i];
                         }
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
         for (int i = 0; i < V; i++) x[i] = on ? x[i] : 0.f;
     }
     float sx = 0.f;
-    if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
+    if constexpr (has_offs<FMT>) {
 #pragma unroll
         for (int i = 0; i < V; i++) sx += x[i];
     }
@@ -482,24 +491,25 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
             n -= bj.start[j];
         }
         crow[r] = uniform_ptr(codes, (uint64_t)n * (uint64_t)(q8_layout<FMT> ? K : K >> 1));
-        srow[r] = uniform_ptr(scales, (uint64_t)n * (uint64_t)((K >> 5) * (q8_layout<FMT> ? 4 : 2)));
+        srow[r] = uniform_ptr(scales, (uint64_t)n * (uint64_t)((K >> (blk16<FMT> ? 4 : 5)) * (q8_layout<FMT> ? 4 : 2)));
         asm volatile("" : "+s"(crow[r]), "+s"(srow[r]));
-        if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
-            // Q4A: bf16 per group; Q8A: f32 per block, laid out as the scales
-            orow[r] = uniform_ptr(offs, (uint64_t)n * (uint64_t)(FMT == FMT_Q8A ? (K >> 5) * 4 : (K / p.group) * 2));
+        if constexpr (has_offs<FMT>) {
+            // Q4A: bf16 per group; Q8A / Q8A16: f32 per block, laid out as the scales
+            orow[r] = uniform_ptr(offs, (uint64_t)n * (uint64_t)(FMT == FMT_Q4A ? (K / p.group) * 2
+                                                                                : (K >> (blk16<FMT> ? 4 : 5)) * 4));
             asm volatile("" : "+s"(orow[r]));
         }
     }
     const uint32_t oc = (uint32_t)(cc * 16);
-    const uint32_t os = q8_layout<FMT> ? (uint32_t)((cc >> 1) * 4) : (uint32_t)(cc * 2);
-    const uint32_t oo = FMT == FMT_Q4A ? (uint32_t)(((cc * 32) / p.group) * 2) : FMT == FMT_Q8A ? os : 0u;
+    const uint32_t os = blk16<FMT> ? (uint32_t)(cc * 4) : q8_layout<FMT> ? (uint32_t)((cc >> 1) * 4) : (uint32_t)(cc * 2);
+    const uint32_t oo = FMT == FMT_Q4A ? (uint32_t)(((cc * 32) / p.group) * 2) : has_offs<FMT> ? os : 0u;
     u32x4_t q[R];
     float d[R], m[R];
     auto issue = [&](int r) __attribute__((always_inline)) {
         q[r] = __builtin_nontemporal_load((const QG_GLOBAL u32x4_t*)(crow[r] + oc));
         if constexpr (q8_layout<FMT>) {
             d[r] = *(const QG_GLOBAL float*)(srow[r] + os);
-            m[r] = FMT == FMT_Q8A ? *(const QG_GLOBAL float*)(orow[r] + oo) : 0.f;
+            m[r] = has_offs<FMT> ? *(const QG_GLOBAL float*)(orow[r] + oo) : 0.f;
         } else {
             d[r] = 0.0625f * f16_to_f32(*(const QG_GLOBAL uint16_t*)(srow[r] + os));
             m[r] = FMT == FMT_Q4A ? bf16_to_f32(*(const QG_GLOBAL uint16_t*)(orow[r] + oo)) : 0.f;
@@ -518,7 +528,7 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
 #pragma unroll
             for (int i = 0; i < 16; i++) pr = fmaf(sbyte_f32((w4[i >> 2] & 0xF0F0F0F0u) ^ 0x80808080u, i & 3), x[16 + i], pr);
         }
-        const float v = row16_sum_dpp(FMT == FMT_Q4A || FMT == FMT_Q8A ? fmaf(d[r], pr, m[r] * sx) : d[r] * pr);
+        const float v = row16_sum_dpp(has_offs<FMT> ? fmaf(d[r], pr, m[r] * sx) : d[r] * pr);
         if ((lane & 15) == 15) part[(r * 16 + wave) * 4 + (lane >> 4)] = v;
     };
     // Issue order (pinned by scheduling barriers): X (above), rows [0, A), the arithmetic of row 0,
@@ -663,7 +673,7 @@ __device__ __forceinline__ void ksplit_pass(const GemmParams& p, const void* cod
                 }
             }
             sx[t] = 0.f;
-            if constexpr (FMT == FMT_Q4A || FMT == FMT_Q8A) {
+            if constexpr (has_offs<FMT>) {
 #pragma unroll
                 for (int i = 0; i < 16; i++) sx[t] += x[t][i];
             }
@@ -975,6 +985,8 @@ hipError_t launch_gemv(int fmt, int xt, const GemmParams& p, bool grouped, hipSt
     if (fmt == FMT_Q4) gemv_xt<FMT_Q4>(xt, p, grouped, s);
     else if (fmt == FMT_Q4A) gemv_xt<FMT_Q4A>(xt, p, grouped, s);
     else if (fmt == FMT_Q8A) gemv_xt<FMT_Q8A>(xt, p, grouped, s);
+    else if (fmt == FMT_Q8A16 && !grouped) gemv_xt<FMT_Q8A16>(xt, p, false, s);
+    else if (fmt == FMT_Q8A16) return hipErrorInvalidValue;
     else gemv_xt<FMT_Q8>(xt, p, grouped, s);
     return hipGetLastError();
 }

@@ -94,6 +94,8 @@ hipError_t launch_repack_q8f(const void* blob, int N, int K, bool has_col, float
 hipError_t launch_col_scale(const void* X, int xt, int T, int K, const float* col, void* Xs, int st, hipStream_t s);
 hipError_t launch_repack_gguf_q8a(int type, const void* src, size_t nblocks, void* codes, float* scales,
                                   float* offs, hipStream_t s);
+hipError_t launch_repack_gguf_q8a16(int type, const void* src, size_t nblk16, void* codes, float* scales,
+                                    float* offs, hipStream_t s);
 // Device address of this GPU's copy of the fixed scratch array (qg_moe_ffn_noalloc), looked up once
 // per device with that device current.
 hipError_t noalloc_scratch(void** ptr);

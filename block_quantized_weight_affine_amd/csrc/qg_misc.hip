@@ -87,6 +87,12 @@ hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, c
     if (fmt == FMT_Q4) dump_st<FMT_Q4>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else if (fmt == FMT_Q4A) dump_st<FMT_Q4A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else if (fmt == FMT_Q8A) dump_st<FMT_Q8A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
+    else if (fmt == FMT_Q8A16) {
+        if (staged != XT_F32) return hipErrorInvalidValue;  // staged in f32 only
+        const int total = rows * (cols >> 5);
+        hipLaunchKernelGGL((dequant_dump_kernel<FMT_Q8A16, XT_F32>), dim3((total + 255) / 256), dim3(256), 0, s, codes,
+                           scales, offs, group, K, n0, k0, rows, cols, out);
+    }
     else dump_st<FMT_Q8>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     return hipGetLastError();
 }
@@ -668,6 +674,93 @@ hipError_t launch_repack_gguf_q8a(int type, const void* src, size_t nblocks, voi
             break;
         case QG_GGUF_Q5_K:
             hipLaunchKernelGGL(repack_gguf_q8a_kernel<QG_GGUF_Q5_K>, dim3(grid), dim3(256), 0, s, w, nblocks, c,
+                               scales, offs);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---- GGUF K-quants with a scale per 16 elements -> Q8A16 ------------------------------------------
+// Page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC (loaders Q6_KW, Q3_KW, Q2_KW).  256 elements per
+// super-block; 32-element sub-block j has half n = j / 4 and position jj = j % 4; its element e lies
+// in 16-element block s16 = 8 n + 2 jj + e / 16.  Field layout, little-endian, h = f16 as f32:
+//   Q6_K 210 B: 128 B ql, 64 B qh, 16 int8 scales, h d.  Code = (nibble of ql[64 n + 32 (jj % 2) + e]
+//        (high for jj >= 2) | bits 2 jj .. 2 jj + 1 of qh[32 n + e] << 4) - 32; scale d * sc[s16].
+//   Q3_K 110 B: 32 B hmask, 64 B qs, 12 scale bytes, h d.  Code = bits 2 jj .. of qs[32 n + e], minus
+//        4 when bit 4 n + jj of hmask[e] is clear; 6-bit scale of s16 = low four bits from byte s16
+//        (s16 < 8, low nibble) or s16 - 8 (high nibble), top two bits from byte 8 + s16 % 4 at bit
+//        2 (s16 / 4); scale d * (that - 32).
+//   Q2_K 84 B: 16 scale bytes s, 64 B qs, h d, h dmin.  Code = bits 2 jj .. of qs[32 n + e]; scale
+//        d * (s[s16] & 15), offset -(dmin * (s[s16] >> 4)).
+// The pages evaluate code * scale (Q2_K: minus the min) in f32; every product here is exact, and
+// Q8A16 computes fl(fl(code * scale) + offset) -- with offset -0 for Q6_K and Q3_K, which leaves
+// every value, zeros' signs included, as the page computes it.  One thread per 16-element block:
+// the block index in a row-major [N][K / 16] grid is (super-block) * 16 + s16.
+template <int GT>
+__global__ void repack_gguf_q8a16_kernel(const uint8_t* src, size_t nblk16, uint8_t* codes, float* scales,
+                                         float* offs) {
+    constexpr int SBB = GT == QG_GGUF_Q6_K ? 210 : GT == QG_GGUF_Q3_K ? 110 : 84;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblk16; i += (size_t)gridDim.x * blockDim.x) {
+        const uint8_t* SB = src + (i >> 4) * SBB;
+        const int s16 = (int)(i & 15), half = s16 >> 3, pos = (s16 & 7) >> 1, e0 = 16 * (s16 & 1);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        float d, m;
+        if constexpr (GT == QG_GGUF_Q6_K) {
+            d = f16_to_f32((uint16_t)(SB[208] | (SB[209] << 8))) * (float)(int8_t)SB[192 + s16];
+            m = -0.0f;
+            const uint8_t* ql = SB + 64 * half + 32 * (pos & 1) + e0;
+            const uint8_t* qh = SB + 128 + 32 * half + e0;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int low = pos >= 2 ? (ql[e] >> 4) : (ql[e] & 15);
+                const int code = (low | (((qh[e] >> (2 * pos)) & 3) << 4)) - 32;
+                w[e >> 2] |= (uint32_t)(uint8_t)(int8_t)code << (8 * (e & 3));
+            }
+        } else if constexpr (GT == QG_GGUF_Q3_K) {
+            const int lo = s16 < 8 ? (SB[96 + s16] & 15) : (SB[96 + s16 - 8] >> 4);
+            const int hi = (SB[104 + (s16 & 3)] >> (2 * (s16 >> 2))) & 3;
+            d = f16_to_f32((uint16_t)(SB[108] | (SB[109] << 8))) * (float)((lo | (hi << 4)) - 32);
+            m = -0.0f;
+            const uint8_t* qs = SB + 32 + 32 * half + e0;
+            const uint8_t* hm = SB + e0;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                int code = (qs[e] >> (2 * pos)) & 3;
+                if (!((hm[e] >> (4 * half + pos)) & 1)) code -= 4;
+                w[e >> 2] |= (uint32_t)(uint8_t)(int8_t)code << (8 * (e & 3));
+            }
+        } else {
+            const int sc = SB[s16];
+            d = f16_to_f32((uint16_t)(SB[80] | (SB[81] << 8))) * (float)(sc & 15);
+            m = -(f16_to_f32((uint16_t)(SB[82] | (SB[83] << 8))) * (float)(sc >> 4));
+            const uint8_t* qs = SB + 16 + 32 * half + e0;
+#pragma unroll
+            for (int e = 0; e < 16; e++) w[e >> 2] |= (uint32_t)((qs[e] >> (2 * pos)) & 3) << (8 * (e & 3));
+        }
+        // the 16 codes of block i sit at byte 16 i of the row-major codes
+        *(u32x4_t*)(codes + 16 * i) = u32x4_t{w[0], w[1], w[2], w[3]};
+        scales[i] = d;
+        offs[i] = m;
+    }
+}
+
+hipError_t launch_repack_gguf_q8a16(int type, const void* src, size_t nblk16, void* codes, float* scales,
+                                    float* offs, hipStream_t s) {
+    const unsigned grid = (unsigned)std::min<size_t>((nblk16 + 255) / 256, 65535);
+    const uint8_t* b = (const uint8_t*)src;
+    uint8_t* c = (uint8_t*)codes;
+    switch (type) {
+        case QG_GGUF_Q6_K:
+            hipLaunchKernelGGL(repack_gguf_q8a16_kernel<QG_GGUF_Q6_K>, dim3(grid), dim3(256), 0, s, b, nblk16, c,
+                               scales, offs);
+            break;
+        case QG_GGUF_Q3_K:
+            hipLaunchKernelGGL(repack_gguf_q8a16_kernel<QG_GGUF_Q3_K>, dim3(grid), dim3(256), 0, s, b, nblk16, c,
+                               scales, offs);
+            break;
+        case QG_GGUF_Q2_K:
+            hipLaunchKernelGGL(repack_gguf_q8a16_kernel<QG_GGUF_Q2_K>, dim3(grid), dim3(256), 0, s, b, nblk16, c,
                                scales, offs);
             break;
         default: return hipErrorInvalidValue;

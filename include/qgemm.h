@@ -69,8 +69,10 @@ typedef enum { QG_X_F32 = 0, QG_X_F16 = 1, QG_X_BF16 = 2 } qg_xtype;
 /* QG_FAST_WEXACT (dense matmuls only): the fast mode with the weights kept exact -- see below. */
 typedef enum { QG_EXACT = 0, QG_FAST = 1, QG_FAST_WEXACT = 2 } qg_mode;
 /* QG_FMT_Q8A: the target layout of the affine GGUF types (see qg_repack_gguf_q8a); dense entry
- * points, the GEMV, the batched call and the dump only. */
-typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2, QG_FMT_Q8A = 3 } qg_format;
+ * points, the GEMV, the batched call and the dump only.  QG_FMT_Q8A16: Q8A with a scale and an
+ * offset per 16-element block, the target layout of QG_GGUF_Q6_K / Q3_K / Q2_K (see
+ * qg_repack_gguf_q8a16); dense entry points and the f32 dump only. */
+typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2, QG_FMT_Q8A = 3, QG_FMT_Q8A16 = 4 } qg_format;
 /* GGUF block types with the scale inside each block (the values are GGML's type ids). */
 typedef enum {
     QG_GGUF_Q4_0 = 2,
@@ -78,8 +80,11 @@ typedef enum {
     QG_GGUF_Q5_0 = 6,
     QG_GGUF_Q5_1 = 7,
     QG_GGUF_Q8_0 = 8,
+    QG_GGUF_Q2_K = 10,
+    QG_GGUF_Q3_K = 11,
     QG_GGUF_Q4_K = 12,
-    QG_GGUF_Q5_K = 13
+    QG_GGUF_Q5_K = 13,
+    QG_GGUF_Q6_K = 14
 } qg_gguf_type;
 
 /* Text for a status code (static storage; never NULL). */
@@ -118,6 +123,16 @@ qg_status qgemm_q8(const int8_t* codes, const float* scales_f32, const void* X, 
 qg_status qgemm_q8a(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
                     const void* X, qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode,
                     hipStream_t stream);
+/* Q8A16: as qgemm_q8a with f32 scales and offsets [N][K/16], one pair per 16-element block
+ * (entry n K/16 + floor(k/16)); w(n, k) = fl(fl(q d) + m).  This holds the GGUF K-quants whose
+ * scale changes every 16 elements exactly (page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC,
+ * the loaders Q6_KW, Q3_KW, Q2_KW; see qg_repack_gguf_q8a16).  T <= 8 runs the GEMV; larger T runs
+ * the exact f32 MFMA kernel in QG_EXACT and in QG_FAST alike (any X type), whose result lies well
+ * inside the fast tolerance; QG_FAST_WEXACT gives QG_EUNSUPPORTED.  Not accepted by qgemm_batch
+ * (QG_EUNSUPPORTED) nor by the grouped and convolution calls. */
+qg_status qgemm_q8a16(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
+                      const void* X, qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode,
+                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * T <= 8 GEMV: one weight row per wavefront group, coalesced 16-byte loads of the packed blocks,
@@ -134,6 +149,9 @@ qg_status qgemv_q8(const int8_t* codes, const float* scales_f32, const void* X, 
                    float* Y, int N, int K, int T, hipStream_t stream);
 qg_status qgemv_q8a(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
                     const void* X, qg_xtype xt, float* Y, int N, int K, int T, hipStream_t stream);
+/* Q8A16 (see qgemm_q8a16): each lane's 16-byte unit of codes is exactly one 16-element block. */
+qg_status qgemv_q8a16(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
+                      const void* X, qg_xtype xt, float* Y, int N, int K, int T, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Debug dump of a staged weight tile: out[r][c] = the value the GEMM kernels stage for element
@@ -142,8 +160,10 @@ qg_status qgemv_q8a(const int8_t* codes, const float* scales_f32, const float* o
  * staged = QG_X_F32: f32 values (exact mode); QG_X_F16 / QG_X_BF16: 16-bit patterns (fast mode).
  * Needs k0 % 32 == 0, cols % 32 == 0, 0 <= n0, n0 + rows <= N, k0 + cols <= K, rows >= 1;
  * out is [rows][cols] of 4 or 2 bytes, 16-byte aligned.  fmt QG_FMT_Q4 / Q4A take uint16 f16
- * scales, QG_FMT_Q8 / Q8A f32 scales; offsets are read for QG_FMT_Q4A (bf16 bits) and QG_FMT_Q8A
- * (f32 values passed through this pointer, 4-byte aligned) only.
+ * scales, QG_FMT_Q8 / Q8A / Q8A16 f32 scales; offsets are read for QG_FMT_Q4A (bf16 bits) and
+ * QG_FMT_Q8A / Q8A16 (f32 values passed through this pointer, 4-byte aligned) only.  QG_FMT_Q8A16
+ * is staged in f32 only (no kernel stages it in 16 bits): another staged type gives
+ * QG_EUNSUPPORTED.
  */
 qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales,
                           const uint16_t* offsets_bf16, int group, int N, int K, int n0, int k0,
@@ -226,6 +246,31 @@ qg_status qg_repack_gguf(qg_gguf_type type, const void* src, int N, int K, void*
  * QG_EINVAL.  Asynchronous on `stream`; nothing is allocated. */
 qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
                              float* scales_f32, float* offsets_f32, hipStream_t stream);
+
+/* GGUF K-quants with a scale per 16 elements to the Q8A16 layout, on the device (page "oxinfer
+ * 0.0.5 src/metal.rs", GGUF_SHADER_SRC, the loaders Q6_KW, Q3_KW, Q2_KW).  src: N rows of K/256
+ * super-blocks, row after row, little-endian, f16 fields as h.  Sub-block j (elements 32 j ..
+ * 32 j + 31 of a super-block) has half n = j / 4 and position jj = j % 4; its element e belongs to
+ * the 16-element block s = 8 n + 2 jj + e / 16.
+ *   QG_GGUF_Q6_K (210 bytes): 128 bytes ql, 64 bytes qh, 16 int8 scales sc, h d.  q = (nibble of
+ *                ql[64 n + 32 (jj % 2) + e], the high one for jj >= 2) | (bits 2 jj, 2 jj + 1 of
+ *                qh[32 n + e]) << 4; value (q - 32) * (d sc[s]).
+ *   QG_GGUF_Q3_K (110 bytes): 32 bytes hmask, 64 bytes qs, 12 scale bytes, h d.  code = bits 2 jj,
+ *                2 jj + 1 of qs[32 n + e], minus 4 when bit 4 n + jj of hmask[e] is clear; the
+ *                6-bit scale of s takes its low four bits from scale byte s (s < 8, low nibble) or
+ *                s - 8 (high nibble) and its top two from byte 8 + s % 4 at bit 2 (s / 4); value
+ *                code * (d (scale - 32)).
+ *   QG_GGUF_Q2_K (84 bytes): 16 scale bytes b, 64 bytes qs, h d, h dmin.  code = bits 2 jj,
+ *                2 jj + 1 of qs[32 n + e]; value code * (d (b[s] & 15)) - dmin (b[s] >> 4).
+ * Every product is exact in f32, so the layout holds the values exactly: codes int8 [N][K] (Q6_K
+ * q - 32), scales f32 [N][K/16] and offsets f32 [N][K/16] (-0 for Q6_K and Q3_K, which keeps a
+ * zero's sign; Q2_K -(dmin (b >> 4))); qgemm_q8a16 / qgemv_q8a16 then compute with the GGUF values.
+ * Device pointers owned by the caller; src 2-byte aligned, codes 16-byte aligned, scales and
+ * offsets 4-byte aligned, else QG_EALIGN; N >= 1, K >= 256, K % 256 == 0, else QG_ESHAPE; a type
+ * not listed here or a null pointer gives QG_EINVAL.  Asynchronous on `stream`; nothing is
+ * allocated. */
+qg_status qg_repack_gguf_q8a16(qg_gguf_type type, const void* src, int N, int K, int8_t* codes,
+                               float* scales_f32, float* offsets_f32, hipStream_t stream);
 
 /* q8_2f and q8_row tensors (page "cortiq-engine 0.8.3 src/gpu_metal/qi21.rs", the block loader's
  * codec match; page "cortiq-engine 0.8.41 src/gpu_metal/clover.rs", q8mm): blob is N*K int8 codes

@@ -1,6 +1,7 @@
 """CPU checks of the C ABI: the library loads, exports every function include/qgemm.h declares,
 rejects bad arguments with the documented codes before any HIP call, and its host routing planner
 and packing helpers agree with the oracle.  Nothing here launches a kernel."""
+import ctypes as C
 import os
 import re
 
@@ -220,6 +221,49 @@ def test_q8a_validation_codes():
     assert rep(codes=A16b + 8) == qg.QG_EALIGN
     assert rep(scales=A16c + 2) == qg.QG_EALIGN
     assert rep(offs=A16d + 2) == qg.QG_EALIGN
+
+
+def test_q8a16_validation_codes():
+    """Q8A16: offsets required, W-exact unsupported, no batched, grouped, convolution or 16-bit dump;
+    the GGUF -> Q8A16 repack checks type, sizes (K % 256), pointers and alignment."""
+    L = qg.lib()
+
+    def gemm(codes=A16, scales=A16b, offs=A16, xt=qg.QG_X_F32, T=16, mode=qg.QG_EXACT):
+        return L.qgemm_q8a16(codes, scales, offs, A16c, xt, A16d, 256, 512, T, mode, None)
+
+    assert gemm(offs=None) == qg.QG_EINVAL
+    assert gemm(offs=A16 + 2) == qg.QG_EALIGN
+    assert gemm(scales=A16b + 2) == qg.QG_EALIGN
+    assert gemm(codes=A16 + 4) == qg.QG_EALIGN
+    assert gemm(T=0, offs=None) == qg.QG_OK
+    assert gemm(xt=qg.QG_X_F16, mode=qg.QG_FAST_WEXACT) == qg.QG_EUNSUPPORTED
+    assert L.qgemv_q8a16(A16, A16b, A16, A16c, 0, A16d, 256, 512, 9, None) == qg.QG_ESHAPE
+    assert L.qgemv_q8a16(A16, A16b, None, A16c, 0, A16d, 256, 512, 1, None) == qg.QG_EINVAL
+    jobs = qg.job_array([(A16, A16b, A16, A16d, 64)])
+    assert L.qgemm_batch(qg.QG_FMT_Q8A16, 64, C.cast(jobs, C.c_void_p), 1, A16c, 0, 512, 2, qg.QG_EXACT,
+                         None) == qg.QG_EUNSUPPORTED
+    assert L.qg_dequant_dump(qg.QG_FMT_Q8A16, A16, A16b, A16, 64, 64, 256, 0, 0, 8, 64, 1, A16c, None) == \
+        qg.QG_EUNSUPPORTED
+    assert L.qgemm_moe_grouped(qg.QG_FMT_Q8A16, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 512, 8, 4,
+                               qg.QG_EXACT, None) == qg.QG_EUNSUPPORTED
+    assert L.qg_conv2d(qg.QG_FMT_Q8A16, A16, A16b, A16c, 8, 8, 32, 3, 1, 64, 0, 0, None, None, 0, A16d,
+                       qg.QG_EXACT, None) == qg.QG_EUNSUPPORTED
+
+    def rep(t=qg.QG_GGUF_Q6_K, src=A16, N=8, K=512, codes=A16b, scales=A16c, offs=A16d):
+        return L.qg_repack_gguf_q8a16(t, src, N, K, codes, scales, offs, None)
+
+    assert rep(t=qg.QG_GGUF_Q4_K) == qg.QG_EINVAL     # a 32-element-scale type
+    assert rep(t=qg.QG_GGUF_Q8_0) == qg.QG_EINVAL
+    assert rep(t=9) == qg.QG_EINVAL
+    assert rep(K=288) == qg.QG_ESHAPE                 # K % 256 == 0
+    assert rep(t=qg.QG_GGUF_Q2_K, K=128) == qg.QG_ESHAPE
+    assert rep(N=0) == qg.QG_ESHAPE
+    assert rep(offs=None) == qg.QG_EINVAL
+    assert rep(src=None) == qg.QG_EINVAL
+    assert rep(src=A16 + 1) == qg.QG_EALIGN
+    assert rep(codes=A16b + 8) == qg.QG_EALIGN
+    assert rep(scales=A16c + 2) == qg.QG_EALIGN
+    assert rep(t=qg.QG_GGUF_Q3_K, offs=A16d + 2) == qg.QG_EALIGN
 
 
 def test_conv_validation_codes():
