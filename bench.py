@@ -304,6 +304,40 @@ def measure_gemv_t(T: int, steps: int, warmup: int) -> dict:
             "bytes_per_step": nbytes}
 
 
+def measure_q6k_decode(steps: int, warmup: int) -> dict:
+    """A GGUF Q6_K matrix (N = K = 4096, seeded super-block bytes) repacked on the device into Q8A16,
+    then the T = 1 decode GEMV (qgemv_q8a16, f32 X): HBM GB/s of the Q8A16 bytes the GEMV reads (codes
+    N K, f32 scale and offset per 16 elements, X, Y), 16 rotating weight copies (403 MB)."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    N = K = 4096
+    nsb = N * K // 256
+    rng = np.random.default_rng(1601)
+    src = rng.integers(0, 256, nsb * 210).astype(np.uint8).reshape(nsb, 210)
+    d = synth.f16_uniform(1601, 1, nsb, 0.001, 0.004)
+    src[:, 208], src[:, 209] = d & 0xFF, d >> 8
+    s = _dev(src.reshape(-1))
+    copies = 16
+    C_ = [torch.empty(N * K, dtype=torch.int8, device="cuda") for _ in range(copies)]
+    S_ = [torch.empty(N * K // 16, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    O_ = [torch.empty(N * K // 16, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    for c, sc, of in zip(C_, S_, O_):
+        qg.qg_repack_gguf_q8a16("q6_k", s, N, K, c, sc, of)
+    X = _dev(synth.normal_as(1601, synth.STREAM_X, K, 0.0, 1.0, "f32").reshape(1, K))
+    Y = torch.empty((1, N), device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    step = _bound("qgemv_q8a16", [c.data_ptr() for c in C_], [x.data_ptr() for x in S_], [o.data_ptr() for o in O_],
+                  X.data_ptr(), qg.QG_X_F32, Y.data_ptr(), N, K, 1, st)
+    ms, _ = _timed(step, steps, warmup)
+    nbytes = float(N * K + N * K // 16 * 8 + K * 4 + N * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "q6_k_gemv_decode", "config": "gguf_q6_k_as_q8a16_N4096_K4096_T1", "mode": "exact",
+            "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f32", "kernel": "gemv1_split_kernel",
+            "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
+            "bytes_per_step": nbytes, "gguf_bytes_per_step": float(nsb * 210)}
+
+
 def measure_q8_prefill(mode: str, steps: int, warmup: int) -> dict:
     """The prefill GEMM shape with Q8 weights (N = K = 4096, T = 512, f16 X N(0, 0.5)) in the two
     fast modes: "fast" rounds each decoded weight q d to f16; "fast_wexact" keeps the codes exact in
@@ -555,6 +589,8 @@ def main():
         r.pop("keep")
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         r = measure_gemv_t(4, 512, 50)
+        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        r = measure_q6k_decode(512, 50)
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         for mode in ("fast", "fast_wexact"):
             r = measure_q8_prefill(mode, 128, 20)
