@@ -278,28 +278,30 @@ def measure_batch(steps: int, warmup: int) -> dict:
             "keep": (arrs, dev_sets, X, arrs4, y4, X4)}
 
 
-def measure_gemv_t(T: int, steps: int, warmup: int) -> dict:
-    """The Q8 GEMV decode shape (N = K = 4096, f32 X) with T = 2..8 rows of X: HBM GB/s of its
-    algorithmic bytes, 16 rotating weight copies."""
+def measure_gemv_t(T: int, steps: int, warmup: int, fmt: str = "q8") -> dict:
+    """The GEMV decode shape (N = K = 4096, f32 X) with T rows of X, Q8 or Q4 weights: HBM GB/s of its
+    algorithmic bytes over rotating weight copies beyond the 256 MB Infinity Cache (Q8: 16 copies,
+    302 MB; Q4: 32 copies, 302 MB)."""
     import torch
     import block_quantized_weight_affine_amd as qg
     import synth
     N = K = 4096
-    w = synth.make_dense("q8", N, K, T, "f32", 1.0, 1001)
-    copies = 16
+    w = synth.make_dense(fmt, N, K, T, "f32", 1.0, 1001)
+    copies = 16 if fmt == "q8" else 32
     C_ = [_dev(w["codes"]) for _ in range(copies)]
     S_ = [_dev(w["scales"]) for _ in range(copies)]
     X = _dev(w["X"].reshape(T, K))
     Y = torch.empty((T, N), device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    step = _bound("qgemv_q8", [c.data_ptr() for c in C_], [s.data_ptr() for s in S_], X.data_ptr(), qg.QG_X_F32,
-                  Y.data_ptr(), N, K, T, st)
+    step = _bound(f"qgemv_{fmt}", [c.data_ptr() for c in C_], [s.data_ptr() for s in S_], X.data_ptr(),
+                  qg.QG_X_F32, Y.data_ptr(), N, K, T, st)
     ms, _ = _timed(step, steps, warmup)
-    nbytes = float(N * K + N * K // 32 * 4 + T * K * 4 + T * N * 4)
+    wbytes = N * K + N * K // 32 * 4 if fmt == "q8" else N * K // 2 + N * K // 32 * 2
+    nbytes = float(wbytes + T * K * 4 + T * N * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": f"q8_gemv_T{T}", "config": f"q8_gemv_T{T}_N4096_K4096", "mode": "exact",
+    return {"workload": f"{fmt}_gemv_T{T}", "config": f"{fmt}_gemv_T{T}_N4096_K4096", "mode": "exact",
             "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f32",
-            "kernel": "gemv_ksplit_kernel",
+            "kernel": "gemv1_split_kernel" if T == 1 else "gemv_ksplit_kernel",
             "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
             "bytes_per_step": nbytes}
 
@@ -588,8 +590,9 @@ def main():
         r = measure_batch(512, 50)
         r.pop("keep")
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
-        r = measure_gemv_t(4, 512, 50)
-        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        for fmt, T in (("q8", 4), ("q4", 1), ("q4", 4)):
+            r = measure_gemv_t(T, 512, 50, fmt)
+            also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         r = measure_q6k_decode(512, 50)
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         for mode in ("fast", "fast_wexact"):

@@ -534,8 +534,9 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
     // Issue order (pinned by scheduling barriers): X (above), rows [0, A), the arithmetic of row 0,
     // rows [A, R), the arithmetic of the rest.  Measured (Q8 4096 x 4096, R = 8): A = 3 or 4 5.03
     // us, A = 2 5.13, A = 1 5.24, the rest issued before row 0's arithmetic 5.23, and the order the
-    // compiler picks by itself 5.05-5.45 depending on the surrounding code.
-    constexpr int A = R >= 8 ? 4 : 1;
+    // compiler picks by itself 5.05-5.45 depending on the surrounding code.  R = 4 (Q4 4096 x 4096,
+    // two wavefronts a row): all four rows first, 5.15-5.23 us against 5.61-5.64 with A = 1.
+    constexpr int A = R >= 8 ? 4 : R;
 #pragma unroll
     for (int r = 0; r < A; r++) issue(r);
     __builtin_amdgcn_sched_barrier(0);
