@@ -377,13 +377,14 @@ def gguf_repack_q8a(gtype, src, N, K) -> tuple:
     return codes, scales, offs
 
 
-def gguf_repack_q8a16(gtype, src, N, K) -> tuple:
-    """(codes int8 [N*K], scales f32 [N*K/16], offsets f32 [N*K/16]) of the Q8A16 layout for the
-    K-quants with a scale per 16 elements (Q6_K, Q3_K, Q2_K)."""
+def gguf_repack_q8a16(gtype, src, N, K, with_offsets=True) -> tuple:
+    """(codes int8 [N*K], scales f32 [N*K/16], offsets f32 [N*K/16] or None) of the Q8A16 layout for
+    the K-quants with a scale per 16 elements (Q6_K, Q3_K, Q2_K); with_offsets=False (Q6_K, Q3_K)
+    gives the offset-free layout."""
     b = _c(src, np.uint8)
     codes = np.empty(N * K, np.int8)
     scales = np.empty(N * K // 16, np.float32)
-    offs = np.empty(N * K // 16, np.float32)
+    offs = np.empty(N * K // 16, np.float32) if with_offsets else None
     lib().orc_gguf_repack_q8a16(GGUF[gtype], _ptr(b), N, K, _ptr(codes), _ptr(scales), _ptr(offs))
     return codes, scales, offs
 

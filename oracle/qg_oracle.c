@@ -23,6 +23,8 @@
  *     at the add is the same).
  *   - Q8A16 (the split layout Q6_K, Q3_K and Q2_K below are repacked into): Q8A with one scale
  *     and one offset per 16-element block, entry n*K/16 + floor(k/16); the same two roundings.
+ *     Without offsets (a NULL array) the value is float(q) * scale alone, as the Q6_K and Q3_K
+ *     loaders compute it.
  *   - Fast-mode staging, MMA_SHADER_SRC (mma_tile): the f32 value is converted to a 16-bit
  *     float as it is written to the tile (round to nearest, ties to even).
  *   - Row scaling to f16, MMA_SHADER_SRC (row_scale, x_half): per row, amax; frexp exponent
@@ -145,7 +147,7 @@ double orc_weight_exact(int fmt, const void* codes, const void* scales, const ui
     if (fmt == ORC_Q8 || fmt == ORC_Q8A || fmt == ORC_Q8A16) {
         int q = ((const int8_t*)codes)[(size_t)n * K + k];
         double v = (double)q * (double)((const float*)scales)[bi];
-        if (fmt != ORC_Q8) v += (double)((const float*)(const void*)offs)[bi];
+        if (fmt != ORC_Q8 && offs) v += (double)((const float*)(const void*)offs)[bi];
         return v;
     }
     int nib = q4_nibble((const uint8_t*)codes, K, n, k);
@@ -163,7 +165,7 @@ float orc_weight_f32(int fmt, const void* codes, const void* scales, const uint1
         int q = ((const int8_t*)codes)[(size_t)n * K + k];
         float d = ((const float*)scales)[bi];
         float v = (float)q * d;
-        if (fmt != ORC_Q8) {
+        if (fmt != ORC_Q8 && offs) {
             float m = ((const float*)(const void*)offs)[bi];
             v = v + m;
         }
@@ -907,7 +909,8 @@ int orc_conv2d(int fmt, const void* codes, const void* scales, const uint16_t* o
 
 /* Q6_K, Q3_K, Q2_K -> the Q8A16 layout: int8 codes [N][K], f32 scales and f32 offsets [N][K/16],
  * with fl(fl(code * scale) + offset) equal to the type's value: Q6_K and Q3_K (code, dl, -0)
- * (adding -0 leaves every value, a zero's sign included, unchanged); Q2_K (code, dl, -ml). */
+ * (adding -0 leaves every value, a zero's sign included, unchanged); Q2_K (code, dl, -ml).
+ * offs may be NULL (Q6_K, Q3_K: the offset-free layout). */
 void orc_gguf_repack_q8a16(int type, const uint8_t* src, int N, int K, int8_t* codes, float* scales, float* offs) {
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++) {
@@ -917,6 +920,6 @@ void orc_gguf_repack_q8a16(int type, const uint8_t* src, int N, int K, int8_t* c
             size_t bi = (size_t)n * (K / 16) + k / 16;
             codes[(size_t)n * K + k] = (int8_t)code;
             scales[bi] = d;
-            offs[bi] = -m;
+            if (offs) offs[bi] = -m;
         }
 }

@@ -989,3 +989,23 @@ def test_q8a16_reduces_to_q8a(orc):
     w = orc.dequant_tile("q8a16", codes, s16, np.repeat(o32, 2), 32, N, K, 0, 0, 1, 32, "f32")[0]
     w0 = orc.dequant_tile("q8a", codes, s32, o32, 32, N, K, 0, 0, 1, 32, "f32")[0]
     assert np.array_equal(w[:16], w0[:16]) and not np.array_equal(w[16:], w0[16:])
+
+
+@pytest.mark.parametrize("gtype", ["q6_k", "q3_k"])
+def test_gguf_q8a16_without_offsets(orc, gtype):
+    """Q6_K and Q3_K need no offset: the offset-free Q8A16 layout (float(q) * scale alone) decodes
+    every element as the in-block loader does, bit for bit, and its GEMM equals the one with the
+    explicit -0 offsets."""
+    N, K, T = 3, 512, 2
+    src = _random_kquant(orc, gtype, N, K, 23)
+    codes, scales, offs = orc.gguf_repack_q8a16(gtype, src, N, K, with_offsets=False)
+    assert offs is None
+    direct = orc.gguf_dequant(gtype, src, N, K)
+    split = orc.dequant_tile("q8a16", codes, scales, None, 32, N, K, 0, 0, N, K, "f32")
+    assert np.array_equal(direct.view(np.uint32), split.view(np.uint32))
+    X = np.random.default_rng(2).standard_normal(T * K).astype(np.float32)
+    c2, s2, o2 = orc.gguf_repack_q8a16(gtype, src, N, K)
+    assert np.all(o2.view(np.uint32) == 0x80000000)
+    Ya, Sa, _ = orc.gemm("q8a16", codes, scales, None, 32, N, K, X, "f32", T)
+    Yb, Sb, _ = orc.gemm("q8a16", c2, s2, o2, 32, N, K, X, "f32", T)
+    assert np.array_equal(Ya, Yb) and np.array_equal(Sa, Sb)
