@@ -307,9 +307,10 @@ def measure_gemv_t(T: int, steps: int, warmup: int, fmt: str = "q8") -> dict:
 
 
 def measure_q6k_decode(steps: int, warmup: int) -> dict:
-    """A GGUF Q6_K matrix (N = K = 4096, seeded super-block bytes) repacked on the device into Q8A16,
-    then the T = 1 decode GEMV (qgemv_q8a16, f32 X): HBM GB/s of the Q8A16 bytes the GEMV reads (codes
-    N K, f32 scale and offset per 16 elements, X, Y), 16 rotating weight copies (403 MB)."""
+    """A GGUF Q6_K matrix (N = K = 4096, seeded super-block bytes) repacked on the device into the
+    offset-free Q8A16 layout, then the T = 1 decode GEMV (qgemv_q8a16, f32 X, no offsets): HBM GB/s of
+    the bytes the GEMV reads (codes N K, an f32 scale per 16 elements, X, Y), 16 rotating weight
+    copies (336 MB)."""
     import torch
     import block_quantized_weight_affine_amd as qg
     import synth
@@ -323,18 +324,17 @@ def measure_q6k_decode(steps: int, warmup: int) -> dict:
     copies = 16
     C_ = [torch.empty(N * K, dtype=torch.int8, device="cuda") for _ in range(copies)]
     S_ = [torch.empty(N * K // 16, dtype=torch.float32, device="cuda") for _ in range(copies)]
-    O_ = [torch.empty(N * K // 16, dtype=torch.float32, device="cuda") for _ in range(copies)]
-    for c, sc, of in zip(C_, S_, O_):
-        qg.qg_repack_gguf_q8a16("q6_k", s, N, K, c, sc, of)
+    for c, sc in zip(C_, S_):
+        qg.qg_repack_gguf_q8a16("q6_k", s, N, K, c, sc, None)
     X = _dev(synth.normal_as(1601, synth.STREAM_X, K, 0.0, 1.0, "f32").reshape(1, K))
     Y = torch.empty((1, N), device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    step = _bound("qgemv_q8a16", [c.data_ptr() for c in C_], [x.data_ptr() for x in S_], [o.data_ptr() for o in O_],
-                  X.data_ptr(), qg.QG_X_F32, Y.data_ptr(), N, K, 1, st)
+    step = _bound("qgemv_q8a16", [c.data_ptr() for c in C_], [x.data_ptr() for x in S_], None, X.data_ptr(),
+                  qg.QG_X_F32, Y.data_ptr(), N, K, 1, st)
     ms, _ = _timed(step, steps, warmup)
-    nbytes = float(N * K + N * K // 16 * 8 + K * 4 + N * 4)
+    nbytes = float(N * K + N * K // 16 * 4 + K * 4 + N * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": "q6_k_gemv_decode", "config": "gguf_q6_k_as_q8a16_N4096_K4096_T1", "mode": "exact",
+    return {"workload": "q6_k_gemv_decode", "config": "gguf_q6_k_as_q8a16_no_offsets_N4096_K4096_T1", "mode": "exact",
             "ms_per_step": ms, "us_per_step": ms * 1e3, "dtype": "f32", "kernel": "gemv1_split_kernel",
             "value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK["hbm"], "frac": gbs / PEAK["hbm"],
             "bytes_per_step": nbytes, "gguf_bytes_per_step": float(nsb * 210)}

@@ -403,7 +403,7 @@ def expert_table(experts, device="cuda"):
 
 def qg_repack_gguf_q8a16(gtype, src, N, K, codes, scales, offsets, stream=None):
     """GGUF Q6_K / Q3_K / Q2_K super-blocks (device uint8 tensor) -> Q8A16 codes (int8 [N*K]), f32 scales
-    and f32 offsets ([N*K/16]), all device tensors."""
+    and f32 offsets ([N*K/16]; None for the offset-free Q6_K / Q3_K layout), all device tensors."""
     _check(lib().qg_repack_gguf_q8a16(GGUF[gtype] if isinstance(gtype, str) else gtype, _ptr(src), N, K,
                                       _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)),
            "qg_repack_gguf_q8a16")

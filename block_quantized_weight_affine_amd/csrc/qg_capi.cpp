@@ -38,9 +38,10 @@ qg_status check_dense(int fmt, const void* codes, const void* scales, const uint
     if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0 || T < 0 || T > kMaxT) return QG_ESHAPE;
     if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
     if (T == 0) return QG_OK;
-    if (!codes || !scales || !X || !Y || (has_offs(fmt) && !offs)) return QG_EINVAL;
+    // Q8A16 offsets are optional (NULL: no offset term)
+    if (!codes || !scales || !X || !Y || (has_offs(fmt) && fmt != QG_FMT_Q8A16 && !offs)) return QG_EINVAL;
     if (!aligned(codes, 16) || !aligned(X, 16) || !aligned(Y, 4) || !aligned(scales, scale_bytes(fmt)) ||
-        (has_offs(fmt) && !aligned(offs, offs_bytes(fmt))))
+        (has_offs(fmt) && offs && !aligned(offs, offs_bytes(fmt))))
         return QG_EALIGN;
     return QG_OK;
 }
@@ -167,9 +168,9 @@ qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales, 
     if (rows < 1 || cols < 32 || (cols % 32) != 0 || (k0 % 32) != 0 || n0 < 0 || k0 < 0 || n0 + rows > N ||
         k0 + cols > K)
         return QG_ESHAPE;
-    if (!codes || !scales || !out || (has_offs(fmt) && !offsets_bf16)) return QG_EINVAL;
+    if (!codes || !scales || !out || (has_offs(fmt) && fmt != QG_FMT_Q8A16 && !offsets_bf16)) return QG_EINVAL;
     if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(scales, scale_bytes(fmt)) ||
-        (has_offs(fmt) && !aligned(offsets_bf16, offs_bytes(fmt))))
+        (has_offs(fmt) && offsets_bf16 && !aligned(offsets_bf16, offs_bytes(fmt))))
         return QG_EALIGN;
     return launched(qg::launch_dequant_dump(fmt, codes, scales, offsets_bf16, group, N, K, n0, k0, rows, cols,
                                             staged, out, stream));
@@ -297,8 +298,10 @@ qg_status qg_repack_gguf_q8a16(qg_gguf_type type, const void* src, int N, int K,
                                float* scales_f32, float* offsets_f32, hipStream_t stream) {
     if (type != QG_GGUF_Q6_K && type != QG_GGUF_Q3_K && type != QG_GGUF_Q2_K) return QG_EINVAL;
     if (N < 1 || N > kMaxN || K < 256 || K > kMaxK || (K % 256) != 0) return QG_ESHAPE;
-    if (!src || !codes || !scales_f32 || !offsets_f32) return QG_EINVAL;
-    if (!aligned(src, 2) || !aligned(codes, 16) || !aligned(scales_f32, 4) || !aligned(offsets_f32, 4))
+    // offsets may be omitted for Q6_K and Q3_K (all -0: the offset-free layout)
+    if (!src || !codes || !scales_f32 || (!offsets_f32 && type == QG_GGUF_Q2_K)) return QG_EINVAL;
+    if (!aligned(src, 2) || !aligned(codes, 16) || !aligned(scales_f32, 4) ||
+        (offsets_f32 && !aligned(offsets_f32, 4)))
         return QG_EALIGN;
     const size_t nblk16 = (size_t)N * (size_t)(K / 16);
     return launched(qg::launch_repack_gguf_q8a16(type, src, nblk16, codes, scales_f32, offsets_f32, stream));

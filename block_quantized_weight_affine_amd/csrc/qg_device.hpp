@@ -151,11 +151,12 @@ __device__ __forceinline__ RawBlock<FMT> load_block(const void* codes, const voi
         r.q1 = make_uint4(c.x, c.y, c.z, c.w);
         r.dh = 0;
         if constexpr (blk16<FMT>) {
+            // no offsets (NULL): -0, which leaves every value, a zero's sign included, unchanged
             const size_t b16 = (size_t)n * (size_t)(K >> 4) + 2 * (size_t)b;
             r.d = gptr<float>(scales)[b16];
-            r.m = gptr<float>((const void*)offs)[b16];
+            r.m = offs ? gptr<float>((const void*)offs)[b16] : -0.0f;
             r.d2 = gptr<float>(scales)[b16 + 1];
-            r.m2 = gptr<float>((const void*)offs)[b16 + 1];
+            r.m2 = offs ? gptr<float>((const void*)offs)[b16 + 1] : -0.0f;
         } else {
             r.d = gptr<float>(scales)[bi];
             r.m = FMT == FMT_Q8A ? gptr<float>((const void*)offs)[bi] : 0.f;

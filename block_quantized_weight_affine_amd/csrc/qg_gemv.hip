@@ -85,7 +85,8 @@ __device__ __forceinline__ Unit<FMT> load_unit(const void* codes, const void* sc
             __builtin_nontemporal_load((const u32x4_t*)((const int8_t*)codes + (size_t)n * K + (size_t)u * 16));
         r.q = make_uint4(v.x, v.y, v.z, v.w);
         r.d = ((const float*)scales)[bi];
-        r.m = has_offs<FMT> ? ((const float*)(const void*)offs)[bi] : 0.f;
+        if constexpr (blk16<FMT>) r.m = offs ? ((const float*)(const void*)offs)[bi] : -0.0f;  // NULL: none
+        else r.m = has_offs<FMT> ? ((const float*)(const void*)offs)[bi] : 0.f;
     } else {
         const u32x2_t v =
             __builtin_nontemporal_load((const u32x2_t*)((const uint8_t*)codes + (size_t)n * (K >> 1) + (size_t)u * 8));
@@ -494,9 +495,10 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
         srow[r] = uniform_ptr(scales, (uint64_t)n * (uint64_t)((K >> (blk16<FMT> ? 4 : 5)) * (q8_layout<FMT> ? 4 : 2)));
         asm volatile("" : "+s"(crow[r]), "+s"(srow[r]));
         if constexpr (has_offs<FMT>) {
-            // Q4A: bf16 per group; Q8A / Q8A16: f32 per block, laid out as the scales
-            orow[r] = uniform_ptr(offs, (uint64_t)n * (uint64_t)(FMT == FMT_Q4A ? (K / p.group) * 2
-                                                                                : (K >> (blk16<FMT> ? 4 : 5)) * 4));
+            // Q4A: bf16 per group; Q8A / Q8A16: f32 per block, laid out as the scales (Q8A16 offsets
+            // may be absent: row 0's base is then never read)
+            orow[r] = uniform_ptr(offs, (uint64_t)(blk16<FMT> && !offs ? 0 : n) *
+                                            (uint64_t)(FMT == FMT_Q4A ? (K / p.group) * 2 : (K >> (blk16<FMT> ? 4 : 5)) * 4));
             asm volatile("" : "+s"(orow[r]));
         }
     }
@@ -505,11 +507,13 @@ __global__ __launch_bounds__(1024) void gemv1_split_kernel(GemmParams p, BatchJo
     const uint32_t oo = FMT == FMT_Q4A ? (uint32_t)(((cc * 32) / p.group) * 2) : has_offs<FMT> ? os : 0u;
     u32x4_t q[R];
     float d[R], m[R];
+    const bool hm = !blk16<FMT> || p.offs != nullptr;  // Q8A16 without offsets: none read
     auto issue = [&](int r) __attribute__((always_inline)) {
         q[r] = __builtin_nontemporal_load((const QG_GLOBAL u32x4_t*)(crow[r] + oc));
         if constexpr (q8_layout<FMT>) {
             d[r] = *(const QG_GLOBAL float*)(srow[r] + os);
-            m[r] = has_offs<FMT> ? *(const QG_GLOBAL float*)(orow[r] + oo) : 0.f;
+            if constexpr (blk16<FMT>) m[r] = hm ? *(const QG_GLOBAL float*)(orow[r] + oo) : -0.0f;
+            else m[r] = has_offs<FMT> ? *(const QG_GLOBAL float*)(orow[r] + oo) : 0.f;
         } else {
             d[r] = 0.0625f * f16_to_f32(*(const QG_GLOBAL uint16_t*)(srow[r] + os));
             m[r] = FMT == FMT_Q4A ? bf16_to_f32(*(const QG_GLOBAL uint16_t*)(orow[r] + oo)) : 0.f;

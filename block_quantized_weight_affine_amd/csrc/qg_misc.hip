@@ -741,7 +741,7 @@ __global__ void repack_gguf_q8a16_kernel(const uint8_t* src, size_t nblk16, uint
         // the 16 codes of block i sit at byte 16 i of the row-major codes
         *(u32x4_t*)(codes + 16 * i) = u32x4_t{w[0], w[1], w[2], w[3]};
         scales[i] = d;
-        offs[i] = m;
+        if (offs) offs[i] = m;  // uniform: NULL for the offset-free layout (Q6_K, Q3_K)
     }
 }
 

@@ -124,7 +124,8 @@ qg_status qgemm_q8a(const int8_t* codes, const float* scales_f32, const float* o
                     const void* X, qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode,
                     hipStream_t stream);
 /* Q8A16: as qgemm_q8a with f32 scales and offsets [N][K/16], one pair per 16-element block
- * (entry n K/16 + floor(k/16)); w(n, k) = fl(fl(q d) + m).  This holds the GGUF K-quants whose
+ * (entry n K/16 + floor(k/16)); w(n, k) = fl(fl(q d) + m).  offsets_f32 may be NULL: no offset
+ * term, w(n, k) = fl(q d) (the Q6_K and Q3_K layout, 4 bytes per 16 weights fewer to read).  This holds the GGUF K-quants whose
  * scale changes every 16 elements exactly (page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC,
  * the loaders Q6_KW, Q3_KW, Q2_KW; see qg_repack_gguf_q8a16).  T <= 8 runs the GEMV; larger T runs
  * the exact f32 MFMA kernel in QG_EXACT and in QG_FAST alike (any X type), whose result lies well
@@ -161,7 +162,8 @@ qg_status qgemv_q8a16(const int8_t* codes, const float* scales_f32, const float*
  * Needs k0 % 32 == 0, cols % 32 == 0, 0 <= n0, n0 + rows <= N, k0 + cols <= K, rows >= 1;
  * out is [rows][cols] of 4 or 2 bytes, 16-byte aligned.  fmt QG_FMT_Q4 / Q4A take uint16 f16
  * scales, QG_FMT_Q8 / Q8A / Q8A16 f32 scales; offsets are read for QG_FMT_Q4A (bf16 bits) and
- * QG_FMT_Q8A / Q8A16 (f32 values passed through this pointer, 4-byte aligned) only.  QG_FMT_Q8A16
+ * QG_FMT_Q8A / Q8A16 (f32 values passed through this pointer, 4-byte aligned; NULL allowed for
+ * QG_FMT_Q8A16, meaning no offset term) only.  QG_FMT_Q8A16
  * is staged in f32 only (no kernel stages it in 16 bits): another staged type gives
  * QG_EUNSUPPORTED.
  */
@@ -265,6 +267,8 @@ qg_status qg_repack_gguf_q8a(qg_gguf_type type, const void* src, int N, int K, i
  * Every product is exact in f32, so the layout holds the values exactly: codes int8 [N][K] (Q6_K
  * q - 32), scales f32 [N][K/16] and offsets f32 [N][K/16] (-0 for Q6_K and Q3_K, which keeps a
  * zero's sign; Q2_K -(dmin (b >> 4))); qgemm_q8a16 / qgemv_q8a16 then compute with the GGUF values.
+ * For Q6_K and Q3_K offsets_f32 may be NULL (nothing written): the offset-free layout, which the
+ * matmuls take with NULL offsets; Q2_K needs it (else QG_EINVAL).
  * Device pointers owned by the caller; src 2-byte aligned, codes 16-byte aligned, scales and
  * offsets 4-byte aligned, else QG_EALIGN; N >= 1, K >= 256, K % 256 == 0, else QG_ESHAPE; a type
  * not listed here or a null pointer gives QG_EINVAL.  Asynchronous on `stream`; nothing is

@@ -231,14 +231,15 @@ def test_q8a16_validation_codes():
     def gemm(codes=A16, scales=A16b, offs=A16, xt=qg.QG_X_F32, T=16, mode=qg.QG_EXACT):
         return L.qgemm_q8a16(codes, scales, offs, A16c, xt, A16d, 256, 512, T, mode, None)
 
-    assert gemm(offs=None) == qg.QG_EINVAL
+    # offsets are optional (NULL: no offset term); only present ones are checked
     assert gemm(offs=A16 + 2) == qg.QG_EALIGN
+    assert gemm(offs=None, scales=A16b + 2) == qg.QG_EALIGN
     assert gemm(scales=A16b + 2) == qg.QG_EALIGN
     assert gemm(codes=A16 + 4) == qg.QG_EALIGN
     assert gemm(T=0, offs=None) == qg.QG_OK
     assert gemm(xt=qg.QG_X_F16, mode=qg.QG_FAST_WEXACT) == qg.QG_EUNSUPPORTED
     assert L.qgemv_q8a16(A16, A16b, A16, A16c, 0, A16d, 256, 512, 9, None) == qg.QG_ESHAPE
-    assert L.qgemv_q8a16(A16, A16b, None, A16c, 0, A16d, 256, 512, 1, None) == qg.QG_EINVAL
+    assert L.qgemv_q8a16(A16, None, None, A16c, 0, A16d, 256, 512, 1, None) == qg.QG_EINVAL
     jobs = qg.job_array([(A16, A16b, A16, A16d, 64)])
     assert L.qgemm_batch(qg.QG_FMT_Q8A16, 64, C.cast(jobs, C.c_void_p), 1, A16c, 0, 512, 2, qg.QG_EXACT,
                          None) == qg.QG_EUNSUPPORTED
@@ -258,11 +259,12 @@ def test_q8a16_validation_codes():
     assert rep(K=288) == qg.QG_ESHAPE                 # K % 256 == 0
     assert rep(t=qg.QG_GGUF_Q2_K, K=128) == qg.QG_ESHAPE
     assert rep(N=0) == qg.QG_ESHAPE
-    assert rep(offs=None) == qg.QG_EINVAL
+    assert rep(t=qg.QG_GGUF_Q2_K, offs=None) == qg.QG_EINVAL    # Q2_K has real offsets
     assert rep(src=None) == qg.QG_EINVAL
     assert rep(src=A16 + 1) == qg.QG_EALIGN
     assert rep(codes=A16b + 8) == qg.QG_EALIGN
     assert rep(scales=A16c + 2) == qg.QG_EALIGN
+    assert rep(offs=None, scales=A16c + 2) == qg.QG_EALIGN
     assert rep(t=qg.QG_GGUF_Q3_K, offs=A16d + 2) == qg.QG_EALIGN
 
 

@@ -38,10 +38,10 @@ def _gguf_bytes(gtype, N, K, seed):
     return src.reshape(-1)
 
 
-def _repack_dev(gtype, src, N, K):
+def _repack_dev(gtype, src, N, K, with_offsets=True):
     codes = torch.empty(N * K, dtype=torch.int8, device="cuda")
     scales = torch.empty(N * K // 16, dtype=torch.float32, device="cuda")
-    offs = torch.empty(N * K // 16, dtype=torch.float32, device="cuda")
+    offs = torch.empty(N * K // 16, dtype=torch.float32, device="cuda") if with_offsets else None
     print(f"repack q8a16 {gtype} N={N} K={K}", flush=True)
     qg.qg_repack_gguf_q8a16(gtype, dev(src), N, K, codes, scales, offs)
     torch.cuda.synchronize()
@@ -186,3 +186,36 @@ def test_q8a16_refused_where_not_built():
         qg.qgemm_batch("q8a16", 64, [(c, s, s, Y, N)], X, K, T)
     with pytest.raises(RuntimeError):
         qg.qgemm_q8a16(c, s, s, X.half(), Y, N, K, T, "fast_wexact")
+
+
+@pytest.mark.parametrize("gtype", ["q6_k", "q3_k"])
+def test_offset_free_layout(orc, gtype):
+    """Q6_K / Q3_K repacked without offsets: codes and scales as the oracle's, the staged tile equal to
+    the in-block decode bit for bit, and matmuls (T = 1 streaming GEMV, T = 3 K-split GEMV, T = 40
+    exact tiles, T = 96 fast) against the oracle's offset-free GEMM; the T = 1 result equals the one
+    with the explicit -0 offsets bit for bit."""
+    N, K = 96, 1024
+    src = _gguf_bytes(gtype, N, K, 91)
+    codes, scales, none = _repack_dev(gtype, src, N, K, with_offsets=False)
+    assert none is None
+    rc, rs, _ = orc.gguf_repack_q8a16(gtype, src, N, K, with_offsets=False)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    qg.qg_dequant_dump("q8a16", codes, scales, None, 64, N, K, 0, 0, N, K, qg.QG_X_F32, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), orc.gguf_dequant(gtype, src, N, K).view(np.uint32))
+    for mode, T, xt in (("exact", 1, "f32"), ("exact", 3, "f16"), ("exact", 40, "f32"), ("fast", 96, "bf16")):
+        X = synth.normal_as(93 + T, synth.STREAM_X, T * K, 0.0, 1.0, xt)
+        Y = torch.full((T, N), float("nan"), device="cuda")
+        print(f"offset-free {gtype} {mode} T={T}", flush=True)
+        qg.qgemm_q8a16(codes, scales, None, _xdev(X, xt), Y, N, K, T, mode)
+        torch.cuda.synchronize()
+        Yr, S, _ = orc.gemm("q8a16", rc, rs, None, 64, N, K, X, xt, T)
+        check_tol(Y.cpu().numpy(), Yr, S, TAU[mode], f"offset-free {gtype} {mode} T={T}")
+        if T == 1:
+            c2, s2, o2 = _repack_dev(gtype, src, N, K)
+            Y2 = torch.full((T, N), float("nan"), device="cuda")
+            qg.qgemv_q8a16(c2, s2, o2, _xdev(X, xt), Y2, N, K, T)
+            torch.cuda.synchronize()
+            assert np.array_equal(Y.cpu().numpy().view(np.uint32), Y2.cpu().numpy().view(np.uint32))
