@@ -74,8 +74,10 @@ qg_status run_dense(int fmt, const void* codes, const void* scales, const uint16
     GemmParams p = dense_params(codes, scales, offs, group, X, Y, N, K, T);
     if (mode == QG_FAST_WEXACT && ((fmt != QG_FMT_Q4 && fmt != QG_FMT_Q8) || xt != QG_X_F16)) return QG_EUNSUPPORTED;
     if (T <= 8) return launched(qg::launch_gemv(fmt, xt, p, false, s));
-    // 16-element blocks: the exact kernel in both modes (its result is well inside the fast tolerance)
-    if (mode == QG_EXACT || fmt == QG_FMT_Q8A16) return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
+    // 16-element blocks with f32 X in fast mode: the exact kernel (its result is well inside the fast
+    // tolerance)
+    if (mode == QG_EXACT || (fmt == QG_FMT_Q8A16 && xt == QG_X_F32))
+        return launched(qg::launch_gemm_exact(fmt, xt, p, false, s));
     if (mode == QG_FAST_WEXACT) return launched(qg::launch_gemm_fast_wexact(fmt, p, s));
     if (xt == QG_X_F32) return QG_EUNSUPPORTED;
     return launched(qg::launch_gemm_fast(fmt, xt, p, false, s));
@@ -162,7 +164,6 @@ qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales, 
                           int group, int N, int K, int n0, int k0, int rows, int cols, qg_xtype staged, void* out,
                           hipStream_t stream) {
     if (!fmt_ok(fmt) || !xt_ok(staged)) return QG_EINVAL;
-    if (fmt == QG_FMT_Q8A16 && staged != QG_X_F32) return QG_EUNSUPPORTED;
     if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || (K % 32) != 0) return QG_ESHAPE;
     if (fmt == QG_FMT_Q4A && (group < 32 || (group % 32) != 0 || (K % group) != 0)) return QG_ESHAPE;
     if (rows < 1 || cols < 32 || (cols % 32) != 0 || (k0 % 32) != 0 || n0 < 0 || k0 < 0 || n0 + rows > N ||

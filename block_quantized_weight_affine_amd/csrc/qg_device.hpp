@@ -206,9 +206,8 @@ __device__ __forceinline__ void value_bytes(const RawBlock<FMT>& r, uint32_t (&c
 // c0 of (1) and whether (1) gives the pages' bits for this block.
 template <int FMT>
 __device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
-    static_assert(!blk16<FMT>, "16-element blocks are staged in f32 only");
     fast = r.d > 0.0f;  // zero or negative scales (and NaN) take the pages' order
-    if constexpr (FMT == FMT_Q8A) {
+    if constexpr (FMT == FMT_Q8A || blk16<FMT>) {
         fast = false;  // two roundings (product, then offset): always the written order
         return -128.0f * r.d;
     } else if constexpr (FMT == FMT_Q8) {
@@ -229,7 +228,7 @@ __device__ __forceinline__ float block_c0(const RawBlock<FMT>& r, bool& fast) {
 // The pages' order of operations for one element (value byte as f32).
 template <int FMT>
 __device__ __forceinline__ float slow_value(const RawBlock<FMT>& r, float cf) {
-    static_assert(!blk16<FMT>, "16-element blocks are staged in f32 only");
+    static_assert(!blk16<FMT>, "16-element blocks: the element's half picks the scale (block_frags16_fixup)");
     if constexpr (FMT == FMT_Q8A)
         return keep_f32((cf - 128.0f) * r.d) + r.m;
     else if constexpr (FMT == FMT_Q8)
@@ -392,7 +391,14 @@ __device__ __forceinline__ void block_frags16_fixup(const RawBlock<FMT>& r, shor
 #pragma unroll
         for (int s = 0; s < 8; s++) {
             const int e = 8 * j + s;
-            f[j][s] = (short)f32_to_16<ST>(keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3))));
+            if constexpr (blk16<FMT>) {
+                // elements 0..15 take (d, m), 16..31 (d2, m2): fl(fl(q d) + m), then the 16-bit rounding
+                const float q = byte_f32(c[e >> 2], e & 3) - 128.0f;
+                const float v = keep_f32(q * (j < 2 ? r.d : r.d2)) + (j < 2 ? r.m : r.m2);
+                f[j][s] = (short)f32_to_16<ST>(keep_f32(v));
+            } else {
+                f[j][s] = (short)f32_to_16<ST>(keep_f32(slow_value<FMT>(r, byte_f32(c[e >> 2], e & 3))));
+            }
         }
 }
 
@@ -400,7 +406,7 @@ __device__ __forceinline__ void block_frags16_fixup(const RawBlock<FMT>& r, shor
 // pages' order.
 template <int FMT, int ST>
 __device__ __forceinline__ void block_to_frags16(const RawBlock<FMT>& r, short8_t (&f)[4]) {
-    if constexpr (FMT == FMT_Q8A) return block_frags16_fixup<FMT, ST>(r, f);  // no shortcut applies
+    if constexpr (FMT == FMT_Q8A || blk16<FMT>) return block_frags16_fixup<FMT, ST>(r, f);  // no shortcut applies
     block_to_frags16_fast<FMT, ST>(r, f);
     if (frags16_need_fixup<FMT, ST>(r)) block_frags16_fixup<FMT, ST>(r, f);
 }

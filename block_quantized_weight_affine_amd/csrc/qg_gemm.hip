@@ -431,9 +431,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
     for (int i = 0; i < WB; i++) {
         const size_t n = (size_t)min(n0 + blk(i) / 2, p.N - 1);
         wc[i] = gptr<uint8_t>((const uint8_t*)wcodes + n * (q8_layout<FMT> ? (size_t)K : (size_t)(K >> 1)));
-        wsc[i] = gptr<uint8_t>((const uint8_t*)wscales + n * (size_t)(K >> 5) * (q8_layout<FMT> ? 4 : 2));
+        wsc[i] = gptr<uint8_t>((const uint8_t*)wscales + n * (size_t)(K >> (blk16<FMT> ? 4 : 5)) * (q8_layout<FMT> ? 4 : 2));
         wof[i] = FMT == FMT_Q4A ? gptr<uint16_t>(woffs + n * (size_t)(K / p.group))
                  : FMT == FMT_Q8A ? gptr<uint16_t>((const float*)(const void*)woffs + n * (size_t)(K >> 5))
+                 : (blk16<FMT> && woffs) ? gptr<uint16_t>((const float*)(const void*)woffs + n * (size_t)(K >> 4))
                                   : nullptr;
     }
     auto load_w = [&](int st, RawBlock<FMT> (&w)[WB]) {
@@ -445,9 +446,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
                 const u32x4_t a = q[0], c = q[1];
                 w[i].q0 = make_uint4(a.x, a.y, a.z, a.w);
                 w[i].q1 = make_uint4(c.x, c.y, c.z, c.w);
-                w[i].d = ((const QG_GLOBAL float*)wsc[i])[b];
-                w[i].m = FMT == FMT_Q8A ? ((const QG_GLOBAL float*)wof[i])[b] : 0.f;
                 w[i].dh = 0;
+                if constexpr (blk16<FMT>) {
+                    // two (scale, offset) pairs; no offsets (NULL): -0, which changes no value
+                    w[i].d = ((const QG_GLOBAL float*)wsc[i])[2 * b];
+                    w[i].d2 = ((const QG_GLOBAL float*)wsc[i])[2 * b + 1];
+                    w[i].m = woffs ? ((const QG_GLOBAL float*)wof[i])[2 * b] : -0.0f;
+                    w[i].m2 = woffs ? ((const QG_GLOBAL float*)wof[i])[2 * b + 1] : -0.0f;
+                } else {
+                    w[i].d = ((const QG_GLOBAL float*)wsc[i])[b];
+                    w[i].m = FMT == FMT_Q8A ? ((const QG_GLOBAL float*)wof[i])[b] : 0.f;
+                }
             } else {
                 const u32x4_t a = *(const QG_GLOBAL u32x4_t*)(wc[i] + 16 * b);
                 w[i].q = make_uint4(a.x, a.y, a.z, a.w);
@@ -464,8 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
 #pragma unroll
         for (int i = 0; i < WB; i++) {
             RawBlock<FMT> r = w[i];
-            r.d = valid ? r.d : 0.f;
-            r.m = valid ? r.m : 0.f;
+            block_clear_if<FMT>(r, valid);
             r.dh = valid ? r.dh : 0u;
             bool fast;
             const float c0 = block_c0<FMT>(r, fast);
@@ -1273,9 +1281,11 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     // Grouped launches: 32-row tiles (MoE segments are short), 128 weight rows (three workgroups
     // per CU; measured 13% faster than 256 rows on the MoE block), 4-deep prefetch; gathered X rows
     // (row_src) take the register-direct kernel.
-    if (grouped) {
-        if (p.row_src) return fast_launch<FMT, ST, 1, 2>(p, grouped, s);
-        return fast_lds_launch<FMT, ST, 1, 1, 1, 4, true>(p, s);
+    if constexpr (!blk16<FMT>) {  // 16-element blocks have no grouped calls
+        if (grouped) {
+            if (p.row_src) return fast_launch<FMT, ST, 1, 2>(p, grouped, s);
+            return fast_lds_launch<FMT, ST, 1, 1, 1, 4, true>(p, s);
+        }
     }
     // The largest tile that still gives about one workgroup per CU: big tiles amortize each
     // decoded weight over more tokens and each staged X row over more weight rows.
@@ -1286,7 +1296,7 @@ static void fast_pick(const GemmParams& p, bool grouped, hipStream_t s) {
     // Smaller shapes: 128 x 64 tiles with K split over the wavefronts (Q4 prefill N = K = 4096, T 512:
     // 31.8 us; Q8 39.2 us); Q8A (its per-block offsets are not in that kernel's ring) the 128 x 128
     // decoded tiles
-    if constexpr (FMT == FMT_Q8A) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
+    if constexpr (FMT == FMT_Q8A || blk16<FMT>) return fast_lds_launch<FMT, ST, 2, 2, 2, 4>(p, s);
     else return fast_kz_launch<FMT, ST, 4, 2, 2>(p, s);
 }
 
@@ -1303,11 +1313,15 @@ hipError_t launch_gemm_fast(int fmt, int st, const GemmParams& p, bool grouped, 
         if (fmt == FMT_Q4) fast_pick<FMT_Q4, XT_F16>(p, grouped, s);
         else if (fmt == FMT_Q4A) fast_pick<FMT_Q4A, XT_F16>(p, grouped, s);
         else if (fmt == FMT_Q8A) fast_pick<FMT_Q8A, XT_F16>(p, grouped, s);
+        else if (fmt == FMT_Q8A16 && !grouped) fast_pick<FMT_Q8A16, XT_F16>(p, false, s);
+        else if (fmt == FMT_Q8A16) return hipErrorInvalidValue;
         else fast_pick<FMT_Q8, XT_F16>(p, grouped, s);
     } else {
         if (fmt == FMT_Q4) fast_pick<FMT_Q4, XT_BF16>(p, grouped, s);
         else if (fmt == FMT_Q4A) fast_pick<FMT_Q4A, XT_BF16>(p, grouped, s);
         else if (fmt == FMT_Q8A) fast_pick<FMT_Q8A, XT_BF16>(p, grouped, s);
+        else if (fmt == FMT_Q8A16 && !grouped) fast_pick<FMT_Q8A16, XT_BF16>(p, false, s);
+        else if (fmt == FMT_Q8A16) return hipErrorInvalidValue;
         else fast_pick<FMT_Q8, XT_BF16>(p, grouped, s);
     }
     return hipGetLastError();

@@ -87,12 +87,7 @@ hipError_t launch_dequant_dump(int fmt, const void* codes, const void* scales, c
     if (fmt == FMT_Q4) dump_st<FMT_Q4>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else if (fmt == FMT_Q4A) dump_st<FMT_Q4A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else if (fmt == FMT_Q8A) dump_st<FMT_Q8A>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
-    else if (fmt == FMT_Q8A16) {
-        if (staged != XT_F32) return hipErrorInvalidValue;  // staged in f32 only
-        const int total = rows * (cols >> 5);
-        hipLaunchKernelGGL((dequant_dump_kernel<FMT_Q8A16, XT_F32>), dim3((total + 255) / 256), dim3(256), 0, s, codes,
-                           scales, offs, group, K, n0, k0, rows, cols, out);
-    }
+    else if (fmt == FMT_Q8A16) dump_st<FMT_Q8A16>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     else dump_st<FMT_Q8>(staged, codes, scales, offs, group, K, n0, k0, rows, cols, out, s);
     return hipGetLastError();
 }

@@ -71,7 +71,7 @@ typedef enum { QG_EXACT = 0, QG_FAST = 1, QG_FAST_WEXACT = 2 } qg_mode;
 /* QG_FMT_Q8A: the target layout of the affine GGUF types (see qg_repack_gguf_q8a); dense entry
  * points, the GEMV, the batched call and the dump only.  QG_FMT_Q8A16: Q8A with a scale and an
  * offset per 16-element block, the target layout of QG_GGUF_Q6_K / Q3_K / Q2_K (see
- * qg_repack_gguf_q8a16); dense entry points and the f32 dump only. */
+ * qg_repack_gguf_q8a16); dense entry points and the dump only. */
 typedef enum { QG_FMT_Q4 = 0, QG_FMT_Q4A = 1, QG_FMT_Q8 = 2, QG_FMT_Q8A = 3, QG_FMT_Q8A16 = 4 } qg_format;
 /* GGUF block types with the scale inside each block (the values are GGML's type ids). */
 typedef enum {
@@ -128,8 +128,9 @@ qg_status qgemm_q8a(const int8_t* codes, const float* scales_f32, const float* o
  * term, w(n, k) = fl(q d) (the Q6_K and Q3_K layout, 4 bytes per 16 weights fewer to read).  This holds the GGUF K-quants whose
  * scale changes every 16 elements exactly (page "oxinfer 0.0.5 src/metal.rs", GGUF_SHADER_SRC,
  * the loaders Q6_KW, Q3_KW, Q2_KW; see qg_repack_gguf_q8a16).  T <= 8 runs the GEMV; larger T runs
- * the exact f32 MFMA kernel in QG_EXACT and in QG_FAST alike (any X type), whose result lies well
- * inside the fast tolerance; QG_FAST_WEXACT gives QG_EUNSUPPORTED.  Not accepted by qgemm_batch
+ * the exact f32 MFMA kernel in QG_EXACT, and in QG_FAST the decoded-tile f16 / bf16 kernel, which
+ * stages each value rounded to the X type (an f32 X in QG_FAST runs the exact kernel, whose result
+ * lies well inside the fast tolerance); QG_FAST_WEXACT gives QG_EUNSUPPORTED.  Not accepted by qgemm_batch
  * (QG_EUNSUPPORTED) nor by the grouped and convolution calls. */
 qg_status qgemm_q8a16(const int8_t* codes, const float* scales_f32, const float* offsets_f32,
                       const void* X, qg_xtype xt, float* Y, int N, int K, int T, qg_mode mode,
@@ -163,9 +164,7 @@ qg_status qgemv_q8a16(const int8_t* codes, const float* scales_f32, const float*
  * out is [rows][cols] of 4 or 2 bytes, 16-byte aligned.  fmt QG_FMT_Q4 / Q4A take uint16 f16
  * scales, QG_FMT_Q8 / Q8A / Q8A16 f32 scales; offsets are read for QG_FMT_Q4A (bf16 bits) and
  * QG_FMT_Q8A / Q8A16 (f32 values passed through this pointer, 4-byte aligned; NULL allowed for
- * QG_FMT_Q8A16, meaning no offset term) only.  QG_FMT_Q8A16
- * is staged in f32 only (no kernel stages it in 16 bits): another staged type gives
- * QG_EUNSUPPORTED.
+ * QG_FMT_Q8A16, meaning no offset term) only.
  */
 qg_status qg_dequant_dump(qg_format fmt, const void* codes, const void* scales,
                           const uint16_t* offsets_bf16, int group, int N, int K, int n0, int k0,

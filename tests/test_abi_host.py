@@ -224,7 +224,7 @@ def test_q8a_validation_codes():
 
 
 def test_q8a16_validation_codes():
-    """Q8A16: offsets required, W-exact unsupported, no batched, grouped, convolution or 16-bit dump;
+    """Q8A16: offsets optional but aligned, W-exact unsupported, no batched, grouped or convolution call;
     the GGUF -> Q8A16 repack checks type, sizes (K % 256), pointers and alignment."""
     L = qg.lib()
 
@@ -243,8 +243,8 @@ def test_q8a16_validation_codes():
     jobs = qg.job_array([(A16, A16b, A16, A16d, 64)])
     assert L.qgemm_batch(qg.QG_FMT_Q8A16, 64, C.cast(jobs, C.c_void_p), 1, A16c, 0, 512, 2, qg.QG_EXACT,
                          None) == qg.QG_EUNSUPPORTED
-    assert L.qg_dequant_dump(qg.QG_FMT_Q8A16, A16, A16b, A16, 64, 64, 256, 0, 0, 8, 64, 1, A16c, None) == \
-        qg.QG_EUNSUPPORTED
+    assert L.qg_dequant_dump(qg.QG_FMT_Q8A16, A16, A16b, A16 + 2, 64, 64, 256, 0, 0, 8, 64, 1, A16c, None) == \
+        qg.QG_EALIGN
     assert L.qgemm_moe_grouped(qg.QG_FMT_Q8A16, A16, 64, A16b, None, 8, A16c, 0, None, A16d, 256, 512, 8, 4,
                                qg.QG_EXACT, None) == qg.QG_EUNSUPPORTED
     assert L.qg_conv2d(qg.QG_FMT_Q8A16, A16, A16b, A16c, 8, 8, 32, 3, 1, 64, 0, 0, None, None, 0, A16d,

@@ -63,7 +63,8 @@ def test_repack_q8a16_bit_exact(orc, gtype, NK):
 @pytest.mark.parametrize("gtype", ["q6_k", "q3_k", "q2_k"])
 def test_q8a16_staged_tile_equals_gguf_decode(orc, gtype):
     """The exact kernels' decode of the repacked weights (qg_dequant_dump, f32) is the pages' value of
-    every element, bit for bit; a 16-bit staging is refused."""
+    every element, bit for bit; the fast kernels' f16 / bf16 staging is its nearest-even rounding, bit
+    for bit against the oracle's."""
     N, K = 37, 768
     src = _gguf_bytes(gtype, N, K, 71)
     codes, scales, offs = _repack_dev(gtype, src, N, K)
@@ -72,9 +73,13 @@ def test_q8a16_staged_tile_equals_gguf_decode(orc, gtype):
     torch.cuda.synchronize()
     ref = orc.gguf_dequant(gtype, src, N, K)
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
-    o16 = torch.empty((N, K), dtype=torch.int16, device="cuda")
-    with pytest.raises(RuntimeError):
-        qg.qg_dequant_dump("q8a16", codes, scales, offs, 64, N, K, 0, 0, N, K, qg.QG_X_F16, o16)
+    rc, rs, ro = orc.gguf_repack_q8a16(gtype, src, N, K)
+    for staged, code in (("f16", qg.QG_X_F16), ("bf16", qg.QG_X_BF16)):
+        o16 = torch.empty((N, K), dtype=torch.int16, device="cuda")
+        qg.qg_dequant_dump("q8a16", codes, scales, offs, 64, N, K, 0, 0, N, K, code, o16)
+        torch.cuda.synchronize()
+        r16 = orc.dequant_tile("q8a16", rc, rs, ro, 64, N, K, 0, 0, N, K, staged)
+        assert np.array_equal(o16.cpu().numpy().view(np.uint16), r16), staged
 
 
 def _fields(N, K, T, xt, seed):
@@ -114,7 +119,24 @@ CASES = [
     (390, 1056, 37, "exact", "f32"),
     (390, 1056, 37, "fast", "bf16"),
     (96, 160, 9, "fast", "f16"),
+    (200, 256, 40, "fast", "f32"),
 ]
+
+
+# fast-mode tile sizes: 256 x 256, 128 x 256 and 128 x 128 (the dispatcher's workgroup-count rule)
+BIG = [(4096, 256, 3328), (4096, 256, 1664), (1024, 128, 3200)]
+
+
+@pytest.mark.parametrize("NKT", BIG, ids=lambda c: "-".join(map(str, c)))
+def test_q8a16_fast_large_tiles_sampled(orc, NKT):
+    N, K, T = NKT
+    codes, sc, of, X = _fields(N, K, T, "f16", 2800 + T)
+    print(f"q8a16 fast {NKT}", flush=True)
+    y = _run(dev(codes), dev(sc), dev(of), X, N, K, T, "fast", "f16")
+    ns, ts = sample_idx(N, 96, 3), sample_idx(T, 40, 4)
+    Yr, S, _ = orc.gemm("q8a16", codes, sc, of, 64, N, K, X, "f16", T, ns=ns, ts=ts)
+    check_tol(y[np.ix_(ts, ns)], Yr, S, TAU["fast"], f"q8a16 fast {NKT}")
+    assert np.all(np.isfinite(y))
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
