@@ -340,6 +340,40 @@ def measure_q6k_decode(steps: int, warmup: int) -> dict:
             "bytes_per_step": nbytes, "gguf_bytes_per_step": float(nsb * 210)}
 
 
+def measure_q6k_prefill(steps: int, warmup: int) -> dict:
+    """The prefill GEMM shape (N = K = 4096, T = 512, f16 X N(0, 0.5)) over a GGUF Q6_K matrix repacked
+    on the device into the offset-free Q8A16 layout: fast mode (the decoded f16 tiles), TFLOP/s vs the
+    f16 MFMA peak; the exact-mode time of the same call beside it."""
+    import torch
+    import block_quantized_weight_affine_amd as qg
+    import synth
+    N = K = 4096
+    T = 512
+    nsb = N * K // 256
+    rng = np.random.default_rng(1701)
+    src = rng.integers(0, 256, nsb * 210).astype(np.uint8).reshape(nsb, 210)
+    d = synth.f16_uniform(1701, 1, nsb, 0.001, 0.004)
+    src[:, 208], src[:, 209] = d & 0xFF, d >> 8
+    codes = torch.empty(N * K, dtype=torch.int8, device="cuda")
+    scales = torch.empty(N * K // 16, dtype=torch.float32, device="cuda")
+    qg.qg_repack_gguf_q8a16("q6_k", _dev(src.reshape(-1)), N, K, codes, scales, None)
+    X = _dev(synth.normal_as(1701, synth.STREAM_X, T * K, 0.0, 0.5, "f16").reshape(T, K))
+    Y = torch.empty((T, N), device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    fast = _bound("qgemm_q8a16", codes.data_ptr(), scales.data_ptr(), None, X.data_ptr(), qg.QG_X_F16, Y.data_ptr(),
+                  N, K, T, qg.QG_FAST, st)
+    exact = _bound("qgemm_q8a16", codes.data_ptr(), scales.data_ptr(), None, X.data_ptr(), qg.QG_X_F16,
+                   Y.data_ptr(), N, K, T, qg.QG_EXACT, st)
+    ms, _ = _timed(fast, steps, warmup)
+    ms_exact, _ = _timed(exact, steps, warmup)
+    flops = 2.0 * T * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "q6_k_prefill_fast", "config": "gguf_q6_k_as_q8a16_no_offsets_N4096_K4096_T512",
+            "mode": "fast", "ms_per_step": ms, "us_per_step": ms * 1e3, "us_exact_mode": ms_exact * 1e3,
+            "dtype": "f16", "kernel": "gemm_fast_lds_kernel", "value": tf, "unit": "TFLOP/s", "bound": "mfma",
+            "peak": PEAK["f16"], "frac": tf / PEAK["f16"], "flops_per_step": flops}
+
+
 def measure_q8_prefill(mode: str, steps: int, warmup: int) -> dict:
     """The prefill GEMM shape with Q8 weights (N = K = 4096, T = 512, f16 X N(0, 0.5)) in the two
     fast modes: "fast" rounds each decoded weight q d to f16; "fast_wexact" keeps the codes exact in
@@ -594,6 +628,8 @@ def main():
             r = measure_gemv_t(T, 512, 50, fmt)
             also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         r = measure_q6k_decode(512, 50)
+        also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        r = measure_q6k_prefill(128, 20)
         also.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         for mode in ("fast", "fast_wexact"):
             r = measure_q8_prefill(mode, 128, 20)
