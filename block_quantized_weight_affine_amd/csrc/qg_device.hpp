@@ -350,13 +350,22 @@ __device__ __forceinline__ short8_t frag16_words_slow(const uint32_t (&c)[2], fl
     for (int s = 0; s < 8; s++) {
         const float cf = byte_f32(c[s >> 2], s & 3);
         float v;
-        if constexpr (FMT == FMT_Q8A) v = keep_f32((cf - 128.0f) * d) + m;
+        if constexpr (FMT == FMT_Q8A || blk16<FMT>) v = keep_f32((cf - 128.0f) * d) + m;
         else if constexpr (FMT == FMT_Q8) v = (cf - 128.0f) * d;
         else if constexpr (FMT == FMT_Q4) v = (cf - 8.0f) * d;
         else v = fmaf(cf - 8.0f, d, m);
         f[s] = (short)f32_to_16<ST>(keep_f32(v));
     }
     return f;
+}
+
+// Fragment jj of a block in the pages' order, for the formats (1) never applies to (Q8A, Q8A16: two
+// roundings); Q8A16 takes the (scale, offset) pair of the fragment's 16-element half.
+template <int FMT, int ST>
+__device__ __forceinline__ short8_t frag16_slow(const RawBlock<FMT>& r, int jj) {
+    const uint32_t c[2] = {value_word<FMT>(r, 2 * jj), value_word<FMT>(r, 2 * jj + 1)};
+    if constexpr (blk16<FMT>) return frag16_words_slow<FMT, ST>(c, jj < 2 ? r.d : r.d2, jj < 2 ? r.m : r.m2);
+    else return frag16_words_slow<FMT, ST>(c, r.d, r.m);
 }
 
 // The fragments as (1) gives them, without the fallback for blocks where (1) does not apply.

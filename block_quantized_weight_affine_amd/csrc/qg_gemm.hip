@@ -467,6 +467,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
         }
     };
     auto w_dst = [&](uint16_t* ws, int i) { return ws + (blk(i) >> 1) * PITCH + 32 * hsel; };
+    // Q8A / Q8A16 (two roundings per value): every fragment is decoded in the pages' order as it is
+    // staged, with no fast pass and no re-decode
+    constexpr bool kSlowOnly = FMT == FMT_Q8A || blk16<FMT>;
     // Fast decode (1) of stage st into ws; need is set where a valid block needs the pages' order.
     auto decode_store = [&](int st, uint16_t* ws, const RawBlock<FMT> (&w)[WB], bool& need) {
         const bool valid = 2 * st + hsel < nblk;
@@ -475,12 +478,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             RawBlock<FMT> r = w[i];
             block_clear_if<FMT>(r, valid);
             r.dh = valid ? r.dh : 0u;
-            bool fast;
-            const float c0 = block_c0<FMT>(r, fast);
-            if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) need = need || (valid && !fast);
             uint16_t* d = w_dst(ws, i);
+            if constexpr (kSlowOnly) {
 #pragma unroll
-            for (int j = 0; j < FPB; j++) *(short8_t*)(d + 8 * (fb + j)) = frag16_fast<FMT, ST>(r, c0, fb + j);
+                for (int j = 0; j < FPB; j++) *(short8_t*)(d + 8 * (fb + j)) = frag16_slow<FMT, ST>(r, fb + j);
+            } else {
+                bool fast;
+                const float c0 = block_c0<FMT>(r, fast);
+                if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) need = need || (valid && !fast);
+#pragma unroll
+                for (int j = 0; j < FPB; j++) *(short8_t*)(d + 8 * (fb + j)) = frag16_fast<FMT, ST>(r, c0, fb + j);
+            }
         }
     };
     // The pages' order for the blocks of stage st (rare: non-positive scales, inexact m - 8d).
@@ -565,12 +573,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
 #pragma unroll
         for (int i = 0; i < WB; i++) {
             r[i] = wr[u % NS][i];
-            r[i].d = valid ? r[i].d : 0.f;
-            r[i].m = valid ? r[i].m : 0.f;
+            block_clear_if<FMT>(r[i], valid);
             r[i].dh = valid ? r[i].dh : 0u;
-            bool fast;
-            c0[i] = block_c0<FMT>(r[i], fast);
-            if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) need = need || (valid && !fast);
+            c0[i] = 0.f;
+            if constexpr (!kSlowOnly) {
+                bool fast;
+                c0[i] = block_c0<FMT>(r[i], fast);
+                if constexpr (!(FMT == FMT_Q4 && ST == XT_F16)) need = need || (valid && !fast);
+            }
         }
 #pragma unroll
         for (int q = 0; q < NCH; q++) {
@@ -587,7 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_lds_kernel(GemmParams p
             if (q % (NCH / FPT) == 0) {
                 const int f = q / (NCH / FPT);  // fragment index of this thread: block f % WB, fragment f / WB
                 const int i = f % WB, jj = fb + f / WB;
-                *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_fast<FMT, ST>(r[i], c0[i], jj);
+                if constexpr (kSlowOnly) *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_slow<FMT, ST>(r[i], jj);
+                else *(short8_t*)(w_dst(wnx, i) + 8 * jj) = frag16_fast<FMT, ST>(r[i], c0[i], jj);
             }
             // In-order issue: VALU work only overlaps an MFMA if it sits between MFMAs, so each
             // MFMA is followed by a share of the chunk's fragment reads and decode arithmetic.
